@@ -1,0 +1,59 @@
+"""CPU tests: planted mistakes in the oracle's C source must fail a pin.
+
+Each mutant below is a plausible slip (a dropped term, a wrong sign or index, a
+transposed operand, a wrong group or size formula). It is compiled from a
+modified copy of oracle/convt_oracle.c and the whole pin suite runs against it
+in a child process; the mutant counts as caught when that process fails. Every
+mutation keeps all memory accesses in bounds.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "convt_oracle.c")
+
+MUTANTS = [
+    ("bias dropped", "const double b0 = bias ? bias[oc] : 0.0;", "const double b0 = 0.0;"),
+    ("padding sign", "const int64_t o2 = i2 * pb.S[2] - pb.P[2] + k2 * pb.D[2];",
+     "const int64_t o2 = i2 * pb.S[2] + pb.P[2] + k2 * pb.D[2];"),
+    ("dilation dropped", "const int64_t o1 = i1 * pb.S[1] - pb.P[1] + k1 * pb.D[1];",
+     "const int64_t o1 = i1 * pb.S[1] - pb.P[1] + k1;"),
+    ("stride of wrong axis", "const int64_t o2 = i2 * pb.S[2] - pb.P[2] + k2 * pb.D[2];",
+     "const int64_t o2 = i2 * pb.S[1] - pb.P[2] + k2 * pb.D[2];"),
+    ("taps flipped", "const double wv = wp[(k0 * pb.K[1] + k1) * pb.K[2] + k2];\n"
+     "                            const int64_t o =",
+     "const double wv = wp[(k0 * pb.K[1] + k1) * pb.K[2] + (pb.K[2] - 1 - k2)];\n"
+     "                            const int64_t o ="),
+    ("input channel reversed", "const double *xp = x + (b * pb.Ci + ci) * isz;\n            const double *wp = w + (ci * pb.Cog + ocl) * ksz;\n            for (int64_t i0",
+     "const double *xp = x + (b * pb.Ci + (pb.Ci - 1 - ci)) * isz;\n            const double *wp = w + (ci * pb.Cog + ocl) * ksz;\n            for (int64_t i0"),
+    ("wrong group of an output channel", "const int64_t g = oc / pb.Cog;", "const int64_t g = oc % pb.G;"),
+    ("output_padding ignored in size", "return (in - 1) * s - 2 * p + d * (k - 1) + op + 1;",
+     "return (in - 1) * s - 2 * p + d * (k - 1) + 1;"),
+    ("padding counted once in size", "return (in - 1) * s - 2 * p + d * (k - 1) + op + 1;",
+     "return (in - 1) * s - p + d * (k - 1) + op + 1;"),
+    ("first output position dropped", "if (o2 < 0 || o2 >= pb.O[2]) continue;",
+     "if (o2 < 1 || o2 >= pb.O[2]) continue;"),
+    ("signed magnitude", "if (sp) sp[o] += fabs(xv * wv);", "if (sp) sp[o] += xv * wv;"),
+    ("negative remainder in the point form", "if (t2 % pb.S[2] != 0) continue;",
+     "if (t2 % pb.S[2] > 0) continue;"),
+    ("weight channel offset transposed", "const double *wp = w + (ci * pb.Cog + ocl) * ksz;\n            for (int64_t k0",
+     "const double *wp = w + ((ci - g * pb.Cig) * pb.Cog + ocl) * ksz;\n            for (int64_t k0"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name!r} not found exactly once"
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(src.replace(old, new))
+    lib = oracle.build(force=True, src=str(msrc), out=str(tmp_path / "libmutant.so"))
+    code = ("import sys; sys.path.insert(0, %r); import oracle; from tests import oracle_pins; "
+            "o = oracle.Oracle(%r); [c(o) for c in oracle_pins.ALL_CHECKS]" % (ROOT, lib))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name!r} passed every pin"

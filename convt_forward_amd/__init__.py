@@ -1,0 +1,303 @@
+"""Python binding of libconvt, the MI355X (gfx950) ConvTranspose forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libconvt.so`` behind the C ABI declared in ``include/convt.h``.
+PyTorch provides device memory and the current stream; nothing here computes
+on the host, and there is no fallback: if the library is missing, importing
+the functions that need it raises.
+
+    y = convt_forward_amd.conv_transpose(x, w, bias, stride=2, padding=1)
+
+x: [B, C_in, I...] and w: [C_in, C_out/groups, k...] are contiguous CUDA
+(HIP) tensors of dtype float32 or bfloat16; bias is [C_out] or None. Scalars
+or per-axis tuples are accepted for stride, padding, dilation and
+output_padding.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconvt.so")
+
+MAX_NDIM = 3
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported request", 3: "device error"}
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i8": 3, "i32": 4, "i64": 5}
+ROUTES = {"auto": 0, "none": 1, "fill": 2, "phase_gemm": 3, "grouped": 4, "direct": 5, "naive": 6}
+ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
+
+
+class ConvtError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, 'unknown status')} (status {status})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("ndim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("x_shape", ctypes.c_int64 * (2 + MAX_NDIM)),
+        ("w_shape", ctypes.c_int64 * (2 + MAX_NDIM)),
+        ("stride", ctypes.c_int64 * MAX_NDIM),
+        ("padding", ctypes.c_int64 * MAX_NDIM),
+        ("dilation", ctypes.c_int64 * MAX_NDIM),
+        ("output_padding", ctypes.c_int64 * MAX_NDIM),
+        ("groups", ctypes.c_int64),
+        ("has_bias", ctypes.c_int32),
+        ("route", ctypes.c_int32),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("out_shape", ctypes.c_int64 * (2 + MAX_NDIM)),
+        ("c_out", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
+        ("n_phases", ctypes.c_int64),
+        ("useful_flops", ctypes.c_int64),
+        ("route", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libconvt.so. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m convt_forward_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.convt_plan.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(vp), ctypes.POINTER(PlanInfo)]
+        L.convt_plan.restype = ctypes.c_int
+        L.convt_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        L.convt_forward.restype = ctypes.c_int
+        L.convt_prepare_weights.argtypes = [vp, vp, vp, vp]
+        L.convt_prepare_weights.restype = ctypes.c_int
+        L.convt_forward_prepared.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        L.convt_forward_prepared.restype = ctypes.c_int
+        L.convt_destroy.argtypes = [vp]
+        L.convt_destroy.restype = None
+        L.convt_status_string.argtypes = [ctypes.c_int]
+        L.convt_status_string.restype = ctypes.c_char_p
+        L.convt_route_name.argtypes = [ctypes.c_int32]
+        L.convt_route_name.restype = ctypes.c_char_p
+        p64 = ctypes.POINTER(ctypes.c_int64)
+        L.convt_plan_axis_phase.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, p64, p64, p64, p64,
+                                            ctypes.c_int64]
+        L.convt_plan_axis_phase.restype = ctypes.c_int
+        L.convt_version.argtypes = []
+        L.convt_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _tup(v, nd: int, name: str) -> Tuple[int, ...]:
+    if isinstance(v, int):
+        return (int(v),) * nd
+    v = tuple(int(t) for t in v)
+    if len(v) != nd:
+        raise ValueError(f"{name} must have {nd} entries")
+    return v
+
+
+def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, padding=0, dilation=1,
+                 output_padding=0, groups: int = 1, has_bias: bool = False, dtype: str = "f32",
+                 route: str = "auto") -> Problem:
+    nd = len(x_shape) - 2
+    if not 1 <= nd <= MAX_NDIM or len(w_shape) != nd + 2:
+        raise ValueError("x must be [B, C_in, I...] and w [C_in, C_out/groups, k...] with 1-3 spatial axes")
+    p = Problem()
+    p.ndim = nd
+    p.dtype = DTYPES[dtype]
+    for i, v in enumerate(x_shape):
+        p.x_shape[i] = int(v)
+    for i, v in enumerate(w_shape):
+        p.w_shape[i] = int(v)
+    for name in ("stride", "padding", "dilation", "output_padding"):
+        arr = getattr(p, name)
+        for i, v in enumerate(_tup(locals()[name], nd, name)):
+            arr[i] = v
+    p.groups = int(groups)
+    p.has_bias = 1 if has_bias else 0
+    p.route = ROUTES[route]
+    return p
+
+
+class Plan:
+    """A validated problem (host only; building it makes no device call)."""
+
+    def __init__(self, problem: Problem):
+        self.problem = problem
+        self._h = ctypes.c_void_p()
+        self.info = PlanInfo()
+        st = lib().convt_plan(ctypes.byref(problem), ctypes.byref(self._h), ctypes.byref(self.info))
+        if st != 0:
+            raise ConvtError(st, "convt_plan")
+        self.ndim = problem.ndim
+
+    @classmethod
+    def create(cls, *args, **kwargs) -> "Plan":
+        return cls(make_problem(*args, **kwargs))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.convt_destroy(h)
+            self._h = ctypes.c_void_p()
+
+    @property
+    def handle(self) -> int:
+        return self._h.value
+
+    @property
+    def out_shape(self) -> Tuple[int, ...]:
+        return tuple(int(self.info.out_shape[i]) for i in range(2 + self.ndim))
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.info.workspace_bytes)
+
+    @property
+    def route(self) -> str:
+        return ROUTE_NAMES[int(self.info.route)]
+
+    @property
+    def useful_flops(self) -> int:
+        return int(self.info.useful_flops)
+
+    @property
+    def n_phases(self) -> int:
+        return int(self.info.n_phases)
+
+    def axis_phase(self, axis: int, residue: int, cap: int = 64):
+        """(q_count, taps, offsets) of one output residue of one spatial axis."""
+        q = ctypes.c_int64()
+        n = ctypes.c_int64()
+        taps = (ctypes.c_int64 * cap)()
+        offs = (ctypes.c_int64 * cap)()
+        st = lib().convt_plan_axis_phase(self._h, axis, residue, ctypes.byref(q), ctypes.byref(n),
+                                         taps, offs, cap)
+        if st != 0:
+            raise ConvtError(st, "convt_plan_axis_phase")
+        k = min(int(n.value), cap)
+        return int(q.value), [int(taps[i]) for i in range(k)], [int(offs[i]) for i in range(k)]
+
+    # --- raw pointer entry points (integers are device addresses) ---------
+    def forward_ptr(self, x: int, w: int, bias: int, y: int, workspace: int, stream: int) -> None:
+        st = lib().convt_forward(self._h, x or None, w or None, bias or None, y or None,
+                                 workspace or None, stream or None)
+        if st != 0:
+            raise ConvtError(st, "convt_forward")
+
+    def prepare_weights_ptr(self, w: int, workspace: int, stream: int) -> None:
+        st = lib().convt_prepare_weights(self._h, w or None, workspace or None, stream or None)
+        if st != 0:
+            raise ConvtError(st, "convt_prepare_weights")
+
+    def forward_prepared_ptr(self, x: int, w: int, bias: int, y: int, workspace: int,
+                             stream: int) -> None:
+        st = lib().convt_forward_prepared(self._h, x or None, w or None, bias or None, y or None,
+                                          workspace or None, stream or None)
+        if st != 0:
+            raise ConvtError(st, "convt_forward_prepared")
+
+    # --- torch tensors ------------------------------------------------------
+    def _check(self, t, shape, name):
+        import torch
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        want = torch.float32 if self.problem.dtype == DTYPES["f32"] else torch.bfloat16
+        if t.dtype != want:
+            raise ValueError(f"{name} must be {want}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def new_output(self, device):
+        import torch
+        dt = torch.float32 if self.problem.dtype == DTYPES["f32"] else torch.bfloat16
+        return torch.empty(self.out_shape, dtype=dt, device=device)
+
+    def new_workspace(self, device):
+        import torch
+        return torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device=device)
+
+    def forward(self, x, w, bias=None, y=None, workspace=None, stream=None):
+        """Enqueue y = convT(x, w) + bias on `stream` (default: torch's current
+        stream of x's device). Allocates y / the workspace with torch when not
+        given. Returns y."""
+        import torch
+        p = self.problem
+        nd = self.ndim
+        self._check(x, tuple(p.x_shape[:2 + nd]), "x")
+        self._check(w, tuple(p.w_shape[:2 + nd]), "w")
+        if p.has_bias:
+            if bias is None:
+                raise ValueError("the plan has a bias")
+            self._check(bias, (self.out_shape[1],), "bias")
+        elif bias is not None:
+            raise ValueError("the plan has no bias")
+        if y is None:
+            y = self.new_output(x.device)
+        else:
+            self._check(y, self.out_shape, "y")
+        if workspace is None:
+            workspace = self.new_workspace(x.device)
+        elif workspace.numel() * workspace.element_size() < self.workspace_bytes:
+            raise ValueError("workspace too small")
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        self.forward_ptr(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else 0,
+                         y.data_ptr(), workspace.data_ptr(), stream)
+        return y
+
+
+_plan_cache: Dict[tuple, Plan] = {}
+
+
+def get_plan(x_shape, w_shape, stride=1, padding=0, dilation=1, output_padding=0, groups=1,
+             has_bias=False, dtype="f32", route="auto") -> Plan:
+    nd = len(x_shape) - 2
+    key = (tuple(x_shape), tuple(w_shape), _tup(stride, nd, "stride"), _tup(padding, nd, "padding"),
+           _tup(dilation, nd, "dilation"), _tup(output_padding, nd, "output_padding"), int(groups),
+           bool(has_bias), dtype, route)
+    pl = _plan_cache.get(key)
+    if pl is None:
+        pl = Plan.create(x_shape, w_shape, stride, padding, dilation, output_padding, groups,
+                         has_bias, dtype, route)
+        _plan_cache[key] = pl
+    return pl
+
+
+def torch_dtype_name(t) -> str:
+    import torch
+    if t.dtype == torch.float32:
+        return "f32"
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float16:
+        return "f16"
+    if t.dtype == torch.int8:
+        return "i8"
+    if t.dtype == torch.int32:
+        return "i32"
+    if t.dtype == torch.int64:
+        return "i64"
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def conv_transpose(x, w, bias=None, stride=1, padding=0, dilation=1, output_padding=0, groups=1,
+                   route: str = "auto", y=None, workspace=None, stream=None):
+    """ConvTranspose forward on the GPU through libconvt. Returns y."""
+    pl = get_plan(tuple(x.shape), tuple(w.shape), stride, padding, dilation, output_padding, groups,
+                  bias is not None, torch_dtype_name(x), route)
+    return pl.forward(x, w, bias, y=y, workspace=workspace, stream=stream)

@@ -1,0 +1,170 @@
+// C ABI of the library (declared in include/convt.h).
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "convt.h"
+#include "convt_internal.h"
+#include "launch.h"
+
+struct convt_plan_s {
+    convt::Plan plan;
+};
+
+namespace {
+
+int64_t numel(const int64_t *shape, int n) {
+    int64_t v = 1;
+    for (int i = 0; i < n; ++i) v *= shape[i];
+    return v;
+}
+
+convt_status device_status(hipError_t e) { return e == hipSuccess ? CONVT_OK : CONVT_ERR_DEVICE; }
+
+bool needs_weights_in_workspace(int route) {
+    return route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_GROUPED;
+}
+
+}  // namespace
+
+extern "C" {
+
+convt_status convt_plan(const convt_problem *problem, convt_plan_t *out, convt_plan_info *info) {
+    if (out) *out = nullptr;
+    if (!problem || !out) return CONVT_ERR_INVALID_ARGUMENT;
+    convt_plan_s *h = new (std::nothrow) convt_plan_s;
+    if (!h) return CONVT_ERR_DEVICE;
+    const convt_status st = convt::make_plan(problem, &h->plan);
+    if (st != CONVT_OK) {
+        delete h;
+        return st;
+    }
+    if (info) *info = h->plan.info;
+    *out = h;
+    return CONVT_OK;
+}
+
+void convt_destroy(convt_plan_t plan) { delete plan; }
+
+convt_status convt_prepare_weights(convt_plan_t plan, const void *w, void *workspace, void *stream) {
+    if (!plan) return CONVT_ERR_INVALID_ARGUMENT;
+    const convt::Plan &pl = plan->plan;
+    if (!needs_weights_in_workspace(pl.route) || pl.wr_elems == 0) return CONVT_OK;
+    const int nd = pl.ndim;
+    if (!w && numel(pl.prob.w_shape, 2 + nd) > 0) return CONVT_ERR_INVALID_ARGUMENT;
+    if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
+    return device_status(convt::launch_reorder(pl, w, workspace, (hipStream_t)stream));
+}
+
+convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void *w,
+                                    const void *bias, void *y, const void *workspace,
+                                    void *stream) {
+    if (!plan) return CONVT_ERR_INVALID_ARGUMENT;
+    const convt::Plan &pl = plan->plan;
+    const int nd = pl.ndim;
+    const hipStream_t s = (hipStream_t)stream;
+    const int64_t yn = numel(pl.info.out_shape, 2 + nd);
+    if (pl.route == CONVT_ROUTE_NONE || yn == 0) return CONVT_OK;
+    if (!y) return CONVT_ERR_INVALID_ARGUMENT;
+    if (pl.prob.has_bias && !bias) return CONVT_ERR_INVALID_ARGUMENT;
+    if (!pl.prob.has_bias && bias) return CONVT_ERR_INVALID_ARGUMENT;
+    const bool x_needed = pl.route != CONVT_ROUTE_FILL;
+    if (x_needed && !x && numel(pl.prob.x_shape, 2 + nd) > 0) return CONVT_ERR_INVALID_ARGUMENT;
+    switch (pl.route) {
+        case CONVT_ROUTE_FILL:
+            return device_status(convt::launch_fill(pl, bias, y, s));
+        case CONVT_ROUTE_NAIVE:
+            if (!w) return CONVT_ERR_INVALID_ARGUMENT;
+            return device_status(convt::launch_naive(pl, x, w, bias, y, s));
+        case CONVT_ROUTE_DIRECT:
+            if (!w) return CONVT_ERR_INVALID_ARGUMENT;
+            return device_status(convt::launch_direct(pl, x, w, bias, y, s));
+        case CONVT_ROUTE_PHASE_GEMM:
+            if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
+            return device_status(convt::launch_phase_gemm(pl, x, workspace, bias, y, s));
+        case CONVT_ROUTE_GROUPED:
+            if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
+            return device_status(convt::launch_grouped(pl, x, workspace, bias, y, s));
+        default:
+            return CONVT_ERR_UNSUPPORTED;
+    }
+}
+
+convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, const void *bias,
+                           void *y, void *workspace, void *stream) {
+    if (!plan) return CONVT_ERR_INVALID_ARGUMENT;
+    const convt::Plan &pl = plan->plan;
+    const int nd = pl.ndim;
+    if (pl.route == CONVT_ROUTE_NONE || numel(pl.info.out_shape, 2 + nd) == 0) return CONVT_OK;
+    // argument checks first, so that nothing is enqueued for a bad call
+    if (!y) return CONVT_ERR_INVALID_ARGUMENT;
+    if (pl.prob.has_bias != (bias != nullptr)) return CONVT_ERR_INVALID_ARGUMENT;
+    if (pl.route != CONVT_ROUTE_FILL && !x) return CONVT_ERR_INVALID_ARGUMENT;
+    if (pl.route != CONVT_ROUTE_FILL && !w) return CONVT_ERR_INVALID_ARGUMENT;
+    if (needs_weights_in_workspace(pl.route) &&
+        (!workspace || ((uintptr_t)workspace % 16) != 0))
+        return CONVT_ERR_INVALID_ARGUMENT;
+    convt_status st = convt_prepare_weights(plan, w, workspace, stream);
+    if (st != CONVT_OK) return st;
+    return convt_forward_prepared(plan, x, w, bias, y, workspace, stream);
+}
+
+const char *convt_status_string(convt_status status) {
+    switch (status) {
+        case CONVT_OK: return "ok";
+        case CONVT_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case CONVT_ERR_UNSUPPORTED: return "unsupported request";
+        case CONVT_ERR_DEVICE: return "device error";
+        default: return "unknown status";
+    }
+}
+
+const char *convt_route_name(int32_t route) {
+    switch (route) {
+        case CONVT_ROUTE_AUTO: return "auto";
+        case CONVT_ROUTE_NONE: return "none";
+        case CONVT_ROUTE_FILL: return "fill";
+        case CONVT_ROUTE_PHASE_GEMM: return "phase_gemm";
+        case CONVT_ROUTE_GROUPED: return "grouped";
+        case CONVT_ROUTE_DIRECT: return "direct";
+        case CONVT_ROUTE_NAIVE: return "naive";
+        default: return "unknown";
+    }
+}
+
+convt_status convt_plan_axis_phase(convt_plan_t plan, int32_t axis, int64_t residue,
+                                   int64_t *q_count, int64_t *n_taps, int64_t *taps,
+                                   int64_t *offsets, int64_t cap) {
+    if (!plan) return CONVT_ERR_INVALID_ARGUMENT;
+    const convt::Plan &pl = plan->plan;
+    if (axis < 0 || axis >= pl.ndim) return CONVT_ERR_INVALID_ARGUMENT;
+    const convt_problem &p = pl.prob;
+    const int64_t I = p.x_shape[2 + axis], K = p.w_shape[2 + axis], S = p.stride[axis],
+                  P = p.padding[axis], D = p.dilation[axis];
+    const int64_t O = pl.info.out_shape[2 + axis];
+    if (residue < 0 || residue >= S) return CONVT_ERR_INVALID_ARGUMENT;
+    if (cap < 0 || (cap > 0 && (!taps || !offsets))) return CONVT_ERR_INVALID_ARGUMENT;
+    const convt::AxisResidue a = convt::axis_residue(I, K, S, P, D, O, residue);
+    if (q_count) *q_count = a.q_count;
+    if (n_taps) *n_taps = a.n_taps;
+    // ascending offset order: kk from kk_first downwards in steps of s / gcd(s, d)
+    int64_t g = S, h = D;
+    while (h) {
+        const int64_t t = g % h;
+        g = h;
+        h = t;
+    }
+    const int64_t kstep = S / g;
+    for (int64_t j = 0; j < a.n_taps && j < cap; ++j) {
+        const int64_t kk = a.kk_first - j * kstep;
+        taps[j] = kk;
+        offsets[j] = (residue + P - kk * D) / S;
+    }
+    return CONVT_OK;
+}
+
+int32_t convt_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Internal plan structures shared by the host planner, the C ABI and the
+// kernels. Plain data only (no HIP types), so the planner builds and runs
+// without a GPU.
+#pragma once
+
+#include <stdint.h>
+
+#include "convt.h"
+
+namespace convt {
+
+// Largest per-axis stride the phase-table routes take (the kernels carry one
+// table row per output residue). Larger strides go to the naive route.
+constexpr int kMaxS = 16;
+
+// Stride-phase table of one spatial axis.
+//
+// The scatter y[i*s - p + kk*d] += x[i] * w[kk] splits by output residue
+// r = o mod s: output s*q + r receives x[q + off] * w[kk] for the taps kk with
+// (r + p - kk*d) divisible by s, off = (r + p - kk*d) / s. Those taps form an
+// arithmetic progression with step kstep = s / gcd(s, d); along it the offset
+// moves by ostep = d / gcd(s, d). Taps are kept in ascending offset order,
+// i.e. descending kk: the tap-reversed orientation of the weights.
+struct DevAxis {
+    int32_t I, O, S, K, P, D;
+    int32_t kstep, ostep;
+    int32_t qmax;        // largest q_count over residues
+    int32_t span_max;    // largest (n - 1) * ostep over residues
+    int32_t umin, umax;  // smallest / largest input offset over all residues (union window)
+    int32_t n[kMaxS];    // taps of residue r
+    int32_t cum[kMaxS];  // taps of residues < r
+    int32_t kk0[kMaxS];  // first tap of residue r in plan order (its largest kk)
+    int32_t off0[kMaxS]; // input offset of that tap (the residue's smallest)
+    int32_t qn[kMaxS];   // q_count of residue r: outputs s*q + r with q < qn
+};
+
+// Everything a kernel needs, passed by value. Axis 0 is depth, 1 height,
+// 2 width; problems of rank < 3 get leading unit axes (I = O = K = S = D = 1,
+// P = 0), which leave the sums unchanged.
+struct DevParams {
+    DevAxis ax[3];
+    int32_t B, Ci, Co, G, Cig, Cog;
+    int32_t cig_pad, cog_pad;  // padded extents of the reordered weights
+    int32_t ktot;              // prod(K): taps over all phases
+    int32_t nphase;            // prod(S)
+    int32_t x_plane, y_plane;  // spatial elements of one x / y channel plane
+    int32_t has_bias;
+    // Tiling of the main kernel (meaning depends on the route).
+    int32_t td, th, tw;        // q-tile extents
+    int32_t hd, hh, hw;        // halo box extents (largest over phases)
+    int32_t nt_d, nt_h, nt_w;  // tiles per axis
+    int32_t n_co_tiles;
+    int32_t n_blocks;          // grid of the main kernel
+    int32_t xcd_remap;         // 1: block ids remapped so each XCD takes a contiguous range
+    int32_t out_rows;          // grouped route: output rows staged per block
+    int32_t grp_w_off, grp_out_off, grp_lds_bytes;  // grouped route: LDS layout (bytes)
+};
+
+struct Plan {
+    convt_problem prob;
+    convt_plan_info info;
+    DevParams dp;
+    int32_t ndim;
+    int32_t route;
+    int64_t wr_elems;   // elements of the reordered weights (workspace)
+    int32_t elem_bytes; // 4 (float32) or 2 (bfloat16)
+};
+
+// Tile constants of the kernels, shared with the planner so that it sizes
+// grids and halos the way the kernels expect.
+namespace tiles {
+// Phase GEMM
+constexpr int kGemmThreads = 256;
+constexpr int kGemmBN = 128;          // positions per block
+constexpr int kGemmBM_bf16 = 128;     // output channels per block
+constexpr int kGemmBM_f32 = 64;
+constexpr int kGemmBK_bf16 = 32;      // input channels per K chunk
+constexpr int kGemmBK_f32 = 16;
+constexpr int kGemmHaloMax = 320;     // halo box positions held in LDS (double-buffered)
+// Grouped route
+constexpr int kGrpThreads = 256;
+constexpr int kGrpCog = 16;           // MFMA N (output channels of a group, padded)
+constexpr int kGrpOutStageBytes = 32768;
+constexpr int kGrpHaloBytes = 32768;
+constexpr int kGrpWBytes = 16384;      // the group's reordered weights, staged in LDS
+// Direct route
+constexpr int kDirThreads = 256;
+constexpr int kDirSlabBytes = 32768;  // weight slab of one group in LDS (float32)
+constexpr int kDirCoChunk = 16;       // output channels accumulated per pass
+}  // namespace tiles
+
+convt_status make_plan(const convt_problem *p, Plan *out);
+
+// Per-axis residue data computed on the host (any stride; used for
+// inspection and to fill DevAxis).
+struct AxisResidue {
+    int64_t q_count, n_taps, kk_first, off_first;
+};
+AxisResidue axis_residue(int64_t I, int64_t K, int64_t S, int64_t P, int64_t D, int64_t O,
+                         int64_t r);
+
+}  // namespace convt

@@ -1,0 +1,270 @@
+// Weight reorder, bias fill, the one-thread-per-output gather kernel and the
+// small-channel direct kernel.
+#include "kcommon.h"
+#include "launch.h"
+
+namespace convt {
+
+// ---------------------------------------------------------------------------
+// Weight reorder + tap flip.
+//
+// W[g*Cig + ci][co][k0][k1][k2] (forward orientation, the layout the SKaiNET
+// convTranspose2d page states) -> Wr[g][tap][co][ci], where `tap` enumerates
+// the taps phase by phase (phases in lexicographic residue order) and, within
+// a phase, in ascending input offset (descending kk per axis: the
+// tap-reversed order). ci is contiguous so that MFMA operands are 16-byte
+// reads; co and ci are zero-padded to cog_pad and cig_pad so that the GEMM
+// loads need no masks. A block transposes a (16 ci) x (16 co) x (32 taps)
+// brick through LDS: reads run along the contiguous taps of W, writes along
+// the contiguous ci of Wr.
+// ---------------------------------------------------------------------------
+constexpr int kRoCi = 16, kRoCo = 16, kRoTk = 32;
+
+template <typename T>
+__global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__restrict__ w,
+                                                       T *__restrict__ wr) {
+    __shared__ T brick[kRoCi][kRoCo][kRoTk + 1];
+    const int nci = (p.cig_pad + kRoCi - 1) / kRoCi;
+    const int nco = (p.cog_pad + kRoCo - 1) / kRoCo;
+    const int ntk = (p.ktot + kRoTk - 1) / kRoTk;
+    int bid = blockIdx.x;
+    const int tk_b = bid % ntk;
+    bid /= ntk;
+    const int co_b = bid % nco;
+    bid /= nco;
+    const int ci_b = bid % nci;
+    const int g = bid / nci;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < kRoCi * kRoCo * kRoTk; e += 256) {
+        const int kl = e % kRoTk, col = (e / kRoTk) % kRoCo, cil = e / (kRoTk * kRoCo);
+        const int ci = ci_b * kRoCi + cil, co = co_b * kRoCo + col, kk = tk_b * kRoTk + kl;
+        T v = from_f32<T>(0.0f);
+        if (ci < p.Cig && co < p.Cog && kk < p.ktot)
+            v = w[((int64_t)(g * p.Cig + ci) * p.Cog + co) * p.ktot + kk];
+        brick[cil][col][kl] = v;
+    }
+    __syncthreads();
+    const int K1 = p.ax[1].K, K2 = p.ax[2].K;
+    for (int e = tid; e < kRoCi * kRoCo * kRoTk; e += 256) {
+        const int cil = e % kRoCi, col = (e / kRoCi) % kRoCo, kl = e / (kRoCi * kRoCo);
+        const int ci = ci_b * kRoCi + cil, co = co_b * kRoCo + col, kk = tk_b * kRoTk + kl;
+        if (ci >= p.cig_pad || co >= p.cog_pad || kk >= p.ktot) continue;
+        const int k2 = kk % K2, k1 = (kk / K2) % K1, k0 = kk / (K1 * K2);
+        const int tg = tap_global(p, k0, k1, k2);
+        wr[(((int64_t)g * p.ktot + tg) * p.cog_pad + co) * p.cig_pad + ci] = brick[cil][col][kl];
+    }
+}
+
+hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t stream) {
+    const DevParams &p = pl.dp;
+    const int64_t nci = (p.cig_pad + kRoCi - 1) / kRoCi;
+    const int64_t nco = (p.cog_pad + kRoCo - 1) / kRoCo;
+    const int64_t ntk = (p.ktot + kRoTk - 1) / kRoTk;
+    const int64_t blocks = nci * nco * ntk * p.G;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (pl.elem_bytes == 2)
+        hipLaunchKernelGGL(reorder_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, p,
+                           (const uint16_t *)w, (uint16_t *)wr);
+    else
+        hipLaunchKernelGGL(reorder_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, p,
+                           (const float *)w, (float *)wr);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fill: y = bias (or 0). Serves problems whose sums are empty (no input
+// channel or an empty input axis): every output is the bias alone.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void fill_kernel(DevParams p, const T *__restrict__ bias,
+                                                    T *__restrict__ y, int64_t total) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int oc = (int)((i / p.y_plane) % p.Co);
+        y[i] = p.has_bias ? bias[oc] : from_f32<T>(0.0f);
+    }
+}
+
+static unsigned grid_for(int64_t total) {
+    int64_t b = (total + 255) / 256;
+    return (unsigned)(b < 1 ? 1 : (b > 65536 ? 65536 : b));
+}
+
+hipError_t launch_fill(const Plan &pl, const void *bias, void *y, hipStream_t stream) {
+    const DevParams &p = pl.dp;
+    const int64_t total = (int64_t)p.B * p.Co * p.y_plane;
+    if (total <= 0) return hipSuccess;
+    if (pl.elem_bytes == 2)
+        hipLaunchKernelGGL(fill_kernel<uint16_t>, dim3(grid_for(total)), dim3(256), 0, stream, p,
+                           (const uint16_t *)bias, (uint16_t *)y, total);
+    else
+        hipLaunchKernelGGL(fill_kernel<float>, dim3(grid_for(total)), dim3(256), 0, stream, p,
+                           (const float *)bias, (float *)y, total);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Naive gather: one thread per output. For output o and tap kk the input
+// position is i = (o + p - kk*d) / s when that division is exact and
+// 0 <= i < I. Products accumulate in float32, then the bias, then one
+// rounding. Serves any stride; used where no other route applies.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void naive_kernel(DevParams p, const T *__restrict__ x,
+                                                     const T *__restrict__ w,
+                                                     const T *__restrict__ bias, T *__restrict__ y,
+                                                     int64_t total) {
+    const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t plane = idx / p.y_plane;
+        const int o = (int)(idx % p.y_plane);
+        const int oc = (int)(plane % p.Co);
+        const int64_t b = plane / p.Co;
+        const int o2 = o % a2.O, o1 = (o / a2.O) % a1.O, o0 = o / (a2.O * a1.O);
+        const int g = oc / p.Cog, ocl = oc % p.Cog;
+        float acc = 0.0f;
+        for (int ci = 0; ci < p.Cig; ++ci) {
+            const T *xp = x + ((int64_t)b * p.Ci + g * p.Cig + ci) * p.x_plane;
+            const T *wp = w + ((int64_t)(g * p.Cig + ci) * p.Cog + ocl) * p.ktot;
+            for (int k0 = 0; k0 < a0.K; ++k0) {
+                const int t0 = o0 + a0.P - k0 * a0.D;
+                if (t0 % a0.S) continue;
+                const int i0 = t0 / a0.S;
+                if (i0 < 0 || i0 >= a0.I) continue;
+                for (int k1 = 0; k1 < a1.K; ++k1) {
+                    const int t1 = o1 + a1.P - k1 * a1.D;
+                    if (t1 % a1.S) continue;
+                    const int i1 = t1 / a1.S;
+                    if (i1 < 0 || i1 >= a1.I) continue;
+                    for (int k2 = 0; k2 < a2.K; ++k2) {
+                        const int t2 = o2 + a2.P - k2 * a2.D;
+                        if (t2 % a2.S) continue;
+                        const int i2 = t2 / a2.S;
+                        if (i2 < 0 || i2 >= a2.I) continue;
+                        acc += to_f32(xp[((int64_t)i0 * a1.I + i1) * a2.I + i2]) *
+                               to_f32(wp[(k0 * a1.K + k1) * a2.K + k2]);
+                    }
+                }
+            }
+        }
+        if (p.has_bias) acc += to_f32(bias[oc]);
+        y[idx] = from_f32<T>(acc);
+    }
+}
+
+hipError_t launch_naive(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
+                        hipStream_t stream) {
+    const DevParams &p = pl.dp;
+    const int64_t total = (int64_t)p.B * p.Co * p.y_plane;
+    if (total <= 0) return hipSuccess;
+    if (pl.elem_bytes == 2)
+        hipLaunchKernelGGL(naive_kernel<uint16_t>, dim3(grid_for(total)), dim3(256), 0, stream, p,
+                           (const uint16_t *)x, (const uint16_t *)w, (const uint16_t *)bias,
+                           (uint16_t *)y, total);
+    else
+        hipLaunchKernelGGL(naive_kernel<float>, dim3(grid_for(total)), dim3(256), 0, stream, p,
+                           (const float *)x, (const float *)w, (const float *)bias, (float *)y,
+                           total);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Direct small-channel kernel. A block owns 256 consecutive output positions
+// of one (batch, group). The group's weight slab W[g*Cig .. +Cig][Cog][k...]
+// is staged once in LDS (as float32). Each lane owns one output position and
+// kCo output channels at a time; every input sample it gathers (through the
+// phase table of its output residue, so only contributing taps are visited)
+// feeds all of them. Lanes own whole outputs, so no cross-lane reduction and
+// no atomics are needed.
+// ---------------------------------------------------------------------------
+constexpr int kDirPos = 256;
+
+template <typename T>
+__global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__restrict__ x,
+                                                      const T *__restrict__ w,
+                                                      const T *__restrict__ bias,
+                                                      T *__restrict__ y) {
+    extern __shared__ float slab[];
+    constexpr int kCo = tiles::kDirCoChunk;
+    const int ntile = (p.y_plane + kDirPos - 1) / kDirPos;
+    int bid = blockIdx.x;
+    const int tile = bid % ntile;
+    bid /= ntile;
+    const int g = bid % p.G;
+    const int b = bid / p.G;
+    const int slab_n = p.Cig * p.Cog * p.ktot;
+    const T *wg = w + (int64_t)g * slab_n;
+    for (int e = threadIdx.x; e < slab_n; e += 256) slab[e] = to_f32(wg[e]);
+    __syncthreads();
+    const int o = tile * kDirPos + threadIdx.x;
+    if (o >= p.y_plane) return;
+    const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
+    const int o2 = o % a2.O, o1 = (o / a2.O) % a1.O, o0 = o / (a2.O * a1.O);
+    const int r0 = o0 % a0.S, r1 = o1 % a1.S, r2 = o2 % a2.S;
+    const int q0 = o0 / a0.S, q1 = o1 / a1.S, q2 = o2 / a2.S;
+    const int n0 = a0.n[r0], n1 = a1.n[r1], n2 = a2.n[r2];
+    const int b0 = q0 + a0.off0[r0], b1 = q1 + a1.off0[r1], b2 = q2 + a2.off0[r2];
+    const int kb0 = a0.kk0[r0], kb1 = a1.kk0[r1], kb2 = a2.kk0[r2];
+    const T *xb = x + ((int64_t)b * p.Ci + (int64_t)g * p.Cig) * p.x_plane;
+    T *yb = y + ((int64_t)b * p.Co + (int64_t)g * p.Cog) * p.y_plane + o;
+    for (int co0 = 0; co0 < p.Cog; co0 += kCo) {
+        float acc[kCo];
+#pragma unroll
+        for (int c = 0; c < kCo; ++c) acc[c] = 0.0f;
+        for (int ci = 0; ci < p.Cig; ++ci) {
+            const T *xp = xb + (int64_t)ci * p.x_plane;
+            const float *wc = slab + (ci * p.Cog + co0) * p.ktot;
+            for (int j0 = 0; j0 < n0; ++j0) {
+                const int i0 = b0 + j0 * a0.ostep;
+                if (i0 < 0 || i0 >= a0.I) continue;
+                const int k0 = kb0 - j0 * a0.kstep;
+                for (int j1 = 0; j1 < n1; ++j1) {
+                    const int i1 = b1 + j1 * a1.ostep;
+                    if (i1 < 0 || i1 >= a1.I) continue;
+                    const int k1 = kb1 - j1 * a1.kstep;
+                    for (int j2 = 0; j2 < n2; ++j2) {
+                        const int i2 = b2 + j2 * a2.ostep;
+                        if (i2 < 0 || i2 >= a2.I) continue;
+                        const int k2 = kb2 - j2 * a2.kstep;
+                        const float xv = to_f32(xp[((int64_t)i0 * a1.I + i1) * a2.I + i2]);
+                        const float *wt = wc + (k0 * a1.K + k1) * a2.K + k2;
+#pragma unroll
+                        for (int c = 0; c < kCo; ++c)
+                            if (co0 + c < p.Cog) acc[c] += xv * wt[c * p.ktot];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kCo; ++c) {
+            const int co = co0 + c;
+            if (co < p.Cog) {
+                float v = acc[c];
+                if (p.has_bias) v += to_f32(bias[g * p.Cog + co]);
+                yb[(int64_t)co * p.y_plane] = from_f32<T>(v);
+            }
+        }
+    }
+}
+
+hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
+                         hipStream_t stream) {
+    const DevParams &p = pl.dp;
+    const int64_t ntile = (p.y_plane + kDirPos - 1) / kDirPos;
+    const int64_t blocks = ntile * p.G * p.B;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const size_t lds = (size_t)p.Cig * p.Cog * p.ktot * sizeof(float);
+    if (pl.elem_bytes == 2)
+        hipLaunchKernelGGL(direct_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds, stream,
+                           p, (const uint16_t *)x, (const uint16_t *)w, (const uint16_t *)bias,
+                           (uint16_t *)y);
+    else
+        hipLaunchKernelGGL(direct_kernel<float>, dim3((unsigned)blocks), dim3(256), lds, stream, p,
+                           (const float *)x, (const float *)w, (const float *)bias, (float *)y);
+    return hipGetLastError();
+}
+
+}  // namespace convt

@@ -1,0 +1,88 @@
+// Device helpers shared by the kernels: element conversions, MFMA operand
+// types, the phase/tap decoding of the plan tables, and the block-id remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "convt_internal.h"
+
+namespace convt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// bfloat16 values travel as their 16-bit patterns.
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+    return __uint_as_float((uint32_t)v << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
+
+// The 8 XCDs take hardware block ids round-robin. With the remap, XCD k runs
+// logical blocks [k*n/8, (k+1)*n/8), so blocks that share input tiles or
+// weight slices share one L2. Requires n % 8 == 0.
+__device__ __forceinline__ int remap_block(int bid, int n, int enable) {
+    return enable ? (bid % 8) * (n / 8) + bid / 8 : bid;
+}
+
+// Phase P (lexicographic over the per-axis residues) of a plan.
+struct PhaseDesc {
+    int r[3];      // residue per axis
+    int n[3];      // taps per axis
+    int ntaps;     // product of n
+    int tapbase;   // index of the phase's first tap in the reordered weights
+};
+
+__device__ __forceinline__ PhaseDesc phase_desc(const DevParams &p, int P) {
+    PhaseDesc ph;
+    const int s1 = p.ax[1].S, s2 = p.ax[2].S;
+    ph.r[2] = P % s2;
+    ph.r[1] = (P / s2) % s1;
+    ph.r[0] = P / (s1 * s2);
+#pragma unroll
+    for (int a = 0; a < 3; ++a) ph.n[a] = p.ax[a].n[ph.r[a]];
+    ph.ntaps = ph.n[0] * ph.n[1] * ph.n[2];
+    // taps of earlier phases: residues r0' < r0 contribute cum0*K1*K2, then
+    // r1' < r1 at r0 contribute n0*cum1*K2, then r2' < r2 contribute n0*n1*cum2
+    ph.tapbase = p.ax[0].cum[ph.r[0]] * p.ax[1].K * p.ax[2].K +
+                 ph.n[0] * (p.ax[1].cum[ph.r[1]] * p.ax[2].K + ph.n[1] * p.ax[2].cum[ph.r[2]]);
+    return ph;
+}
+
+// Index, in the reordered weights, of the tap (k0, k1, k2) of the forward
+// kernel: its phase's tapbase plus its rank within the phase.
+__device__ __forceinline__ int tap_global(const DevParams &p, int k0, int k1, int k2) {
+    int kk[3] = {k0, k1, k2};
+    int r[3], j[3], n[3], cum[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        const DevAxis &ax = p.ax[a];
+        // residue of the outputs this tap reaches: r = (kk*d - p) mod s
+        int v = (kk[a] * ax.D - ax.P) % ax.S;
+        r[a] = v < 0 ? v + ax.S : v;
+        j[a] = (ax.kk0[r[a]] - kk[a]) / ax.kstep;
+        n[a] = ax.n[r[a]];
+        cum[a] = ax.cum[r[a]];
+    }
+    const int tapbase = cum[0] * p.ax[1].K * p.ax[2].K + n[0] * (cum[1] * p.ax[2].K + n[1] * cum[2]);
+    return tapbase + (j[0] * n[1] + j[1]) * n[2] + j[2];
+}
+
+}  // namespace convt

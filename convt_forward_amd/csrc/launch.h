@@ -1,0 +1,22 @@
+// Host-side launchers of the kernels. Each enqueues its kernel(s) on `stream`
+// and returns the launch status; none synchronises.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "convt_internal.h"
+
+namespace convt {
+
+hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t stream);
+hipError_t launch_fill(const Plan &pl, const void *bias, void *y, hipStream_t stream);
+hipError_t launch_naive(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
+                        hipStream_t stream);
+hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
+                         hipStream_t stream);
+hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, const void *bias,
+                             void *y, hipStream_t stream);
+hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const void *bias, void *y,
+                          hipStream_t stream);
+
+}  // namespace convt

@@ -1,0 +1,375 @@
+// Host planner: validation, output sizes, stride-phase tables, route and tile
+// choice, workspace size. Makes no HIP call, so it runs without a GPU.
+#include <string.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <limits>
+#include <numeric>
+
+#include "convt_internal.h"
+
+namespace convt {
+
+namespace {
+
+int64_t gcd64(int64_t a, int64_t b) { return std::gcd(a, b); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Python-style modulo (result in [0, m)).
+int64_t pmod(int64_t a, int64_t m) {
+    int64_t r = a % m;
+    return r < 0 ? r + m : r;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > limit / a) return false;
+    *out = a * b;
+    return true;
+}
+
+}  // namespace
+
+// Residue r of one axis: outputs s*q + r, q in [0, q_count); taps kk with
+// (r + p - kk*d) divisible by s; kk_first is the largest such kk (the first in
+// ascending-offset order) and off_first its offset (r + p - kk_first*d) / s.
+AxisResidue axis_residue(int64_t I, int64_t K, int64_t S, int64_t P, int64_t D, int64_t O,
+                         int64_t r) {
+    (void)I;
+    AxisResidue a{0, 0, -1, 0};
+    a.q_count = r < O ? ceil_div(O - r, S) : 0;
+    // Solve kk*d == r + p (mod s) for kk in [0, K).
+    const int64_t g = gcd64(S, D);
+    const int64_t kstep = S / g;
+    int64_t first = -1;
+    for (int64_t kk = 0; kk < std::min<int64_t>(K, kstep); ++kk) {
+        if (pmod(r + P - kk * D, S) == 0) {
+            first = kk;
+            break;
+        }
+    }
+    if (first < 0) return a;
+    a.n_taps = (K - 1 - first) / kstep + 1;
+    a.kk_first = first + (a.n_taps - 1) * kstep;
+    a.off_first = (r + P - a.kk_first * D) / S;  // exact
+    return a;
+}
+
+namespace {
+
+void fill_axis(DevAxis *ax, int64_t I, int64_t K, int64_t S, int64_t P, int64_t D, int64_t O) {
+    memset(ax, 0, sizeof(*ax));
+    ax->I = (int32_t)I;
+    ax->O = (int32_t)O;
+    ax->S = (int32_t)S;
+    ax->K = (int32_t)K;
+    ax->P = (int32_t)P;
+    ax->D = (int32_t)D;
+    const int64_t g = gcd64(S, D);
+    ax->kstep = (int32_t)(S / g);
+    ax->ostep = (int32_t)(D / g);
+    if (S > kMaxS) return;
+    int32_t cum = 0;
+    bool any = false;
+    for (int64_t r = 0; r < S; ++r) {
+        AxisResidue a = axis_residue(I, K, S, P, D, O, r);
+        ax->n[r] = (int32_t)a.n_taps;
+        ax->cum[r] = cum;
+        cum += (int32_t)a.n_taps;
+        ax->kk0[r] = (int32_t)a.kk_first;
+        ax->off0[r] = (int32_t)a.off_first;
+        ax->qn[r] = (int32_t)a.q_count;
+        ax->qmax = std::max<int32_t>(ax->qmax, (int32_t)a.q_count);
+        if (a.n_taps > 0) {
+            const int32_t lo = (int32_t)a.off_first;
+            const int32_t hi = (int32_t)(a.off_first + (a.n_taps - 1) * ax->ostep);
+            ax->span_max = std::max<int32_t>(ax->span_max, hi - lo);
+            ax->umin = any ? std::min(ax->umin, lo) : lo;
+            ax->umax = any ? std::max(ax->umax, hi) : hi;
+            any = true;
+        }
+    }
+}
+
+bool strides_fit(const DevParams &dp) {
+    for (int a = 0; a < 3; ++a)
+        if (dp.ax[a].S > kMaxS) return false;
+    return true;
+}
+
+// ---- phase GEMM tiling ----------------------------------------------------
+// A block computes BN positions of one phase for BM output channels. The q
+// tile is a (td, th, tw) box with td*th*tw == BN; its input halo grows by the
+// tap span of the phase on each axis and must fit the LDS halo buffer.
+bool choose_gemm_tile(DevParams *dp, int ndim) {
+    const int BN = tiles::kGemmBN;
+    int64_t best_cost = std::numeric_limits<int64_t>::max();
+    int bd = 0, bh = 0, bw = 0;
+    for (int tw = 1; tw <= BN; tw *= 2) {
+        for (int th = 1; th * tw <= BN; th *= 2) {
+            if (BN % (th * tw)) continue;
+            const int td = BN / (th * tw);
+            if (ndim < 3 && td != 1) continue;
+            if (ndim < 2 && th != 1) continue;
+            const int64_t hd = td + dp->ax[0].span_max;
+            const int64_t hh = th + dp->ax[1].span_max;
+            const int64_t hw = tw + dp->ax[2].span_max;
+            if (hd * hh * hw > tiles::kGemmHaloMax) continue;
+            const int64_t nt = ceil_div(dp->ax[0].qmax, td) * ceil_div(dp->ax[1].qmax, th) *
+                               ceil_div(dp->ax[2].qmax, tw);
+            // MFMA work of a tile (masked positions included) dominates; halo
+            // loads add a smaller term per position.
+            const int64_t avg_taps = std::max<int64_t>(1, dp->ktot / std::max(1, dp->nphase));
+            const int64_t cost = nt * (BN * avg_taps * 4 + hd * hh * hw);
+            if (cost < best_cost) {
+                best_cost = cost;
+                bd = td;
+                bh = th;
+                bw = tw;
+            }
+        }
+    }
+    if (!bw) return false;
+    dp->td = bd;
+    dp->th = bh;
+    dp->tw = bw;
+    dp->hd = bd + dp->ax[0].span_max;
+    dp->hh = bh + dp->ax[1].span_max;
+    dp->hw = bw + dp->ax[2].span_max;
+    dp->nt_d = (int32_t)ceil_div(dp->ax[0].qmax, bd);
+    dp->nt_h = (int32_t)ceil_div(dp->ax[1].qmax, bh);
+    dp->nt_w = (int32_t)ceil_div(dp->ax[2].qmax, bw);
+    return true;
+}
+
+bool gemm_eligible(const DevParams &dp, int dtype, int ndim) {
+    if (!strides_fit(dp)) return false;
+    if (dtype != CONVT_DTYPE_F32 && dtype != CONVT_DTYPE_BF16) return false;
+    DevParams tmp = dp;
+    return choose_gemm_tile(&tmp, ndim);
+}
+
+// ---- grouped route tiling -------------------------------------------------
+// A block computes every phase of a tile of q rows (qh) at one qd, over the
+// full q width, for the Cog channels of one group, and stages the output
+// rows in LDS so that they leave as dense rows.
+bool choose_grouped_tile(DevParams *dp) {
+    const DevAxis &ad = dp->ax[0], &ah = dp->ax[1], &aw = dp->ax[2];
+    // the halo covers the union of every phase's input window
+    const int64_t hw = aw.qmax + (aw.umax - aw.umin);
+    const int64_t hd = 1 + (ad.umax - ad.umin);
+    auto al = [](int64_t v) { return (v + 15) / 16 * 16; };
+    const int64_t w_bytes = (int64_t)dp->ktot * tiles::kGrpCog * dp->Cig * 2;
+    int best = 0;
+    int64_t best_halo = 0, best_out = 0;
+    for (int rows = 1; rows <= 64; rows *= 2) {
+        if (rows > ah.qmax && rows > 1) break;
+        const int64_t hh = rows + (ah.umax - ah.umin);
+        const int64_t halo_bytes = hd * hh * hw * dp->Cig * 2;
+        const int64_t out_bytes = (int64_t)dp->Cog * ad.S * ah.S * rows * aw.O * 2;
+        // dynamic LDS stays within the 64 KiB a launch gets without opting in
+        if (halo_bytes > tiles::kGrpHaloBytes || out_bytes > tiles::kGrpOutStageBytes ||
+            al(halo_bytes) + al(w_bytes) + al(out_bytes) > 65536)
+            break;
+        best = rows;
+        best_halo = halo_bytes;
+        best_out = out_bytes;
+        if ((int64_t)rows * aw.qmax >= 256) break;  // enough positions per block
+    }
+    if (!best || w_bytes > tiles::kGrpWBytes) return false;
+    dp->td = 1;
+    dp->th = best;
+    dp->tw = aw.qmax;
+    dp->hd = (int32_t)hd;
+    dp->hh = best + (ah.umax - ah.umin);
+    dp->hw = (int32_t)hw;
+    dp->nt_d = ad.qmax;
+    dp->nt_h = (int32_t)ceil_div(ah.qmax, best);
+    dp->nt_w = 1;
+    dp->out_rows = best * ah.S;
+    dp->grp_w_off = (int32_t)al(best_halo);
+    dp->grp_out_off = (int32_t)(al(best_halo) + al(w_bytes));
+    dp->grp_lds_bytes = (int32_t)(al(best_halo) + al(w_bytes) + al(best_out));
+    return true;
+}
+
+bool grouped_eligible(const DevParams &dp, int dtype) {
+    if (dtype != CONVT_DTYPE_BF16) return false;
+    if (!strides_fit(dp)) return false;
+    if (dp.Cig % 8 != 0 || dp.Cig > 64 || dp.Cog > tiles::kGrpCog) return false;
+    if ((int64_t)dp.ktot * tiles::kGrpCog * dp.Cig * 2 > tiles::kGrpWBytes) return false;
+    DevParams tmp = dp;
+    return choose_grouped_tile(&tmp);
+}
+
+bool direct_eligible(const DevParams &dp) {
+    if (!strides_fit(dp)) return false;
+    const int64_t slab = (int64_t)dp.Cig * dp.Cog * dp.ktot * 4;
+    return slab <= tiles::kDirSlabBytes;
+}
+
+}  // namespace
+
+convt_status make_plan(const convt_problem *p, Plan *pl) {
+    memset(pl, 0, sizeof(*pl));
+    if (!p) return CONVT_ERR_INVALID_ARGUMENT;
+    pl->prob = *p;
+    const int nd = p->ndim;
+    if (nd < 1 || nd > CONVT_MAX_NDIM) return CONVT_ERR_INVALID_ARGUMENT;
+    if (p->has_bias != 0 && p->has_bias != 1) return CONVT_ERR_INVALID_ARGUMENT;
+    if (p->route < CONVT_ROUTE_AUTO || p->route > CONVT_ROUTE_NAIVE)
+        return CONVT_ERR_INVALID_ARGUMENT;
+    const int64_t B = p->x_shape[0], Ci = p->x_shape[1];
+    const int64_t G = p->groups;
+    if (B < 0 || Ci < 0 || G < 1) return CONVT_ERR_INVALID_ARGUMENT;
+    if (p->w_shape[0] != Ci || p->w_shape[1] < 0) return CONVT_ERR_INVALID_ARGUMENT;
+    if (Ci % G != 0) return CONVT_ERR_INVALID_ARGUMENT;
+    const int64_t Cog = p->w_shape[1];
+    const int64_t Cig = Ci / G;
+    const int64_t lim = (int64_t)1 << 62;
+    int64_t Co;
+    if (!mul_ok(Cog, G, lim, &Co)) return CONVT_ERR_INVALID_ARGUMENT;
+
+    int64_t I[3] = {1, 1, 1}, K[3] = {1, 1, 1}, S[3] = {1, 1, 1}, P[3] = {0, 0, 0},
+            D[3] = {1, 1, 1}, OP[3] = {0, 0, 0}, O[3] = {1, 1, 1};
+    const int lead = 3 - nd;
+    for (int j = 0; j < nd; ++j) {
+        const int a = lead + j;
+        I[a] = p->x_shape[2 + j];
+        K[a] = p->w_shape[2 + j];
+        S[a] = p->stride[j];
+        P[a] = p->padding[j];
+        D[a] = p->dilation[j];
+        OP[a] = p->output_padding[j];
+        if (I[a] < 0 || K[a] < 1 || S[a] < 1 || P[a] < 0 || D[a] < 1 || OP[a] < 0)
+            return CONVT_ERR_INVALID_ARGUMENT;
+        if (OP[a] >= std::max(S[a], D[a])) return CONVT_ERR_INVALID_ARGUMENT;
+        // sizes are bounded so that the output-size arithmetic cannot overflow
+        if (I[a] > ((int64_t)1 << 31) || K[a] > ((int64_t)1 << 20) || S[a] > ((int64_t)1 << 20) ||
+            D[a] > ((int64_t)1 << 20) || P[a] > ((int64_t)1 << 40))
+            return CONVT_ERR_INVALID_ARGUMENT;
+        O[a] = (I[a] - 1) * S[a] - 2 * P[a] + D[a] * (K[a] - 1) + OP[a] + 1;
+        if (O[a] < 1) return CONVT_ERR_INVALID_ARGUMENT;
+    }
+    if (p->dtype < CONVT_DTYPE_F32 || p->dtype > CONVT_DTYPE_I64)
+        return CONVT_ERR_INVALID_ARGUMENT;
+    if (p->dtype != CONVT_DTYPE_F32 && p->dtype != CONVT_DTYPE_BF16) return CONVT_ERR_UNSUPPORTED;
+
+    // element counts
+    int64_t xpl = I[0], ypl = O[0], ktot = K[0], nph = S[0], t;
+    for (int a = 1; a < 3; ++a) {
+        if (!mul_ok(xpl, I[a], lim, &xpl) || !mul_ok(ypl, O[a], lim, &ypl) ||
+            !mul_ok(ktot, K[a], lim, &ktot) || !mul_ok(nph, S[a], lim, &nph))
+            return CONVT_ERR_INVALID_ARGUMENT;
+    }
+    int64_t xn, yn, wn;
+    if (!mul_ok(B, Ci, lim, &t) || !mul_ok(t, xpl, lim, &xn)) return CONVT_ERR_INVALID_ARGUMENT;
+    if (!mul_ok(B, Co, lim, &t) || !mul_ok(t, ypl, lim, &yn)) return CONVT_ERR_INVALID_ARGUMENT;
+    if (!mul_ok(Ci, Cog, lim, &t) || !mul_ok(t, ktot, lim, &wn)) return CONVT_ERR_INVALID_ARGUMENT;
+    const int64_t i31 = ((int64_t)1 << 31) - 1;
+    if (xpl > i31 || ypl > i31 || ktot > i31) return CONVT_ERR_INVALID_ARGUMENT;
+    if (B > i31 || Ci > i31 || Co > i31) return CONVT_ERR_INVALID_ARGUMENT;
+    (void)xn;
+    (void)wn;
+
+    pl->ndim = nd;
+    pl->elem_bytes = p->dtype == CONVT_DTYPE_F32 ? 4 : 2;
+    convt_plan_info &info = pl->info;
+    info.out_shape[0] = B;
+    info.out_shape[1] = Co;
+    for (int j = 0; j < nd; ++j) info.out_shape[2 + j] = O[lead + j];
+    info.c_out = Co;
+    info.n_phases = nph;
+    {
+        // 2 * B * C_in * Cog * prod(k) * prod(I), saturating
+        long double f = 2.0L * B * Ci * Cog * ktot * xpl;
+        info.useful_flops = f > (long double)INT64_MAX ? INT64_MAX : (int64_t)f;
+    }
+
+    DevParams &dp = pl->dp;
+    for (int a = 0; a < 3; ++a) fill_axis(&dp.ax[a], I[a], K[a], S[a], P[a], D[a], O[a]);
+    dp.B = (int32_t)B;
+    dp.Ci = (int32_t)Ci;
+    dp.Co = (int32_t)Co;
+    dp.G = (int32_t)G;
+    dp.Cig = (int32_t)Cig;
+    dp.Cog = (int32_t)Cog;
+    dp.ktot = (int32_t)ktot;
+    dp.nphase = nph > i31 ? i31 : (int32_t)nph;
+    dp.x_plane = (int32_t)xpl;
+    dp.y_plane = (int32_t)ypl;
+    dp.has_bias = p->has_bias;
+
+    // ---- route ------------------------------------------------------------
+    const bool empty_out = (B == 0 || Co == 0);
+    const bool no_terms = (Cig == 0 || xpl == 0);
+    int route = p->route;
+    const int dt = p->dtype;
+    if (route == CONVT_ROUTE_AUTO) {
+        if (empty_out)
+            route = CONVT_ROUTE_NONE;
+        else if (no_terms)
+            route = CONVT_ROUTE_FILL;
+        else if (grouped_eligible(dp, dt) && (G > 1 || Cog <= 16))
+            route = CONVT_ROUTE_GROUPED;
+        else if (direct_eligible(dp) && (Cig * ktot <= 64 || Cog <= 4))
+            route = CONVT_ROUTE_DIRECT;
+        else if (gemm_eligible(dp, dt, nd))
+            route = CONVT_ROUTE_PHASE_GEMM;
+        else if (direct_eligible(dp))
+            route = CONVT_ROUTE_DIRECT;
+        else
+            route = CONVT_ROUTE_NAIVE;
+    } else {
+        // A forced route must be able to serve the problem.
+        bool ok = false;
+        switch (route) {
+            case CONVT_ROUTE_NONE: ok = empty_out; break;
+            case CONVT_ROUTE_FILL: ok = !empty_out && no_terms; break;
+            case CONVT_ROUTE_PHASE_GEMM: ok = !empty_out && !no_terms && gemm_eligible(dp, dt, nd); break;
+            case CONVT_ROUTE_GROUPED: ok = !empty_out && !no_terms && grouped_eligible(dp, dt); break;
+            case CONVT_ROUTE_DIRECT: ok = !empty_out && !no_terms && direct_eligible(dp); break;
+            case CONVT_ROUTE_NAIVE: ok = !empty_out && !no_terms; break;
+            default: ok = false;
+        }
+        if (!ok) return CONVT_ERR_UNSUPPORTED;
+    }
+    pl->route = route;
+    info.route = route;
+
+    // ---- tiles and workspace ------------------------------------------------
+    int64_t blocks = 0;
+    if (route == CONVT_ROUTE_PHASE_GEMM) {
+        choose_gemm_tile(&dp, nd);
+        const int BM = dt == CONVT_DTYPE_BF16 ? tiles::kGemmBM_bf16 : tiles::kGemmBM_f32;
+        const int BK = dt == CONVT_DTYPE_BF16 ? tiles::kGemmBK_bf16 : tiles::kGemmBK_f32;
+        dp.cog_pad = (int32_t)(ceil_div(Cog, BM) * BM);
+        dp.cig_pad = (int32_t)(ceil_div(Cig, BK) * BK);
+        dp.n_co_tiles = (int32_t)ceil_div(Cog, BM);
+        blocks = (int64_t)dp.nt_d * dp.nt_h * dp.nt_w * dp.n_co_tiles * nph * G * B;
+    } else if (route == CONVT_ROUTE_GROUPED) {
+        choose_grouped_tile(&dp);
+        dp.cog_pad = tiles::kGrpCog;
+        dp.cig_pad = (int32_t)Cig;
+        dp.n_co_tiles = 1;
+        blocks = (int64_t)dp.nt_d * dp.nt_h * G * B;
+    }
+    if (blocks > i31) return CONVT_ERR_UNSUPPORTED;
+    dp.n_blocks = (int32_t)blocks;
+    dp.xcd_remap = (blocks % 8 == 0) ? 1 : 0;
+    if (route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_GROUPED) {
+        int64_t wr;
+        if (!mul_ok((int64_t)G * ktot, (int64_t)dp.cog_pad * dp.cig_pad, lim, &wr))
+            return CONVT_ERR_INVALID_ARGUMENT;
+        pl->wr_elems = wr;
+        info.workspace_bytes = wr * pl->elem_bytes;
+    } else {
+        pl->wr_elems = 0;
+        info.workspace_bytes = 0;
+    }
+    return CONVT_OK;
+}
+
+}  // namespace convt

@@ -1,0 +1,206 @@
+/*
+ * convt.h — C ABI of the MI355X (gfx950) ConvTranspose forward library.
+ *
+ * The operation is the transposed ("fractionally strided") convolution of an
+ * NC[D]HW input, with stride, padding, dilation, output_padding, groups and an
+ * optional bias, as defined by the scatter-add
+ *     y[b, oc, i*s - p + kk*d] += x[b, ci, i] * W[ci, oc - g*Cog, kk]
+ * over each spatial axis (SKaiNET pull request "feat(ops): implement
+ * convTranspose2d", Summary; extended per axis to 1-D and 3-D), with output
+ * size per axis (I - 1)*s - 2*p + d*(k - 1) + output_padding + 1 (same page,
+ * Summary; AWS Neuron conv3d_transpose page, Dimensions), channel ci of group g
+ * feeding output channels g*Cog ... g*Cog + Cog - 1 and C_out = Cog * groups
+ * (SKaiNET page, "groups-aware C_out"), bias added once per output channel
+ * (huggingface ai.onnx.ConvTranspose page, Description; AWS Neuron page,
+ * :param bias:).
+ *
+ * Layouts (all row-major, contiguous, element strides implied by the shapes):
+ *   x    [B, C_in, I_1..I_n]            device memory
+ *   W    [C_in, C_out/groups, k_1..k_n] device memory, forward (not flipped)
+ *                                       orientation, the layout the SKaiNET
+ *                                       page states
+ *   bias [C_out]                        device memory, optional
+ *   y    [B, C_out, O_1..O_n]           device memory, written by the library
+ * x, W, bias and y share one element type (float32 or bfloat16; the output
+ * type follows the inputs as on the huggingface page, "Use with"). Products
+ * are accumulated in float32 and the result is rounded once to the output
+ * type, after the bias is added.
+ *
+ * Ownership: the caller allocates and owns every device buffer, including the
+ * workspace (its size is reported by convt_plan). The library allocates no
+ * device memory and keeps no pointer after a call returns. A plan is host
+ * memory owned by the library until convt_destroy; it is immutable after
+ * convt_plan, so one plan may serve concurrent calls on different streams as
+ * long as each call has its own workspace and output.
+ *
+ * Errors: every entry point returns a convt_status. Argument errors are
+ * detected on the host before anything is enqueued. Device work is
+ * asynchronous on the given stream: a launch failure is reported as
+ * CONVT_ERR_DEVICE, a fault inside a kernel surfaces at the caller's next
+ * synchronisation.
+ *
+ * Stream arguments are hipStream_t values passed as void* (NULL = the null
+ * stream), so this header needs no HIP header.
+ */
+#ifndef CONVT_H
+#define CONVT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONVT_MAX_NDIM 3
+
+typedef enum convt_status {
+    CONVT_OK = 0,
+    /* a validation rule failed (see convt_plan), a NULL where a pointer is
+     * required, or a bias pointer that disagrees with has_bias */
+    CONVT_ERR_INVALID_ARGUMENT = 1,
+    /* a well-formed request this library does not compute: a non-float element
+     * type (the SKaiNET page's dtype guard: such requests fail loudly rather
+     * than corrupt), or a forced route that cannot serve the problem */
+    CONVT_ERR_UNSUPPORTED = 2,
+    /* the HIP runtime refused a launch */
+    CONVT_ERR_DEVICE = 3
+} convt_status;
+
+typedef enum convt_dtype {
+    CONVT_DTYPE_F32 = 0,
+    CONVT_DTYPE_BF16 = 1,
+    /* the codes below name element types that are refused with
+     * CONVT_ERR_UNSUPPORTED */
+    CONVT_DTYPE_F16 = 2,
+    CONVT_DTYPE_I8 = 3,
+    CONVT_DTYPE_I32 = 4,
+    CONVT_DTYPE_I64 = 5
+} convt_dtype;
+
+/* Which device route serves a plan. CONVT_ROUTE_AUTO lets the planner pick
+ * from the shapes and the element type (the huggingface page picks one
+ * implementation per call the same way, "Implementation variants"); any other
+ * value forces that route, or fails with CONVT_ERR_UNSUPPORTED if the route
+ * cannot serve the problem. */
+typedef enum convt_route {
+    CONVT_ROUTE_AUTO = 0,
+    CONVT_ROUTE_NONE = 1,       /* the output is empty: nothing to launch */
+    CONVT_ROUTE_FILL = 2,       /* no input channels: y = bias (or 0) */
+    CONVT_ROUTE_PHASE_GEMM = 3, /* stride-phase implicit-gather GEMM on MFMA */
+    CONVT_ROUTE_GROUPED = 4,    /* grouped / few-channel stride-phase kernel, MFMA, LDS-staged output */
+    CONVT_ROUTE_DIRECT = 5,     /* small-channel direct kernel, weight slab in LDS */
+    CONVT_ROUTE_NAIVE = 6       /* one thread per output, gathers its terms */
+} convt_route;
+
+/* The problem, in the terms the pages use. Only the first 2 + ndim entries
+ * of the shape arrays and the first ndim entries of the attribute arrays are
+ * read. Padding is symmetric per axis. */
+typedef struct convt_problem {
+    int32_t ndim;                               /* 1, 2 or 3 spatial axes */
+    int32_t dtype;                              /* convt_dtype of x, W, bias and y */
+    int64_t x_shape[2 + CONVT_MAX_NDIM];        /* [B, C_in, I...] */
+    int64_t w_shape[2 + CONVT_MAX_NDIM];        /* [C_in, C_out/groups, k...] */
+    int64_t stride[CONVT_MAX_NDIM];             /* >= 1 */
+    int64_t padding[CONVT_MAX_NDIM];            /* >= 0 */
+    int64_t dilation[CONVT_MAX_NDIM];           /* >= 1 */
+    int64_t output_padding[CONVT_MAX_NDIM];     /* 0 <= op < max(stride, dilation) */
+    int64_t groups;                             /* >= 1, divides C_in */
+    int32_t has_bias;                           /* 0 or 1 */
+    int32_t route;                              /* convt_route; CONVT_ROUTE_AUTO normally */
+} convt_problem;
+
+typedef struct convt_plan_info {
+    int64_t out_shape[2 + CONVT_MAX_NDIM];      /* [B, C_out, O...] (first 2 + ndim entries) */
+    int64_t c_out;                              /* w_shape[1] * groups */
+    int64_t workspace_bytes;                    /* device workspace the caller must pass (may be 0) */
+    int64_t n_phases;                           /* product of the strides */
+    int64_t useful_flops;                       /* 2 * B * C_in * (C_out/groups) * prod(k) * prod(I) */
+    int32_t route;                              /* the convt_route chosen */
+    int32_t reserved;
+} convt_plan_info;
+
+typedef struct convt_plan_s *convt_plan_t;
+
+/*
+ * Validate a problem and build a plan. Host only: no device call is made.
+ *
+ * Validation (SKaiNET page, commit message and Summary: stride, padding,
+ * outputPadding < max(stride, dilation) per axis, dilation, groups
+ * divisibility, bias shape, dtype guard; plus shape consistency):
+ *   ndim in 1..3; all sizes >= 0; kernel sizes >= 1; stride >= 1;
+ *   padding >= 0; dilation >= 1; 0 <= output_padding < max(stride, dilation);
+ *   groups >= 1 dividing C_in; w_shape[0] == C_in; every output size >= 1;
+ *   has_bias in {0, 1}; element counts of x, W and y below 2^62 and each
+ *   plane (one batch item, one channel) below 2^31 elements.
+ * A batch of 0 or C_out of 0 is valid and plans CONVT_ROUTE_NONE; C_in of 0
+ * (or an input axis of size 0 with positive output size) plans
+ * CONVT_ROUTE_FILL.
+ *
+ * On success *out receives a plan and, if info is not NULL, *info is filled.
+ * On failure *out is set to NULL (when out is not NULL) and the status says
+ * why: CONVT_ERR_INVALID_ARGUMENT or CONVT_ERR_UNSUPPORTED.
+ */
+convt_status convt_plan(const convt_problem *problem, convt_plan_t *out, convt_plan_info *info);
+
+/*
+ * y = convT(x, W) + bias, enqueued on `stream`; no host synchronisation.
+ * x, W, y: device pointers with the plan's shapes and element type; bias: a
+ * device pointer to C_out elements, required (non-NULL) iff has_bias, NULL
+ * otherwise. workspace: device memory of at least info.workspace_bytes bytes
+ * (NULL allowed when that is 0), 16-byte aligned; it must not be used by
+ * another call until this call's work on `stream` has finished. y must not
+ * overlap x, W, bias or the workspace. Runs convt_prepare_weights and then
+ * convt_forward_prepared.
+ */
+convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, const void *bias,
+                           void *y, void *workspace, void *stream);
+
+/*
+ * First half of convt_forward: reorder W into the workspace, with taps
+ * flipped and grouped by stride phase (the plan's weight layout). Weights are
+ * taken in forward orientation and reversed by the library, the behaviour the
+ * AWS Neuron page calls flip_filter_taps_in_kernel=True. Does nothing for
+ * routes that read W directly. Arguments as in convt_forward.
+ */
+convt_status convt_prepare_weights(convt_plan_t plan, const void *w, void *workspace, void *stream);
+
+/*
+ * Second half of convt_forward: compute y from x, the workspace written by
+ * convt_prepare_weights (for the same plan and the same W), W itself (used
+ * by the routes that read it directly; may be NULL for the others) and bias.
+ * Arguments as in convt_forward.
+ */
+convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void *w,
+                                    const void *bias, void *y, const void *workspace,
+                                    void *stream);
+
+/* Free a plan. NULL is accepted and ignored. */
+void convt_destroy(convt_plan_t plan);
+
+/* Static text for a status code (never NULL). */
+const char *convt_status_string(convt_status status);
+
+/* Static name of a route ("phase_gemm", ...; never NULL). */
+const char *convt_route_name(int32_t route);
+
+/*
+ * Stride-phase table of one axis of a plan, for inspection. For output residue
+ * r (0 <= r < stride of the axis) it reports the output positions s*q + r,
+ * q in [0, q_count), and the taps kk whose products land on them, in the
+ * order the plan uses (ascending input offset), with each tap's input offset
+ * off = (r + p - kk*d) / s (exact), so that y[s*q + r] gathers x[q + off] * W[kk].
+ * `axis` counts spatial axes from 0. taps/offsets receive at most `cap`
+ * entries; *n_taps gets the full count. Host only.
+ */
+convt_status convt_plan_axis_phase(convt_plan_t plan, int32_t axis, int64_t residue,
+                                   int64_t *q_count, int64_t *n_taps, int64_t *taps,
+                                   int64_t *offsets, int64_t cap);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t convt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVT_H */

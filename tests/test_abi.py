@@ -1,0 +1,232 @@
+"""CPU tests of the C ABI: the library loads and exports what include/convt.h
+declares, the planner validates and sizes problems (host only, no device call),
+the stride-phase tables have the properties the phase split relies on, and the
+entry points refuse bad arguments before touching the device."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import convt_forward_amd as C
+import oracle
+import workloads
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convt.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(convt_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.lib()
+    names = declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in convt.h but not exported"
+
+
+def test_status_and_route_names():
+    L = C.lib()
+    assert L.convt_status_string(0) == b"ok"
+    assert L.convt_status_string(1) == b"invalid argument"
+    assert L.convt_status_string(2) == b"unsupported request"
+    assert L.convt_status_string(3) == b"device error"
+    for name, code in C.ROUTES.items():
+        assert L.convt_route_name(code).decode() == name
+    assert L.convt_version() >= 100
+
+
+def plan(**kw):
+    base = dict(x_shape=(1, 1, 3), w_shape=(1, 2, 2), stride=1, padding=0, dilation=1,
+                output_padding=0, groups=1, has_bias=False, dtype="f32", route="auto")
+    base.update(kw)
+    return C.Plan.create(**base)
+
+
+def status_of(**kw):
+    try:
+        plan(**kw)
+    except C.ConvtError as e:
+        return e.status
+    return 0
+
+
+def test_page_example_shape():
+    # huggingface ai.onnx.ConvTranspose usage example: x [1,1,3], w [1,2,2], defaults
+    assert plan().out_shape == (1, 2, 4)
+
+
+@pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
+def test_workload_plans(name):
+    wl = workloads.get(name)
+    pl = plan(x_shape=wl.x_shape, w_shape=wl.w_shape, stride=wl.stride, padding=wl.padding,
+              dilation=wl.dilation, output_padding=wl.output_padding, groups=wl.groups,
+              has_bias=wl.has_bias, dtype=wl.dtype)
+    assert pl.out_shape == oracle.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding,
+                                            wl.dilation, wl.output_padding, wl.groups)
+    expect_route = {"c1_2d_f32_small": "direct", "c2_1d_f32_upsampler": "phase_gemm",
+                    "c3_2d_bf16_generator": "phase_gemm", "c4a_2d_bf16_grouped": "grouped",
+                    "c4b_2d_bf16_dilated": "phase_gemm", "c5_3d_bf16_video": "phase_gemm"}[name]
+    assert pl.route == expect_route
+    b, cin = wl.x_shape[:2]
+    assert pl.useful_flops == 2 * b * cin * wl.w_shape[1] * int(np.prod(wl.w_shape[2:])) * int(
+        np.prod(wl.x_shape[2:]))
+    assert pl.n_phases == int(np.prod(wl.stride))
+
+
+def test_plan_shapes_match_oracle_on_random_grid():
+    rng = np.random.default_rng(5)
+    for prm in oracle_pins.random_grid(rng, 300):
+        xs = (prm["B"], prm["Ci"]) + tuple(prm["I"])
+        ws = (prm["Ci"], prm["Cog"]) + tuple(prm["k"])
+        pl = plan(x_shape=xs, w_shape=ws, stride=prm["s"], padding=prm["p"], dilation=prm["d"],
+                  output_padding=prm["op"], groups=prm["groups"])
+        assert pl.out_shape == oracle.out_shape(xs, ws, prm["s"], prm["p"], prm["d"], prm["op"],
+                                                prm["groups"])
+
+
+REJECT = [
+    # SKaiNET convTranspose2d page, validation rules
+    dict(output_padding=1),                                 # op must be < max(stride, dilation) = 1
+    dict(stride=2, output_padding=2),                       # op == stride
+    dict(x_shape=(1, 3, 4), w_shape=(3, 1, 2), groups=2),   # groups must divide C_in
+    dict(x_shape=(1, 2, 4), w_shape=(3, 1, 2)),             # C_in of x and W differ
+    dict(stride=0),
+    dict(dilation=0),
+    dict(padding=-1),
+    dict(output_padding=-1),
+    dict(groups=0),
+    dict(x_shape=(1, 1, 1), w_shape=(1, 1, 1), padding=1),  # output size (1-1)*1 - 2 + 0 + 1 < 1
+    dict(w_shape=(1, 2, 0)),                                # empty kernel
+    dict(x_shape=(-1, 1, 3)),
+]
+
+
+@pytest.mark.parametrize("kw", REJECT)
+def test_plan_rejects_invalid(kw):
+    assert status_of(**kw) == 1
+
+
+@pytest.mark.parametrize("dt", ["f16", "i8", "i32", "i64"])
+def test_plan_refuses_other_dtypes_loudly(dt):
+    assert status_of(dtype=dt) == 2
+
+
+def test_plan_rejects_malformed_struct():
+    p = C.make_problem((1, 1, 3), (1, 2, 2))
+    for field, val in [("ndim", 0), ("ndim", 4), ("has_bias", 2), ("route", 99), ("dtype", 42)]:
+        q = C.make_problem((1, 1, 3), (1, 2, 2))
+        setattr(q, field, val)
+        h = ctypes.c_void_p()
+        st = C.lib().convt_plan(ctypes.byref(q), ctypes.byref(h), None)
+        assert st == 1, (field, val)
+        assert not h.value
+    h = ctypes.c_void_p(1234)
+    assert C.lib().convt_plan(None, ctypes.byref(h), None) == 1
+    assert not h.value
+    assert C.lib().convt_plan(ctypes.byref(p), None, None) == 1
+
+
+def test_edge_routes():
+    assert plan(x_shape=(0, 1, 3)).route == "none"                       # empty batch
+    assert plan(x_shape=(2, 0, 3), w_shape=(0, 2, 2)).route == "fill"    # no input channels
+    pl = plan(x_shape=(2, 3, 0), w_shape=(3, 2, 3), has_bias=True)       # empty input axis
+    assert pl.out_shape == (2, 2, 2) and pl.route == "fill"
+    assert plan(x_shape=(1, 2, 4), w_shape=(2, 3, 2), stride=17).route in ("naive", "direct")
+    # stride 17 is beyond the phase tables: only the naive route serves it
+    assert plan(x_shape=(1, 64, 4), w_shape=(64, 64, 2), stride=17).route == "naive"
+
+
+def test_forced_routes():
+    # grouped needs bfloat16 and groups of 8k channels
+    assert status_of(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2, groups=2,
+                     route="grouped") == 2
+    assert plan(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2, groups=2, dtype="bf16",
+                route="grouped").route == "grouped"
+    assert plan(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2, route="naive").route == "naive"
+    assert status_of(x_shape=(0, 1, 3), route="naive") == 2   # nothing to compute
+    assert status_of(x_shape=(1, 64, 4), w_shape=(64, 64, 2), stride=17, route="phase_gemm") == 2
+
+
+def test_workspace_sizes():
+    wl = workloads.get("c3")
+    pl = plan(x_shape=wl.x_shape, w_shape=wl.w_shape, stride=wl.stride, padding=wl.padding,
+              dtype="bf16", has_bias=True)
+    assert pl.workspace_bytes == 512 * 256 * 16 * 2  # no padding needed at these sizes
+    pl = plan(x_shape=(1, 3, 5), w_shape=(3, 5, 3), stride=2, route="phase_gemm")
+    # channels padded to the f32 tile: 16 input, 64 output
+    assert pl.workspace_bytes == 1 * 3 * 64 * 16 * 4
+    assert plan(x_shape=(1, 3, 5), w_shape=(3, 5, 3), route="naive").workspace_bytes == 0
+
+
+def test_phase_table_properties():
+    """For every residue r: taps kk with (r + p - kk*d) divisible by s, each
+    with offset (r + p - kk*d)/s, ascending; the residues partition the taps
+    and their q counts partition the outputs."""
+    rng = np.random.default_rng(6)
+    for prm in oracle_pins.random_grid(rng, 200):
+        xs = (prm["B"], prm["Ci"]) + tuple(prm["I"])
+        ws = (prm["Ci"], prm["Cog"]) + tuple(prm["k"])
+        pl = plan(x_shape=xs, w_shape=ws, stride=prm["s"], padding=prm["p"], dilation=prm["d"],
+                  output_padding=prm["op"], groups=prm["groups"])
+        for a in range(prm["nd"]):
+            s, p, d, k = prm["s"][a], prm["p"][a], prm["d"][a], prm["k"][a]
+            O = pl.out_shape[2 + a]
+            seen, qsum = [], 0
+            for r in range(s):
+                q, taps, offs = pl.axis_phase(a, r)
+                qsum += q
+                assert q == len(range(r, O, s))
+                assert offs == sorted(offs)
+                for kk, off in zip(taps, offs):
+                    assert 0 <= kk < k
+                    assert r + p - kk * d == off * s
+                assert sorted(taps) == [kk for kk in range(k) if (r + p - kk * d) % s == 0]
+                seen += taps
+            assert sorted(seen) == list(range(k))
+            assert qsum == O
+
+
+def test_forward_refuses_bad_arguments_before_launch():
+    """Each call below fails a host-side check, so nothing reaches the device."""
+    L = C.lib()
+    pl = plan(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2, has_bias=True, route="phase_gemm")
+    h = pl.handle
+    fake = 4096  # never dereferenced: every call fails an argument check first
+    assert L.convt_forward(None, fake, fake, fake, fake, fake, None) == 1
+    assert L.convt_forward(h, fake, fake, None, fake, fake, None) == 1          # bias required
+    assert L.convt_forward(h, fake, fake, fake, None, fake, None) == 1          # y required
+    assert L.convt_forward(h, None, fake, fake, fake, fake, None) == 1          # x required
+    assert L.convt_forward(h, fake, fake, fake, fake, None, None) == 1          # workspace required
+    assert L.convt_forward(h, fake, fake, fake, fake, fake + 8, None) == 1      # misaligned workspace
+    assert L.convt_prepare_weights(h, fake, None, None) == 1
+    assert L.convt_prepare_weights(None, fake, fake, None) == 1
+    assert L.convt_forward_prepared(h, fake, fake, None, fake, fake, None) == 1
+    assert L.convt_forward_prepared(None, fake, fake, fake, fake, fake, None) == 1
+    pl2 = plan(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2, has_bias=False, route="naive")
+    assert L.convt_forward(pl2.handle, fake, fake, fake, fake, None, None) == 1  # unexpected bias
+    # an empty output needs no pointers at all
+    pl3 = plan(x_shape=(0, 16, 8), w_shape=(16, 8, 4), stride=2)
+    assert L.convt_forward(pl3.handle, None, None, None, None, None, None) == 0
+    L.convt_destroy(None)
+
+
+def test_axis_phase_arguments():
+    pl = plan(x_shape=(1, 1, 5), w_shape=(1, 1, 4), stride=2, padding=1)
+    q = ctypes.c_int64()
+    n = ctypes.c_int64()
+    assert C.lib().convt_plan_axis_phase(pl.handle, 1, 0, ctypes.byref(q), ctypes.byref(n),
+                                         None, None, 0) == 1   # axis out of range
+    assert C.lib().convt_plan_axis_phase(pl.handle, 0, 2, ctypes.byref(q), ctypes.byref(n),
+                                         None, None, 0) == 1   # residue out of range
+    assert C.lib().convt_plan_axis_phase(pl.handle, 0, 1, ctypes.byref(q), ctypes.byref(n),
+                                         None, None, 0) == 0
+    assert (q.value, n.value) == (5, 2)

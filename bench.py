@@ -1,0 +1,252 @@
+"""Benchmark of the ConvTranspose forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one convt_forward call (weight reorder + main kernel) on one batch
+of seeded synthetic input already resident in HBM. Steps rotate over enough
+buffer sets (x, W, bias, y, workspace) that their total exceeds the 256 MB
+Infinity Cache, so each step reads its inputs from HBM rather than from a
+cache warmed by the previous step. The default workload is the 1-D float32
+upsampler x[16,128,1024] W[128,64,8] stride 4 pad 2.
+
+Printed: one JSON line with the useful-FLOP throughput (2*B*C_in*(C_out/g)*
+prod(k)*prod(I) per step / seconds per step), the roofline of the dominant
+kernel (its average duration measured live with HIP events on the stream it
+runs on) and the CPU oracle's throughput on a bounded sample of the same
+workload (a reported baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+import workloads
+
+DEFAULT_WORKLOAD = "c2_1d_f32_upsampler"
+
+# MI355X published peaks (dense)
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+
+# the source files whose change invalidates stored PMC traffic figures
+KERNEL_SOURCES = {
+    "phase_gemm": ["k_phase_gemm.hip", "kcommon.h", "plan.cpp"],
+    "grouped": ["k_grouped.hip", "kcommon.h", "plan.cpp"],
+    "direct": ["k_misc.hip", "kcommon.h", "plan.cpp"],
+    "naive": ["k_misc.hip", "kcommon.h", "plan.cpp"],
+}
+KERNEL_SYMBOL = {
+    "phase_gemm": "phase_gemm_kernel",
+    "grouped": "grouped_kernel",
+    "direct": "direct_kernel",
+    "naive": "naive_kernel",
+}
+
+
+def kernel_hash(route: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(route, []):
+        with open(os.path.join(ROOT, "convt_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl: workloads.Workload, out_shape) -> int:
+    """x + W + bias read once, y written once, in the workload's element type."""
+    eb = 4 if wl.dtype == "f32" else 2
+    n = int(np.prod(wl.x_shape)) + int(np.prod(wl.w_shape)) + int(np.prod(out_shape))
+    if wl.has_bias:
+        n += wl.c_out
+    return n * eb
+
+
+def useful_flops(wl: workloads.Workload) -> int:
+    b, cin = wl.x_shape[0], wl.x_shape[1]
+    return 2 * b * cin * wl.w_shape[1] * int(np.prod(wl.w_shape[2:])) * int(np.prod(wl.x_shape[2:]))
+
+
+def stored_traffic(route: str, wl_name: str):
+    """HBM bytes per launch from the committed PMC summary of this kernel and
+    workload, or None if there is none or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"{route}_{wl_name}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"^kernel_source_sha256_16:\s*(\S+)", txt, re.M)
+    m_tr = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m_hash or not m_tr or m_hash.group(1) != kernel_hash(route):
+        return None
+    return float(m_tr.group(1))
+
+
+def cpu_baseline(wl: workloads.Workload, tens: workloads.Tensors, target_s: float = 12.0):
+    """The oracle (untuned) on the host cores, on a batch subset of the
+    workload sized to roughly target_s seconds (at least one batch item; the
+    whole batch repeated if it is faster than that)."""
+    import oracle
+
+    prm = dict(stride=wl.stride, padding=wl.padding, dilation=wl.dilation,
+               output_padding=wl.output_padding, groups=wl.groups)
+    flops_per_item = useful_flops(wl) / wl.x_shape[0]
+    # probe with one batch item
+    t0 = time.perf_counter()
+    oracle.forward(tens.x[:1], tens.w, tens.bias, with_scale=False, **prm)
+    t1 = time.perf_counter() - t0
+    items = int(max(1, min(wl.x_shape[0], target_s / max(t1, 1e-6))))
+    reps = 1
+    if items == wl.x_shape[0]:
+        reps = int(max(1, target_s / max(t1 * items, 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.forward(tens.x[:items], tens.w, tens.bias, with_scale=False, **prm)
+    dt = time.perf_counter() - t0
+    flops = flops_per_item * items * reps
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{items} of {wl.x_shape[0]} batch items x {reps} pass(es), value-only fp64 "
+                  f"scatter-add, {dt:.1f} s wall",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="one of " + ", ".join(sorted(workloads.WORKLOADS)) + " or a short alias")
+    ap.add_argument("--rotate-mb", type=float, default=1024.0,
+                    help="total size of the rotated buffer sets (defeats the 256 MB cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import convt_forward_amd as C
+
+    wl = workloads.get(args.workload)
+    tens = workloads.workload_tensors(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pl = C.get_plan(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.dilation,
+                    wl.output_padding, wl.groups, wl.has_bias, wl.dtype)
+
+    def to_dev(a):
+        if wl.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x0, w0 = to_dev(tens.x_dev), to_dev(tens.w_dev)
+    b0 = to_dev(tens.bias_dev) if wl.has_bias else None
+    eb = 4 if wl.dtype == "f32" else 2
+    set_bytes = (x0.numel() + w0.numel() + (b0.numel() if b0 is not None else 0) +
+                 int(np.prod(pl.out_shape))) * eb + pl.workspace_bytes
+    nsets = int(max(1, min(256, np.ceil(args.rotate_mb * 1e6 / set_bytes))))
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(x=x0 if i == 0 else x0.clone(), w=w0 if i == 0 else w0.clone(),
+                         b=(b0 if i == 0 else b0.clone()) if b0 is not None else None,
+                         y=pl.new_output(dev), ws=pl.new_workspace(dev)))
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def step(s, ev0=None, ev1=None):
+        pl.prepare_weights_ptr(s["w"].data_ptr(), s["ws"].data_ptr(), sh)
+        if ev0 is not None:
+            ev0.record(stream)
+        pl.forward_prepared_ptr(s["x"].data_ptr(), s["w"].data_ptr(),
+                                s["b"].data_ptr() if s["b"] is not None else 0, s["y"].data_ptr(),
+                                s["ws"].data_ptr(), sh)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % nsets], ev[i][0], ev[i][1])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_per_step = (t1 - t0) / K
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_s = float(np.mean(kern_ms)) / 1e3
+
+    flops = useful_flops(wl)
+    abytes = algorithmic_bytes(wl, pl.out_shape)
+    route = pl.route
+    if route in ("phase_gemm", "direct", "naive") and wl.dtype in PEAK_TFLOPS and \
+            flops / abytes > 50.0:
+        bound, unit = "mfma", "TFLOP/s"
+        achieved = flops / kern_s / 1e12
+        peak = PEAK_TFLOPS[wl.dtype]
+    else:
+        bound, unit = "hbm", "GB/s"
+        achieved = abytes / kern_s / 1e9
+        peak = PEAK_HBM_GBS
+    traffic = stored_traffic(route, wl.name)
+    roofline = {
+        "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+        "frac": achieved / peak, "traffic": traffic,
+        "kernel": KERNEL_SYMBOL.get(route, route), "kernel_us": kern_s * 1e6,
+        "algorithmic_flops": flops, "algorithmic_bytes": abytes,
+        "kernel_source_sha256_16": kernel_hash(route),
+    }
+
+    result = {
+        "metric": "useful TFLOP/s (2*B*Cin*Cout/g*taps*in_spatial)",
+        "value": flops / sec_per_step / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": sec_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "description": wl.description,
+            "x_shape": list(wl.x_shape), "w_shape": list(wl.w_shape),
+            "stride": list(wl.stride), "padding": list(wl.padding),
+            "dilation": list(wl.dilation), "output_padding": list(wl.output_padding),
+            "groups": wl.groups, "bias": wl.has_bias, "out_shape": list(pl.out_shape),
+            "route": route, "buffer_sets": nsets,
+            "algorithmic_GBps_per_step": abytes / sec_per_step / 1e9,
+        },
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, tens)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

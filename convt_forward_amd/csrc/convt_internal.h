@@ -54,6 +54,8 @@ struct DevParams {
     int32_t xcd_remap;         // 1: block ids remapped so each XCD takes a contiguous range
     int32_t out_rows;          // grouped route: output rows staged per block
     int32_t grp_w_off, grp_out_off, grp_lds_bytes;  // grouped route: LDS layout (bytes)
+    int32_t grp_out_cstride;   // grouped route: output-tile channel stride (elements)
+    int32_t gemm_cfg;          // phase GEMM: index into tiles::kGemmCfg
 };
 
 struct Plan {
@@ -69,20 +71,28 @@ struct Plan {
 // Tile constants of the kernels, shared with the planner so that it sizes
 // grids and halos the way the kernels expect.
 namespace tiles {
-// Phase GEMM
+// Phase GEMM: tile configurations (block = 256 threads as 2 x 2 waves).
+// BM output channels x BN positions per block, BK input channels per K chunk,
+// HALO input positions of LDS halo buffer (double-buffered).
+struct GemmTile {
+    int bm, bn, bk, halo;
+};
 constexpr int kGemmThreads = 256;
-constexpr int kGemmBN = 128;          // positions per block
-constexpr int kGemmBM_bf16 = 128;     // output channels per block
-constexpr int kGemmBM_f32 = 64;
-constexpr int kGemmBK_bf16 = 32;      // input channels per K chunk
-constexpr int kGemmBK_f32 = 16;
-constexpr int kGemmHaloMax = 320;     // halo box positions held in LDS (double-buffered)
+constexpr int kGemmCfgCount = 5;
+constexpr GemmTile kGemmCfg[kGemmCfgCount] = {
+    {128, 128, 32, 320},  // 0: bf16
+    {128, 256, 32, 512},  // 1: bf16
+    {256, 128, 32, 320},  // 2: bf16
+    {64, 128, 16, 320},   // 3: f32
+    {64, 256, 16, 512},   // 4: f32
+};
 // Grouped route
 constexpr int kGrpThreads = 256;
 constexpr int kGrpCog = 16;           // MFMA N (output channels of a group, padded)
 constexpr int kGrpOutStageBytes = 32768;
 constexpr int kGrpHaloBytes = 32768;
 constexpr int kGrpWBytes = 16384;      // the group's reordered weights, staged in LDS
+constexpr int kGrpMaxKSteps = 4;       // MFMA K steps (32 each) per phase
 // Direct route
 constexpr int kDirThreads = 256;
 constexpr int kDirSlabBytes = 32768;  // weight slab of one group in LDS (float32)

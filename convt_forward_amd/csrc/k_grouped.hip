@@ -14,17 +14,23 @@
 //  1. the input halo (the q tile grown by the union of all phases' input
 //     windows) for the group's Cig channels goes to LDS with channels
 //     contiguous, and the group's reordered weights [tap][16 co][Cig] too;
-//  2. for each (phase, 16 positions) pair a wave runs ceil(taps*Cig/32)
+//  2. per phase, each wave keeps the phase's weight fragments in registers
+//     and runs, for each of its 16-position segments of a q row, up to four
 //     v_mfma_f32_16x16x32_bf16: rows = 16 positions, columns = the group's
 //     output channels (padded to 16), K = (tap, 8-channel slice) slots, four
 //     per MFMA. A lane reads its 8 channels of one tap as one 16-byte LDS row;
 //  3. results + bias are rounded to bfloat16 into an LDS output tile
 //     [co][depth residue][rows][O_w], interleaving the phases;
 //  4. the tile is written to y row by row with 16-byte stores.
+// The kernel's loops carry no per-lane integer division: positions advance
+// by 16-wide segments of a row and the K-slot decode is done once per phase.
 #include "kcommon.h"
 #include "launch.h"
 
 namespace convt {
+
+constexpr int kGrpRsrcWord3 = 0x00020000;
+constexpr uint32_t kGrpOutOfRange = 0x80000000u;
 
 __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_t *__restrict__ x,
                                                       const uint16_t *__restrict__ wr,
@@ -35,7 +41,9 @@ __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_
     uint16_t *wsl = (uint16_t *)(lds + p.grp_w_off);
     uint16_t *os = (uint16_t *)(lds + p.grp_out_off);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // uniform per wave: lets the plan tables be read with scalar loads
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int bid = remap_block(blockIdx.x, p.n_blocks, p.xcd_remap);
     const int th_i = bid % p.nt_h;
     bid /= p.nt_h;
@@ -51,20 +59,27 @@ __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_
     const int q0h = th_i * R;
     const int h0 = qd + a0.umin, h1 = q0h + a1.umin, h2 = a2.umin;
 
-    // 1a. input halo -> LDS [row][Cig]
+    // 1a. input halo -> LDS [row][Cig]; positions outside the input read
+    // an out-of-range offset (zero)
     const int hrows = p.hd * HH * HW;
-    const uint16_t *xg = x + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane;
-    const int64_t xpl = p.x_plane;
+    const uint32_t xpl_bytes = (uint32_t)p.x_plane * 2;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane), (short)0,
+        (int)((uint32_t)Cig * xpl_bytes), kGrpRsrcWord3);
     for (int it = tid; it < hrows * noct; it += 256) {
         const int oct = it / hrows, row = it - oct * hrows;
         const int c2 = row % HW, c1 = (row / HW) % HH, c0 = row / (HW * HH);
         const int i0 = h0 + c0, i1 = h1 + c1, i2 = h2 + c2;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I && i2 >= 0 && i2 < a2.I) {
-            const uint16_t *src = xg + (int64_t)(oct * 8) * xpl + ((i0 * a1.I + i1) * a2.I + i2);
+        const bool ok = i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I && i2 >= 0 && i2 < a2.I;
+        const uint32_t off = ok ? (uint32_t)(oct * 8) * xpl_bytes +
+                                      (uint32_t)((i0 * a1.I + i1) * a2.I + i2) * 2
+                                : kGrpOutOfRange;
+        u32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = (uint32_t)src[(2 * e) * xpl] | ((uint32_t)src[(2 * e + 1) * xpl] << 16);
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(xrs, off + (2 * e) * xpl_bytes, 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(xrs, off + (2 * e + 1) * xpl_bytes, 0, 0);
+            v[e] = lo | (hi << 16);
         }
         *(u32x4 *)&xs[row * Cig + oct * 8] = v;
     }
@@ -76,78 +91,94 @@ __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_
     }
     __syncthreads();
 
-    // 2-3. MFMA per (phase, 16 positions); results into the output tile
-    const int npos = R * Qw;
-    const int nmb = (npos + 15) >> 4;
-    const int npairs = p.nphase * nmb;
+    // 2-3. MFMA per (phase, 16-position row segment); results into the tile
     const int l16 = lane & 15, kg4 = lane >> 4;
     const int Cog = p.Cog;
+    const int co = l16;
     const int orows = p.out_rows;
     const int O2 = a2.O;
-    for (int pair = wave; pair < npairs; pair += 4) {
-        const int P = pair / nmb, mb = pair - P * nmb;
+    const int cstride = p.grp_out_cstride;
+    const int nseg = (Qw + 15) >> 4;
+    const int nmb = R * nseg;
+    const float bvf = (p.has_bias && co < Cog) ? bf16_to_f32(bias[g * Cog + co]) : 0.0f;
+    uint16_t *os_co = os + co * cstride;
+    for (int P = 0; P < p.nphase; ++P) {
         const PhaseDesc ph = phase_desc(p, P);
-        const int m = mb * 16 + l16;
-        const int qh_l = m / Qw, qw = m - qh_l * Qw;
-        const int base = ((a0.off0[ph.r[0]] - a0.umin) * HH + (qh_l + a1.off0[ph.r[1]] - a1.umin)) * HW +
-                         (qw + a2.off0[ph.r[2]] - a2.umin);
+        const int qn0 = a0.qn[ph.r[0]], qn1 = a1.qn[ph.r[1]], qn2 = a2.qn[ph.r[2]];
+        if (qd >= qn0) continue;  // uniform: no output of this phase in this block
         const int nslots = ph.ntaps * noct;
+        const int nkb = (nslots + 3) >> 2;  // <= kGrpMaxKSteps (planner)
         const int n1 = ph.n[1], n2 = ph.n[2];
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kb = 0; kb < nslots; kb += 4) {
-            const int slot = kb + kg4;
-            u32x4 av = {0u, 0u, 0u, 0u}, bv = {0u, 0u, 0u, 0u};
-            if (slot < nslots) {
-                const int tap = slot / noct, oct = slot - tap * noct;
-                const int j2 = tap % n2, j1 = (tap / n2) % n1, j0 = tap / (n2 * n1);
-                if (m < npos) {
-                    const int row = base + ((j0 * a0.ostep) * HH + j1 * a1.ostep) * HW + j2 * a2.ostep;
-                    av = *(const u32x4 *)&xs[row * Cig + oct * 8];
-                }
-                bv = *(const u32x4 *)&wsl[((ph.tapbase + tap) * tiles::kGrpCog + l16) * Cig + oct * 8];
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
-        }
-        // D[m = 4*kg4 + i][n = l16]: position rows, channel columns
-        const int co = l16;
-        if (co < Cog && qd < a0.qn[ph.r[0]]) {
-            const float bvf = p.has_bias ? bf16_to_f32(bias[g * Cog + co]) : 0.0f;
+        // this lane's K slot per MFMA step: halo row delta and channel slice,
+        // plus the weight fragment (constant over the phase)
+        int dl[tiles::kGrpMaxKSteps];
+        bool sl_ok[tiles::kGrpMaxKSteps];
+        bf16x8 bw[tiles::kGrpMaxKSteps];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int mm = mb * 16 + 4 * kg4 + i;
-                if (mm < npos) {
-                    const int ql = mm / Qw, qw2 = mm - ql * Qw;
-                    if (q0h + ql < a1.qn[ph.r[1]] && qw2 < a2.qn[ph.r[2]]) {
-                        const int oh_l = a1.S * ql + ph.r[1], ow = a2.S * qw2 + ph.r[2];
-                        os[((co * a0.S + ph.r[0]) * orows + oh_l) * O2 + ow] = f32_to_bf16(acc[i] + bvf);
-                    }
+        for (int kb = 0; kb < tiles::kGrpMaxKSteps; ++kb) {
+            const int slot = kb * 4 + kg4;
+            sl_ok[kb] = kb < nkb && slot < nslots;
+            const int sl = sl_ok[kb] ? slot : 0;
+            const int tap = sl / noct, oct = sl - tap * noct;
+            const int j2 = tap % n2, j1 = (tap / n2) % n1, j0 = tap / (n2 * n1);
+            dl[kb] = (((a0.off0[ph.r[0]] - a0.umin + j0 * a0.ostep) * HH +
+                       (a1.off0[ph.r[1]] - a1.umin + j1 * a1.ostep)) * HW +
+                      (a2.off0[ph.r[2]] - a2.umin + j2 * a2.ostep)) * Cig + oct * 8;
+            const u32x4 wv = *(const u32x4 *)&wsl[((ph.tapbase + tap) * tiles::kGrpCog + l16) * Cig + oct * 8];
+            bw[kb] = __builtin_bit_cast(bf16x8, sl_ok[kb] ? wv : u32x4{0u, 0u, 0u, 0u});
+        }
+        uint16_t *os_ph = os_co + ph.r[0] * orows * O2 + ph.r[1] * O2 + ph.r[2];
+        for (int mb = wave; mb < nmb; mb += 4) {
+            const int ql = mb / nseg, seg = mb - ql * nseg;  // uniform
+            if (q0h + ql >= qn1) continue;                   // uniform
+            const int qw = seg * 16 + l16;
+            const int arow = (ql * HW + qw) * Cig;
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb < tiles::kGrpMaxKSteps; ++kb) {
+                if (kb < nkb) {
+                    u32x4 av = {0u, 0u, 0u, 0u};
+                    if (sl_ok[kb] && qw < Qw) av = *(const u32x4 *)&xs[arow + dl[kb]];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                  bw[kb], acc, 0, 0, 0);
                 }
+            }
+            // D[m = 4*kg4 + i][n = l16]: positions qw0 + i of row ql, channel co
+            if (co < Cog) {
+                const int qw0 = seg * 16 + 4 * kg4;
+                uint16_t *dst = os_ph + a1.S * ql * O2 + a2.S * qw0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (qw0 + i < qn2) dst[a2.S * i] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] + bvf));
             }
         }
     }
     __syncthreads();
 
     // 4. dense rows out
-    const int nrows = Cog * a0.S * orows;
+    const int rows_co = a0.S * orows;
+    const int nrows = Cog * rows_co;
     uint16_t *yb = y + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane;
     if (vec_store) {
         const int vpr = O2 >> 3;
         for (int v = tid; v < nrows * vpr; v += 256) {
             const int row = v / vpr, c = v - row * vpr;
-            const int oh_l = row % orows, r0 = (row / orows) % a0.S, co = row / (orows * a0.S);
+            const int cc = row / rows_co, rr = row - cc * rows_co;
+            const int r0 = rr / orows, oh_l = rr - r0 * orows;
             const int od = a0.S * qd + r0, oh = a1.S * q0h + oh_l;
             if (od < a0.O && oh < a1.O)
-                *(u32x4 *)&yb[(int64_t)co * p.y_plane + ((int64_t)od * a1.O + oh) * O2 + c * 8] =
-                    *(const u32x4 *)&os[row * O2 + c * 8];
+                *(u32x4 *)&yb[(int64_t)cc * p.y_plane + ((int64_t)od * a1.O + oh) * O2 + c * 8] =
+                    *(const u32x4 *)&os[cc * cstride + rr * O2 + c * 8];
         }
     } else {
         for (int e = tid; e < nrows * O2; e += 256) {
             const int row = e / O2, c = e - row * O2;
-            const int oh_l = row % orows, r0 = (row / orows) % a0.S, co = row / (orows * a0.S);
+            const int cc = row / rows_co, rr = row - cc * rows_co;
+            const int r0 = rr / orows, oh_l = rr - r0 * orows;
             const int od = a0.S * qd + r0, oh = a1.S * q0h + oh_l;
             if (od < a0.O && oh < a1.O)
-                yb[(int64_t)co * p.y_plane + ((int64_t)od * a1.O + oh) * O2 + c] = os[row * O2 + c];
+                yb[(int64_t)cc * p.y_plane + ((int64_t)od * a1.O + oh) * O2 + c] =
+                    os[cc * cstride + rr * O2 + c];
         }
     }
 }

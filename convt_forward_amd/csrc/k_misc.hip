@@ -14,61 +14,86 @@ namespace convt {
 // a phase, in ascending input offset (descending kk per axis: the
 // tap-reversed order). ci is contiguous so that MFMA operands are 16-byte
 // reads; co and ci are zero-padded to cog_pad and cig_pad so that the GEMM
-// loads need no masks. A block transposes a (16 ci) x (16 co) x (32 taps)
-// brick through LDS: reads run along the contiguous taps of W, writes along
-// the contiguous ci of Wr.
+// loads need no masks.
+//
+// A block owns one 16-byte vector of input channels (VEC = 8 bfloat16 or 4
+// float32 channels) and a block of `ocb` output channels, over all taps. For
+// each of its channels the [ocb][ktot] slab is contiguous in W, so the block
+// reads it with consecutive lanes on consecutive elements into LDS; each lane
+// then assembles whole destination vectors (VEC channels of one (tap, co))
+// and writes them with one 16-byte store.
 // ---------------------------------------------------------------------------
-constexpr int kRoCi = 16, kRoCo = 16, kRoTk = 32;
-
 template <typename T>
 __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__restrict__ w,
-                                                       T *__restrict__ wr) {
-    __shared__ T brick[kRoCi][kRoCo][kRoTk + 1];
-    const int nci = (p.cig_pad + kRoCi - 1) / kRoCi;
-    const int nco = (p.cog_pad + kRoCo - 1) / kRoCo;
-    const int ntk = (p.ktot + kRoTk - 1) / kRoTk;
+                                                       T *__restrict__ wr, int ocb) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    T *brick = (T *)lds_raw;
+    constexpr int VEC = 16 / sizeof(T);
+    const int ktot = p.ktot;
+    const int nci = p.cig_pad / VEC;
+    const int nco = (p.cog_pad + ocb - 1) / ocb;
     int bid = blockIdx.x;
-    const int tk_b = bid % ntk;
-    bid /= ntk;
     const int co_b = bid % nco;
     bid /= nco;
     const int ci_b = bid % nci;
     const int g = bid / nci;
-    const int tid = threadIdx.x;
-    for (int e = tid; e < kRoCi * kRoCo * kRoTk; e += 256) {
-        const int kl = e % kRoTk, col = (e / kRoTk) % kRoCo, cil = e / (kRoTk * kRoCo);
-        const int ci = ci_b * kRoCi + cil, co = co_b * kRoCo + col, kk = tk_b * kRoTk + kl;
+    const int n = ocb * ktot;
+    const int co0 = co_b * ocb;
+    for (int e = threadIdx.x; e < VEC * n; e += 256) {
+        const int cil = e / n, r = e - cil * n;
+        const int ci = ci_b * VEC + cil, co = co0 + r / ktot;
         T v = from_f32<T>(0.0f);
-        if (ci < p.Cig && co < p.Cog && kk < p.ktot)
-            v = w[((int64_t)(g * p.Cig + ci) * p.Cog + co) * p.ktot + kk];
-        brick[cil][col][kl] = v;
+        if (ci < p.Cig && co < p.Cog)
+            v = w[((int64_t)(g * p.Cig + ci) * p.Cog + co0) * ktot + r];
+        brick[cil * n + r] = v;
     }
     __syncthreads();
     const int K1 = p.ax[1].K, K2 = p.ax[2].K;
-    for (int e = tid; e < kRoCi * kRoCo * kRoTk; e += 256) {
-        const int cil = e % kRoCi, col = (e / kRoCi) % kRoCo, kl = e / (kRoCi * kRoCo);
-        const int ci = ci_b * kRoCi + cil, co = co_b * kRoCo + col, kk = tk_b * kRoTk + kl;
-        if (ci >= p.cig_pad || co >= p.cog_pad || kk >= p.ktot) continue;
+    for (int v = threadIdx.x; v < n; v += 256) {
+        const int col = v / ktot, kk = v - col * ktot;
+        const int co = co0 + col;
+        if (co >= p.cog_pad) continue;
         const int k2 = kk % K2, k1 = (kk / K2) % K1, k0 = kk / (K1 * K2);
         const int tg = tap_global(p, k0, k1, k2);
-        wr[(((int64_t)g * p.ktot + tg) * p.cog_pad + co) * p.cig_pad + ci] = brick[cil][col][kl];
+        u32x4 out;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = (uint32_t)brick[(2 * e) * n + v] | ((uint32_t)brick[(2 * e + 1) * n + v] << 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = __float_as_uint((float)brick[e * n + v]);
+        }
+        *(u32x4 *)&wr[(((int64_t)g * ktot + tg) * p.cog_pad + co) * p.cig_pad + ci_b * VEC] = out;
     }
+}
+
+// Output channels per reorder block: the LDS brick (16 bytes per output
+// channel and tap) stays within 32 KiB.
+static int reorder_ocb(const DevParams &p) {
+    int ocb = 32768 / (16 * p.ktot);
+    if (ocb < 1) ocb = 1;
+    if (ocb > p.cog_pad) ocb = p.cog_pad;
+    return ocb;
 }
 
 hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t stream) {
     const DevParams &p = pl.dp;
-    const int64_t nci = (p.cig_pad + kRoCi - 1) / kRoCi;
-    const int64_t nco = (p.cog_pad + kRoCo - 1) / kRoCo;
-    const int64_t ntk = (p.ktot + kRoTk - 1) / kRoTk;
-    const int64_t blocks = nci * nco * ntk * p.G;
+    const int vec = 16 / pl.elem_bytes;
+    if (p.cig_pad % vec) return hipErrorInvalidValue;
+    const int ocb = reorder_ocb(p);
+    const int64_t nco = (p.cog_pad + ocb - 1) / ocb;
+    const int64_t blocks = (int64_t)p.G * (p.cig_pad / vec) * nco;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const size_t lds = (size_t)16 * ocb * p.ktot;
+    if (lds > 65536) return hipErrorInvalidConfiguration;
     if (pl.elem_bytes == 2)
-        hipLaunchKernelGGL(reorder_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, p,
-                           (const uint16_t *)w, (uint16_t *)wr);
+        hipLaunchKernelGGL(reorder_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds, stream,
+                           p, (const uint16_t *)w, (uint16_t *)wr, ocb);
     else
-        hipLaunchKernelGGL(reorder_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, p,
-                           (const float *)w, (float *)wr);
+        hipLaunchKernelGGL(reorder_kernel<float>, dim3((unsigned)blocks), dim3(256), lds, stream, p,
+                           (const float *)w, (float *)wr, ocb);
     return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <limits>
 #include <numeric>
@@ -103,8 +104,7 @@ bool strides_fit(const DevParams &dp) {
 // A block computes BN positions of one phase for BM output channels. The q
 // tile is a (td, th, tw) box with td*th*tw == BN; its input halo grows by the
 // tap span of the phase on each axis and must fit the LDS halo buffer.
-bool choose_gemm_tile(DevParams *dp, int ndim) {
-    const int BN = tiles::kGemmBN;
+bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max) {
     int64_t best_cost = std::numeric_limits<int64_t>::max();
     int bd = 0, bh = 0, bw = 0;
     for (int tw = 1; tw <= BN; tw *= 2) {
@@ -116,7 +116,7 @@ bool choose_gemm_tile(DevParams *dp, int ndim) {
             const int64_t hd = td + dp->ax[0].span_max;
             const int64_t hh = th + dp->ax[1].span_max;
             const int64_t hw = tw + dp->ax[2].span_max;
-            if (hd * hh * hw > tiles::kGemmHaloMax) continue;
+            if (hd * hh * hw > halo_max) continue;
             const int64_t nt = ceil_div(dp->ax[0].qmax, td) * ceil_div(dp->ax[1].qmax, th) *
                                ceil_div(dp->ax[2].qmax, tw);
             // MFMA work of a tile (masked positions included) dominates; halo
@@ -144,11 +144,48 @@ bool choose_gemm_tile(DevParams *dp, int ndim) {
     return true;
 }
 
+// Pick the tile configuration with the smallest modelled time: blocks run in
+// rounds over 256 CUs (two per CU when their LDS allows), each round costing
+// its blocks' padded MFMA work weighted by LDS operand reads per MFMA.
+int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
+    const bool bf16 = dtype == CONVT_DTYPE_BF16;
+    int best = -1;
+    double best_t = 0;
+    DevParams best_dp{};
+    for (int c = 0; c < tiles::kGemmCfgCount; ++c) {
+        const tiles::GemmTile &t = tiles::kGemmCfg[c];
+        if ((t.bk == 32) != bf16) continue;
+        DevParams tmp = *dp;
+        if (!choose_gemm_tile(&tmp, ndim, t.bn, t.halo)) continue;
+        const int64_t co_tiles = ceil_div(tmp.Cog, t.bm);
+        const int64_t blocks =
+            (int64_t)tmp.nt_d * tmp.nt_h * tmp.nt_w * co_tiles * tmp.nphase * tmp.G * tmp.B;
+        const int esz = bf16 ? 2 : 4;
+        const int64_t lds = 2LL * (t.halo + t.bm) * (t.bk + 16 / esz) * esz;
+        const int bpc = lds <= 80 * 1024 ? 2 : 1;
+        // LDS fragment reads per MFMA for the wave tile (bm/2 x bn/2)
+        const double mt = t.bm / 64.0, nt = t.bn / 64.0;
+        const double lds_factor = (mt + nt) / (mt * nt);
+        const double rounds = std::ceil((double)blocks / (256.0 * bpc));
+        const double time = rounds * bpc * (double)t.bm * t.bn * lds_factor;
+        if (best < 0 || time < best_t * 0.999) {
+            best = c;
+            best_t = time;
+            best_dp = tmp;
+        }
+    }
+    if (best >= 0) {
+        *dp = best_dp;
+        dp->gemm_cfg = best;
+    }
+    return best;
+}
+
 bool gemm_eligible(const DevParams &dp, int dtype, int ndim) {
-    if (!strides_fit(dp)) return false;
+    if (!strides_fit(dp) || dp.ktot > 4096) return false;
     if (dtype != CONVT_DTYPE_F32 && dtype != CONVT_DTYPE_BF16) return false;
     DevParams tmp = dp;
-    return choose_gemm_tile(&tmp, ndim);
+    return pick_gemm_cfg(&tmp, dtype, ndim) >= 0;
 }
 
 // ---- grouped route tiling -------------------------------------------------
@@ -163,12 +200,15 @@ bool choose_grouped_tile(DevParams *dp) {
     auto al = [](int64_t v) { return (v + 15) / 16 * 16; };
     const int64_t w_bytes = (int64_t)dp->ktot * tiles::kGrpCog * dp->Cig * 2;
     int best = 0;
-    int64_t best_halo = 0, best_out = 0;
+    int64_t best_halo = 0, best_out = 0, best_cstride = 0;
     for (int rows = 1; rows <= 64; rows *= 2) {
         if (rows > ah.qmax && rows > 1) break;
         const int64_t hh = rows + (ah.umax - ah.umin);
         const int64_t halo_bytes = hd * hh * hw * dp->Cig * 2;
-        const int64_t out_bytes = (int64_t)dp->Cog * ad.S * ah.S * rows * aw.O * 2;
+        // output tile [co][depth residue][rows][O_w]; the channel stride is
+        // padded by 8 elements to spread the channels over LDS banks
+        const int64_t cstride = (int64_t)ad.S * ah.S * rows * aw.O + 8;
+        const int64_t out_bytes = (int64_t)dp->Cog * cstride * 2;
         // dynamic LDS stays within the 64 KiB a launch gets without opting in
         if (halo_bytes > tiles::kGrpHaloBytes || out_bytes > tiles::kGrpOutStageBytes ||
             al(halo_bytes) + al(w_bytes) + al(out_bytes) > 65536)
@@ -176,6 +216,7 @@ bool choose_grouped_tile(DevParams *dp) {
         best = rows;
         best_halo = halo_bytes;
         best_out = out_bytes;
+        best_cstride = cstride;
         if ((int64_t)rows * aw.qmax >= 256) break;  // enough positions per block
     }
     if (!best || w_bytes > tiles::kGrpWBytes) return false;
@@ -189,6 +230,7 @@ bool choose_grouped_tile(DevParams *dp) {
     dp->nt_h = (int32_t)ceil_div(ah.qmax, best);
     dp->nt_w = 1;
     dp->out_rows = best * ah.S;
+    dp->grp_out_cstride = (int32_t)best_cstride;
     dp->grp_w_off = (int32_t)al(best_halo);
     dp->grp_out_off = (int32_t)(al(best_halo) + al(w_bytes));
     dp->grp_lds_bytes = (int32_t)(al(best_halo) + al(w_bytes) + al(best_out));
@@ -196,9 +238,17 @@ bool choose_grouped_tile(DevParams *dp) {
 }
 
 bool grouped_eligible(const DevParams &dp, int dtype) {
-    if (dtype != CONVT_DTYPE_BF16) return false;
+    if (dtype != CONVT_DTYPE_BF16 || dp.ktot > 4096) return false;
     if (!strides_fit(dp)) return false;
     if (dp.Cig % 8 != 0 || dp.Cig > 64 || dp.Cog > tiles::kGrpCog) return false;
+    // every phase's K slots (tap x 8-channel slice) fit four MFMA steps
+    int64_t max_taps = 1;
+    for (int a = 0; a < 3; ++a) {
+        int64_t m = 0;
+        for (int r = 0; r < dp.ax[a].S; ++r) m = std::max<int64_t>(m, dp.ax[a].n[r]);
+        max_taps *= m;
+    }
+    if (max_taps * (dp.Cig / 8) > 4 * tiles::kGrpMaxKSteps) return false;
     if ((int64_t)dp.ktot * tiles::kGrpCog * dp.Cig * 2 > tiles::kGrpWBytes) return false;
     DevParams tmp = dp;
     return choose_grouped_tile(&tmp);
@@ -342,12 +392,11 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     // ---- tiles and workspace ------------------------------------------------
     int64_t blocks = 0;
     if (route == CONVT_ROUTE_PHASE_GEMM) {
-        choose_gemm_tile(&dp, nd);
-        const int BM = dt == CONVT_DTYPE_BF16 ? tiles::kGemmBM_bf16 : tiles::kGemmBM_f32;
-        const int BK = dt == CONVT_DTYPE_BF16 ? tiles::kGemmBK_bf16 : tiles::kGemmBK_f32;
-        dp.cog_pad = (int32_t)(ceil_div(Cog, BM) * BM);
-        dp.cig_pad = (int32_t)(ceil_div(Cig, BK) * BK);
-        dp.n_co_tiles = (int32_t)ceil_div(Cog, BM);
+        pick_gemm_cfg(&dp, dt, nd);
+        const tiles::GemmTile &t = tiles::kGemmCfg[dp.gemm_cfg];
+        dp.cog_pad = (int32_t)(ceil_div(Cog, t.bm) * t.bm);
+        dp.cig_pad = (int32_t)(ceil_div(Cig, t.bk) * t.bk);
+        dp.n_co_tiles = (int32_t)ceil_div(Cog, t.bm);
         blocks = (int64_t)dp.nt_d * dp.nt_h * dp.nt_w * dp.n_co_tiles * nph * G * B;
     } else if (route == CONVT_ROUTE_GROUPED) {
         choose_grouped_tile(&dp);

@@ -34,6 +34,17 @@ struct DevAxis {
     int32_t qn[kMaxS];   // q_count of residue r: outputs s*q + r with q < qn
 };
 
+// One stride phase, packed so that a kernel fetches it with a single 32-byte
+// scalar load: per axis, rn = residue | taps << 8 and qo = q_count (low 16
+// bits) | first input offset << 16 (signed); then the phase's tap count and
+// the index of its first tap in the reordered weights.
+constexpr int kMaxPhaseTab = 64;
+struct PhaseRec {
+    int32_t rn[3];
+    int32_t qo[3];
+    int32_t ntaps, tapbase;
+};
+
 // Everything a kernel needs, passed by value. Axis 0 is depth, 1 height,
 // 2 width; problems of rank < 3 get leading unit axes (I = O = K = S = D = 1,
 // P = 0), which leave the sums unchanged.
@@ -55,7 +66,11 @@ struct DevParams {
     int32_t out_rows;          // grouped route: output rows staged per block
     int32_t grp_w_off, grp_out_off, grp_lds_bytes;  // grouped route: LDS layout (bytes)
     int32_t grp_out_cstride;   // grouped route: output-tile channel stride (elements)
+    int32_t grp_tab_off;       // grouped route: LDS offset (bytes) of the K-slot table
+    int32_t grp_ksteps;        // grouped route: MFMA K steps per phase (1, 2 or 4)
     int32_t gemm_cfg;          // phase GEMM: index into tiles::kGemmCfg
+    int32_t ph_tab_ok;         // 1: ph[] holds every phase (nphase <= kMaxPhaseTab)
+    PhaseRec ph[kMaxPhaseTab];
 };
 
 struct Plan {
@@ -93,6 +108,9 @@ constexpr int kGrpOutStageBytes = 32768;
 constexpr int kGrpHaloBytes = 32768;
 constexpr int kGrpWBytes = 16384;      // the group's reordered weights, staged in LDS
 constexpr int kGrpMaxKSteps = 4;       // MFMA K steps (32 each) per phase
+constexpr int kGrpMinPositions = 512;  // q positions per block the tile choice aims for
+constexpr int kGrpLdsBudget = 20480;   // LDS per block, for 8 blocks per CU
+constexpr int kGrpMaxS2 = 4;           // stride of the last axis (residues kept in registers)
 // Direct route
 constexpr int kDirThreads = 256;
 constexpr int kDirSlabBytes = 32768;  // weight slab of one group in LDS (float32)

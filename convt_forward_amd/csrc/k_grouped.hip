@@ -30,16 +30,17 @@
 namespace convt {
 
 constexpr int kGrpRsrcWord3 = 0x00020000;
+
 constexpr uint32_t kGrpOutOfRange = 0x80000000u;
 
+template <int S2, int KS>
 __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_t *__restrict__ x,
                                                       const uint16_t *__restrict__ wr,
                                                       const uint16_t *__restrict__ bias,
-                                                      uint16_t *__restrict__ y, int vec_store) {
+                                                      uint16_t *__restrict__ y) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     uint16_t *xs = (uint16_t *)lds;
     uint16_t *wsl = (uint16_t *)(lds + p.grp_w_off);
-    uint16_t *os = (uint16_t *)(lds + p.grp_out_off);
 
     const int tid = threadIdx.x, lane = tid & 63;
     // uniform per wave: lets the plan tables be read with scalar loads
@@ -60,28 +61,70 @@ __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_
     const int h0 = qd + a0.umin, h1 = q0h + a1.umin, h2 = a2.umin;
 
     // 1a. input halo -> LDS [row][Cig]; positions outside the input read
-    // an out-of-range offset (zero)
-    const int hrows = p.hd * HH * HW;
+    // an out-of-range offset (zero). A wave takes whole halo rows (one
+    // 8-channel slice each); its lanes walk the row's positions.
     const uint32_t xpl_bytes = (uint32_t)p.x_plane * 2;
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(x + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane), (short)0,
         (int)((uint32_t)Cig * xpl_bytes), kGrpRsrcWord3);
-    for (int it = tid; it < hrows * noct; it += 256) {
-        const int oct = it / hrows, row = it - oct * hrows;
-        const int c2 = row % HW, c1 = (row / HW) % HH, c0 = row / (HW * HH);
-        const int i0 = h0 + c0, i1 = h1 + c1, i2 = h2 + c2;
-        const bool ok = i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I && i2 >= 0 && i2 < a2.I;
-        const uint32_t off = ok ? (uint32_t)(oct * 8) * xpl_bytes +
-                                      (uint32_t)((i0 * a1.I + i1) * a2.I + i2) * 2
-                                : kGrpOutOfRange;
-        u32x4 v;
+    {
+        // (slice, depth, row) triples are dealt to the waves in turn; a wave
+        // issues the loads of four of its rows before writing any of them
+        const int nrow = p.hd * HH, total = nrow * noct;
+        int pr = wave, oct = 0, c0 = 0, c1 = wave;
+        auto norm = [&]() __attribute__((always_inline)) {
+            while (c1 >= HH) {
+                c1 -= HH;
+                if (++c0 == p.hd) {
+                    c0 = 0;
+                    ++oct;
+                }
+            }
+        };
+        norm();
+        for (int c2b = 0; c2b < HW; c2b += 64) {
+            int spr = pr, soct = oct, sc0 = c0, sc1 = c1;
+            const int c2 = c2b + lane;
+            const int i2 = h2 + c2;
+            const bool col_ok = c2 < HW && i2 >= 0 && i2 < a2.I;
+            while (spr < total) {  // uniform
+                u32x4 v[4];
+                int dst[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(xrs, off + (2 * e) * xpl_bytes, 0, 0);
-            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(xrs, off + (2 * e + 1) * xpl_bytes, 0, 0);
-            v[e] = lo | (hi << 16);
+                for (int u = 0; u < 4; ++u) {
+                    dst[u] = -1;
+                    if (spr < total) {  // uniform
+                        const int i0 = h0 + sc0, i1 = h1 + sc1;
+                        const bool ok = col_ok && i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I;
+                        const uint32_t off =
+                            ok ? (uint32_t)(soct * 8) * xpl_bytes +
+                                     (uint32_t)((i0 * a1.I + i1) * a2.I + i2) * 2
+                               : kGrpOutOfRange;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                                xrs, off + (2 * e) * xpl_bytes, 0, 0);
+                            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                                xrs, off + (2 * e + 1) * xpl_bytes, 0, 0);
+                            v[u][e] = lo | (hi << 16);
+                        }
+                        dst[u] = ((sc0 * HH + sc1) * HW + c2) * Cig + soct * 8;
+                        spr += 4;
+                        sc1 += 4;
+                        while (sc1 >= HH) {
+                            sc1 -= HH;
+                            if (++sc0 == p.hd) {
+                                sc0 = 0;
+                                ++soct;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (dst[u] >= 0 && c2 < HW) *(u32x4 *)&xs[dst[u]] = v[u];
+            }
         }
-        *(u32x4 *)&xs[row * Cig + oct * 8] = v;
     }
     // 1b. the group's weights [tap][16][Cig] -> LDS
     {
@@ -89,108 +132,172 @@ __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_
         const u32x4 *src = (const u32x4 *)(wr + (int64_t)g * p.ktot * tiles::kGrpCog * Cig);
         for (int v = tid; v < nvec; v += 256) ((u32x4 *)wsl)[v] = src[v];
     }
+    // 1c. K-slot table: for slot (tap, 8-channel slice) of every phase, the
+    // halo element offset of the tap's window origin and the weight offset
+    int2 *tab = (int2 *)(lds + p.grp_tab_off);
+    for (int P = 0; P < p.nphase; ++P) {  // uniform
+        const PhaseDesc ph = phase_desc(p, P);
+        const int nslots = ph.ntaps * noct;
+        const int n1 = ph.n[1], n2 = ph.n[2];
+        for (int sl = tid; sl < nslots; sl += 256) {
+            const int tap = sl / noct, oct = sl - tap * noct;
+            const int j2 = tap % n2, j1 = (tap / n2) % n1, j0 = tap / (n2 * n1);
+            const int dl = (((ph.off0[0] - a0.umin + j0 * a0.ostep) * HH +
+                             (ph.off0[1] - a1.umin + j1 * a1.ostep)) * HW +
+                            (ph.off0[2] - a2.umin + j2 * a2.ostep)) * Cig + oct * 8;
+            tab[ph.tapbase * noct + sl] = make_int2(dl, (ph.tapbase + tap) * tiles::kGrpCog * Cig + oct * 8);
+        }
+    }
     __syncthreads();
 
-    // 2-3. MFMA per (phase, 16-position row segment); results into the tile
+    // 2. Per (depth residue, height residue) pair, each wave takes 16-position
+    // segments of the block's q rows. For a segment it runs the MFMA chain of
+    // every width residue r2 < S2 (kept in registers), so lane l (channel
+    // l%16, positions 4*(l/16) + i of the segment) holds the outputs
+    // ow = S2*q + r2 for four consecutive q and every r2: a contiguous run of
+    // 4*S2 outputs, stored straight from registers.
     const int l16 = lane & 15, kg4 = lane >> 4;
     const int Cog = p.Cog;
     const int co = l16;
-    const int orows = p.out_rows;
     const int O2 = a2.O;
-    const int cstride = p.grp_out_cstride;
     const int nseg = (Qw + 15) >> 4;
-    const int nmb = R * nseg;
     const float bvf = (p.has_bias && co < Cog) ? bf16_to_f32(bias[g * Cog + co]) : 0.0f;
-    uint16_t *os_co = os + co * cstride;
-    for (int P = 0; P < p.nphase; ++P) {
-        const PhaseDesc ph = phase_desc(p, P);
-        const int qn0 = a0.qn[ph.r[0]], qn1 = a1.qn[ph.r[1]], qn2 = a2.qn[ph.r[2]];
-        if (qd >= qn0) continue;  // uniform: no output of this phase in this block
-        const int nslots = ph.ntaps * noct;
-        const int nkb = (nslots + 3) >> 2;  // <= kGrpMaxKSteps (planner)
-        const int n1 = ph.n[1], n2 = ph.n[2];
-        // this lane's K slot per MFMA step: halo row delta and channel slice,
-        // plus the weight fragment (constant over the phase)
-        int dl[tiles::kGrpMaxKSteps];
-        bool sl_ok[tiles::kGrpMaxKSteps];
-        bf16x8 bw[tiles::kGrpMaxKSteps];
+    // output plane of this lane's channel; rows past the group's channels are
+    // outside the resource and dropped
+    const uint32_t ypl_bytes = (uint32_t)p.y_plane * 2;
+    const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(y + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane), (short)0,
+        (int)((uint32_t)Cog * ypl_bytes), kGrpRsrcWord3);
+    const uint32_t co_bytes = co < Cog ? (uint32_t)co * ypl_bytes : kGrpOutOfRange;
+    const bool row_pairs = (O2 & 1) == 0;  // outputs of a row start 4-byte aligned
+    constexpr int MS = S2;  // width residues kept in registers
+    for (int r0 = 0; r0 < a0.S; ++r0) {
+        for (int r1 = 0; r1 < a1.S; ++r1) {
+            // phases (r0, r1, r2 < S2): their records and this lane's K slots
+            int qn0 = 0, qn1 = 0, qn2[MS], nkb[MS], dl[MS][KS];
+            bf16x8 bw[MS][KS];
+            bool sl_ok[MS][KS];
 #pragma unroll
-        for (int kb = 0; kb < tiles::kGrpMaxKSteps; ++kb) {
-            const int slot = kb * 4 + kg4;
-            sl_ok[kb] = kb < nkb && slot < nslots;
-            const int sl = sl_ok[kb] ? slot : 0;
-            const int tap = sl / noct, oct = sl - tap * noct;
-            const int j2 = tap % n2, j1 = (tap / n2) % n1, j0 = tap / (n2 * n1);
-            dl[kb] = (((a0.off0[ph.r[0]] - a0.umin + j0 * a0.ostep) * HH +
-                       (a1.off0[ph.r[1]] - a1.umin + j1 * a1.ostep)) * HW +
-                      (a2.off0[ph.r[2]] - a2.umin + j2 * a2.ostep)) * Cig + oct * 8;
-            const u32x4 wv = *(const u32x4 *)&wsl[((ph.tapbase + tap) * tiles::kGrpCog + l16) * Cig + oct * 8];
-            bw[kb] = __builtin_bit_cast(bf16x8, sl_ok[kb] ? wv : u32x4{0u, 0u, 0u, 0u});
-        }
-        uint16_t *os_ph = os_co + ph.r[0] * orows * O2 + ph.r[1] * O2 + ph.r[2];
-        for (int mb = wave; mb < nmb; mb += 4) {
-            const int ql = mb / nseg, seg = mb - ql * nseg;  // uniform
-            if (q0h + ql >= qn1) continue;                   // uniform
-            const int qw = seg * 16 + l16;
-            const int arow = (ql * HW + qw) * Cig;
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int r2 = 0; r2 < MS; ++r2) {
+                {
+                    const PhaseDesc ph = phase_desc(p, (r0 * a1.S + r1) * S2 + r2);
+                    qn0 = ph.qn[0];
+                    qn1 = ph.qn[1];
+                    qn2[r2] = ph.qn[2];
+                    const int nslots = ph.ntaps * noct;
+                    nkb[r2] = (nslots + 3) >> 2;
 #pragma unroll
-            for (int kb = 0; kb < tiles::kGrpMaxKSteps; ++kb) {
-                if (kb < nkb) {
-                    u32x4 av = {0u, 0u, 0u, 0u};
-                    if (sl_ok[kb] && qw < Qw) av = *(const u32x4 *)&xs[arow + dl[kb]];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                  bw[kb], acc, 0, 0, 0);
+                    for (int kb = 0; kb < KS; ++kb) {
+                        const int slot = kb * 4 + kg4;
+                        sl_ok[r2][kb] = kb < nkb[r2] && slot < nslots;
+                        int2 e = make_int2(0, 0);
+                        u32x4 wv = {0u, 0u, 0u, 0u};
+                        if (sl_ok[r2][kb]) {
+                            e = tab[ph.tapbase * noct + slot];
+                            wv = *(const u32x4 *)&wsl[e.y + l16 * Cig];
+                        }
+                        dl[r2][kb] = e.x;
+                        bw[r2][kb] = __builtin_bit_cast(bf16x8, wv);
+                    }
                 }
             }
-            // D[m = 4*kg4 + i][n = l16]: positions qw0 + i of row ql, channel co
-            if (co < Cog) {
-                const int qw0 = seg * 16 + 4 * kg4;
-                uint16_t *dst = os_ph + a1.S * ql * O2 + a2.S * qw0;
+            if (qd >= qn0) continue;  // uniform: these phases have no output here
+            const int od = a0.S * qd + r0;
+            int mb = 0;
+            for (int ql = 0; ql < R; ++ql) {
+                const int qh = q0h + ql;
+                if (qh >= qn1) break;  // uniform: rows past this residue's q range
+                const uint32_t row_bytes = (uint32_t)(((int64_t)od * a1.O + a1.S * qh + r1) * O2 * 2);
+                for (int seg = 0; seg < nseg; ++seg, ++mb) {
+                    if ((mb & 3) != wave) continue;  // uniform
+                    const int qw = seg * 16 + l16;
+                    const int arow = (ql * HW + qw) * Cig;
+                    f32x4 acc[MS];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (qw0 + i < qn2) dst[a2.S * i] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i] + bvf));
+                    for (int r2 = 0; r2 < MS; ++r2) {
+                        acc[r2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        {
+#pragma unroll
+                            for (int kb = 0; kb < KS; ++kb) {
+                                if (kb < nkb[r2]) {
+                                    u32x4 av = {0u, 0u, 0u, 0u};
+                                    if (sl_ok[r2][kb] && qw < Qw)
+                                        av = *(const u32x4 *)&xs[arow + dl[r2][kb]];
+                                    acc[r2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        __builtin_bit_cast(bf16x8, av), bw[r2][kb], acc[r2], 0, 0, 0);
+                                }
+                            }
+                        }
+                    }
+                    // lane: positions q = qb + i (i < 4), outputs ow = S2*q + r2
+                    const int qb = seg * 16 + 4 * kg4;
+                    const uint32_t base = co_bytes + row_bytes + (uint32_t)(S2 * qb) * 2;
+                    bool full = true;  // every output of the run inside the row
+#pragma unroll
+                    for (int r2 = 0; r2 < MS; ++r2)
+                        full = full && (qb + 3 < qn2[r2]);
+                    if (full && row_pairs) {
+                        // 4*S2 consecutive outputs as 2*S2 dwords
+#pragma unroll
+                        for (int e2 = 0; e2 < 2 * MS; ++e2) {
+                            {
+                                const int ea = 2 * e2, eb = 2 * e2 + 1;  // output indices S2*i + r2
+                                const float va = acc[ea % S2][ea / S2] + bvf;
+                                const float vb = acc[eb % S2][eb / S2] + bvf;
+                                const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)va) |
+                                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)vb) << 16);
+                                __builtin_amdgcn_raw_buffer_store_b32(pk, ys, base + e2 * 4, 0, 0);
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int r2 = 0; r2 < MS; ++r2)
+                                if (qb + i < qn2[r2])
+                                    __builtin_amdgcn_raw_buffer_store_b16(
+                                        __builtin_bit_cast(uint16_t, (__bf16)(acc[r2][i] + bvf)), ys,
+                                        base + (S2 * i + r2) * 2, 0, 0);
+                    }
+                }
             }
         }
     }
-    __syncthreads();
+}
 
-    // 4. dense rows out
-    const int rows_co = a0.S * orows;
-    const int nrows = Cog * rows_co;
-    uint16_t *yb = y + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane;
-    if (vec_store) {
-        const int vpr = O2 >> 3;
-        for (int v = tid; v < nrows * vpr; v += 256) {
-            const int row = v / vpr, c = v - row * vpr;
-            const int cc = row / rows_co, rr = row - cc * rows_co;
-            const int r0 = rr / orows, oh_l = rr - r0 * orows;
-            const int od = a0.S * qd + r0, oh = a1.S * q0h + oh_l;
-            if (od < a0.O && oh < a1.O)
-                *(u32x4 *)&yb[(int64_t)cc * p.y_plane + ((int64_t)od * a1.O + oh) * O2 + c * 8] =
-                    *(const u32x4 *)&os[cc * cstride + rr * O2 + c * 8];
-        }
-    } else {
-        for (int e = tid; e < nrows * O2; e += 256) {
-            const int row = e / O2, c = e - row * O2;
-            const int cc = row / rows_co, rr = row - cc * rows_co;
-            const int r0 = rr / orows, oh_l = rr - r0 * orows;
-            const int od = a0.S * qd + r0, oh = a1.S * q0h + oh_l;
-            if (od < a0.O && oh < a1.O)
-                yb[(int64_t)cc * p.y_plane + ((int64_t)od * a1.O + oh) * O2 + c] =
-                    os[cc * cstride + rr * O2 + c];
-        }
+template <int S2, int KS>
+static void launch_grouped_t(const DevParams &p, const void *x, const void *wr, const void *bias,
+                             void *y, hipStream_t stream) {
+    hipLaunchKernelGGL((grouped_kernel<S2, KS>), dim3(p.n_blocks), dim3(256), (size_t)p.grp_lds_bytes,
+                       stream, p, (const uint16_t *)x, (const uint16_t *)wr, (const uint16_t *)bias,
+                       (uint16_t *)y);
+}
+
+template <int S2>
+static hipError_t launch_grouped_s(const DevParams &p, const void *x, const void *wr,
+                                   const void *bias, void *y, hipStream_t stream) {
+    switch (p.grp_ksteps) {
+        case 1: launch_grouped_t<S2, 1>(p, x, wr, bias, y, stream); break;
+        case 2: launch_grouped_t<S2, 2>(p, x, wr, bias, y, stream); break;
+        case 4: launch_grouped_t<S2, 4>(p, x, wr, bias, y, stream); break;
+        default: return hipErrorInvalidValue;
     }
+    return hipSuccess;
 }
 
 hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const void *bias, void *y,
                           hipStream_t stream) {
     const DevParams &p = pl.dp;
     if (p.n_blocks <= 0) return hipSuccess;
-    const int vec = (p.ax[2].O % 8 == 0 && ((uintptr_t)y % 16) == 0) ? 1 : 0;
-    hipLaunchKernelGGL(grouped_kernel, dim3(p.n_blocks), dim3(256), (size_t)p.grp_lds_bytes, stream,
-                       p, (const uint16_t *)x, (const uint16_t *)wr, (const uint16_t *)bias,
-                       (uint16_t *)y, vec);
+    hipError_t e;
+    switch (p.ax[2].S) {
+        case 1: e = launch_grouped_s<1>(p, x, wr, bias, y, stream); break;
+        case 2: e = launch_grouped_s<2>(p, x, wr, bias, y, stream); break;
+        case 3: e = launch_grouped_s<3>(p, x, wr, bias, y, stream); break;
+        case 4: e = launch_grouped_s<4>(p, x, wr, bias, y, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -39,13 +39,28 @@ __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__re
     const int g = bid / nci;
     const int n = ocb * ktot;
     const int co0 = co_b * ocb;
-    for (int e = threadIdx.x; e < VEC * n; e += 256) {
-        const int cil = e / n, r = e - cil * n;
-        const int ci = ci_b * VEC + cil, co = co0 + r / ktot;
-        T v = from_f32<T>(0.0f);
-        if (ci < p.Cig && co < p.Cog)
-            v = w[((int64_t)(g * p.Cig + ci) * p.Cog + co0) * ktot + r];
-        brick[cil * n + r] = v;
+    // loads are unconditional (a masked element reads the slab's first
+    // element and is then zeroed) and issued in batches of 8 before their
+    // LDS stores, so that a batch is in flight together
+    const T *wg = w + (int64_t)g * p.Cig * p.Cog * ktot;
+    const int lim = (p.Cog - co0) * ktot;  // elements of a channel row inside W
+    const int total = VEC * n;
+    for (int e0 = threadIdx.x; e0 < total; e0 += 256 * 8) {
+        T v[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + 256 * u;
+            const int cil = e / n, r = e - cil * n;
+            const int ci = ci_b * VEC + cil;
+            ok[u] = e < total && ci < p.Cig && r < lim;
+            v[u] = wg[ok[u] ? ((int64_t)ci * p.Cog + co0) * ktot + r : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + 256 * u;
+            if (e < total) brick[e] = ok[u] ? v[u] : from_f32<T>(0.0f);
+        }
     }
     __syncthreads();
     const int K1 = p.ax[1].K, K2 = p.ax[2].K;

@@ -113,9 +113,9 @@ __global__ __launch_bounds__(256) void phase_gemm_kernel(DevParams p, const T *_
     const int E1 = T1 + (ph.n[1] > 0 ? (ph.n[1] - 1) * a1.ostep : 0);
     const int E2 = T2 + (ph.n[2] > 0 ? (ph.n[2] - 1) * a2.ostep : 0);
     const int hsz = E0 * E1 * E2;
-    const int h00 = q00 + a0.off0[ph.r[0]];
-    const int h01 = q01 + a1.off0[ph.r[1]];
-    const int h02 = q02 + a2.off0[ph.r[2]];
+    const int h00 = q00 + ph.off0[0];
+    const int h01 = q01 + ph.off0[1];
+    const int h02 = q02 + ph.off0[2];
 
     f32x16 acc[MT][NT];
 #pragma unroll
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void phase_gemm_kernel(DevParams p, const T *_
         const int c2 = n % T2, c1 = (n / T2) % T1, c0 = n / (T2 * T1);
         const int qd = q00 + c0, qh = q01 + c1, qw = q02 + c2;
         yoff[nt] = kOutOfRange;
-        if (qd < a0.qn[ph.r[0]] && qh < a1.qn[ph.r[1]] && qw < a2.qn[ph.r[2]]) {
+        if (qd < ph.qn[0] && qh < ph.qn[1] && qw < ph.qn[2]) {
             const int o0 = a0.S * qd + ph.r[0], o1 = a1.S * qh + ph.r[1], o2 = a2.S * qw + ph.r[2];
             yoff[nt] = (uint32_t)((o0 * a1.O + o1) * a2.O + o2) * ES;
         }

@@ -42,27 +42,29 @@ __device__ __forceinline__ int remap_block(int bid, int n, int enable) {
     return enable ? (bid % 8) * (n / 8) + bid / 8 : bid;
 }
 
-// Phase P (lexicographic over the per-axis residues) of a plan.
+// Phase P (lexicographic over the per-axis residues) of a plan, unpacked
+// from its table record (one scalar load).
 struct PhaseDesc {
     int r[3];      // residue per axis
     int n[3];      // taps per axis
+    int qn[3];     // q count per axis
+    int off0[3];   // first (smallest) input offset per axis
     int ntaps;     // product of n
     int tapbase;   // index of the phase's first tap in the reordered weights
 };
 
 __device__ __forceinline__ PhaseDesc phase_desc(const DevParams &p, int P) {
+    const PhaseRec rec = p.ph[P];
     PhaseDesc ph;
-    const int s1 = p.ax[1].S, s2 = p.ax[2].S;
-    ph.r[2] = P % s2;
-    ph.r[1] = (P / s2) % s1;
-    ph.r[0] = P / (s1 * s2);
 #pragma unroll
-    for (int a = 0; a < 3; ++a) ph.n[a] = p.ax[a].n[ph.r[a]];
-    ph.ntaps = ph.n[0] * ph.n[1] * ph.n[2];
-    // taps of earlier phases: residues r0' < r0 contribute cum0*K1*K2, then
-    // r1' < r1 at r0 contribute n0*cum1*K2, then r2' < r2 contribute n0*n1*cum2
-    ph.tapbase = p.ax[0].cum[ph.r[0]] * p.ax[1].K * p.ax[2].K +
-                 ph.n[0] * (p.ax[1].cum[ph.r[1]] * p.ax[2].K + ph.n[1] * p.ax[2].cum[ph.r[2]]);
+    for (int a = 0; a < 3; ++a) {
+        ph.r[a] = rec.rn[a] & 0xff;
+        ph.n[a] = rec.rn[a] >> 8;
+        ph.qn[a] = rec.qo[a] & 0xffff;
+        ph.off0[a] = rec.qo[a] >> 16;  // arithmetic shift keeps the sign
+    }
+    ph.ntaps = rec.ntaps;
+    ph.tapbase = rec.tapbase;
     return ph;
 }
 

@@ -94,10 +94,50 @@ void fill_axis(DevAxis *ax, int64_t I, int64_t K, int64_t S, int64_t P, int64_t 
     }
 }
 
+// Raw buffer resources address a (batch, group) slice with 32-bit offsets
+// and treat offsets >= 2^31 as out of range; every slice must stay below.
+bool buffer_fits(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31) - (1 << 20); }
+
+bool slices_fit(const DevParams &dp, int esz) {
+    return buffer_fits((int64_t)dp.Cig * dp.x_plane * esz) &&
+           buffer_fits((int64_t)dp.Cog * dp.y_plane * esz) &&
+           buffer_fits((int64_t)dp.ktot * std::max(dp.Cog, 256) * std::max(dp.Cig, 64) * esz);
+}
+
 bool strides_fit(const DevParams &dp) {
     for (int a = 0; a < 3; ++a)
         if (dp.ax[a].S > kMaxS) return false;
-    return true;
+    return dp.ph_tab_ok != 0;
+}
+
+// Fill the packed per-phase table (phases in lexicographic residue order).
+// Leaves ph_tab_ok = 0 when a phase does not fit the packed fields.
+void fill_phase_table(DevParams *dp) {
+    dp->ph_tab_ok = 0;
+    for (int a = 0; a < 3; ++a)
+        if (dp->ax[a].S > kMaxS) return;
+    const int64_t np = (int64_t)dp->ax[0].S * dp->ax[1].S * dp->ax[2].S;
+    if (np > kMaxPhaseTab) return;
+    int P = 0, tapbase = 0;
+    for (int r0 = 0; r0 < dp->ax[0].S; ++r0)
+        for (int r1 = 0; r1 < dp->ax[1].S; ++r1)
+            for (int r2 = 0; r2 < dp->ax[2].S; ++r2, ++P) {
+                const int r[3] = {r0, r1, r2};
+                PhaseRec &pr = dp->ph[P];
+                int ntaps = 1;
+                for (int a = 0; a < 3; ++a) {
+                    const DevAxis &ax = dp->ax[a];
+                    const int n = ax.n[r[a]], qn = ax.qn[r[a]], off = ax.off0[r[a]];
+                    if (n >= (1 << 23) || qn >= (1 << 16) || off < -32768 || off > 32767) return;
+                    pr.rn[a] = r[a] | (n << 8);
+                    pr.qo[a] = (qn & 0xffff) | (int32_t)((uint32_t)(off & 0xffff) << 16);
+                    ntaps *= n;
+                }
+                pr.ntaps = ntaps;
+                pr.tapbase = tapbase;
+                tapbase += ntaps;
+            }
+    dp->ph_tab_ok = 1;
 }
 
 // ---- phase GEMM tiling ----------------------------------------------------
@@ -183,6 +223,7 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
 
 bool gemm_eligible(const DevParams &dp, int dtype, int ndim) {
     if (!strides_fit(dp) || dp.ktot > 4096) return false;
+    if (!slices_fit(dp, dtype == CONVT_DTYPE_F32 ? 4 : 2)) return false;
     if (dtype != CONVT_DTYPE_F32 && dtype != CONVT_DTYPE_BF16) return false;
     DevParams tmp = dp;
     return pick_gemm_cfg(&tmp, dtype, ndim) >= 0;
@@ -199,25 +240,20 @@ bool choose_grouped_tile(DevParams *dp) {
     const int64_t hd = 1 + (ad.umax - ad.umin);
     auto al = [](int64_t v) { return (v + 15) / 16 * 16; };
     const int64_t w_bytes = (int64_t)dp->ktot * tiles::kGrpCog * dp->Cig * 2;
+    // K-slot table: (halo offset, weight offset) per (tap, 8-channel slice)
+    const int64_t tab_bytes = (int64_t)dp->ktot * (dp->Cig / 8) * 8;
     int best = 0;
-    int64_t best_halo = 0, best_out = 0, best_cstride = 0;
+    int64_t best_halo = 0;
     for (int rows = 1; rows <= 64; rows *= 2) {
         if (rows > ah.qmax && rows > 1) break;
         const int64_t hh = rows + (ah.umax - ah.umin);
         const int64_t halo_bytes = hd * hh * hw * dp->Cig * 2;
-        // output tile [co][depth residue][rows][O_w]; the channel stride is
-        // padded by 8 elements to spread the channels over LDS banks
-        const int64_t cstride = (int64_t)ad.S * ah.S * rows * aw.O + 8;
-        const int64_t out_bytes = (int64_t)dp->Cog * cstride * 2;
-        // dynamic LDS stays within the 64 KiB a launch gets without opting in
-        if (halo_bytes > tiles::kGrpHaloBytes || out_bytes > tiles::kGrpOutStageBytes ||
-            al(halo_bytes) + al(w_bytes) + al(out_bytes) > 65536)
+        if (halo_bytes > tiles::kGrpHaloBytes ||
+            al(halo_bytes) + al(w_bytes) + al(tab_bytes) > tiles::kGrpLdsBudget)
             break;
         best = rows;
         best_halo = halo_bytes;
-        best_out = out_bytes;
-        best_cstride = cstride;
-        if ((int64_t)rows * aw.qmax >= 256) break;  // enough positions per block
+        if ((int64_t)rows * aw.qmax >= tiles::kGrpMinPositions) break;
     }
     if (!best || w_bytes > tiles::kGrpWBytes) return false;
     dp->td = 1;
@@ -230,17 +266,20 @@ bool choose_grouped_tile(DevParams *dp) {
     dp->nt_h = (int32_t)ceil_div(ah.qmax, best);
     dp->nt_w = 1;
     dp->out_rows = best * ah.S;
-    dp->grp_out_cstride = (int32_t)best_cstride;
+    dp->grp_out_cstride = 0;
     dp->grp_w_off = (int32_t)al(best_halo);
-    dp->grp_out_off = (int32_t)(al(best_halo) + al(w_bytes));
-    dp->grp_lds_bytes = (int32_t)(al(best_halo) + al(w_bytes) + al(best_out));
+    dp->grp_out_off = 0;
+    dp->grp_tab_off = (int32_t)(al(best_halo) + al(w_bytes));
+    dp->grp_lds_bytes = (int32_t)(al(best_halo) + al(w_bytes) + al(tab_bytes));
     return true;
 }
 
 bool grouped_eligible(const DevParams &dp, int dtype) {
     if (dtype != CONVT_DTYPE_BF16 || dp.ktot > 4096) return false;
+    if (!slices_fit(dp, 2)) return false;
     if (!strides_fit(dp)) return false;
     if (dp.Cig % 8 != 0 || dp.Cig > 64 || dp.Cog > tiles::kGrpCog) return false;
+    if (dp.ax[2].S > tiles::kGrpMaxS2) return false;
     // every phase's K slots (tap x 8-channel slice) fit four MFMA steps
     int64_t max_taps = 1;
     for (int a = 0; a < 3; ++a) {
@@ -340,6 +379,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
 
     DevParams &dp = pl->dp;
     for (int a = 0; a < 3; ++a) fill_axis(&dp.ax[a], I[a], K[a], S[a], P[a], D[a], O[a]);
+    fill_phase_table(&dp);
     dp.B = (int32_t)B;
     dp.Ci = (int32_t)Ci;
     dp.Co = (int32_t)Co;
@@ -400,6 +440,15 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
         blocks = (int64_t)dp.nt_d * dp.nt_h * dp.nt_w * dp.n_co_tiles * nph * G * B;
     } else if (route == CONVT_ROUTE_GROUPED) {
         choose_grouped_tile(&dp);
+        {
+            // MFMA K steps of the widest phase, rounded up to 1, 2 or 4
+            int64_t ks = 1;
+            for (int P = 0; P < dp.nphase; ++P) {
+                const int64_t need = (dp.ph[P].ntaps * (Cig / 8) + 3) / 4;
+                while (ks < need) ks *= 2;
+            }
+            dp.grp_ksteps = (int32_t)ks;
+        }
         dp.cog_pad = tiles::kGrpCog;
         dp.cig_pad = (int32_t)Cig;
         dp.n_co_tiles = 1;

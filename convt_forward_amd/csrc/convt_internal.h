@@ -69,6 +69,10 @@ struct DevParams {
     int32_t grp_tab_off;       // grouped route: LDS offset (bytes) of the K-slot table
     int32_t grp_ksteps;        // grouped route: MFMA K steps per phase (1, 2 or 4)
     int32_t gemm_cfg;          // phase GEMM: index into tiles::kGemmCfg
+    int32_t gemm_gs;           // phase GEMM: taps per pipeline stage (1..kGemmTapGroup)
+    int32_t wr_chunked;        // reordered weights: 1 = [g][tap][chunk][co][32 B], 0 = [g][tap][co][ci]
+    int32_t ktot_pad;          // taps per group in the reordered weights (phase GEMM: each
+                               // phase padded with zero taps to a multiple of gemm_gs)
     int32_t ph_tab_ok;         // 1: ph[] holds every phase (nphase <= kMaxPhaseTab)
     PhaseRec ph[kMaxPhaseTab];
 };
@@ -86,21 +90,45 @@ struct Plan {
 // Tile constants of the kernels, shared with the planner so that it sizes
 // grids and halos the way the kernels expect.
 namespace tiles {
-// Phase GEMM: tile configurations (block = 256 threads as 2 x 2 waves).
-// BM output channels x BN positions per block, BK input channels per K chunk,
-// HALO input positions of LDS halo buffer (double-buffered).
+// Phase GEMM: tile configurations (block = 512 threads, 8 waves as WGM x 8/WGM).
+// BM output channels x BN positions per block; a K chunk is 32 bytes of input
+// channels (16 bfloat16 or 8 float32). Weight tiles of gemm_gs (<= 4) taps
+// per stage stream through a ring of kGemmWRing LDS buffers of 32-byte rows;
+// the input halo of a chunk (HALO positions at most) sits in LDS as one row
+// of 4-byte elements per channel, in a ring of XB buffers.
 struct GemmTile {
-    int bm, bn, bk, halo;
+    int bm, bn, wgm, halo, xb, bf16;
 };
-constexpr int kGemmThreads = 256;
-constexpr int kGemmCfgCount = 5;
+constexpr int kGemmThreads = 512;
+constexpr int kGemmTapGroup = 4;   // taps per pipeline stage, at most (the planner picks 1..4)
+constexpr int kGemmWRing = 3;      // weight-tile buffers: two stages in flight
+constexpr int kGemmWRowBytes = 32; // weight row: one chunk of channels
+constexpr int kGemmCfgCount = 7;
 constexpr GemmTile kGemmCfg[kGemmCfgCount] = {
-    {128, 128, 32, 320},  // 0: bf16
-    {128, 256, 32, 512},  // 1: bf16
-    {256, 128, 32, 320},  // 2: bf16
-    {64, 128, 16, 320},   // 3: f32
-    {64, 256, 16, 512},   // 4: f32
+    {256, 256, 2, 320, 3, 1},  // 0: bf16, waves 128 x 64
+    {128, 512, 1, 832, 2, 1},  // 1: bf16, waves 128 x 64
+    {64, 512, 1, 832, 2, 1},   // 2: bf16, waves 64 x 64
+    {128, 256, 1, 576, 3, 1},  // 3: bf16, waves 128 x 32
+    {64, 256, 1, 1024, 3, 0},  // 4: f32, waves 64 x 32
+    {128, 256, 1, 1024, 3, 0}, // 5: f32, waves 128 x 32
+    {64, 512, 1, 1024, 3, 0},  // 6: f32, waves 64 x 64
 };
+// channels of a chunk, and the byte stride of a channel row in the halo buffer
+// (padded so that the two halves of a wave reading rows 8 (bf16) or 4 (f32)
+// apart fall on different LDS banks)
+constexpr int gemm_chunk_ch(const GemmTile &t) { return t.bf16 ? 16 : 8; }
+constexpr int gemm_xrow_bytes(const GemmTile &t) { return t.halo * 4 + (t.bf16 ? 16 : 32); }
+constexpr int gemm_lds_bytes(const GemmTile &t) {
+    return kGemmWRing * kGemmTapGroup * t.bm * kGemmWRowBytes +
+           t.xb * gemm_chunk_ch(t) * gemm_xrow_bytes(t);
+}
+static_assert(gemm_lds_bytes(kGemmCfg[0]) <= 160 * 1024, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[1]) <= 160 * 1024, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[2]) <= 160 * 1024, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[3]) <= 160 * 1024, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[4]) <= 160 * 1024, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[5]) <= 160 * 1024, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[6]) <= 160 * 1024, "LDS");
 // Grouped route
 constexpr int kGrpThreads = 256;
 constexpr int kGrpCog = 16;           // MFMA N (output channels of a group, padded)

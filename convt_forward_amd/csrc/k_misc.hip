@@ -9,7 +9,9 @@ namespace convt {
 // Weight reorder + tap flip.
 //
 // W[g*Cig + ci][co][k0][k1][k2] (forward orientation, the layout the SKaiNET
-// convTranspose2d page states) -> Wr[g][tap][co][ci], where `tap` enumerates
+// convTranspose2d page states) -> Wr[g][tap][co][ci] (grouped route) or
+// Wr[g][tap][chunk][co][32 bytes of ci] (phase GEMM, the two 16-byte halves of
+// a row swapped where bit 3 of co is set), where `tap` enumerates
 // the taps phase by phase (phases in lexicographic residue order) and, within
 // a phase, in ascending input offset (descending kk per axis: the
 // tap-reversed order). ci is contiguous so that MFMA operands are 16-byte
@@ -64,12 +66,25 @@ __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__re
     }
     __syncthreads();
     const int K1 = p.ax[1].K, K2 = p.ax[2].K;
+    const int nchunks = p.cig_pad / (2 * VEC);
+    // destination of the vector (tap t, channel co) of this block's input channels
+    auto dst_of = [&](int t, int co) -> int64_t {
+        if (p.wr_chunked) {
+            // [g][tap][chunk][co][2 vectors]; the two vectors of a row swap
+            // places where bit 3 of co is set
+            const int half = (ci_b & 1) ^ ((co >> 3) & 1);
+            return ((((int64_t)g * p.ktot_pad + t) * nchunks + (ci_b >> 1)) * p.cog_pad + co) *
+                       (2 * VEC) +
+                   half * VEC;
+        }
+        return (((int64_t)g * ktot + t) * p.cog_pad + co) * p.cig_pad + ci_b * VEC;
+    };
     for (int v = threadIdx.x; v < n; v += 256) {
         const int col = v / ktot, kk = v - col * ktot;
         const int co = co0 + col;
         if (co >= p.cog_pad) continue;
         const int k2 = kk % K2, k1 = (kk / K2) % K1, k0 = kk / (K1 * K2);
-        const int tg = tap_global(p, k0, k1, k2);
+        const int tg = p.wr_chunked ? tap_in_table(p, k0, k1, k2) : tap_global(p, k0, k1, k2);
         u32x4 out;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -79,7 +94,20 @@ __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__re
 #pragma unroll
             for (int e = 0; e < 4; ++e) out[e] = __float_as_uint((float)brick[e * n + v]);
         }
-        *(u32x4 *)&wr[(((int64_t)g * ktot + tg) * p.cog_pad + co) * p.cig_pad + ci_b * VEC] = out;
+        *(u32x4 *)&wr[dst_of(tg, co)] = out;
+    }
+    if (p.wr_chunked) {
+        // the zero taps that pad each phase to whole tap groups
+        const int gs = p.gemm_gs;
+        for (int P = 0; P < p.nphase; ++P) {
+            const int nt = p.ph[P].ntaps;
+            const int npad = (nt + gs - 1) / gs * gs - nt;
+            for (int v = threadIdx.x; v < npad * ocb; v += 256) {
+                const int co = co0 + v % ocb;
+                if (co < p.cog_pad)
+                    *(u32x4 *)&wr[dst_of(p.ph[P].tapbase + nt + v / ocb, co)] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
     }
 }
 
@@ -95,7 +123,7 @@ static int reorder_ocb(const DevParams &p) {
 hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t stream) {
     const DevParams &p = pl.dp;
     const int vec = 16 / pl.elem_bytes;
-    if (p.cig_pad % vec) return hipErrorInvalidValue;
+    if (p.cig_pad % (p.wr_chunked ? 2 * vec : vec)) return hipErrorInvalidValue;
     const int ocb = reorder_ocb(p);
     const int64_t nco = (p.cog_pad + ocb - 1) / ocb;
     const int64_t blocks = (int64_t)p.G * (p.cig_pad / vec) * nco;

@@ -13,81 +13,166 @@
 // stored directly, no column matrix), extended here to every stride through
 // the phase split its stride-phase variants name.
 //
-// Block: 256 threads (4 waves, 2 x 2), BM output channels x BN positions of
-// one phase. The BN positions form a (td, th, tw) box in q space; for each
-// chunk of BK input channels the block stages the box's input halo (the box
-// grown by the phase's tap span) in LDS, transposed to channel-contiguous
-// rows, and reuses it for every tap of the phase: tap t reads the halo rows
-// shifted by its offset. Weight tiles [BM][BK] per (tap, chunk) stream
-// through a second LDS buffer. Both are double-buffered: the halo of chunk
-// c+1 is requested when chunk c starts, the weight tile of the next stage
-// one stage ahead; one barrier per (tap, chunk) stage.
+// Block: 512 threads (8 waves as WGM x 8/WGM), BM output channels x BN
+// positions of one phase; two waves share each SIMD, so one wave's LDS and
+// barrier waits overlap the other's MFMAs. The BN positions form a
+// (td, th, tw) box in q space. K runs over chunks of 32 bytes of input
+// channels (16 bfloat16 / 8 float32) and, within a chunk, over groups of up
+// to four taps; one (chunk, tap group) pair is a pipeline stage.
 //
-// Loads and stores go through raw buffer resources, whose range check
-// returns zero for reads (and drops writes) past the resource's size: x is
-// read through a resource that ends at the last input channel of the group,
-// so a ragged channel chunk reads zeros, and positions outside the input use
-// an offset of 2^31, always out of range. Every per-lane offset is a
-// 32-bit byte offset fixed per block; the per-stage parts are uniform.
+// All operands move global -> LDS by buffer loads with an LDS destination
+// (lane l of a wave instruction writes its element at the destination base +
+// l * element slot), so no registers stage them and the only waits are the
+// explicit vector-memory counts before each barrier.
+//
+// Halo: for each chunk the block stages the box's input halo (the box grown
+// by the phase's tap span) in LDS, one row per channel of 4-byte slots over
+// the box positions (a bfloat16 load fills the low half of its slot), and
+// reuses it for every tap (tap t reads the positions shifted by its offset).
+// A wave instruction copies 64 consecutive box positions of one channel, each
+// lane gathering its own position of the channel-planar input. The halo of a
+// chunk is requested XB - 1 chunks ahead through a ring of XB buffers.
+//
+// Weights: the reordered weights hold, per (tap, chunk), the [co][32 bytes]
+// tile contiguously, its two 16-byte halves swapped on rows with bit 3 of co
+// set (an XOR swizzle that spreads a wave's A-operand reads over all LDS
+// banks). Each stage's tiles are copied 1 KiB per wave instruction, two
+// stages ahead, through a ring of three buffers.
+//
+// Loads go through raw buffer resources, whose range check returns zero for
+// reads past the resource's size: each input channel is read through a
+// resource covering its plane (empty for channels past the group's last, so
+// a ragged channel chunk reads zeros), and positions outside the input use an
+// offset of 2^31, always out of range. Every per-lane offset is a 32-bit
+// byte offset.
 //
 // MFMA: bfloat16 inputs use v_mfma_f32_32x32x16_bf16 (each lane supplies 8
-// consecutive channels of one row of each operand), float32 inputs use
-// v_mfma_f32_32x32x2_f32 (each lane reads 4 consecutive channels and feeds
-// them to 4 MFMAs; A and B pair the same channel in every lane, so the sum
-// is the full reduction). Operand A is the weight tile (rows = co), operand B
-// the gathered inputs (columns = positions), so the accumulator columns are
-// positions and each store instruction writes runs of consecutive outputs.
+// consecutive channels of one row of each operand; the input operand is
+// assembled from 8 two-byte LDS reads), float32 inputs use
+// v_mfma_f32_32x32x2_f32 (each lane reads 4 consecutive channels of its
+// weight row and feeds them to 4 MFMAs, with the input of the same channel;
+// A and B pair the same channel in every lane, so the sum is the full
+// reduction). Operand A is the weight tile (rows = co), operand B the
+// gathered inputs (columns = positions). Within a stage, the operands of tap
+// u+1 are read from LDS while the MFMAs of tap u run.
 //
 // Epilogue: acc + bias[co] in float32, one rounding to the output type
 // (v_cvt_pk_bf16_f32 rounds to nearest even), stored to
 // y[b][g*Cog+co][s*q + r]; outputs beyond the phase's q range or past Cog
 // fall outside the store resource and are dropped.
+#include <type_traits>
+
 #include "kcommon.h"
 #include "launch.h"
 
 namespace convt {
 
-template <typename T, int CFG> struct GemmCfg {
-    static constexpr int BM = tiles::kGemmCfg[CFG].bm, BN = tiles::kGemmCfg[CFG].bn;
-    static constexpr int BK = tiles::kGemmCfg[CFG].bk, HALO = tiles::kGemmCfg[CFG].halo;
-    static constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte vector
-    static_assert(BK == (sizeof(T) == 2 ? 32 : 16), "tile config does not match the element type");
-};
+namespace {
 
 // Buffer resource word 3 for gfx9-family raw buffers.
-constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
 // A byte offset that is out of range for every resource used here (each
-// covers less than 2^31 bytes), also after adding a channel offset.
+// covers less than 2^31 bytes), also after adding a tap or chunk offset.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
+                                             (int)kRsrcWord3);
 }
 
-template <typename T, int CFG>
-__global__ __launch_bounds__(256) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
+// The same resource as four scalar words, for the copy instructions below.
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = kRsrcWord3;
+    return r;
+}
+
+
+// Global -> LDS copies: every lane reads BYTES at its offset in the resource
+// and writes them at lds + lane * max(BYTES, 4). Out-of-range reads write
+// zeros. Issued as plain instructions so that the compiler neither waits for
+// them nor reorders them with the barriers; completion is awaited by the
+// counts of stage_barrier. They set M0, a register the compiler reserves and
+// does not otherwise use in this kernel.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(uint32_t lds, uint32_t voff, const u32x4 &rs) {
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     ::"s"(lds), "v"(voff), "s"(rs));
+    else if constexpr (BYTES == 4)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     ::"s"(lds), "v"(voff), "s"(rs));
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
+                     ::"s"(lds), "v"(voff), "s"(rs));
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// and its LDS operations are done, then join the block's barrier. The
+// memory clobber keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// The same with a wave-uniform count n (clamped to MAXN).
+template <int MAXN>
+__device__ __forceinline__ void stage_barrier_n(int n) {
+    if constexpr (MAXN > 0) {
+        if (n >= MAXN) {
+            stage_barrier<MAXN>();
+            return;
+        }
+        stage_barrier_n<MAXN - 1>(n);
+    } else {
+        stage_barrier<0>();
+    }
+}
+
+}  // namespace
+
+template <typename T, int CFG, int GS>
+__global__ __launch_bounds__(512) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
                                                          const T *__restrict__ wr,
                                                          const T *__restrict__ bias,
                                                          T *__restrict__ y) {
-    using C = GemmCfg<T, CFG>;
-    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, VEC = C::VEC;
+    constexpr tiles::GemmTile CT = tiles::kGemmCfg[CFG];
+    static_assert((CT.bf16 != 0) == (sizeof(T) == 2), "tile config does not match the element type");
+    static_assert(GS >= 1 && GS <= tiles::kGemmTapGroup, "taps per stage");
+    constexpr int BM = CT.bm, BN = CT.bn, WGM = CT.wgm, HALO = CT.halo, XB = CT.xb;
     constexpr int ES = (int)sizeof(T);
-    constexpr int LDK = BK + VEC;  // LDS row: BK channels + 16 bytes of padding
-    constexpr int NKV = BK / VEC;  // 16-byte vectors per row
-    constexpr int HALO = C::HALO;
-    constexpr int XITEMS = (HALO * NKV + 255) / 256;
-    constexpr int WVEC = BM * NKV / 256;
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int BK = tiles::gemm_chunk_ch(CT);      // channels per chunk (32 bytes)
+    constexpr int XROW = tiles::gemm_xrow_bytes(CT);  // halo row (one channel) bytes
+    constexpr int XBUF = BK * XROW;                   // one halo buffer
+    constexpr int WROW = tiles::kGemmWRowBytes;       // weight row bytes
+    constexpr int NW = 8, WGN = NW / WGM;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MT = WM / 32, NT = WN / 32;
-    static_assert(WVEC * 256 == BM * NKV, "weight tile must split evenly over the block");
+    constexpr int WSLOT = BM * WROW;                  // bytes of one tap's weight tile
+    constexpr int WBUF = GS * WSLOT;                  // bytes of one stage's weight tiles
+    constexpr int NPIECE = WBUF / 1024;               // 1 KiB weight copies per stage
+    constexpr int NDMA = (NPIECE + NW - 1) / NW;      // per wave, at most
+    constexpr int XCH = BK / NW;                      // halo channels per wave
+    constexpr int XJ = (HALO + 63) / 64;              // 64-position pieces of a halo row, at most
+    static_assert(MT >= 1 && NT >= 1 && WM * WGM == BM && WN * WGN == BN, "wave tiling");
+    static_assert(NPIECE * 1024 == WBUF && WSLOT % 1024 == 0, "weight tiles are whole KiB");
+    static_assert(XCH * NW == BK && BK * ES == WROW, "chunk split");
+    static_assert(XROW % 16 == 0 && XJ * 256 <= XROW, "halo rows hold whole pieces");
 
-    __shared__ __attribute__((aligned(16))) T xs[2][HALO * LDK];
-    __shared__ __attribute__((aligned(16))) T ws[2][BM * LDK];
+    __shared__ __attribute__((aligned(1024))) unsigned char ws[tiles::kGemmWRing][WBUF];
+    __shared__ __attribute__((aligned(256))) unsigned char xs[XB][XBUF];
+
+    // LDS byte addresses of the buffers, for the copy instructions
+    const uint32_t ws_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)&ws[0][0];
+    const uint32_t xs_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)&xs[0][0];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
 
     int bid = remap_block(blockIdx.x, p.n_blocks, p.xcd_remap);
     const int co_t = bid % p.n_co_tiles;
@@ -131,182 +216,201 @@ __global__ __launch_bounds__(256) void phase_gemm_kernel(DevParams p, const T *_
     const uint32_t xpl_bytes = (uint32_t)p.x_plane * ES;
 
     if (ntaps > 0) {
-        // --- per-thread halo items: (row, 16-byte channel vector) pairs ---
-        // xoff: byte offset of the item's first channel at its position,
-        // relative to the chunk's first channel; out of range outside the input.
-        const int nitems = hsz * NKV;
-        uint32_t xoff[XITEMS];
-        int lds_off[XITEMS];
+        // ---- halo copies: wave w copies channels w*XCH ... of each chunk,
+        // in pieces of 64 box positions; xsp[j] is this lane's byte offset
+        // in the channel plane for piece j, out of range outside the input ----
+        const int xj = (hsz + 63) / 64;  // pieces in use (uniform)
+        uint32_t xsp[XJ];
 #pragma unroll
-        for (int i = 0; i < XITEMS; ++i) {
-            const int it = tid + 256 * i;
-            lds_off[i] = -1;
-            xoff[i] = kOutOfRange;
-            if (it < nitems) {
-                const int kv = it / hsz, row = it - kv * hsz;
-                const int c2 = row % E2, c1 = (row / E2) % E1, c0 = row / (E2 * E1);
-                const int i0 = h00 + c0, i1 = h01 + c1, i2 = h02 + c2;
-                lds_off[i] = row * LDK + kv * VEC;
-                if (i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I && i2 >= 0 && i2 < a2.I)
-                    xoff[i] = (uint32_t)(kv * VEC) * xpl_bytes +
-                              (uint32_t)((i0 * a1.I + i1) * a2.I + i2) * ES;
-            }
+        for (int j = 0; j < XJ; ++j) {
+            const int row = j * 64 + lane;
+            const int c2 = row % E2, c1 = (row / E2) % E1, c0 = row / (E2 * E1);
+            const int i0 = h00 + c0, i1 = h01 + c1, i2 = h02 + c2;
+            xsp[j] = (row < hsz && i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I && i2 >= 0 &&
+                      i2 < a2.I)
+                         ? (uint32_t)((i0 * a1.I + i1) * a2.I + i2) * ES
+                         : kOutOfRange;
         }
         const T *xslice = x + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane;
-        u32x4 xr[XITEMS];
-        auto load_x = [&](int chunk) __attribute__((always_inline)) {
-            // resource from the chunk's first channel to the group's last one
-            const __amdgpu_buffer_rsrc_t rs =
-                make_rsrc(xslice + (int64_t)chunk * BK * p.x_plane,
-                          (uint32_t)(Cig - chunk * BK) * xpl_bytes);
+        // halo of chunk c into buffer xbuf
+        auto load_x = [&](int xbi, int c) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < XITEMS; ++i) {
-                if (i * 256 < nitems) {  // uniform: skip items no lane holds
-                    if constexpr (ES == 2) {
+            for (int h = 0; h < XCH; ++h) {
+                const int ch = wave * XCH + h;   // channel within the chunk
+                const int ci = c * BK + ch;      // channel within the group
+                const u32x4 rs = rsrc_words(xslice + (int64_t)ci * p.x_plane, ci < Cig ? xpl_bytes : 0u);
+                const uint32_t dst = xs_lds + (uint32_t)(xbi * XBUF + ch * XROW);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
-                                rs, xoff[i] + (2 * e) * xpl_bytes, 0, 0);
-                            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
-                                rs, xoff[i] + (2 * e + 1) * xpl_bytes, 0, 0);
-                            xr[i][e] = lo | (hi << 16);
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            xr[i][e] =
-                                __builtin_amdgcn_raw_buffer_load_b32(rs, xoff[i] + e * xpl_bytes, 0, 0);
-                    }
-                }
+                for (int j = 0; j < XJ; ++j)
+                    if (j < xj) copy_to_lds<ES>(dst + j * 256, xsp[j], rs);
             }
         };
-        auto store_x = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < XITEMS; ++i)
-                if (i * 256 < nitems && lds_off[i] >= 0) *(u32x4 *)&xs[buf][lds_off[i]] = xr[i];
-        };
 
-        // --- weight tiles: lanes take 16-byte vectors row by row ---
+        // ---- weight tiles: per stage GS slots of [BM][32 bytes]; wave w
+        // copies the 1 KiB pieces j*8 + w (piece q = slot q / (BM/32), rows
+        // (q % (BM/32))*32 ... +32), lane l taking 16 bytes at 16*l ----
         const uint32_t tap_bytes = (uint32_t)p.cog_pad * p.cig_pad * ES;
-        const __amdgpu_buffer_rsrc_t wrs =
-            make_rsrc(wr + (int64_t)(g * p.ktot + ph.tapbase) * p.cog_pad * p.cig_pad,
-                      (uint32_t)ntaps * tap_bytes);
-        uint32_t woff[WVEC];
-        int wlds[WVEC];
+        const uint32_t chunk_bytes = (uint32_t)p.cog_pad * WROW;
+        const int ngrp = (ntaps + GS - 1) / GS;  // tap groups; the phase is padded with zero taps
+        const u32x4 wrs =
+            rsrc_words(wr + (int64_t)(g * p.ktot_pad + ph.tapbase) * p.cog_pad * p.cig_pad,
+                       (uint32_t)(ngrp * GS) * tap_bytes);
+        const int ndma = (NPIECE - wave + NW - 1) / NW;  // pieces of this wave (uniform)
+        uint32_t wv[NDMA];
 #pragma unroll
-        for (int i = 0; i < WVEC; ++i) {
-            const int v = tid + 256 * i, m = v / NKV, kv = v % NKV;
-            woff[i] = (uint32_t)((co_t * BM + m) * p.cig_pad + kv * VEC) * ES;
-            wlds[i] = m * LDK + kv * VEC;
+        for (int j = 0; j < NDMA; ++j) {
+            const int q = j * NW + wave, u = q / (BM / 32), rb = q % (BM / 32);
+            wv[j] = (uint32_t)u * tap_bytes + (uint32_t)(co_t * BM + rb * 32) * WROW + (uint32_t)lane * 16;
         }
-        u32x4 wrg[WVEC];
-        auto load_w = [&](int t, int chunk) __attribute__((always_inline)) {
-            const uint32_t soff = (uint32_t)t * tap_bytes + (uint32_t)(chunk * BK * ES);
+        // weight tiles of tap group gi of chunk c into buffer wbuf
+        auto load_w = [&](int wbi, int gi, int c) __attribute__((always_inline)) {
+            const uint32_t base = (uint32_t)(gi * GS) * tap_bytes + (uint32_t)c * chunk_bytes;
 #pragma unroll
-            for (int i = 0; i < WVEC; ++i)
-                wrg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, woff[i], soff, 0));
-        };
-        auto store_w = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < WVEC; ++i) *(u32x4 *)&ws[buf][wlds[i]] = wrg[i];
+            for (int j = 0; j < NDMA; ++j)
+                if (j < ndma)
+                    copy_to_lds<16>(ws_lds + (uint32_t)(wbi * WBUF + (j * NW + wave) * 1024), wv[j] + base, wrs);
         };
 
-        // --- operand rows of this lane ---
-        int brow[NT];
+        // ---- operand addresses of this lane ----
+        // A: row m of the slot, 16-byte half kv = lane/32, stored at half
+        // kv ^ (bit 3 of m); 8 (bf16) or 4 (f32) channels
+        const int am = wm * WM + (lane & 31);
+        const int aoff = am * WROW + (((lane >> 5) ^ ((am >> 3) & 1)) * 16);
+        // B: the lane's position row; channels start at kv * 8 (bf16) or kv * 4 (f32)
+        constexpr int KVCH = ES == 2 ? 8 : 4;
+        int boff[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int n = wn * WN + nt * 32 + (lane & 31);
             const int c2 = n % T2, c1 = (n / T2) % T1, c0 = n / (T2 * T1);
-            brow[nt] = ((c0 * E1 + c1) * E2 + c2) * LDK + (lane >> 5) * VEC;
+            boff[nt] = ((c0 * E1 + c1) * E2 + c2) * 4 + (lane >> 5) * KVCH * XROW;
         }
-        const int arow = (wm * WM + (lane & 31)) * LDK + (lane >> 5) * VEC;
-        const int n1 = ph.n[1], n2 = ph.n[2];
-        const int dstep2 = a2.ostep * LDK, dstep1 = a1.ostep * E2 * LDK,
-                  dstep0 = a0.ostep * E1 * E2 * LDK;
+        const int n0 = ph.n[0], n1 = ph.n[1], n2 = ph.n[2];
+        const int dstep2 = a2.ostep * 4, dstep1 = a1.ostep * E2 * 4, dstep0 = a0.ostep * E1 * E2 * 4;
 
-        auto compute = [&](int xbuf, int wbuf, int delta) __attribute__((always_inline)) {
-            const T *xsb = xs[xbuf] + delta;
-            const T *wsb = ws[wbuf] + arow;
+        using Frag = typename std::conditional<ES == 2, bf16x8, f32x4>::type;
+        auto read_frags = [&](Frag (&fa)[MT], Frag (&fb)[NT], const unsigned char *wsl,
+                              const unsigned char *xsl) __attribute__((always_inline)) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                fa[mt] = __builtin_bit_cast(Frag, *(const u32x4 *)(wsl + aoff + mt * 32 * WROW));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const unsigned char *bp = xsl + boff[nt];
+                if constexpr (ES == 2) {
+                    u32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = (uint32_t)*(const uint16_t *)(bp + (2 * e) * XROW) |
+                               ((uint32_t)*(const uint16_t *)(bp + (2 * e + 1) * XROW) << 16);
+                    fb[nt] = __builtin_bit_cast(Frag, v);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) fb[nt][e] = *(const float *)(bp + e * XROW);
+                }
+            }
+        };
+        auto mfma = [&](const Frag (&fa)[MT], const Frag (&fb)[NT]) __attribute__((always_inline)) {
             if constexpr (ES == 2) {
 #pragma unroll
-                for (int ks = 0; ks < BK / 16; ++ks) {
-                    bf16x8 A[MT], Bv[NT];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        A[mt] = __builtin_bit_cast(bf16x8,
-                                                   *(const u32x4 *)&wsb[mt * 32 * LDK + ks * 16]);
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
-                        Bv[nt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)&xsb[brow[nt] + ks * 16]);
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[nt],
+                                                                              acc[mt][nt], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt)
-                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mt], Bv[nt],
-                                                                                  acc[mt][nt], 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int kq = 0; kq < BK / 8; ++kq) {
-                    f32x4 A[MT], Bv[NT];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        A[mt] = *(const f32x4 *)&wsb[mt * 32 * LDK + kq * 8];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        Bv[nt] = *(const f32x4 *)&xsb[brow[nt] + kq * 8];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                            for (int nt = 0; nt < NT; ++nt)
-                                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                    A[mt][i], Bv[nt][i], acc[mt][nt], 0, 0, 0);
-                }
+                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[mt][i], fb[nt][i],
+                                                                              acc[mt][nt], 0, 0, 0);
             }
         };
 
-        // --- pipeline over (chunk, tap) stages ---
-        load_x(0);
-        load_w(0, 0);
-        store_x(0);
-        store_w(0);
-        __syncthreads();
-        int chunk = 0, t = 0, j0 = 0, j1 = 0, j2 = 0, sb = 0;
-        for (;;) {
-            // next stage
-            int t1 = t + 1, c1 = chunk;
-            if (t1 == ntaps) {
-                t1 = 0;
-                ++c1;
+        // ---- pipeline ----
+        // Stage s = chunk * ngrp + gi computes tap group gi of the chunk from
+        // weight buffer s % 3 and halo buffer chunk % XB. At its start it
+        // requests the halo of chunk + XB - 1 (first group of a chunk only)
+        // and the weights of stage s + 2; at its end it waits for what stage
+        // s + 1 reads and joins the barrier.
+        const int nstages = nchunks * ngrp;
+        const int nx = XCH * xj;  // halo copies of one chunk per wave
+        int chunk = 0, gi = 0;      // of stage s
+        int c2n = 0, gi2 = 0;       // of stage s + 2
+        int j0 = 0, j1 = 0, j2 = 0; // next tap of the chunk, as per-axis counters
+        load_x(0, 0);
+        if (XB == 3 && nchunks > 1) load_x(1, 1);
+        load_w(0, 0, 0);
+        if (++gi2 == ngrp) {
+            gi2 = 0;
+            ++c2n;
+        }
+        if (nstages > 1) load_w(1, gi2, c2n);
+        if (++gi2 == ngrp) {
+            gi2 = 0;
+            ++c2n;
+        }
+        stage_barrier<0>();
+        int wb = 0, xb = 0;  // buffers of stage s: s % 3, chunk % XB
+        for (int s = 0; s < nstages; ++s) {
+            const bool x_issue = gi == 0 && chunk + XB - 1 < nchunks;
+            if (x_issue) {
+                const int xb2 = xb == 0 ? XB - 1 : xb - 1;  // (chunk + XB - 1) % XB
+                load_x(xb2, chunk + XB - 1);
             }
-            const bool has_next = c1 < nchunks;
-            const bool new_chunk_next = has_next && t1 == 0;
-            if (t == 0 && chunk + 1 < nchunks) load_x(chunk + 1);
-            if (has_next) load_w(t1, c1);
-            compute(chunk & 1, sb, j0 * dstep0 + j1 * dstep1 + j2 * dstep2);
-            if (has_next) store_w(sb ^ 1);
-            if (new_chunk_next) store_x(c1 & 1);
-            __syncthreads();
-            if (!has_next) break;
-            // tap counters of the next stage (taps in (j0, j1, j2) order)
-            if (t1 == 0) {
-                j0 = j1 = j2 = 0;
-            } else if (++j2 == n2) {
-                j2 = 0;
-                if (++j1 == n1) {
-                    j1 = 0;
-                    ++j0;
-                }
+            const bool w_issue = s + 2 < nstages;
+            if (w_issue) load_w(wb == 0 ? 2 : wb - 1, gi2, c2n);
+            // halo shifts of the group's taps (padding taps reuse shift 0)
+            const int t0 = gi * GS;
+            int dl[GS];
+#pragma unroll
+            for (int u = 0; u < GS; ++u) {
+                const bool real = t0 + u < ntaps;
+                dl[u] = real ? j0 * dstep0 + j1 * dstep1 + j2 * dstep2 : 0;
+                // next tap in (j0, j1, j2) order; wraps to 0 after the last
+                const int k2 = j2 + 1, w2 = k2 == n2;
+                const int k1 = j1 + w2, w1 = k1 == n1;
+                const int k0 = j0 + w1, w0 = k0 == n0;
+                j2 = real ? (w2 ? 0 : k2) : j2;
+                j1 = real ? (w1 ? 0 : k1) : j1;
+                j0 = real ? (w0 ? 0 : k0) : j0;
             }
-            t = t1;
-            chunk = c1;
-            sb ^= 1;
+            const unsigned char *wsb = ws[wb];
+            const unsigned char *xsb = xs[xb];
+            Frag fa[2][MT], fb[2][NT];
+            read_frags(fa[0], fb[0], wsb, xsb + dl[0]);
+#pragma unroll
+            for (int u = 0; u < GS; ++u) {
+                if (u + 1 < GS)
+                    read_frags(fa[(u + 1) & 1], fb[(u + 1) & 1], wsb + (u + 1) * WSLOT, xsb + dl[u + 1]);
+                mfma(fa[u & 1], fb[u & 1]);
+            }
+            if (s + 1 < nstages) {
+                // what stage s + 1 reads must have landed: the weights of
+                // s + 1 (requested a stage ago) and, when s + 1 opens a chunk,
+                // its halo (requested at this stage's start if XB == 2).
+                // The weights of s + 2 and, with XB == 3, the halo requested
+                // now may still fly.
+                const int fly = (w_issue ? ndma : 0) + (XB == 3 && x_issue ? nx : 0);
+                stage_barrier_n<NDMA + XCH * XJ>(fly);
+            }
+            wb = wb == 2 ? 0 : wb + 1;
+            if (++gi == ngrp) {
+                gi = 0;
+                ++chunk;
+                xb = xb == XB - 1 ? 0 : xb + 1;
+            }
+            if (w_issue && ++gi2 == ngrp) {
+                gi2 = 0;
+                ++c2n;
+            }
         }
     }
 
-    // --- epilogue: bias, one rounding, strided stores ---
+    // ---- epilogue: bias, one rounding, strided stores ----
     // per position: byte offset in the output plane, out of range if masked
     uint32_t yoff[NT];
 #pragma unroll
@@ -315,7 +419,7 @@ __global__ __launch_bounds__(256) void phase_gemm_kernel(DevParams p, const T *_
         const int c2 = n % T2, c1 = (n / T2) % T1, c0 = n / (T2 * T1);
         const int qd = q00 + c0, qh = q01 + c1, qw = q02 + c2;
         yoff[nt] = kOutOfRange;
-        if (qd < ph.qn[0] && qh < ph.qn[1] && qw < ph.qn[2]) {
+        if (c0 < T0 && qd < ph.qn[0] && qh < ph.qn[1] && qw < ph.qn[2]) {
             const int o0 = a0.S * qd + ph.r[0], o1 = a1.S * qh + ph.r[1], o2 = a2.S * qw + ph.r[2];
             yoff[nt] = (uint32_t)((o0 * a1.O + o1) * a2.O + o2) * ES;
         }
@@ -358,26 +462,41 @@ __global__ __launch_bounds__(256) void phase_gemm_kernel(DevParams p, const T *_
     }
 }
 
-template <typename T, int CFG>
+template <typename T, int CFG, int GS>
 static void launch_cfg(const DevParams &p, const void *x, const void *wr, const void *bias, void *y,
                        hipStream_t stream) {
-    hipLaunchKernelGGL((phase_gemm_kernel<T, CFG>), dim3(p.n_blocks), dim3(256), 0, stream, p,
-                       (const T *)x, (const T *)wr, (const T *)bias, (T *)y);
+    hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS>), dim3(p.n_blocks), dim3(tiles::kGemmThreads),
+                       0, stream, p, (const T *)x, (const T *)wr, (const T *)bias, (T *)y);
+}
+
+template <typename T, int CFG>
+static hipError_t launch_gs(const DevParams &p, const void *x, const void *wr, const void *bias,
+                            void *y, hipStream_t stream) {
+    switch (p.gemm_gs) {
+        case 1: launch_cfg<T, CFG, 1>(p, x, wr, bias, y, stream); break;
+        case 2: launch_cfg<T, CFG, 2>(p, x, wr, bias, y, stream); break;
+        case 3: launch_cfg<T, CFG, 3>(p, x, wr, bias, y, stream); break;
+        case 4: launch_cfg<T, CFG, 4>(p, x, wr, bias, y, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, const void *bias,
                              void *y, hipStream_t stream) {
     const DevParams &p = pl.dp;
     if (p.n_blocks <= 0) return hipSuccess;
+    if (!p.wr_chunked) return hipErrorInvalidValue;
     switch (p.gemm_cfg) {
-        case 0: launch_cfg<uint16_t, 0>(p, x, wr, bias, y, stream); break;
-        case 1: launch_cfg<uint16_t, 1>(p, x, wr, bias, y, stream); break;
-        case 2: launch_cfg<uint16_t, 2>(p, x, wr, bias, y, stream); break;
-        case 3: launch_cfg<float, 3>(p, x, wr, bias, y, stream); break;
-        case 4: launch_cfg<float, 4>(p, x, wr, bias, y, stream); break;
+        case 0: return launch_gs<uint16_t, 0>(p, x, wr, bias, y, stream);
+        case 1: return launch_gs<uint16_t, 1>(p, x, wr, bias, y, stream);
+        case 2: return launch_gs<uint16_t, 2>(p, x, wr, bias, y, stream);
+        case 3: return launch_gs<uint16_t, 3>(p, x, wr, bias, y, stream);
+        case 4: return launch_gs<float, 4>(p, x, wr, bias, y, stream);
+        case 5: return launch_gs<float, 5>(p, x, wr, bias, y, stream);
+        case 6: return launch_gs<float, 6>(p, x, wr, bias, y, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace convt

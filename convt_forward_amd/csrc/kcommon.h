@@ -87,4 +87,21 @@ __device__ __forceinline__ int tap_global(const DevParams &p, int k0, int k1, in
     return tapbase + (j[0] * n[1] + j[1]) * n[2] + j[2];
 }
 
+// Index of tap (k0, k1, k2) when phase P's taps start at ph[P].tapbase (the
+// phase GEMM's layout, where each phase is padded to whole tap groups).
+__device__ __forceinline__ int tap_in_table(const DevParams &p, int k0, int k1, int k2) {
+    int kk[3] = {k0, k1, k2};
+    int r[3], j[3], n[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        const DevAxis &ax = p.ax[a];
+        int v = (kk[a] * ax.D - ax.P) % ax.S;
+        r[a] = v < 0 ? v + ax.S : v;
+        j[a] = (ax.kk0[r[a]] - kk[a]) / ax.kstep;
+        n[a] = ax.n[r[a]];
+    }
+    const int P = (r[0] * p.ax[1].S + r[1]) * p.ax[2].S + r[2];
+    return p.ph[P].tapbase + (j[0] * n[1] + j[1]) * n[2] + j[2];
+}
+
 }  // namespace convt

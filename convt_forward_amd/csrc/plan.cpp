@@ -101,7 +101,9 @@ bool buffer_fits(int64_t bytes) { return bytes >= 0 && bytes < ((int64_t)1 << 31
 bool slices_fit(const DevParams &dp, int esz) {
     return buffer_fits((int64_t)dp.Cig * dp.x_plane * esz) &&
            buffer_fits((int64_t)dp.Cog * dp.y_plane * esz) &&
-           buffer_fits((int64_t)dp.ktot * std::max(dp.Cog, 256) * std::max(dp.Cig, 64) * esz);
+           // the reordered weights of a group, with every padding the tile
+           // configurations and tap groups can add
+           buffer_fits(((int64_t)dp.ktot + 3 * dp.nphase) * (dp.Cog + 255) * (dp.Cig + 63) * esz);
 }
 
 bool strides_fit(const DevParams &dp) {
@@ -185,8 +187,9 @@ bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max) {
 }
 
 // Pick the tile configuration with the smallest modelled time: blocks run in
-// rounds over 256 CUs (two per CU when their LDS allows), each round costing
-// its blocks' padded MFMA work weighted by LDS operand reads per MFMA.
+// rounds of one per CU, each round costing its block's padded MFMA work,
+// scaled up where the wave tile's LDS operand reads would outrun the MFMAs
+// and by a per-MFMA overhead that small wave tiles amortise worse.
 int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
     const bool bf16 = dtype == CONVT_DTYPE_BF16;
     int best = -1;
@@ -194,20 +197,19 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
     DevParams best_dp{};
     for (int c = 0; c < tiles::kGemmCfgCount; ++c) {
         const tiles::GemmTile &t = tiles::kGemmCfg[c];
-        if ((t.bk == 32) != bf16) continue;
+        if ((t.bf16 != 0) != bf16) continue;
         DevParams tmp = *dp;
         if (!choose_gemm_tile(&tmp, ndim, t.bn, t.halo)) continue;
         const int64_t co_tiles = ceil_div(tmp.Cog, t.bm);
         const int64_t blocks =
             (int64_t)tmp.nt_d * tmp.nt_h * tmp.nt_w * co_tiles * tmp.nphase * tmp.G * tmp.B;
-        const int esz = bf16 ? 2 : 4;
-        const int64_t lds = 2LL * (t.halo + t.bm) * (t.bk + 16 / esz) * esz;
-        const int bpc = lds <= 80 * 1024 ? 2 : 1;
-        // LDS fragment reads per MFMA for the wave tile (bm/2 x bn/2)
-        const double mt = t.bm / 64.0, nt = t.bn / 64.0;
-        const double lds_factor = (mt + nt) / (mt * nt);
-        const double rounds = std::ceil((double)blocks / (256.0 * bpc));
-        const double time = rounds * bpc * (double)t.bm * t.bn * lds_factor;
+        const double mt = t.bm / t.wgm / 32.0, nt = t.bn / (8.0 / t.wgm) / 32.0;
+        // LDS read time over MFMA time per tap (float32 MFMAs take 4x the
+        // cycles per byte of operands)
+        const double lds_ratio = 0.67 * (mt + nt) / (mt * nt) * (bf16 ? 1.0 : 0.25);
+        const double eff = std::max(1.0, lds_ratio) * (1.0 + 0.25 / (mt * nt));
+        const double rounds = std::ceil((double)blocks / 256.0);
+        const double time = rounds * (double)t.bm * t.bn * eff;
         if (best < 0 || time < best_t * 0.999) {
             best = c;
             best_t = time;
@@ -434,8 +436,35 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     if (route == CONVT_ROUTE_PHASE_GEMM) {
         pick_gemm_cfg(&dp, dt, nd);
         const tiles::GemmTile &t = tiles::kGemmCfg[dp.gemm_cfg];
+        const int64_t bk = 32 / pl->elem_bytes;  // channels of a 32-byte chunk
         dp.cog_pad = (int32_t)(ceil_div(Cog, t.bm) * t.bm);
-        dp.cig_pad = (int32_t)(ceil_div(Cig, t.bk) * t.bk);
+        dp.cig_pad = (int32_t)(ceil_div(Cig, bk) * bk);
+        dp.wr_chunked = 1;
+        // Taps per pipeline stage: phases are padded with zero taps to whole
+        // groups; the model weighs the padded MFMA work against a per-stage
+        // overhead (barrier, operand refill) of about 0.3 tap.
+        {
+            int best_gs = 1;
+            double best_cost = 0;
+            for (int gs = 1; gs <= tiles::kGemmTapGroup; ++gs) {
+                int64_t padded = 0;
+                for (int P = 0; P < dp.nphase; ++P)
+                    padded += ceil_div(dp.ph[P].ntaps, gs) * gs;
+                const double cost = (double)padded * (1.0 + 0.3 / gs);
+                if (gs == 1 || cost < best_cost * 0.999) {
+                    best_gs = gs;
+                    best_cost = cost;
+                }
+            }
+            dp.gemm_gs = best_gs;
+            int64_t base = 0;
+            for (int P = 0; P < dp.nphase; ++P) {
+                dp.ph[P].tapbase = (int32_t)base;
+                base += ceil_div(dp.ph[P].ntaps, best_gs) * best_gs;
+            }
+            if (base > i31) return CONVT_ERR_UNSUPPORTED;
+            dp.ktot_pad = (int32_t)base;
+        }
         dp.n_co_tiles = (int32_t)ceil_div(Cog, t.bm);
         blocks = (int64_t)dp.nt_d * dp.nt_h * dp.nt_w * dp.n_co_tiles * nph * G * B;
     } else if (route == CONVT_ROUTE_GROUPED) {
@@ -459,7 +488,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     dp.xcd_remap = (blocks % 8 == 0) ? 1 : 0;
     if (route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_GROUPED) {
         int64_t wr;
-        if (!mul_ok((int64_t)G * ktot, (int64_t)dp.cog_pad * dp.cig_pad, lim, &wr))
+        const int64_t taps = route == CONVT_ROUTE_PHASE_GEMM ? dp.ktot_pad : ktot;
+        if (!mul_ok((int64_t)G * taps, (int64_t)dp.cog_pad * dp.cig_pad, lim, &wr))
             return CONVT_ERR_INVALID_ARGUMENT;
         pl->wr_elems = wr;
         info.workspace_bytes = wr * pl->elem_bytes;

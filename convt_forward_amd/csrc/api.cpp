@@ -59,8 +59,7 @@ convt_status convt_prepare_weights(convt_plan_t plan, const void *w, void *works
 }
 
 convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void *w,
-                                    const void *bias, void *y, const void *workspace,
-                                    void *stream) {
+                                    const void *bias, void *y, void *workspace, void *stream) {
     if (!plan) return CONVT_ERR_INVALID_ARGUMENT;
     const convt::Plan &pl = plan->plan;
     const int nd = pl.ndim;
@@ -81,9 +80,18 @@ convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void
         case CONVT_ROUTE_DIRECT:
             if (!w) return CONVT_ERR_INVALID_ARGUMENT;
             return device_status(convt::launch_direct(pl, x, w, bias, y, s));
-        case CONVT_ROUTE_PHASE_GEMM:
+        case CONVT_ROUTE_PHASE_GEMM: {
             if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
-            return device_status(convt::launch_phase_gemm(pl, x, workspace, bias, y, s));
+            const void *xin = x;
+            if (pl.xp_bytes > 0) {
+                // bfloat16: stage the channel-chunked copy of x after the weights
+                void *xp = (char *)workspace + pl.xp_offset;
+                const convt_status st = device_status(convt::launch_pack_x(pl, x, xp, s));
+                if (st != CONVT_OK) return st;
+                xin = xp;
+            }
+            return device_status(convt::launch_phase_gemm(pl, xin, workspace, bias, y, s));
+        }
         case CONVT_ROUTE_GROUPED:
             if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
             return device_status(convt::launch_grouped(pl, x, workspace, bias, y, s));

@@ -83,7 +83,9 @@ struct Plan {
     DevParams dp;
     int32_t ndim;
     int32_t route;
-    int64_t wr_elems;   // elements of the reordered weights (workspace)
+    int64_t wr_elems;   // elements of the reordered weights (workspace, from offset 0)
+    int64_t xp_offset;  // bfloat16 phase GEMM: byte offset of the channel-chunked copy of x
+    int64_t xp_bytes;   // its size (0 when not used)
     int32_t elem_bytes; // 4 (float32) or 2 (bfloat16)
 };
 
@@ -93,34 +95,40 @@ namespace tiles {
 // Phase GEMM: tile configurations (block = 512 threads, 8 waves as WGM x 8/WGM).
 // BM output channels x BN positions per block; a K chunk is 32 bytes of input
 // channels (16 bfloat16 or 8 float32). Weight tiles of gemm_gs (<= 4) taps
-// per stage stream through a ring of kGemmWRing LDS buffers of 32-byte rows;
-// the input halo of a chunk (HALO positions at most) sits in LDS as one row
-// of 4-byte elements per channel, in a ring of XB buffers.
+// per stage stream through a ring of kGemmWRing LDS buffers of 32-byte rows.
+// The input halo of a chunk (HALO positions at most) streams through a ring
+// of kGemmXRing LDS buffers: bfloat16 as one 32-byte row per position (from
+// the channel-chunked copy of x), float32 as one row of 4-byte elements per
+// channel (straight from x).
 struct GemmTile {
-    int bm, bn, wgm, halo, xb, bf16;
+    int bm, bn, wgm, halo, bf16;
 };
 constexpr int kGemmThreads = 512;
 constexpr int kGemmTapGroup = 4;   // taps per pipeline stage, at most (the planner picks 1..4)
 constexpr int kGemmWRing = 3;      // weight-tile buffers: two stages in flight
+constexpr int kGemmXRing = 3;      // halo buffers: two chunks in flight
 constexpr int kGemmWRowBytes = 32; // weight row: one chunk of channels
 constexpr int kGemmCfgCount = 7;
 constexpr GemmTile kGemmCfg[kGemmCfgCount] = {
-    {256, 256, 2, 320, 3, 1},  // 0: bf16, waves 128 x 64
-    {128, 512, 1, 832, 2, 1},  // 1: bf16, waves 128 x 64
-    {64, 512, 1, 832, 2, 1},   // 2: bf16, waves 64 x 64
-    {128, 256, 1, 576, 3, 1},  // 3: bf16, waves 128 x 32
-    {64, 256, 1, 1024, 3, 0},  // 4: f32, waves 64 x 32
-    {128, 256, 1, 1024, 3, 0}, // 5: f32, waves 128 x 32
-    {64, 512, 1, 1024, 3, 0},  // 6: f32, waves 64 x 64
+    {256, 256, 2, 640, 1},   // 0: bf16, waves 128 x 64
+    {128, 512, 1, 1152, 1},  // 1: bf16, waves 128 x 64
+    {64, 512, 1, 1152, 1},   // 2: bf16, waves 64 x 64
+    {128, 256, 1, 1152, 1},  // 3: bf16, waves 128 x 32
+    {64, 256, 1, 1024, 0},   // 4: f32, waves 64 x 32
+    {128, 256, 1, 1024, 0},  // 5: f32, waves 128 x 32
+    {64, 512, 1, 1024, 0},   // 6: f32, waves 64 x 64
 };
-// channels of a chunk, and the byte stride of a channel row in the halo buffer
-// (padded so that the two halves of a wave reading rows 8 (bf16) or 4 (f32)
-// apart fall on different LDS banks)
+// channels of a chunk
 constexpr int gemm_chunk_ch(const GemmTile &t) { return t.bf16 ? 16 : 8; }
-constexpr int gemm_xrow_bytes(const GemmTile &t) { return t.halo * 4 + (t.bf16 ? 16 : 32); }
+// float32 halo: byte stride of a channel row (padded so that the two halves
+// of a wave, reading rows 4 apart, fall on different LDS banks)
+constexpr int gemm_xrow_bytes(const GemmTile &t) { return t.halo * 4 + 32; }
+// bytes of one halo buffer
+constexpr int gemm_xbuf_bytes(const GemmTile &t) {
+    return t.bf16 ? (t.halo + 31) / 32 * 1024 : gemm_chunk_ch(t) * gemm_xrow_bytes(t);
+}
 constexpr int gemm_lds_bytes(const GemmTile &t) {
-    return kGemmWRing * kGemmTapGroup * t.bm * kGemmWRowBytes +
-           t.xb * gemm_chunk_ch(t) * gemm_xrow_bytes(t);
+    return kGemmWRing * kGemmTapGroup * t.bm * kGemmWRowBytes + kGemmXRing * gemm_xbuf_bytes(t);
 }
 static_assert(gemm_lds_bytes(kGemmCfg[0]) <= 160 * 1024, "LDS");
 static_assert(gemm_lds_bytes(kGemmCfg[1]) <= 160 * 1024, "LDS");

@@ -141,6 +141,55 @@ hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------
+// Input re-layout for the bfloat16 phase GEMM:
+//     x[b][g*Cig + ci][pos] -> xp[b][g][chunk][pos][16 channels]
+// (32 bytes per position and chunk, channels past Cig zero), so that the GEMM
+// copies a halo row of one chunk as two 16-byte pieces. One thread per
+// (b, g, chunk, position): 16 two-byte loads, coalesced over the positions
+// of a wave, and two 16-byte stores.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_x_kernel(DevParams p, const uint16_t *__restrict__ x,
+                                                      uint16_t *__restrict__ xp, int ptiles) {
+    const int nchunks = p.cig_pad / 16;
+    const int64_t plane = p.x_plane;
+    int bid = blockIdx.x;
+    const int pt = bid % ptiles;
+    bid /= ptiles;
+    const int c = bid % nchunks;
+    bid /= nchunks;
+    const int g = bid % p.G;
+    const int b = bid / p.G;
+    const int64_t pos = (int64_t)pt * 256 + threadIdx.x;
+    if (pos >= plane) return;
+    const uint16_t *src = x + ((int64_t)b * p.Ci + (int64_t)g * p.Cig + c * 16) * plane + pos;
+    const int nch = p.Cig - c * 16;  // channels of this chunk inside the group (>= 1)
+    uint32_t v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = e < nch ? src[e * plane] : 0u;
+    u32x4 o0, o1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        o0[k] = v[2 * k] | (v[2 * k + 1] << 16);
+        o1[k] = v[8 + 2 * k] | (v[9 + 2 * k] << 16);
+    }
+    u32x4 *dst = (u32x4 *)(xp + ((((int64_t)b * p.G + g) * nchunks + c) * plane + pos) * 16);
+    dst[0] = o0;
+    dst[1] = o1;
+}
+
+hipError_t launch_pack_x(const Plan &pl, const void *x, void *xp, hipStream_t stream) {
+    const DevParams &p = pl.dp;
+    if (pl.xp_bytes == 0) return hipSuccess;
+    const int64_t ptiles = ((int64_t)p.x_plane + 255) / 256;
+    const int64_t blocks = (int64_t)p.B * p.G * (p.cig_pad / 16) * ptiles;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p,
+                       (const uint16_t *)x, (uint16_t *)xp, (int)ptiles);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Fill: y = bias (or 0). Serves problems whose sums are empty (no input
 // channel or an empty input axis): every output is the bias alone.
 // ---------------------------------------------------------------------------

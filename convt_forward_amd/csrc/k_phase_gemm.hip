@@ -136,18 +136,19 @@ __device__ __forceinline__ void stage_barrier_n(int n) {
 }  // namespace
 
 template <typename T, int CFG, int GS>
-__global__ __launch_bounds__(512) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
                                                          const T *__restrict__ wr,
                                                          const T *__restrict__ bias,
                                                          T *__restrict__ y) {
     constexpr tiles::GemmTile CT = tiles::kGemmCfg[CFG];
     static_assert((CT.bf16 != 0) == (sizeof(T) == 2), "tile config does not match the element type");
     static_assert(GS >= 1 && GS <= tiles::kGemmTapGroup, "taps per stage");
-    constexpr int BM = CT.bm, BN = CT.bn, WGM = CT.wgm, HALO = CT.halo, XB = CT.xb;
+    constexpr int BM = CT.bm, BN = CT.bn, WGM = CT.wgm, HALO = CT.halo;
     constexpr int ES = (int)sizeof(T);
     constexpr int BK = tiles::gemm_chunk_ch(CT);      // channels per chunk (32 bytes)
-    constexpr int XROW = tiles::gemm_xrow_bytes(CT);  // halo row (one channel) bytes
-    constexpr int XBUF = BK * XROW;                   // one halo buffer
+    constexpr int XROW = tiles::gemm_xrow_bytes(CT);  // float32 halo: one channel row, bytes
+    constexpr int XBUF = tiles::gemm_xbuf_bytes(CT);  // one halo buffer
+    constexpr int XB = tiles::kGemmXRing;
     constexpr int WROW = tiles::kGemmWRowBytes;       // weight row bytes
     constexpr int NW = 8, WGN = NW / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -156,12 +157,16 @@ __global__ __launch_bounds__(512) void phase_gemm_kernel(DevParams p, const T *_
     constexpr int WBUF = GS * WSLOT;                  // bytes of one stage's weight tiles
     constexpr int NPIECE = WBUF / 1024;               // 1 KiB weight copies per stage
     constexpr int NDMA = (NPIECE + NW - 1) / NW;      // per wave, at most
-    constexpr int XCH = BK / NW;                      // halo channels per wave
-    constexpr int XJ = (HALO + 63) / 64;              // 64-position pieces of a halo row, at most
+    // halo copies per wave and chunk, at most: bfloat16 in 1 KiB pieces of 32
+    // rows dealt over the waves; float32 one channel per wave in pieces of 64
+    // positions
+    constexpr int XJ = ES == 2 ? ((HALO + 31) / 32 + NW - 1) / NW : (HALO + 63) / 64;
     static_assert(MT >= 1 && NT >= 1 && WM * WGM == BM && WN * WGN == BN, "wave tiling");
     static_assert(NPIECE * 1024 == WBUF && WSLOT % 1024 == 0, "weight tiles are whole KiB");
-    static_assert(XCH * NW == BK && BK * ES == WROW, "chunk split");
-    static_assert(XROW % 16 == 0 && XJ * 256 <= XROW, "halo rows hold whole pieces");
+    static_assert(BK * ES == WROW && (ES == 2 || BK == NW), "chunk split");
+    static_assert(ES == 2 ? XJ * NW * 1024 >= XBUF && XBUF % 1024 == 0
+                          : XROW % 16 == 0 && XJ * 256 <= XROW,
+                  "halo buffers hold whole pieces");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ws[tiles::kGemmWRing][WBUF];
     __shared__ __attribute__((aligned(256))) unsigned char xs[XB][XBUF];
@@ -216,33 +221,50 @@ __global__ __launch_bounds__(512) void phase_gemm_kernel(DevParams p, const T *_
     const uint32_t xpl_bytes = (uint32_t)p.x_plane * ES;
 
     if (ntaps > 0) {
-        // ---- halo copies: wave w copies channels w*XCH ... of each chunk,
-        // in pieces of 64 box positions; xsp[j] is this lane's byte offset
-        // in the channel plane for piece j, out of range outside the input ----
-        const int xj = (hsz + 63) / 64;  // pieces in use (uniform)
+        // ---- halo copies ----
+        // bfloat16: x here is the channel-chunked copy [b][g][chunk][pos][32 B];
+        // a chunk's halo is hsz rows of 32 bytes, copied in 1 KiB pieces of 32
+        // rows, piece q by wave q % 8; lane l takes row q*32 + l/2, 16-byte
+        // half l&1, which holds the row's logical half (l&1) ^ (bit 3 of the
+        // row) (the rows' XOR swizzle, undone by the operand reads).
+        // float32: wave w copies channel w of the chunk from x itself, in
+        // pieces of 64 consecutive box positions, lane l taking position
+        // 64j + l.
+        // xsp[j]: this lane's byte offset for its piece j, out of range
+        // outside the input.
+        const int xpieces = ES == 2 ? (hsz + 31) / 32 : (hsz + 63) / 64;
+        const int nxw = ES == 2 ? (xpieces - wave + NW - 1) / NW : xpieces;  // pieces of this wave
         uint32_t xsp[XJ];
 #pragma unroll
         for (int j = 0; j < XJ; ++j) {
-            const int row = j * 64 + lane;
+            const int row = ES == 2 ? (j * NW + wave) * 32 + (lane >> 1) : j * 64 + lane;
             const int c2 = row % E2, c1 = (row / E2) % E1, c0 = row / (E2 * E1);
             const int i0 = h00 + c0, i1 = h01 + c1, i2 = h02 + c2;
+            const uint32_t pos = (uint32_t)((i0 * a1.I + i1) * a2.I + i2);
+            const uint32_t off = ES == 2 ? pos * 32 + (uint32_t)(((lane & 1) ^ ((row >> 3) & 1)) * 16)
+                                         : pos * 4;
             xsp[j] = (row < hsz && i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I && i2 >= 0 &&
                       i2 < a2.I)
-                         ? (uint32_t)((i0 * a1.I + i1) * a2.I + i2) * ES
+                         ? off
                          : kOutOfRange;
         }
-        const T *xslice = x + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane;
-        // halo of chunk c into buffer xbuf
+        // halo of chunk c into buffer xbi
         auto load_x = [&](int xbi, int c) __attribute__((always_inline)) {
-#pragma unroll
-            for (int h = 0; h < XCH; ++h) {
-                const int ch = wave * XCH + h;   // channel within the chunk
-                const int ci = c * BK + ch;      // channel within the group
-                const u32x4 rs = rsrc_words(xslice + (int64_t)ci * p.x_plane, ci < Cig ? xpl_bytes : 0u);
-                const uint32_t dst = xs_lds + (uint32_t)(xbi * XBUF + ch * XROW);
+            if constexpr (ES == 2) {
+                const T *src = x + (((int64_t)b * p.G + g) * nchunks + c) * p.x_plane * 16;
+                const u32x4 rs = rsrc_words(src, xpl_bytes * 16);
 #pragma unroll
                 for (int j = 0; j < XJ; ++j)
-                    if (j < xj) copy_to_lds<ES>(dst + j * 256, xsp[j], rs);
+                    if (j < nxw)
+                        copy_to_lds<16>(xs_lds + (uint32_t)(xbi * XBUF + (j * NW + wave) * 1024), xsp[j], rs);
+            } else {
+                const int ci = c * BK + wave;  // channel within the group
+                const T *src = x + ((int64_t)b * p.Ci + (int64_t)g * Cig + ci) * p.x_plane;
+                const u32x4 rs = rsrc_words(src, ci < Cig ? xpl_bytes : 0u);
+                const uint32_t dst = xs_lds + (uint32_t)(xbi * XBUF + wave * XROW);
+#pragma unroll
+                for (int j = 0; j < XJ; ++j)
+                    if (j < nxw) copy_to_lds<4>(dst + j * 256, xsp[j], rs);
             }
         };
 
@@ -276,37 +298,38 @@ __global__ __launch_bounds__(512) void phase_gemm_kernel(DevParams p, const T *_
         // kv ^ (bit 3 of m); 8 (bf16) or 4 (f32) channels
         const int am = wm * WM + (lane & 31);
         const int aoff = am * WROW + (((lane >> 5) ^ ((am >> 3) & 1)) * 16);
-        // B: the lane's position row; channels start at kv * 8 (bf16) or kv * 4 (f32)
-        constexpr int KVCH = ES == 2 ? 8 : 4;
-        int boff[NT];
+        // B: the lane's halo row (position) for each 32-position tile
+        int brow[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int n = wn * WN + nt * 32 + (lane & 31);
             const int c2 = n % T2, c1 = (n / T2) % T1, c0 = n / (T2 * T1);
-            boff[nt] = ((c0 * E1 + c1) * E2 + c2) * 4 + (lane >> 5) * KVCH * XROW;
+            brow[nt] = (c0 * E1 + c1) * E2 + c2;
         }
+        const int kvl = lane >> 5;
         const int n0 = ph.n[0], n1 = ph.n[1], n2 = ph.n[2];
-        const int dstep2 = a2.ostep * 4, dstep1 = a1.ostep * E2 * 4, dstep0 = a0.ostep * E1 * E2 * 4;
+        // halo row shift per tap step along each axis
+        const int dstep2 = a2.ostep, dstep1 = a1.ostep * E2, dstep0 = a0.ostep * E1 * E2;
 
         using Frag = typename std::conditional<ES == 2, bf16x8, f32x4>::type;
+        // operands of one tap: weight slot wsl, halo rows shifted by drow
         auto read_frags = [&](Frag (&fa)[MT], Frag (&fb)[NT], const unsigned char *wsl,
-                              const unsigned char *xsl) __attribute__((always_inline)) {
+                              const unsigned char *xsl, int drow) __attribute__((always_inline)) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 fa[mt] = __builtin_bit_cast(Frag, *(const u32x4 *)(wsl + aoff + mt * 32 * WROW));
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const unsigned char *bp = xsl + boff[nt];
+                const int r = brow[nt] + drow;
                 if constexpr (ES == 2) {
-                    u32x4 v;
+                    // 8 channels kv*8..: 16-byte half kv of row r, swizzled
+                    fb[nt] = __builtin_bit_cast(
+                        Frag, *(const u32x4 *)(xsl + r * 32 + ((kvl ^ ((r >> 3) & 1)) << 4)));
+                } else {
+                    // channels kv*4 + e, one row per channel
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        v[e] = (uint32_t)*(const uint16_t *)(bp + (2 * e) * XROW) |
-                               ((uint32_t)*(const uint16_t *)(bp + (2 * e + 1) * XROW) << 16);
-                    fb[nt] = __builtin_bit_cast(Frag, v);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) fb[nt][e] = *(const float *)(bp + e * XROW);
+                        fb[nt][e] = *(const float *)(xsl + (kvl * 4 + e) * XROW + r * 4);
                 }
             }
         };
@@ -332,17 +355,16 @@ __global__ __launch_bounds__(512) void phase_gemm_kernel(DevParams p, const T *_
 
         // ---- pipeline ----
         // Stage s = chunk * ngrp + gi computes tap group gi of the chunk from
-        // weight buffer s % 3 and halo buffer chunk % XB. At its start it
-        // requests the halo of chunk + XB - 1 (first group of a chunk only)
-        // and the weights of stage s + 2; at its end it waits for what stage
+        // weight buffer s % 3 and halo buffer chunk % 3. At its start it
+        // requests the halo of chunk + 2 (first group of a chunk only) and
+        // the weights of stage s + 2; at its end it waits for what stage
         // s + 1 reads and joins the barrier.
         const int nstages = nchunks * ngrp;
-        const int nx = XCH * xj;  // halo copies of one chunk per wave
         int chunk = 0, gi = 0;      // of stage s
         int c2n = 0, gi2 = 0;       // of stage s + 2
         int j0 = 0, j1 = 0, j2 = 0; // next tap of the chunk, as per-axis counters
         load_x(0, 0);
-        if (XB == 3 && nchunks > 1) load_x(1, 1);
+        if (nchunks > 1) load_x(1, 1);
         load_w(0, 0, 0);
         if (++gi2 == ngrp) {
             gi2 = 0;
@@ -380,22 +402,25 @@ __global__ __launch_bounds__(512) void phase_gemm_kernel(DevParams p, const T *_
             }
             const unsigned char *wsb = ws[wb];
             const unsigned char *xsb = xs[xb];
+            // operands of tap u + 1 are read before the MFMAs of tap u issue;
+            // the scheduling barriers keep the compiler from reordering them
             Frag fa[2][MT], fb[2][NT];
-            read_frags(fa[0], fb[0], wsb, xsb + dl[0]);
+            read_frags(fa[0], fb[0], wsb, xsb, dl[0]);
 #pragma unroll
             for (int u = 0; u < GS; ++u) {
                 if (u + 1 < GS)
-                    read_frags(fa[(u + 1) & 1], fb[(u + 1) & 1], wsb + (u + 1) * WSLOT, xsb + dl[u + 1]);
+                    read_frags(fa[(u + 1) & 1], fb[(u + 1) & 1], wsb + (u + 1) * WSLOT, xsb, dl[u + 1]);
+                __builtin_amdgcn_sched_barrier(0);
                 mfma(fa[u & 1], fb[u & 1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
             if (s + 1 < nstages) {
                 // what stage s + 1 reads must have landed: the weights of
-                // s + 1 (requested a stage ago) and, when s + 1 opens a chunk,
-                // its halo (requested at this stage's start if XB == 2).
-                // The weights of s + 2 and, with XB == 3, the halo requested
-                // now may still fly.
-                const int fly = (w_issue ? ndma : 0) + (XB == 3 && x_issue ? nx : 0);
-                stage_barrier_n<NDMA + XCH * XJ>(fly);
+                // s + 1 and, when s + 1 opens chunk c + 1, its halo (both
+                // requested in earlier stages). What this stage requested
+                // (the weights of s + 2, the halo of chunk + 2) may still fly.
+                const int fly = (w_issue ? ndma : 0) + (x_issue ? nxw : 0);
+                stage_barrier_n<NDMA + XJ>(fly);
             }
             wb = wb == 2 ? 0 : wb + 1;
             if (++gi == ngrp) {

@@ -9,6 +9,7 @@
 namespace convt {
 
 hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t stream);
+hipError_t launch_pack_x(const Plan &pl, const void *x, void *xp, hipStream_t stream);
 hipError_t launch_fill(const Plan &pl, const void *bias, void *y, hipStream_t stream);
 hipError_t launch_naive(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
                         hipStream_t stream);

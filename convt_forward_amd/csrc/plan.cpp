@@ -103,7 +103,9 @@ bool slices_fit(const DevParams &dp, int esz) {
            buffer_fits((int64_t)dp.Cog * dp.y_plane * esz) &&
            // the reordered weights of a group, with every padding the tile
            // configurations and tap groups can add
-           buffer_fits(((int64_t)dp.ktot + 3 * dp.nphase) * (dp.Cog + 255) * (dp.Cig + 63) * esz);
+           buffer_fits(((int64_t)dp.ktot + 3 * dp.nphase) * (dp.Cog + 255) * (dp.Cig + 63) * esz) &&
+           // a (batch, group) slice of the channel-chunked copy of x
+           buffer_fits((int64_t)(dp.Cig + 15) * dp.x_plane * 2);
 }
 
 bool strides_fit(const DevParams &dp) {
@@ -493,6 +495,15 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
             return CONVT_ERR_INVALID_ARGUMENT;
         pl->wr_elems = wr;
         info.workspace_bytes = wr * pl->elem_bytes;
+        if (route == CONVT_ROUTE_PHASE_GEMM && dt == CONVT_DTYPE_BF16) {
+            // the channel-chunked copy of x: [B][G][chunk][position][32 bytes]
+            int64_t xp;
+            if (!mul_ok(B * G, (int64_t)dp.cig_pad / 16, lim, &t) || !mul_ok(t, xpl * 32, lim, &xp))
+                return CONVT_ERR_INVALID_ARGUMENT;
+            pl->xp_offset = (info.workspace_bytes + 255) / 256 * 256;
+            pl->xp_bytes = xp;
+            info.workspace_bytes = pl->xp_offset + xp;
+        }
     } else {
         pl->wr_elems = 0;
         info.workspace_bytes = 0;

@@ -168,11 +168,13 @@ convt_status convt_prepare_weights(convt_plan_t plan, const void *w, void *works
  * Second half of convt_forward: compute y from x, the workspace written by
  * convt_prepare_weights (for the same plan and the same W), W itself (used
  * by the routes that read it directly; may be NULL for the others) and bias.
- * Arguments as in convt_forward.
+ * The prepared weights at the start of the workspace are left unchanged; the
+ * rest of it is scratch that the call overwrites (the bfloat16 phase-GEMM
+ * route stages a channel-chunked copy of x there). Arguments as in
+ * convt_forward.
  */
 convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void *w,
-                                    const void *bias, void *y, const void *workspace,
-                                    void *stream);
+                                    const void *bias, void *y, void *workspace, void *stream);
 
 /* Free a plan. NULL is accepted and ignored. */
 void convt_destroy(convt_plan_t plan);

@@ -84,6 +84,7 @@ struct Plan {
     int32_t ndim;
     int32_t route;
     int64_t wr_elems;   // elements of the reordered weights (workspace, from offset 0)
+    int64_t tab_offset; // phase GEMM: byte offset of the per-tap halo shift table (int32 per tap)
     int64_t xp_offset;  // bfloat16 phase GEMM: byte offset of the channel-chunked copy of x
     int64_t xp_bytes;   // its size (0 when not used)
     int32_t elem_bytes; // 4 (float32) or 2 (bfloat16)
@@ -92,51 +93,59 @@ struct Plan {
 // Tile constants of the kernels, shared with the planner so that it sizes
 // grids and halos the way the kernels expect.
 namespace tiles {
-// Phase GEMM: tile configurations (block = 512 threads, 8 waves as WGM x 8/WGM).
-// BM output channels x BN positions per block; a K chunk is 32 bytes of input
-// channels (16 bfloat16 or 8 float32). Weight tiles of gemm_gs (<= 4) taps
-// per stage stream through a ring of kGemmWRing LDS buffers of 32-byte rows.
-// The input halo of a chunk (HALO positions at most) streams through a ring
-// of kGemmXRing LDS buffers: bfloat16 as one 32-byte row per position (from
-// the channel-chunked copy of x), float32 as one row of 4-byte elements per
-// channel (straight from x).
+// Phase GEMM: tile configurations (block = 256 threads, 4 waves as WGM x 4/WGM,
+// two blocks per CU). BM output channels x BN positions per block; a K chunk
+// is 32 bytes of input channels (16 bfloat16 or 8 float32). Weight tiles of
+// gs (1..4) taps per stage stream through a ring of kGemmWRing LDS buffers of
+// 32-byte rows; the input halo of a chunk streams through a ring of
+// kGemmXRing buffers that share the rest of the block's LDS budget: bfloat16
+// as one 32-byte row per position (from the channel-chunked copy of x),
+// float32 as one row of 4-byte elements per channel (straight from x).
 struct GemmTile {
-    int bm, bn, wgm, halo, bf16;
+    int bm, bn, wgm, bf16;
 };
-constexpr int kGemmThreads = 512;
+constexpr int kGemmThreads = 256;
+constexpr int kGemmWaves = 4;
+constexpr int kGemmLdsBudget = 80 * 1024;  // per block: two blocks share a CU
 constexpr int kGemmTapGroup = 4;   // taps per pipeline stage, at most (the planner picks 1..4)
 constexpr int kGemmWRing = 3;      // weight-tile buffers: two stages in flight
-constexpr int kGemmXRing = 3;      // halo buffers: two chunks in flight
+constexpr int kGemmXRing = 2;      // halo buffers: the next chunk's in flight
 constexpr int kGemmWRowBytes = 32; // weight row: one chunk of channels
-constexpr int kGemmCfgCount = 7;
+constexpr int kGemmCfgCount = 6;
 constexpr GemmTile kGemmCfg[kGemmCfgCount] = {
-    {256, 256, 2, 640, 1},   // 0: bf16, waves 128 x 64
-    {128, 512, 1, 1152, 1},  // 1: bf16, waves 128 x 64
-    {64, 512, 1, 1152, 1},   // 2: bf16, waves 64 x 64
-    {128, 256, 1, 1152, 1},  // 3: bf16, waves 128 x 32
-    {64, 256, 1, 1024, 0},   // 4: f32, waves 64 x 32
-    {128, 256, 1, 1024, 0},  // 5: f32, waves 128 x 32
-    {64, 512, 1, 1024, 0},   // 6: f32, waves 64 x 64
+    {128, 256, 1, 1},  // 0: bf16, waves 128 x 64
+    {64, 256, 1, 1},   // 1: bf16, waves 64 x 64
+    {128, 128, 1, 1},  // 2: bf16, waves 128 x 32
+    {64, 256, 1, 0},   // 3: f32, waves 64 x 64
+    {64, 128, 1, 0},   // 4: f32, waves 64 x 32
+    {128, 128, 1, 0},  // 5: f32, waves 128 x 32
 };
-// channels of a chunk
 constexpr int gemm_chunk_ch(const GemmTile &t) { return t.bf16 ? 16 : 8; }
-// float32 halo: byte stride of a channel row (padded so that the two halves
-// of a wave, reading rows 4 apart, fall on different LDS banks)
-constexpr int gemm_xrow_bytes(const GemmTile &t) { return t.halo * 4 + 32; }
-// bytes of one halo buffer
-constexpr int gemm_xbuf_bytes(const GemmTile &t) {
-    return t.bf16 ? (t.halo + 31) / 32 * 1024 : gemm_chunk_ch(t) * gemm_xrow_bytes(t);
+// one stage's weight tiles
+constexpr int gemm_wbuf_bytes(const GemmTile &t, int gs) { return gs * t.bm * kGemmWRowBytes; }
+// halo positions one buffer holds: bfloat16 in whole 1 KiB pieces of 32
+// rows, float32 in whole pieces of 64 positions per channel row
+constexpr int gemm_halo_cap(const GemmTile &t, int gs) {
+    return t.bf16 ? (kGemmLdsBudget - kGemmWRing * gemm_wbuf_bytes(t, gs)) / kGemmXRing / 1024 * 32
+                  : ((kGemmLdsBudget - kGemmWRing * gemm_wbuf_bytes(t, gs)) / kGemmXRing / 8 - 32) /
+                        4 / 64 * 64;
 }
-constexpr int gemm_lds_bytes(const GemmTile &t) {
-    return kGemmWRing * kGemmTapGroup * t.bm * kGemmWRowBytes + kGemmXRing * gemm_xbuf_bytes(t);
+// float32 halo: byte stride of a channel row (padded by 32 bytes so that the
+// two halves of a wave, reading rows 4 apart, fall on different LDS banks)
+constexpr int gemm_xrow_bytes(const GemmTile &t, int gs) { return gemm_halo_cap(t, gs) * 4 + 32; }
+// one halo buffer
+constexpr int gemm_xbuf_bytes(const GemmTile &t, int gs) {
+    return t.bf16 ? gemm_halo_cap(t, gs) / 32 * 1024 : gemm_chunk_ch(t) * gemm_xrow_bytes(t, gs);
 }
-static_assert(gemm_lds_bytes(kGemmCfg[0]) <= 160 * 1024, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[1]) <= 160 * 1024, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[2]) <= 160 * 1024, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[3]) <= 160 * 1024, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[4]) <= 160 * 1024, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[5]) <= 160 * 1024, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[6]) <= 160 * 1024, "LDS");
+constexpr int gemm_lds_bytes(const GemmTile &t, int gs) {
+    return kGemmWRing * gemm_wbuf_bytes(t, gs) + kGemmXRing * gemm_xbuf_bytes(t, gs);
+}
+static_assert(gemm_lds_bytes(kGemmCfg[0], 4) <= kGemmLdsBudget, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[2], 4) <= kGemmLdsBudget, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[3], 4) <= kGemmLdsBudget, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[5], 4) <= kGemmLdsBudget, "LDS");
+static_assert(gemm_halo_cap(kGemmCfg[0], 4) >= 256 && gemm_halo_cap(kGemmCfg[5], 4) >= 128,
+              "halo buffers hold at least the tile");
 // Grouped route
 constexpr int kGrpThreads = 256;
 constexpr int kGrpCog = 16;           // MFMA N (output channels of a group, padded)

@@ -9,9 +9,8 @@ namespace convt {
 // Weight reorder + tap flip.
 //
 // W[g*Cig + ci][co][k0][k1][k2] (forward orientation, the layout the SKaiNET
-// convTranspose2d page states) -> Wr[g][tap][co][ci] (grouped route) or
-// Wr[g][tap][chunk][co][32 bytes of ci] (phase GEMM, the two 16-byte halves of
-// a row swapped where bit 3 of co is set), where `tap` enumerates
+// convTranspose2d page states) -> Wr[g][tap][co][ci] (the grouped route's
+// layout; the phase GEMM's follows below), where `tap` enumerates
 // the taps phase by phase (phases in lexicographic residue order) and, within
 // a phase, in ascending input offset (descending kk per axis: the
 // tap-reversed order). ci is contiguous so that MFMA operands are 16-byte
@@ -66,25 +65,12 @@ __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__re
     }
     __syncthreads();
     const int K1 = p.ax[1].K, K2 = p.ax[2].K;
-    const int nchunks = p.cig_pad / (2 * VEC);
-    // destination of the vector (tap t, channel co) of this block's input channels
-    auto dst_of = [&](int t, int co) -> int64_t {
-        if (p.wr_chunked) {
-            // [g][tap][chunk][co][2 vectors]; the two vectors of a row swap
-            // places where bit 3 of co is set
-            const int half = (ci_b & 1) ^ ((co >> 3) & 1);
-            return ((((int64_t)g * p.ktot_pad + t) * nchunks + (ci_b >> 1)) * p.cog_pad + co) *
-                       (2 * VEC) +
-                   half * VEC;
-        }
-        return (((int64_t)g * ktot + t) * p.cog_pad + co) * p.cig_pad + ci_b * VEC;
-    };
     for (int v = threadIdx.x; v < n; v += 256) {
         const int col = v / ktot, kk = v - col * ktot;
         const int co = co0 + col;
         if (co >= p.cog_pad) continue;
         const int k2 = kk % K2, k1 = (kk / K2) % K1, k0 = kk / (K1 * K2);
-        const int tg = p.wr_chunked ? tap_in_table(p, k0, k1, k2) : tap_global(p, k0, k1, k2);
+        const int tg = tap_global(p, k0, k1, k2);
         u32x4 out;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -94,20 +80,7 @@ __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__re
 #pragma unroll
             for (int e = 0; e < 4; ++e) out[e] = __float_as_uint((float)brick[e * n + v]);
         }
-        *(u32x4 *)&wr[dst_of(tg, co)] = out;
-    }
-    if (p.wr_chunked) {
-        // the zero taps that pad each phase to whole tap groups
-        const int gs = p.gemm_gs;
-        for (int P = 0; P < p.nphase; ++P) {
-            const int nt = p.ph[P].ntaps;
-            const int npad = (nt + gs - 1) / gs * gs - nt;
-            for (int v = threadIdx.x; v < npad * ocb; v += 256) {
-                const int co = co0 + v % ocb;
-                if (co < p.cog_pad)
-                    *(u32x4 *)&wr[dst_of(p.ph[P].tapbase + nt + v / ocb, co)] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
+        *(u32x4 *)&wr[(((int64_t)g * ktot + tg) * p.cog_pad + co) * p.cig_pad + ci_b * VEC] = out;
     }
 }
 
@@ -120,10 +93,198 @@ static int reorder_ocb(const DevParams &p) {
     return ocb;
 }
 
+// ---------------------------------------------------------------------------
+// Weight reorder for the phase GEMM:
+//     W[g*Cig + ci][co][kk] -> Wr[g][tap][chunk][co][32 bytes of ci]
+// where tap is kk's index in the plan's tap order (phase by phase, each phase
+// padded with zero taps to whole groups of gemm_gs), chunk = ci / BK (BK =
+// 16 bfloat16 or 8 float32 channels), and the two 16-byte halves of a row
+// swap places where bit 3 of co is set. Channels past Cig and rows past Cog
+// are zero.
+//
+// A block owns one chunk, CO output channels and KT consecutive taps kk of
+// W: it reads the BK runs W[ci][co0 .. co0 + CO)[kk0 .. kk0 + KT) with
+// consecutive lanes on consecutive elements into LDS, then each lane
+// assembles 16-byte destination halves (VEC channels of one (tap, co)) and
+// stores them, consecutive lanes on consecutive co. The blocks of the first
+// tap range also zero the padding taps of their (chunk, co) tile, and block 0
+// writes the per-tap halo shift table the GEMM reads: entry tapbase(P) + t
+// holds, for tap t of phase P in (j0, j1, j2) order, the shift of its input
+// window within the phase's halo box in box positions,
+// (j0 * ostep0 * E1 + j1 * ostep1) * E2 + j2 * ostep2 (E1, E2: the box
+// extents of that phase), and 0 for the padding taps.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const T *__restrict__ w,
+                                                              T *__restrict__ wr,
+                                                              int32_t *__restrict__ tab, int CO,
+                                                              int KT, int vec_runs) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    constexpr int VEC = 16 / sizeof(T), BK = 2 * VEC;
+    const int ktot = p.ktot;
+    const int nchunks = p.cig_pad / BK;
+    const int nco = (p.cog_pad + CO - 1) / CO;
+    const int nkt = (ktot + KT - 1) / KT;
+    int bid = blockIdx.x;
+    const int kb = bid % nkt;
+    bid /= nkt;
+    const int cb = bid % nco;
+    bid /= nco;
+    const int c = bid % nchunks;
+    const int g = bid / nchunks;
+    const int co0 = cb * CO, kk0 = kb * KT;
+    const int nk = ktot - kk0 < KT ? ktot - kk0 : KT;  // taps of this block
+    T *brick = (T *)lds_raw;                              // [BK][CO][KT]
+    int *dst_tap = (int *)(lds_raw + (size_t)BK * CO * KT * sizeof(T));
+    const int K1 = p.ax[1].K, K2 = p.ax[2].K;
+    for (int k = threadIdx.x; k < nk; k += 256) {
+        const int kk = kk0 + k;
+        dst_tap[k] = tap_in_table(p, kk / (K1 * K2), (kk / K2) % K1, kk % K2);
+    }
+    // 1. load. With vec_runs (KT == ktot, whole 16-byte aligned runs, the
+    // block's channels inside or wholly outside Cog), each channel's run
+    // [co0, co0 + CO) x [0, ktot) moves as 16-byte vectors, 4 per lane in
+    // flight; otherwise elements, 8 per lane in flight.
+    const int n_in = BK * CO * nk;
+    if (vec_runs) {
+        const int nvr = CO * ktot * (int)sizeof(T) / 16;  // vectors of one channel's run
+        const int nv = BK * nvr;
+        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 4) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int vi = v0 + 256 * u;
+                const int i = vi / nvr, r = vi - i * nvr;
+                const int ci = c * BK + i;
+                v[u] = u32x4{0u, 0u, 0u, 0u};
+                if (vi < nv && ci < p.Cig && co0 < p.Cog)
+                    v[u] = ((const u32x4 *)(w + (((int64_t)g * p.Cig + ci) * p.Cog + co0) * ktot))[r];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int vi = v0 + 256 * u;
+                if (vi < nv) {
+                    const int i = vi / nvr, r = vi - i * nvr;
+                    ((u32x4 *)(brick + (size_t)i * CO * KT))[r] = v[u];
+                }
+            }
+        }
+    } else {
+        for (int e0 = threadIdx.x; e0 < n_in; e0 += 256 * 8) {
+            T v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = e0 + 256 * u;
+                const int i = e / (CO * nk), r = e - i * (CO * nk);
+                const int col = r / nk, k = r - col * nk;
+                const int ci = c * BK + i, co = co0 + col;
+                const bool ok = e < n_in && ci < p.Cig && co < p.Cog;
+                v[u] = w[ok ? (((int64_t)g * p.Cig + ci) * p.Cog + co) * ktot + kk0 + k : 0];
+                if (!ok) v[u] = from_f32<T>(0.0f);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = e0 + 256 * u;
+                if (e < n_in) {
+                    const int i = e / (CO * nk), r = e - i * (CO * nk);
+                    brick[(i * CO + r / nk) * KT + r % nk] = v[u];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // 2. destination halves: v = (k * CO + col) * 2 + half
+    const int64_t chunk_elems = (int64_t)p.cog_pad * BK;
+    T *wg = wr + (int64_t)g * p.ktot_pad * nchunks * chunk_elems + (int64_t)c * chunk_elems;
+    const int n_out = nk * CO * 2;
+    for (int v = threadIdx.x; v < n_out; v += 256) {
+        const int half = v & 1, col = (v >> 1) % CO, k = (v >> 1) / CO;
+        const int co = co0 + col;
+        if (co >= p.cog_pad) continue;
+        u32x4 out;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i0 = half * VEC + 2 * e;
+                out[e] = (uint32_t)brick[(i0 * CO + col) * KT + k] |
+                         ((uint32_t)brick[((i0 + 1) * CO + col) * KT + k] << 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = __float_as_uint((float)brick[((half * VEC + e) * CO + col) * KT + k]);
+        }
+        const int phys = half ^ ((co >> 3) & 1);
+        *(u32x4 *)&wg[(int64_t)dst_tap[k] * nchunks * chunk_elems + (int64_t)co * BK + phys * VEC] = out;
+    }
+    // 3. padding taps of this (chunk, co) tile
+    if (kb == 0) {
+        const int gs = p.gemm_gs;
+        for (int P = 0; P < p.nphase; ++P) {
+            const int nt = p.ph[P].ntaps;
+            const int npad = (nt + gs - 1) / gs * gs - nt;
+            for (int v = threadIdx.x; v < npad * CO * 2; v += 256) {
+                const int co = co0 + (v >> 1) % CO;
+                if (co < p.cog_pad)
+                    *(u32x4 *)&wg[(int64_t)(p.ph[P].tapbase + nt + (v >> 1) / CO) * nchunks * chunk_elems +
+                                  (int64_t)co * BK + (v & 1) * VEC] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    // 4. the halo shift table
+    if (blockIdx.x == 0) {
+        const int gs = p.gemm_gs;
+        for (int P = 0; P < p.nphase; ++P) {
+            const PhaseDesc ph = phase_desc(p, P);
+            const int padded = (ph.ntaps + gs - 1) / gs * gs;
+            const int n1 = ph.n[1], n2 = ph.n[2];
+            const int E1 = p.th + (n1 > 0 ? (n1 - 1) * p.ax[1].ostep : 0);
+            const int E2 = p.tw + (n2 > 0 ? (n2 - 1) * p.ax[2].ostep : 0);
+            for (int t = threadIdx.x; t < padded; t += 256) {
+                int v = 0;
+                if (t < ph.ntaps) {
+                    const int j2 = t % n2, j1 = (t / n2) % n1, j0 = t / (n1 * n2);
+                    v = (j0 * p.ax[0].ostep * E1 + j1 * p.ax[1].ostep) * E2 + j2 * p.ax[2].ostep;
+                }
+                tab[ph.tapbase + t] = v;
+            }
+        }
+    }
+}
+
 hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t stream) {
     const DevParams &p = pl.dp;
+    if (p.wr_chunked) {
+        const int bk = 32 / pl.elem_bytes;
+        if (p.cig_pad % bk) return hipErrorInvalidValue;
+        // KT taps x CO output channels per block: at most 1024 (co, tap)
+        // pairs, and CO halved while the grid has fewer than 1024 blocks
+        const int KT = p.ktot < 256 ? p.ktot : 256;
+        const int nkt = (p.ktot + KT - 1) / KT;
+        const int64_t base = (int64_t)p.G * (p.cig_pad / bk) * nkt;
+        int CO = 1024 / KT;
+        if (CO < 1) CO = 1;
+        if (CO > p.cog_pad) CO = p.cog_pad;
+        while (CO > 1 && base * ((p.cog_pad + CO - 1) / CO) < 1024) CO /= 2;
+        const int64_t blocks = base * ((p.cog_pad + CO - 1) / CO);
+        const int64_t run_bytes = (int64_t)CO * p.ktot * pl.elem_bytes;
+        const int vec_runs = KT == p.ktot && run_bytes % 16 == 0 &&
+                             ((int64_t)p.Cog * p.ktot * pl.elem_bytes) % 16 == 0 &&
+                             p.Cog % CO == 0 && (uintptr_t)w % 16 == 0;
+        if (blocks <= 0) return hipSuccess;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        const size_t lds = (size_t)32 * CO * KT + (size_t)4 * KT;
+        int32_t *tab = (int32_t *)((char *)wr + pl.tab_offset);
+        if (pl.elem_bytes == 2)
+            hipLaunchKernelGGL(reorder_chunked_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds,
+                               stream, p, (const uint16_t *)w, (uint16_t *)wr, tab, CO, KT, vec_runs);
+        else
+            hipLaunchKernelGGL(reorder_chunked_kernel<float>, dim3((unsigned)blocks), dim3(256), lds,
+                               stream, p, (const float *)w, (float *)wr, tab, CO, KT, vec_runs);
+        return hipGetLastError();
+    }
     const int vec = 16 / pl.elem_bytes;
-    if (p.cig_pad % (p.wr_chunked ? 2 * vec : vec)) return hipErrorInvalidValue;
+    if (p.cig_pad % vec) return hipErrorInvalidValue;
     const int ocb = reorder_ocb(p);
     const int64_t nco = (p.cog_pad + ocb - 1) / ocb;
     const int64_t blocks = (int64_t)p.G * (p.cig_pad / vec) * nco;

@@ -13,9 +13,10 @@
 // stored directly, no column matrix), extended here to every stride through
 // the phase split its stride-phase variants name.
 //
-// Block: 512 threads (8 waves as WGM x 8/WGM), BM output channels x BN
-// positions of one phase; two waves share each SIMD, so one wave's LDS and
-// barrier waits overlap the other's MFMAs. The BN positions form a
+// Block: 256 threads (4 waves as WGM x 4/WGM, one per SIMD), BM output
+// channels x BN positions of one phase; its LDS stays within 80 KiB, so two
+// blocks share each CU and one block's barrier and LDS waits overlap the
+// other's MFMAs. The BN positions form a
 // (td, th, tw) box in q space. K runs over chunks of 32 bytes of input
 // channels (16 bfloat16 / 8 float32) and, within a chunk, over groups of up
 // to four taps; one (chunk, tap group) pair is a pipeline stage.
@@ -31,7 +32,7 @@
 // reuses it for every tap (tap t reads the positions shifted by its offset).
 // A wave instruction copies 64 consecutive box positions of one channel, each
 // lane gathering its own position of the channel-planar input. The halo of a
-// chunk is requested XB - 1 chunks ahead through a ring of XB buffers.
+// chunk is requested one chunk ahead through two buffers.
 //
 // Weights: the reordered weights hold, per (tap, chunk), the [co][32 bytes]
 // tile contiguously, its two 16-byte halves swapped on rows with bit 3 of co
@@ -136,37 +137,41 @@ __device__ __forceinline__ void stage_barrier_n(int n) {
 }  // namespace
 
 template <typename T, int CFG, int GS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
                                                          const T *__restrict__ wr,
+                                                         const int32_t *__restrict__ tab,
                                                          const T *__restrict__ bias,
                                                          T *__restrict__ y) {
     constexpr tiles::GemmTile CT = tiles::kGemmCfg[CFG];
     static_assert((CT.bf16 != 0) == (sizeof(T) == 2), "tile config does not match the element type");
     static_assert(GS >= 1 && GS <= tiles::kGemmTapGroup, "taps per stage");
-    constexpr int BM = CT.bm, BN = CT.bn, WGM = CT.wgm, HALO = CT.halo;
+    constexpr int BM = CT.bm, BN = CT.bn, WGM = CT.wgm;
     constexpr int ES = (int)sizeof(T);
-    constexpr int BK = tiles::gemm_chunk_ch(CT);      // channels per chunk (32 bytes)
-    constexpr int XROW = tiles::gemm_xrow_bytes(CT);  // float32 halo: one channel row, bytes
-    constexpr int XBUF = tiles::gemm_xbuf_bytes(CT);  // one halo buffer
+    constexpr int BK = tiles::gemm_chunk_ch(CT);          // channels per chunk (32 bytes)
+    constexpr int HALO = tiles::gemm_halo_cap(CT, GS);    // halo positions per buffer
+    constexpr int XROW = tiles::gemm_xrow_bytes(CT, GS);  // float32 halo: one channel row, bytes
+    constexpr int XBUF = tiles::gemm_xbuf_bytes(CT, GS);  // one halo buffer
     constexpr int XB = tiles::kGemmXRing;
-    constexpr int WROW = tiles::kGemmWRowBytes;       // weight row bytes
-    constexpr int NW = 8, WGN = NW / WGM;
+    constexpr int WROW = tiles::kGemmWRowBytes;           // weight row bytes
+    constexpr int NW = tiles::kGemmWaves, WGN = NW / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MT = WM / 32, NT = WN / 32;
-    constexpr int WSLOT = BM * WROW;                  // bytes of one tap's weight tile
-    constexpr int WBUF = GS * WSLOT;                  // bytes of one stage's weight tiles
-    constexpr int NPIECE = WBUF / 1024;               // 1 KiB weight copies per stage
-    constexpr int NDMA = (NPIECE + NW - 1) / NW;      // per wave, at most
+    constexpr int WSLOT = BM * WROW;                      // bytes of one tap's weight tile
+    constexpr int WBUF = GS * WSLOT;                      // bytes of one stage's weight tiles
+    constexpr int NPIECE = WBUF / 1024;                   // 1 KiB weight copies per stage
+    constexpr int NDMA = (NPIECE + NW - 1) / NW;          // per wave, at most
     // halo copies per wave and chunk, at most: bfloat16 in 1 KiB pieces of 32
-    // rows dealt over the waves; float32 one channel per wave in pieces of 64
-    // positions
-    constexpr int XJ = ES == 2 ? ((HALO + 31) / 32 + NW - 1) / NW : (HALO + 63) / 64;
+    // rows dealt over the waves; float32 XCH channels per wave, each in
+    // pieces of 64 positions
+    constexpr int XCH = ES == 2 ? 1 : BK / NW;
+    constexpr int XJ = ES == 2 ? (HALO / 32 + NW - 1) / NW : HALO / 64;
     static_assert(MT >= 1 && NT >= 1 && WM * WGM == BM && WN * WGN == BN, "wave tiling");
     static_assert(NPIECE * 1024 == WBUF && WSLOT % 1024 == 0, "weight tiles are whole KiB");
-    static_assert(BK * ES == WROW && (ES == 2 || BK == NW), "chunk split");
-    static_assert(ES == 2 ? XJ * NW * 1024 >= XBUF && XBUF % 1024 == 0
-                          : XROW % 16 == 0 && XJ * 256 <= XROW,
+    static_assert(BK * ES == WROW && (ES == 2 || XCH * NW == BK), "chunk split");
+    static_assert(ES == 2 ? HALO % 32 == 0 && XBUF == HALO / 32 * 1024
+                          : HALO % 64 == 0 && XJ * 256 <= XROW,
                   "halo buffers hold whole pieces");
+    static_assert(tiles::kGemmWRing * WBUF + XB * XBUF <= tiles::kGemmLdsBudget, "LDS budget");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ws[tiles::kGemmWRing][WBUF];
     __shared__ __attribute__((aligned(256))) unsigned char xs[XB][XBUF];
@@ -258,13 +263,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     if (j < nxw)
                         copy_to_lds<16>(xs_lds + (uint32_t)(xbi * XBUF + (j * NW + wave) * 1024), xsp[j], rs);
             } else {
-                const int ci = c * BK + wave;  // channel within the group
-                const T *src = x + ((int64_t)b * p.Ci + (int64_t)g * Cig + ci) * p.x_plane;
-                const u32x4 rs = rsrc_words(src, ci < Cig ? xpl_bytes : 0u);
-                const uint32_t dst = xs_lds + (uint32_t)(xbi * XBUF + wave * XROW);
 #pragma unroll
-                for (int j = 0; j < XJ; ++j)
-                    if (j < nxw) copy_to_lds<4>(dst + j * 256, xsp[j], rs);
+                for (int h = 0; h < XCH; ++h) {
+                    const int ch = wave * XCH + h;  // channel within the chunk
+                    const int ci = c * BK + ch;     // channel within the group
+                    const T *src = x + ((int64_t)b * p.Ci + (int64_t)g * Cig + ci) * p.x_plane;
+                    const u32x4 rs = rsrc_words(src, ci < Cig ? xpl_bytes : 0u);
+                    const uint32_t dst = xs_lds + (uint32_t)(xbi * XBUF + ch * XROW);
+#pragma unroll
+                    for (int j = 0; j < XJ; ++j)
+                        if (j < nxw) copy_to_lds<4>(dst + j * 256, xsp[j], rs);
+                }
             }
         };
 
@@ -307,9 +316,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             brow[nt] = (c0 * E1 + c1) * E2 + c2;
         }
         const int kvl = lane >> 5;
-        const int n0 = ph.n[0], n1 = ph.n[1], n2 = ph.n[2];
-        // halo row shift per tap step along each axis
-        const int dstep2 = a2.ostep, dstep1 = a1.ostep * E2, dstep0 = a0.ostep * E1 * E2;
+        // halo shifts of the phase's taps (the zero taps that pad it to whole
+        // groups shift by 0)
+        const int32_t *ptab = tab + ph.tapbase;
 
         using Frag = typename std::conditional<ES == 2, bf16x8, f32x4>::type;
         // operands of one tap: weight slot wsl, halo rows shifted by drow
@@ -355,16 +364,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         // ---- pipeline ----
         // Stage s = chunk * ngrp + gi computes tap group gi of the chunk from
-        // weight buffer s % 3 and halo buffer chunk % 3. At its start it
-        // requests the halo of chunk + 2 (first group of a chunk only) and
-        // the weights of stage s + 2; at its end it waits for what stage
-        // s + 1 reads and joins the barrier.
+        // weight buffer s % 3 and halo buffer chunk % 2. At its start it
+        // requests the halo of chunk + 1 (first group of a chunk only), then
+        // the weights of stage s + 2; at its end it waits for everything but
+        // those weights and joins the barrier.
         const int nstages = nchunks * ngrp;
-        int chunk = 0, gi = 0;      // of stage s
-        int c2n = 0, gi2 = 0;       // of stage s + 2
-        int j0 = 0, j1 = 0, j2 = 0; // next tap of the chunk, as per-axis counters
+        int chunk = 0, gi = 0;  // of stage s
+        int c2n = 0, gi2 = 0;   // of stage s + 2
         load_x(0, 0);
-        if (nchunks > 1) load_x(1, 1);
         load_w(0, 0, 0);
         if (++gi2 == ngrp) {
             gi2 = 0;
@@ -376,32 +383,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             ++c2n;
         }
         stage_barrier<0>();
-        int wb = 0, xb = 0;  // buffers of stage s: s % 3, chunk % XB
+        int wb = 0;  // weight buffer of stage s: s % 3
         for (int s = 0; s < nstages; ++s) {
-            const bool x_issue = gi == 0 && chunk + XB - 1 < nchunks;
-            if (x_issue) {
-                const int xb2 = xb == 0 ? XB - 1 : xb - 1;  // (chunk + XB - 1) % XB
-                load_x(xb2, chunk + XB - 1);
-            }
+            if (gi == 0 && chunk + 1 < nchunks) load_x((chunk + 1) & 1, chunk + 1);
             const bool w_issue = s + 2 < nstages;
             if (w_issue) load_w(wb == 0 ? 2 : wb - 1, gi2, c2n);
-            // halo shifts of the group's taps (padding taps reuse shift 0)
-            const int t0 = gi * GS;
             int dl[GS];
 #pragma unroll
-            for (int u = 0; u < GS; ++u) {
-                const bool real = t0 + u < ntaps;
-                dl[u] = real ? j0 * dstep0 + j1 * dstep1 + j2 * dstep2 : 0;
-                // next tap in (j0, j1, j2) order; wraps to 0 after the last
-                const int k2 = j2 + 1, w2 = k2 == n2;
-                const int k1 = j1 + w2, w1 = k1 == n1;
-                const int k0 = j0 + w1, w0 = k0 == n0;
-                j2 = real ? (w2 ? 0 : k2) : j2;
-                j1 = real ? (w1 ? 0 : k1) : j1;
-                j0 = real ? (w0 ? 0 : k0) : j0;
-            }
+            for (int u = 0; u < GS; ++u) dl[u] = ptab[gi * GS + u];
             const unsigned char *wsb = ws[wb];
-            const unsigned char *xsb = xs[xb];
+            const unsigned char *xsb = xs[chunk & 1];
             // operands of tap u + 1 are read before the MFMAs of tap u issue;
             // the scheduling barriers keep the compiler from reordering them
             Frag fa[2][MT], fb[2][NT];
@@ -415,18 +406,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (s + 1 < nstages) {
-                // what stage s + 1 reads must have landed: the weights of
-                // s + 1 and, when s + 1 opens chunk c + 1, its halo (both
-                // requested in earlier stages). What this stage requested
-                // (the weights of s + 2, the halo of chunk + 2) may still fly.
-                const int fly = (w_issue ? ndma : 0) + (x_issue ? nxw : 0);
-                stage_barrier_n<NDMA + XJ>(fly);
+                // everything stage s + 1 reads was requested before this
+                // stage's weight copies, which alone may still fly
+                if (!w_issue)
+                    stage_barrier<0>();
+                else if (ndma == NDMA)
+                    stage_barrier<NDMA>();
+                else
+                    stage_barrier_n<NDMA>(ndma);
             }
             wb = wb == 2 ? 0 : wb + 1;
             if (++gi == ngrp) {
                 gi = 0;
                 ++chunk;
-                xb = xb == XB - 1 ? 0 : xb + 1;
             }
             if (w_issue && ++gi2 == ngrp) {
                 gi2 = 0;
@@ -488,20 +480,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 template <typename T, int CFG, int GS>
-static void launch_cfg(const DevParams &p, const void *x, const void *wr, const void *bias, void *y,
+static void launch_cfg(const Plan &pl, const void *x, const void *ws, const void *bias, void *y,
                        hipStream_t stream) {
+    const DevParams &p = pl.dp;
     hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS>), dim3(p.n_blocks), dim3(tiles::kGemmThreads),
-                       0, stream, p, (const T *)x, (const T *)wr, (const T *)bias, (T *)y);
+                       0, stream, p, (const T *)x, (const T *)ws,
+                       (const int32_t *)((const char *)ws + pl.tab_offset), (const T *)bias, (T *)y);
 }
 
 template <typename T, int CFG>
-static hipError_t launch_gs(const DevParams &p, const void *x, const void *wr, const void *bias,
+static hipError_t launch_gs(const Plan &pl, const void *x, const void *ws, const void *bias,
                             void *y, hipStream_t stream) {
-    switch (p.gemm_gs) {
-        case 1: launch_cfg<T, CFG, 1>(p, x, wr, bias, y, stream); break;
-        case 2: launch_cfg<T, CFG, 2>(p, x, wr, bias, y, stream); break;
-        case 3: launch_cfg<T, CFG, 3>(p, x, wr, bias, y, stream); break;
-        case 4: launch_cfg<T, CFG, 4>(p, x, wr, bias, y, stream); break;
+    switch (pl.dp.gemm_gs) {
+        case 1: launch_cfg<T, CFG, 1>(pl, x, ws, bias, y, stream); break;
+        case 2: launch_cfg<T, CFG, 2>(pl, x, ws, bias, y, stream); break;
+        case 3: launch_cfg<T, CFG, 3>(pl, x, ws, bias, y, stream); break;
+        case 4: launch_cfg<T, CFG, 4>(pl, x, ws, bias, y, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -513,13 +507,12 @@ hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, cons
     if (p.n_blocks <= 0) return hipSuccess;
     if (!p.wr_chunked) return hipErrorInvalidValue;
     switch (p.gemm_cfg) {
-        case 0: return launch_gs<uint16_t, 0>(p, x, wr, bias, y, stream);
-        case 1: return launch_gs<uint16_t, 1>(p, x, wr, bias, y, stream);
-        case 2: return launch_gs<uint16_t, 2>(p, x, wr, bias, y, stream);
-        case 3: return launch_gs<uint16_t, 3>(p, x, wr, bias, y, stream);
-        case 4: return launch_gs<float, 4>(p, x, wr, bias, y, stream);
-        case 5: return launch_gs<float, 5>(p, x, wr, bias, y, stream);
-        case 6: return launch_gs<float, 6>(p, x, wr, bias, y, stream);
+        case 0: return launch_gs<uint16_t, 0>(pl, x, wr, bias, y, stream);
+        case 1: return launch_gs<uint16_t, 1>(pl, x, wr, bias, y, stream);
+        case 2: return launch_gs<uint16_t, 2>(pl, x, wr, bias, y, stream);
+        case 3: return launch_gs<float, 3>(pl, x, wr, bias, y, stream);
+        case 4: return launch_gs<float, 4>(pl, x, wr, bias, y, stream);
+        case 5: return launch_gs<float, 5>(pl, x, wr, bias, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -15,6 +15,7 @@ hipError_t launch_naive(const Plan &pl, const void *x, const void *w, const void
                         hipStream_t stream);
 hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
                          hipStream_t stream);
+// wr: the workspace (reordered weights at offset 0, tap table at tab_offset)
 hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, const void *bias,
                              void *y, hipStream_t stream);
 hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const void *bias, void *y,

@@ -188,12 +188,31 @@ bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max) {
     return true;
 }
 
+// Taps per pipeline stage: phases are padded with zero taps to whole
+// groups; the model weighs the padded MFMA work against a per-stage overhead
+// (barrier, operand refill) of about 0.3 tap.
+int choose_gemm_gs(const DevParams &dp) {
+    int best_gs = 1;
+    double best_cost = 0;
+    for (int gs = 1; gs <= tiles::kGemmTapGroup; ++gs) {
+        int64_t padded = 0;
+        for (int P = 0; P < dp.nphase; ++P) padded += ceil_div(dp.ph[P].ntaps, gs) * gs;
+        const double cost = (double)padded * (1.0 + 0.3 / gs);
+        if (gs == 1 || cost < best_cost * 0.999) {
+            best_gs = gs;
+            best_cost = cost;
+        }
+    }
+    return best_gs;
+}
+
 // Pick the tile configuration with the smallest modelled time: blocks run in
-// rounds of one per CU, each round costing its block's padded MFMA work,
+// rounds of two per CU, each round costing its blocks' padded MFMA work,
 // scaled up where the wave tile's LDS operand reads would outrun the MFMAs
 // and by a per-MFMA overhead that small wave tiles amortise worse.
 int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
     const bool bf16 = dtype == CONVT_DTYPE_BF16;
+    const int gs = choose_gemm_gs(*dp);
     int best = -1;
     double best_t = 0;
     DevParams best_dp{};
@@ -201,16 +220,17 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
         const tiles::GemmTile &t = tiles::kGemmCfg[c];
         if ((t.bf16 != 0) != bf16) continue;
         DevParams tmp = *dp;
-        if (!choose_gemm_tile(&tmp, ndim, t.bn, t.halo)) continue;
+        if (!choose_gemm_tile(&tmp, ndim, t.bn, tiles::gemm_halo_cap(t, gs))) continue;
         const int64_t co_tiles = ceil_div(tmp.Cog, t.bm);
         const int64_t blocks =
             (int64_t)tmp.nt_d * tmp.nt_h * tmp.nt_w * co_tiles * tmp.nphase * tmp.G * tmp.B;
-        const double mt = t.bm / t.wgm / 32.0, nt = t.bn / (8.0 / t.wgm) / 32.0;
+        const int wgn = tiles::kGemmWaves / t.wgm;
+        const double mt = t.bm / t.wgm / 32.0, nt = t.bn / (double)wgn / 32.0;
         // LDS read time over MFMA time per tap (float32 MFMAs take 4x the
         // cycles per byte of operands)
         const double lds_ratio = 0.67 * (mt + nt) / (mt * nt) * (bf16 ? 1.0 : 0.25);
         const double eff = std::max(1.0, lds_ratio) * (1.0 + 0.25 / (mt * nt));
-        const double rounds = std::ceil((double)blocks / 256.0);
+        const double rounds = std::ceil((double)blocks / 512.0);
         const double time = rounds * (double)t.bm * t.bn * eff;
         if (best < 0 || time < best_t * 0.999) {
             best = c;
@@ -221,6 +241,7 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
     if (best >= 0) {
         *dp = best_dp;
         dp->gemm_cfg = best;
+        dp->gemm_gs = gs;
     }
     return best;
 }
@@ -442,27 +463,12 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
         dp.cog_pad = (int32_t)(ceil_div(Cog, t.bm) * t.bm);
         dp.cig_pad = (int32_t)(ceil_div(Cig, bk) * bk);
         dp.wr_chunked = 1;
-        // Taps per pipeline stage: phases are padded with zero taps to whole
-        // groups; the model weighs the padded MFMA work against a per-stage
-        // overhead (barrier, operand refill) of about 0.3 tap.
         {
-            int best_gs = 1;
-            double best_cost = 0;
-            for (int gs = 1; gs <= tiles::kGemmTapGroup; ++gs) {
-                int64_t padded = 0;
-                for (int P = 0; P < dp.nphase; ++P)
-                    padded += ceil_div(dp.ph[P].ntaps, gs) * gs;
-                const double cost = (double)padded * (1.0 + 0.3 / gs);
-                if (gs == 1 || cost < best_cost * 0.999) {
-                    best_gs = gs;
-                    best_cost = cost;
-                }
-            }
-            dp.gemm_gs = best_gs;
+            // each phase's taps padded to whole groups of gemm_gs
             int64_t base = 0;
             for (int P = 0; P < dp.nphase; ++P) {
                 dp.ph[P].tapbase = (int32_t)base;
-                base += ceil_div(dp.ph[P].ntaps, best_gs) * best_gs;
+                base += ceil_div(dp.ph[P].ntaps, dp.gemm_gs) * dp.gemm_gs;
             }
             if (base > i31) return CONVT_ERR_UNSUPPORTED;
             dp.ktot_pad = (int32_t)base;
@@ -495,6 +501,11 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
             return CONVT_ERR_INVALID_ARGUMENT;
         pl->wr_elems = wr;
         info.workspace_bytes = wr * pl->elem_bytes;
+        if (route == CONVT_ROUTE_PHASE_GEMM) {
+            // the per-tap halo shift table (int32 per padded tap of a group)
+            pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
+            info.workspace_bytes = pl->tab_offset + (int64_t)dp.ktot_pad * 4;
+        }
         if (route == CONVT_ROUTE_PHASE_GEMM && dt == CONVT_DTYPE_BF16) {
             // the channel-chunked copy of x: [B][G][chunk][position][32 bytes]
             int64_t xp;

@@ -41,7 +41,7 @@ PEAK_HBM_GBS = 8000.0
 
 # the source files whose change invalidates stored PMC traffic figures
 KERNEL_SOURCES = {
-    "phase_gemm": ["k_phase_gemm.hip", "kcommon.h", "plan.cpp"],
+    "phase_gemm": ["k_phase_gemm.hip", "kcommon.h", "convt_internal.h", "plan.cpp"],
     "grouped": ["k_grouped.hip", "kcommon.h", "plan.cpp"],
     "direct": ["k_misc.hip", "kcommon.h", "plan.cpp"],
     "naive": ["k_misc.hip", "kcommon.h", "plan.cpp"],
@@ -238,10 +238,15 @@ def main() -> int:
         achieved = abytes / kern_s / 1e9
         peak = PEAK_HBM_GBS
     traffic = stored_traffic(route, wl.name)
+    kernel = KERNEL_SYMBOL.get(route, route)
+    if route == "phase_gemm" and wl.dtype == "bf16":
+        # the bfloat16 GEMM reads a channel-chunked copy of x that a pack
+        # kernel writes inside the same forward call: kernel_us covers both
+        kernel = "pack_x_kernel+" + kernel
     roofline = {
         "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
         "frac": achieved / peak, "traffic": traffic,
-        "kernel": KERNEL_SYMBOL.get(route, route), "kernel_us": kern_s * 1e6,
+        "kernel": kernel, "kernel_us": kern_s * 1e6,
         "kernel_us_in_step": kern_in_step_s * 1e6,
         "algorithmic_flops": flops, "algorithmic_bytes": abytes,
         "kernel_source_sha256_16": kernel_hash(route),

@@ -94,51 +94,61 @@ struct Plan {
 // grids and halos the way the kernels expect.
 namespace tiles {
 // Phase GEMM: tile configurations (block = 256 threads, 4 waves as WGM x 4/WGM,
-// two blocks per CU). BM output channels x BN positions per block; a K chunk
-// is 32 bytes of input channels (16 bfloat16 or 8 float32). Weight tiles of
-// gs (1..4) taps per stage stream through a ring of kGemmWRing LDS buffers of
-// 32-byte rows; the input halo of a chunk streams through a ring of
-// kGemmXRing buffers that share the rest of the block's LDS budget: bfloat16
-// as one 32-byte row per position (from the channel-chunked copy of x),
-// float32 as one row of 4-byte elements per channel (straight from x).
+// two blocks per CU). BM output channels x BN positions per block. A K chunk
+// is 32 bytes of input channels (16 bfloat16 or 8 float32); a pipeline stage
+// covers SC consecutive chunks and gs (1..4) taps. The weight tiles of a
+// stage stream through a ring of kGemmWRing LDS buffers of 32-byte rows; the
+// input halo of SC chunks (HALO positions at most) streams through a ring of
+// kGemmXRing buffers that share the rest of the block's LDS budget:
+// bfloat16 as one 32-byte row per position (from the channel-chunked copy of
+// x), float32 as one row of 4-byte elements per channel (straight from x).
 struct GemmTile {
-    int bm, bn, wgm, bf16;
+    int bm, bn, wgm, bf16, sc;
 };
 constexpr int kGemmThreads = 256;
 constexpr int kGemmWaves = 4;
 constexpr int kGemmLdsBudget = 80 * 1024;  // per block: two blocks share a CU
 constexpr int kGemmTapGroup = 4;   // taps per pipeline stage, at most (the planner picks 1..4)
 constexpr int kGemmWRing = 3;      // weight-tile buffers: two stages in flight
-constexpr int kGemmXRing = 2;      // halo buffers: the next chunk's in flight
+constexpr int kGemmXRing = 3;      // halo buffers: two chunk groups in flight
 constexpr int kGemmWRowBytes = 32; // weight row: one chunk of channels
 constexpr int kGemmCfgCount = 6;
 constexpr GemmTile kGemmCfg[kGemmCfgCount] = {
-    {128, 256, 1, 1},  // 0: bf16, waves 128 x 64
-    {64, 256, 1, 1},   // 1: bf16, waves 64 x 64
-    {128, 128, 1, 1},  // 2: bf16, waves 128 x 32
-    {64, 256, 1, 0},   // 3: f32, waves 64 x 64
-    {64, 128, 1, 0},   // 4: f32, waves 64 x 32
-    {128, 128, 1, 0},  // 5: f32, waves 128 x 32
+    {128, 256, 1, 1, 1},  // 0: bf16, waves 128 x 64
+    {64, 256, 1, 1, 1},   // 1: bf16, waves 64 x 64
+    {128, 128, 1, 1, 1},  // 2: bf16, waves 128 x 32
+    {64, 256, 1, 0, 1},   // 3: f32, waves 64 x 64
+    {64, 128, 1, 0, 2},   // 4: f32, waves 64 x 32, two chunks per stage
+    {128, 128, 1, 0, 1},  // 5: f32, waves 128 x 32
 };
 constexpr int gemm_chunk_ch(const GemmTile &t) { return t.bf16 ? 16 : 8; }
 // one stage's weight tiles
-constexpr int gemm_wbuf_bytes(const GemmTile &t, int gs) { return gs * t.bm * kGemmWRowBytes; }
-// halo positions one buffer holds: bfloat16 in whole 1 KiB pieces of 32
-// rows, float32 in whole pieces of 64 positions per channel row
+constexpr int gemm_wbuf_bytes(const GemmTile &t, int gs) {
+    return t.sc * gs * t.bm * kGemmWRowBytes;
+}
+// bytes available to the halo of one chunk in one ring slot
+constexpr int gemm_xsub_avail(const GemmTile &t, int gs) {
+    return (kGemmLdsBudget - kGemmWRing * gemm_wbuf_bytes(t, gs)) / kGemmXRing / t.sc;
+}
+// halo positions one chunk's buffer holds: bfloat16 in whole 1 KiB pieces of
+// 32 rows, float32 in whole pieces of 64 positions per channel row
 constexpr int gemm_halo_cap(const GemmTile &t, int gs) {
-    return t.bf16 ? (kGemmLdsBudget - kGemmWRing * gemm_wbuf_bytes(t, gs)) / kGemmXRing / 1024 * 32
-                  : ((kGemmLdsBudget - kGemmWRing * gemm_wbuf_bytes(t, gs)) / kGemmXRing / 8 - 32) /
-                        4 / 64 * 64;
+    return t.bf16 ? gemm_xsub_avail(t, gs) / 1024 * 32 : (gemm_xsub_avail(t, gs) / 8 - 32) / 4 / 64 * 64;
 }
 // float32 halo: byte stride of a channel row (padded by 32 bytes so that the
 // two halves of a wave, reading rows 4 apart, fall on different LDS banks)
 constexpr int gemm_xrow_bytes(const GemmTile &t, int gs) { return gemm_halo_cap(t, gs) * 4 + 32; }
-// one halo buffer
-constexpr int gemm_xbuf_bytes(const GemmTile &t, int gs) {
+// one chunk's halo buffer
+constexpr int gemm_xsub_bytes(const GemmTile &t, int gs) {
     return t.bf16 ? gemm_halo_cap(t, gs) / 32 * 1024 : gemm_chunk_ch(t) * gemm_xrow_bytes(t, gs);
 }
+// whether a configuration can run with gs taps per stage (its halo buffers
+// hold at least one copy piece)
+constexpr bool gemm_cfg_valid(const GemmTile &t, int gs) {
+    return gemm_halo_cap(t, gs) >= (t.bf16 ? 32 : 64);
+}
 constexpr int gemm_lds_bytes(const GemmTile &t, int gs) {
-    return kGemmWRing * gemm_wbuf_bytes(t, gs) + kGemmXRing * gemm_xbuf_bytes(t, gs);
+    return kGemmWRing * gemm_wbuf_bytes(t, gs) + kGemmXRing * t.sc * gemm_xsub_bytes(t, gs);
 }
 static_assert(gemm_lds_bytes(kGemmCfg[0], 4) <= kGemmLdsBudget, "LDS");
 static_assert(gemm_lds_bytes(kGemmCfg[2], 4) <= kGemmLdsBudget, "LDS");

@@ -32,7 +32,7 @@
 // reuses it for every tap (tap t reads the positions shifted by its offset).
 // A wave instruction copies 64 consecutive box positions of one channel, each
 // lane gathering its own position of the channel-planar input. The halo of a
-// chunk is requested one chunk ahead through two buffers.
+// chunk is requested two chunks ahead through a ring of three buffers.
 //
 // Weights: the reordered weights hold, per (tap, chunk), the [co][32 bytes]
 // tile contiguously, its two 16-byte halves swapped on rows with bit 3 of co
@@ -145,19 +145,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr tiles::GemmTile CT = tiles::kGemmCfg[CFG];
     static_assert((CT.bf16 != 0) == (sizeof(T) == 2), "tile config does not match the element type");
     static_assert(GS >= 1 && GS <= tiles::kGemmTapGroup, "taps per stage");
-    constexpr int BM = CT.bm, BN = CT.bn, WGM = CT.wgm;
+    constexpr int BM = CT.bm, BN = CT.bn, WGM = CT.wgm, SC = CT.sc;
     constexpr int ES = (int)sizeof(T);
     constexpr int BK = tiles::gemm_chunk_ch(CT);          // channels per chunk (32 bytes)
-    constexpr int HALO = tiles::gemm_halo_cap(CT, GS);    // halo positions per buffer
+    constexpr int BKS = SC * BK;                          // channels per stage (chunk group)
+    constexpr int HALO = tiles::gemm_halo_cap(CT, GS);    // halo positions per chunk buffer
     constexpr int XROW = tiles::gemm_xrow_bytes(CT, GS);  // float32 halo: one channel row, bytes
-    constexpr int XBUF = tiles::gemm_xbuf_bytes(CT, GS);  // one halo buffer
+    constexpr int XSUB = tiles::gemm_xsub_bytes(CT, GS);  // one chunk's halo buffer
+    constexpr int XBUF = SC * XSUB;                       // one ring slot: a chunk group's halos
     constexpr int XB = tiles::kGemmXRing;
     constexpr int WROW = tiles::kGemmWRowBytes;           // weight row bytes
     constexpr int NW = tiles::kGemmWaves, WGN = NW / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MT = WM / 32, NT = WN / 32;
-    constexpr int WSLOT = BM * WROW;                      // bytes of one tap's weight tile
-    constexpr int WBUF = GS * WSLOT;                      // bytes of one stage's weight tiles
+    constexpr int WSLOT = BM * WROW;                      // bytes of one (chunk, tap) weight tile
+    constexpr int NV = SC * GS;                           // (chunk, tap) pairs of a stage
+    constexpr int WBUF = NV * WSLOT;                      // bytes of one stage's weight tiles
     constexpr int NPIECE = WBUF / 1024;                   // 1 KiB weight copies per stage
     constexpr int NDMA = (NPIECE + NW - 1) / NW;          // per wave, at most
     // halo copies per wave and chunk, at most: bfloat16 in 1 KiB pieces of 32
@@ -165,10 +168,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // pieces of 64 positions
     constexpr int XCH = ES == 2 ? 1 : BK / NW;
     constexpr int XJ = ES == 2 ? (HALO / 32 + NW - 1) / NW : HALO / 64;
+    static_assert(tiles::gemm_cfg_valid(CT, GS), "configuration invalid for this tap count");
     static_assert(MT >= 1 && NT >= 1 && WM * WGM == BM && WN * WGN == BN, "wave tiling");
     static_assert(NPIECE * 1024 == WBUF && WSLOT % 1024 == 0, "weight tiles are whole KiB");
     static_assert(BK * ES == WROW && (ES == 2 || XCH * NW == BK), "chunk split");
-    static_assert(ES == 2 ? HALO % 32 == 0 && XBUF == HALO / 32 * 1024
+    static_assert(ES == 2 ? HALO % 32 == 0 && XSUB == HALO / 32 * 1024
                           : HALO % 64 == 0 && XJ * 256 <= XROW,
                   "halo buffers hold whole pieces");
     static_assert(tiles::kGemmWRing * WBUF + XB * XBUF <= tiles::kGemmLdsBudget, "LDS budget");
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.0f;
 
     const int ntaps = ph.ntaps;
-    const int nchunks = p.cig_pad / BK;
+    const int nchunks = p.cig_pad / BKS;  // chunk groups (one per stage and tap group)
     const int Cig = p.Cig;
     const uint32_t xpl_bytes = (uint32_t)p.x_plane * ES;
 
@@ -253,32 +257,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                          ? off
                          : kOutOfRange;
         }
-        // halo of chunk c into buffer xbi
-        auto load_x = [&](int xbi, int c) __attribute__((always_inline)) {
-            if constexpr (ES == 2) {
-                const T *src = x + (((int64_t)b * p.G + g) * nchunks + c) * p.x_plane * 16;
-                const u32x4 rs = rsrc_words(src, xpl_bytes * 16);
+        // halos of the chunks of group cg into ring slot xbi
+        auto load_x = [&](int xbi, int cg) __attribute__((always_inline)) {
 #pragma unroll
-                for (int j = 0; j < XJ; ++j)
-                    if (j < nxw)
-                        copy_to_lds<16>(xs_lds + (uint32_t)(xbi * XBUF + (j * NW + wave) * 1024), xsp[j], rs);
-            } else {
-#pragma unroll
-                for (int h = 0; h < XCH; ++h) {
-                    const int ch = wave * XCH + h;  // channel within the chunk
-                    const int ci = c * BK + ch;     // channel within the group
-                    const T *src = x + ((int64_t)b * p.Ci + (int64_t)g * Cig + ci) * p.x_plane;
-                    const u32x4 rs = rsrc_words(src, ci < Cig ? xpl_bytes : 0u);
-                    const uint32_t dst = xs_lds + (uint32_t)(xbi * XBUF + ch * XROW);
+            for (int sc = 0; sc < SC; ++sc) {
+                const int c = cg * SC + sc;  // chunk
+                const uint32_t sub = xs_lds + (uint32_t)(xbi * XBUF + sc * XSUB);
+                if constexpr (ES == 2) {
+                    const T *src =
+                        x + (((int64_t)b * p.G + g) * (p.cig_pad / 16) + c) * p.x_plane * 16;
+                    const u32x4 rs = rsrc_words(src, xpl_bytes * 16);
 #pragma unroll
                     for (int j = 0; j < XJ; ++j)
-                        if (j < nxw) copy_to_lds<4>(dst + j * 256, xsp[j], rs);
+                        if (j < nxw) copy_to_lds<16>(sub + (uint32_t)((j * NW + wave) * 1024), xsp[j], rs);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < XCH; ++h) {
+                        const int ch = wave * XCH + h;  // channel within the chunk
+                        const int ci = c * BK + ch;     // channel within the group
+                        const T *src = x + ((int64_t)b * p.Ci + (int64_t)g * Cig + ci) * p.x_plane;
+                        const u32x4 rs = rsrc_words(src, ci < Cig ? xpl_bytes : 0u);
+                        const uint32_t dst = sub + (uint32_t)(ch * XROW);
+#pragma unroll
+                        for (int j = 0; j < XJ; ++j)
+                            if (j < nxw) copy_to_lds<4>(dst + j * 256, xsp[j], rs);
+                    }
                 }
             }
         };
 
-        // ---- weight tiles: per stage GS slots of [BM][32 bytes]; wave w
-        // copies the 1 KiB pieces j*8 + w (piece q = slot q / (BM/32), rows
+        // ---- weight tiles: per stage NV = SC * GS slots of [BM][32 bytes],
+        // slot sc * GS + u holding chunk sc of the group and tap u; wave w
+        // copies the 1 KiB pieces j*4 + w (piece q: slot q / (BM/32), rows
         // (q % (BM/32))*32 ... +32), lane l taking 16 bytes at 16*l ----
         const uint32_t tap_bytes = (uint32_t)p.cog_pad * p.cig_pad * ES;
         const uint32_t chunk_bytes = (uint32_t)p.cog_pad * WROW;
@@ -290,12 +300,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         uint32_t wv[NDMA];
 #pragma unroll
         for (int j = 0; j < NDMA; ++j) {
-            const int q = j * NW + wave, u = q / (BM / 32), rb = q % (BM / 32);
-            wv[j] = (uint32_t)u * tap_bytes + (uint32_t)(co_t * BM + rb * 32) * WROW + (uint32_t)lane * 16;
+            const int q = j * NW + wave, slot = q / (BM / 32), rb = q % (BM / 32);
+            const int sc = slot / GS, u = slot % GS;
+            wv[j] = (uint32_t)u * tap_bytes + (uint32_t)sc * chunk_bytes +
+                    (uint32_t)(co_t * BM + rb * 32) * WROW + (uint32_t)lane * 16;
         }
-        // weight tiles of tap group gi of chunk c into buffer wbuf
-        auto load_w = [&](int wbi, int gi, int c) __attribute__((always_inline)) {
-            const uint32_t base = (uint32_t)(gi * GS) * tap_bytes + (uint32_t)c * chunk_bytes;
+        // weight tiles of tap group gi of chunk group cg into buffer wbi
+        auto load_w = [&](int wbi, int gi, int cg) __attribute__((always_inline)) {
+            const uint32_t base = (uint32_t)(gi * GS) * tap_bytes + (uint32_t)(cg * SC) * chunk_bytes;
 #pragma unroll
             for (int j = 0; j < NDMA; ++j)
                 if (j < ndma)
@@ -363,15 +375,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         };
 
         // ---- pipeline ----
-        // Stage s = chunk * ngrp + gi computes tap group gi of the chunk from
-        // weight buffer s % 3 and halo buffer chunk % 2. At its start it
-        // requests the halo of chunk + 1 (first group of a chunk only), then
-        // the weights of stage s + 2; at its end it waits for everything but
-        // those weights and joins the barrier.
+        // Stage s = chunk * ngrp + gi computes tap group gi of chunk group
+        // `chunk` from weight buffer s % 3 and halo slot chunk % 3. At its
+        // start it requests the halos of group chunk + 2 (first tap group
+        // only), then the weights of stage s + 2; at its end it waits for
+        // everything requested before (the stage s + 1 reads) and joins the
+        // barrier.
         const int nstages = nchunks * ngrp;
-        int chunk = 0, gi = 0;  // of stage s
-        int c2n = 0, gi2 = 0;   // of stage s + 2
+        const int nx = SC * XCH * nxw;  // halo copies of one chunk group by this wave
+        int chunk = 0, gi = 0;          // of stage s
+        int c2n = 0, gi2 = 0;           // of stage s + 2
         load_x(0, 0);
+        if (nchunks > 1) load_x(1, 1);
         load_w(0, 0, 0);
         if (++gi2 == ngrp) {
             gi2 = 0;
@@ -382,43 +397,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             gi2 = 0;
             ++c2n;
         }
-        stage_barrier<0>();
-        int wb = 0;  // weight buffer of stage s: s % 3
-        for (int s = 0; s < nstages; ++s) {
-            if (gi == 0 && chunk + 1 < nchunks) load_x((chunk + 1) & 1, chunk + 1);
-            const bool w_issue = s + 2 < nstages;
-            if (w_issue) load_w(wb == 0 ? 2 : wb - 1, gi2, c2n);
-            int dl[GS];
+        // halo shifts of the first stage's taps
+        int dl[GS];
 #pragma unroll
-            for (int u = 0; u < GS; ++u) dl[u] = ptab[gi * GS + u];
+        for (int u = 0; u < GS; ++u) dl[u] = ptab[u];
+        stage_barrier<0>();
+        int wb = 0, xb = 0;  // buffers of stage s: s % 3, chunk % 3
+        for (int s = 0; s < nstages; ++s) {
             const unsigned char *wsb = ws[wb];
-            const unsigned char *xsb = xs[chunk & 1];
-            // operands of tap u + 1 are read before the MFMAs of tap u issue;
-            // the scheduling barriers keep the compiler from reordering them
+            const unsigned char *xsb = xs[xb];
+            // (chunk, tap) pair v = sc * GS + u: weight slot v, the halo of
+            // chunk sc shifted by dl[u]. The operands of the first pair are
+            // requested first; then this stage's copies; then, pair by pair,
+            // the operands of v + 1 before the MFMAs of v. The scheduling
+            // barriers keep the compiler from reordering these groups.
             Frag fa[2][MT], fb[2][NT];
             read_frags(fa[0], fb[0], wsb, xsb, dl[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool x_issue = gi == 0 && chunk + 2 < nchunks;
+            if (x_issue) load_x(xb == 0 ? 2 : xb - 1, chunk + 2);
+            const bool w_issue = s + 2 < nstages;
+            if (w_issue) load_w(wb == 0 ? 2 : wb - 1, gi2, c2n);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < GS; ++u) {
-                if (u + 1 < GS)
-                    read_frags(fa[(u + 1) & 1], fb[(u + 1) & 1], wsb + (u + 1) * WSLOT, xsb, dl[u + 1]);
+            for (int v = 0; v < NV; ++v) {
+                if (v + 1 < NV)
+                    read_frags(fa[(v + 1) & 1], fb[(v + 1) & 1], wsb + (v + 1) * WSLOT,
+                               xsb + ((v + 1) / GS) * XSUB, dl[(v + 1) % GS]);
                 __builtin_amdgcn_sched_barrier(0);
-                mfma(fa[u & 1], fb[u & 1]);
+                mfma(fa[v & 1], fb[v & 1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // the next stage's halo shifts, fetched before the barrier
+            const int gin = gi + 1 == ngrp ? 0 : gi + 1;
+#pragma unroll
+            for (int u = 0; u < GS; ++u) dl[u] = ptab[gin * GS + u];
             if (s + 1 < nstages) {
-                // everything stage s + 1 reads was requested before this
-                // stage's weight copies, which alone may still fly
-                if (!w_issue)
+                // what this stage requested may still fly; everything older
+                // (all that stage s + 1 reads) must have landed
+                const int fly = (x_issue ? nx : 0) + (w_issue ? ndma : 0);
+                if (fly == 0)
                     stage_barrier<0>();
-                else if (ndma == NDMA)
-                    stage_barrier<NDMA>();
                 else
-                    stage_barrier_n<NDMA>(ndma);
+                    stage_barrier_n<NDMA + SC * XCH * XJ>(fly);
             }
             wb = wb == 2 ? 0 : wb + 1;
             if (++gi == ngrp) {
                 gi = 0;
                 ++chunk;
+                xb = xb == 2 ? 0 : xb + 1;
             }
             if (w_issue && ++gi2 == ngrp) {
                 gi2 = 0;
@@ -483,7 +510,8 @@ template <typename T, int CFG, int GS>
 static void launch_cfg(const Plan &pl, const void *x, const void *ws, const void *bias, void *y,
                        hipStream_t stream) {
     const DevParams &p = pl.dp;
-    hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS>), dim3(p.n_blocks), dim3(tiles::kGemmThreads),
+    if constexpr (tiles::gemm_cfg_valid(tiles::kGemmCfg[CFG], GS))
+        hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS>), dim3(p.n_blocks), dim3(tiles::kGemmThreads),
                        0, stream, p, (const T *)x, (const T *)ws,
                        (const int32_t *)((const char *)ws + pl.tab_offset), (const T *)bias, (T *)y);
 }
@@ -491,7 +519,10 @@ static void launch_cfg(const Plan &pl, const void *x, const void *ws, const void
 template <typename T, int CFG>
 static hipError_t launch_gs(const Plan &pl, const void *x, const void *ws, const void *bias,
                             void *y, hipStream_t stream) {
-    switch (pl.dp.gemm_gs) {
+    const int gs = pl.dp.gemm_gs;
+    if (gs < 1 || gs > tiles::kGemmTapGroup || !tiles::gemm_cfg_valid(tiles::kGemmCfg[CFG], gs))
+        return hipErrorInvalidValue;
+    switch (gs) {
         case 1: launch_cfg<T, CFG, 1>(pl, x, ws, bias, y, stream); break;
         case 2: launch_cfg<T, CFG, 2>(pl, x, ws, bias, y, stream); break;
         case 3: launch_cfg<T, CFG, 3>(pl, x, ws, bias, y, stream); break;

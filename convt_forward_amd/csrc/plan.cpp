@@ -218,7 +218,7 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
     DevParams best_dp{};
     for (int c = 0; c < tiles::kGemmCfgCount; ++c) {
         const tiles::GemmTile &t = tiles::kGemmCfg[c];
-        if ((t.bf16 != 0) != bf16) continue;
+        if ((t.bf16 != 0) != bf16 || !tiles::gemm_cfg_valid(t, gs)) continue;
         DevParams tmp = *dp;
         if (!choose_gemm_tile(&tmp, ndim, t.bn, tiles::gemm_halo_cap(t, gs))) continue;
         const int64_t co_tiles = ceil_div(tmp.Cog, t.bm);
@@ -459,7 +459,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     if (route == CONVT_ROUTE_PHASE_GEMM) {
         pick_gemm_cfg(&dp, dt, nd);
         const tiles::GemmTile &t = tiles::kGemmCfg[dp.gemm_cfg];
-        const int64_t bk = 32 / pl->elem_bytes;  // channels of a 32-byte chunk
+        // channels of a stage: SC chunks of 32 bytes
+        const int64_t bk = 32 / pl->elem_bytes * t.sc;
         dp.cog_pad = (int32_t)(ceil_div(Cog, t.bm) * t.bm);
         dp.cig_pad = (int32_t)(ceil_div(Cig, bk) * bk);
         dp.wr_chunked = 1;

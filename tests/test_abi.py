@@ -166,9 +166,10 @@ def test_workspace_sizes():
     wr_bytes = 512 * 256 * 16 * 2
     assert pl.workspace_bytes == wr_bytes + 256 + 64 * 512 * 16 * 16 * 2
     pl = plan(x_shape=(1, 3, 5), w_shape=(3, 5, 3), stride=2, route="phase_gemm")
-    # channels padded to the f32 tile: 8 input, 64 output, 3 taps (phases of
-    # 2 and 1 taps, one tap per stage); then the tap table, 4 bytes per tap
-    assert pl.workspace_bytes == 1 * 3 * 64 * 8 * 4 + 3 * 4
+    # channels padded to the f32 tile: 16 input (two 8-channel chunks per
+    # stage), 64 output, 3 taps (phases of 2 and 1 taps, one tap per stage);
+    # then the tap table, 4 bytes per tap
+    assert pl.workspace_bytes == 1 * 3 * 64 * 16 * 4 + 3 * 4
     assert plan(x_shape=(1, 3, 5), w_shape=(3, 5, 3), route="naive").workspace_bytes == 0
 
 

@@ -99,27 +99,27 @@ namespace tiles {
 // covers SC consecutive chunks and gs (1..4) taps. The weight tiles of a
 // stage stream through a ring of kGemmWRing LDS buffers of 32-byte rows; the
 // input halo of SC chunks (HALO positions at most) streams through a ring of
-// kGemmXRing buffers that share the rest of the block's LDS budget:
+// xb buffers that share the rest of the block's LDS budget:
 // bfloat16 as one 32-byte row per position (from the channel-chunked copy of
 // x), float32 as one row of 4-byte elements per channel (straight from x).
 struct GemmTile {
-    int bm, bn, wgm, bf16, sc;
+    int bm, bn, wgm, bf16, sc, xb;  // xb: halo ring buffers (3: two groups in flight, 2: one)
 };
 constexpr int kGemmThreads = 256;
 constexpr int kGemmWaves = 4;
 constexpr int kGemmLdsBudget = 80 * 1024;  // per block: two blocks share a CU
 constexpr int kGemmTapGroup = 4;   // taps per pipeline stage, at most (the planner picks 1..4)
 constexpr int kGemmWRing = 3;      // weight-tile buffers: two stages in flight
-constexpr int kGemmXRing = 3;      // halo buffers: two chunk groups in flight
 constexpr int kGemmWRowBytes = 32; // weight row: one chunk of channels
-constexpr int kGemmCfgCount = 6;
+constexpr int kGemmCfgCount = 7;
 constexpr GemmTile kGemmCfg[kGemmCfgCount] = {
-    {128, 256, 1, 1, 1},  // 0: bf16, waves 128 x 64
-    {64, 256, 1, 1, 1},   // 1: bf16, waves 64 x 64
-    {128, 128, 1, 1, 1},  // 2: bf16, waves 128 x 32
-    {64, 256, 1, 0, 1},   // 3: f32, waves 64 x 64
-    {64, 128, 1, 0, 2},   // 4: f32, waves 64 x 32, two chunks per stage
-    {128, 128, 1, 0, 1},  // 5: f32, waves 128 x 32
+    {128, 256, 1, 1, 1, 3},  // 0: bf16, waves 128 x 64
+    {64, 256, 1, 1, 1, 3},   // 1: bf16, waves 64 x 64
+    {128, 128, 1, 1, 1, 3},  // 2: bf16, waves 128 x 32
+    {64, 256, 1, 0, 1, 3},   // 3: f32, waves 64 x 64
+    {64, 128, 1, 0, 2, 3},   // 4: f32, waves 64 x 32, two chunks per stage
+    {128, 128, 1, 0, 1, 3},  // 5: f32, waves 128 x 32
+    {128, 256, 1, 1, 1, 2},  // 6: bf16, waves 128 x 64, larger halos (3-D tiles)
 };
 constexpr int gemm_chunk_ch(const GemmTile &t) { return t.bf16 ? 16 : 8; }
 // one stage's weight tiles
@@ -128,7 +128,7 @@ constexpr int gemm_wbuf_bytes(const GemmTile &t, int gs) {
 }
 // bytes available to the halo of one chunk in one ring slot
 constexpr int gemm_xsub_avail(const GemmTile &t, int gs) {
-    return (kGemmLdsBudget - kGemmWRing * gemm_wbuf_bytes(t, gs)) / kGemmXRing / t.sc;
+    return (kGemmLdsBudget - kGemmWRing * gemm_wbuf_bytes(t, gs)) / t.xb / t.sc;
 }
 // halo positions one chunk's buffer holds: bfloat16 in whole 1 KiB pieces of
 // 32 rows, float32 in whole pieces of 64 positions per channel row
@@ -148,7 +148,7 @@ constexpr bool gemm_cfg_valid(const GemmTile &t, int gs) {
     return gemm_halo_cap(t, gs) >= (t.bf16 ? 32 : 64);
 }
 constexpr int gemm_lds_bytes(const GemmTile &t, int gs) {
-    return kGemmWRing * gemm_wbuf_bytes(t, gs) + kGemmXRing * t.sc * gemm_xsub_bytes(t, gs);
+    return kGemmWRing * gemm_wbuf_bytes(t, gs) + t.xb * t.sc * gemm_xsub_bytes(t, gs);
 }
 static_assert(gemm_lds_bytes(kGemmCfg[0], 4) <= kGemmLdsBudget, "LDS");
 static_assert(gemm_lds_bytes(kGemmCfg[2], 4) <= kGemmLdsBudget, "LDS");

@@ -32,7 +32,8 @@
 // reuses it for every tap (tap t reads the positions shifted by its offset).
 // A wave instruction copies 64 consecutive box positions of one channel, each
 // lane gathering its own position of the channel-planar input. The halo of a
-// chunk is requested two chunks ahead through a ring of three buffers.
+// chunk is requested one or two chunks ahead through a ring of two or three
+// buffers (a tile configuration's choice: two leave room for larger halos).
 //
 // Weights: the reordered weights hold, per (tap, chunk), the [co][32 bytes]
 // tile contiguously, its two 16-byte halves swapped on rows with bit 3 of co
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int XROW = tiles::gemm_xrow_bytes(CT, GS);  // float32 halo: one channel row, bytes
     constexpr int XSUB = tiles::gemm_xsub_bytes(CT, GS);  // one chunk's halo buffer
     constexpr int XBUF = SC * XSUB;                       // one ring slot: a chunk group's halos
-    constexpr int XB = tiles::kGemmXRing;
+    constexpr int XB = CT.xb;  // halo ring slots
     constexpr int WROW = tiles::kGemmWRowBytes;           // weight row bytes
     constexpr int NW = tiles::kGemmWaves, WGN = NW / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -376,17 +377,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         // ---- pipeline ----
         // Stage s = chunk * ngrp + gi computes tap group gi of chunk group
-        // `chunk` from weight buffer s % 3 and halo slot chunk % 3. At its
-        // start it requests the halos of group chunk + 2 (first tap group
-        // only), then the weights of stage s + 2; at its end it waits for
-        // everything requested before (the stage s + 1 reads) and joins the
-        // barrier.
+        // `chunk` from weight buffer s % 3 and halo slot chunk % XB. At its
+        // start it requests the halos of group chunk + XB - 1 (first tap
+        // group only), then the weights of stage s + 2; at its end it waits
+        // for what stage s + 1 reads and joins the barrier.
         const int nstages = nchunks * ngrp;
         const int nx = SC * XCH * nxw;  // halo copies of one chunk group by this wave
         int chunk = 0, gi = 0;          // of stage s
         int c2n = 0, gi2 = 0;           // of stage s + 2
         load_x(0, 0);
-        if (nchunks > 1) load_x(1, 1);
+        if (XB == 3 && nchunks > 1) load_x(1, 1);
         load_w(0, 0, 0);
         if (++gi2 == ngrp) {
             gi2 = 0;
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int u = 0; u < GS; ++u) dl[u] = ptab[u];
         stage_barrier<0>();
-        int wb = 0, xb = 0;  // buffers of stage s: s % 3, chunk % 3
+        int wb = 0, xb = 0;  // buffers of stage s: s % 3, chunk % XB
         for (int s = 0; s < nstages; ++s) {
             const unsigned char *wsb = ws[wb];
             const unsigned char *xsb = xs[xb];
@@ -414,8 +414,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             Frag fa[2][MT], fb[2][NT];
             read_frags(fa[0], fb[0], wsb, xsb, dl[0]);
             __builtin_amdgcn_sched_barrier(0);
-            const bool x_issue = gi == 0 && chunk + 2 < nchunks;
-            if (x_issue) load_x(xb == 0 ? 2 : xb - 1, chunk + 2);
+            const bool x_issue = gi == 0 && chunk + XB - 1 < nchunks;
+            if (x_issue) load_x(xb == 0 ? XB - 1 : xb - 1, chunk + XB - 1);
             const bool w_issue = s + 2 < nstages;
             if (w_issue) load_w(wb == 0 ? 2 : wb - 1, gi2, c2n);
             __builtin_amdgcn_sched_barrier(0);
@@ -433,9 +433,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int u = 0; u < GS; ++u) dl[u] = ptab[gin * GS + u];
             if (s + 1 < nstages) {
-                // what this stage requested may still fly; everything older
-                // (all that stage s + 1 reads) must have landed
-                const int fly = (x_issue ? nx : 0) + (w_issue ? ndma : 0);
+                // the weights of stage s + 2 may still fly, and with three
+                // halo slots the halos requested now; everything older (all
+                // that stage s + 1 reads) must have landed. (With two slots
+                // the halo requested now, before the weights, is awaited.)
+                const int fly = (XB == 3 && x_issue ? nx : 0) + (w_issue ? ndma : 0);
                 if (fly == 0)
                     stage_barrier<0>();
                 else
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (++gi == ngrp) {
                 gi = 0;
                 ++chunk;
-                xb = xb == 2 ? 0 : xb + 1;
+                xb = xb == XB - 1 ? 0 : xb + 1;
             }
             if (w_issue && ++gi2 == ngrp) {
                 gi2 = 0;
@@ -544,6 +546,7 @@ hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, cons
         case 3: return launch_gs<float, 3>(pl, x, wr, bias, y, stream);
         case 4: return launch_gs<float, 4>(pl, x, wr, bias, y, stream);
         case 5: return launch_gs<float, 5>(pl, x, wr, bias, y, stream);
+        case 6: return launch_gs<uint16_t, 6>(pl, x, wr, bias, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -338,9 +338,70 @@ __global__ __launch_bounds__(256) void pack_x_kernel(DevParams p, const uint16_t
     dst[1] = o1;
 }
 
+// The same re-layout for planes of a multiple of 8 positions (16-byte
+// aligned channel rows), through LDS: a block owns (b, g, chunk) and 256
+// positions; it reads the 16 channel rows with 16-byte loads (consecutive
+// lanes on consecutive pieces of a row), and writes the 256 x 32-byte
+// destination rows with 16-byte stores, consecutive lanes on consecutive
+// 16 bytes.
+__global__ __launch_bounds__(256) void pack_x8_kernel(DevParams p, const uint16_t *__restrict__ x,
+                                                       uint16_t *__restrict__ xp, int ptiles) {
+    constexpr int RS = 256 + 2;  // LDS row stride (elements): 256 positions + 4 bytes
+    __shared__ uint16_t tile[16 * RS];
+    const int nchunks = p.cig_pad / 16;
+    const int64_t plane = p.x_plane;
+    int bid = blockIdx.x;
+    const int pt = bid % ptiles;
+    bid /= ptiles;
+    const int c = bid % nchunks;
+    bid /= nchunks;
+    const int g = bid % p.G;
+    const int64_t b = bid / p.G;
+    const int64_t pos0 = (int64_t)pt * 256;
+    const uint16_t *src = x + ((b * p.Ci + (int64_t)g * p.Cig + c * 16) * plane + pos0);
+    const int nch = p.Cig - c * 16;  // channels of this chunk inside the group (>= 1)
+    u32x4 v[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int idx = threadIdx.x + 256 * k, ch = idx / 32, pg = idx % 32;
+        v[k] = ch < nch && pos0 + pg * 8 < plane ? *(const u32x4 *)(src + ch * plane + pg * 8)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int idx = threadIdx.x + 256 * k, ch = idx / 32, pg = idx % 32;
+        uint32_t *row = (uint32_t *)&tile[ch * RS + pg * 8];  // 4-byte aligned (RS even)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) row[e] = v[k][e];
+    }
+    __syncthreads();
+    u32x4 *dst = (u32x4 *)(xp + (((b * p.G + g) * nchunks + c) * plane + pos0) * 16);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int idx = threadIdx.x + 256 * k, pos = idx / 2, half = idx % 2;
+        if (pos0 + pos < plane) {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = (uint32_t)tile[(half * 8 + 2 * e) * RS + pos] |
+                       ((uint32_t)tile[(half * 8 + 2 * e + 1) * RS + pos] << 16);
+            dst[idx] = o;
+        }
+    }
+}
+
 hipError_t launch_pack_x(const Plan &pl, const void *x, void *xp, hipStream_t stream) {
     const DevParams &p = pl.dp;
     if (pl.xp_bytes == 0) return hipSuccess;
+    if (p.x_plane % 8 == 0 && (uintptr_t)x % 16 == 0) {
+        const int64_t ptiles = ((int64_t)p.x_plane + 255) / 256;
+        const int64_t blocks = (int64_t)p.B * p.G * (p.cig_pad / 16) * ptiles;
+        if (blocks <= 0) return hipSuccess;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(pack_x8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p,
+                           (const uint16_t *)x, (uint16_t *)xp, (int)ptiles);
+        return hipGetLastError();
+    }
     const int64_t ptiles = ((int64_t)p.x_plane + 255) / 256;
     const int64_t blocks = (int64_t)p.B * p.G * (p.cig_pad / 16) * ptiles;
     if (blocks <= 0) return hipSuccess;

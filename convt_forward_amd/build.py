@@ -28,6 +28,13 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source device flags. The grouped kernel keeps its MFMA accumulators in
+# ordinary VGPRs (no AGPR copies around its short MFMA chains).
+SOURCE_FLAGS = {
+    "k_grouped.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if c and (os.path.sep not in c or os.path.exists(c)):
@@ -37,7 +44,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + HIP_FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

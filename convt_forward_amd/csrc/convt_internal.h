@@ -63,10 +63,15 @@ struct DevParams {
     int32_t n_co_tiles;
     int32_t n_blocks;          // grid of the main kernel
     int32_t xcd_remap;         // 1: block ids remapped so each XCD takes a contiguous range
-    int32_t out_rows;          // grouped route: output rows staged per block
-    int32_t grp_w_off, grp_out_off, grp_lds_bytes;  // grouped route: LDS layout (bytes)
-    int32_t grp_out_cstride;   // grouped route: output-tile channel stride (elements)
-    int32_t grp_tab_off;       // grouped route: LDS offset (bytes) of the K-slot table
+    int32_t grp_w_off, grp_tab_off, grp_lds_bytes;  // grouped route: LDS layout (bytes)
+    int32_t grp_hwp;           // grouped route: halo row pitch in 16-byte cells (>= hw)
+    int32_t grp_hshift;        // grouped route: pitch column of halo position 0
+    int32_t grp_nk;            // grouped route: 8-position chunks of an x row (0: rows are
+                               // not whole chunks); chunk k sits at column 8k + hshift - umin
+    int32_t grp_nsc;           // grouped route: q segments (16 positions) per staged chunk
+                               // (0: segment pairs leave through DPP, no staging)
+    int32_t grp_st_off;        // grouped route: LDS offset (bytes) of the per-wave output staging
+    int32_t grp_st_pitch;      // grouped route: staging bytes per channel (chunk bytes + 16)
     int32_t grp_ksteps;        // grouped route: MFMA K steps per phase (1, 2 or 4)
     int32_t gemm_cfg;          // phase GEMM: index into tiles::kGemmCfg
     int32_t gemm_gs;           // phase GEMM: taps per pipeline stage (1..kGemmTapGroup)

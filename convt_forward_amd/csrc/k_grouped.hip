@@ -3,74 +3,188 @@
 // For grouped problems with few channels per group (C_in/groups a multiple
 // of 8 up to 64, C_out/groups up to 16) the phase GEMM's tiles would be
 // mostly empty. Here one block owns one (batch, group) and a tile of q rows
-// at one q-depth, over the full q width, for EVERY stride phase, so that the
-// block's output rows are complete and leave as dense 16-byte stores: the
+// at one q-depth, over the full q width, for EVERY stride phase: the
 // huggingface ai.onnx.ConvTranspose page's grouped stride-phase blocked
 // variant (an invocation owns output pixels and a block of its group's output
 // channels; every gathered input sample feeds the whole channel block; the
 // group's weight slab is staged once per workgroup), laid out for gfx950.
 //
-// Per block:
-//  1. the input halo (the q tile grown by the union of all phases' input
-//     windows) for the group's Cig channels goes to LDS with channels
-//     contiguous, and the group's reordered weights [tap][16 co][Cig] too;
-//  2. per phase, each wave keeps the phase's weight fragments in registers
-//     and runs, for each of its 16-position segments of a q row, up to four
-//     v_mfma_f32_16x16x32_bf16: rows = 16 positions, columns = the group's
-//     output channels (padded to 16), K = (tap, 8-channel slice) slots, four
-//     per MFMA. A lane reads its 8 channels of one tap as one 16-byte LDS row;
-//  3. results + bias are rounded to bfloat16 into an LDS output tile
-//     [co][depth residue][rows][O_w], interleaving the phases;
-//  4. the tile is written to y row by row with 16-byte stores.
-// The kernel's loops carry no per-lane integer division: positions advance
-// by 16-wide segments of a row and the K-slot decode is done once per phase.
+// The work per output is tiny (a few K slots) and the output is 4x the
+// input, so the kernel is written for a small instruction count per stored
+// byte and for stores that write whole 128-byte rows:
+//  1. the group's reordered weights [tap][16 co][Cig] and a slot table (a
+//     record per phase; per (tap, 8-channel slice) slot the LDS offset of the
+//     tap's window and of its weights), both prepared with the weights, are
+//     copied to LDS; the input halo (the q tile grown by the union of all
+//     phases' input windows) goes to LDS as 16-byte cells of 8 channels,
+//     [halo row][slice][column]. When x rows are whole 16-byte chunks, a lane
+//     loads 8 positions of each of 8 channels (eight 16-byte loads),
+//     transposes the 8 x 8 block in registers (v_perm) and writes 8 cells;
+//     otherwise it falls back to 2-byte loads;
+//  2. per (depth, height) residue pair, a wave keeps the weight fragments of
+//     every width residue in registers and takes chunks of 16-position
+//     segments of the block's q rows in turn: per segment and width residue
+//     up to four v_mfma_f32_16x16x32_bf16 (rows = 16 positions, columns =
+//     the group's output channels padded to 16, K = (tap, slice) slots, four
+//     per MFMA), with the bias as the accumulator's initial value. A lane
+//     then holds, for one channel, 4*S2 consecutive outputs of one row;
+//  3. the outputs are rounded to bfloat16 in pairs and leave as 16-byte
+//     stores in which 8 consecutive lanes cover 128 contiguous bytes: with
+//     width stride 2 and at most 8 channels, a segment pair's second half
+//     moves into the padding lanes (DPP) and a lane permutation orders the
+//     row pieces; otherwise chunks go through a per-wave LDS staging area.
+//     Edge segments are stored straight from registers.
 #include "kcommon.h"
 #include "launch.h"
 
 namespace convt {
 
 constexpr int kGrpRsrcWord3 = 0x00020000;
-
 constexpr uint32_t kGrpOutOfRange = 0x80000000u;
+// flag in the kernel's st_align argument: y takes 16-byte stores of row
+// pieces (the low bits hold the widest aligned store of a lane's run)
+constexpr int kStageOk = 32;
+
+// v_perm_b32 selectors pairing the low (resp. high) 16-bit halves of two
+// words: result = {second.lo, first.lo} (resp. {second.hi, first.hi}).
+constexpr uint32_t kPermLo = 0x05040100u;
+constexpr uint32_t kPermHi = 0x07060302u;
+
+template <bool B> struct BoolTag {
+    static constexpr bool value = B;
+};
+template <int V> struct IntTag {
+    static constexpr int value = V;
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two float32 -> two bfloat16 (RNE) in one word, first value in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// a lane's run of 4*S2 outputs (2*S2 words) into the staging row
+template <int S2>
+__device__ __forceinline__ void stage_run_t(const uint32_t *pk, unsigned char *w) {
+    if constexpr ((S2 & 1) == 0) {
+#pragma unroll
+        for (int k = 0; k < S2 / 2; ++k)
+            *(u32x4 *)(w + 16 * k) = u32x4{pk[4 * k], pk[4 * k + 1], pk[4 * k + 2], pk[4 * k + 3]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < S2; ++k) *(u32x2 *)(w + 8 * k) = u32x2{pk[2 * k], pk[2 * k + 1]};
+    }
+}
+
+// The kernel's arguments: the plan fields it reads, packed into a few cache
+// lines (kernel arguments are fetched line by line on first use).
+struct GrpAxis {
+    int32_t I, O, S, umin;
+};
+struct GrpArgs {
+    GrpAxis ax[3];
+    int32_t G, Ci, Co, Cig, Cog, has_bias;
+    int32_t x_plane, y_plane;
+    int32_t th, tw, hd, hh, hw;
+    int32_t grp_hwp, grp_hshift, grp_nk, grp_nsc;
+    int32_t grp_w_off, grp_tab_off, grp_st_off, grp_st_pitch;
+    int32_t ktot, nphase;
+};
 
 template <int S2, int KS>
-__global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_t *__restrict__ x,
-                                                      const uint16_t *__restrict__ wr,
-                                                      const uint16_t *__restrict__ bias,
-                                                      uint16_t *__restrict__ y) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void grouped_kernel(
+    GrpArgs p, const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const int2 *__restrict__ gtab, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
+    int st_align, int x_vec) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    uint16_t *xs = (uint16_t *)lds;
-    uint16_t *wsl = (uint16_t *)(lds + p.grp_w_off);
+    const uint16_t *wsl = (const uint16_t *)(lds + p.grp_w_off);
 
     const int tid = threadIdx.x, lane = tid & 63;
     // uniform per wave: lets the plan tables be read with scalar loads
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int bid = remap_block(blockIdx.x, p.n_blocks, p.xcd_remap);
-    const int th_i = bid % p.nt_h;
-    bid /= p.nt_h;
-    const int qd = bid % p.nt_d;
-    bid /= p.nt_d;
-    const int g = bid % p.G;
-    const int b = bid / p.G;
+    // grid: (group + G * batch, row tile, q depth)
+    const int th_i = blockIdx.y, qd = blockIdx.z;
+    const int b = blockIdx.x / p.G, g = blockIdx.x - b * p.G;
 
-    const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
+    const GrpAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
     const int Cig = p.Cig, noct = Cig >> 3;
     const int R = p.th, Qw = p.tw;
-    const int HH = p.hh, HW = p.hw;
+    const int HH = p.hh, HW = p.hw, HWP = p.grp_hwp;
     const int q0h = th_i * R;
     const int h0 = qd + a0.umin, h1 = q0h + a1.umin, h2 = a2.umin;
+    const int nrow = p.hd * HH;
 
-    // 1a. input halo -> LDS [row][Cig]; positions outside the input read
-    // an out-of-range offset (zero). A wave takes whole halo rows (one
-    // 8-channel slice each); its lanes walk the row's positions.
+    // 1a. the group's weights [tap][16][Cig] and the slot table (written
+    // with the reordered weights: a record per phase, then per (tap, slice)
+    // slot the LDS byte offset of the tap's window origin in the halo and the
+    // weight offset) -> LDS. Their loads go out first; the halo loads follow.
+    const int nvec = p.ktot * tiles::kGrpCog * noct, nslot = 2 * p.nphase + p.ktot * noct;
+    const u32x4 *wsrc = (const u32x4 *)(wr + (int64_t)g * p.ktot * tiles::kGrpCog * Cig);
+    u32x4 *wdst = (u32x4 *)(lds + p.grp_w_off);
+    int2 *tdst = (int2 *)(lds + p.grp_tab_off);
+    const bool w_one = nvec <= 256 && nslot <= 256;  // one of each per thread at most (uniform)
+    u32x4 wv = {0u, 0u, 0u, 0u};
+    int2 tv = make_int2(0, 0);
+    if (w_one) {  // loaded here, written to LDS after the halo
+        if (tid < nvec) wv = wsrc[tid];
+        if (tid < nslot) tv = gtab[tid];
+    } else {
+        for (int v = tid; v < nvec; v += 256) wdst[v] = wsrc[v];
+        for (int v = tid; v < nslot; v += 256) tdst[v] = gtab[v];
+    }
+    // 1b. input halo -> LDS cells; positions outside the input read an
+    // out-of-range offset (zero).
     const uint32_t xpl_bytes = (uint32_t)p.x_plane * 2;
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(x + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane), (short)0,
         (int)((uint32_t)Cig * xpl_bytes), kGrpRsrcWord3);
-    {
-        // (slice, depth, row) triples are dealt to the waves in turn; a wave
-        // issues the loads of four of its rows before writing any of them
-        const int nrow = p.hd * HH, total = nrow * noct;
+    if (x_vec) {  // uniform
+        // unit = (halo row, slice, chunk k of 8 input positions 8k .. 8k+7),
+        // whose cells are columns col0 + 8k .. +7 of the row; rows outside the
+        // input read zero. Neighbouring lanes take neighbouring rows, whose
+        // cells the odd row pitch spreads over the LDS banks.
+        const int nk = p.grp_nk, col0 = p.grp_hshift - a2.umin;
+        const int units = nrow * noct * nk;
+        for (int u = tid; u < units; u += 256) {
+            const int row = u % nrow, t = u / nrow;
+            const int oct = t % noct, k = t / noct;
+            const int d = row / HH, h = row - d * HH;
+            const int i0 = h0 + d, i1 = h1 + h;
+            const bool ok = i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I;
+            const uint32_t off =
+                ok ? (uint32_t)(oct * 8) * xpl_bytes + (uint32_t)((i0 * a1.I + i1) * a2.I + 8 * k) * 2
+                   : kGrpOutOfRange;
+            u32x4 v[8];  // v[c]: positions 8k .. 8k+7 of channel 8*oct + c
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                v[c] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off + c * xpl_bytes, 0, 0);
+            unsigned char *dst = lds + ((row * noct + oct) * HWP + col0 + 8 * k) * 16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                u32x4 cell;  // position 8k + e, channels 2i, 2i+1 in word i
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    cell[i] = __builtin_amdgcn_perm(v[2 * i + 1][e >> 1], v[2 * i][e >> 1],
+                                                    (e & 1) ? kPermHi : kPermLo);
+                *(u32x4 *)(dst + e * 16) = cell;
+            }
+        }
+        // zero cells: columns left of the row (col0 of them) and right of it
+        const int zl = col0, zn = HWP - a2.I;
+        const int zunits = nrow * noct * zn;
+        for (int u = tid; u < zunits; u += 256) {
+            const int ro = u / zn, z = u - ro * zn;
+            const int col = z < zl ? z : z + a2.I;
+            *(u32x4 *)(lds + (ro * HWP + col) * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+    } else {
+        // Element loads: a wave takes whole halo rows (one slice each) and its
+        // lanes walk the row's positions. (slice, depth, row) triples are
+        // dealt to the waves in turn; a wave issues the loads of four of its
+        // rows before writing any of them.
+        const int total = nrow * noct, hshift = p.grp_hshift;
         int pr = wave, oct = 0, c0 = 0, c1 = wave;
         auto norm = [&]() __attribute__((always_inline)) {
             while (c1 >= HH) {
@@ -108,7 +222,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_
                                 xrs, off + (2 * e + 1) * xpl_bytes, 0, 0);
                             v[u][e] = lo | (hi << 16);
                         }
-                        dst[u] = ((sc0 * HH + sc1) * HW + c2) * Cig + soct * 8;
+                        dst[u] = (((sc0 * HH + sc1) * noct + soct) * HWP + c2 + hshift) * 16;
                         spr += 4;
                         sc1 += 4;
                         while (sc1 >= HH) {
@@ -122,164 +236,374 @@ __global__ __launch_bounds__(256) void grouped_kernel(DevParams p, const uint16_
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (dst[u] >= 0 && c2 < HW) *(u32x4 *)&xs[dst[u]] = v[u];
+                    if (dst[u] >= 0 && c2 < HW) *(u32x4 *)(lds + dst[u]) = v[u];
             }
         }
     }
-    // 1b. the group's weights [tap][16][Cig] -> LDS
-    {
-        const int nvec = p.ktot * tiles::kGrpCog * noct;
-        const u32x4 *src = (const u32x4 *)(wr + (int64_t)g * p.ktot * tiles::kGrpCog * Cig);
-        for (int v = tid; v < nvec; v += 256) ((u32x4 *)wsl)[v] = src[v];
+    if (w_one) {
+        if (tid < nvec) wdst[tid] = wv;
+        if (tid < nslot) tdst[tid] = tv;
     }
-    // 1c. K-slot table: for slot (tap, 8-channel slice) of every phase, the
-    // halo element offset of the tap's window origin and the weight offset
-    int2 *tab = (int2 *)(lds + p.grp_tab_off);
-    for (int P = 0; P < p.nphase; ++P) {  // uniform
-        const PhaseDesc ph = phase_desc(p, P);
-        const int nslots = ph.ntaps * noct;
-        const int n1 = ph.n[1], n2 = ph.n[2];
-        for (int sl = tid; sl < nslots; sl += 256) {
-            const int tap = sl / noct, oct = sl - tap * noct;
-            const int j2 = tap % n2, j1 = (tap / n2) % n1, j0 = tap / (n2 * n1);
-            const int dl = (((ph.off0[0] - a0.umin + j0 * a0.ostep) * HH +
-                             (ph.off0[1] - a1.umin + j1 * a1.ostep)) * HW +
-                            (ph.off0[2] - a2.umin + j2 * a2.ostep)) * Cig + oct * 8;
-            tab[ph.tapbase * noct + sl] = make_int2(dl, (ph.tapbase + tap) * tiles::kGrpCog * Cig + oct * 8);
-        }
-    }
+    const int4 *precs = (const int4 *)(lds + p.grp_tab_off);
+    const int2 *tab = (const int2 *)(lds + p.grp_tab_off + 16 * p.nphase);
     __syncthreads();
 
-    // 2. Per (depth residue, height residue) pair, each wave takes 16-position
-    // segments of the block's q rows. For a segment it runs the MFMA chain of
-    // every width residue r2 < S2 (kept in registers), so lane l (channel
-    // l%16, positions 4*(l/16) + i of the segment) holds the outputs
-    // ow = S2*q + r2 for four consecutive q and every r2: a contiguous run of
-    // 4*S2 outputs, stored straight from registers.
+    // 2. Per (depth residue, height residue) pair, each wave takes chunks of
+    // nsc 16-position segments of the block's q rows in turn. For a segment
+    // it runs the MFMA chain of every width residue r2 < S2, so lane l
+    // (channel l%16, positions 4*(l/16) + i of the segment) holds the
+    // outputs ow = S2*q + r2 for four consecutive q and every r2: a run of
+    // 4*S2 outputs of one output row.
+    // 3. Whole chunks go through the wave's LDS staging area,
+    // [channel][chunk of the output row], and leave as 16-byte pieces of
+    // whole rows (1 KiB per store instruction at the workloads' shapes);
+    // other segments are stored from registers.
     const int l16 = lane & 15, kg4 = lane >> 4;
     const int Cog = p.Cog;
-    const int co = l16;
     const int O2 = a2.O;
     const int nseg = (Qw + 15) >> 4;
-    const float bvf = (p.has_bias && co < Cog) ? bf16_to_f32(bias[g * Cog + co]) : 0.0f;
-    // output plane of this lane's channel; rows past the group's channels are
-    // outside the resource and dropped
+    // nsc == 0: width stride 2, at most 8 channels, an even segment count:
+    // chunks are segment pairs that leave through DPP (no staging)
+    const bool pair_dpp = p.grp_nsc == 0;
+    const int nsc = pair_dpp ? 2 : p.grp_nsc, nchunk = (nseg + nsc - 1) / nsc;
+    const float bvf = (p.has_bias && l16 < Cog) ? bf16_to_f32(bias[g * Cog + l16]) : 0.0f;
+    const f32x4 binit = {bvf, bvf, bvf, bvf};
+    // output planes of the group; a lane's channel plane, or out of range
+    // (dropped) for the padding channels
     const uint32_t ypl_bytes = (uint32_t)p.y_plane * 2;
     const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(y + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane), (short)0,
         (int)((uint32_t)Cog * ypl_bytes), kGrpRsrcWord3);
-    const uint32_t co_bytes = co < Cog ? (uint32_t)co * ypl_bytes : kGrpOutOfRange;
-    const bool row_pairs = (O2 & 1) == 0;  // outputs of a row start 4-byte aligned
+    const uint32_t lane_st =
+        (l16 < Cog ? (uint32_t)l16 * ypl_bytes : kGrpOutOfRange) + (uint32_t)(S2 * 4 * kg4) * 2;
+    // staging: this lane's run in segment s of a chunk at st_w + s * 32 * S2
+    // (the padding channels' lanes all write one spare row); read back in
+    // passes of 1 KiB, flat byte f = 1024 * pass + 16 * lane of the chunk's
+    // [channel][cb] bytes
+    const int st_pitch = p.grp_st_pitch;
+    const uint32_t cb = (uint32_t)(nsc * S2 * 32);
+    unsigned char *stg = lds + p.grp_st_off + wave * (Cog + 1) * st_pitch;
+    const uint32_t st_w = (uint32_t)(min(l16, Cog) * st_pitch + kg4 * S2 * 8);
+    const int st_tot = Cog * (int)cb, npass = (st_tot + 1023) >> 10;
+    // DPP pairs: after the merge, lane 16k + 8h + c holds 16-byte piece
+    // 4h + k of channel c's 128-byte row; a lane permutation then gives lane
+    // 8c + j piece j of channel c, so that 8 consecutive lanes store a row
+    const int bp_src = 4 * (16 * (lane & 3) + 8 * ((lane >> 2) & 1) + (lane >> 3));
+    const uint32_t dpp_st =
+        ((lane >> 3) < Cog ? (uint32_t)(lane >> 3) * ypl_bytes : kGrpOutOfRange) + (uint32_t)((lane & 7) * 16);
+    uint32_t st_r[2], st_y[2];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+        const int f = 1024 * ps + 16 * lane;
+        const int c = f / (int)cb, o = f - c * (int)cb;
+        st_r[ps] = f < st_tot ? (uint32_t)(c * st_pitch + o) : 0u;
+        st_y[ps] = f < st_tot ? (uint32_t)c * ypl_bytes + (uint32_t)o : kGrpOutOfRange;
+    }
+    const uint32_t row_lds = (uint32_t)(noct * HWP * 16);  // halo bytes per q row
+    // this wave's chunks are items wave, wave + 4, ... of (row, chunk): per
+    // step the chunk advances by dc and the row by dq (plus a carry)
+    const int dq = 4 / nchunk, dc = 4 - dq * nchunk;
+    const int ql0 = wave / nchunk, ch0 = wave - ql0 * nchunk;
+    const uint32_t yrow_bytes = (uint32_t)(a1.S * O2 * 2);  // y bytes per q row
+    const uint32_t seg_lds = 256, seg_y = (uint32_t)(S2 * 32);  // per segment
+    // offsets advance by dq rows and dc chunks per step, plus one row minus a
+    // row's chunks on a carry
+    const uint32_t ub_step = (uint32_t)dq * row_lds + (uint32_t)(dc * nsc) * seg_lds;
+    const uint32_t so_step = (uint32_t)dq * yrow_bytes + (uint32_t)(dc * nsc) * seg_y;
+    const uint32_t ub_wrap = row_lds - (uint32_t)(nchunk * nsc) * seg_lds;
+    const uint32_t so_wrap = yrow_bytes - (uint32_t)(nchunk * nsc) * seg_y;
     constexpr int MS = S2;  // width residues kept in registers
+    auto stage_run = [](const uint32_t *pk, unsigned char *w) __attribute__((always_inline)) {
+        stage_run_t<S2>(pk, w);
+    };
     for (int r0 = 0; r0 < a0.S; ++r0) {
         for (int r1 = 0; r1 < a1.S; ++r1) {
             // phases (r0, r1, r2 < S2): their records and this lane's K slots
-            int qn0 = 0, qn1 = 0, qn2[MS], nkb[MS], dl[MS][KS];
+            int qn0 = 0, qn1 = 0, qn2min = 1 << 30, qn2[MS];
+            uint32_t rd[MS][KS];  // LDS byte offset of the lane's A cell, segment origin excluded
             bf16x8 bw[MS][KS];
             bool sl_ok[MS][KS];
+            bool regular = true;  // every phase fills all KS steps with real slots (uniform)
 #pragma unroll
             for (int r2 = 0; r2 < MS; ++r2) {
-                {
-                    const PhaseDesc ph = phase_desc(p, (r0 * a1.S + r1) * S2 + r2);
-                    qn0 = ph.qn[0];
-                    qn1 = ph.qn[1];
-                    qn2[r2] = ph.qn[2];
-                    const int nslots = ph.ntaps * noct;
-                    nkb[r2] = (nslots + 3) >> 2;
+                // record: q counts per axis, then slot base | slot count << 16
+                const int4 rec = precs[(r0 * a1.S + r1) * S2 + r2];
+                qn0 = __builtin_amdgcn_readfirstlane(rec.x);
+                qn1 = __builtin_amdgcn_readfirstlane(rec.y);
+                qn2[r2] = __builtin_amdgcn_readfirstlane(rec.z);
+                qn2min = min(qn2min, qn2[r2]);
+                const int sw = __builtin_amdgcn_readfirstlane(rec.w);
+                const int sbase = sw & 0xffff, nslots = sw >> 16;
+                regular = regular && nslots == 4 * KS;
 #pragma unroll
-                    for (int kb = 0; kb < KS; ++kb) {
-                        const int slot = kb * 4 + kg4;
-                        sl_ok[r2][kb] = kb < nkb[r2] && slot < nslots;
-                        int2 e = make_int2(0, 0);
-                        u32x4 wv = {0u, 0u, 0u, 0u};
-                        if (sl_ok[r2][kb]) {
-                            e = tab[ph.tapbase * noct + slot];
-                            wv = *(const u32x4 *)&wsl[e.y + l16 * Cig];
-                        }
-                        dl[r2][kb] = e.x;
-                        bw[r2][kb] = __builtin_bit_cast(bf16x8, wv);
+                for (int kb = 0; kb < KS; ++kb) {
+                    const int slot = kb * 4 + kg4;
+                    sl_ok[r2][kb] = slot < nslots;
+                    int2 e = make_int2(0, 0);
+                    u32x4 wv = {0u, 0u, 0u, 0u};
+                    if (sl_ok[r2][kb]) {
+                        e = tab[sbase + slot];
+                        wv = *(const u32x4 *)&wsl[e.y + l16 * Cig];
                     }
+                    rd[r2][kb] = (uint32_t)e.x + (uint32_t)l16 * 16;
+                    bw[r2][kb] = __builtin_bit_cast(bf16x8, wv);
                 }
             }
-            if (qd >= qn0) continue;  // uniform: these phases have no output here
-            const int od = a0.S * qd + r0;
-            int mb = 0;
-            for (int ql = 0; ql < R; ++ql) {
-                const int qh = q0h + ql;
-                if (qh >= qn1) break;  // uniform: rows past this residue's q range
-                const uint32_t row_bytes = (uint32_t)(((int64_t)od * a1.O + a1.S * qh + r1) * O2 * 2);
-                for (int seg = 0; seg < nseg; ++seg, ++mb) {
-                    if ((mb & 3) != wave) continue;  // uniform
-                    const int qw = seg * 16 + l16;
-                    const int arow = (ql * HW + qw) * Cig;
-                    f32x4 acc[MS];
+            const int rows = min(R, qn1 - q0h);  // q rows of the tile with outputs here
+            if (qd >= qn0 || rows <= 0) continue;  // uniform
+            const int nitems = rows * nchunk;
+            // segments whose 16 positions are inside every residue's q range;
+            // chunks of only such segments are staged when y takes 16-byte
+            // stores of row pieces
+            const int nfull = min(nseg, qn2min >> 4);
+            const int nstaged = (!pair_dpp && (st_align & kStageOk)) ? nfull / nsc : 0;  // no staging area with DPP pairs
+            const bool seg_b128 = (MS & 1) == 0 && (st_align & 31) >= 16;
+            const uint32_t so0 = (uint32_t)(((int64_t)(a0.S * qd + r0) * a1.O + a1.S * q0h + r1) * O2 * 2);
+            // the chunk loop, instantiated without (regular) and with masks
+            // for the padding slots (A cells of padding slots read as zero)
+            auto run_items = [&](auto pad_tag) __attribute__((always_inline)) {
+                constexpr bool PAD = decltype(pad_tag)::value;
+                int it = wave, ch = ch0;
+                // LDS offset and y offset of the chunk (uniform), advanced with it
+                uint32_t ub = (uint32_t)ql0 * row_lds + (uint32_t)(ch0 * nsc) * seg_lds;
+                uint32_t so = so0 + (uint32_t)ql0 * yrow_bytes + (uint32_t)(ch0 * nsc) * seg_y;
+                while (it < nitems) {  // uniform
+                    const bool staged = ch < nstaged;
+                    for (int s = 0; s < nsc; ++s) {  // uniform
+                        const int seg = ch * nsc + s;
+                        if (seg >= nseg) break;
+                        const uint32_t ubs = ub + (uint32_t)s * seg_lds, sos = so + (uint32_t)s * seg_y;
+                        f32x4 acc[MS];
 #pragma unroll
-                    for (int r2 = 0; r2 < MS; ++r2) {
-                        acc[r2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                        {
+                        for (int r2 = 0; r2 < MS; ++r2) {
+                            acc[r2] = binit;
 #pragma unroll
                             for (int kb = 0; kb < KS; ++kb) {
-                                if (kb < nkb[r2]) {
-                                    u32x4 av = {0u, 0u, 0u, 0u};
-                                    if (sl_ok[r2][kb] && qw < Qw)
-                                        av = *(const u32x4 *)&xs[arow + dl[r2][kb]];
+                                u32x4 av = *(const u32x4 *)(lds + rd[r2][kb] + ubs);
+                                if constexpr (PAD) {
+                                    if (!sl_ok[r2][kb]) av = u32x4{0u, 0u, 0u, 0u};
+                                }
+                                acc[r2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, av), bw[r2][kb], acc[r2], 0, 0, 0);
+                            }
+                        }
+                        // the run's 4*S2 outputs as 2*S2 words (word e2:
+                        // outputs 2*e2, 2*e2 + 1; output index S2*i + r2)
+                        uint32_t pk[2 * MS];
+#pragma unroll
+                        for (int e2 = 0; e2 < 2 * MS; ++e2) {
+                            const int ea = 2 * e2, eb = 2 * e2 + 1;
+                            pk[e2] = pack_bf16x2(acc[ea % S2][ea / S2], acc[eb % S2][eb / S2]);
+                        }
+                        if (staged) {  // uniform
+                            stage_run(pk, stg + st_w + (uint32_t)s * seg_y);
+                            continue;
+                        }
+                        const int q0 = seg * 16;
+                        if (seg_b128 && seg < nfull) {  // uniform: 16-byte runs, all inside
+                            if constexpr ((MS & 1) == 0) {
+#pragma unroll
+                                for (int k = 0; k < MS / 2; ++k)
+                                    __builtin_amdgcn_raw_buffer_store_b128(
+                                        u32x4{pk[4 * k], pk[4 * k + 1], pk[4 * k + 2], pk[4 * k + 3]},
+                                        ys, lane_st + k * 16, sos, 0);
+                            }
+                            continue;
+                        }
+                        const int qb = q0 + 4 * kg4;
+                        bool full = true;  // every output of the lane's run inside the row
+#pragma unroll
+                        for (int r2 = 0; r2 < MS; ++r2) full = full && (qb + 3 < qn2[r2]);
+                        const int al = st_align & 31;
+                        if (full && al >= 8) {
+#pragma unroll
+                            for (int k = 0; k < MS; ++k)
+                                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pk[2 * k], pk[2 * k + 1]}, ys,
+                                                                      lane_st + k * 8, sos, 0);
+                        } else if (full && al >= 4) {
+#pragma unroll
+                            for (int e2 = 0; e2 < 2 * MS; ++e2)
+                                __builtin_amdgcn_raw_buffer_store_b32(pk[e2], ys, lane_st + e2 * 4, sos, 0);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                for (int r2 = 0; r2 < MS; ++r2) {
+                                    const int e = S2 * i + r2;
+                                    if (qb + i < qn2[r2])
+                                        __builtin_amdgcn_raw_buffer_store_b16(
+                                            (uint16_t)(pk[e >> 1] >> (16 * (e & 1))), ys,
+                                            lane_st + e * 2, sos, 0);
+                                }
+                        }
+                    }
+                    if (staged) {  // uniform
+                        // the wave's LDS accesses complete in order: the
+                        // staged runs are read back after their writes, and
+                        // the next chunk's writes follow these reads
+                        asm volatile("" ::: "memory");
+                        for (int ps = 0; ps < npass; ++ps) {  // uniform
+                            const u32x4 v = *(const u32x4 *)(stg + st_r[ps]);
+                            __builtin_amdgcn_raw_buffer_store_b128(v, ys, st_y[ps], so, 0);
+                        }
+                        asm volatile("" ::: "memory");
+                    }
+                    it += 4;
+                    ch += dc;
+                    ub += ub_step;
+                    so += so_step;
+                    if (ch >= nchunk) {
+                        ch -= nchunk;
+                        ub += ub_wrap;
+                        so += so_wrap;
+                    }
+                }
+            };
+            // the common case (every chunk staged, no padding slots): the
+            // chunk loop unrolled over its segments, with immediate offsets
+            auto run_fast = [&](auto nsc_tag) __attribute__((always_inline)) {
+                constexpr int NSC = decltype(nsc_tag)::value;
+                int it = wave, ch = ch0;
+                uint32_t ub = (uint32_t)ql0 * row_lds + (uint32_t)(ch0 * NSC) * seg_lds;
+                uint32_t so = so0 + (uint32_t)ql0 * yrow_bytes + (uint32_t)(ch0 * NSC) * seg_y;
+                unsigned char *sw = stg + st_w;
+                while (it < nitems) {  // uniform
+#pragma unroll
+                    for (int s = 0; s < NSC; ++s) {
+                        f32x4 acc[MS];
+#pragma unroll
+                        for (int r2 = 0; r2 < MS; ++r2) {
+                            acc[r2] = binit;
+#pragma unroll
+                            for (int kb = 0; kb < KS; ++kb) {
+                                const u32x4 av = *(const u32x4 *)(lds + rd[r2][kb] + ub + s * 256);
+                                acc[r2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, av), bw[r2][kb], acc[r2], 0, 0, 0);
+                            }
+                        }
+                        uint32_t pk[2 * MS];
+#pragma unroll
+                        for (int e2 = 0; e2 < 2 * MS; ++e2) {
+                            const int ea = 2 * e2, eb = 2 * e2 + 1;
+                            pk[e2] = pack_bf16x2(acc[ea % S2][ea / S2], acc[eb % S2][eb / S2]);
+                        }
+                        stage_run(pk, sw + s * 32 * S2);
+                    }
+                    // the wave's LDS accesses complete in order: the staged
+                    // runs are read back after their writes, and the next
+                    // chunk's writes follow these reads
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4 *)(stg + st_r[0]), ys, st_y[0], so, 0);
+                    if (npass > 1)
+                        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4 *)(stg + st_r[1]), ys, st_y[1],
+                                                               so, 0);
+                    asm volatile("" ::: "memory");
+                    it += 4;
+                    ch += dc;
+                    ub += ub_step;
+                    so += so_step;
+                    if (ch >= nchunk) {
+                        ch -= nchunk;
+                        ub += ub_wrap;
+                        so += so_wrap;
+                    }
+                }
+            };
+            if constexpr (MS == 2 && KS >= 1) {
+                if (pair_dpp && regular && (st_align & kStageOk) && nfull == nseg) {  // uniform
+                    // segment pairs: the second segment's runs move into lanes
+                    // 8..15 of each 16-lane row (the padding channels), then the
+                    // lanes are permuted so that one 16-byte store writes 8
+                    // channels x one whole 128-byte row, 8 lanes per row
+                    int it = wave, ch = ch0;
+                    uint32_t ub = (uint32_t)ql0 * row_lds + (uint32_t)(ch0 * 2) * seg_lds;
+                    uint32_t so = so0 + (uint32_t)ql0 * yrow_bytes + (uint32_t)(ch0 * 2) * seg_y;
+                    while (it < nitems) {  // uniform
+                        u32x4 pr[2];
+#pragma unroll
+                        for (int s = 0; s < 2; ++s) {
+                            f32x4 acc[MS];
+#pragma unroll
+                            for (int r2 = 0; r2 < MS; ++r2) {
+                                acc[r2] = binit;
+#pragma unroll
+                                for (int kb = 0; kb < KS; ++kb) {
+                                    const u32x4 av = *(const u32x4 *)(lds + rd[r2][kb] + ub + s * 256);
                                     acc[r2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                         __builtin_bit_cast(bf16x8, av), bw[r2][kb], acc[r2], 0, 0, 0);
                                 }
                             }
+#pragma unroll
+                            for (int e2 = 0; e2 < 4; ++e2)
+                                pr[s][e2] = pack_bf16x2(acc[(2 * e2) % 2][(2 * e2) / 2],
+                                                        acc[(2 * e2 + 1) % 2][(2 * e2 + 1) / 2]);
+                        }
+                        // row_ror:8 (lane i of a row takes lane i - 8), written
+                        // to lanes 8..15 of each row only (bank mask 0b1100)
+                        u32x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = __builtin_amdgcn_update_dpp((int)pr[0][e], (int)pr[1][e], 0x128, 0xf,
+                                                                      0xc, false);
+                            v[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(bp_src, m);
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b128(v, ys, dpp_st, so, 0);
+                        it += 4;
+                        ch += dc;
+                        ub += ub_step;
+                        so += so_step;
+                        if (ch >= nchunk) {
+                            ch -= nchunk;
+                            ub += ub_wrap;
+                            so += so_wrap;
                         }
                     }
-                    // lane: positions q = qb + i (i < 4), outputs ow = S2*q + r2
-                    const int qb = seg * 16 + 4 * kg4;
-                    const uint32_t base = co_bytes + row_bytes + (uint32_t)(S2 * qb) * 2;
-                    bool full = true;  // every output of the run inside the row
-#pragma unroll
-                    for (int r2 = 0; r2 < MS; ++r2)
-                        full = full && (qb + 3 < qn2[r2]);
-                    if (full && row_pairs) {
-                        // 4*S2 consecutive outputs as 2*S2 dwords
-#pragma unroll
-                        for (int e2 = 0; e2 < 2 * MS; ++e2) {
-                            {
-                                const int ea = 2 * e2, eb = 2 * e2 + 1;  // output indices S2*i + r2
-                                const float va = acc[ea % S2][ea / S2] + bvf;
-                                const float vb = acc[eb % S2][eb / S2] + bvf;
-                                const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)va) |
-                                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)vb) << 16);
-                                __builtin_amdgcn_raw_buffer_store_b32(pk, ys, base + e2 * 4, 0, 0);
-                            }
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int r2 = 0; r2 < MS; ++r2)
-                                if (qb + i < qn2[r2])
-                                    __builtin_amdgcn_raw_buffer_store_b16(
-                                        __builtin_bit_cast(uint16_t, (__bf16)(acc[r2][i] + bvf)), ys,
-                                        base + (S2 * i + r2) * 2, 0, 0);
-                    }
+                    continue;
                 }
             }
+            if (regular && nstaged == nchunk && nsc == 1)
+                run_fast(IntTag<1>{});
+            else if (regular && nstaged == nchunk && nsc == 2)
+                run_fast(IntTag<2>{});
+            else if (regular && nstaged == nchunk && nsc == 4)
+                run_fast(IntTag<4>{});
+            else if (regular)
+                run_items(BoolTag<false>{});
+            else
+                run_items(BoolTag<true>{});
         }
     }
 }
 
+static GrpArgs grp_args(const DevParams &p) {
+    GrpArgs a;
+    for (int i = 0; i < 3; ++i) a.ax[i] = GrpAxis{p.ax[i].I, p.ax[i].O, p.ax[i].S, p.ax[i].umin};
+    a.G = p.G; a.Ci = p.Ci; a.Co = p.Co; a.Cig = p.Cig; a.Cog = p.Cog; a.has_bias = p.has_bias;
+    a.x_plane = p.x_plane; a.y_plane = p.y_plane;
+    a.th = p.th; a.tw = p.tw; a.hd = p.hd; a.hh = p.hh; a.hw = p.hw;
+    a.grp_hwp = p.grp_hwp; a.grp_hshift = p.grp_hshift; a.grp_nk = p.grp_nk; a.grp_nsc = p.grp_nsc;
+    a.grp_w_off = p.grp_w_off; a.grp_tab_off = p.grp_tab_off; a.grp_st_off = p.grp_st_off;
+    a.grp_st_pitch = p.grp_st_pitch;
+    a.ktot = p.ktot; a.nphase = p.nphase;
+    return a;
+}
+
 template <int S2, int KS>
-static void launch_grouped_t(const DevParams &p, const void *x, const void *wr, const void *bias,
-                             void *y, hipStream_t stream) {
-    hipLaunchKernelGGL((grouped_kernel<S2, KS>), dim3(p.n_blocks), dim3(256), (size_t)p.grp_lds_bytes,
-                       stream, p, (const uint16_t *)x, (const uint16_t *)wr, (const uint16_t *)bias,
-                       (uint16_t *)y);
+static void launch_grouped_t(const DevParams &p, const void *x, const void *wr, const int2 *gtab,
+                             const void *bias, void *y, int st_align, int x_vec, hipStream_t stream) {
+    hipLaunchKernelGGL((grouped_kernel<S2, KS>), dim3(p.G * p.B, p.nt_h, p.nt_d), dim3(256),
+                       (size_t)p.grp_lds_bytes, stream, grp_args(p), (const uint16_t *)x,
+                       (const uint16_t *)wr, gtab, (const uint16_t *)bias, (uint16_t *)y, st_align, x_vec);
 }
 
 template <int S2>
 static hipError_t launch_grouped_s(const DevParams &p, const void *x, const void *wr,
-                                   const void *bias, void *y, hipStream_t stream) {
+                                   const int2 *gtab, const void *bias, void *y, int st_align,
+                                   int x_vec, hipStream_t stream) {
     switch (p.grp_ksteps) {
-        case 1: launch_grouped_t<S2, 1>(p, x, wr, bias, y, stream); break;
-        case 2: launch_grouped_t<S2, 2>(p, x, wr, bias, y, stream); break;
-        case 4: launch_grouped_t<S2, 4>(p, x, wr, bias, y, stream); break;
+        case 1: launch_grouped_t<S2, 1>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
+        case 2: launch_grouped_t<S2, 2>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
+        case 4: launch_grouped_t<S2, 4>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipSuccess;
@@ -289,12 +613,31 @@ hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const v
                           hipStream_t stream) {
     const DevParams &p = pl.dp;
     if (p.n_blocks <= 0) return hipSuccess;
+    // Widest store (bytes) that every output run starts aligned to: a run of
+    // 4*S2 outputs starts at 8*S2*(q/4) bytes into a row; rows and channel
+    // planes start at multiples of 2*O_w bytes from y.
+    const int S2 = p.ax[2].S;
+    int st_align = 2;
+    for (int a = 16; a >= 4; a /= 2) {
+        if ((uintptr_t)y % a == 0 && (2 * (int64_t)p.ax[2].O) % a == 0 && (8 * S2) % a == 0) {
+            st_align = a;
+            break;
+        }
+    }
+    // staged chunks leave as 16-byte pieces of rows
+    if ((uintptr_t)y % 16 == 0 && (2 * (int64_t)p.ax[2].O) % 16 == 0) st_align |= kStageOk;
+    // chunked halo gather: x rows are whole 16-byte chunks (the plan then
+    // gives the halo rows whole chunks of columns)
+    const int x_vec = (uintptr_t)x % 16 == 0 && p.grp_nk > 0;
+    const int2 *gtab = (const int2 *)((const char *)wr + pl.tab_offset);
+    if ((int64_t)p.G * p.B > 0x7fffffff || p.nt_h > 65535 || p.nt_d > 65535)
+        return hipErrorInvalidConfiguration;
     hipError_t e;
-    switch (p.ax[2].S) {
-        case 1: e = launch_grouped_s<1>(p, x, wr, bias, y, stream); break;
-        case 2: e = launch_grouped_s<2>(p, x, wr, bias, y, stream); break;
-        case 3: e = launch_grouped_s<3>(p, x, wr, bias, y, stream); break;
-        case 4: e = launch_grouped_s<4>(p, x, wr, bias, y, stream); break;
+    switch (S2) {
+        case 1: e = launch_grouped_s<1>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
+        case 2: e = launch_grouped_s<2>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
+        case 3: e = launch_grouped_s<3>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
+        case 4: e = launch_grouped_s<4>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

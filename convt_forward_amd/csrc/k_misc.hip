@@ -23,11 +23,44 @@ namespace convt {
 // reads it with consecutive lanes on consecutive elements into LDS; each lane
 // then assembles whole destination vectors (VEC channels of one (tap, co))
 // and writes them with one 16-byte store.
+//
+// Block 0 also writes the grouped kernel's slot table: first one int4
+// record per phase P (its q counts per axis, then the index of its first
+// slot | its slot count << 16), then per phase and slot (tap, 8-channel
+// slice), at index tapbase(P) * slices + slot, the byte offset of the tap's
+// window origin in that kernel's LDS halo, [halo row][slice][column] of
+// 16-byte cells with hh rows per depth plane, grp_hwp cells per row and halo
+// position 0 at column grp_hshift, and the element offset of (tap, co 0,
+// slice) in the group's Wr slab.
 // ---------------------------------------------------------------------------
+__device__ void grouped_slot_table(const DevParams &p, int2 *__restrict__ gtab) {
+    const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
+    const int noct = p.Cig >> 3, HH = p.hh, HWP = p.grp_hwp;
+    int2 *tab = gtab + 2 * p.nphase;
+    for (int P = 0; P < p.nphase; ++P) {
+        const PhaseDesc ph = phase_desc(p, P);
+        const int nslots = ph.ntaps * noct;
+        if (threadIdx.x == 0)
+            ((int4 *)gtab)[P] = make_int4(ph.qn[0], ph.qn[1], ph.qn[2], ph.tapbase * noct | nslots << 16);
+        const int n1 = ph.n[1], n2 = ph.n[2];
+        for (int sl = threadIdx.x; sl < nslots; sl += blockDim.x) {
+            const int tap = sl / noct, oct = sl - tap * noct;
+            const int j2 = tap % n2, j1 = (tap / n2) % n1, j0 = tap / (n2 * n1);
+            const int hrow = (ph.off0[0] - a0.umin + j0 * a0.ostep) * HH +
+                             (ph.off0[1] - a1.umin + j1 * a1.ostep);
+            const int col = ph.off0[2] - a2.umin + j2 * a2.ostep + p.grp_hshift;
+            tab[ph.tapbase * noct + sl] = make_int2(((hrow * noct + oct) * HWP + col) * 16,
+                                                    (ph.tapbase + tap) * tiles::kGrpCog * p.Cig + oct * 8);
+        }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__restrict__ w,
-                                                       T *__restrict__ wr, int ocb) {
+                                                       T *__restrict__ wr, int ocb,
+                                                       int2 *__restrict__ gtab) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    if (blockIdx.x == 0 && gtab != nullptr) grouped_slot_table(p, gtab);
     T *brick = (T *)lds_raw;
     constexpr int VEC = 16 / sizeof(T);
     const int ktot = p.ktot;
@@ -292,12 +325,13 @@ hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t s
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)16 * ocb * p.ktot;
     if (lds > 65536) return hipErrorInvalidConfiguration;
+    int2 *gtab = pl.route == CONVT_ROUTE_GROUPED ? (int2 *)((char *)wr + pl.tab_offset) : nullptr;
     if (pl.elem_bytes == 2)
         hipLaunchKernelGGL(reorder_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds, stream,
-                           p, (const uint16_t *)w, (uint16_t *)wr, ocb);
+                           p, (const uint16_t *)w, (uint16_t *)wr, ocb, gtab);
     else
         hipLaunchKernelGGL(reorder_kernel<float>, dim3((unsigned)blocks), dim3(256), lds, stream, p,
-                           (const float *)w, (float *)wr, ocb);
+                           (const float *)w, (float *)wr, ocb, gtab);
     return hipGetLastError();
 }
 

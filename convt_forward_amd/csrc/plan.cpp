@@ -261,41 +261,77 @@ bool gemm_eligible(const DevParams &dp, int dtype, int ndim) {
 bool choose_grouped_tile(DevParams *dp) {
     const DevAxis &ad = dp->ax[0], &ah = dp->ax[1], &aw = dp->ax[2];
     // the halo covers the union of every phase's input window
-    const int64_t hw = aw.qmax + (aw.umax - aw.umin);
+    const int64_t span_w = aw.umax - aw.umin;
+    const int64_t hw = aw.qmax + span_w;
     const int64_t hd = 1 + (ad.umax - ad.umin);
+    // Halo row columns: input position i at column i - pmin, so halo
+    // position 0 (input position umin) is at column hshift. The pitch covers
+    // every column a 16-position segment reads and, when x rows are whole
+    // 8-position (16-byte) chunks that the kernel copies as such, the whole
+    // input row; columns of positions outside the row hold zeros. An odd
+    // pitch puts the same column of neighbouring rows (and slices) on
+    // different LDS banks.
+    const int64_t pmin = std::min<int64_t>(aw.umin, 0);
+    const int64_t hshift = aw.umin - pmin;
+    const int64_t nk = aw.I % 8 == 0 ? aw.I / 8 : 0;
+    const int64_t hwp =
+        std::max<int64_t>(hshift + ceil_div(aw.qmax, 16) * 16 + span_w, nk ? aw.I - pmin : 0) | 1;
+    // Output staging, per wave: a chunk of nsc segments of one output row for
+    // every channel of the group (16 * S2 outputs per segment), aiming at
+    // 1 KiB per store instruction; rows padded by 16 bytes against bank
+    // conflicts.
+    const int64_t seg_bytes = 32 * aw.S;
+    const int64_t nseg = ceil_div(aw.qmax, 16);
+    const int64_t nsc_max = std::min<int64_t>(nseg, 1024 / (std::max(dp->Cog, 1) * seg_bytes));
+    const int64_t nsc = nsc_max >= 4 ? 4 : nsc_max >= 2 ? 2 : 1;  // the kernel's unrolled sizes
+    const int64_t st_pitch = nsc * seg_bytes + 16;
+    // (one more row per wave takes the padding lanes' writes). Width stride
+    // 2 with at most 8 channels per group and whole segment pairs needs no
+    // staging: the kernel moves a pair's second segment into the padding
+    // lanes (DPP) and stores whole 128-byte rows straight from registers.
+    const bool pair_dpp = aw.S == 2 && dp->Cog <= 8 && nseg % 2 == 0;
+    const int64_t st_bytes =
+        pair_dpp ? 0 : (int64_t)tiles::kGrpThreads / 64 * (dp->Cog + 1) * st_pitch;
     auto al = [](int64_t v) { return (v + 15) / 16 * 16; };
     const int64_t w_bytes = (int64_t)dp->ktot * tiles::kGrpCog * dp->Cig * 2;
-    // K-slot table: (halo offset, weight offset) per (tap, 8-channel slice)
-    const int64_t tab_bytes = (int64_t)dp->ktot * (dp->Cig / 8) * 8;
+    // slot table: a 16-byte record per phase, then (halo offset, weight
+    // offset) per (tap, 8-channel slice)
+    const int64_t tab_bytes = 16 * (int64_t)dp->nphase + (int64_t)dp->ktot * (dp->Cig / 8) * 8;
     int best = 0;
     int64_t best_halo = 0;
     for (int rows = 1; rows <= 64; rows *= 2) {
         if (rows > ah.qmax && rows > 1) break;
         const int64_t hh = rows + (ah.umax - ah.umin);
-        const int64_t halo_bytes = hd * hh * hw * dp->Cig * 2;
+        const int64_t halo_bytes = hd * hh * hwp * dp->Cig * 2;
         if (halo_bytes > tiles::kGrpHaloBytes ||
-            al(halo_bytes) + al(w_bytes) + al(tab_bytes) > tiles::kGrpLdsBudget)
+            al(halo_bytes) + al(w_bytes) + al(tab_bytes) + st_bytes > tiles::kGrpLdsBudget)
             break;
         best = rows;
         best_halo = halo_bytes;
         if ((int64_t)rows * aw.qmax >= tiles::kGrpMinPositions) break;
     }
     if (!best || w_bytes > tiles::kGrpWBytes) return false;
+    // the kernel's grid is (G * B, row tiles, q depths)
+    if (ceil_div(ah.qmax, best) > 65535 || ad.qmax > 65535 || (int64_t)dp->G * dp->B > 0x7fffffff)
+        return false;
     dp->td = 1;
     dp->th = best;
     dp->tw = aw.qmax;
     dp->hd = (int32_t)hd;
     dp->hh = best + (ah.umax - ah.umin);
     dp->hw = (int32_t)hw;
+    dp->grp_hwp = (int32_t)hwp;
+    dp->grp_hshift = (int32_t)hshift;
+    dp->grp_nk = (int32_t)nk;
+    dp->grp_nsc = pair_dpp ? 0 : (int32_t)nsc;  // 0: segment pairs through DPP
+    dp->grp_st_pitch = (int32_t)st_pitch;
     dp->nt_d = ad.qmax;
     dp->nt_h = (int32_t)ceil_div(ah.qmax, best);
     dp->nt_w = 1;
-    dp->out_rows = best * ah.S;
-    dp->grp_out_cstride = 0;
     dp->grp_w_off = (int32_t)al(best_halo);
-    dp->grp_out_off = 0;
     dp->grp_tab_off = (int32_t)(al(best_halo) + al(w_bytes));
-    dp->grp_lds_bytes = (int32_t)(al(best_halo) + al(w_bytes) + al(tab_bytes));
+    dp->grp_st_off = (int32_t)(al(best_halo) + al(w_bytes) + al(tab_bytes));
+    dp->grp_lds_bytes = (int32_t)(dp->grp_st_off + st_bytes);
     return true;
 }
 
@@ -494,7 +530,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     }
     if (blocks > i31) return CONVT_ERR_UNSUPPORTED;
     dp.n_blocks = (int32_t)blocks;
-    dp.xcd_remap = (blocks % 8 == 0) ? 1 : 0;
+    // the grouped kernel runs a 3-D grid in plain order
+    dp.xcd_remap = (blocks % 8 == 0 && route != CONVT_ROUTE_GROUPED) ? 1 : 0;
     if (route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_GROUPED) {
         int64_t wr;
         const int64_t taps = route == CONVT_ROUTE_PHASE_GEMM ? dp.ktot_pad : ktot;
@@ -506,6 +543,11 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
             // the per-tap halo shift table (int32 per padded tap of a group)
             pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
             info.workspace_bytes = pl->tab_offset + (int64_t)dp.ktot_pad * 4;
+        } else {
+            // the grouped kernel's slot table: a 16-byte record per phase,
+            // then (halo byte offset, weight offset) per (tap, 8-channel slice)
+            pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
+            info.workspace_bytes = pl->tab_offset + 16 * (int64_t)dp.nphase + (int64_t)ktot * (Cig / 8) * 8;
         }
         if (route == CONVT_ROUTE_PHASE_GEMM && dt == CONVT_DTYPE_BF16) {
             // the channel-chunked copy of x: [B][G][chunk][position][32 bytes]

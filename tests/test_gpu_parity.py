@@ -186,6 +186,13 @@ GROUPED = [
     ((1, 24, 3, 4, 5), (24, 4, 3, 2, 2), (2, 1, 2), (1, 0, 1), (1, 1, 1), (1, 0, 0), 1),
     ((2, 32, 8, 8), (32, 8, 4, 4), (1, 1), (1, 1), (1, 1), (0, 0), 4),
     ((1, 16, 4, 33), (16, 16, 2, 4), (4, 2), (0, 1), (1, 1), (3, 1), 2),
+    # input rows of whole 16-byte chunks (the chunked halo gather): borders,
+    # chunks left of the row (dilation 5), width strides 1..4, 3-D
+    ((2, 16, 5, 16), (16, 4, 3, 3), (2, 2), (1, 1), (1, 1), (1, 1), 2),
+    ((1, 32, 3, 24), (32, 8, 4, 5), (1, 3), (2, 3), (1, 1), (0, 2), 2),
+    ((1, 64, 4, 8, 16), (64, 2, 2, 3, 4), (2, 2, 4), (0, 1, 1), (1, 1, 1), (0, 0, 3), 8),
+    ((1, 16, 6, 16), (16, 8, 3, 3), (1, 1), (0, 0), (5, 5), (0, 0), 2),
+    ((3, 32, 9, 40), (32, 8, 4, 4), (2, 2), (1, 1), (1, 1), (0, 0), 4),
 ]
 
 

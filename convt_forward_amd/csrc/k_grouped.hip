@@ -93,8 +93,12 @@ struct GrpArgs {
     int32_t ktot, nphase;
 };
 
+// Eight waves per SIMD (8 blocks per CU) where the registers allow it: the
+// scalar registers are capped too, since more of them than the cap admits
+// keep blocks from being resident. Instances with more weight fragments in
+// registers (S2 * KS > 2) trade occupancy for having no spills.
 template <int S2, int KS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void grouped_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 2 ? 8 : 4, 8))) void grouped_kernel(
     GrpArgs p, const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const int2 *__restrict__ gtab, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
     int st_align, int x_vec) {
@@ -119,20 +123,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     // 1a. the group's weights [tap][16][Cig] and the slot table (written
     // with the reordered weights: a record per phase, then per (tap, slice)
     // slot the LDS byte offset of the tap's window origin in the halo and the
-    // weight offset) -> LDS. Their loads go out first; the halo loads follow.
+    // weight offset) -> LDS by DMA, in 1 KiB and 256-byte pieces dealt to the
+    // waves (their areas are whole pieces); the halo follows.
     const int nvec = p.ktot * tiles::kGrpCog * noct, nslot = 2 * p.nphase + p.ktot * noct;
-    const u32x4 *wsrc = (const u32x4 *)(wr + (int64_t)g * p.ktot * tiles::kGrpCog * Cig);
-    u32x4 *wdst = (u32x4 *)(lds + p.grp_w_off);
-    int2 *tdst = (int2 *)(lds + p.grp_tab_off);
-    const bool w_one = nvec <= 256 && nslot <= 256;  // one of each per thread at most (uniform)
-    u32x4 wv = {0u, 0u, 0u, 0u};
-    int2 tv = make_int2(0, 0);
-    if (w_one) {  // loaded here, written to LDS after the halo
-        if (tid < nvec) wv = wsrc[tid];
-        if (tid < nslot) tv = gtab[tid];
-    } else {
-        for (int v = tid; v < nvec; v += 256) wdst[v] = wsrc[v];
-        for (int v = tid; v < nslot; v += 256) tdst[v] = gtab[v];
+    {
+        const u32x4 wrw = rsrc_words(wr + (int64_t)g * p.ktot * tiles::kGrpCog * Cig, (uint32_t)nvec * 16);
+        const uint32_t w_lds =
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(lds + p.grp_w_off);
+        for (int j = wave; j * 64 < nvec; j += 4)  // uniform
+            copy_to_lds<16>(w_lds + (uint32_t)j * 1024, (uint32_t)(j * 64 + lane) * 16, wrw);
+        const u32x4 trw = rsrc_words(gtab, (uint32_t)nslot * 8);
+        const uint32_t t_lds =
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(lds + p.grp_tab_off);
+        for (int j = wave; j * 64 < 2 * nslot; j += 4)  // uniform
+            copy_to_lds<4>(t_lds + (uint32_t)j * 256, (uint32_t)(j * 64 + lane) * 4, trw);
     }
     // 1b. input halo -> LDS cells; positions outside the input read an
     // out-of-range offset (zero).
@@ -140,12 +144,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(x + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane), (short)0,
         (int)((uint32_t)Cig * xpl_bytes), kGrpRsrcWord3);
+    const int nk = p.grp_nk, col0 = p.grp_hshift - a2.umin;
+    if (x_vec) {  // uniform
+        // zero cells: columns left of the row (col0 of them) and right of it
+        const int zl = col0, zn = HWP - a2.I;
+        const int zunits = nrow * noct * zn;
+        for (int u = tid; u < zunits; u += 256) {
+            const int ro = u / zn, z = u - ro * zn;
+            const int col = z < zl ? z : z + a2.I;
+            *(u32x4 *)(lds + (ro * HWP + col) * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
     if (x_vec) {  // uniform
         // unit = (halo row, slice, chunk k of 8 input positions 8k .. 8k+7),
         // whose cells are columns col0 + 8k .. +7 of the row; rows outside the
         // input read zero. Neighbouring lanes take neighbouring rows, whose
         // cells the odd row pitch spreads over the LDS banks.
-        const int nk = p.grp_nk, col0 = p.grp_hshift - a2.umin;
         const int units = nrow * noct * nk;
         for (int u = tid; u < units; u += 256) {
             const int row = u % nrow, t = u / nrow;
@@ -170,14 +184,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                                                     (e & 1) ? kPermHi : kPermLo);
                 *(u32x4 *)(dst + e * 16) = cell;
             }
-        }
-        // zero cells: columns left of the row (col0 of them) and right of it
-        const int zl = col0, zn = HWP - a2.I;
-        const int zunits = nrow * noct * zn;
-        for (int u = tid; u < zunits; u += 256) {
-            const int ro = u / zn, z = u - ro * zn;
-            const int col = z < zl ? z : z + a2.I;
-            *(u32x4 *)(lds + (ro * HWP + col) * 16) = u32x4{0u, 0u, 0u, 0u};
         }
     } else {
         // Element loads: a wave takes whole halo rows (one slice each) and its
@@ -240,13 +246,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             }
         }
     }
-    if (w_one) {
-        if (tid < nvec) wdst[tid] = wv;
-        if (tid < nslot) tdst[tid] = tv;
-    }
     const int4 *precs = (const int4 *)(lds + p.grp_tab_off);
     const int2 *tab = (const int2 *)(lds + p.grp_tab_off + 16 * p.nphase);
-    __syncthreads();
+    // every wave's copies (weights, table; halo without DMA) have landed and
+    // the cells are written
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // 2. Per (depth residue, height residue) pair, each wave takes chunks of
     // nsc 16-position segments of the block's q rows in turn. For a segment
@@ -316,6 +320,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     auto stage_run = [](const uint32_t *pk, unsigned char *w) __attribute__((always_inline)) {
         stage_run_t<S2>(pk, w);
     };
+    // the tile's q rows [rlo, rhi), every phase
+    auto compute_rows = [&](int rlo, int rhi) __attribute__((always_inline)) {
+    const int qb0 = rlo + ql0;  // this wave's first row
     for (int r0 = 0; r0 < a0.S; ++r0) {
         for (int r1 = 0; r1 < a1.S; ++r1) {
             // phases (r0, r1, r2 < S2): their records and this lane's K slots
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                     bw[r2][kb] = __builtin_bit_cast(bf16x8, wv);
                 }
             }
-            const int rows = min(R, qn1 - q0h);  // q rows of the tile with outputs here
+            const int rows = min(rhi, qn1 - q0h) - rlo;  // q rows of the range with outputs here
             if (qd >= qn0 || rows <= 0) continue;  // uniform
             const int nitems = rows * nchunk;
             // segments whose 16 positions are inside every residue's q range;
@@ -365,8 +372,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                 constexpr bool PAD = decltype(pad_tag)::value;
                 int it = wave, ch = ch0;
                 // LDS offset and y offset of the chunk (uniform), advanced with it
-                uint32_t ub = (uint32_t)ql0 * row_lds + (uint32_t)(ch0 * nsc) * seg_lds;
-                uint32_t so = so0 + (uint32_t)ql0 * yrow_bytes + (uint32_t)(ch0 * nsc) * seg_y;
+                uint32_t ub = (uint32_t)qb0 * row_lds + (uint32_t)(ch0 * nsc) * seg_lds;
+                uint32_t so = so0 + (uint32_t)qb0 * yrow_bytes + (uint32_t)(ch0 * nsc) * seg_y;
                 while (it < nitems) {  // uniform
                     const bool staged = ch < nstaged;
                     for (int s = 0; s < nsc; ++s) {  // uniform
@@ -464,8 +471,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
             auto run_fast = [&](auto nsc_tag) __attribute__((always_inline)) {
                 constexpr int NSC = decltype(nsc_tag)::value;
                 int it = wave, ch = ch0;
-                uint32_t ub = (uint32_t)ql0 * row_lds + (uint32_t)(ch0 * NSC) * seg_lds;
-                uint32_t so = so0 + (uint32_t)ql0 * yrow_bytes + (uint32_t)(ch0 * NSC) * seg_y;
+                uint32_t ub = (uint32_t)qb0 * row_lds + (uint32_t)(ch0 * NSC) * seg_lds;
+                uint32_t so = so0 + (uint32_t)qb0 * yrow_bytes + (uint32_t)(ch0 * NSC) * seg_y;
                 unsigned char *sw = stg + st_w;
                 while (it < nitems) {  // uniform
 #pragma unroll
@@ -516,8 +523,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                     // lanes are permuted so that one 16-byte store writes 8
                     // channels x one whole 128-byte row, 8 lanes per row
                     int it = wave, ch = ch0;
-                    uint32_t ub = (uint32_t)ql0 * row_lds + (uint32_t)(ch0 * 2) * seg_lds;
-                    uint32_t so = so0 + (uint32_t)ql0 * yrow_bytes + (uint32_t)(ch0 * 2) * seg_y;
+                    uint32_t ub = (uint32_t)qb0 * row_lds + (uint32_t)(ch0 * 2) * seg_lds;
+                    uint32_t so = so0 + (uint32_t)qb0 * yrow_bytes + (uint32_t)(ch0 * 2) * seg_y;
                     while (it < nitems) {  // uniform
                         u32x4 pr[2];
 #pragma unroll
@@ -573,6 +580,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
                 run_items(BoolTag<true>{});
         }
     }
+    };
+    compute_rows(0, R);
 }
 
 static GrpArgs grp_args(const DevParams &p) {

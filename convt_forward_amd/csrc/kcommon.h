@@ -105,4 +105,71 @@ __device__ __forceinline__ int tap_in_table(const DevParams &p, int k0, int k1, 
     return p.ph[P].tapbase + (j[0] * n[1] + j[1]) * n[2] + j[2];
 }
 
+// ---- raw buffers and global -> LDS copies (phase GEMM, grouped kernel) ----
+
+// Buffer resource word 3 for gfx9-family raw buffers.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+// A byte offset that is out of range for every resource used here (each
+// covers less than 2^31 bytes), also after adding a tap or chunk offset.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             (int)kRsrcWord3);
+}
+
+// The same resource as four scalar words, for the copy instructions below.
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = kRsrcWord3;
+    return r;
+}
+
+
+// Global -> LDS copies: every lane reads BYTES at its offset in the resource
+// and writes them at lds + lane * max(BYTES, 4). Out-of-range reads write
+// zeros. Issued as plain instructions so that the compiler neither waits for
+// them nor reorders them with the barriers; completion is awaited by the
+// counts of stage_barrier. They set M0, a register the compiler reserves and
+// does not otherwise use in the kernels that call these.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(uint32_t lds, uint32_t voff, const u32x4 &rs) {
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     ::"s"(lds), "v"(voff), "s"(rs));
+    else if constexpr (BYTES == 4)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     ::"s"(lds), "v"(voff), "s"(rs));
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
+                     ::"s"(lds), "v"(voff), "s"(rs));
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// and its LDS operations are done, then join the block's barrier. The
+// memory clobber keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// The same with a wave-uniform count n (clamped to MAXN).
+template <int MAXN>
+__device__ __forceinline__ void stage_barrier_n(int n) {
+    if constexpr (MAXN > 0) {
+        if (n >= MAXN) {
+            stage_barrier<MAXN>();
+            return;
+        }
+        stage_barrier_n<MAXN - 1>(n);
+    } else {
+        stage_barrier<0>();
+    }
+}
+
+
 }  // namespace convt

@@ -293,10 +293,13 @@ bool choose_grouped_tile(DevParams *dp) {
     const int64_t st_bytes =
         pair_dpp ? 0 : (int64_t)tiles::kGrpThreads / 64 * (dp->Cog + 1) * st_pitch;
     auto al = [](int64_t v) { return (v + 15) / 16 * 16; };
-    const int64_t w_bytes = (int64_t)dp->ktot * tiles::kGrpCog * dp->Cig * 2;
+    // the weights and the slot table reach LDS by DMA in 1 KiB and 256-byte
+    // pieces: their areas are whole pieces
+    const int64_t w_bytes = ((int64_t)dp->ktot * tiles::kGrpCog * dp->Cig * 2 + 1023) / 1024 * 1024;
     // slot table: a 16-byte record per phase, then (halo offset, weight
     // offset) per (tap, 8-channel slice)
-    const int64_t tab_bytes = 16 * (int64_t)dp->nphase + (int64_t)dp->ktot * (dp->Cig / 8) * 8;
+    const int64_t tab_bytes =
+        (16 * (int64_t)dp->nphase + (int64_t)dp->ktot * (dp->Cig / 8) * 8 + 255) / 256 * 256;
     int best = 0;
     int64_t best_halo = 0;
     for (int rows = 1; rows <= 64; rows *= 2) {
@@ -310,7 +313,7 @@ bool choose_grouped_tile(DevParams *dp) {
         best_halo = halo_bytes;
         if ((int64_t)rows * aw.qmax >= tiles::kGrpMinPositions) break;
     }
-    if (!best || w_bytes > tiles::kGrpWBytes) return false;
+    if (!best || (int64_t)dp->ktot * tiles::kGrpCog * dp->Cig * 2 > tiles::kGrpWBytes) return false;
     // the kernel's grid is (G * B, row tiles, q depths)
     if (ceil_div(ah.qmax, best) > 65535 || ad.qmax > 65535 || (int64_t)dp->G * dp->B > 0x7fffffff)
         return false;

@@ -98,34 +98,38 @@ struct Plan {
 // Tile constants of the kernels, shared with the planner so that it sizes
 // grids and halos the way the kernels expect.
 namespace tiles {
-// Phase GEMM: tile configurations (block = 256 threads, 4 waves as WGM x 4/WGM,
-// two blocks per CU). BM output channels x BN positions per block. A K chunk
+// Phase GEMM: tile configurations. A block has nw waves (4: two blocks
+// share a CU and cover each other's barrier waits; one 8-wave block per CU
+// measured slower, its waves all meeting at every barrier), laid out as
+// WGM x nw/WGM; each wave holds
+// a 32-aligned sub-tile of the BM output channels x BN positions. A K chunk
 // is 32 bytes of input channels (16 bfloat16 or 8 float32); a pipeline stage
 // covers SC consecutive chunks and gs (1..4) taps. The weight tiles of a
 // stage stream through a ring of kGemmWRing LDS buffers of 32-byte rows; the
 // input halo of SC chunks (HALO positions at most) streams through a ring of
-// xb buffers that share the rest of the block's LDS budget:
+// xb buffers that share the rest of the block's LDS budget (20 KiB per wave:
+// a CU's 160 KiB over its 8 resident waves):
 // bfloat16 as one 32-byte row per position (from the channel-chunked copy of
 // x), float32 as one row of 4-byte elements per channel (straight from x).
 struct GemmTile {
     int bm, bn, wgm, bf16, sc, xb;  // xb: halo ring buffers (3: two groups in flight, 2: one)
+    int nw;                         // waves per block (4 or 8)
 };
-constexpr int kGemmThreads = 256;
-constexpr int kGemmWaves = 4;
-constexpr int kGemmLdsBudget = 80 * 1024;  // per block: two blocks share a CU
+constexpr int kGemmLdsPerWave = 20 * 1024;
 constexpr int kGemmTapGroup = 4;   // taps per pipeline stage, at most (the planner picks 1..4)
 constexpr int kGemmWRing = 3;      // weight-tile buffers: two stages in flight
 constexpr int kGemmWRowBytes = 32; // weight row: one chunk of channels
 constexpr int kGemmCfgCount = 7;
 constexpr GemmTile kGemmCfg[kGemmCfgCount] = {
-    {128, 256, 1, 1, 1, 3},  // 0: bf16, waves 128 x 64
-    {64, 256, 1, 1, 1, 3},   // 1: bf16, waves 64 x 64
-    {128, 128, 1, 1, 1, 3},  // 2: bf16, waves 128 x 32
-    {64, 256, 1, 0, 1, 3},   // 3: f32, waves 64 x 64
-    {64, 128, 1, 0, 2, 3},   // 4: f32, waves 64 x 32, two chunks per stage
-    {128, 128, 1, 0, 1, 3},  // 5: f32, waves 128 x 32
-    {128, 256, 1, 1, 1, 2},  // 6: bf16, waves 128 x 64, larger halos (3-D tiles)
+    {128, 256, 1, 1, 1, 3, 4},  // 0: bf16, waves 128 x 64
+    {64, 256, 1, 1, 1, 3, 4},   // 1: bf16, waves 64 x 64
+    {128, 128, 1, 1, 1, 3, 4},  // 2: bf16, waves 128 x 32
+    {64, 256, 1, 0, 1, 3, 4},   // 3: f32, waves 64 x 64
+    {64, 128, 1, 0, 2, 3, 4},   // 4: f32, waves 64 x 32, two chunks per stage
+    {128, 128, 1, 0, 1, 3, 4},  // 5: f32, waves 128 x 32
+    {128, 256, 1, 1, 1, 2, 4},  // 6: bf16, waves 128 x 64, larger halos (3-D tiles)
 };
+constexpr int gemm_lds_budget(const GemmTile &t) { return kGemmLdsPerWave * t.nw; }
 constexpr int gemm_chunk_ch(const GemmTile &t) { return t.bf16 ? 16 : 8; }
 // one stage's weight tiles
 constexpr int gemm_wbuf_bytes(const GemmTile &t, int gs) {
@@ -133,7 +137,7 @@ constexpr int gemm_wbuf_bytes(const GemmTile &t, int gs) {
 }
 // bytes available to the halo of one chunk in one ring slot
 constexpr int gemm_xsub_avail(const GemmTile &t, int gs) {
-    return (kGemmLdsBudget - kGemmWRing * gemm_wbuf_bytes(t, gs)) / t.xb / t.sc;
+    return (gemm_lds_budget(t) - kGemmWRing * gemm_wbuf_bytes(t, gs)) / t.xb / t.sc;
 }
 // halo positions one chunk's buffer holds: bfloat16 in whole 1 KiB pieces of
 // 32 rows, float32 in whole pieces of 64 positions per channel row
@@ -155,10 +159,11 @@ constexpr bool gemm_cfg_valid(const GemmTile &t, int gs) {
 constexpr int gemm_lds_bytes(const GemmTile &t, int gs) {
     return kGemmWRing * gemm_wbuf_bytes(t, gs) + t.xb * t.sc * gemm_xsub_bytes(t, gs);
 }
-static_assert(gemm_lds_bytes(kGemmCfg[0], 4) <= kGemmLdsBudget, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[2], 4) <= kGemmLdsBudget, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[3], 4) <= kGemmLdsBudget, "LDS");
-static_assert(gemm_lds_bytes(kGemmCfg[5], 4) <= kGemmLdsBudget, "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[0], 4) <= gemm_lds_budget(kGemmCfg[0]), "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[2], 4) <= gemm_lds_budget(kGemmCfg[2]), "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[3], 4) <= gemm_lds_budget(kGemmCfg[3]), "LDS");
+static_assert(gemm_lds_bytes(kGemmCfg[5], 4) <= gemm_lds_budget(kGemmCfg[5]), "LDS");
+
 static_assert(gemm_halo_cap(kGemmCfg[0], 4) >= 256 && gemm_halo_cap(kGemmCfg[5], 4) >= 128,
               "halo buffers hold at least the tile");
 // Grouped route

@@ -70,7 +70,7 @@
 namespace convt {
 
 template <typename T, int CFG, int GS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
+__global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
                                                          const T *__restrict__ wr,
                                                          const int32_t *__restrict__ tab,
                                                          const T *__restrict__ bias,
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int XBUF = SC * XSUB;                       // one ring slot: a chunk group's halos
     constexpr int XB = CT.xb;  // halo ring slots
     constexpr int WROW = tiles::kGemmWRowBytes;           // weight row bytes
-    constexpr int NW = tiles::kGemmWaves, WGN = NW / WGM;
+    constexpr int NW = CT.nw, WGN = NW / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MT = WM / 32, NT = WN / 32;
     constexpr int WSLOT = BM * WROW;                      // bytes of one (chunk, tap) weight tile
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     static_assert(ES == 2 ? HALO % 32 == 0 && XSUB == HALO / 32 * 1024
                           : HALO % 64 == 0 && XJ * 256 <= XROW,
                   "halo buffers hold whole pieces");
-    static_assert(tiles::kGemmWRing * WBUF + XB * XBUF <= tiles::kGemmLdsBudget, "LDS budget");
+    static_assert(tiles::kGemmWRing * WBUF + XB * XBUF <= tiles::gemm_lds_budget(CT), "LDS budget");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ws[tiles::kGemmWRing][WBUF];
     __shared__ __attribute__((aligned(256))) unsigned char xs[XB][XBUF];
@@ -445,7 +445,7 @@ static void launch_cfg(const Plan &pl, const void *x, const void *ws, const void
                        hipStream_t stream) {
     const DevParams &p = pl.dp;
     if constexpr (tiles::gemm_cfg_valid(tiles::kGemmCfg[CFG], GS))
-        hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS>), dim3(p.n_blocks), dim3(tiles::kGemmThreads),
+        hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS>), dim3(p.n_blocks), dim3(tiles::kGemmCfg[CFG].nw * 64),
                        0, stream, p, (const T *)x, (const T *)ws,
                        (const int32_t *)((const char *)ws + pl.tab_offset), (const T *)bias, (T *)y);
 }

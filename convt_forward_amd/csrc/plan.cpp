@@ -164,9 +164,12 @@ bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max) {
             const int64_t nt = ceil_div(dp->ax[0].qmax, td) * ceil_div(dp->ax[1].qmax, th) *
                                ceil_div(dp->ax[2].qmax, tw);
             // MFMA work of a tile (masked positions included) dominates; halo
-            // loads add a smaller term per position.
+            // loads add a smaller term per position, and the epilogue one per
+            // output row that 32 consecutive positions (the lanes of one
+            // store) touch.
             const int64_t avg_taps = std::max<int64_t>(1, dp->ktot / std::max(1, dp->nphase));
-            const int64_t cost = nt * (BN * avg_taps * 4 + hd * hh * hw);
+            const int64_t rows_per_store = std::max(1, 32 / tw);
+            const int64_t cost = nt * (BN * avg_taps * 4 + hd * hh * hw + BN * rows_per_store);
             if (cost < best_cost) {
                 best_cost = cost;
                 bd = td;
@@ -224,13 +227,13 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
         const int64_t co_tiles = ceil_div(tmp.Cog, t.bm);
         const int64_t blocks =
             (int64_t)tmp.nt_d * tmp.nt_h * tmp.nt_w * co_tiles * tmp.nphase * tmp.G * tmp.B;
-        const int wgn = tiles::kGemmWaves / t.wgm;
+        const int wgn = t.nw / t.wgm;
         const double mt = t.bm / t.wgm / 32.0, nt = t.bn / (double)wgn / 32.0;
         // LDS read time over MFMA time per tap (float32 MFMAs take 4x the
         // cycles per byte of operands)
         const double lds_ratio = 0.67 * (mt + nt) / (mt * nt) * (bf16 ? 1.0 : 0.25);
         const double eff = std::max(1.0, lds_ratio) * (1.0 + 0.25 / (mt * nt));
-        const double rounds = std::ceil((double)blocks / 512.0);
+        const double rounds = std::ceil((double)blocks / (256.0 * 8 / t.nw));
         const double time = rounds * (double)t.bm * t.bn * eff;
         if (best < 0 || time < best_t * 0.999) {
             best = c;

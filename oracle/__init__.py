@@ -40,13 +40,14 @@ def _bind(path: str):
     lib = ctypes.CDLL(path)
     p64 = ctypes.POINTER(ctypes.c_int64)
     pd = ctypes.POINTER(ctypes.c_double)
-    lib.convt_oracle_out_shape.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64,
+    # (ndim, x_shape, w_shape, stride, padding, padding_end, dilation, output_padding, groups, ...)
+    lib.convt_oracle_out_shape.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64, p64,
                                            ctypes.c_int64, p64]
     lib.convt_oracle_out_shape.restype = ctypes.c_int
-    lib.convt_oracle_forward.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64,
+    lib.convt_oracle_forward.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64, p64,
                                          ctypes.c_int64, pd, pd, pd, pd, pd, ctypes.c_int]
     lib.convt_oracle_forward.restype = ctypes.c_int
-    lib.convt_oracle_points.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64,
+    lib.convt_oracle_points.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64, p64,
                                         ctypes.c_int64, pd, pd, pd, ctypes.c_int64, p64, pd,
                                         pd, ctypes.c_int]
     lib.convt_oracle_points.restype = ctypes.c_int
@@ -68,6 +69,10 @@ def _f64(a: Optional[np.ndarray]):
 
 
 def _attrs(x_shape, w_shape, stride, padding, dilation, output_padding):
+    """(ndim, stride, low padding, high padding, dilation, output_padding) per axis.
+
+    padding: an int, one int per axis (both ends), or one (low, high) pair per
+    axis (the AWS Neuron conv3d_transpose page's asymmetric form)."""
     nd = len(x_shape) - 2
     if len(w_shape) != nd + 2:
         raise ValueError("x and W ranks differ")
@@ -81,7 +86,13 @@ def _attrs(x_shape, w_shape, stride, padding, dilation, output_padding):
             raise ValueError("attribute rank mismatch")
         return tuple(int(t) for t in v)
 
-    return (nd, tup(stride, 1), tup(padding, 0), tup(dilation, 1), tup(output_padding, 0))
+    if padding is not None and not isinstance(padding, int) and len(padding) == nd and \
+            all(not isinstance(v, (int, np.integer)) for v in padding):
+        lo = tuple(int(v[0]) for v in padding)
+        hi = tuple(int(v[1]) for v in padding)
+    else:
+        lo = hi = tup(padding, 0)
+    return (nd, tup(stride, 1), lo, hi, tup(dilation, 1), tup(output_padding, 0))
 
 
 class Oracle:
@@ -97,8 +108,8 @@ class Oracle:
     def out_shape(self, x_shape, w_shape, stride=None, padding=None, dilation=None,
                   output_padding=None, groups: int = 1) -> Tuple[int, ...]:
         """Output shape [B, C_out, O...]; raises ValueError for an ill-formed problem."""
-        nd, s, p, d, op = _attrs(x_shape, w_shape, stride, padding, dilation, output_padding)
-        keep = [_i64(x_shape), _i64(w_shape), _i64(s), _i64(p), _i64(d), _i64(op)]
+        nd, s, p, ph, d, op = _attrs(x_shape, w_shape, stride, padding, dilation, output_padding)
+        keep = [_i64(x_shape), _i64(w_shape), _i64(s), _i64(p), _i64(ph), _i64(d), _i64(op)]
         out = np.zeros(2 + nd, dtype=np.int64)
         rc = self.lib.convt_oracle_out_shape(nd, *[k[1] for k in keep], int(groups),
                                              out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
@@ -110,8 +121,8 @@ class Oracle:
                 stride=None, padding=None, dilation=None, output_padding=None, groups: int = 1,
                 with_scale: bool = True, nthreads: int = 0):
         """Full forward pass in float64. Returns (y, scale); scale is None unless asked."""
-        nd, s, p, d, op = _attrs(x.shape, w.shape, stride, padding, dilation, output_padding)
-        oshape = self.out_shape(x.shape, w.shape, s, p, d, op, groups)
+        nd, s, p, ph, d, op = _attrs(x.shape, w.shape, stride, padding, dilation, output_padding)
+        oshape = self.out_shape(x.shape, w.shape, s, list(zip(p, ph)), d, op, groups)
         xa, xp = _f64(x)
         wa, wp = _f64(w)
         ba, bp = _f64(bias)
@@ -119,7 +130,7 @@ class Oracle:
             raise ValueError("bias must have shape [C_out]")
         y = np.empty(oshape, dtype=np.float64)
         sc = np.empty(oshape, dtype=np.float64) if with_scale else None
-        keep = [_i64(x.shape), _i64(w.shape), _i64(s), _i64(p), _i64(d), _i64(op)]
+        keep = [_i64(x.shape), _i64(w.shape), _i64(s), _i64(p), _i64(ph), _i64(d), _i64(op)]
         rc = self.lib.convt_oracle_forward(
             nd, *[k[1] for k in keep], int(groups), xp, wp, bp,
             y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
@@ -137,7 +148,7 @@ class Oracle:
         ``pts`` is an int array [n, 2 + ndim] of (b, oc, o...). Returns (y, scale)
         as float64 arrays of length n.
         """
-        nd, s, p, d, op = _attrs(x.shape, w.shape, stride, padding, dilation, output_padding)
+        nd, s, p, ph, d, op = _attrs(x.shape, w.shape, stride, padding, dilation, output_padding)
         pa = np.ascontiguousarray(np.asarray(pts, dtype=np.int64).reshape(-1, 2 + nd))
         xa, xp = _f64(x)
         wa, wp = _f64(w)
@@ -145,7 +156,7 @@ class Oracle:
         n = pa.shape[0]
         yv = np.empty(n, dtype=np.float64)
         sv = np.empty(n, dtype=np.float64)
-        keep = [_i64(x.shape), _i64(w.shape), _i64(s), _i64(p), _i64(d), _i64(op)]
+        keep = [_i64(x.shape), _i64(w.shape), _i64(s), _i64(p), _i64(ph), _i64(d), _i64(op)]
         rc = self.lib.convt_oracle_points(
             nd, *[k[1] for k in keep], int(groups), xp, wp, bp, n,
             pa.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),

@@ -27,6 +27,14 @@
  * page, Summary; the AWS Neuron conv3d_transpose page's Dimensions list gives
  * the op = 0 form).
  *
+ * Padding may differ between the two ends of an axis (the AWS Neuron
+ * conv3d_transpose page's padding parameter: a low and a high value per
+ * axis). Read here as: the low value p is the p of the scatter above (it
+ * shifts every output), and the high value p_hi only trims the end, so that
+ * O = (I - 1)*s - (p + p_hi) + d*(k - 1) + op + 1; the symmetric form is
+ * p_hi = p. The same reading makes the result the window [p, p + O) of the
+ * unpadded (p = p_hi = 0) output.
+ *
  * Alongside y it can accumulate scale[b, oc, o] = sum of |x * W| over the same
  * terms, the per-output magnitude used to normalise the GPU error.
  *
@@ -47,20 +55,24 @@
 
 typedef struct {
     int64_t B, Ci, Co, G, Cig, Cog;
-    int64_t I[3], K[3], S[3], P[3], D[3], OP[3], O[3];
+    int64_t I[3], K[3], S[3], P[3], PH[3], D[3], OP[3], O[3];
 } oracle_prob;
 
-/* Output size of one axis; returns < 1 when the axis has no outputs. */
-static int64_t axis_out(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d, int64_t op)
+/* Output size of one axis (p: low padding, ph: high padding); returns < 1
+ * when the axis has no outputs. */
+static int64_t axis_out(int64_t in, int64_t k, int64_t s, int64_t p, int64_t ph, int64_t d,
+                        int64_t op)
 {
-    return (in - 1) * s - 2 * p + d * (k - 1) + op + 1;
+    return (in - 1) * s - (p + ph) + d * (k - 1) + op + 1;
 }
 
-/* Fill an oracle_prob from rank-ndim arguments. Returns 0, or -1 when the
- * arguments do not describe a well-formed transposed convolution. */
+/* Fill an oracle_prob from rank-ndim arguments (padding_end NULL: the high
+ * padding equals the low one). Returns 0, or -1 when the arguments do not
+ * describe a well-formed transposed convolution. */
 static int make_prob(int ndim, const int64_t *x_shape, const int64_t *w_shape,
-                     const int64_t *stride, const int64_t *padding, const int64_t *dilation,
-                     const int64_t *output_padding, int64_t groups, oracle_prob *pb)
+                     const int64_t *stride, const int64_t *padding, const int64_t *padding_end,
+                     const int64_t *dilation, const int64_t *output_padding, int64_t groups,
+                     oracle_prob *pb)
 {
     if (ndim < 1 || ndim > 3 || groups < 1) return -1;
     pb->B = x_shape[0];
@@ -74,20 +86,22 @@ static int make_prob(int ndim, const int64_t *x_shape, const int64_t *w_shape,
     int lead = 3 - ndim;
     for (int a = 0; a < 3; ++a) {
         if (a < lead) {
-            pb->I[a] = 1; pb->K[a] = 1; pb->S[a] = 1; pb->P[a] = 0; pb->D[a] = 1; pb->OP[a] = 0;
+            pb->I[a] = 1; pb->K[a] = 1; pb->S[a] = 1; pb->P[a] = 0; pb->PH[a] = 0; pb->D[a] = 1;
+            pb->OP[a] = 0;
         } else {
             int j = a - lead;
             pb->I[a] = x_shape[2 + j];
             pb->K[a] = w_shape[2 + j];
             pb->S[a] = stride[j];
             pb->P[a] = padding[j];
+            pb->PH[a] = padding_end ? padding_end[j] : padding[j];
             pb->D[a] = dilation[j];
             pb->OP[a] = output_padding[j];
         }
-        if (pb->I[a] < 0 || pb->K[a] < 1 || pb->S[a] < 1 || pb->P[a] < 0 || pb->D[a] < 1 ||
-            pb->OP[a] < 0)
+        if (pb->I[a] < 0 || pb->K[a] < 1 || pb->S[a] < 1 || pb->P[a] < 0 || pb->PH[a] < 0 ||
+            pb->D[a] < 1 || pb->OP[a] < 0)
             return -1;
-        pb->O[a] = axis_out(pb->I[a], pb->K[a], pb->S[a], pb->P[a], pb->D[a], pb->OP[a]);
+        pb->O[a] = axis_out(pb->I[a], pb->K[a], pb->S[a], pb->P[a], pb->PH[a], pb->D[a], pb->OP[a]);
         if (pb->O[a] < 1) return -1;
     }
     return 0;
@@ -95,11 +109,13 @@ static int make_prob(int ndim, const int64_t *x_shape, const int64_t *w_shape,
 
 /* Output spatial sizes (rank ndim). Returns 0 or -1 (as make_prob). */
 int convt_oracle_out_shape(int ndim, const int64_t *x_shape, const int64_t *w_shape,
-                           const int64_t *stride, const int64_t *padding, const int64_t *dilation,
+                           const int64_t *stride, const int64_t *padding,
+                           const int64_t *padding_end, const int64_t *dilation,
                            const int64_t *output_padding, int64_t groups, int64_t *out_shape)
 {
     oracle_prob pb;
-    if (make_prob(ndim, x_shape, w_shape, stride, padding, dilation, output_padding, groups, &pb))
+    if (make_prob(ndim, x_shape, w_shape, stride, padding, padding_end, dilation, output_padding,
+                  groups, &pb))
         return -1;
     out_shape[0] = pb.B;
     out_shape[1] = pb.Co;
@@ -111,13 +127,14 @@ int convt_oracle_out_shape(int ndim, const int64_t *x_shape, const int64_t *w_sh
  * bias: [C_out] or NULL, y: [B, C_out, O...], scale: same shape as y or NULL.
  * nthreads <= 0 leaves the OpenMP default. Returns 0 or -1. */
 int convt_oracle_forward(int ndim, const int64_t *x_shape, const int64_t *w_shape,
-                         const int64_t *stride, const int64_t *padding, const int64_t *dilation,
-                         const int64_t *output_padding, int64_t groups, const double *x,
-                         const double *w, const double *bias, double *y, double *scale,
-                         int nthreads)
+                         const int64_t *stride, const int64_t *padding, const int64_t *padding_end,
+                         const int64_t *dilation, const int64_t *output_padding, int64_t groups,
+                         const double *x, const double *w, const double *bias, double *y,
+                         double *scale, int nthreads)
 {
     oracle_prob pb;
-    if (make_prob(ndim, x_shape, w_shape, stride, padding, dilation, output_padding, groups, &pb))
+    if (make_prob(ndim, x_shape, w_shape, stride, padding, padding_end, dilation, output_padding,
+                  groups, &pb))
         return -1;
     const int64_t isz = pb.I[0] * pb.I[1] * pb.I[2];
     const int64_t ksz = pb.K[0] * pb.K[1] * pb.K[2];
@@ -178,13 +195,14 @@ int convt_oracle_forward(int ndim, const int64_t *x_shape, const int64_t *w_shap
  * entries). yv and sv (sv may be NULL) receive one value per point. Returns 0,
  * or -1 for a malformed problem or an out-of-range point. */
 int convt_oracle_points(int ndim, const int64_t *x_shape, const int64_t *w_shape,
-                        const int64_t *stride, const int64_t *padding, const int64_t *dilation,
-                        const int64_t *output_padding, int64_t groups, const double *x,
-                        const double *w, const double *bias, int64_t npts, const int64_t *pts,
-                        double *yv, double *sv, int nthreads)
+                        const int64_t *stride, const int64_t *padding, const int64_t *padding_end,
+                        const int64_t *dilation, const int64_t *output_padding, int64_t groups,
+                        const double *x, const double *w, const double *bias, int64_t npts,
+                        const int64_t *pts, double *yv, double *sv, int nthreads)
 {
     oracle_prob pb;
-    if (make_prob(ndim, x_shape, w_shape, stride, padding, dilation, output_padding, groups, &pb))
+    if (make_prob(ndim, x_shape, w_shape, stride, padding, padding_end, dilation, output_padding,
+                  groups, &pb))
         return -1;
     const int lead = 3 - ndim;
     for (int64_t n = 0; n < npts; ++n) {

@@ -63,11 +63,12 @@ def _pad_or_crop(a: np.ndarray, axis: int, lo: int, hi: int) -> np.ndarray:
     return np.pad(a, widths)
 
 
-def lowered_reference(x, w, bias, s, p, d, op, groups):
+def lowered_reference(x, w, bias, s, p, d, op, groups, ph=None):
     """Transposed convolution via the lowering on the pages: dilate the input by
     the stride (stride-1 zeros between samples), pad low d*(k-1)-p and high
-    that plus op, flip the taps, then a stride-1 dilated forward correlation,
-    one group at a time."""
+    d*(k-1)-p_hi+op (p_hi = p when the padding is symmetric), flip the taps,
+    then a stride-1 dilated forward correlation, one group at a time."""
+    ph = p if ph is None else ph
     nd = x.ndim - 2
     B, Ci = x.shape[:2]
     Cig, Cog = Ci // groups, w.shape[1]
@@ -77,7 +78,8 @@ def lowered_reference(x, w, bias, s, p, d, op, groups):
     xd[(slice(None), slice(None)) + tuple(slice(None, None, sa) for sa in s)] = x
     for a in range(nd):
         lo = d[a] * (k[a] - 1) - p[a]
-        xd = _pad_or_crop(xd, 2 + a, lo, lo + op[a])
+        hi = d[a] * (k[a] - 1) - ph[a] + op[a]
+        xd = _pad_or_crop(xd, 2 + a, lo, hi)
     wf = w[(slice(None), slice(None)) + (slice(None, None, -1),) * nd]
     out_sp = tuple(xd.shape[2 + a] - d[a] * (k[a] - 1) for a in range(nd))
     y = np.zeros((B, Cog * groups) + out_sp)
@@ -124,14 +126,18 @@ def forward_conv_gather(yv, w, s, p, d, in_sp, groups):
     return out
 
 
-def brute_force(x, w, bias, s, p, d, op, groups):
-    """Every output by enumerating all (input position, tap) pairs in Python."""
+def brute_force(x, w, bias, s, p, d, op, groups, ph=None):
+    """Every output by enumerating all (input position, tap) pairs in Python;
+    the low padding p shifts the outputs, the high padding p_hi only shortens
+    the axis."""
+    ph = p if ph is None else ph
     nd = x.ndim - 2
     B, Ci = x.shape[:2]
     Cig, Cog = Ci // groups, w.shape[1]
     k = w.shape[2:]
     I = x.shape[2:]
-    O = tuple((I[a] - 1) * s[a] - 2 * p[a] + d[a] * (k[a] - 1) + op[a] + 1 for a in range(nd))
+    O = tuple((I[a] - 1) * s[a] - p[a] - ph[a] + d[a] * (k[a] - 1) + op[a] + 1
+              for a in range(nd))
     y = np.zeros((B, Cog * groups) + O)
     for b in range(B):
         for oc in range(Cog * groups):
@@ -147,7 +153,8 @@ def brute_force(x, w, bias, s, p, d, op, groups):
     return y
 
 
-def _rand_problem(rng, nd, B, Ci, Cog, groups, I, k, s, p, d, op, bias=True, ints=False):
+def _rand_problem(rng, nd, B, Ci, Cog, groups, I, k, s, p, d, op, bias=True, ints=False,
+                  ph=None):
     Ci_t = Ci
     if ints:
         x = rng.integers(-4, 5, size=(B, Ci_t) + tuple(I)).astype(np.float64)
@@ -157,7 +164,8 @@ def _rand_problem(rng, nd, B, Ci, Cog, groups, I, k, s, p, d, op, bias=True, int
         x = rng.standard_normal((B, Ci_t) + tuple(I))
         w = rng.standard_normal((Ci_t, Cog) + tuple(k))
         b = rng.standard_normal(Cog * groups) if bias else None
-    return x, w, b, dict(stride=tuple(s), padding=tuple(p), dilation=tuple(d),
+    pad = tuple(p) if ph is None or list(ph) == list(p) else tuple(zip(p, ph))
+    return x, w, b, dict(stride=tuple(s), padding=pad, dilation=tuple(d),
                          output_padding=tuple(op), groups=groups)
 
 
@@ -169,9 +177,11 @@ def _close(a, b, rtol=1e-12, atol=1e-12):
     assert err <= max(rtol, atol), f"max relative error {err}"
 
 
-def random_grid(rng, n, nds=(1, 2, 3)):
+def random_grid(rng, n, nds=(1, 2, 3), asym=True):
     """Seeded random valid parameter sets (output_padding < max(stride,
-    dilation)), including pads beyond d*(k-1) and phases with no taps."""
+    dilation)), including pads beyond d*(k-1) and phases with no taps. With
+    asym, about half the sets get a high padding ``ph`` that differs from the
+    low one on some axis; otherwise ``ph`` equals ``p``."""
     out = []
     while len(out) < n:
         nd = int(rng.choice(nds))
@@ -185,11 +195,14 @@ def random_grid(rng, n, nds=(1, 2, 3)):
         d = [int(rng.integers(1, 4)) for _ in range(nd)]
         p = [int(rng.integers(0, d[a] * (k[a] - 1) + 2)) for a in range(nd)]
         op = [int(rng.integers(0, max(s[a], d[a]))) for a in range(nd)]
-        O = [(I[a] - 1) * s[a] - 2 * p[a] + d[a] * (k[a] - 1) + op[a] + 1 for a in range(nd)]
+        ph = list(p)
+        if asym and rng.integers(0, 2):
+            ph = [int(rng.integers(0, d[a] * (k[a] - 1) + 2)) for a in range(nd)]
+        O = [(I[a] - 1) * s[a] - p[a] - ph[a] + d[a] * (k[a] - 1) + op[a] + 1 for a in range(nd)]
         if min(O) < 1:
             continue
         out.append(dict(nd=nd, B=B, Ci=Cig * groups, Cog=Cog, groups=groups, I=I, k=k, s=s, p=p,
-                        d=d, op=op))
+                        ph=ph, d=d, op=op))
     return out
 
 
@@ -226,6 +239,44 @@ def check_output_shapes(orc):
     c = case["cases"][0]
     y, _ = orc.forward(np.ones(c["x_shape"]), np.ones(c["w_shape"]))
     assert list(y.shape) == c["y_shape"]
+
+
+def check_asymmetric_sizes(orc):
+    """Sizes with a low and a high padding per axis (the AWS Neuron
+    conv3d_transpose page's padding parameter), worked by hand from
+    O = (I-1)*s - (p_lo + p_hi) + d*(k-1) + op + 1."""
+    cases = [
+        # (x_shape, w_shape, stride, padding pairs, dilation, output_padding, groups, y_shape)
+        ((1, 1, 5), (1, 1, 3), (2,), ((1, 0),), (1,), (0,), 1, (1, 1, 10)),
+        ((1, 1, 5), (1, 1, 3), (2,), ((0, 1),), (1,), (0,), 1, (1, 1, 10)),
+        ((1, 2, 4, 6), (2, 3, 3, 2), (2, 3), ((0, 2), (1, 0)), (1, 2), (1, 0), 1, (1, 3, 8, 17)),
+        ((2, 4, 3, 3, 3), (4, 1, 2, 2, 2), (1, 2, 2), ((0, 1), (1, 1), (2, 0)), (1, 1, 1),
+         (0, 1, 0), 4, (2, 4, 3, 5, 4)),
+    ]
+    for xs, ws, st, pad, dl, op, g, ys in cases:
+        assert tuple(orc.out_shape(xs, ws, st, pad, dl, op, g)) == ys, (xs, ws, pad)
+    # equal ends give the symmetric size
+    assert orc.out_shape((1, 1, 5), (1, 1, 3), 2, ((1, 1),), 1, 0) == \
+        orc.out_shape((1, 1, 5), (1, 1, 3), 2, 1, 1, 0)
+
+
+def check_asymmetric_window(orc):
+    """Low padding p_lo drops the first p_lo outputs and high padding p_hi the
+    last p_hi of the unpadded result, so the padded output is the window
+    [p_lo, p_lo + O) of the p = 0 output, bit for bit."""
+    rng = np.random.default_rng(22)
+    for prm in random_grid(rng, 40):
+        x, w, b, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
+                                    prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
+                                    prm["d"], prm["op"], ph=prm["ph"])
+        y, sc = orc.forward(x, w, b, **kw)
+        kw0 = dict(kw, padding=0)
+        y0, sc0 = orc.forward(x, w, b, **kw0)
+        win = (slice(None), slice(None)) + tuple(
+            slice(prm["p"][a], prm["p"][a] + y.shape[2 + a]) for a in range(prm["nd"]))
+        assert all(y0.shape[2 + a] - y.shape[2 + a] == prm["p"][a] + prm["ph"][a]
+                   for a in range(prm["nd"]))
+        assert np.array_equal(y, y0[win]) and np.array_equal(sc, sc0[win])
 
 
 def check_full_scatter_is_full_convolution(orc):
@@ -279,9 +330,10 @@ def check_lowering_equivalence(orc):
     for prm in random_grid(rng, 60):
         x, w, b, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
                                     prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
-                                    prm["d"], prm["op"])
+                                    prm["d"], prm["op"], ph=prm["ph"])
         y, _ = orc.forward(x, w, b, **kw)
-        ref = lowered_reference(x, w, b, prm["s"], prm["p"], prm["d"], prm["op"], prm["groups"])
+        ref = lowered_reference(x, w, b, prm["s"], prm["p"], prm["d"], prm["op"], prm["groups"],
+                                prm["ph"])
         _close(y, ref)
 
 
@@ -290,7 +342,7 @@ def check_adjoint_identity(orc):
     for prm in random_grid(rng, 40):
         x, w, _, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
                                     prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
-                                    prm["d"], prm["op"], bias=False)
+                                    prm["d"], prm["op"], bias=False, ph=prm["ph"])
         y, _ = orc.forward(x, w, None, **kw)
         yr = rng.standard_normal(y.shape)
         lhs = float(np.sum(y * yr))
@@ -309,7 +361,7 @@ def check_groups_concatenate(orc):
             continue
         x, w, b, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
                                     prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
-                                    prm["d"], prm["op"])
+                                    prm["d"], prm["op"], ph=prm["ph"])
         y, _ = orc.forward(x, w, b, **kw)
         G, Cig, Cog = prm["groups"], prm["Ci"] // prm["groups"], prm["Cog"]
         parts = []
@@ -326,7 +378,7 @@ def check_bias_linearity_and_mass(orc):
     for prm in random_grid(rng, 30):
         x, w, b, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
                                     prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
-                                    prm["d"], prm["op"], ints=True)
+                                    prm["d"], prm["op"], ints=True, ph=prm["ph"])
         nd = prm["nd"]
         y_b, _ = orc.forward(x, w, b, **kw)
         y_0, _ = orc.forward(x, w, None, **kw)
@@ -352,9 +404,10 @@ def check_brute_force(orc):
     for prm in random_grid(rng, 25, nds=(1, 2)):
         x, w, b, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
                                     prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
-                                    prm["d"], prm["op"])
+                                    prm["d"], prm["op"], ph=prm["ph"])
         y, _ = orc.forward(x, w, b, **kw)
-        ref = brute_force(x, w, b, prm["s"], prm["p"], prm["d"], prm["op"], prm["groups"])
+        ref = brute_force(x, w, b, prm["s"], prm["p"], prm["d"], prm["op"], prm["groups"],
+                          prm["ph"])
         _close(y, ref)
 
 
@@ -363,12 +416,12 @@ def check_scale_is_abs_convt(orc):
     for prm in random_grid(rng, 20):
         x, w, b, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
                                     prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
-                                    prm["d"], prm["op"])
+                                    prm["d"], prm["op"], ph=prm["ph"])
         _, sc = orc.forward(x, w, b, **kw)
         ref, _ = orc.forward(np.abs(x), np.abs(w), None, **kw)
         _close(sc, ref)
         ref2 = lowered_reference(np.abs(x), np.abs(w), None, prm["s"], prm["p"], prm["d"],
-                                 prm["op"], prm["groups"])
+                                 prm["op"], prm["groups"], prm["ph"])
         _close(sc, ref2)
 
 
@@ -377,7 +430,7 @@ def check_points_match_forward(orc):
     for prm in random_grid(rng, 30):
         x, w, b, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
                                     prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
-                                    prm["d"], prm["op"])
+                                    prm["d"], prm["op"], ph=prm["ph"])
         y, sc = orc.forward(x, w, b, **kw)
         pts = np.array(list(itertools.product(*[range(t) for t in y.shape])), dtype=np.int64)
         yv, sv = orc.points(x, w, b, pts, **kw)
@@ -402,6 +455,8 @@ def check_rejects_ill_formed(orc):
         dict(x=(1, 3, 4), w=(3, 1, 2), s=(1,), p=(0,), d=(1,), op=(0,), g=2),   # 2 does not divide 3
         dict(x=(1, 2, 4), w=(3, 1, 2), s=(1,), p=(0,), d=(1,), op=(0,), g=1),   # C_in mismatch
         dict(x=(1, 2, 4), w=(2, 1, 2), s=(0,), p=(0,), d=(1,), op=(0,), g=1),   # stride 0
+        dict(x=(1, 1, 4), w=(1, 1, 2), s=(1,), p=((0, -1),), d=(1,), op=(0,), g=1),  # p_hi < 0
+        dict(x=(1, 1, 2), w=(1, 1, 2), s=(1,), p=((0, 3),), d=(1,), op=(0,), g=1),   # O = 0
     ]
     for c in bad:
         try:
@@ -414,6 +469,8 @@ def check_rejects_ill_formed(orc):
 ALL_CHECKS = [
     check_golden_cases,
     check_output_shapes,
+    check_asymmetric_sizes,
+    check_asymmetric_window,
     check_full_scatter_is_full_convolution,
     check_stamp_is_kron,
     check_pointwise_is_matmul,

@@ -84,7 +84,7 @@ def test_workload_plans(name):
 
 def test_plan_shapes_match_oracle_on_random_grid():
     rng = np.random.default_rng(5)
-    for prm in oracle_pins.random_grid(rng, 300):
+    for prm in oracle_pins.random_grid(rng, 300, asym=False):
         xs = (prm["B"], prm["Ci"]) + tuple(prm["I"])
         ws = (prm["Ci"], prm["Cog"]) + tuple(prm["k"])
         pl = plan(x_shape=xs, w_shape=ws, stride=prm["s"], padding=prm["p"], dilation=prm["d"],
@@ -178,7 +178,7 @@ def test_phase_table_properties():
     with offset (r + p - kk*d)/s, ascending; the residues partition the taps
     and their q counts partition the outputs."""
     rng = np.random.default_rng(6)
-    for prm in oracle_pins.random_grid(rng, 200):
+    for prm in oracle_pins.random_grid(rng, 200, asym=False):
         xs = (prm["B"], prm["Ci"]) + tuple(prm["I"])
         ws = (prm["Ci"], prm["Cog"]) + tuple(prm["k"])
         pl = plan(x_shape=xs, w_shape=ws, stride=prm["s"], padding=prm["p"], dilation=prm["d"],

@@ -143,7 +143,7 @@ def test_integer_inputs_exact_full_c3_sampled():
 def grid_cases(n, seed):
     rng = np.random.default_rng(seed)
     out = []
-    for prm in oracle_pins.random_grid(rng, n):
+    for prm in oracle_pins.random_grid(rng, n, asym=False):
         scale_c = int(rng.choice([1, 1, 4, 12]))
         prm = dict(prm)
         prm["Ci"] *= scale_c

@@ -32,10 +32,18 @@ MUTANTS = [
     ("input channel reversed", "const double *xp = x + (b * pb.Ci + ci) * isz;\n            const double *wp = w + (ci * pb.Cog + ocl) * ksz;\n            for (int64_t i0",
      "const double *xp = x + (b * pb.Ci + (pb.Ci - 1 - ci)) * isz;\n            const double *wp = w + (ci * pb.Cog + ocl) * ksz;\n            for (int64_t i0"),
     ("wrong group of an output channel", "const int64_t g = oc / pb.Cog;", "const int64_t g = oc % pb.G;"),
-    ("output_padding ignored in size", "return (in - 1) * s - 2 * p + d * (k - 1) + op + 1;",
-     "return (in - 1) * s - 2 * p + d * (k - 1) + 1;"),
-    ("padding counted once in size", "return (in - 1) * s - 2 * p + d * (k - 1) + op + 1;",
+    ("output_padding ignored in size", "return (in - 1) * s - (p + ph) + d * (k - 1) + op + 1;",
+     "return (in - 1) * s - (p + ph) + d * (k - 1) + 1;"),
+    ("padding counted once in size", "return (in - 1) * s - (p + ph) + d * (k - 1) + op + 1;",
      "return (in - 1) * s - p + d * (k - 1) + op + 1;"),
+    ("low padding counted twice in size", "return (in - 1) * s - (p + ph) + d * (k - 1) + op + 1;",
+     "return (in - 1) * s - 2 * p + d * (k - 1) + op + 1;"),
+    ("high padding read as the low one", "pb->PH[a] = padding_end ? padding_end[j] : padding[j];",
+     "pb->PH[a] = padding[j];"),
+    ("high padding shifts the outputs", "const int64_t o2 = i2 * pb.S[2] - pb.P[2] + k2 * pb.D[2];",
+     "const int64_t o2 = i2 * pb.S[2] - pb.PH[2] + k2 * pb.D[2];"),
+    ("high padding shifts the point form", "const int64_t t1 = o[1] + pb.P[1] - k1 * pb.D[1];",
+     "const int64_t t1 = o[1] + pb.PH[1] - k1 * pb.D[1];"),
     ("first output position dropped", "if (o2 < 0 || o2 >= pb.O[2]) continue;",
      "if (o2 < 1 || o2 >= pb.O[2]) continue;"),
     ("signed magnitude", "if (sp) sp[o] += fabs(xv * wv);", "if (sp) sp[o] += xv * wv;"),

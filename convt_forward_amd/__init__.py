@@ -11,7 +11,8 @@ the functions that need it raises.
 x: [B, C_in, I...] and w: [C_in, C_out/groups, k...] are contiguous CUDA
 (HIP) tensors of dtype float32 or bfloat16; bias is [C_out] or None. Scalars
 or per-axis tuples are accepted for stride, padding, dilation and
-output_padding.
+output_padding; padding may also give a (low, high) pair per axis, for
+different padding at the two ends of an axis.
 """
 from __future__ import annotations
 
@@ -49,6 +50,9 @@ class Problem(ctypes.Structure):
         ("groups", ctypes.c_int64),
         ("has_bias", ctypes.c_int32),
         ("route", ctypes.c_int32),
+        ("has_padding_hi", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("padding_hi", ctypes.c_int64 * MAX_NDIM),
     ]
 
 
@@ -108,6 +112,18 @@ def _tup(v, nd: int, name: str) -> Tuple[int, ...]:
     return v
 
 
+def _pads(v, nd: int) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
+    """(low, high) padding per axis from an int, one int per axis, or one
+    (low, high) pair per axis."""
+    if not isinstance(v, int) and len(v) == nd and all(not isinstance(t, int) for t in v):
+        pairs = [tuple(int(u) for u in t) for t in v]
+        if any(len(t) != 2 for t in pairs):
+            raise ValueError("padding pairs must be (low, high)")
+        return tuple(t[0] for t in pairs), tuple(t[1] for t in pairs)
+    lo = _tup(v, nd, "padding")
+    return lo, lo
+
+
 def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, padding=0, dilation=1,
                  output_padding=0, groups: int = 1, has_bias: bool = False, dtype: str = "f32",
                  route: str = "auto") -> Problem:
@@ -121,10 +137,15 @@ def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, paddi
         p.x_shape[i] = int(v)
     for i, v in enumerate(w_shape):
         p.w_shape[i] = int(v)
-    for name in ("stride", "padding", "dilation", "output_padding"):
+    for name in ("stride", "dilation", "output_padding"):
         arr = getattr(p, name)
         for i, v in enumerate(_tup(locals()[name], nd, name)):
             arr[i] = v
+    lo, hi = _pads(padding, nd)
+    for i in range(nd):
+        p.padding[i] = lo[i]
+        p.padding_hi[i] = hi[i]
+    p.has_padding_hi = 1 if lo != hi else 0
     p.groups = int(groups)
     p.has_bias = 1 if has_bias else 0
     p.route = ROUTES[route]
@@ -267,7 +288,7 @@ _plan_cache: Dict[tuple, Plan] = {}
 def get_plan(x_shape, w_shape, stride=1, padding=0, dilation=1, output_padding=0, groups=1,
              has_bias=False, dtype="f32", route="auto") -> Plan:
     nd = len(x_shape) - 2
-    key = (tuple(x_shape), tuple(w_shape), _tup(stride, nd, "stride"), _tup(padding, nd, "padding"),
+    key = (tuple(x_shape), tuple(w_shape), _tup(stride, nd, "stride"), _pads(padding, nd),
            _tup(dilation, nd, "dilation"), _tup(output_padding, nd, "output_padding"), int(groups),
            bool(has_bias), dtype, route)
     pl = _plan_cache.get(key)

@@ -173,6 +173,6 @@ convt_status convt_plan_axis_phase(convt_plan_t plan, int32_t axis, int64_t resi
     return CONVT_OK;
 }
 
-int32_t convt_version(void) { return 100; }
+int32_t convt_version(void) { return 200; }
 
 }  // extern "C"

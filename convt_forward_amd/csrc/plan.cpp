@@ -377,6 +377,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     if (p->has_bias != 0 && p->has_bias != 1) return CONVT_ERR_INVALID_ARGUMENT;
     if (p->route < CONVT_ROUTE_AUTO || p->route > CONVT_ROUTE_NAIVE)
         return CONVT_ERR_INVALID_ARGUMENT;
+    if ((p->has_padding_hi != 0 && p->has_padding_hi != 1) || p->reserved0 != 0)
+        return CONVT_ERR_INVALID_ARGUMENT;
     const int64_t B = p->x_shape[0], Ci = p->x_shape[1];
     const int64_t G = p->groups;
     if (B < 0 || Ci < 0 || G < 1) return CONVT_ERR_INVALID_ARGUMENT;
@@ -397,16 +399,19 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
         K[a] = p->w_shape[2 + j];
         S[a] = p->stride[j];
         P[a] = p->padding[j];
+        // the high padding only shortens the axis: the kernels see the low
+        // padding P and the output size O
+        const int64_t PH = p->has_padding_hi ? p->padding_hi[j] : P[a];
         D[a] = p->dilation[j];
         OP[a] = p->output_padding[j];
-        if (I[a] < 0 || K[a] < 1 || S[a] < 1 || P[a] < 0 || D[a] < 1 || OP[a] < 0)
+        if (I[a] < 0 || K[a] < 1 || S[a] < 1 || P[a] < 0 || PH < 0 || D[a] < 1 || OP[a] < 0)
             return CONVT_ERR_INVALID_ARGUMENT;
         if (OP[a] >= std::max(S[a], D[a])) return CONVT_ERR_INVALID_ARGUMENT;
         // sizes are bounded so that the output-size arithmetic cannot overflow
         if (I[a] > ((int64_t)1 << 31) || K[a] > ((int64_t)1 << 20) || S[a] > ((int64_t)1 << 20) ||
-            D[a] > ((int64_t)1 << 20) || P[a] > ((int64_t)1 << 40))
+            D[a] > ((int64_t)1 << 20) || P[a] > ((int64_t)1 << 40) || PH > ((int64_t)1 << 40))
             return CONVT_ERR_INVALID_ARGUMENT;
-        O[a] = (I[a] - 1) * S[a] - 2 * P[a] + D[a] * (K[a] - 1) + OP[a] + 1;
+        O[a] = (I[a] - 1) * S[a] - (P[a] + PH) + D[a] * (K[a] - 1) + OP[a] + 1;
         if (O[a] < 1) return CONVT_ERR_INVALID_ARGUMENT;
     }
     if (p->dtype < CONVT_DTYPE_F32 || p->dtype > CONVT_DTYPE_I64)

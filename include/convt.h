@@ -8,7 +8,12 @@
  * over each spatial axis (SKaiNET pull request "feat(ops): implement
  * convTranspose2d", Summary; extended per axis to 1-D and 3-D), with output
  * size per axis (I - 1)*s - 2*p + d*(k - 1) + output_padding + 1 (same page,
- * Summary; AWS Neuron conv3d_transpose page, Dimensions), channel ci of group g
+ * Summary; AWS Neuron conv3d_transpose page, Dimensions), or, when the two
+ * ends of an axis are padded differently (AWS Neuron page, :param padding:),
+ * (I - 1)*s - (p_lo + p_hi) + d*(k - 1) + output_padding + 1, where the low
+ * padding p_lo is the p of the scatter and the high padding p_hi only
+ * shortens the axis (y is the window [p_lo, p_lo + O) of the unpadded
+ * result), channel ci of group g
  * feeding output channels g*Cog ... g*Cog + Cog - 1 and C_out = Cog * groups
  * (SKaiNET page, "groups-aware C_out"), bias added once per output channel
  * (huggingface ai.onnx.ConvTranspose page, Description; AWS Neuron page,
@@ -94,7 +99,10 @@ typedef enum convt_route {
 
 /* The problem, in the terms the pages use. Only the first 2 + ndim entries
  * of the shape arrays and the first ndim entries of the attribute arrays are
- * read. Padding is symmetric per axis. */
+ * read. padding is the low (leading) padding of each axis; the high
+ * (trailing) padding equals it unless has_padding_hi is 1, in which case it
+ * is padding_hi (the AWS Neuron page's pad_*_lo / pad_*_hi pairs). A
+ * zero-initialised tail (has_padding_hi = 0) keeps symmetric padding. */
 typedef struct convt_problem {
     int32_t ndim;                               /* 1, 2 or 3 spatial axes */
     int32_t dtype;                              /* convt_dtype of x, W, bias and y */
@@ -107,6 +115,9 @@ typedef struct convt_problem {
     int64_t groups;                             /* >= 1, divides C_in */
     int32_t has_bias;                           /* 0 or 1 */
     int32_t route;                              /* convt_route; CONVT_ROUTE_AUTO normally */
+    int32_t has_padding_hi;                     /* 0: high padding = padding; 1: = padding_hi */
+    int32_t reserved0;                          /* must be 0 */
+    int64_t padding_hi[CONVT_MAX_NDIM];         /* >= 0; read only when has_padding_hi = 1 */
 } convt_problem;
 
 typedef struct convt_plan_info {
@@ -128,7 +139,8 @@ typedef struct convt_plan_s *convt_plan_t;
  * outputPadding < max(stride, dilation) per axis, dilation, groups
  * divisibility, bias shape, dtype guard; plus shape consistency):
  *   ndim in 1..3; all sizes >= 0; kernel sizes >= 1; stride >= 1;
- *   padding >= 0; dilation >= 1; 0 <= output_padding < max(stride, dilation);
+ *   padding >= 0 (both ends); has_padding_hi in {0, 1}; reserved0 == 0;
+ *   dilation >= 1; 0 <= output_padding < max(stride, dilation);
  *   groups >= 1 dividing C_in; w_shape[0] == C_in; every output size >= 1;
  *   has_bias in {0, 1}; element counts of x, W and y below 2^62 and each
  *   plane (one batch item, one channel) below 2^31 elements.
@@ -190,7 +202,8 @@ const char *convt_route_name(int32_t route);
  * r (0 <= r < stride of the axis) it reports the output positions s*q + r,
  * q in [0, q_count), and the taps kk whose products land on them, in the
  * order the plan uses (ascending input offset), with each tap's input offset
- * off = (r + p - kk*d) / s (exact), so that y[s*q + r] gathers x[q + off] * W[kk].
+ * off = (r + p - kk*d) / s (exact; p is the low padding), so that y[s*q + r]
+ * gathers x[q + off] * W[kk].
  * `axis` counts spatial axes from 0. taps/offsets receive at most `cap`
  * entries; *n_taps gets the full count. Host only.
  */

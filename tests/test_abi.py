@@ -41,7 +41,7 @@ def test_status_and_route_names():
     assert L.convt_status_string(3) == b"device error"
     for name, code in C.ROUTES.items():
         assert L.convt_route_name(code).decode() == name
-    assert L.convt_version() >= 100
+    assert L.convt_version() >= 200
 
 
 def plan(**kw):
@@ -84,12 +84,13 @@ def test_workload_plans(name):
 
 def test_plan_shapes_match_oracle_on_random_grid():
     rng = np.random.default_rng(5)
-    for prm in oracle_pins.random_grid(rng, 300, asym=False):
+    for prm in oracle_pins.random_grid(rng, 300):
         xs = (prm["B"], prm["Ci"]) + tuple(prm["I"])
         ws = (prm["Ci"], prm["Cog"]) + tuple(prm["k"])
-        pl = plan(x_shape=xs, w_shape=ws, stride=prm["s"], padding=prm["p"], dilation=prm["d"],
+        pad = tuple(zip(prm["p"], prm["ph"]))
+        pl = plan(x_shape=xs, w_shape=ws, stride=prm["s"], padding=pad, dilation=prm["d"],
                   output_padding=prm["op"], groups=prm["groups"])
-        assert pl.out_shape == oracle.out_shape(xs, ws, prm["s"], prm["p"], prm["d"], prm["op"],
+        assert pl.out_shape == oracle.out_shape(xs, ws, prm["s"], pad, prm["d"], prm["op"],
                                                 prm["groups"])
 
 
@@ -105,6 +106,8 @@ REJECT = [
     dict(output_padding=-1),
     dict(groups=0),
     dict(x_shape=(1, 1, 1), w_shape=(1, 1, 1), padding=1),  # output size (1-1)*1 - 2 + 0 + 1 < 1
+    dict(padding=((0, -1),)),                               # negative high padding
+    dict(x_shape=(1, 1, 2), w_shape=(1, 1, 2), padding=((0, 3),)),  # 1 - 3 + 1 + 1 < 1
     dict(w_shape=(1, 2, 0)),                                # empty kernel
     dict(x_shape=(-1, 1, 3)),
 ]
@@ -178,10 +181,11 @@ def test_phase_table_properties():
     with offset (r + p - kk*d)/s, ascending; the residues partition the taps
     and their q counts partition the outputs."""
     rng = np.random.default_rng(6)
-    for prm in oracle_pins.random_grid(rng, 200, asym=False):
+    for prm in oracle_pins.random_grid(rng, 200):
         xs = (prm["B"], prm["Ci"]) + tuple(prm["I"])
         ws = (prm["Ci"], prm["Cog"]) + tuple(prm["k"])
-        pl = plan(x_shape=xs, w_shape=ws, stride=prm["s"], padding=prm["p"], dilation=prm["d"],
+        pl = plan(x_shape=xs, w_shape=ws, stride=prm["s"], padding=tuple(zip(prm["p"], prm["ph"])),
+                  dilation=prm["d"],
                   output_padding=prm["op"], groups=prm["groups"])
         for a in range(prm["nd"]):
             s, p, d, k = prm["s"][a], prm["p"][a], prm["d"][a], prm["k"][a]
@@ -236,3 +240,37 @@ def test_axis_phase_arguments():
     assert C.lib().convt_plan_axis_phase(pl.handle, 0, 1, ctypes.byref(q), ctypes.byref(n),
                                          None, None, 0) == 0
     assert (q.value, n.value) == (5, 2)
+
+
+def test_problem_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of convt_problem has the header's size and offsets
+    (compiled from include/convt.h with the host C compiler)."""
+    fields = [f[0] for f in C.Problem._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"convt.h\"\nint main(void){\n"
+                   "printf(\"%zu\\n\", sizeof(convt_problem));\n"
+                   + "".join("printf(\"%%zu\\n\", offsetof(convt_problem, %s));\n" % f for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(t) for t in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(C.Problem)
+    assert out[1:] == [getattr(C.Problem, f).offset for f in fields]
+
+
+def test_padding_hi_fields_validated():
+    L = C.lib()
+    for has_hi, res, hi, want in [(2, 0, 0, 1), (0, 1, 0, 1), (1, 0, -1, 1), (1, 0, 1, 0), (1, 0, 3, 0),
+                                  (0, 0, -5, 0)]:
+        p = C.make_problem((1, 1, 4), (1, 1, 3), stride=2, padding=1)
+        p.has_padding_hi, p.reserved0, p.padding_hi[0] = has_hi, res, hi
+        h = ctypes.c_void_p()
+        info = C.PlanInfo()
+        st = L.convt_plan(ctypes.byref(p), ctypes.byref(h), ctypes.byref(info))
+        assert st == want, (has_hi, res, hi, st)
+        if st == 0:
+            # (4-1)*2 - (1 + p_hi) + (3-1) + 1, p_hi read only when has_padding_hi is 1
+            assert info.out_shape[2] == 8 - (hi if has_hi else 1)
+            L.convt_destroy(h)

@@ -140,10 +140,10 @@ def test_integer_inputs_exact_full_c3_sampled():
 # (including pads beyond d*(k-1)), output paddings, groups and dtypes, on
 # every route that serves each problem.
 # ---------------------------------------------------------------------------
-def grid_cases(n, seed):
+def grid_cases(n, seed, asym=False):
     rng = np.random.default_rng(seed)
     out = []
-    for prm in oracle_pins.random_grid(rng, n, asym=False):
+    for prm in oracle_pins.random_grid(rng, n, asym=asym):
         scale_c = int(rng.choice([1, 1, 4, 12]))
         prm = dict(prm)
         prm["Ci"] *= scale_c
@@ -155,15 +155,30 @@ def grid_cases(n, seed):
 
 
 GRID = grid_cases(60, 2024)
+# the same with different low and high padding on about half the cases
+GRID_ASYM = grid_cases(40, 2025, asym=True)
+
+
+def grid_params(prm):
+    pad = tuple(prm["p"]) if prm["p"] == prm["ph"] else tuple(zip(prm["p"], prm["ph"]))
+    return dict(stride=tuple(prm["s"]), padding=pad, dilation=tuple(prm["d"]),
+                output_padding=tuple(prm["op"]), groups=prm["groups"])
 
 
 @pytest.mark.parametrize("idx", range(len(GRID)))
 def test_random_grid_all_routes(idx):
-    prm = GRID[idx]
+    run_grid_case(GRID[idx], f"grid[{idx}]")
+
+
+@pytest.mark.parametrize("idx", range(len(GRID_ASYM)))
+def test_random_grid_asymmetric_padding_all_routes(idx):
+    run_grid_case(GRID_ASYM[idx], f"grid_asym[{idx}]")
+
+
+def run_grid_case(prm, tag):
     xs = (prm["B"], prm["Ci"]) + tuple(prm["I"])
     ws = (prm["Ci"], prm["Cog"]) + tuple(prm["k"])
-    params = dict(stride=tuple(prm["s"]), padding=tuple(prm["p"]), dilation=tuple(prm["d"]),
-                  output_padding=tuple(prm["op"]), groups=prm["groups"])
+    params = grid_params(prm)
     has_bias = bool(prm["seed"] % 2)
     tens = workloads.make_tensors(xs, ws, prm["Cog"] * prm["groups"], has_bias, prm["dtype"],
                                   "normal(1)", "normal(1)", "normal(1)", prm["seed"])
@@ -174,7 +189,7 @@ def test_random_grid_all_routes(idx):
         except C.ConvtError as e:
             assert e.status == 2
             continue
-        check_full(tens, params, route=route, tag=f"grid[{idx}]")
+        check_full(tens, params, route=route, tag=tag)
 
 
 GROUPED = [
@@ -204,6 +219,53 @@ def test_grouped_route_cases(idx):
                                   500 + idx)
     for route in ["grouped", "auto", "phase_gemm"]:
         check_full(tens, params, route=route, tag=f"grouped[{idx}]")
+
+
+# ---------------------------------------------------------------------------
+# Different low and high padding per axis (the AWS Neuron conv3d_transpose
+# page's padding pairs): workload-like shapes on every route, with pads that
+# trim only one end, pads beyond d*(k-1) and zero pads next to large ones.
+# ---------------------------------------------------------------------------
+ASYM = [
+    # name, x shape, w shape, stride, (lo, hi) pads, dil, op, groups, dtype
+    ("c1_like_f32", (2, 4, 8, 8), (4, 8, 3, 3), (2, 2), ((1, 0), (0, 2)), (1, 1), (1, 1), 1, "f32"),
+    ("c2_like_f32", (2, 40, 300), (40, 24, 8), (4,), ((3, 1),), (1,), (0,), 1, "f32"),
+    ("c3_like_bf16", (2, 72, 9, 13), (72, 136, 4, 4), (2, 2), ((0, 2), (2, 1)), (1, 1), (0, 0), 1,
+     "bf16"),
+    ("c4a_like_bf16", (2, 32, 7, 9), (32, 8, 4, 4), (2, 2), ((2, 0), (0, 1)), (1, 1), (0, 0), 4,
+     "bf16"),
+    ("c4b_like_bf16", (2, 40, 11, 13), (40, 40, 3, 3), (1, 1), ((0, 4), (3, 1)), (2, 2), (0, 0), 1,
+     "bf16"),
+    ("c5_like_bf16", (1, 40, 3, 5, 7), (40, 24, 4, 4, 4), (2, 2, 2), ((1, 2), (0, 1), (2, 0)),
+     (1, 1, 1), (0, 0, 0), 1, "bf16"),
+    ("beyond_dk_f32", (1, 16, 6, 7), (16, 8, 3, 3), (2, 2), ((4, 0), (0, 5)), (1, 1), (1, 0), 1,
+     "f32"),
+    ("grouped_chunks_bf16", (2, 16, 5, 16), (16, 4, 3, 3), (2, 2), ((0, 2), (2, 0)), (1, 1), (1, 1),
+     2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", ASYM, ids=[c[0] for c in ASYM])
+@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "grouped"])
+def test_asymmetric_padding_every_route(case, route):
+    name, xs, ws, s, p, d, op, g, dt = case
+    prm = dict(stride=s, padding=p, dilation=d, output_padding=op, groups=g)
+    for dist, seed in (("uniform", 40), ("int(4)", 41)):
+        tens = workloads.make_tensors(xs, ws, ws[1] * g, True, dt, dist, dist, dist, seed)
+        try:
+            C.get_plan(xs, ws, s, p, d, op, g, True, dt, route)
+        except C.ConvtError as e:
+            assert e.status == 2
+            pytest.skip(f"route {route} does not serve this problem")
+        if dist == "uniform":
+            check_full(tens, prm, route=route, tag=f"asym {name}/{route}")
+            continue
+        say(f"[gpu] integer asym {name} route={route}")
+        y, _ = run_gpu(tens, prm, route)
+        ref, _ = oracle_full(tens, prm)
+        expect = ref if dt == "f32" else rne_bf16(ref)
+        bad = np.argwhere(y != expect)
+        assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0]}"
 
 
 # ---------------------------------------------------------------------------

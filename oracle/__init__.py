@@ -1,4 +1,5 @@
-"""CPU oracle for the ConvTranspose forward pass (double precision).
+"""CPU oracle for the ConvTranspose forward pass and its input gradient
+(double precision).
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline leg are the only code that may import this package. The GPU library
@@ -51,6 +52,13 @@ def _bind(path: str):
                                         ctypes.c_int64, pd, pd, pd, ctypes.c_int64, p64, pd,
                                         pd, ctypes.c_int]
     lib.convt_oracle_points.restype = ctypes.c_int
+    lib.convt_oracle_backward_data.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64, p64,
+                                               ctypes.c_int64, pd, pd, pd, pd, ctypes.c_int]
+    lib.convt_oracle_backward_data.restype = ctypes.c_int
+    lib.convt_oracle_backward_data_points.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64,
+                                                      p64, ctypes.c_int64, pd, pd, ctypes.c_int64,
+                                                      p64, pd, pd, ctypes.c_int]
+    lib.convt_oracle_backward_data_points.restype = ctypes.c_int
     lib.convt_oracle_max_threads.argtypes = []
     lib.convt_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -167,6 +175,57 @@ class Oracle:
         return yv, sv
 
 
+    def backward_data(self, dy: np.ndarray, w: np.ndarray, x_shape, stride=None, padding=None,
+                      dilation=None, output_padding=None, groups: int = 1,
+                      with_scale: bool = True, nthreads: int = 0):
+        """Input gradient dx (shape x_shape) for the upstream gradient dy (the
+        forward output's shape), in float64. Returns (dx, scale)."""
+        x_shape = tuple(int(v) for v in x_shape)
+        nd, s, p, ph, d, op = _attrs(x_shape, w.shape, stride, padding, dilation, output_padding)
+        oshape = self.out_shape(x_shape, w.shape, s, list(zip(p, ph)), d, op, groups)
+        if tuple(dy.shape) != oshape:
+            raise ValueError(f"dy must have the output shape {oshape}")
+        ya, yp = _f64(dy)
+        wa, wp = _f64(w)
+        dx = np.empty(x_shape, dtype=np.float64)
+        sc = np.empty(x_shape, dtype=np.float64) if with_scale else None
+        keep = [_i64(x_shape), _i64(w.shape), _i64(s), _i64(p), _i64(ph), _i64(d), _i64(op)]
+        rc = self.lib.convt_oracle_backward_data(
+            nd, *[k[1] for k in keep], int(groups), yp, wp,
+            dx.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            sc.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if sc is not None else None,
+            int(nthreads))
+        if rc != 0:
+            raise ValueError("ill-formed transposed convolution")
+        return dx, sc
+
+    def backward_data_points(self, dy: np.ndarray, w: np.ndarray, x_shape, pts: np.ndarray,
+                             stride=None, padding=None, dilation=None, output_padding=None,
+                             groups: int = 1, nthreads: int = 0):
+        """dx at the given points (rows of (b, ci, i...)), each on its own.
+        Returns (dx, scale) as float64 arrays of length n."""
+        x_shape = tuple(int(v) for v in x_shape)
+        nd, s, p, ph, d, op = _attrs(x_shape, w.shape, stride, padding, dilation, output_padding)
+        oshape = self.out_shape(x_shape, w.shape, s, list(zip(p, ph)), d, op, groups)
+        if tuple(dy.shape) != oshape:
+            raise ValueError(f"dy must have the output shape {oshape}")
+        pa = np.ascontiguousarray(np.asarray(pts, dtype=np.int64).reshape(-1, 2 + nd))
+        ya, yp = _f64(dy)
+        wa, wp = _f64(w)
+        n = pa.shape[0]
+        xv = np.empty(n, dtype=np.float64)
+        sv = np.empty(n, dtype=np.float64)
+        keep = [_i64(x_shape), _i64(w.shape), _i64(s), _i64(p), _i64(ph), _i64(d), _i64(op)]
+        rc = self.lib.convt_oracle_backward_data_points(
+            nd, *[k[1] for k in keep], int(groups), yp, wp, n,
+            pa.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            xv.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            sv.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(nthreads))
+        if rc != 0:
+            raise ValueError("ill-formed problem or point out of range")
+        return xv, sv
+
+
 _default: Optional[Oracle] = None
 
 
@@ -194,3 +253,11 @@ def forward(*args, **kwargs):
 
 def points(*args, **kwargs):
     return default().points(*args, **kwargs)
+
+
+def backward_data(*args, **kwargs):
+    return default().backward_data(*args, **kwargs)
+
+
+def backward_data_points(*args, **kwargs):
+    return default().backward_data_points(*args, **kwargs)

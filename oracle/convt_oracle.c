@@ -44,6 +44,19 @@
  * Parallelism: OpenMP over (b, oc) output planes. Each plane is written by one
  * thread only and its terms are added in a fixed order, so results do not
  * depend on the thread count.
+ *
+ * Backward data (the input gradient, named as the adjoint for the input in
+ * the SKaiNET page's Summary, convTranspose2dBackward): y is linear in x, and
+ * x[b, ci, i] enters exactly the terms listed above, so for an upstream
+ * gradient dy of y's shape
+ *
+ *   dx[b, ci, i] = sum over oc in the group of ci and taps kk
+ *                  with o = i*s - p + kk*d (per axis) and 0 <= o < O:
+ *                    dy[b, oc, o] * W[ci, oc - g*Cog, kk]
+ *
+ * (the same index relation read from the input side; no bias term). It is
+ * computed one (b, ci) plane at a time, with its own magnitude sum of
+ * |dy * W| over the same terms.
  */
 #include <math.h>
 #include <stddef.h>
@@ -266,4 +279,128 @@ int convt_oracle_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* Backward data: dx = d<y, dy>/dx for the problem's shapes. dy: [B, C_out,
+ * O...], w: [C_in, Cog, k...], dx: [B, C_in, I...], scale: dx's shape or NULL.
+ * Each dx element gathers the (oc, kk) terms whose output o = i*s - p + kk*d
+ * lies inside y. Returns 0 or -1. */
+int convt_oracle_backward_data(int ndim, const int64_t *x_shape, const int64_t *w_shape,
+                               const int64_t *stride, const int64_t *padding,
+                               const int64_t *padding_end, const int64_t *dilation,
+                               const int64_t *output_padding, int64_t groups, const double *dy,
+                               const double *w, double *dx, double *scale, int nthreads)
+{
+    oracle_prob pb;
+    if (make_prob(ndim, x_shape, w_shape, stride, padding, padding_end, dilation, output_padding,
+                  groups, &pb))
+        return -1;
+    const int64_t isz = pb.I[0] * pb.I[1] * pb.I[2];
+    const int64_t ksz = pb.K[0] * pb.K[1] * pb.K[2];
+    const int64_t osz = pb.O[0] * pb.O[1] * pb.O[2];
+    const int64_t planes = pb.B * pb.Ci;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t plane = 0; plane < planes; ++plane) {
+        const int64_t b = plane / pb.Ci;
+        const int64_t ci = plane % pb.Ci;
+        const int64_t g = ci / pb.Cig;
+        double *xp = dx + plane * isz;
+        double *sp = scale ? scale + plane * isz : NULL;
+        for (int64_t i0 = 0; i0 < pb.I[0]; ++i0)
+        for (int64_t i1 = 0; i1 < pb.I[1]; ++i1)
+        for (int64_t i2 = 0; i2 < pb.I[2]; ++i2) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t ocl = 0; ocl < pb.Cog; ++ocl) {
+                const double *yp = dy + (b * pb.Co + g * pb.Cog + ocl) * osz;
+                const double *wp = w + (ci * pb.Cog + ocl) * ksz;
+                for (int64_t k0 = 0; k0 < pb.K[0]; ++k0) {
+                    const int64_t o0 = i0 * pb.S[0] - pb.P[0] + k0 * pb.D[0];
+                    if (o0 < 0 || o0 >= pb.O[0]) continue;
+                    for (int64_t k1 = 0; k1 < pb.K[1]; ++k1) {
+                        const int64_t o1 = i1 * pb.S[1] - pb.P[1] + k1 * pb.D[1];
+                        if (o1 < 0 || o1 >= pb.O[1]) continue;
+                        for (int64_t k2 = 0; k2 < pb.K[2]; ++k2) {
+                            const int64_t o2 = i2 * pb.S[2] - pb.P[2] + k2 * pb.D[2];
+                            if (o2 < 0 || o2 >= pb.O[2]) continue;
+                            const double t = yp[(o0 * pb.O[1] + o1) * pb.O[2] + o2] *
+                                             wp[(k0 * pb.K[1] + k1) * pb.K[2] + k2];
+                            acc += t;
+                            mag += fabs(t);
+                        }
+                    }
+                }
+            }
+            const int64_t i = (i0 * pb.I[1] + i1) * pb.I[2] + i2;
+            xp[i] = acc;
+            if (sp) sp[i] = mag;
+        }
+    }
+    return 0;
+}
+
+/* Selected dx elements of the backward-data pass, each from the definition
+ * above. pts: npts rows of (b, ci, i...). Returns 0, or -1 for a malformed
+ * problem or an out-of-range point. */
+int convt_oracle_backward_data_points(int ndim, const int64_t *x_shape, const int64_t *w_shape,
+                                      const int64_t *stride, const int64_t *padding,
+                                      const int64_t *padding_end, const int64_t *dilation,
+                                      const int64_t *output_padding, int64_t groups,
+                                      const double *dy, const double *w, int64_t npts,
+                                      const int64_t *pts, double *dxv, double *sv, int nthreads)
+{
+    oracle_prob pb;
+    if (make_prob(ndim, x_shape, w_shape, stride, padding, padding_end, dilation, output_padding,
+                  groups, &pb))
+        return -1;
+    const int lead = 3 - ndim;
+    for (int64_t n = 0; n < npts; ++n) {
+        const int64_t *pt = pts + n * (2 + ndim);
+        if (pt[0] < 0 || pt[0] >= pb.B || pt[1] < 0 || pt[1] >= pb.Ci) return -1;
+        for (int j = 0; j < ndim; ++j)
+            if (pt[2 + j] < 0 || pt[2 + j] >= pb.I[lead + j]) return -1;
+    }
+    const int64_t ksz = pb.K[0] * pb.K[1] * pb.K[2];
+    const int64_t osz = pb.O[0] * pb.O[1] * pb.O[2];
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t n = 0; n < npts; ++n) {
+        const int64_t *pt = pts + n * (2 + ndim);
+        int64_t i[3] = {0, 0, 0};
+        for (int j = 0; j < ndim; ++j) i[lead + j] = pt[2 + j];
+        const int64_t b = pt[0], ci = pt[1], g = ci / pb.Cig;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t ocl = 0; ocl < pb.Cog; ++ocl) {
+            const double *yp = dy + (b * pb.Co + g * pb.Cog + ocl) * osz;
+            const double *wp = w + (ci * pb.Cog + ocl) * ksz;
+            for (int64_t k0 = 0; k0 < pb.K[0]; ++k0) {
+                const int64_t o0 = i[0] * pb.S[0] - pb.P[0] + k0 * pb.D[0];
+                if (o0 < 0 || o0 >= pb.O[0]) continue;
+                for (int64_t k1 = 0; k1 < pb.K[1]; ++k1) {
+                    const int64_t o1 = i[1] * pb.S[1] - pb.P[1] + k1 * pb.D[1];
+                    if (o1 < 0 || o1 >= pb.O[1]) continue;
+                    for (int64_t k2 = 0; k2 < pb.K[2]; ++k2) {
+                        const int64_t o2 = i[2] * pb.S[2] - pb.P[2] + k2 * pb.D[2];
+                        if (o2 < 0 || o2 >= pb.O[2]) continue;
+                        const double t = yp[(o0 * pb.O[1] + o1) * pb.O[2] + o2] *
+                                         wp[(k0 * pb.K[1] + k1) * pb.K[2] + k2];
+                        acc += t;
+                        mag += fabs(t);
+                    }
+                }
+            }
+        }
+        dxv[n] = acc;
+        if (sv) sv[n] = mag;
+    }
+    return 0;
 }

@@ -466,6 +466,118 @@ def check_rejects_ill_formed(orc):
         raise AssertionError(f"accepted {c}")
 
 
+# ---------------------------------------------------------------------------
+# Backward data (input gradient)
+# ---------------------------------------------------------------------------
+
+def check_bwd_is_jacobian_transpose(orc):
+    """y is linear in x: column j of its Jacobian is the forward pass of the
+    unit input e_j (no bias). The input gradient must be J^T dy, exactly on
+    integer data."""
+    rng = np.random.default_rng(30)
+    for prm in random_grid(rng, 14):
+        x, w, _, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
+                                    prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
+                                    prm["d"], prm["op"], ints=True, bias=False, ph=prm["ph"])
+        y0, _ = orc.forward(x, w, None, with_scale=False, **kw)
+        cols = []
+        for j in range(x.size):
+            e = np.zeros(x.size)
+            e[j] = 1.0
+            cols.append(orc.forward(e.reshape(x.shape), w, None, with_scale=False, **kw)[0].ravel())
+        J = np.stack(cols, axis=1)  # [y.size, x.size]
+        dy = rng.integers(-4, 5, size=y0.shape).astype(np.float64)
+        dx, _ = orc.backward_data(dy, w, x.shape, **kw)
+        assert np.array_equal(dx.ravel(), J.T @ dy.ravel()), prm
+
+
+def check_bwd_adjoint_identity(orc):
+    """<convT(x, W), dy> = <x, dx(dy, W)> on random real data."""
+    rng = np.random.default_rng(31)
+    for prm in random_grid(rng, 40):
+        x, w, _, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
+                                    prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
+                                    prm["d"], prm["op"], bias=False, ph=prm["ph"])
+        y, _ = orc.forward(x, w, None, with_scale=False, **kw)
+        dy = rng.standard_normal(y.shape)
+        dx, sc = orc.backward_data(dy, w, x.shape, **kw)
+        lhs, rhs = float(np.sum(y * dy)), float(np.sum(x * dx))
+        mag = float(np.sum(np.abs(x) * sc)) + 1.0
+        assert abs(lhs - rhs) <= 1e-12 * mag, (prm, lhs, rhs)
+
+
+def check_bwd_valid_correlation(orc):
+    """Stride 1, no padding, dilation 1: the forward pass is a full
+    convolution, so its input gradient is the valid cross-correlation of dy
+    with the kernel (scipy)."""
+    rng = np.random.default_rng(32)
+    for shape_x, shape_w in [((7,), (3,)), ((5, 4), (3, 2)), ((3, 4, 2), (2, 3, 2))]:
+        w = rng.standard_normal(shape_w)
+        oshape = tuple(a + b - 1 for a, b in zip(shape_x, shape_w))
+        dy = rng.standard_normal(oshape)
+        dx, _ = orc.backward_data(dy[None, None], w[None, None], (1, 1) + shape_x)
+        ref = scipy.signal.correlate(dy, w, mode="valid", method="direct")
+        _close(dx[0, 0], ref)
+
+
+def brute_force_bwd(dy, w, x_shape, s, p, d, groups):
+    """dx by enumerating every (input position, tap, output channel) in
+    Python: dx[b, ci, i] collects dy[b, oc, o] * W[ci, oc - g*Cog, kk] for
+    o = i*s - p + kk*d inside dy."""
+    nd = len(x_shape) - 2
+    B, Ci = x_shape[:2]
+    Cig, Cog = Ci // groups, w.shape[1]
+    k = w.shape[2:]
+    I = x_shape[2:]
+    O = dy.shape[2:]
+    dx = np.zeros(x_shape)
+    for b in range(B):
+        for ci in range(Ci):
+            g = ci // Cig
+            for i in itertools.product(*[range(t) for t in I]):
+                acc = 0.0
+                for oc in range(g * Cog, (g + 1) * Cog):
+                    for kk in itertools.product(*[range(t) for t in k]):
+                        o = tuple(i[a] * s[a] - p[a] + kk[a] * d[a] for a in range(nd))
+                        if all(0 <= o[a] < O[a] for a in range(nd)):
+                            acc += float(dy[(b, oc) + o]) * float(w[(ci, oc - g * Cog) + kk])
+                dx[(b, ci) + i] = acc
+    return dx
+
+
+def check_bwd_brute_force(orc):
+    rng = np.random.default_rng(33)
+    for prm in random_grid(rng, 20, nds=(1, 2)):
+        x, w, _, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
+                                    prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
+                                    prm["d"], prm["op"], bias=False, ph=prm["ph"])
+        oshape = orc.out_shape(x.shape, w.shape, kw["stride"], kw["padding"], kw["dilation"],
+                               kw["output_padding"], kw["groups"])
+        dy = rng.standard_normal(oshape)
+        dx, _ = orc.backward_data(dy, w, x.shape, **kw)
+        _close(dx, brute_force_bwd(dy, w, x.shape, prm["s"], prm["p"], prm["d"], prm["groups"]))
+
+
+def check_bwd_points_and_scale(orc):
+    """The point form equals the full pass, and the magnitude sum equals the
+    input gradient of |dy| with |W|."""
+    rng = np.random.default_rng(34)
+    for prm in random_grid(rng, 25):
+        x, w, _, kw = _rand_problem(rng, prm["nd"], prm["B"], prm["Ci"], prm["Cog"],
+                                    prm["groups"], prm["I"], prm["k"], prm["s"], prm["p"],
+                                    prm["d"], prm["op"], bias=False, ph=prm["ph"])
+        oshape = orc.out_shape(x.shape, w.shape, kw["stride"], kw["padding"], kw["dilation"],
+                               kw["output_padding"], kw["groups"])
+        dy = rng.standard_normal(oshape)
+        dx, sc = orc.backward_data(dy, w, x.shape, **kw)
+        pts = np.array(list(itertools.product(*[range(t) for t in x.shape])), dtype=np.int64)
+        xv, sv = orc.backward_data_points(dy, w, x.shape, pts, **kw)
+        _close(xv, dx.ravel())
+        _close(sv, sc.ravel())
+        ref, _ = orc.backward_data(np.abs(dy), np.abs(w), x.shape, **kw)
+        _close(sc, ref)
+
+
 ALL_CHECKS = [
     check_golden_cases,
     check_output_shapes,
@@ -483,4 +595,9 @@ ALL_CHECKS = [
     check_points_match_forward,
     check_thread_count_independent,
     check_rejects_ill_formed,
+    check_bwd_is_jacobian_transpose,
+    check_bwd_adjoint_identity,
+    check_bwd_valid_correlation,
+    check_bwd_brute_force,
+    check_bwd_points_and_scale,
 ]

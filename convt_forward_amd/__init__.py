@@ -51,7 +51,7 @@ class Problem(ctypes.Structure):
         ("has_bias", ctypes.c_int32),
         ("route", ctypes.c_int32),
         ("has_padding_hi", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("route_bwd", ctypes.c_int32),
         ("padding_hi", ctypes.c_int64 * MAX_NDIM),
     ]
 
@@ -64,7 +64,8 @@ class PlanInfo(ctypes.Structure):
         ("n_phases", ctypes.c_int64),
         ("useful_flops", ctypes.c_int64),
         ("route", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("route_bwd", ctypes.c_int32),
+        ("bwd_workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -75,6 +76,13 @@ def lib() -> ctypes.CDLL:
     """The loaded libconvt.so. Raises if it has not been built."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime; loading it first makes this library
+        # bind to that same runtime (a second copy of the runtime in the
+        # process, loaded by this library first, finds no device)
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with `python -m convt_forward_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
@@ -87,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.convt_prepare_weights.restype = ctypes.c_int
         L.convt_forward_prepared.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.convt_forward_prepared.restype = ctypes.c_int
+        L.convt_backward_data.argtypes = [vp, vp, vp, vp, vp, vp]
+        L.convt_backward_data.restype = ctypes.c_int
         L.convt_destroy.argtypes = [vp]
         L.convt_destroy.restype = None
         L.convt_status_string.argtypes = [ctypes.c_int]
@@ -126,7 +136,7 @@ def _pads(v, nd: int) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
 
 def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, padding=0, dilation=1,
                  output_padding=0, groups: int = 1, has_bias: bool = False, dtype: str = "f32",
-                 route: str = "auto") -> Problem:
+                 route: str = "auto", route_bwd: str = "auto") -> Problem:
     nd = len(x_shape) - 2
     if not 1 <= nd <= MAX_NDIM or len(w_shape) != nd + 2:
         raise ValueError("x must be [B, C_in, I...] and w [C_in, C_out/groups, k...] with 1-3 spatial axes")
@@ -149,6 +159,7 @@ def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, paddi
     p.groups = int(groups)
     p.has_bias = 1 if has_bias else 0
     p.route = ROUTES[route]
+    p.route_bwd = ROUTES[route_bwd]
     return p
 
 
@@ -191,6 +202,14 @@ class Plan:
         return ROUTE_NAMES[int(self.info.route)]
 
     @property
+    def route_bwd(self) -> str:
+        return ROUTE_NAMES[int(self.info.route_bwd)]
+
+    @property
+    def bwd_workspace_bytes(self) -> int:
+        return int(self.info.bwd_workspace_bytes)
+
+    @property
     def useful_flops(self) -> int:
         return int(self.info.useful_flops)
 
@@ -229,6 +248,12 @@ class Plan:
                                           workspace or None, stream or None)
         if st != 0:
             raise ConvtError(st, "convt_forward_prepared")
+
+    def backward_data_ptr(self, dy: int, w: int, dx: int, workspace: int, stream: int) -> None:
+        st = lib().convt_backward_data(self._h, dy or None, w or None, dx or None,
+                                       workspace or None, stream or None)
+        if st != 0:
+            raise ConvtError(st, "convt_backward_data")
 
     # --- torch tensors ------------------------------------------------------
     def _check(self, t, shape, name):
@@ -281,20 +306,52 @@ class Plan:
                          y.data_ptr(), workspace.data_ptr(), stream)
         return y
 
+    def new_input_grad(self, device):
+        import torch
+        dt = torch.float32 if self.problem.dtype == DTYPES["f32"] else torch.bfloat16
+        return torch.empty(tuple(self.problem.x_shape[:2 + self.ndim]), dtype=dt, device=device)
+
+    def new_bwd_workspace(self, device):
+        import torch
+        return torch.empty(max(self.bwd_workspace_bytes, 16), dtype=torch.uint8, device=device)
+
+    def backward_data(self, dy, w, dx=None, workspace=None, stream=None):
+        """Enqueue dx = the gradient with respect to x for the upstream gradient
+        dy (shape out_shape). Allocates dx / the workspace with torch when not
+        given. Returns dx."""
+        import torch
+        p = self.problem
+        nd = self.ndim
+        self._check(dy, self.out_shape, "dy")
+        self._check(w, tuple(p.w_shape[:2 + nd]), "w")
+        if dx is None:
+            dx = self.new_input_grad(dy.device)
+        else:
+            self._check(dx, tuple(p.x_shape[:2 + nd]), "dx")
+        if workspace is None:
+            workspace = self.new_bwd_workspace(dy.device)
+        elif workspace.numel() * workspace.element_size() < self.bwd_workspace_bytes:
+            raise ValueError("workspace too small")
+        if stream is None:
+            stream = torch.cuda.current_stream(dy.device).cuda_stream
+        self.backward_data_ptr(dy.data_ptr(), w.data_ptr(), dx.data_ptr(), workspace.data_ptr(),
+                               stream)
+        return dx
+
 
 _plan_cache: Dict[tuple, Plan] = {}
 
 
 def get_plan(x_shape, w_shape, stride=1, padding=0, dilation=1, output_padding=0, groups=1,
-             has_bias=False, dtype="f32", route="auto") -> Plan:
+             has_bias=False, dtype="f32", route="auto", route_bwd="auto") -> Plan:
     nd = len(x_shape) - 2
     key = (tuple(x_shape), tuple(w_shape), _tup(stride, nd, "stride"), _pads(padding, nd),
            _tup(dilation, nd, "dilation"), _tup(output_padding, nd, "output_padding"), int(groups),
-           bool(has_bias), dtype, route)
+           bool(has_bias), dtype, route, route_bwd)
     pl = _plan_cache.get(key)
     if pl is None:
         pl = Plan.create(x_shape, w_shape, stride, padding, dilation, output_padding, groups,
-                         has_bias, dtype, route)
+                         has_bias, dtype, route, route_bwd)
         _plan_cache[key] = pl
     return pl
 
@@ -322,3 +379,14 @@ def conv_transpose(x, w, bias=None, stride=1, padding=0, dilation=1, output_padd
     pl = get_plan(tuple(x.shape), tuple(w.shape), stride, padding, dilation, output_padding, groups,
                   bias is not None, torch_dtype_name(x), route)
     return pl.forward(x, w, bias, y=y, workspace=workspace, stream=stream)
+
+
+def conv_transpose_backward_data(dy, w, x_shape, stride=1, padding=0, dilation=1,
+                                 output_padding=0, groups=1, route: str = "auto", dx=None,
+                                 workspace=None, stream=None):
+    """Gradient of a loss with respect to the input x of conv_transpose, given
+    its gradient dy with respect to the output (on the GPU through libconvt).
+    Returns dx, of shape x_shape."""
+    pl = get_plan(tuple(x_shape), tuple(w.shape), stride, padding, dilation, output_padding,
+                  groups, False, torch_dtype_name(dy), "auto", route)
+    return pl.backward_data(dy, w, dx=dx, workspace=workspace, stream=stream)

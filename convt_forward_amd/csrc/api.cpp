@@ -119,6 +119,39 @@ convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, cons
     return convt_forward_prepared(plan, x, w, bias, y, workspace, stream);
 }
 
+convt_status convt_backward_data(convt_plan_t plan, const void *dy, const void *w, void *dx,
+                                 void *workspace, void *stream) {
+    if (!plan) return CONVT_ERR_INVALID_ARGUMENT;
+    const convt::Plan &pl = plan->plan;
+    const int nd = pl.ndim;
+    const hipStream_t s = (hipStream_t)stream;
+    if (pl.route_bwd == CONVT_ROUTE_NONE || numel(pl.prob.x_shape, 2 + nd) == 0) return CONVT_OK;
+    if (!dx) return CONVT_ERR_INVALID_ARGUMENT;
+    if (pl.route_bwd == CONVT_ROUTE_FILL)
+        return device_status(convt::launch_fill_dp(pl.bdp, pl.elem_bytes, nullptr, dx, s));
+    if (!dy || !w) return CONVT_ERR_INVALID_ARGUMENT;
+    switch (pl.route_bwd) {
+        case CONVT_ROUTE_NAIVE:
+            return device_status(convt::launch_naive_bwd(pl, dy, w, dx, s));
+        case CONVT_ROUTE_PHASE_GEMM: {
+            if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
+            convt_status st = device_status(convt::launch_reorder_bwd(pl, w, workspace, s));
+            if (st != CONVT_OK) return st;
+            const void *yin = dy;
+            if (pl.bwd_xp_bytes > 0) {
+                // bfloat16: the channel-chunked copy of dy after the weights
+                void *xp = (char *)workspace + pl.bwd_xp_offset;
+                st = device_status(convt::launch_pack_dp(pl.bdp, dy, xp, s));
+                if (st != CONVT_OK) return st;
+                yin = xp;
+            }
+            return device_status(convt::launch_phase_gemm_bwd(pl, yin, workspace, dx, s));
+        }
+        default:
+            return CONVT_ERR_UNSUPPORTED;
+    }
+}
+
 const char *convt_status_string(convt_status status) {
     switch (status) {
         case CONVT_OK: return "ok";

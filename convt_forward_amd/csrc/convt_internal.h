@@ -79,6 +79,7 @@ struct DevParams {
     int32_t ktot_pad;          // taps per group in the reordered weights (phase GEMM: each
                                // phase padded with zero taps to a multiple of gemm_gs)
     int32_t ph_tab_ok;         // 1: ph[] holds every phase (nphase <= kMaxPhaseTab)
+    int32_t bwd_nstages;       // backward-data GEMM: pipeline stages of a block (all phases)
     PhaseRec ph[kMaxPhaseTab];
 };
 
@@ -93,6 +94,16 @@ struct Plan {
     int64_t xp_offset;  // bfloat16 phase GEMM: byte offset of the channel-chunked copy of x
     int64_t xp_bytes;   // its size (0 when not used)
     int32_t elem_bytes; // 4 (float32) or 2 (bfloat16)
+    // Backward data. bdp is the problem as the backward kernels see it: the
+    // input is dy (ax[a].I = O, channels Co in groups of Cog), the output is
+    // dx (ax[a].O = I, channels Ci in groups of Cig); the axes keep the
+    // forward's stride-phase tables (residues, taps, offsets).
+    int32_t route_bwd;
+    DevParams bdp;
+    int64_t bwd_wr_elems;    // elements of the backward-reordered weights (offset 0)
+    int64_t bwd_tab_offset;  // byte offset of the per-tap halo shift table
+    int64_t bwd_xp_offset;   // bfloat16: byte offset of the channel-chunked copy of dy
+    int64_t bwd_xp_bytes;    // its size (0 when not used)
 };
 
 // Tile constants of the kernels, shared with the planner so that it sizes

@@ -425,8 +425,11 @@ __global__ __launch_bounds__(256) void pack_x8_kernel(DevParams p, const uint16_
 }
 
 hipError_t launch_pack_x(const Plan &pl, const void *x, void *xp, hipStream_t stream) {
-    const DevParams &p = pl.dp;
     if (pl.xp_bytes == 0) return hipSuccess;
+    return launch_pack_dp(pl.dp, x, xp, stream);
+}
+
+hipError_t launch_pack_dp(const DevParams &p, const void *x, void *xp, hipStream_t stream) {
     if (p.x_plane % 8 == 0 && (uintptr_t)x % 16 == 0) {
         const int64_t ptiles = ((int64_t)p.x_plane + 255) / 256;
         const int64_t blocks = (int64_t)p.B * p.G * (p.cig_pad / 16) * ptiles;
@@ -465,10 +468,14 @@ static unsigned grid_for(int64_t total) {
 }
 
 hipError_t launch_fill(const Plan &pl, const void *bias, void *y, hipStream_t stream) {
-    const DevParams &p = pl.dp;
+    return launch_fill_dp(pl.dp, pl.elem_bytes, bias, y, stream);
+}
+
+hipError_t launch_fill_dp(const DevParams &p, int elem_bytes, const void *bias, void *y,
+                          hipStream_t stream) {
     const int64_t total = (int64_t)p.B * p.Co * p.y_plane;
     if (total <= 0) return hipSuccess;
-    if (pl.elem_bytes == 2)
+    if (elem_bytes == 2)
         hipLaunchKernelGGL(fill_kernel<uint16_t>, dim3(grid_for(total)), dim3(256), 0, stream, p,
                            (const uint16_t *)bias, (uint16_t *)y, total);
     else
@@ -637,6 +644,221 @@ hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const voi
     else
         hipLaunchKernelGGL(direct_kernel<float>, dim3((unsigned)blocks), dim3(256), lds, stream, p,
                            (const float *)x, (const float *)w, (const float *)bias, (float *)y);
+    return hipGetLastError();
+}
+
+}  // namespace convt
+
+namespace convt {
+
+// ---------------------------------------------------------------------------
+// Backward data, naive gather: one thread per dx element. dx[b, ci, i]
+// collects dy[b, oc, o] * W[ci, oc - g*Cog, kk] over the taps kk whose output
+// o = i*s - p + kk*d lies inside y and the Cog output channels of ci's group;
+// float32 accumulation, one rounding. Serves any problem.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void naive_bwd_kernel(DevParams p, const T *__restrict__ dy,
+                                                         const T *__restrict__ w,
+                                                         T *__restrict__ dx, int64_t total) {
+    const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t plane = idx / p.x_plane;
+        const int i = (int)(idx % p.x_plane);
+        const int ci = (int)(plane % p.Ci);
+        const int64_t b = plane / p.Ci;
+        const int i2 = i % a2.I, i1 = (i / a2.I) % a1.I, i0 = i / (a2.I * a1.I);
+        const int g = ci / p.Cig;
+        const T *yb = dy + ((int64_t)b * p.Co + (int64_t)g * p.Cog) * p.y_plane;
+        const T *wb = w + (int64_t)ci * p.Cog * p.ktot;
+        float acc = 0.0f;
+        for (int k0 = 0; k0 < a0.K; ++k0) {
+            const int o0 = i0 * a0.S - a0.P + k0 * a0.D;
+            if (o0 < 0 || o0 >= a0.O) continue;
+            for (int k1 = 0; k1 < a1.K; ++k1) {
+                const int o1 = i1 * a1.S - a1.P + k1 * a1.D;
+                if (o1 < 0 || o1 >= a1.O) continue;
+                for (int k2 = 0; k2 < a2.K; ++k2) {
+                    const int o2 = i2 * a2.S - a2.P + k2 * a2.D;
+                    if (o2 < 0 || o2 >= a2.O) continue;
+                    const int64_t opos = ((int64_t)o0 * a1.O + o1) * a2.O + o2;
+                    const int kk = (k0 * a1.K + k1) * a2.K + k2;
+                    for (int ocl = 0; ocl < p.Cog; ++ocl)
+                        acc += to_f32(yb[(int64_t)ocl * p.y_plane + opos]) *
+                               to_f32(wb[(int64_t)ocl * p.ktot + kk]);
+                }
+            }
+        }
+        dx[idx] = from_f32<T>(acc);
+    }
+}
+
+hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void *dx,
+                            hipStream_t stream) {
+    const DevParams &p = pl.dp;  // the forward problem's axes and channels
+    const int64_t total = (int64_t)p.B * p.Ci * p.x_plane;
+    if (total <= 0) return hipSuccess;
+    if (pl.elem_bytes == 2)
+        hipLaunchKernelGGL(naive_bwd_kernel<uint16_t>, dim3(grid_for(total)), dim3(256), 0, stream,
+                           p, (const uint16_t *)dy, (const uint16_t *)w, (uint16_t *)dx, total);
+    else
+        hipLaunchKernelGGL(naive_bwd_kernel<float>, dim3(grid_for(total)), dim3(256), 0, stream, p,
+                           (const float *)dy, (const float *)w, (float *)dx, total);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weight reorder for the backward-data GEMM (p: the backward problem, whose
+// rows m are the Cig input channels of a group and whose K channels are its
+// Cog output channels):
+//     W[g*Cig + m][oc][kk] -> Wb[g][tap][chunk][m][32 bytes of oc]
+// tap: kk's index in the plan's tap order (phase by phase, each padded with
+// zero taps to whole groups of gemm_gs); chunk = oc / BK (16 bfloat16 or 8
+// float32 channels); the two 16-byte halves of a row swap where bit 3 of m
+// is set (the operand reads' XOR swizzle). Rows past Cig, channels past Cog
+// and padding taps are zero.
+//
+// A block owns 8 rows m, OCB channels oc (whole chunks) and KT taps kk: it
+// reads the runs W[m][oc0 .. oc0 + OCB)[kk0 .. kk0 + KT) into LDS with
+// consecutive lanes on consecutive elements, then writes, per (tap, chunk),
+// the 8 rows' 256 contiguous bytes, consecutive lanes on consecutive 16-byte
+// halves. Block 0 also writes the halo shift table: entry tapbase(P) + t
+// holds, for tap t = (j0, j1, j2) of phase P with input offsets off_a =
+// off0_a + j_a * ostep_a, the row of its window in the halo box,
+// ((umax0 - off0) * E1 + (umax1 - off1)) * E2 + (umax2 - off2), E1 and E2 the
+// box extents (the dx tile plus umax - umin); padding taps get 0.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *__restrict__ w,
+                                                          T *__restrict__ wr,
+                                                          int32_t *__restrict__ tab, int OCB,
+                                                          int KT) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    constexpr int VEC = 16 / sizeof(T), BK = 2 * VEC, MB = 8;
+    const int Cm = p.Cog, Coc = p.Cig, ktot = p.ktot;
+    const int nchunks = p.cig_pad / BK;
+    const int nob = (p.cig_pad + OCB - 1) / OCB;
+    const int nmb = p.cog_pad / MB;
+    const int nkt = (ktot + KT - 1) / KT;
+    int bid = blockIdx.x;
+    const int kb = bid % nkt;
+    bid /= nkt;
+    const int ob = bid % nob;
+    bid /= nob;
+    const int mb = bid % nmb;
+    const int g = bid / nmb;
+    const int m0 = mb * MB, oc0 = ob * OCB, kk0 = kb * KT;
+    const int nk = ktot - kk0 < KT ? ktot - kk0 : KT;
+    const int noc = p.cig_pad - oc0 < OCB ? p.cig_pad - oc0 : OCB;  // whole chunks
+    T *brick = (T *)lds_raw;  // [MB][OCB][KT]
+    int *dst_tap = (int *)(lds_raw + (size_t)MB * OCB * KT * sizeof(T));
+    const int K1 = p.ax[1].K, K2 = p.ax[2].K;
+    for (int k = threadIdx.x; k < nk; k += 256) {
+        const int kk = kk0 + k;
+        dst_tap[k] = tap_in_table(p, kk / (K1 * K2), (kk / K2) % K1, kk % K2);
+    }
+    const int n_in = MB * noc * nk;
+    for (int e0 = threadIdx.x; e0 < n_in; e0 += 256 * 8) {
+        T v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + 256 * u;
+            const int i = e / (noc * nk), r = e - i * (noc * nk);
+            const int col = r / nk, k = r - col * nk;
+            const int m = m0 + i, oc = oc0 + col;
+            const bool ok = e < n_in && m < Cm && oc < Coc;
+            v[u] = w[ok ? (((int64_t)g * Cm + m) * Coc + oc) * ktot + kk0 + k : 0];
+            if (!ok) v[u] = from_f32<T>(0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + 256 * u;
+            if (e < n_in) {
+                const int i = e / (noc * nk), r = e - i * (noc * nk);
+                brick[(i * OCB + r / nk) * KT + r % nk] = v[u];
+            }
+        }
+    }
+    __syncthreads();
+    const int64_t chunk_elems = (int64_t)p.cog_pad * BK;
+    T *wg = wr + (int64_t)g * p.ktot_pad * nchunks * chunk_elems;
+    const int ncc = noc / BK;
+    const int n_out = nk * ncc * MB * 2;
+    for (int n = threadIdx.x; n < n_out; n += 256) {
+        const int half = n & 1, i = (n >> 1) & (MB - 1), rest = n >> 4;
+        const int cc = rest % ncc, k = rest / ncc;
+        const int m = m0 + i;
+        const T *src = brick + (i * OCB + cc * BK + half * VEC) * KT + k;
+        u32x4 out;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = (uint32_t)src[(2 * e) * KT] | ((uint32_t)src[(2 * e + 1) * KT] << 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = __float_as_uint((float)src[e * KT]);
+        }
+        const int phys = half ^ ((m >> 3) & 1);
+        *(u32x4 *)&wg[((int64_t)dst_tap[k] * nchunks + oc0 / BK + cc) * chunk_elems + (int64_t)m * BK +
+                      phys * VEC] = out;
+    }
+    // padding taps of this (rows, chunks) tile
+    if (kb == 0) {
+        const int gs = p.gemm_gs;
+        for (int P = 0; P < p.nphase; ++P) {
+            const int nt = p.ph[P].ntaps;
+            const int npad = (nt + gs - 1) / gs * gs - nt;
+            for (int n = threadIdx.x; n < npad * ncc * MB * 2; n += 256) {
+                const int half = n & 1, i = (n >> 1) & (MB - 1), rest = n >> 4;
+                const int cc = rest % ncc, t = nt + rest / ncc;
+                *(u32x4 *)&wg[((int64_t)(p.ph[P].tapbase + t) * nchunks + oc0 / BK + cc) * chunk_elems +
+                              (int64_t)(m0 + i) * BK + half * VEC] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    if (blockIdx.x == 0) {
+        const int gs = p.gemm_gs;
+        const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
+        const int E1 = p.th + a1.umax - a1.umin, E2 = p.tw + a2.umax - a2.umin;
+        for (int P = 0; P < p.nphase; ++P) {
+            const PhaseDesc ph = phase_desc(p, P);
+            const int padded = (ph.ntaps + gs - 1) / gs * gs;
+            const int n1 = ph.n[1], n2 = ph.n[2];
+            for (int t = threadIdx.x; t < padded; t += 256) {
+                int v = 0;
+                if (t < ph.ntaps) {
+                    const int j2 = t % n2, j1 = (t / n2) % n1, j0 = t / (n1 * n2);
+                    const int f0 = ph.off0[0] + j0 * a0.ostep, f1 = ph.off0[1] + j1 * a1.ostep,
+                              f2 = ph.off0[2] + j2 * a2.ostep;
+                    v = ((a0.umax - f0) * E1 + (a1.umax - f1)) * E2 + (a2.umax - f2);
+                }
+                tab[ph.tapbase + t] = v;
+            }
+        }
+    }
+}
+
+hipError_t launch_reorder_bwd(const Plan &pl, const void *w, void *wr, hipStream_t stream) {
+    const DevParams &p = pl.bdp;
+    const int es = pl.elem_bytes, bk = 32 / es;
+    if (p.cig_pad % bk || p.cog_pad % 8) return hipErrorInvalidValue;
+    int KT = p.ktot < 128 ? p.ktot : 128;
+    int OCB = 32768 / (8 * KT * es) / bk * bk;
+    if (OCB < bk) OCB = bk;
+    if (OCB > p.cig_pad) OCB = p.cig_pad;
+    const int64_t nkt = (p.ktot + KT - 1) / KT;
+    const int64_t blocks = (int64_t)p.G * (p.cog_pad / 8) * ((p.cig_pad + OCB - 1) / OCB) * nkt;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const size_t lds = (size_t)8 * OCB * KT * es + (size_t)4 * KT;
+    int32_t *tab = (int32_t *)((char *)wr + pl.bwd_tab_offset);
+    if (es == 2)
+        hipLaunchKernelGGL(reorder_bwd_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds,
+                           stream, p, (const uint16_t *)w, (uint16_t *)wr, tab, OCB, KT);
+    else
+        hipLaunchKernelGGL(reorder_bwd_kernel<float>, dim3((unsigned)blocks), dim3(256), lds,
+                           stream, p, (const float *)w, (float *)wr, tab, OCB, KT);
     return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@
 
 namespace convt {
 
-template <typename T, int CFG, int GS>
+template <typename T, int CFG, int GS, bool BWD>
 __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
                                                          const T *__restrict__ wr,
                                                          const int32_t *__restrict__ tab,
@@ -124,8 +124,12 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
     int bid = remap_block(blockIdx.x, p.n_blocks, p.xcd_remap);
     const int co_t = bid % p.n_co_tiles;
     bid /= p.n_co_tiles;
-    const int P = bid % p.nphase;
-    bid /= p.nphase;
+    // backward data: every block runs all phases (no phase in the grid)
+    int P = 0;
+    if constexpr (!BWD) {
+        P = bid % p.nphase;
+        bid /= p.nphase;
+    }
     const int tw_i = bid % p.nt_w;
     bid /= p.nt_w;
     const int th_i = bid % p.nt_h;
@@ -140,14 +144,16 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
     const int T0 = p.td, T1 = p.th, T2 = p.tw;
     const int q00 = td_i * T0, q01 = th_i * T1, q02 = tw_i * T2;
     // this phase's halo box: the q box grown by its tap span, starting at the
-    // phase's smallest input offset
-    const int E0 = T0 + (ph.n[0] > 0 ? (ph.n[0] - 1) * a0.ostep : 0);
-    const int E1 = T1 + (ph.n[1] > 0 ? (ph.n[1] - 1) * a1.ostep : 0);
-    const int E2 = T2 + (ph.n[2] > 0 ? (ph.n[2] - 1) * a2.ostep : 0);
+    // phase's smallest input offset. Backward data: dx position i reads the
+    // phase plane at i - off for the phase's offsets off, so the box of
+    // every phase spans [q - umax, q + T - 1 - umin] (the union of offsets).
+    const int E0 = BWD ? T0 + a0.umax - a0.umin : T0 + (ph.n[0] > 0 ? (ph.n[0] - 1) * a0.ostep : 0);
+    const int E1 = BWD ? T1 + a1.umax - a1.umin : T1 + (ph.n[1] > 0 ? (ph.n[1] - 1) * a1.ostep : 0);
+    const int E2 = BWD ? T2 + a2.umax - a2.umin : T2 + (ph.n[2] > 0 ? (ph.n[2] - 1) * a2.ostep : 0);
     const int hsz = E0 * E1 * E2;
-    const int h00 = q00 + ph.off0[0];
-    const int h01 = q01 + ph.off0[1];
-    const int h02 = q02 + ph.off0[2];
+    const int h00 = BWD ? q00 - a0.umax : q00 + ph.off0[0];
+    const int h01 = BWD ? q01 - a1.umax : q01 + ph.off0[1];
+    const int h02 = BWD ? q02 - a2.umax : q02 + ph.off0[2];
 
     f32x16 acc[MT][NT];
 #pragma unroll
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.0f;
 
-    const int ntaps = ph.ntaps;
+    const int ntaps = BWD ? p.bwd_nstages : ph.ntaps;
     const int nchunks = p.cig_pad / BKS;  // chunk groups (one per stage and tap group)
     const int Cig = p.Cig;
     const uint32_t xpl_bytes = (uint32_t)p.x_plane * ES;
@@ -173,23 +179,32 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         // pieces of 64 consecutive box positions, lane l taking position
         // 64j + l.
         // xsp[j]: this lane's byte offset for its piece j, out of range
-        // outside the input.
+        // outside the input. Backward data: box position j of the phase with
+        // residues r is dy position s*j + r (set before each halo copy).
         const int xpieces = ES == 2 ? (hsz + 31) / 32 : (hsz + 63) / 64;
         const int nxw = ES == 2 ? (xpieces - wave + NW - 1) / NW : xpieces;  // pieces of this wave
         uint32_t xsp[XJ];
+        auto halo_offsets = [&](int r0, int r1, int r2) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < XJ; ++j) {
-            const int row = ES == 2 ? (j * NW + wave) * 32 + (lane >> 1) : j * 64 + lane;
-            const int c2 = row % E2, c1 = (row / E2) % E1, c0 = row / (E2 * E1);
-            const int i0 = h00 + c0, i1 = h01 + c1, i2 = h02 + c2;
-            const uint32_t pos = (uint32_t)((i0 * a1.I + i1) * a2.I + i2);
-            const uint32_t off = ES == 2 ? pos * 32 + (uint32_t)(((lane & 1) ^ ((row >> 3) & 1)) * 16)
-                                         : pos * 4;
-            xsp[j] = (row < hsz && i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I && i2 >= 0 &&
-                      i2 < a2.I)
-                         ? off
-                         : kOutOfRange;
-        }
+            for (int j = 0; j < XJ; ++j) {
+                const int row = ES == 2 ? (j * NW + wave) * 32 + (lane >> 1) : j * 64 + lane;
+                const int c2 = row % E2, c1 = (row / E2) % E1, c0 = row / (E2 * E1);
+                int i0 = h00 + c0, i1 = h01 + c1, i2 = h02 + c2;
+                if constexpr (BWD) {
+                    i0 = i0 * a0.S + r0;
+                    i1 = i1 * a1.S + r1;
+                    i2 = i2 * a2.S + r2;
+                }
+                const uint32_t pos = (uint32_t)((i0 * a1.I + i1) * a2.I + i2);
+                const uint32_t off = ES == 2 ? pos * 32 + (uint32_t)(((lane & 1) ^ ((row >> 3) & 1)) * 16)
+                                             : pos * 4;
+                xsp[j] = (row < hsz && i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I && i2 >= 0 &&
+                          i2 < a2.I)
+                             ? off
+                             : kOutOfRange;
+            }
+        };
+        if constexpr (!BWD) halo_offsets(0, 0, 0);
         // halos of the chunks of group cg into ring slot xbi
         auto load_x = [&](int xbi, int cg) __attribute__((always_inline)) {
 #pragma unroll
@@ -226,9 +241,12 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         const uint32_t tap_bytes = (uint32_t)p.cog_pad * p.cig_pad * ES;
         const uint32_t chunk_bytes = (uint32_t)p.cog_pad * WROW;
         const int ngrp = (ntaps + GS - 1) / GS;  // tap groups; the phase is padded with zero taps
+        // backward data: the resource spans the group's taps of every phase
         const u32x4 wrs =
-            rsrc_words(wr + (int64_t)(g * p.ktot_pad + ph.tapbase) * p.cog_pad * p.cig_pad,
-                       (uint32_t)(ngrp * GS) * tap_bytes);
+            BWD ? rsrc_words(wr + (int64_t)g * p.ktot_pad * p.cog_pad * p.cig_pad,
+                             (uint32_t)p.ktot_pad * tap_bytes)
+                : rsrc_words(wr + (int64_t)(g * p.ktot_pad + ph.tapbase) * p.cog_pad * p.cig_pad,
+                             (uint32_t)(ngrp * GS) * tap_bytes);
         const int ndma = (NPIECE - wave + NW - 1) / NW;  // pieces of this wave (uniform)
         uint32_t wv[NDMA];
 #pragma unroll
@@ -238,9 +256,11 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
             wv[j] = (uint32_t)u * tap_bytes + (uint32_t)sc * chunk_bytes +
                     (uint32_t)(co_t * BM + rb * 32) * WROW + (uint32_t)lane * 16;
         }
-        // weight tiles of tap group gi of chunk group cg into buffer wbi
-        auto load_w = [&](int wbi, int gi, int cg) __attribute__((always_inline)) {
-            const uint32_t base = (uint32_t)(gi * GS) * tap_bytes + (uint32_t)(cg * SC) * chunk_bytes;
+        // weight tiles of tap group gi of chunk group cg into buffer wbi (tb:
+        // the phase's first tap, backward data only)
+        auto load_w = [&](int wbi, int gi, int cg, int tb) __attribute__((always_inline)) {
+            const uint32_t base =
+                (uint32_t)(tb + gi * GS) * tap_bytes + (uint32_t)(cg * SC) * chunk_bytes;
 #pragma unroll
             for (int j = 0; j < NDMA; ++j)
                 if (j < ndma)
@@ -263,7 +283,7 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         const int kvl = lane >> 5;
         // halo shifts of the phase's taps (the zero taps that pad it to whole
         // groups shift by 0)
-        const int32_t *ptab = tab + ph.tapbase;
+        const int32_t *ptab = tab + (BWD ? 0 : ph.tapbase);
 
         using Frag = typename std::conditional<ES == 2, bf16x8, f32x4>::type;
         // operands of one tap: weight slot wsl, halo rows shifted by drow
@@ -313,28 +333,68 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         // start it requests the halos of group chunk + XB - 1 (first tap
         // group only), then the weights of stage s + 2; at its end it waits
         // for what stage s + 1 reads and joins the barrier.
-        const int nstages = nchunks * ngrp;
+        // Backward data: the halo unit is (chunk group, phase), phases inner
+        // and those without taps skipped, each unit with its phase's tap
+        // groups as stages and a halo slot of its own (the phase plane's
+        // box); halo copies run XB - 1 units ahead through a unit cursor.
+        const int nstages = BWD ? p.bwd_nstages : nchunks * ngrp;
         const int nx = SC * XCH * nxw;  // halo copies of one chunk group by this wave
-        int chunk = 0, gi = 0;          // of stage s
-        int c2n = 0, gi2 = 0;           // of stage s + 2
-        load_x(0, 0);
-        if (XB == 3 && nchunks > 1) load_x(1, 1);
-        load_w(0, 0, 0);
-        if (++gi2 == ngrp) {
-            gi2 = 0;
-            ++c2n;
+        // the next phase with taps after q (-1: none), and a phase's tap groups
+        auto live_after = [&](int q) __attribute__((always_inline)) {
+            for (int n = q + 1; n < p.nphase; ++n)
+                if (p.ph[n].ntaps > 0) return n;
+            return -1;
+        };
+        auto groups_of = [&](int q) __attribute__((always_inline)) {
+            return BWD ? (p.ph[q].ntaps + GS - 1) / GS : ngrp;
+        };
+        auto tapbase_of = [&](int q) __attribute__((always_inline)) {
+            return BWD ? p.ph[q].tapbase : 0;
+        };
+        const int first = BWD ? live_after(-1) : P;
+        auto next_unit = [&](int &c, int &q) __attribute__((always_inline)) {
+            ++c;
+            if constexpr (BWD) {
+                q = live_after(q);
+                if (q < 0)
+                    q = first;
+                else
+                    --c;
+            }
+        };
+        auto next_stage = [&](int &c, int &q, int &gi) __attribute__((always_inline)) {
+            if (++gi == groups_of(q)) {
+                gi = 0;
+                next_unit(c, q);
+            }
+        };
+        // backward data: halo copy of the unit at the cursor (cx, qx)
+        int cx = 0, qx = first;
+        auto issue_x = [&](int xbi) __attribute__((always_inline)) {
+            const PhaseRec &rec = p.ph[qx];
+            halo_offsets(rec.rn[0] & 0xff, rec.rn[1] & 0xff, rec.rn[2] & 0xff);
+            load_x(xbi, cx);
+            next_unit(cx, qx);
+        };
+        int chunk = 0, gi = 0, qc = first;  // of stage s
+        int c2n = 0, gi2 = 0, q2 = first;   // of stage s + 2
+        if constexpr (BWD) {
+            issue_x(0);
+            if (XB == 3 && cx < nchunks) issue_x(1);
+        } else {
+            load_x(0, 0);
+            if (XB == 3 && nchunks > 1) load_x(1, 1);
         }
-        if (nstages > 1) load_w(1, gi2, c2n);
-        if (++gi2 == ngrp) {
-            gi2 = 0;
-            ++c2n;
-        }
+        load_w(0, 0, 0, tapbase_of(q2));
+        next_stage(c2n, q2, gi2);
+        if (nstages > 1) load_w(1, gi2, c2n, tapbase_of(q2));
+        next_stage(c2n, q2, gi2);
         // halo shifts of the first stage's taps
         int dl[GS];
 #pragma unroll
-        for (int u = 0; u < GS; ++u) dl[u] = ptab[u];
+        for (int u = 0; u < GS; ++u) dl[u] = ptab[tapbase_of(qc) + u];
         stage_barrier<0>();
-        int wb = 0, xb = 0;  // buffers of stage s: s % 3, chunk % XB
+        int wb = 0, xb = 0;  // buffers of stage s: s % 3, its unit % XB
         for (int s = 0; s < nstages; ++s) {
             const unsigned char *wsb = ws[wb];
             const unsigned char *xsb = xs[xb];
@@ -346,10 +406,16 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
             Frag fa[2][MT], fb[2][NT];
             read_frags(fa[0], fb[0], wsb, xsb, dl[0]);
             __builtin_amdgcn_sched_barrier(0);
-            const bool x_issue = gi == 0 && chunk + XB - 1 < nchunks;
-            if (x_issue) load_x(xb == 0 ? XB - 1 : xb - 1, chunk + XB - 1);
+            const bool x_issue = gi == 0 && (BWD ? cx < nchunks : chunk + XB - 1 < nchunks);
+            if (x_issue) {
+                const int xbi = xb == 0 ? XB - 1 : xb - 1;
+                if constexpr (BWD)
+                    issue_x(xbi);
+                else
+                    load_x(xbi, chunk + XB - 1);
+            }
             const bool w_issue = s + 2 < nstages;
-            if (w_issue) load_w(wb == 0 ? 2 : wb - 1, gi2, c2n);
+            if (w_issue) load_w(wb == 0 ? 2 : wb - 1, gi2, c2n, tapbase_of(q2));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
@@ -361,9 +427,12 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
                 __builtin_amdgcn_sched_barrier(0);
             }
             // the next stage's halo shifts, fetched before the barrier
-            const int gin = gi + 1 == ngrp ? 0 : gi + 1;
+            {
+                int cn = chunk, qn = qc, gin = gi;
+                next_stage(cn, qn, gin);
 #pragma unroll
-            for (int u = 0; u < GS; ++u) dl[u] = ptab[gin * GS + u];
+                for (int u = 0; u < GS; ++u) dl[u] = ptab[tapbase_of(qn) + gin * GS + u];
+            }
             if (s + 1 < nstages) {
                 // the weights of stage s + 2 may still fly, and with three
                 // halo slots the halos requested now; everything older (all
@@ -376,15 +445,9 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
                     stage_barrier_n<NDMA + SC * XCH * XJ>(fly);
             }
             wb = wb == 2 ? 0 : wb + 1;
-            if (++gi == ngrp) {
-                gi = 0;
-                ++chunk;
-                xb = xb == XB - 1 ? 0 : xb + 1;
-            }
-            if (w_issue && ++gi2 == ngrp) {
-                gi2 = 0;
-                ++c2n;
-            }
+            next_stage(chunk, qc, gi);
+            if (gi == 0) xb = xb == XB - 1 ? 0 : xb + 1;
+            if (w_issue) next_stage(c2n, q2, gi2);
         }
     }
 
@@ -397,7 +460,11 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         const int c2 = n % T2, c1 = (n / T2) % T1, c0 = n / (T2 * T1);
         const int qd = q00 + c0, qh = q01 + c1, qw = q02 + c2;
         yoff[nt] = kOutOfRange;
-        if (c0 < T0 && qd < ph.qn[0] && qh < ph.qn[1] && qw < ph.qn[2]) {
+        if constexpr (BWD) {
+            // dx positions: the box itself
+            if (c0 < T0 && qd < a0.O && qh < a1.O && qw < a2.O)
+                yoff[nt] = (uint32_t)((qd * a1.O + qh) * a2.O + qw) * ES;
+        } else if (c0 < T0 && qd < ph.qn[0] && qh < ph.qn[1] && qw < ph.qn[2]) {
             const int o0 = a0.S * qd + ph.r[0], o1 = a1.S * qh + ph.r[1], o2 = a2.S * qw + ph.r[2];
             yoff[nt] = (uint32_t)((o0 * a1.O + o1) * a2.O + o2) * ES;
         }
@@ -440,47 +507,60 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
     }
 }
 
-template <typename T, int CFG, int GS>
-static void launch_cfg(const Plan &pl, const void *x, const void *ws, const void *bias, void *y,
-                       hipStream_t stream) {
-    const DevParams &p = pl.dp;
+template <typename T, int CFG, int GS, bool BWD>
+static void launch_cfg(const DevParams &p, int64_t tab_offset, const void *x, const void *ws,
+                       const void *bias, void *y, hipStream_t stream) {
     if constexpr (tiles::gemm_cfg_valid(tiles::kGemmCfg[CFG], GS))
-        hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS>), dim3(p.n_blocks), dim3(tiles::kGemmCfg[CFG].nw * 64),
-                       0, stream, p, (const T *)x, (const T *)ws,
-                       (const int32_t *)((const char *)ws + pl.tab_offset), (const T *)bias, (T *)y);
+        hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS, BWD>), dim3(p.n_blocks),
+                           dim3(tiles::kGemmCfg[CFG].nw * 64), 0, stream, p, (const T *)x,
+                           (const T *)ws, (const int32_t *)((const char *)ws + tab_offset),
+                           (const T *)bias, (T *)y);
 }
 
-template <typename T, int CFG>
-static hipError_t launch_gs(const Plan &pl, const void *x, const void *ws, const void *bias,
-                            void *y, hipStream_t stream) {
-    const int gs = pl.dp.gemm_gs;
+template <typename T, int CFG, bool BWD>
+static hipError_t launch_gs(const DevParams &p, int64_t tab_offset, const void *x, const void *ws,
+                            const void *bias, void *y, hipStream_t stream) {
+    const int gs = p.gemm_gs;
     if (gs < 1 || gs > tiles::kGemmTapGroup || !tiles::gemm_cfg_valid(tiles::kGemmCfg[CFG], gs))
         return hipErrorInvalidValue;
     switch (gs) {
-        case 1: launch_cfg<T, CFG, 1>(pl, x, ws, bias, y, stream); break;
-        case 2: launch_cfg<T, CFG, 2>(pl, x, ws, bias, y, stream); break;
-        case 3: launch_cfg<T, CFG, 3>(pl, x, ws, bias, y, stream); break;
-        case 4: launch_cfg<T, CFG, 4>(pl, x, ws, bias, y, stream); break;
+        case 1: launch_cfg<T, CFG, 1, BWD>(p, tab_offset, x, ws, bias, y, stream); break;
+        case 2: launch_cfg<T, CFG, 2, BWD>(p, tab_offset, x, ws, bias, y, stream); break;
+        case 3: launch_cfg<T, CFG, 3, BWD>(p, tab_offset, x, ws, bias, y, stream); break;
+        case 4: launch_cfg<T, CFG, 4, BWD>(p, tab_offset, x, ws, bias, y, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, const void *bias,
-                             void *y, hipStream_t stream) {
-    const DevParams &p = pl.dp;
+template <bool BWD>
+static hipError_t launch_any(const DevParams &p, int64_t tab_offset, const void *x, const void *wr,
+                             const void *bias, void *y, hipStream_t stream) {
     if (p.n_blocks <= 0) return hipSuccess;
     if (!p.wr_chunked) return hipErrorInvalidValue;
     switch (p.gemm_cfg) {
-        case 0: return launch_gs<uint16_t, 0>(pl, x, wr, bias, y, stream);
-        case 1: return launch_gs<uint16_t, 1>(pl, x, wr, bias, y, stream);
-        case 2: return launch_gs<uint16_t, 2>(pl, x, wr, bias, y, stream);
-        case 3: return launch_gs<float, 3>(pl, x, wr, bias, y, stream);
-        case 4: return launch_gs<float, 4>(pl, x, wr, bias, y, stream);
-        case 5: return launch_gs<float, 5>(pl, x, wr, bias, y, stream);
-        case 6: return launch_gs<uint16_t, 6>(pl, x, wr, bias, y, stream);
+        case 0: return launch_gs<uint16_t, 0, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 1: return launch_gs<uint16_t, 1, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 2: return launch_gs<uint16_t, 2, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 3: return launch_gs<float, 3, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 4: return launch_gs<float, 4, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 5: return launch_gs<float, 5, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 6: return launch_gs<uint16_t, 6, BWD>(p, tab_offset, x, wr, bias, y, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, const void *bias,
+                             void *y, hipStream_t stream) {
+    return launch_any<false>(pl.dp, pl.tab_offset, x, wr, bias, y, stream);
+}
+
+// Backward data: x is dy (channel-chunked copy for bfloat16), y is dx, no
+// bias (the backward problem has has_bias = 0, so the bias resource is
+// empty; dx stands in for its pointer).
+hipError_t launch_phase_gemm_bwd(const Plan &pl, const void *dy, const void *wr, void *dx,
+                                 hipStream_t stream) {
+    return launch_any<true>(pl.bdp, pl.bwd_tab_offset, dy, wr, dx, dx, stream);
 }
 
 }  // namespace convt

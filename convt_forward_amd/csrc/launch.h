@@ -21,4 +21,15 @@ hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, cons
 hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const void *bias, void *y,
                           hipStream_t stream);
 
+// Backward data (dx from dy). The channel-chunked copy and the fill use the
+// kernels of the forward with the backward problem's parameters.
+hipError_t launch_pack_dp(const DevParams &p, const void *x, void *xp, hipStream_t stream);
+hipError_t launch_fill_dp(const DevParams &p, int elem_bytes, const void *bias, void *y,
+                          hipStream_t stream);
+hipError_t launch_reorder_bwd(const Plan &pl, const void *w, void *wr, hipStream_t stream);
+hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void *dx,
+                            hipStream_t stream);
+hipError_t launch_phase_gemm_bwd(const Plan &pl, const void *dy, const void *wr, void *dx,
+                                 hipStream_t stream);
+
 }  // namespace convt

@@ -148,7 +148,10 @@ void fill_phase_table(DevParams *dp) {
 // A block computes BN positions of one phase for BM output channels. The q
 // tile is a (td, th, tw) box with td*th*tw == BN; its input halo grows by the
 // tap span of the phase on each axis and must fit the LDS halo buffer.
-bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max) {
+// Backward data (bwd): the tile is a box of dx positions, and its halo in a
+// phase plane of dy spans the union of every phase's offsets (span_max holds
+// umax - umin there); a block runs every phase's taps.
+bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max, bool bwd) {
     int64_t best_cost = std::numeric_limits<int64_t>::max();
     int bd = 0, bh = 0, bw = 0;
     for (int tw = 1; tw <= BN; tw *= 2) {
@@ -167,7 +170,8 @@ bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max) {
             // loads add a smaller term per position, and the epilogue one per
             // output row that 32 consecutive positions (the lanes of one
             // store) touch.
-            const int64_t avg_taps = std::max<int64_t>(1, dp->ktot / std::max(1, dp->nphase));
+            const int64_t avg_taps =
+                bwd ? dp->ktot : std::max<int64_t>(1, dp->ktot / std::max(1, dp->nphase));
             const int64_t rows_per_store = std::max(1, 32 / tw);
             const int64_t cost = nt * (BN * avg_taps * 4 + hd * hh * hw + BN * rows_per_store);
             if (cost < best_cost) {
@@ -213,9 +217,20 @@ int choose_gemm_gs(const DevParams &dp) {
 // rounds of two per CU, each round costing its blocks' padded MFMA work,
 // scaled up where the wave tile's LDS operand reads would outrun the MFMAs
 // and by a per-MFMA overhead that small wave tiles amortise worse.
-int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
+int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs);
+
+// With the preferred taps per stage first, then fewer (smaller weight
+// buffers leave more LDS to the halo) until some configuration fits.
+int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd) {
+    for (int gs = choose_gemm_gs(*dp); gs >= 1; --gs) {
+        const int c = pick_gemm_cfg(dp, dtype, ndim, bwd, gs);
+        if (c >= 0) return c;
+    }
+    return -1;
+}
+
+int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs) {
     const bool bf16 = dtype == CONVT_DTYPE_BF16;
-    const int gs = choose_gemm_gs(*dp);
     int best = -1;
     double best_t = 0;
     DevParams best_dp{};
@@ -223,10 +238,10 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
         const tiles::GemmTile &t = tiles::kGemmCfg[c];
         if ((t.bf16 != 0) != bf16 || !tiles::gemm_cfg_valid(t, gs)) continue;
         DevParams tmp = *dp;
-        if (!choose_gemm_tile(&tmp, ndim, t.bn, tiles::gemm_halo_cap(t, gs))) continue;
+        if (!choose_gemm_tile(&tmp, ndim, t.bn, tiles::gemm_halo_cap(t, gs), bwd)) continue;
         const int64_t co_tiles = ceil_div(tmp.Cog, t.bm);
-        const int64_t blocks =
-            (int64_t)tmp.nt_d * tmp.nt_h * tmp.nt_w * co_tiles * tmp.nphase * tmp.G * tmp.B;
+        const int64_t blocks = (int64_t)tmp.nt_d * tmp.nt_h * tmp.nt_w * co_tiles *
+                               (bwd ? 1 : tmp.nphase) * tmp.G * tmp.B;
         const int wgn = t.nw / t.wgm;
         const double mt = t.bm / t.wgm / 32.0, nt = t.bn / (double)wgn / 32.0;
         // LDS read time over MFMA time per tap (float32 MFMAs take 4x the
@@ -249,12 +264,12 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim) {
     return best;
 }
 
-bool gemm_eligible(const DevParams &dp, int dtype, int ndim) {
+bool gemm_eligible(const DevParams &dp, int dtype, int ndim, bool bwd = false) {
     if (!strides_fit(dp) || dp.ktot > 4096) return false;
     if (!slices_fit(dp, dtype == CONVT_DTYPE_F32 ? 4 : 2)) return false;
     if (dtype != CONVT_DTYPE_F32 && dtype != CONVT_DTYPE_BF16) return false;
     DevParams tmp = dp;
-    return pick_gemm_cfg(&tmp, dtype, ndim) >= 0;
+    return pick_gemm_cfg(&tmp, dtype, ndim, bwd) >= 0;
 }
 
 // ---- grouped route tiling -------------------------------------------------
@@ -368,6 +383,111 @@ bool direct_eligible(const DevParams &dp) {
 
 }  // namespace
 
+// ---- backward data ---------------------------------------------------------
+// dx[i] gathers dy[s*i - p + kk*d] * W[kk]. Output residue r of the forward
+// split holds the taps whose products land on dy positions s*j + r, at
+// j = i - off(kk): per phase, a stride-1 correlation of the phase plane
+// dy_r[j] = dy[s*j + r] with the phase's taps, and dx is the sum over the
+// phases. The backward GEMM runs these sums in one K loop per block.
+convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], const int64_t S[3],
+                           const int64_t P[3], const int64_t D[3], const int64_t O[3]) {
+    const convt_problem *p = &pl->prob;
+    const DevParams &fp = pl->dp;
+    DevParams &b = pl->bdp;
+    memset(&b, 0, sizeof(b));
+    for (int a = 0; a < 3; ++a) fill_axis(&b.ax[a], I[a], K[a], S[a], P[a], D[a], O[a]);
+    fill_phase_table(&b);
+    for (int a = 0; a < 3; ++a) {
+        DevAxis &ax = b.ax[a];
+        ax.I = (int32_t)O[a];  // the input is dy
+        ax.O = (int32_t)I[a];  // the output is dx
+        ax.qmax = (int32_t)I[a];
+        ax.span_max = ax.umax - ax.umin;
+    }
+    b.B = fp.B;
+    b.Ci = fp.Co;
+    b.Co = fp.Ci;
+    b.G = fp.G;
+    b.Cig = fp.Cog;
+    b.Cog = fp.Cig;
+    b.ktot = fp.ktot;
+    b.nphase = fp.nphase;
+    b.x_plane = fp.y_plane;
+    b.y_plane = fp.x_plane;
+    b.has_bias = 0;
+    const int dt = p->dtype;
+    const int nd = pl->ndim;
+    const bool empty_out = b.B == 0 || b.Co == 0 || b.y_plane == 0;
+    const bool no_terms = b.Cig == 0;
+    int route = p->route_bwd;
+    if (route == CONVT_ROUTE_AUTO) {
+        if (empty_out)
+            route = CONVT_ROUTE_NONE;
+        else if (no_terms)
+            route = CONVT_ROUTE_FILL;
+        else if (gemm_eligible(b, dt, nd, true))
+            route = CONVT_ROUTE_PHASE_GEMM;
+        else
+            route = CONVT_ROUTE_NAIVE;
+    } else {
+        bool ok = false;
+        switch (route) {
+            case CONVT_ROUTE_NONE: ok = empty_out; break;
+            case CONVT_ROUTE_FILL: ok = !empty_out && no_terms; break;
+            case CONVT_ROUTE_PHASE_GEMM: ok = !empty_out && !no_terms && gemm_eligible(b, dt, nd, true); break;
+            case CONVT_ROUTE_NAIVE: ok = !empty_out && !no_terms; break;
+            default: ok = false;
+        }
+        if (!ok) return CONVT_ERR_UNSUPPORTED;
+    }
+    pl->route_bwd = route;
+    pl->info.route_bwd = route;
+    pl->info.bwd_workspace_bytes = 0;
+    if (route != CONVT_ROUTE_PHASE_GEMM) return CONVT_OK;
+
+    const int64_t i31 = ((int64_t)1 << 31) - 1, lim = (int64_t)1 << 62;
+    pick_gemm_cfg(&b, dt, nd, true);
+    const tiles::GemmTile &t = tiles::kGemmCfg[b.gemm_cfg];
+    const int64_t bk = 32 / pl->elem_bytes * t.sc;  // K channels (of dy) per stage
+    b.cog_pad = (int32_t)(ceil_div(b.Cog, t.bm) * t.bm);
+    b.cig_pad = (int32_t)(ceil_div(b.Cig, bk) * bk);
+    b.wr_chunked = 1;
+    int64_t base = 0, stages = 0;
+    for (int ph = 0; ph < b.nphase; ++ph) {
+        const int64_t ng = ceil_div(b.ph[ph].ntaps, b.gemm_gs);
+        b.ph[ph].tapbase = (int32_t)base;
+        base += ng * b.gemm_gs;
+        stages += ng * (b.cig_pad / bk);
+    }
+    if (base > i31 || stages > i31) return CONVT_ERR_UNSUPPORTED;
+    b.ktot_pad = (int32_t)base;
+    b.bwd_nstages = (int32_t)stages;
+    b.n_co_tiles = (int32_t)ceil_div(b.Cog, t.bm);
+    const int64_t blocks = (int64_t)b.nt_d * b.nt_h * b.nt_w * b.n_co_tiles * b.G * b.B;
+    if (blocks > i31) return CONVT_ERR_UNSUPPORTED;
+    b.n_blocks = (int32_t)blocks;
+    b.xcd_remap = blocks % 8 == 0 ? 1 : 0;
+    int64_t wr, tmp, ws;
+    if (!mul_ok((int64_t)b.G * b.ktot_pad, (int64_t)b.cog_pad * b.cig_pad, lim, &wr))
+        return CONVT_ERR_INVALID_ARGUMENT;
+    pl->bwd_wr_elems = wr;
+    ws = wr * pl->elem_bytes;
+    pl->bwd_tab_offset = (ws + 255) / 256 * 256;
+    ws = pl->bwd_tab_offset + (int64_t)b.ktot_pad * 4;
+    if (dt == CONVT_DTYPE_BF16) {
+        // the channel-chunked copy of dy: [B][G][chunk][position][32 bytes]
+        int64_t xp;
+        if (!mul_ok((int64_t)b.B * b.G, (int64_t)b.cig_pad / 16, lim, &tmp) ||
+            !mul_ok(tmp, (int64_t)b.x_plane * 32, lim, &xp))
+            return CONVT_ERR_INVALID_ARGUMENT;
+        pl->bwd_xp_offset = (ws + 255) / 256 * 256;
+        pl->bwd_xp_bytes = xp;
+        ws = pl->bwd_xp_offset + xp;
+    }
+    pl->info.bwd_workspace_bytes = ws;
+    return CONVT_OK;
+}
+
 convt_status make_plan(const convt_problem *p, Plan *pl) {
     memset(pl, 0, sizeof(*pl));
     if (!p) return CONVT_ERR_INVALID_ARGUMENT;
@@ -377,7 +497,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     if (p->has_bias != 0 && p->has_bias != 1) return CONVT_ERR_INVALID_ARGUMENT;
     if (p->route < CONVT_ROUTE_AUTO || p->route > CONVT_ROUTE_NAIVE)
         return CONVT_ERR_INVALID_ARGUMENT;
-    if ((p->has_padding_hi != 0 && p->has_padding_hi != 1) || p->reserved0 != 0)
+    if (p->has_padding_hi != 0 && p->has_padding_hi != 1) return CONVT_ERR_INVALID_ARGUMENT;
+    if (p->route_bwd < CONVT_ROUTE_AUTO || p->route_bwd > CONVT_ROUTE_NAIVE)
         return CONVT_ERR_INVALID_ARGUMENT;
     const int64_t B = p->x_shape[0], Ci = p->x_shape[1];
     const int64_t G = p->groups;
@@ -504,7 +625,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     // ---- tiles and workspace ------------------------------------------------
     int64_t blocks = 0;
     if (route == CONVT_ROUTE_PHASE_GEMM) {
-        pick_gemm_cfg(&dp, dt, nd);
+        pick_gemm_cfg(&dp, dt, nd, false);
         const tiles::GemmTile &t = tiles::kGemmCfg[dp.gemm_cfg];
         // channels of a stage: SC chunks of 32 bytes
         const int64_t bk = 32 / pl->elem_bytes * t.sc;
@@ -573,7 +694,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
         pl->wr_elems = 0;
         info.workspace_bytes = 0;
     }
-    return CONVT_OK;
+    return plan_backward(pl, I, K, S, P, D, O);
 }
 
 }  // namespace convt

@@ -116,7 +116,7 @@ typedef struct convt_problem {
     int32_t has_bias;                           /* 0 or 1 */
     int32_t route;                              /* convt_route; CONVT_ROUTE_AUTO normally */
     int32_t has_padding_hi;                     /* 0: high padding = padding; 1: = padding_hi */
-    int32_t reserved0;                          /* must be 0 */
+    int32_t route_bwd;                          /* convt_route of convt_backward_data; AUTO normally */
     int64_t padding_hi[CONVT_MAX_NDIM];         /* >= 0; read only when has_padding_hi = 1 */
 } convt_problem;
 
@@ -127,7 +127,8 @@ typedef struct convt_plan_info {
     int64_t n_phases;                           /* product of the strides */
     int64_t useful_flops;                       /* 2 * B * C_in * (C_out/groups) * prod(k) * prod(I) */
     int32_t route;                              /* the convt_route chosen */
-    int32_t reserved;
+    int32_t route_bwd;                          /* the route of convt_backward_data */
+    int64_t bwd_workspace_bytes;                /* device workspace convt_backward_data needs */
 } convt_plan_info;
 
 typedef struct convt_plan_s *convt_plan_t;
@@ -139,7 +140,8 @@ typedef struct convt_plan_s *convt_plan_t;
  * outputPadding < max(stride, dilation) per axis, dilation, groups
  * divisibility, bias shape, dtype guard; plus shape consistency):
  *   ndim in 1..3; all sizes >= 0; kernel sizes >= 1; stride >= 1;
- *   padding >= 0 (both ends); has_padding_hi in {0, 1}; reserved0 == 0;
+ *   padding >= 0 (both ends); has_padding_hi in {0, 1}; route and route_bwd
+ *   valid convt_route codes;
  *   dilation >= 1; 0 <= output_padding < max(stride, dilation);
  *   groups >= 1 dividing C_in; w_shape[0] == C_in; every output size >= 1;
  *   has_bias in {0, 1}; element counts of x, W and y below 2^62 and each
@@ -187,6 +189,28 @@ convt_status convt_prepare_weights(convt_plan_t plan, const void *w, void *works
  */
 convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void *w,
                                     const void *bias, void *y, void *workspace, void *stream);
+
+/*
+ * Backward data: the gradient of a loss with respect to x, given its gradient
+ * dy with respect to y (the SKaiNET page's Summary names this adjoint for the
+ * input, convTranspose2dBackward). y is linear in x, so
+ *     dx[b, ci, i] = sum over oc in the group of ci and taps kk with
+ *                    o = i*s - p + kk*d inside y:  dy[b, oc, o] * W[ci, oc - g*Cog, kk]
+ * per axis, p the low padding; the bias does not enter.
+ *
+ * dy: [B, C_out, O...] (the plan's out_shape), W as for convt_forward, dx:
+ * [B, C_in, I...] (x's shape), all device memory of the plan's element type;
+ * dx is overwritten and must not alias dy or W. Products are accumulated in
+ * float32 and rounded once to the element type. workspace: device memory of
+ * at least info.bwd_workspace_bytes bytes, 16-byte aligned (may be NULL when
+ * that is 0); it is scratch, and may be the forward's workspace buffer if
+ * large enough, but not in use by a concurrent call. Asynchronous on stream,
+ * errors as for convt_forward. Routes (info.route_bwd): NONE (dx empty),
+ * FILL (no output channels: dx = 0), PHASE_GEMM (stride phases summed inside
+ * one implicit-gather GEMM on MFMA), NAIVE (one thread per dx element).
+ */
+convt_status convt_backward_data(convt_plan_t plan, const void *dy, const void *w, void *dx,
+                                 void *workspace, void *stream);
 
 /* Free a plan. NULL is accepted and ignored. */
 void convt_destroy(convt_plan_t plan);

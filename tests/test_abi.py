@@ -262,15 +262,42 @@ def test_problem_struct_layout_matches_header(tmp_path):
 
 def test_padding_hi_fields_validated():
     L = C.lib()
-    for has_hi, res, hi, want in [(2, 0, 0, 1), (0, 1, 0, 1), (1, 0, -1, 1), (1, 0, 1, 0), (1, 0, 3, 0),
+    for has_hi, rb, hi, want in [(2, 0, 0, 1), (0, 99, 0, 1), (1, 0, -1, 1), (1, 0, 1, 0), (1, 0, 3, 0),
                                   (0, 0, -5, 0)]:
         p = C.make_problem((1, 1, 4), (1, 1, 3), stride=2, padding=1)
-        p.has_padding_hi, p.reserved0, p.padding_hi[0] = has_hi, res, hi
+        p.has_padding_hi, p.route_bwd, p.padding_hi[0] = has_hi, rb, hi
         h = ctypes.c_void_p()
         info = C.PlanInfo()
         st = L.convt_plan(ctypes.byref(p), ctypes.byref(h), ctypes.byref(info))
-        assert st == want, (has_hi, res, hi, st)
+        assert st == want, (has_hi, rb, hi, st)
         if st == 0:
             # (4-1)*2 - (1 + p_hi) + (3-1) + 1, p_hi read only when has_padding_hi is 1
             assert info.out_shape[2] == 8 - (hi if has_hi else 1)
             L.convt_destroy(h)
+
+
+def test_backward_data_refuses_bad_arguments_before_launch():
+    """Host-side checks of convt_backward_data: nothing reaches the device."""
+    L = C.lib()
+    pl = plan(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2)
+    assert pl.route_bwd == "phase_gemm" and pl.bwd_workspace_bytes > 0
+    h = pl.handle
+    fake = 4096  # never dereferenced
+    assert L.convt_backward_data(None, fake, fake, fake, fake, None) == 1
+    assert L.convt_backward_data(h, fake, fake, None, fake, None) == 1        # dx required
+    assert L.convt_backward_data(h, None, fake, fake, fake, None) == 1        # dy required
+    assert L.convt_backward_data(h, fake, None, fake, fake, None) == 1        # w required
+    assert L.convt_backward_data(h, fake, fake, fake, None, None) == 1        # workspace required
+    assert L.convt_backward_data(h, fake, fake, fake, fake + 8, None) == 1    # misaligned
+
+
+def test_backward_routes():
+    """Routes of the backward pass: forced routes that cannot serve are
+    refused; the naive route serves any problem."""
+    assert plan(x_shape=(0, 2, 5), w_shape=(2, 3, 3)).route_bwd == "none"
+    assert plan(x_shape=(1, 2, 5), w_shape=(2, 0, 3)).route_bwd == "fill"
+    assert plan(x_shape=(1, 2, 5), w_shape=(2, 3, 3), stride=19).route_bwd == "naive"
+    assert plan(x_shape=(1, 2, 5), w_shape=(2, 3, 3), route_bwd="naive").route_bwd == "naive"
+    assert status_of(x_shape=(1, 2, 5), w_shape=(2, 3, 3), stride=19, route_bwd="phase_gemm") == 2
+    assert status_of(x_shape=(1, 2, 5), w_shape=(2, 3, 3), route_bwd="fill") == 2
+    assert status_of(x_shape=(1, 2, 5), w_shape=(2, 3, 3), route_bwd="grouped") == 2

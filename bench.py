@@ -13,7 +13,9 @@ Printed: one JSON line with the useful-FLOP throughput (2*B*C_in*(C_out/g)*
 prod(k)*prod(I) per step / seconds per step), the roofline of the dominant
 kernel (its average duration measured live with HIP events on the stream it
 runs on) and the CPU oracle's throughput on a bounded sample of the same
-workload (a reported baseline, not a target).
+workload (a reported baseline, not a target). A "backward_data" object adds
+the input-gradient pass (convt_backward_data) on the same workload, timed
+the same way outside the forward steps (--no-backward skips it).
 """
 from __future__ import annotations
 
@@ -122,6 +124,44 @@ def cpu_baseline(wl: workloads.Workload, tens: workloads.Tensors, target_s: floa
     }
 
 
+def measure_backward(pl, wl, sets, stream, K, warmup):
+    """convt_backward_data on the same workload: dx from dy through the same
+    weights, back-to-back calls over the rotating buffer sets (dy: the sets'
+    forward outputs; dx overwrites their inputs), bracketed by one event
+    pair on the launch stream. A call is the whole backward pass: weight
+    reorder, the channel-chunked copy of dy (bfloat16) and the GEMM."""
+    import torch
+    dev = sets[0]["x"].device
+    sh = stream.cuda_stream
+    wss = [pl.new_bwd_workspace(dev) for _ in sets]
+
+    def call(i):
+        s = sets[i % len(sets)]
+        pl.backward_data_ptr(s["y"].data_ptr(), s["w"].data_ptr(), s["x"].data_ptr(),
+                             wss[i % len(sets)].data_ptr(), sh)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / K
+    flops = useful_flops(wl)
+    peak = PEAK_TFLOPS.get(wl.dtype)
+    return {
+        "route": pl.route_bwd,
+        "us_per_call": t * 1e6,
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "frac_of_mfma_peak": flops / t / 1e12 / peak if peak else None,
+        "calls": K,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +172,8 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=float, default=1024.0,
                     help="total size of the rotated buffer sets (defeats the 256 MB cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-data (input gradient) measurement")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (3 times), "
                          "the reference kernel for scaling HBM byte counters")
@@ -283,6 +325,8 @@ def main() -> int:
         },
         "roofline": roofline,
     }
+    if not args.no_backward and pl.route_bwd != "none":
+        result["backward_data"] = measure_backward(pl, wl, sets, stream, K, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, tens)
     print(json.dumps(result), flush=True)

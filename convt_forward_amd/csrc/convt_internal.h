@@ -80,6 +80,8 @@ struct DevParams {
                                // phase padded with zero taps to a multiple of gemm_gs)
     int32_t ph_tab_ok;         // 1: ph[] holds every phase (nphase <= kMaxPhaseTab)
     int32_t bwd_nstages;       // backward-data GEMM: pipeline stages of a block (all phases)
+    int32_t bwd_nlive;         // backward-data GEMM: phases with taps
+    uint8_t bwd_live[kMaxPhaseTab];  // their indices, ascending
     PhaseRec ph[kMaxPhaseTab];
 };
 

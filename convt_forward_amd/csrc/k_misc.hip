@@ -725,15 +725,16 @@ hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void 
 // the 8 rows' 256 contiguous bytes, consecutive lanes on consecutive 16-byte
 // halves. Block 0 also writes the halo shift table: entry tapbase(P) + t
 // holds, for tap t = (j0, j1, j2) of phase P with input offsets off_a =
-// off0_a + j_a * ostep_a, the row of its window in the halo box,
-// ((umax0 - off0) * E1 + (umax1 - off1)) * E2 + (umax2 - off2), E1 and E2 the
-// box extents (the dx tile plus umax - umin); padding taps get 0.
+// off0_a + j_a * ostep_a, the row of its window in the phase's halo box
+// (which starts at the phase's largest offset u_a = off0_a + (n_a - 1) *
+// ostep_a), ((u0 - off0) * E1 + (u1 - off1)) * E2 + (u2 - off2), E1 and E2
+// the box extents (the dx tile plus span_max); padding taps get 0.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *__restrict__ w,
                                                           T *__restrict__ wr,
                                                           int32_t *__restrict__ tab, int OCB,
-                                                          int KT) {
+                                                          int KT, int vec_runs) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     constexpr int VEC = 16 / sizeof(T), BK = 2 * VEC, MB = 8;
     const int Cm = p.Cog, Coc = p.Cig, ktot = p.ktot;
@@ -758,7 +759,33 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
         const int kk = kk0 + k;
         dst_tap[k] = tap_in_table(p, kk / (K1 * K2), (kk / K2) % K1, kk % K2);
     }
-    const int n_in = MB * noc * nk;
+    // With vec_runs (KT == ktot, every chunk of the block inside or wholly
+    // outside Cog, 16-byte aligned runs), each row's run [oc0, oc0 + OCB) x
+    // [0, ktot) moves as 16-byte vectors, 4 per lane in flight.
+    const int n_in = vec_runs ? 0 : MB * noc * nk;
+    if (vec_runs) {
+        const int nvr = noc * ktot * (int)sizeof(T) / 16;  // vectors of one row's run
+        const int nv = MB * nvr;
+        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 4) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int vi = v0 + 256 * u;
+                const int i = vi / nvr, r = vi - i * nvr;
+                v[u] = u32x4{0u, 0u, 0u, 0u};
+                if (vi < nv && m0 + i < Cm && oc0 < Coc)
+                    v[u] = ((const u32x4 *)(w + (((int64_t)g * Cm + m0 + i) * Coc + oc0) * ktot))[r];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int vi = v0 + 256 * u;
+                if (vi < nv) {
+                    const int i = vi / nvr, r = vi - i * nvr;
+                    ((u32x4 *)(brick + (size_t)i * OCB * KT))[r] = v[u];
+                }
+            }
+        }
+    }
     for (int e0 = threadIdx.x; e0 < n_in; e0 += 256 * 8) {
         T v[8];
 #pragma unroll
@@ -820,7 +847,7 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
     if (blockIdx.x == 0) {
         const int gs = p.gemm_gs;
         const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
-        const int E1 = p.th + a1.umax - a1.umin, E2 = p.tw + a2.umax - a2.umin;
+        const int E1 = p.th + a1.span_max, E2 = p.tw + a2.span_max;
         for (int P = 0; P < p.nphase; ++P) {
             const PhaseDesc ph = phase_desc(p, P);
             const int padded = (ph.ntaps + gs - 1) / gs * gs;
@@ -831,7 +858,9 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
                     const int j2 = t % n2, j1 = (t / n2) % n1, j0 = t / (n1 * n2);
                     const int f0 = ph.off0[0] + j0 * a0.ostep, f1 = ph.off0[1] + j1 * a1.ostep,
                               f2 = ph.off0[2] + j2 * a2.ostep;
-                    v = ((a0.umax - f0) * E1 + (a1.umax - f1)) * E2 + (a2.umax - f2);
+                    const int u0 = ph.off0[0] + (ph.n[0] - 1) * a0.ostep,
+                              u1 = ph.off0[1] + (n1 - 1) * a1.ostep, u2 = ph.off0[2] + (n2 - 1) * a2.ostep;
+                    v = ((u0 - f0) * E1 + (u1 - f1)) * E2 + (u2 - f2);
                 }
                 tab[ph.tapbase + t] = v;
             }
@@ -843,22 +872,29 @@ hipError_t launch_reorder_bwd(const Plan &pl, const void *w, void *wr, hipStream
     const DevParams &p = pl.bdp;
     const int es = pl.elem_bytes, bk = 32 / es;
     if (p.cig_pad % bk || p.cog_pad % 8) return hipErrorInvalidValue;
+    // 8 rows x OCB channels (whole chunks) x KT taps per block, the brick
+    // within 32 KiB, OCB halved while the grid has fewer than 1024 blocks
     int KT = p.ktot < 128 ? p.ktot : 128;
     int OCB = 32768 / (8 * KT * es) / bk * bk;
     if (OCB < bk) OCB = bk;
     if (OCB > p.cig_pad) OCB = p.cig_pad;
     const int64_t nkt = (p.ktot + KT - 1) / KT;
-    const int64_t blocks = (int64_t)p.G * (p.cog_pad / 8) * ((p.cig_pad + OCB - 1) / OCB) * nkt;
+    const int64_t base = (int64_t)p.G * (p.cog_pad / 8) * nkt;
+    while (OCB > bk && base * ((p.cig_pad + OCB - 1) / OCB) < 1024) OCB = (OCB / 2 + bk - 1) / bk * bk;
+    const int64_t blocks = base * ((p.cig_pad + OCB - 1) / OCB);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int vec_runs = KT == p.ktot && p.Cig % OCB == 0 && p.cig_pad % OCB == 0 &&
+                         ((int64_t)p.Cig * p.ktot * es) % 16 == 0 &&
+                         ((int64_t)OCB * p.ktot * es) % 16 == 0 && (uintptr_t)w % 16 == 0;
     const size_t lds = (size_t)8 * OCB * KT * es + (size_t)4 * KT;
     int32_t *tab = (int32_t *)((char *)wr + pl.bwd_tab_offset);
     if (es == 2)
         hipLaunchKernelGGL(reorder_bwd_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds,
-                           stream, p, (const uint16_t *)w, (uint16_t *)wr, tab, OCB, KT);
+                           stream, p, (const uint16_t *)w, (uint16_t *)wr, tab, OCB, KT, vec_runs);
     else
         hipLaunchKernelGGL(reorder_bwd_kernel<float>, dim3((unsigned)blocks), dim3(256), lds,
-                           stream, p, (const float *)w, (float *)wr, tab, OCB, KT);
+                           stream, p, (const float *)w, (float *)wr, tab, OCB, KT, vec_runs);
     return hipGetLastError();
 }
 

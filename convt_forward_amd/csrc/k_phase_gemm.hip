@@ -145,15 +145,16 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
     const int q00 = td_i * T0, q01 = th_i * T1, q02 = tw_i * T2;
     // this phase's halo box: the q box grown by its tap span, starting at the
     // phase's smallest input offset. Backward data: dx position i reads the
-    // phase plane at i - off for the phase's offsets off, so the box of
-    // every phase spans [q - umax, q + T - 1 - umin] (the union of offsets).
-    const int E0 = BWD ? T0 + a0.umax - a0.umin : T0 + (ph.n[0] > 0 ? (ph.n[0] - 1) * a0.ostep : 0);
-    const int E1 = BWD ? T1 + a1.umax - a1.umin : T1 + (ph.n[1] > 0 ? (ph.n[1] - 1) * a1.ostep : 0);
-    const int E2 = BWD ? T2 + a2.umax - a2.umin : T2 + (ph.n[2] > 0 ? (ph.n[2] - 1) * a2.ostep : 0);
+    // phase plane at i - off for the phase's offsets off, so phase P's box
+    // starts at q - (its largest offset); every phase's box gets the extents
+    // of the widest tap span (span_max), so one layout serves all phases.
+    const int E0 = BWD ? T0 + a0.span_max : T0 + (ph.n[0] > 0 ? (ph.n[0] - 1) * a0.ostep : 0);
+    const int E1 = BWD ? T1 + a1.span_max : T1 + (ph.n[1] > 0 ? (ph.n[1] - 1) * a1.ostep : 0);
+    const int E2 = BWD ? T2 + a2.span_max : T2 + (ph.n[2] > 0 ? (ph.n[2] - 1) * a2.ostep : 0);
     const int hsz = E0 * E1 * E2;
-    const int h00 = BWD ? q00 - a0.umax : q00 + ph.off0[0];
-    const int h01 = BWD ? q01 - a1.umax : q01 + ph.off0[1];
-    const int h02 = BWD ? q02 - a2.umax : q02 + ph.off0[2];
+    const int h00 = q00 + ph.off0[0];  // forward only; the backward box is set per phase
+    const int h01 = q01 + ph.off0[1];
+    const int h02 = q02 + ph.off0[2];
 
     f32x16 acc[MT][NT];
 #pragma unroll
@@ -179,22 +180,20 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         // pieces of 64 consecutive box positions, lane l taking position
         // 64j + l.
         // xsp[j]: this lane's byte offset for its piece j, out of range
-        // outside the input. Backward data: box position j of the phase with
-        // residues r is dy position s*j + r (set before each halo copy).
+        // outside the input. Forward: the box starts at input position (b0,
+        // b1, b2). Backward data: the box is in the phase plane
+        // dy_r[j] = dy[s*j + r] of the phase with residues r (set before each
+        // halo copy), read from dy itself (its channel-chunked copy for
+        // bfloat16) at stride s.
         const int xpieces = ES == 2 ? (hsz + 31) / 32 : (hsz + 63) / 64;
         const int nxw = ES == 2 ? (xpieces - wave + NW - 1) / NW : xpieces;  // pieces of this wave
         uint32_t xsp[XJ];
-        auto halo_offsets = [&](int r0, int r1, int r2) __attribute__((always_inline)) {
+        auto halo_offsets = [&](int b0, int b1, int b2) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < XJ; ++j) {
                 const int row = ES == 2 ? (j * NW + wave) * 32 + (lane >> 1) : j * 64 + lane;
                 const int c2 = row % E2, c1 = (row / E2) % E1, c0 = row / (E2 * E1);
-                int i0 = h00 + c0, i1 = h01 + c1, i2 = h02 + c2;
-                if constexpr (BWD) {
-                    i0 = i0 * a0.S + r0;
-                    i1 = i1 * a1.S + r1;
-                    i2 = i2 * a2.S + r2;
-                }
+                const int i0 = b0 + c0, i1 = b1 + c1, i2 = b2 + c2;
                 const uint32_t pos = (uint32_t)((i0 * a1.I + i1) * a2.I + i2);
                 const uint32_t off = ES == 2 ? pos * 32 + (uint32_t)(((lane & 1) ^ ((row >> 3) & 1)) * 16)
                                              : pos * 4;
@@ -204,7 +203,40 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
                              : kOutOfRange;
             }
         };
-        if constexpr (!BWD) halo_offsets(0, 0, 0);
+        if constexpr (!BWD) halo_offsets(h00, h01, h02);
+        // Backward data: the box coordinates of this lane's rows, packed as
+        // c2 | c1 << 11 | c0 << 22 (all-ones past the box), and their byte
+        // offsets relative to the box origin at stride s, computed once; a
+        // phase then needs per-axis bounds on c and one add (halo_phase).
+        uint32_t hcode[BWD ? XJ : 1], hrel[BWD ? XJ : 1];
+        if constexpr (BWD) {
+#pragma unroll
+            for (int j = 0; j < XJ; ++j) {
+                const int row = ES == 2 ? (j * NW + wave) * 32 + (lane >> 1) : j * 64 + lane;
+                const int c2 = row % E2, c1 = (row / E2) % E1, c0 = row / (E2 * E1);
+                hcode[j] = row < hsz ? (uint32_t)c2 | (uint32_t)c1 << 11 | (uint32_t)c0 << 22 : ~0u;
+                const uint32_t rel = (uint32_t)((c0 * a0.S * a1.I + c1 * a1.S) * a2.I + c2 * a2.S);
+                hrel[j] = ES == 2 ? rel * 32 + (uint32_t)(((lane & 1) ^ ((row >> 3) & 1)) * 16) : rel * 4;
+            }
+        }
+        // box starting at phase-plane position b of the phase with residues
+        // r and q counts qn: phase-plane position b + c holds dy[(b + c)*s + r]
+        // for 0 <= b + c < qn, i.e. c in [max(0, -b), qn - 1 - b] per axis
+        auto halo_phase = [&](int b0, int b1, int b2, int r0, int r1, int r2, int n0, int n1,
+                              int n2) __attribute__((always_inline)) {
+            const int e0 = b0 * a0.S + r0, e1 = b1 * a1.S + r1, e2 = b2 * a2.S + r2;
+            const int lo0 = b0 < 0 ? -b0 : 0, lo1 = b1 < 0 ? -b1 : 0, lo2 = b2 < 0 ? -b2 : 0;
+            const int hi0 = n0 - 1 - b0, hi1 = n1 - 1 - b1, hi2 = n2 - 1 - b2;
+            const int kb = ((e0 * a1.I + e1) * a2.I + e2) * (ES == 2 ? 32 : 4);
+#pragma unroll
+            for (int j = 0; j < XJ; ++j) {
+                const int c2 = (int)(hcode[j] & 0x7ffu), c1 = (int)((hcode[j] >> 11) & 0x7ffu),
+                          c0 = (int)(hcode[j] >> 22);
+                const bool ok = c0 >= lo0 && c0 <= hi0 && c1 >= lo1 && c1 <= hi1 && c2 >= lo2 &&
+                                c2 <= hi2;
+                xsp[j] = ok ? hrel[j] + (uint32_t)kb : kOutOfRange;
+            }
+        };
         // halos of the chunks of group cg into ring slot xbi
         auto load_x = [&](int xbi, int cg) __attribute__((always_inline)) {
 #pragma unroll
@@ -339,19 +371,20 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         // box); halo copies run XB - 1 units ahead through a unit cursor.
         const int nstages = BWD ? p.bwd_nstages : nchunks * ngrp;
         const int nx = SC * XCH * nxw;  // halo copies of one chunk group by this wave
-        // the next phase with taps after q (-1: none), and a phase's tap groups
-        auto live_after = [&](int q) __attribute__((always_inline)) {
-            for (int n = q + 1; n < p.nphase; ++n)
-                if (p.ph[n].ntaps > 0) return n;
-            return -1;
+        // backward data: the phases with taps, in order (p.bwd_live), by index k
+        auto live_after = [&](int k) __attribute__((always_inline)) {
+            return k + 1 < p.bwd_nlive ? k + 1 : -1;
         };
-        auto groups_of = [&](int q) __attribute__((always_inline)) {
-            return BWD ? (p.ph[q].ntaps + GS - 1) / GS : ngrp;
+        auto phase_of = [&](int k) __attribute__((always_inline)) {
+            return BWD ? (int)p.bwd_live[k] : P;
         };
-        auto tapbase_of = [&](int q) __attribute__((always_inline)) {
-            return BWD ? p.ph[q].tapbase : 0;
+        auto groups_of = [&](int k) __attribute__((always_inline)) {
+            return BWD ? (p.ph[phase_of(k)].ntaps + GS - 1) / GS : ngrp;
         };
-        const int first = BWD ? live_after(-1) : P;
+        auto tapbase_of = [&](int k) __attribute__((always_inline)) {
+            return BWD ? p.ph[phase_of(k)].tapbase : 0;
+        };
+        const int first = 0;
         auto next_unit = [&](int &c, int &q) __attribute__((always_inline)) {
             ++c;
             if constexpr (BWD) {
@@ -371,8 +404,13 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         // backward data: halo copy of the unit at the cursor (cx, qx)
         int cx = 0, qx = first;
         auto issue_x = [&](int xbi) __attribute__((always_inline)) {
-            const PhaseRec &rec = p.ph[qx];
-            halo_offsets(rec.rn[0] & 0xff, rec.rn[1] & 0xff, rec.rn[2] & 0xff);
+            // the box starts at q - (the phase's largest offset per axis: first
+            // offset + (taps - 1) * ostep)
+            const PhaseDesc d = phase_desc(p, phase_of(qx));
+            halo_phase(q00 - d.off0[0] - (d.n[0] - 1) * a0.ostep,
+                       q01 - d.off0[1] - (d.n[1] - 1) * a1.ostep,
+                       q02 - d.off0[2] - (d.n[2] - 1) * a2.ostep, d.r[0], d.r[1], d.r[2], d.qn[0],
+                       d.qn[1], d.qn[2]);
             load_x(xbi, cx);
             next_unit(cx, qx);
         };

@@ -148,9 +148,9 @@ void fill_phase_table(DevParams *dp) {
 // A block computes BN positions of one phase for BM output channels. The q
 // tile is a (td, th, tw) box with td*th*tw == BN; its input halo grows by the
 // tap span of the phase on each axis and must fit the LDS halo buffer.
-// Backward data (bwd): the tile is a box of dx positions, and its halo in a
-// phase plane of dy spans the union of every phase's offsets (span_max holds
-// umax - umin there); a block runs every phase's taps.
+// Backward data (bwd): the tile is a box of dx positions and its halo in a
+// phase plane of dy grows by the phase's tap span (at most span_max); a
+// block runs every phase's taps.
 bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max, bool bwd) {
     int64_t best_cost = std::numeric_limits<int64_t>::max();
     int bd = 0, bh = 0, bw = 0;
@@ -164,6 +164,8 @@ bool choose_gemm_tile(DevParams *dp, int ndim, int BN, int halo_max, bool bwd) {
             const int64_t hh = th + dp->ax[1].span_max;
             const int64_t hw = tw + dp->ax[2].span_max;
             if (hd * hh * hw > halo_max) continue;
+            // the backward kernel packs box coordinates in 10 + 11 + 11 bits
+            if (bwd && (hd > 1023 || hh > 2047 || hw > 2047)) continue;
             const int64_t nt = ceil_div(dp->ax[0].qmax, td) * ceil_div(dp->ax[1].qmax, th) *
                                ceil_div(dp->ax[2].qmax, tw);
             // MFMA work of a tile (masked positions included) dominates; halo
@@ -217,19 +219,48 @@ int choose_gemm_gs(const DevParams &dp) {
 // rounds of two per CU, each round costing its blocks' padded MFMA work,
 // scaled up where the wave tile's LDS operand reads would outrun the MFMAs
 // and by a per-MFMA overhead that small wave tiles amortise worse.
-int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs);
+int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs, double *t_out);
 
-// With the preferred taps per stage first, then fewer (smaller weight
-// buffers leave more LDS to the halo) until some configuration fits.
-int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd) {
-    for (int gs = choose_gemm_gs(*dp); gs >= 1; --gs) {
-        const int c = pick_gemm_cfg(dp, dtype, ndim, bwd, gs);
-        if (c >= 0) return c;
-    }
-    return -1;
+// Padded tap work of gs taps per stage, with the per-stage overhead of
+// choose_gemm_gs.
+double tap_work(const DevParams &dp, int gs) {
+    int64_t padded = 0;
+    for (int P = 0; P < dp.nphase; ++P) padded += ceil_div(dp.ph[P].ntaps, gs) * gs;
+    return (double)padded * (1.0 + 0.3 / gs);
 }
 
-int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs) {
+// Forward: the preferred taps per stage first, then fewer (smaller weight
+// buffers leave more LDS to the halo) until some configuration fits.
+// Backward data, whose halos are larger: every (taps per stage,
+// configuration) pair, by modelled time.
+int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd) {
+    if (!bwd) {
+        for (int gs = choose_gemm_gs(*dp); gs >= 1; --gs) {
+            const int c = pick_gemm_cfg(dp, dtype, ndim, false, gs, nullptr);
+            if (c >= 0) return c;
+        }
+        return -1;
+    }
+    int best = -1;
+    double best_t = 0;
+    DevParams best_dp{};
+    for (int gs = tiles::kGemmTapGroup; gs >= 1; --gs) {
+        DevParams tmp = *dp;
+        double t = 0;
+        const int c = pick_gemm_cfg(&tmp, dtype, ndim, true, gs, &t);
+        if (c < 0) continue;
+        t *= tap_work(*dp, gs);
+        if (best < 0 || t < best_t * 0.999) {
+            best = c;
+            best_t = t;
+            best_dp = tmp;
+        }
+    }
+    if (best >= 0) *dp = best_dp;
+    return best;
+}
+
+int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs, double *t_out) {
     const bool bf16 = dtype == CONVT_DTYPE_BF16;
     int best = -1;
     double best_t = 0;
@@ -260,6 +291,7 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs) {
         *dp = best_dp;
         dp->gemm_cfg = best;
         dp->gemm_gs = gs;
+        if (t_out) *t_out = best_t;
     }
     return best;
 }
@@ -397,12 +429,13 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
     memset(&b, 0, sizeof(b));
     for (int a = 0; a < 3; ++a) fill_axis(&b.ax[a], I[a], K[a], S[a], P[a], D[a], O[a]);
     fill_phase_table(&b);
+    // The input is dy (ax.I = O), the output dx (ax.O = qmax = I); span_max
+    // stays the widest phase's tap span.
     for (int a = 0; a < 3; ++a) {
         DevAxis &ax = b.ax[a];
-        ax.I = (int32_t)O[a];  // the input is dy
-        ax.O = (int32_t)I[a];  // the output is dx
+        ax.I = (int32_t)O[a];
+        ax.O = (int32_t)I[a];
         ax.qmax = (int32_t)I[a];
-        ax.span_max = ax.umax - ax.umin;
     }
     b.B = fp.B;
     b.Ci = fp.Co;
@@ -434,7 +467,9 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
         switch (route) {
             case CONVT_ROUTE_NONE: ok = empty_out; break;
             case CONVT_ROUTE_FILL: ok = !empty_out && no_terms; break;
-            case CONVT_ROUTE_PHASE_GEMM: ok = !empty_out && !no_terms && gemm_eligible(b, dt, nd, true); break;
+            case CONVT_ROUTE_PHASE_GEMM:
+                ok = !empty_out && !no_terms && gemm_eligible(b, dt, nd, true);
+                break;
             case CONVT_ROUTE_NAIVE: ok = !empty_out && !no_terms; break;
             default: ok = false;
         }
@@ -453,11 +488,13 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
     b.cig_pad = (int32_t)(ceil_div(b.Cig, bk) * bk);
     b.wr_chunked = 1;
     int64_t base = 0, stages = 0;
+    b.bwd_nlive = 0;
     for (int ph = 0; ph < b.nphase; ++ph) {
         const int64_t ng = ceil_div(b.ph[ph].ntaps, b.gemm_gs);
         b.ph[ph].tapbase = (int32_t)base;
         base += ng * b.gemm_gs;
         stages += ng * (b.cig_pad / bk);
+        if (ng > 0) b.bwd_live[b.bwd_nlive++] = (uint8_t)ph;
     }
     if (base > i31 || stages > i31) return CONVT_ERR_UNSUPPORTED;
     b.ktot_pad = (int32_t)base;

@@ -29,6 +29,34 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported request", 3: "device e
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i8": 3, "i32": 4, "i64": 5}
 ROUTES = {"auto": 0, "none": 1, "fill": 2, "phase_gemm": 3, "grouped": 4, "direct": 5, "naive": 6}
 ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
+# filter layouts (element (ci, ocl, kk) of W; see include/convt.h):
+#   ci_co_k [C_in][C_out/groups][k...], k_ci_co [k...][C_in][C_out/groups],
+#   k_co_ci [k...][C_out][C_in/groups]
+FILTER_LAYOUTS = {"ci_co_k": 0, "k_ci_co": 1, "k_co_ci": 2}
+
+
+def layout_w_shape(w_shape: Sequence[int], groups: int, layout: str) -> Tuple[int, ...]:
+    """Shape of W in `layout`, from its [C_in, C_out/groups, k...] shape."""
+    ci, cog, k = int(w_shape[0]), int(w_shape[1]), tuple(int(v) for v in w_shape[2:])
+    if layout == "ci_co_k":
+        return (ci, cog) + k
+    if layout == "k_ci_co":
+        return k + (ci, cog)
+    if layout == "k_co_ci":
+        return k + (cog * groups, ci // groups)
+    raise ValueError(f"unknown filter layout {layout!r}")
+
+
+def canonical_w_shape(shape: Sequence[int], groups: int, layout: str) -> Tuple[int, ...]:
+    """[C_in, C_out/groups, k...] from the shape of W in `layout`."""
+    shape = tuple(int(v) for v in shape)
+    if layout == "ci_co_k":
+        return shape
+    if layout == "k_ci_co":
+        return (shape[-2], shape[-1]) + shape[:-2]
+    if layout == "k_co_ci":
+        return (shape[-1] * groups, shape[-2] // groups) + shape[:-2]
+    raise ValueError(f"unknown filter layout {layout!r}")
 
 
 class ConvtError(RuntimeError):
@@ -53,6 +81,8 @@ class Problem(ctypes.Structure):
         ("has_padding_hi", ctypes.c_int32),
         ("route_bwd", ctypes.c_int32),
         ("padding_hi", ctypes.c_int64 * MAX_NDIM),
+        ("filter_layout", ctypes.c_int32),
+        ("taps_flipped", ctypes.c_int32),
     ]
 
 
@@ -136,7 +166,10 @@ def _pads(v, nd: int) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
 
 def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, padding=0, dilation=1,
                  output_padding=0, groups: int = 1, has_bias: bool = False, dtype: str = "f32",
-                 route: str = "auto", route_bwd: str = "auto") -> Problem:
+                 route: str = "auto", route_bwd: str = "auto", filter_layout: str = "ci_co_k",
+                 taps_flipped: bool = False) -> Problem:
+    """w_shape is [C_in, C_out/groups, k...] whatever filter_layout says about
+    W's memory order."""
     nd = len(x_shape) - 2
     if not 1 <= nd <= MAX_NDIM or len(w_shape) != nd + 2:
         raise ValueError("x must be [B, C_in, I...] and w [C_in, C_out/groups, k...] with 1-3 spatial axes")
@@ -160,6 +193,8 @@ def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, paddi
     p.has_bias = 1 if has_bias else 0
     p.route = ROUTES[route]
     p.route_bwd = ROUTES[route_bwd]
+    p.filter_layout = FILTER_LAYOUTS[filter_layout]
+    p.taps_flipped = 1 if taps_flipped else 0
     return p
 
 
@@ -200,6 +235,13 @@ class Plan:
     @property
     def route(self) -> str:
         return ROUTE_NAMES[int(self.info.route)]
+
+    @property
+    def w_layout_shape(self) -> Tuple[int, ...]:
+        """The shape W has in the plan's filter layout."""
+        p = self.problem
+        name = {v: k for k, v in FILTER_LAYOUTS.items()}[int(p.filter_layout)]
+        return layout_w_shape(tuple(p.w_shape[:2 + self.ndim]), int(p.groups), name)
 
     @property
     def route_bwd(self) -> str:
@@ -285,7 +327,7 @@ class Plan:
         p = self.problem
         nd = self.ndim
         self._check(x, tuple(p.x_shape[:2 + nd]), "x")
-        self._check(w, tuple(p.w_shape[:2 + nd]), "w")
+        self._check(w, self.w_layout_shape, "w")
         if p.has_bias:
             if bias is None:
                 raise ValueError("the plan has a bias")
@@ -323,7 +365,7 @@ class Plan:
         p = self.problem
         nd = self.ndim
         self._check(dy, self.out_shape, "dy")
-        self._check(w, tuple(p.w_shape[:2 + nd]), "w")
+        self._check(w, self.w_layout_shape, "w")
         if dx is None:
             dx = self.new_input_grad(dy.device)
         else:
@@ -343,15 +385,17 @@ _plan_cache: Dict[tuple, Plan] = {}
 
 
 def get_plan(x_shape, w_shape, stride=1, padding=0, dilation=1, output_padding=0, groups=1,
-             has_bias=False, dtype="f32", route="auto", route_bwd="auto") -> Plan:
+             has_bias=False, dtype="f32", route="auto", route_bwd="auto",
+             filter_layout="ci_co_k", taps_flipped=False) -> Plan:
+    """A cached plan; w_shape is [C_in, C_out/groups, k...]."""
     nd = len(x_shape) - 2
     key = (tuple(x_shape), tuple(w_shape), _tup(stride, nd, "stride"), _pads(padding, nd),
            _tup(dilation, nd, "dilation"), _tup(output_padding, nd, "output_padding"), int(groups),
-           bool(has_bias), dtype, route, route_bwd)
+           bool(has_bias), dtype, route, route_bwd, filter_layout, bool(taps_flipped))
     pl = _plan_cache.get(key)
     if pl is None:
         pl = Plan.create(x_shape, w_shape, stride, padding, dilation, output_padding, groups,
-                         has_bias, dtype, route, route_bwd)
+                         has_bias, dtype, route, route_bwd, filter_layout, taps_flipped)
         _plan_cache[key] = pl
     return pl
 
@@ -374,19 +418,24 @@ def torch_dtype_name(t) -> str:
 
 
 def conv_transpose(x, w, bias=None, stride=1, padding=0, dilation=1, output_padding=0, groups=1,
-                   route: str = "auto", y=None, workspace=None, stream=None):
-    """ConvTranspose forward on the GPU through libconvt. Returns y."""
-    pl = get_plan(tuple(x.shape), tuple(w.shape), stride, padding, dilation, output_padding, groups,
-                  bias is not None, torch_dtype_name(x), route)
+                   route: str = "auto", y=None, workspace=None, stream=None,
+                   filter_layout: str = "ci_co_k", taps_flipped: bool = False):
+    """ConvTranspose forward on the GPU through libconvt. Returns y. w is in
+    `filter_layout` (and spatially reversed when taps_flipped)."""
+    pl = get_plan(tuple(x.shape), canonical_w_shape(w.shape, groups, filter_layout), stride,
+                  padding, dilation, output_padding, groups, bias is not None,
+                  torch_dtype_name(x), route, "auto", filter_layout, taps_flipped)
     return pl.forward(x, w, bias, y=y, workspace=workspace, stream=stream)
 
 
 def conv_transpose_backward_data(dy, w, x_shape, stride=1, padding=0, dilation=1,
                                  output_padding=0, groups=1, route: str = "auto", dx=None,
-                                 workspace=None, stream=None):
+                                 workspace=None, stream=None, filter_layout: str = "ci_co_k",
+                                 taps_flipped: bool = False):
     """Gradient of a loss with respect to the input x of conv_transpose, given
     its gradient dy with respect to the output (on the GPU through libconvt).
     Returns dx, of shape x_shape."""
-    pl = get_plan(tuple(x_shape), tuple(w.shape), stride, padding, dilation, output_padding,
-                  groups, False, torch_dtype_name(dy), "auto", route)
+    pl = get_plan(tuple(x_shape), canonical_w_shape(w.shape, groups, filter_layout), stride,
+                  padding, dilation, output_padding, groups, False, torch_dtype_name(dy), "auto",
+                  route, filter_layout, taps_flipped)
     return pl.backward_data(dy, w, dx=dx, workspace=workspace, stream=stream)

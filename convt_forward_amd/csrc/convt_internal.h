@@ -56,6 +56,8 @@ struct DevParams {
     int32_t nphase;            // prod(S)
     int32_t x_plane, y_plane;  // spatial elements of one x / y channel plane
     int32_t has_bias;
+    int32_t w_layout;          // convt_filter_layout of W
+    int32_t w_flip;            // 1: W's taps are stored spatially reversed
     // Tiling of the main kernel (meaning depends on the route).
     int32_t td, th, tw;        // q-tile extents
     int32_t hd, hh, hw;        // halo box extents (largest over phases)

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__re
     const T *wg = w + (int64_t)g * p.Cig * p.Cog * ktot;
     const int lim = (p.Cog - co0) * ktot;  // elements of a channel row inside W
     const int total = VEC * n;
+    const bool plain = w_plain(p);
     for (int e0 = threadIdx.x; e0 < total; e0 += 256 * 8) {
         T v[8];
         bool ok[8];
@@ -88,7 +89,10 @@ __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__re
             const int cil = e / n, r = e - cil * n;
             const int ci = ci_b * VEC + cil;
             ok[u] = e < total && ci < p.Cig && r < lim;
-            v[u] = wg[ok[u] ? ((int64_t)ci * p.Cog + co0) * ktot + r : 0];
+            if (plain)
+                v[u] = wg[ok[u] ? ((int64_t)ci * p.Cog + co0) * ktot + r : 0];
+            else
+                v[u] = w[ok[u] ? w_offset(p, g * p.Cig + ci, co0 + r / ktot, r % ktot) : 0];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
                 const int col = r / nk, k = r - col * nk;
                 const int ci = c * BK + i, co = co0 + col;
                 const bool ok = e < n_in && ci < p.Cig && co < p.Cog;
-                v[u] = w[ok ? (((int64_t)g * p.Cig + ci) * p.Cog + co) * ktot + kk0 + k : 0];
+                v[u] = w[ok ? w_offset(p, g * p.Cig + ci, co, kk0 + k) : 0];
                 if (!ok) v[u] = from_f32<T>(0.0f);
             }
 #pragma unroll
@@ -301,7 +305,8 @@ hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t s
         while (CO > 1 && base * ((p.cog_pad + CO - 1) / CO) < 1024) CO /= 2;
         const int64_t blocks = base * ((p.cog_pad + CO - 1) / CO);
         const int64_t run_bytes = (int64_t)CO * p.ktot * pl.elem_bytes;
-        const int vec_runs = KT == p.ktot && run_bytes % 16 == 0 &&
+        const int vec_runs = p.w_layout == CONVT_FILTER_CI_CO_K && !p.w_flip && KT == p.ktot &&
+                             run_bytes % 16 == 0 &&
                              ((int64_t)p.Cog * p.ktot * pl.elem_bytes) % 16 == 0 &&
                              p.Cog % CO == 0 && (uintptr_t)w % 16 == 0;
         if (blocks <= 0) return hipSuccess;
@@ -507,7 +512,7 @@ __global__ __launch_bounds__(256) void naive_kernel(DevParams p, const T *__rest
         float acc = 0.0f;
         for (int ci = 0; ci < p.Cig; ++ci) {
             const T *xp = x + ((int64_t)b * p.Ci + g * p.Cig + ci) * p.x_plane;
-            const T *wp = w + ((int64_t)(g * p.Cig + ci) * p.Cog + ocl) * p.ktot;
+            const int cig = g * p.Cig + ci;
             for (int k0 = 0; k0 < a0.K; ++k0) {
                 const int t0 = o0 + a0.P - k0 * a0.D;
                 if (t0 % a0.S) continue;
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(256) void naive_kernel(DevParams p, const T *__rest
                         const int i2 = t2 / a2.S;
                         if (i2 < 0 || i2 >= a2.I) continue;
                         acc += to_f32(xp[((int64_t)i0 * a1.I + i1) * a2.I + i2]) *
-                               to_f32(wp[(k0 * a1.K + k1) * a2.K + k2]);
+                               to_f32(w[w_offset(p, cig, ocl, (k0 * a1.K + k1) * a2.K + k2)]);
                     }
                 }
             }
@@ -576,7 +581,15 @@ __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__res
     const int b = bid / p.G;
     const int slab_n = p.Cig * p.Cog * p.ktot;
     const T *wg = w + (int64_t)g * slab_n;
-    for (int e = threadIdx.x; e < slab_n; e += 256) slab[e] = to_f32(wg[e]);
+    if (w_plain(p)) {
+        for (int e = threadIdx.x; e < slab_n; e += 256) slab[e] = to_f32(wg[e]);
+    } else {
+        // slab element e = (ci * Cog + co) * ktot + kk
+        for (int e = threadIdx.x; e < slab_n; e += 256) {
+            const int kk = e % p.ktot, co = (e / p.ktot) % p.Cog, ci = e / (p.ktot * p.Cog);
+            slab[e] = to_f32(w[w_offset(p, g * p.Cig + ci, co, kk)]);
+        }
+    }
     __syncthreads();
     const int o = tile * kDirPos + threadIdx.x;
     if (o >= p.y_plane) return;
@@ -671,7 +684,6 @@ __global__ __launch_bounds__(256) void naive_bwd_kernel(DevParams p, const T *__
         const int i2 = i % a2.I, i1 = (i / a2.I) % a1.I, i0 = i / (a2.I * a1.I);
         const int g = ci / p.Cig;
         const T *yb = dy + ((int64_t)b * p.Co + (int64_t)g * p.Cog) * p.y_plane;
-        const T *wb = w + (int64_t)ci * p.Cog * p.ktot;
         float acc = 0.0f;
         for (int k0 = 0; k0 < a0.K; ++k0) {
             const int o0 = i0 * a0.S - a0.P + k0 * a0.D;
@@ -686,7 +698,7 @@ __global__ __launch_bounds__(256) void naive_bwd_kernel(DevParams p, const T *__
                     const int kk = (k0 * a1.K + k1) * a2.K + k2;
                     for (int ocl = 0; ocl < p.Cog; ++ocl)
                         acc += to_f32(yb[(int64_t)ocl * p.y_plane + opos]) *
-                               to_f32(wb[(int64_t)ocl * p.ktot + kk]);
+                               to_f32(w[w_offset(p, ci, ocl, kk)]);
                 }
             }
         }
@@ -795,7 +807,11 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
             const int col = r / nk, k = r - col * nk;
             const int m = m0 + i, oc = oc0 + col;
             const bool ok = e < n_in && m < Cm && oc < Coc;
-            v[u] = w[ok ? (((int64_t)g * Cm + m) * Coc + oc) * ktot + kk0 + k : 0];
+            // p is the backward problem: the forward's Ci = p.Co, Co = p.Ci,
+            // Cig = Cm, Cog = Coc
+            v[u] = w[ok ? w_offset(p.w_layout, p.w_flip, p.Co, p.Ci, Cm, Coc, p.ax[0].K, p.ax[1].K,
+                                   p.ax[2].K, g * Cm + m, oc, kk0 + k)
+                        : 0];
             if (!ok) v[u] = from_f32<T>(0.0f);
         }
 #pragma unroll
@@ -884,7 +900,8 @@ hipError_t launch_reorder_bwd(const Plan &pl, const void *w, void *wr, hipStream
     const int64_t blocks = base * ((p.cig_pad + OCB - 1) / OCB);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const int vec_runs = KT == p.ktot && p.Cig % OCB == 0 && p.cig_pad % OCB == 0 &&
+    const int vec_runs = p.w_layout == CONVT_FILTER_CI_CO_K && !p.w_flip && KT == p.ktot &&
+                         p.Cig % OCB == 0 && p.cig_pad % OCB == 0 &&
                          ((int64_t)p.Cig * p.ktot * es) % 16 == 0 &&
                          ((int64_t)OCB * p.ktot * es) % 16 == 0 && (uintptr_t)w % 16 == 0;
     const size_t lds = (size_t)8 * OCB * KT * es + (size_t)4 * KT;

@@ -105,6 +105,34 @@ __device__ __forceinline__ int tap_in_table(const DevParams &p, int k0, int k1, 
     return p.ph[P].tapbase + (j[0] * n[1] + j[1]) * n[2] + j[2];
 }
 
+// Element offset in W of the weight from input channel ci (global) to output
+// channel ocl of ci's group at forward tap kk (row-major over K0, K1, K2),
+// for the filter layouts of convt.h; Ci, Co, Cig, Cog are the forward
+// problem's channel counts.
+__device__ __forceinline__ int64_t w_offset(int layout, int flip, int Ci, int Co, int Cig, int Cog,
+                                            int K0, int K1, int K2, int ci, int ocl, int kk) {
+    if (flip) {
+        const int k2 = kk % K2, k1 = (kk / K2) % K1, k0 = kk / (K1 * K2);
+        kk = ((K0 - 1 - k0) * K1 + (K1 - 1 - k1)) * K2 + (K2 - 1 - k2);
+    }
+    const int ktot = K0 * K1 * K2;
+    if (layout == CONVT_FILTER_K_CI_CO) return ((int64_t)kk * Ci + ci) * Cog + ocl;
+    if (layout == CONVT_FILTER_K_CO_CI) {
+        const int g = ci / Cig;
+        return ((int64_t)kk * Co + (int64_t)g * Cog + ocl) * Cig + (ci - g * Cig);
+    }
+    return ((int64_t)ci * Cog + ocl) * ktot + kk;
+}
+// The same for a forward problem's parameters.
+__device__ __forceinline__ int64_t w_offset(const DevParams &p, int ci, int ocl, int kk) {
+    return w_offset(p.w_layout, p.w_flip, p.Ci, p.Co, p.Cig, p.Cog, p.ax[0].K, p.ax[1].K, p.ax[2].K,
+                    ci, ocl, kk);
+}
+// Whether W is in the default layout and orientation (the vector paths).
+__device__ __forceinline__ bool w_plain(const DevParams &p) {
+    return p.w_layout == CONVT_FILTER_CI_CO_K && !p.w_flip;
+}
+
 // ---- raw buffers and global -> LDS copies (phase GEMM, grouped kernel) ----
 
 // Buffer resource word 3 for gfx9-family raw buffers.

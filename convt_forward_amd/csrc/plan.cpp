@@ -448,6 +448,8 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
     b.x_plane = fp.y_plane;
     b.y_plane = fp.x_plane;
     b.has_bias = 0;
+    b.w_layout = fp.w_layout;
+    b.w_flip = fp.w_flip;
     const int dt = p->dtype;
     const int nd = pl->ndim;
     const bool empty_out = b.B == 0 || b.Co == 0 || b.y_plane == 0;
@@ -535,6 +537,9 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     if (p->route < CONVT_ROUTE_AUTO || p->route > CONVT_ROUTE_NAIVE)
         return CONVT_ERR_INVALID_ARGUMENT;
     if (p->has_padding_hi != 0 && p->has_padding_hi != 1) return CONVT_ERR_INVALID_ARGUMENT;
+    if (p->filter_layout < CONVT_FILTER_CI_CO_K || p->filter_layout > CONVT_FILTER_K_CO_CI ||
+        (p->taps_flipped != 0 && p->taps_flipped != 1))
+        return CONVT_ERR_INVALID_ARGUMENT;
     if (p->route_bwd < CONVT_ROUTE_AUTO || p->route_bwd > CONVT_ROUTE_NAIVE)
         return CONVT_ERR_INVALID_ARGUMENT;
     const int64_t B = p->x_shape[0], Ci = p->x_shape[1];
@@ -621,6 +626,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     dp.x_plane = (int32_t)xpl;
     dp.y_plane = (int32_t)ypl;
     dp.has_bias = p->has_bias;
+    dp.w_layout = p->filter_layout;
+    dp.w_flip = p->taps_flipped;
 
     // ---- route ------------------------------------------------------------
     const bool empty_out = (B == 0 || Co == 0);

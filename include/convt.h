@@ -97,6 +97,23 @@ typedef enum convt_route {
     CONVT_ROUTE_NAIVE = 6       /* one thread per output, gathers its terms */
 } convt_route;
 
+/* How W is laid out in memory (the AWS Neuron conv3d_transpose page's
+ * filter_shape, extended to groups). Element (ci, ocl, kk) is the weight
+ * from input channel ci (global) to output channel g*Cog + ocl of ci's group
+ * g, at tap kk (row-major over the kernel axes):
+ *   CI_CO_K  [C_in][C_out/groups][k...]   (the SKaiNET page's layout; default)
+ *   K_CI_CO  [k...][C_in][C_out/groups]   (the Neuron page's KDHW_CI_CO)
+ *   K_CO_CI  [k...][C_out][C_in/groups]   (the Neuron page's KDHW_CO_CI)
+ * w_shape in convt_problem stays [C_in, C_out/groups, k...] whatever the
+ * layout. With taps_flipped = 1 the stored tap kk holds the forward tap
+ * (k_1-1-kk_1, ..., k_n-1-kk_n): the caller has spatially reversed the
+ * filter (the Neuron page's flip_filter_taps_in_kernel = False). */
+typedef enum convt_filter_layout {
+    CONVT_FILTER_CI_CO_K = 0,
+    CONVT_FILTER_K_CI_CO = 1,
+    CONVT_FILTER_K_CO_CI = 2
+} convt_filter_layout;
+
 /* The problem, in the terms the pages use. Only the first 2 + ndim entries
  * of the shape arrays and the first ndim entries of the attribute arrays are
  * read. padding is the low (leading) padding of each axis; the high
@@ -118,6 +135,8 @@ typedef struct convt_problem {
     int32_t has_padding_hi;                     /* 0: high padding = padding; 1: = padding_hi */
     int32_t route_bwd;                          /* convt_route of convt_backward_data; AUTO normally */
     int64_t padding_hi[CONVT_MAX_NDIM];         /* >= 0; read only when has_padding_hi = 1 */
+    int32_t filter_layout;                      /* convt_filter_layout of W */
+    int32_t taps_flipped;                       /* 1: W's taps are spatially reversed */
 } convt_problem;
 
 typedef struct convt_plan_info {
@@ -141,7 +160,8 @@ typedef struct convt_plan_s *convt_plan_t;
  * divisibility, bias shape, dtype guard; plus shape consistency):
  *   ndim in 1..3; all sizes >= 0; kernel sizes >= 1; stride >= 1;
  *   padding >= 0 (both ends); has_padding_hi in {0, 1}; route and route_bwd
- *   valid convt_route codes;
+ *   valid convt_route codes; filter_layout a convt_filter_layout;
+ *   taps_flipped in {0, 1};
  *   dilation >= 1; 0 <= output_padding < max(stride, dilation);
  *   groups >= 1 dividing C_in; w_shape[0] == C_in; every output size >= 1;
  *   has_bias in {0, 1}; element counts of x, W and y below 2^62 and each

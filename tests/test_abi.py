@@ -301,3 +301,22 @@ def test_backward_routes():
     assert status_of(x_shape=(1, 2, 5), w_shape=(2, 3, 3), stride=19, route_bwd="phase_gemm") == 2
     assert status_of(x_shape=(1, 2, 5), w_shape=(2, 3, 3), route_bwd="fill") == 2
     assert status_of(x_shape=(1, 2, 5), w_shape=(2, 3, 3), route_bwd="grouped") == 2
+
+
+def test_filter_layout_shapes_and_validation():
+    """W's shape in each filter layout (include/convt.h) and back; bad codes
+    are refused."""
+    ws = (6, 5, 3, 4)  # C_in 6, C_out/groups 5, k 3x4, groups 2
+    assert C.layout_w_shape(ws, 2, "ci_co_k") == ws
+    assert C.layout_w_shape(ws, 2, "k_ci_co") == (3, 4, 6, 5)
+    assert C.layout_w_shape(ws, 2, "k_co_ci") == (3, 4, 10, 3)
+    for lay in C.FILTER_LAYOUTS:
+        assert C.canonical_w_shape(C.layout_w_shape(ws, 2, lay), 2, lay) == ws
+    L = C.lib()
+    for fl, tf in [(3, 0), (-1, 0), (0, 2)]:
+        p = C.make_problem((1, 6, 5, 5), ws, groups=2)
+        p.filter_layout, p.taps_flipped = fl, tf
+        h = ctypes.c_void_p()
+        assert L.convt_plan(ctypes.byref(p), ctypes.byref(h), None) == 1
+    pl = plan(x_shape=(1, 6, 5, 5), w_shape=ws, groups=2, filter_layout="k_co_ci", taps_flipped=True)
+    assert pl.w_layout_shape == (3, 4, 10, 3)

@@ -52,6 +52,8 @@ def _bind(path: str):
                                         ctypes.c_int64, pd, pd, pd, ctypes.c_int64, p64, pd,
                                         pd, ctypes.c_int]
     lib.convt_oracle_points.restype = ctypes.c_int
+    lib.convt_oracle_activation.argtypes = [ctypes.c_int, pd, pd, ctypes.c_int64]
+    lib.convt_oracle_activation.restype = ctypes.c_int
     lib.convt_oracle_backward_data.argtypes = [ctypes.c_int, p64, p64, p64, p64, p64, p64, p64,
                                                ctypes.c_int64, pd, pd, pd, pd, ctypes.c_int]
     lib.convt_oracle_backward_data.restype = ctypes.c_int
@@ -125,10 +127,24 @@ class Oracle:
             raise ValueError("ill-formed transposed convolution")
         return tuple(int(v) for v in out)
 
+    def activation(self, act: int, v: np.ndarray) -> np.ndarray:
+        """The activation with code act (0 none, 1 ReLU, 2 sigmoid, 3 tanh,
+        4 SiLU, 5 GELU) applied to each element of v, in float64."""
+        a = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty_like(a)
+        rc = self.lib.convt_oracle_activation(int(act), a.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                              out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                              int(a.size))
+        if rc != 0:
+            raise ValueError(f"unknown activation {act}")
+        return out
+
     def forward(self, x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray] = None,
                 stride=None, padding=None, dilation=None, output_padding=None, groups: int = 1,
-                with_scale: bool = True, nthreads: int = 0):
-        """Full forward pass in float64. Returns (y, scale); scale is None unless asked."""
+                with_scale: bool = True, nthreads: int = 0, activation: int = 0):
+        """Full forward pass in float64, then the activation (code as in
+        activation()). Returns (y, scale); scale (the magnitude sum of the
+        terms before the activation) is None unless asked."""
         nd, s, p, ph, d, op = _attrs(x.shape, w.shape, stride, padding, dilation, output_padding)
         oshape = self.out_shape(x.shape, w.shape, s, list(zip(p, ph)), d, op, groups)
         xa, xp = _f64(x)
@@ -146,12 +162,15 @@ class Oracle:
             int(nthreads))
         if rc != 0:
             raise ValueError("ill-formed transposed convolution")
+        if activation:
+            y = self.activation(activation, y)
         return y, sc
 
     def points(self, x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], pts: np.ndarray,
                stride=None, padding=None, dilation=None, output_padding=None, groups: int = 1,
-               nthreads: int = 0):
-        """Outputs at the given points, each computed on its own.
+               nthreads: int = 0, activation: int = 0):
+        """Outputs at the given points, each computed on its own, then the
+        activation.
 
         ``pts`` is an int array [n, 2 + ndim] of (b, oc, o...). Returns (y, scale)
         as float64 arrays of length n.
@@ -172,8 +191,9 @@ class Oracle:
             sv.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(nthreads))
         if rc != 0:
             raise ValueError("ill-formed problem or point out of range")
+        if activation:
+            yv = self.activation(activation, yv)
         return yv, sv
-
 
     def backward_data(self, dy: np.ndarray, w: np.ndarray, x_shape, stride=None, padding=None,
                       dilation=None, output_padding=None, groups: int = 1,
@@ -261,3 +281,7 @@ def backward_data(*args, **kwargs):
 
 def backward_data_points(*args, **kwargs):
     return default().backward_data_points(*args, **kwargs)
+
+
+def activation(*args, **kwargs):
+    return default().activation(*args, **kwargs)

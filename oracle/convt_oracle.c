@@ -45,6 +45,13 @@
  * thread only and its terms are added in a fixed order, so results do not
  * depend on the thread count.
  *
+ * Activation (the AWS Neuron conv3d_transpose page's activation_fn, an
+ * optional function applied after the convolution; the page names no
+ * functions). Read here as one of a fixed set applied to each output after
+ * the bias: code 1 ReLU max(v, 0); 2 logistic sigmoid 1/(1 + e^-v); 3 tanh;
+ * 4 SiLU v/(1 + e^-v); 5 GELU v/2 (1 + erf(v/sqrt 2)); 0 none
+ * (convt_oracle_activation, applied by the caller to the forward result).
+ *
  * Backward data (the input gradient, named as the adjoint for the input in
  * the SKaiNET page's Summary, convTranspose2dBackward): y is linear in x, and
  * x[b, ci, i] enters exactly the terms listed above, so for an upstream
@@ -401,6 +408,27 @@ int convt_oracle_backward_data_points(int ndim, const int64_t *x_shape, const in
         }
         dxv[n] = acc;
         if (sv) sv[n] = mag;
+    }
+    return 0;
+}
+
+/* out[i] = f(in[i]) for activation code act (0..5, see the header); in and
+ * out may be the same array. Returns 0, or -1 for an unknown code. */
+int convt_oracle_activation(int act, const double *in, double *out, int64_t n)
+{
+    if (act < 0 || act > 5) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const double v = in[i];
+        double r = v;
+        switch (act) {
+            case 1: r = v > 0.0 ? v : 0.0; break;
+            case 2: r = 1.0 / (1.0 + exp(-v)); break;
+            case 3: r = tanh(v); break;
+            case 4: r = v / (1.0 + exp(-v)); break;
+            case 5: r = 0.5 * v * (1.0 + erf(v / sqrt(2.0))); break;
+            default: break;
+        }
+        out[i] = r;
     }
     return 0;
 }

@@ -578,6 +578,54 @@ def check_bwd_points_and_scale(orc):
         _close(sc, ref)
 
 
+# ---------------------------------------------------------------------------
+# Activation (applied after the bias)
+# ---------------------------------------------------------------------------
+
+def check_activation_closed_forms(orc):
+    """Each activation against its textbook form through numpy / scipy, over
+    values from deep negative to deep positive, and its exact special values."""
+    from scipy.special import erf, expit
+    v = np.concatenate([np.linspace(-40.0, 40.0, 4001), [-745.0, -1e-300, 0.0, 1e-300, 709.0]])
+    ref = {
+        1: np.maximum(v, 0.0),
+        2: expit(v),
+        3: np.tanh(v),
+        4: v * expit(v),
+        5: 0.5 * v * (1.0 + erf(v / np.sqrt(2.0))),
+    }
+    assert np.array_equal(orc.activation(0, v), v)
+    for a, r in ref.items():
+        got = orc.activation(a, v)
+        assert np.all(np.abs(got - r) <= 1e-13 * (np.abs(r) + 1e-300) + 1e-300), a
+    z = np.zeros(1)
+    assert orc.activation(2, z)[0] == 0.5 and orc.activation(3, z)[0] == 0.0
+    assert orc.activation(4, z)[0] == 0.0 and orc.activation(5, z)[0] == 0.0
+    try:
+        orc.activation(6, z)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("activation code 6 accepted")
+
+
+def check_activation_follows_bias(orc):
+    """The activation applies to each output after the bias is added: a
+    bias shift moves the pre-activation value, which only ReLU's flat side
+    can hide."""
+    from scipy.special import expit
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((2, 4, 5, 6))
+    w = rng.standard_normal((4, 3, 3, 3))
+    b = rng.standard_normal(3) * 3.0
+    kw = dict(stride=2, padding=1, dilation=1, output_padding=1, groups=1)
+    y0, _ = orc.forward(x, w, b, **kw)
+    y2, _ = orc.forward(x, w, b, activation=2, **kw)
+    _close(y2, expit(y0))
+    p, _ = orc.points(x, w, b, np.array([[1, 2, 3, 4], [0, 0, 0, 0]]), activation=2, **kw)
+    _close(p, expit(y0[(np.array([1, 0]), np.array([2, 0]), np.array([3, 0]), np.array([4, 0]))]))
+
+
 ALL_CHECKS = [
     check_golden_cases,
     check_output_shapes,
@@ -600,4 +648,6 @@ ALL_CHECKS = [
     check_bwd_valid_correlation,
     check_bwd_brute_force,
     check_bwd_points_and_scale,
+    check_activation_closed_forms,
+    check_activation_follows_bias,
 ]

@@ -79,6 +79,15 @@ MUTANTS = [
      "const int64_t o0 = i[0] * pb.S[0] - pb.P[0] + k0;"),
     ("bwd points: signed magnitude", "acc += t;\n                        mag += fabs(t);",
      "acc += t;\n                        mag += t;"),
+    # activation
+    ("sigmoid sign", "case 2: r = 1.0 / (1.0 + exp(-v)); break;",
+     "case 2: r = 1.0 / (1.0 + exp(v)); break;"),
+    ("GELU by its tanh approximation", "case 5: r = 0.5 * v * (1.0 + erf(v / sqrt(2.0))); break;",
+     "case 5: r = 0.5 * v * (1.0 + tanh(0.7978845608028654 * (v + 0.044715 * v * v * v))); break;"),
+    ("leaky ReLU", "case 1: r = v > 0.0 ? v : 0.0; break;", "case 1: r = v > 0.0 ? v : 0.01 * v; break;"),
+    ("SiLU with the sigmoid of -v", "case 4: r = v / (1.0 + exp(-v)); break;",
+     "case 4: r = v / (1.0 + exp(v)); break;"),
+    ("tanh dropped", "case 3: r = tanh(v); break;", "case 3: r = v; break;"),
     ("bwd: high padding shifts the gradient",
      "                            const int64_t o2 = i2 * pb.S[2] - pb.P[2] + k2 * pb.D[2];\n"
      "                            if (o2 < 0 || o2 >= pb.O[2]) continue;\n"

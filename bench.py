@@ -38,7 +38,7 @@ import workloads
 DEFAULT_WORKLOAD = "c2_1d_f32_upsampler"
 
 # MI355X published peaks (dense)
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 
 # the source files whose change invalidates stored PMC traffic figures
@@ -172,6 +172,11 @@ def main() -> int:
     ap.add_argument("--rotate-mb", type=float, default=1024.0,
                     help="total size of the rotated buffer sets (defeats the 256 MB cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", choices=["f32", "bf16", "f16"], default=None,
+                    help="element type (default: the workload's)")
+    ap.add_argument("--activation", default="none",
+                    choices=["none", "relu", "sigmoid", "tanh", "silu", "gelu"],
+                    help="activation fused after the bias (default none, as the workloads)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-data (input gradient) measurement")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -189,16 +194,21 @@ def main() -> int:
     import convt_forward_amd as C
 
     wl = workloads.get(args.workload)
+    if args.dtype is not None and args.dtype != wl.dtype:
+        import dataclasses
+        wl = dataclasses.replace(wl, dtype=args.dtype)
     tens = workloads.workload_tensors(wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pl = C.get_plan(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.dilation,
-                    wl.output_padding, wl.groups, wl.has_bias, wl.dtype)
+                    wl.output_padding, wl.groups, wl.has_bias, wl.dtype,
+                    activation=args.activation)
 
     def to_dev(a):
         if wl.dtype == "f32":
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        return t.view(torch.float16 if wl.dtype == "f16" else torch.bfloat16)
 
     x0, w0 = to_dev(tens.x_dev), to_dev(tens.w_dev)
     b0 = to_dev(tens.bias_dev) if wl.has_bias else None
@@ -287,8 +297,8 @@ def main() -> int:
         peak = PEAK_HBM_GBS
     traffic = stored_traffic(route, wl.name)
     kernel = KERNEL_SYMBOL.get(route, route)
-    if route == "phase_gemm" and wl.dtype == "bf16":
-        # the bfloat16 GEMM reads a channel-chunked copy of x that a pack
+    if route == "phase_gemm" and wl.dtype != "f32":
+        # the two-byte GEMM reads a channel-chunked copy of x that a pack
         # kernel writes inside the same forward call: kernel_us covers both
         kernel = "pack_x_kernel+" + kernel
     roofline = {
@@ -319,7 +329,8 @@ def main() -> int:
             "x_shape": list(wl.x_shape), "w_shape": list(wl.w_shape),
             "stride": list(wl.stride), "padding": list(wl.padding),
             "dilation": list(wl.dilation), "output_padding": list(wl.output_padding),
-            "groups": wl.groups, "bias": wl.has_bias, "out_shape": list(pl.out_shape),
+            "groups": wl.groups, "bias": wl.has_bias, "activation": args.activation,
+            "out_shape": list(pl.out_shape),
             "route": route, "buffer_sets": nsets,
             "algorithmic_GBps_per_step": abytes / sec_per_step / 1e9,
         },

@@ -9,7 +9,7 @@ the functions that need it raises.
     y = convt_forward_amd.conv_transpose(x, w, bias, stride=2, padding=1)
 
 x: [B, C_in, I...] and w: [C_in, C_out/groups, k...] are contiguous CUDA
-(HIP) tensors of dtype float32 or bfloat16; bias is [C_out] or None. Scalars
+(HIP) tensors of dtype float32, bfloat16 or float16; bias is [C_out] or None. Scalars
 or per-axis tuples are accepted for stride, padding, dilation and
 output_padding; padding may also give a (low, high) pair per axis, for
 different padding at the two ends of an axis.
@@ -33,6 +33,8 @@ ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
 #   ci_co_k [C_in][C_out/groups][k...], k_ci_co [k...][C_in][C_out/groups],
 #   k_co_ci [k...][C_out][C_in/groups]
 FILTER_LAYOUTS = {"ci_co_k": 0, "k_ci_co": 1, "k_co_ci": 2}
+# activation applied to y after the bias (convt_activation)
+ACTIVATIONS = {"none": 0, "relu": 1, "sigmoid": 2, "tanh": 3, "silu": 4, "gelu": 5}
 
 
 def layout_w_shape(w_shape: Sequence[int], groups: int, layout: str) -> Tuple[int, ...]:
@@ -83,6 +85,8 @@ class Problem(ctypes.Structure):
         ("padding_hi", ctypes.c_int64 * MAX_NDIM),
         ("filter_layout", ctypes.c_int32),
         ("taps_flipped", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -167,7 +171,7 @@ def _pads(v, nd: int) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
 def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, padding=0, dilation=1,
                  output_padding=0, groups: int = 1, has_bias: bool = False, dtype: str = "f32",
                  route: str = "auto", route_bwd: str = "auto", filter_layout: str = "ci_co_k",
-                 taps_flipped: bool = False) -> Problem:
+                 taps_flipped: bool = False, activation: str = "none") -> Problem:
     """w_shape is [C_in, C_out/groups, k...] whatever filter_layout says about
     W's memory order."""
     nd = len(x_shape) - 2
@@ -195,6 +199,7 @@ def make_problem(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, paddi
     p.route_bwd = ROUTES[route_bwd]
     p.filter_layout = FILTER_LAYOUTS[filter_layout]
     p.taps_flipped = 1 if taps_flipped else 0
+    p.activation = ACTIVATIONS[activation]
     return p
 
 
@@ -302,7 +307,7 @@ class Plan:
         import torch
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be a device tensor")
-        want = torch.float32 if self.problem.dtype == DTYPES["f32"] else torch.bfloat16
+        want = self.torch_dtype
         if t.dtype != want:
             raise ValueError(f"{name} must be {want}")
         if tuple(t.shape) != tuple(shape):
@@ -310,10 +315,15 @@ class Plan:
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
 
+    @property
+    def torch_dtype(self):
+        import torch
+        return {DTYPES["f32"]: torch.float32, DTYPES["bf16"]: torch.bfloat16,
+                DTYPES["f16"]: torch.float16}[int(self.problem.dtype)]
+
     def new_output(self, device):
         import torch
-        dt = torch.float32 if self.problem.dtype == DTYPES["f32"] else torch.bfloat16
-        return torch.empty(self.out_shape, dtype=dt, device=device)
+        return torch.empty(self.out_shape, dtype=self.torch_dtype, device=device)
 
     def new_workspace(self, device):
         import torch
@@ -350,8 +360,8 @@ class Plan:
 
     def new_input_grad(self, device):
         import torch
-        dt = torch.float32 if self.problem.dtype == DTYPES["f32"] else torch.bfloat16
-        return torch.empty(tuple(self.problem.x_shape[:2 + self.ndim]), dtype=dt, device=device)
+        return torch.empty(tuple(self.problem.x_shape[:2 + self.ndim]), dtype=self.torch_dtype,
+                           device=device)
 
     def new_bwd_workspace(self, device):
         import torch
@@ -386,16 +396,17 @@ _plan_cache: Dict[tuple, Plan] = {}
 
 def get_plan(x_shape, w_shape, stride=1, padding=0, dilation=1, output_padding=0, groups=1,
              has_bias=False, dtype="f32", route="auto", route_bwd="auto",
-             filter_layout="ci_co_k", taps_flipped=False) -> Plan:
+             filter_layout="ci_co_k", taps_flipped=False, activation="none") -> Plan:
     """A cached plan; w_shape is [C_in, C_out/groups, k...]."""
     nd = len(x_shape) - 2
     key = (tuple(x_shape), tuple(w_shape), _tup(stride, nd, "stride"), _pads(padding, nd),
            _tup(dilation, nd, "dilation"), _tup(output_padding, nd, "output_padding"), int(groups),
-           bool(has_bias), dtype, route, route_bwd, filter_layout, bool(taps_flipped))
+           bool(has_bias), dtype, route, route_bwd, filter_layout, bool(taps_flipped), activation)
     pl = _plan_cache.get(key)
     if pl is None:
         pl = Plan.create(x_shape, w_shape, stride, padding, dilation, output_padding, groups,
-                         has_bias, dtype, route, route_bwd, filter_layout, taps_flipped)
+                         has_bias, dtype, route, route_bwd, filter_layout, taps_flipped,
+                         activation)
         _plan_cache[key] = pl
     return pl
 
@@ -419,12 +430,14 @@ def torch_dtype_name(t) -> str:
 
 def conv_transpose(x, w, bias=None, stride=1, padding=0, dilation=1, output_padding=0, groups=1,
                    route: str = "auto", y=None, workspace=None, stream=None,
-                   filter_layout: str = "ci_co_k", taps_flipped: bool = False):
-    """ConvTranspose forward on the GPU through libconvt. Returns y. w is in
-    `filter_layout` (and spatially reversed when taps_flipped)."""
+                   filter_layout: str = "ci_co_k", taps_flipped: bool = False,
+                   activation: str = "none"):
+    """ConvTranspose forward on the GPU through libconvt, then `activation`
+    (one of ACTIVATIONS). Returns y. w is in `filter_layout` (and spatially
+    reversed when taps_flipped)."""
     pl = get_plan(tuple(x.shape), canonical_w_shape(w.shape, groups, filter_layout), stride,
                   padding, dilation, output_padding, groups, bias is not None,
-                  torch_dtype_name(x), route, "auto", filter_layout, taps_flipped)
+                  torch_dtype_name(x), route, "auto", filter_layout, taps_flipped, activation)
     return pl.forward(x, w, bias, y=y, workspace=workspace, stream=stream)
 
 

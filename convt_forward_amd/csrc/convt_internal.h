@@ -58,6 +58,8 @@ struct DevParams {
     int32_t has_bias;
     int32_t w_layout;          // convt_filter_layout of W
     int32_t w_flip;            // 1: W's taps are stored spatially reversed
+    int32_t act;               // convt_activation of the forward output
+    int32_t f16;               // two-byte elements are IEEE half (else bfloat16)
     // Tiling of the main kernel (meaning depends on the route).
     int32_t td, th, tw;        // q-tile extents
     int32_t hd, hh, hw;        // halo box extents (largest over phases)

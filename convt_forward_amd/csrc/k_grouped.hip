@@ -1,4 +1,5 @@
-// Grouped / few-channel stride-phase kernel (bfloat16, MFMA 16x16x32).
+// Grouped / few-channel stride-phase kernel (bfloat16 or half, MFMA
+// 16x16x32).
 //
 // For grouped problems with few channels per group (C_in/groups a multiple
 // of 8 up to 64, C_out/groups up to 16) the phase GEMM's tiles would be
@@ -24,11 +25,12 @@
 //  2. per (depth, height) residue pair, a wave keeps the weight fragments of
 //     every width residue in registers and takes chunks of 16-position
 //     segments of the block's q rows in turn: per segment and width residue
-//     up to four v_mfma_f32_16x16x32_bf16 (rows = 16 positions, columns =
+//     up to four 16x16x32 MFMAs (rows = 16 positions, columns =
 //     the group's output channels padded to 16, K = (tap, slice) slots, four
 //     per MFMA), with the bias as the accumulator's initial value. A lane
 //     then holds, for one channel, 4*S2 consecutive outputs of one row;
-//  3. the outputs are rounded to bfloat16 in pairs and leave as 16-byte
+//  3. the outputs (after the activation, if any) are rounded to the element
+//     type in pairs and leave as 16-byte
 //     stores in which 8 consecutive lanes cover 128 contiguous bytes: with
 //     width stride 2 and at most 8 channels, a segment pair's second half
 //     moves into the padding lanes (DPP) and a lane permutation orders the
@@ -57,13 +59,20 @@ template <int V> struct IntTag {
     static constexpr int value = V;
 };
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// two float32 -> two bfloat16 (RNE) in one word, first value in the low half
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
+// One 16x16x32 MFMA step on two-byte elements of type E (bfloat16 or half).
+template <typename E> struct GrpElem;
+template <> struct GrpElem<__bf16> {
+    typedef bf16x8 v8;
+    static __device__ __forceinline__ f32x4 mfma(const u32x4 &a, const v8 &b, const f32x4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), b, c, 0, 0, 0);
+    }
+};
+template <> struct GrpElem<_Float16> {
+    typedef f16x8 v8;
+    static __device__ __forceinline__ f32x4 mfma(const u32x4 &a, const v8 &b, const f32x4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), b, c, 0, 0, 0);
+    }
+};
 
 // a lane's run of 4*S2 outputs (2*S2 words) into the staging row
 template <int S2>
@@ -91,13 +100,14 @@ struct GrpArgs {
     int32_t grp_hwp, grp_hshift, grp_nk, grp_nsc;
     int32_t grp_w_off, grp_tab_off, grp_st_off, grp_st_pitch;
     int32_t ktot, nphase;
+    int32_t act;  // convt_activation of the outputs
 };
 
 // Eight waves per SIMD (8 blocks per CU) where the registers allow it: the
 // scalar registers are capped too, since more of them than the cap admits
 // keep blocks from being resident. Instances with more weight fragments in
 // registers (S2 * KS > 2) trade occupancy for having no spills.
-template <int S2, int KS>
+template <int S2, int KS, typename E, bool ACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 2 ? 8 : 4, 8))) void grouped_kernel(
     GrpArgs p, const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const int2 *__restrict__ gtab, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
@@ -270,7 +280,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     // chunks are segment pairs that leave through DPP (no staging)
     const bool pair_dpp = p.grp_nsc == 0;
     const int nsc = pair_dpp ? 2 : p.grp_nsc, nchunk = (nseg + nsc - 1) / nsc;
-    const float bvf = (p.has_bias && l16 < Cog) ? bf16_to_f32(bias[g * Cog + l16]) : 0.0f;
+    const float bvf = (p.has_bias && l16 < Cog) ? half_to_f32<E>(bias[g * Cog + l16]) : 0.0f;
+    // the outputs' activation, then one rounding to E, two per word
+    const int act = p.act;
+    auto pack2 = [act](float a, float b) __attribute__((always_inline)) {
+        if constexpr (ACT) {
+            a = activate(act, a);
+            b = activate(act, b);
+        }
+        return pack_half2<E>(a, b);
+    };
     const f32x4 binit = {bvf, bvf, bvf, bvf};
     // output planes of the group; a lane's channel plane, or out of range
     // (dropped) for the padding channels
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
             // phases (r0, r1, r2 < S2): their records and this lane's K slots
             int qn0 = 0, qn1 = 0, qn2min = 1 << 30, qn2[MS];
             uint32_t rd[MS][KS];  // LDS byte offset of the lane's A cell, segment origin excluded
-            bf16x8 bw[MS][KS];
+            typename GrpElem<E>::v8 bw[MS][KS];
             bool sl_ok[MS][KS];
             bool regular = true;  // every phase fills all KS steps with real slots (uniform)
 #pragma unroll
@@ -353,7 +372,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
                         wv = *(const u32x4 *)&wsl[e.y + l16 * Cig];
                     }
                     rd[r2][kb] = (uint32_t)e.x + (uint32_t)l16 * 16;
-                    bw[r2][kb] = __builtin_bit_cast(bf16x8, wv);
+                    bw[r2][kb] = __builtin_bit_cast(typename GrpElem<E>::v8, wv);
                 }
             }
             const int rows = min(rhi, qn1 - q0h) - rlo;  // q rows of the range with outputs here
@@ -390,8 +409,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
                                 if constexpr (PAD) {
                                     if (!sl_ok[r2][kb]) av = u32x4{0u, 0u, 0u, 0u};
                                 }
-                                acc[r2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8, av), bw[r2][kb], acc[r2], 0, 0, 0);
+                                acc[r2] = GrpElem<E>::mfma(av, bw[r2][kb], acc[r2]);
                             }
                         }
                         // the run's 4*S2 outputs as 2*S2 words (word e2:
@@ -400,7 +418,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
 #pragma unroll
                         for (int e2 = 0; e2 < 2 * MS; ++e2) {
                             const int ea = 2 * e2, eb = 2 * e2 + 1;
-                            pk[e2] = pack_bf16x2(acc[ea % S2][ea / S2], acc[eb % S2][eb / S2]);
+                            pk[e2] = pack2(acc[ea % S2][ea / S2], acc[eb % S2][eb / S2]);
                         }
                         if (staged) {  // uniform
                             stage_run(pk, stg + st_w + (uint32_t)s * seg_y);
@@ -484,15 +502,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
 #pragma unroll
                             for (int kb = 0; kb < KS; ++kb) {
                                 const u32x4 av = *(const u32x4 *)(lds + rd[r2][kb] + ub + s * 256);
-                                acc[r2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8, av), bw[r2][kb], acc[r2], 0, 0, 0);
+                                acc[r2] = GrpElem<E>::mfma(av, bw[r2][kb], acc[r2]);
                             }
                         }
                         uint32_t pk[2 * MS];
 #pragma unroll
                         for (int e2 = 0; e2 < 2 * MS; ++e2) {
                             const int ea = 2 * e2, eb = 2 * e2 + 1;
-                            pk[e2] = pack_bf16x2(acc[ea % S2][ea / S2], acc[eb % S2][eb / S2]);
+                            pk[e2] = pack2(acc[ea % S2][ea / S2], acc[eb % S2][eb / S2]);
                         }
                         stage_run(pk, sw + s * 32 * S2);
                     }
@@ -536,13 +553,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
 #pragma unroll
                                 for (int kb = 0; kb < KS; ++kb) {
                                     const u32x4 av = *(const u32x4 *)(lds + rd[r2][kb] + ub + s * 256);
-                                    acc[r2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        __builtin_bit_cast(bf16x8, av), bw[r2][kb], acc[r2], 0, 0, 0);
+                                    acc[r2] = GrpElem<E>::mfma(av, bw[r2][kb], acc[r2]);
                                 }
                             }
 #pragma unroll
                             for (int e2 = 0; e2 < 4; ++e2)
-                                pr[s][e2] = pack_bf16x2(acc[(2 * e2) % 2][(2 * e2) / 2],
+                                pr[s][e2] = pack2(acc[(2 * e2) % 2][(2 * e2) / 2],
                                                         acc[(2 * e2 + 1) % 2][(2 * e2 + 1) / 2]);
                         }
                         // row_ror:8 (lane i of a row takes lane i - 8), written
@@ -594,15 +610,33 @@ static GrpArgs grp_args(const DevParams &p) {
     a.grp_w_off = p.grp_w_off; a.grp_tab_off = p.grp_tab_off; a.grp_st_off = p.grp_st_off;
     a.grp_st_pitch = p.grp_st_pitch;
     a.ktot = p.ktot; a.nphase = p.nphase;
+    a.act = p.act;
     return a;
 }
 
 template <int S2, int KS>
 static void launch_grouped_t(const DevParams &p, const void *x, const void *wr, const int2 *gtab,
                              const void *bias, void *y, int st_align, int x_vec, hipStream_t stream) {
-    hipLaunchKernelGGL((grouped_kernel<S2, KS>), dim3(p.G * p.B, p.nt_h, p.nt_d), dim3(256),
-                       (size_t)p.grp_lds_bytes, stream, grp_args(p), (const uint16_t *)x,
-                       (const uint16_t *)wr, gtab, (const uint16_t *)bias, (uint16_t *)y, st_align, x_vec);
+    const dim3 grid(p.G * p.B, p.nt_h, p.nt_d);
+    const size_t lds = (size_t)p.grp_lds_bytes;
+    const GrpArgs a = grp_args(p);
+    const uint16_t *xs = (const uint16_t *)x, *ws = (const uint16_t *)wr,
+                   *bs = (const uint16_t *)bias;
+    uint16_t *ys = (uint16_t *)y;
+    // instances with an activation are separate (no activation code otherwise)
+    const bool act = p.act != CONVT_ACT_NONE;
+    if (p.f16 && act)
+        hipLaunchKernelGGL((grouped_kernel<S2, KS, _Float16, true>), grid, dim3(256), lds, stream,
+                           a, xs, ws, gtab, bs, ys, st_align, x_vec);
+    else if (p.f16)
+        hipLaunchKernelGGL((grouped_kernel<S2, KS, _Float16, false>), grid, dim3(256), lds, stream,
+                           a, xs, ws, gtab, bs, ys, st_align, x_vec);
+    else if (act)
+        hipLaunchKernelGGL((grouped_kernel<S2, KS, __bf16, true>), grid, dim3(256), lds, stream,
+                           a, xs, ws, gtab, bs, ys, st_align, x_vec);
+    else
+        hipLaunchKernelGGL((grouped_kernel<S2, KS, __bf16, false>), grid, dim3(256), lds, stream,
+                           a, xs, ws, gtab, bs, ys, st_align, x_vec);
 }
 
 template <int S2>

@@ -463,7 +463,9 @@ __global__ __launch_bounds__(256) void fill_kernel(DevParams p, const T *__restr
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * 256) {
         const int oc = (int)((i / p.y_plane) % p.Co);
-        y[i] = p.has_bias ? bias[oc] : from_f32<T>(0.0f);
+        float v = p.has_bias ? to_f32(bias[oc]) : 0.0f;
+        if (p.act != CONVT_ACT_NONE) v = activate(p.act, v);
+        y[i] = from_f32<T>(v);
     }
 }
 
@@ -480,7 +482,10 @@ hipError_t launch_fill_dp(const DevParams &p, int elem_bytes, const void *bias, 
                           hipStream_t stream) {
     const int64_t total = (int64_t)p.B * p.Co * p.y_plane;
     if (total <= 0) return hipSuccess;
-    if (elem_bytes == 2)
+    if (elem_bytes == 2 && p.f16)
+        hipLaunchKernelGGL(fill_kernel<_Float16>, dim3(grid_for(total)), dim3(256), 0, stream, p,
+                           (const _Float16 *)bias, (_Float16 *)y, total);
+    else if (elem_bytes == 2)
         hipLaunchKernelGGL(fill_kernel<uint16_t>, dim3(grid_for(total)), dim3(256), 0, stream, p,
                            (const uint16_t *)bias, (uint16_t *)y, total);
     else
@@ -535,6 +540,7 @@ __global__ __launch_bounds__(256) void naive_kernel(DevParams p, const T *__rest
             }
         }
         if (p.has_bias) acc += to_f32(bias[oc]);
+        if (p.act != CONVT_ACT_NONE) acc = activate(p.act, acc);
         y[idx] = from_f32<T>(acc);
     }
 }
@@ -544,7 +550,11 @@ hipError_t launch_naive(const Plan &pl, const void *x, const void *w, const void
     const DevParams &p = pl.dp;
     const int64_t total = (int64_t)p.B * p.Co * p.y_plane;
     if (total <= 0) return hipSuccess;
-    if (pl.elem_bytes == 2)
+    if (pl.elem_bytes == 2 && p.f16)
+        hipLaunchKernelGGL(naive_kernel<_Float16>, dim3(grid_for(total)), dim3(256), 0, stream, p,
+                           (const _Float16 *)x, (const _Float16 *)w, (const _Float16 *)bias,
+                           (_Float16 *)y, total);
+    else if (pl.elem_bytes == 2)
         hipLaunchKernelGGL(naive_kernel<uint16_t>, dim3(grid_for(total)), dim3(256), 0, stream, p,
                            (const uint16_t *)x, (const uint16_t *)w, (const uint16_t *)bias,
                            (uint16_t *)y, total);
@@ -566,7 +576,7 @@ hipError_t launch_naive(const Plan &pl, const void *x, const void *w, const void
 // ---------------------------------------------------------------------------
 constexpr int kDirPos = 256;
 
-template <typename T>
+template <typename T, bool ACT>
 __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__restrict__ x,
                                                       const T *__restrict__ w,
                                                       const T *__restrict__ bias,
@@ -636,10 +646,23 @@ __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__res
             if (co < p.Cog) {
                 float v = acc[c];
                 if (p.has_bias) v += to_f32(bias[g * p.Cog + co]);
+                if constexpr (ACT) v = activate(p.act, v);
                 yb[(int64_t)co * p.y_plane] = from_f32<T>(v);
             }
         }
     }
+}
+
+// instances with an activation are separate (none of its code otherwise)
+template <typename T>
+static void launch_direct_t(const DevParams &p, int64_t blocks, size_t lds, const void *x,
+                            const void *w, const void *bias, void *y, hipStream_t stream) {
+    if (p.act != CONVT_ACT_NONE)
+        hipLaunchKernelGGL((direct_kernel<T, true>), dim3((unsigned)blocks), dim3(256), lds, stream,
+                           p, (const T *)x, (const T *)w, (const T *)bias, (T *)y);
+    else
+        hipLaunchKernelGGL((direct_kernel<T, false>), dim3((unsigned)blocks), dim3(256), lds,
+                           stream, p, (const T *)x, (const T *)w, (const T *)bias, (T *)y);
 }
 
 hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
@@ -650,13 +673,12 @@ hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const voi
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)p.Cig * p.Cog * p.ktot * sizeof(float);
-    if (pl.elem_bytes == 2)
-        hipLaunchKernelGGL(direct_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds, stream,
-                           p, (const uint16_t *)x, (const uint16_t *)w, (const uint16_t *)bias,
-                           (uint16_t *)y);
+    if (pl.elem_bytes == 2 && p.f16)
+        launch_direct_t<_Float16>(p, blocks, lds, x, w, bias, y, stream);
+    else if (pl.elem_bytes == 2)
+        launch_direct_t<uint16_t>(p, blocks, lds, x, w, bias, y, stream);
     else
-        hipLaunchKernelGGL(direct_kernel<float>, dim3((unsigned)blocks), dim3(256), lds, stream, p,
-                           (const float *)x, (const float *)w, (const float *)bias, (float *)y);
+        launch_direct_t<float>(p, blocks, lds, x, w, bias, y, stream);
     return hipGetLastError();
 }
 
@@ -711,7 +733,10 @@ hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void 
     const DevParams &p = pl.dp;  // the forward problem's axes and channels
     const int64_t total = (int64_t)p.B * p.Ci * p.x_plane;
     if (total <= 0) return hipSuccess;
-    if (pl.elem_bytes == 2)
+    if (pl.elem_bytes == 2 && p.f16)
+        hipLaunchKernelGGL(naive_bwd_kernel<_Float16>, dim3(grid_for(total)), dim3(256), 0, stream,
+                           p, (const _Float16 *)dy, (const _Float16 *)w, (_Float16 *)dx, total);
+    else if (pl.elem_bytes == 2)
         hipLaunchKernelGGL(naive_bwd_kernel<uint16_t>, dim3(grid_for(total)), dim3(256), 0, stream,
                            p, (const uint16_t *)dy, (const uint16_t *)w, (uint16_t *)dx, total);
     else

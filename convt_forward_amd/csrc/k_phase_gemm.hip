@@ -48,9 +48,9 @@
 // offset of 2^31, always out of range. Every per-lane offset is a 32-bit
 // byte offset.
 //
-// MFMA: bfloat16 inputs use v_mfma_f32_32x32x16_bf16 (each lane supplies 8
-// consecutive channels of one row of each operand; the input operand is
-// assembled from 8 two-byte LDS reads), float32 inputs use
+// MFMA: two-byte inputs use v_mfma_f32_32x32x16_bf16 or _f16 (each lane
+// supplies 8 consecutive channels of one row of each operand, one 16-byte
+// LDS read each), float32 inputs use
 // v_mfma_f32_32x32x2_f32 (each lane reads 4 consecutive channels of its
 // weight row and feeds them to 4 MFMAs, with the input of the same channel;
 // A and B pair the same channel in every lane, so the sum is the full
@@ -58,10 +58,19 @@
 // gathered inputs (columns = positions). Within a stage, the operands of tap
 // u+1 are read from LDS while the MFMAs of tap u run.
 //
-// Epilogue: acc + bias[co] in float32, one rounding to the output type
-// (v_cvt_pk_bf16_f32 rounds to nearest even), stored to
+// Epilogue: acc + bias[co] in float32, the activation if the plan has one,
+// one rounding to the output type (nearest even), stored to
 // y[b][g*Cog+co][s*q + r]; outputs beyond the phase's q range or past Cog
 // fall outside the store resource and are dropped.
+//
+// Backward data (BWD): dx[i] gathers dy[s*i - p + kk*d] * W[kk]; the taps of
+// forward output residue r read the dy phase plane dy_r[j] = dy[s*j + r] at
+// j = i - off(kk), so dx is the sum over phases of stride-1 correlations.
+// The same kernel runs it with the roles swapped (rows = input channels, K =
+// output channels x taps, columns = dx positions): a block owns a box of dx
+// positions and runs every phase's taps in one K loop, in units of (channel
+// chunk, phase) whose halo is the box in that phase plane (gathered at
+// stride s from dy, or from its channel-chunked copy), stored densely.
 #include <type_traits>
 
 #include "kcommon.h"
@@ -69,7 +78,7 @@
 
 namespace convt {
 
-template <typename T, int CFG, int GS, bool BWD>
+template <typename T, int CFG, int GS, bool BWD, bool ACT>
 __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
                                                          const T *__restrict__ wr,
                                                          const int32_t *__restrict__ tab,
@@ -317,7 +326,9 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         // groups shift by 0)
         const int32_t *ptab = tab + (BWD ? 0 : ph.tapbase);
 
-        using Frag = typename std::conditional<ES == 2, bf16x8, f32x4>::type;
+        using Frag = typename std::conditional<
+            ES == 2, typename std::conditional<std::is_same<T, _Float16>::value, f16x8, bf16x8>::type,
+            f32x4>::type;
         // operands of one tap: weight slot wsl, halo rows shifted by drow
         auto read_frags = [&](Frag (&fa)[MT], Frag (&fb)[NT], const unsigned char *wsl,
                               const unsigned char *xsl, int drow) __attribute__((always_inline)) {
@@ -340,7 +351,14 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
             }
         };
         auto mfma = [&](const Frag (&fa)[MT], const Frag (&fb)[NT]) __attribute__((always_inline)) {
-            if constexpr (ES == 2) {
+            if constexpr (std::is_same<T, _Float16>::value) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[mt], fb[nt],
+                                                                             acc[mt][nt], 0, 0, 0);
+            } else if constexpr (ES == 2) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -508,6 +526,9 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         }
     }
     const int co_w = co_t * BM + wm * WM;  // first output channel of this wave
+    const int act = p.act;  // the activation after the bias (ACT instances only)
+    // arithmetic type of two-byte elements
+    using HT = typename std::conditional<std::is_same<T, _Float16>::value, _Float16, __bf16>::type;
     const uint32_t ypl_bytes = (uint32_t)p.y_plane * ES;
     // the group's output planes from this wave's first channel to Cog
     const int co_left = p.Cog - co_w;
@@ -526,17 +547,17 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
                 const uint32_t co_u = mt * 32 + 8 * (j >> 2) + (j & 3);
                 float bv;
                 if constexpr (ES == 2)
-                    bv = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(bs, (co_u + lane_co) * 2, 0, 0));
+                    bv = half_to_f32<HT>(__builtin_amdgcn_raw_buffer_load_b16(bs, (co_u + lane_co) * 2, 0, 0));
                 else
                     bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (co_u + lane_co) * 4, 0, 0));
                 const uint32_t cbytes = (co_u + lane_co) * ypl_bytes;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const float v = acc[mt][nt][j] + bv;
+                    float v = acc[mt][nt][j] + bv;
+                    if constexpr (ACT) v = activate(act, v);
                     const uint32_t off = yoff[nt] + cbytes;
                     if constexpr (ES == 2)
-                        __builtin_amdgcn_raw_buffer_store_b16(
-                            __builtin_bit_cast(uint16_t, (__bf16)v), ys, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_half<HT>(v), ys, off, 0, 0);
                     else
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ys, off, 0, 0);
                 }
@@ -545,14 +566,25 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
     }
 }
 
+// Instances with an activation (ACT) are separate, so that kernels without
+// one carry none of its code in their unrolled epilogue.
 template <typename T, int CFG, int GS, bool BWD>
 static void launch_cfg(const DevParams &p, int64_t tab_offset, const void *x, const void *ws,
                        const void *bias, void *y, hipStream_t stream) {
-    if constexpr (tiles::gemm_cfg_valid(tiles::kGemmCfg[CFG], GS))
-        hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS, BWD>), dim3(p.n_blocks),
-                           dim3(tiles::kGemmCfg[CFG].nw * 64), 0, stream, p, (const T *)x,
-                           (const T *)ws, (const int32_t *)((const char *)ws + tab_offset),
-                           (const T *)bias, (T *)y);
+    if constexpr (tiles::gemm_cfg_valid(tiles::kGemmCfg[CFG], GS)) {
+        const int32_t *tab = (const int32_t *)((const char *)ws + tab_offset);
+        const dim3 grid(p.n_blocks), block(tiles::kGemmCfg[CFG].nw * 64);
+        if constexpr (!BWD) {
+            if (p.act != CONVT_ACT_NONE) {
+                hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS, false, true>), grid, block, 0,
+                                   stream, p, (const T *)x, (const T *)ws, tab, (const T *)bias,
+                                   (T *)y);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((phase_gemm_kernel<T, CFG, GS, BWD, false>), grid, block, 0, stream, p,
+                           (const T *)x, (const T *)ws, tab, (const T *)bias, (T *)y);
+    }
 }
 
 template <typename T, int CFG, bool BWD>
@@ -577,13 +609,17 @@ static hipError_t launch_any(const DevParams &p, int64_t tab_offset, const void 
     if (p.n_blocks <= 0) return hipSuccess;
     if (!p.wr_chunked) return hipErrorInvalidValue;
     switch (p.gemm_cfg) {
-        case 0: return launch_gs<uint16_t, 0, BWD>(p, tab_offset, x, wr, bias, y, stream);
-        case 1: return launch_gs<uint16_t, 1, BWD>(p, tab_offset, x, wr, bias, y, stream);
-        case 2: return launch_gs<uint16_t, 2, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 0: return p.f16 ? launch_gs<_Float16, 0, BWD>(p, tab_offset, x, wr, bias, y, stream)
+                             : launch_gs<uint16_t, 0, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 1: return p.f16 ? launch_gs<_Float16, 1, BWD>(p, tab_offset, x, wr, bias, y, stream)
+                             : launch_gs<uint16_t, 1, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 2: return p.f16 ? launch_gs<_Float16, 2, BWD>(p, tab_offset, x, wr, bias, y, stream)
+                             : launch_gs<uint16_t, 2, BWD>(p, tab_offset, x, wr, bias, y, stream);
         case 3: return launch_gs<float, 3, BWD>(p, tab_offset, x, wr, bias, y, stream);
         case 4: return launch_gs<float, 4, BWD>(p, tab_offset, x, wr, bias, y, stream);
         case 5: return launch_gs<float, 5, BWD>(p, tab_offset, x, wr, bias, y, stream);
-        case 6: return launch_gs<uint16_t, 6, BWD>(p, tab_offset, x, wr, bias, y, stream);
+        case 6: return p.f16 ? launch_gs<_Float16, 6, BWD>(p, tab_offset, x, wr, bias, y, stream)
+                             : launch_gs<uint16_t, 6, BWD>(p, tab_offset, x, wr, bias, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

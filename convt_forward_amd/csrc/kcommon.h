@@ -14,6 +14,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // bfloat16 values travel as their 16-bit patterns.
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
@@ -32,9 +34,48 @@ template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
 
+template <> __device__ __forceinline__ float to_f32<_Float16>(_Float16 v) { return (float)v; }
+
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
+// float32 -> IEEE half, round to nearest even
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return (_Float16)v; }
+
+// Two-byte element types travel as 16-bit patterns; E (__bf16 or _Float16)
+// is the arithmetic type they hold. Conversions round to nearest even.
+template <typename E> __device__ __forceinline__ float half_to_f32(uint16_t v) {
+    return (float)__builtin_bit_cast(E, v);
+}
+template <typename E> __device__ __forceinline__ uint16_t f32_to_half(float v) {
+    return __builtin_bit_cast(uint16_t, (E)v);
+}
+// two float32 -> two E (RNE) in one word, the first value in the low half
+template <typename E> __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+    typedef E e2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, e2));
+}
+
+// 1 / (1 + e^-v) from e^-v = 2^(-v * log2 e) on the hardware exp2 and
+// reciprocal instructions (each within about 1 ulp); the relative error of
+// the result grows like |v| * 2^-24 through the product, below the
+// pre-activation error the outputs already carry for any |v| it matters at.
+__device__ __forceinline__ float logistic(float v) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
+}
+
+// The activation applied to an output after its bias (convt_activation),
+// in float32.
+__device__ __forceinline__ float activate(int act, float v) {
+    switch (act) {
+        case CONVT_ACT_RELU: return v > 0.0f ? v : 0.0f;
+        case CONVT_ACT_SIGMOID: return logistic(v);
+        case CONVT_ACT_TANH: return tanhf(v);
+        case CONVT_ACT_SILU: return v * logistic(v);
+        case CONVT_ACT_GELU: return 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
+        default: return v;
+    }
+}
 
 // The 8 XCDs take hardware block ids round-robin. With the remap, XCD k runs
 // logical blocks [k*n/8, (k+1)*n/8), so blocks that share input tiles or

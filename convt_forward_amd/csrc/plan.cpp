@@ -261,7 +261,7 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd) {
 }
 
 int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs, double *t_out) {
-    const bool bf16 = dtype == CONVT_DTYPE_BF16;
+    const bool bf16 = dtype == CONVT_DTYPE_BF16 || dtype == CONVT_DTYPE_F16;  // two-byte configs
     int best = -1;
     double best_t = 0;
     DevParams best_dp{};
@@ -299,7 +299,8 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs, double *
 bool gemm_eligible(const DevParams &dp, int dtype, int ndim, bool bwd = false) {
     if (!strides_fit(dp) || dp.ktot > 4096) return false;
     if (!slices_fit(dp, dtype == CONVT_DTYPE_F32 ? 4 : 2)) return false;
-    if (dtype != CONVT_DTYPE_F32 && dtype != CONVT_DTYPE_BF16) return false;
+    if (dtype != CONVT_DTYPE_F32 && dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16)
+        return false;
     DevParams tmp = dp;
     return pick_gemm_cfg(&tmp, dtype, ndim, bwd) >= 0;
 }
@@ -389,7 +390,7 @@ bool choose_grouped_tile(DevParams *dp) {
 }
 
 bool grouped_eligible(const DevParams &dp, int dtype) {
-    if (dtype != CONVT_DTYPE_BF16 || dp.ktot > 4096) return false;
+    if ((dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16) || dp.ktot > 4096) return false;
     if (!slices_fit(dp, 2)) return false;
     if (!strides_fit(dp)) return false;
     if (dp.Cig % 8 != 0 || dp.Cig > 64 || dp.Cog > tiles::kGrpCog) return false;
@@ -450,6 +451,8 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
     b.has_bias = 0;
     b.w_layout = fp.w_layout;
     b.w_flip = fp.w_flip;
+    b.act = CONVT_ACT_NONE;
+    b.f16 = fp.f16;
     const int dt = p->dtype;
     const int nd = pl->ndim;
     const bool empty_out = b.B == 0 || b.Co == 0 || b.y_plane == 0;
@@ -513,7 +516,7 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
     ws = wr * pl->elem_bytes;
     pl->bwd_tab_offset = (ws + 255) / 256 * 256;
     ws = pl->bwd_tab_offset + (int64_t)b.ktot_pad * 4;
-    if (dt == CONVT_DTYPE_BF16) {
+    if (dt != CONVT_DTYPE_F32) {
         // the channel-chunked copy of dy: [B][G][chunk][position][32 bytes]
         int64_t xp;
         if (!mul_ok((int64_t)b.B * b.G, (int64_t)b.cig_pad / 16, lim, &tmp) ||
@@ -539,6 +542,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     if (p->has_padding_hi != 0 && p->has_padding_hi != 1) return CONVT_ERR_INVALID_ARGUMENT;
     if (p->filter_layout < CONVT_FILTER_CI_CO_K || p->filter_layout > CONVT_FILTER_K_CO_CI ||
         (p->taps_flipped != 0 && p->taps_flipped != 1))
+        return CONVT_ERR_INVALID_ARGUMENT;
+    if (p->activation < CONVT_ACT_NONE || p->activation > CONVT_ACT_GELU || p->reserved1 != 0)
         return CONVT_ERR_INVALID_ARGUMENT;
     if (p->route_bwd < CONVT_ROUTE_AUTO || p->route_bwd > CONVT_ROUTE_NAIVE)
         return CONVT_ERR_INVALID_ARGUMENT;
@@ -579,7 +584,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     }
     if (p->dtype < CONVT_DTYPE_F32 || p->dtype > CONVT_DTYPE_I64)
         return CONVT_ERR_INVALID_ARGUMENT;
-    if (p->dtype != CONVT_DTYPE_F32 && p->dtype != CONVT_DTYPE_BF16) return CONVT_ERR_UNSUPPORTED;
+    if (p->dtype != CONVT_DTYPE_F32 && p->dtype != CONVT_DTYPE_BF16 && p->dtype != CONVT_DTYPE_F16)
+        return CONVT_ERR_UNSUPPORTED;
 
     // element counts
     int64_t xpl = I[0], ypl = O[0], ktot = K[0], nph = S[0], t;
@@ -628,6 +634,8 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     dp.has_bias = p->has_bias;
     dp.w_layout = p->filter_layout;
     dp.w_flip = p->taps_flipped;
+    dp.act = p->activation;
+    dp.f16 = p->dtype == CONVT_DTYPE_F16;
 
     // ---- route ------------------------------------------------------------
     const bool empty_out = (B == 0 || Co == 0);
@@ -725,7 +733,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
             pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
             info.workspace_bytes = pl->tab_offset + 16 * (int64_t)dp.nphase + (int64_t)ktot * (Cig / 8) * 8;
         }
-        if (route == CONVT_ROUTE_PHASE_GEMM && dt == CONVT_DTYPE_BF16) {
+        if (route == CONVT_ROUTE_PHASE_GEMM && dt != CONVT_DTYPE_F32) {
             // the channel-chunked copy of x: [B][G][chunk][position][32 bytes]
             int64_t xp;
             if (!mul_ok(B * G, (int64_t)dp.cig_pad / 16, lim, &t) || !mul_ok(t, xpl * 32, lim, &xp))

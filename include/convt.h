@@ -26,7 +26,7 @@
  *                                       page states
  *   bias [C_out]                        device memory, optional
  *   y    [B, C_out, O_1..O_n]           device memory, written by the library
- * x, W, bias and y share one element type (float32 or bfloat16; the output
+ * x, W, bias and y share one element type (float32, bfloat16 or float16; the output
  * type follows the inputs as on the huggingface page, "Use with"). Products
  * are accumulated in float32 and the result is rounded once to the output
  * type, after the bias is added.
@@ -74,9 +74,10 @@ typedef enum convt_status {
 typedef enum convt_dtype {
     CONVT_DTYPE_F32 = 0,
     CONVT_DTYPE_BF16 = 1,
+    /* IEEE half (the huggingface page's shader-f16 variants) */
+    CONVT_DTYPE_F16 = 2,
     /* the codes below name element types that are refused with
      * CONVT_ERR_UNSUPPORTED */
-    CONVT_DTYPE_F16 = 2,
     CONVT_DTYPE_I8 = 3,
     CONVT_DTYPE_I32 = 4,
     CONVT_DTYPE_I64 = 5
@@ -114,6 +115,21 @@ typedef enum convt_filter_layout {
     CONVT_FILTER_K_CO_CI = 2
 } convt_filter_layout;
 
+/* Activation applied to each output after the bias, in float32 before the
+ * single rounding to the output type (the AWS Neuron conv3d_transpose
+ * page's activation_fn, which names no functions; this set is the reading
+ * adopted): ReLU max(v, 0); logistic sigmoid 1/(1 + e^-v); tanh;
+ * SiLU v/(1 + e^-v); GELU v/2 (1 + erf(v/sqrt 2)). convt_backward_data
+ * ignores it (it is the gradient of the convolution alone). */
+typedef enum convt_activation {
+    CONVT_ACT_NONE = 0,
+    CONVT_ACT_RELU = 1,
+    CONVT_ACT_SIGMOID = 2,
+    CONVT_ACT_TANH = 3,
+    CONVT_ACT_SILU = 4,
+    CONVT_ACT_GELU = 5
+} convt_activation;
+
 /* The problem, in the terms the pages use. Only the first 2 + ndim entries
  * of the shape arrays and the first ndim entries of the attribute arrays are
  * read. padding is the low (leading) padding of each axis; the high
@@ -137,6 +153,8 @@ typedef struct convt_problem {
     int64_t padding_hi[CONVT_MAX_NDIM];         /* >= 0; read only when has_padding_hi = 1 */
     int32_t filter_layout;                      /* convt_filter_layout of W */
     int32_t taps_flipped;                       /* 1: W's taps are spatially reversed */
+    int32_t activation;                         /* convt_activation applied to y */
+    int32_t reserved1;                          /* must be 0 */
 } convt_problem;
 
 typedef struct convt_plan_info {
@@ -161,7 +179,7 @@ typedef struct convt_plan_s *convt_plan_t;
  *   ndim in 1..3; all sizes >= 0; kernel sizes >= 1; stride >= 1;
  *   padding >= 0 (both ends); has_padding_hi in {0, 1}; route and route_bwd
  *   valid convt_route codes; filter_layout a convt_filter_layout;
- *   taps_flipped in {0, 1};
+ *   taps_flipped in {0, 1}; activation a convt_activation; reserved1 == 0;
  *   dilation >= 1; 0 <= output_padding < max(stride, dilation);
  *   groups >= 1 dividing C_in; w_shape[0] == C_in; every output size >= 1;
  *   has_bias in {0, 1}; element counts of x, W and y below 2^62 and each
@@ -203,7 +221,7 @@ convt_status convt_prepare_weights(convt_plan_t plan, const void *w, void *works
  * convt_prepare_weights (for the same plan and the same W), W itself (used
  * by the routes that read it directly; may be NULL for the others) and bias.
  * The prepared weights at the start of the workspace are left unchanged; the
- * rest of it is scratch that the call overwrites (the bfloat16 phase-GEMM
+ * rest of it is scratch that the call overwrites (the two-byte phase-GEMM
  * route stages a channel-chunked copy of x there). Arguments as in
  * convt_forward.
  */

@@ -19,7 +19,14 @@ import convt_forward_amd as C
 import oracle
 import workloads
 
-TOL = {"f32": 1e-5, "bf16": 1e-2}
+# float16: one rounding of the output (2^-11 of its magnitude, which the
+# denominator bounds) plus float32 accumulation: 1e-3
+TOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 1e-3}
+# Lipschitz constant of each activation (convt_activation code): with an
+# activation f the denominator becomes L_f * (scale + |bias|) + |f(y_ref)|,
+# the bound on the pre-activation error carried through f plus the rounding
+# of f's value
+ACT_LIPSCHITZ = {0: 1.0, 1: 1.0, 2: 0.25, 3: 1.0, 4: 1.1, 5: 1.13}
 
 
 def say(*a):
@@ -32,7 +39,7 @@ def to_device(arr: np.ndarray, dtype: str):
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
     a = np.ascontiguousarray(arr, dtype=np.uint16).view(np.int16)
-    return torch.from_numpy(a).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda().view(torch.float16 if dtype == "f16" else torch.bfloat16)
 
 
 def to_host64(t) -> np.ndarray:
@@ -48,7 +55,7 @@ def run_gpu(tens: workloads.Tensors, params: dict, route: str = "auto", stream=N
     b = to_device(tens.bias_dev, tens.dtype) if tens.bias is not None else None
     pl = C.get_plan(tuple(x.shape), tuple(w.shape), params["stride"], params["padding"],
                     params["dilation"], params["output_padding"], params["groups"], b is not None,
-                    tens.dtype, route)
+                    tens.dtype, route, activation=params.get("activation", "none"))
     y = pl.forward(x, w, b, stream=stream)
     torch.cuda.synchronize()
     return to_host64(y), pl
@@ -60,13 +67,20 @@ def params_of(wl: workloads.Workload) -> dict:
 
 
 def oracle_full(tens: workloads.Tensors, params: dict):
+    """(y, scale): y after the activation, scale the magnitude sum of the
+    terms before it."""
     return oracle.forward(tens.x, tens.w, tens.bias, params["stride"], params["padding"],
-                          params["dilation"], params["output_padding"], params["groups"])
+                          params["dilation"], params["output_padding"], params["groups"],
+                          activation=C.ACTIVATIONS[params.get("activation", "none")])
 
 
-def norm_error(y_gpu: np.ndarray, y_ref: np.ndarray, scale: np.ndarray, bias_abs: np.ndarray):
-    """max normalised error; outputs with zero denominator must match exactly."""
+def norm_error(y_gpu: np.ndarray, y_ref: np.ndarray, scale: np.ndarray, bias_abs: np.ndarray,
+               act: int = 0):
+    """max normalised error; outputs with zero denominator must match exactly.
+    With an activation, the denominator is L_f * (scale + |bias|) + |y_ref|."""
     den = scale + bias_abs
+    if act:
+        den = ACT_LIPSCHITZ[act] * den + np.abs(y_ref)
     diff = np.abs(y_gpu - y_ref)
     zero = den == 0
     if np.any(zero) and np.any(diff[zero] != 0):
@@ -88,7 +102,8 @@ def check_full(tens, params, route="auto", tag=""):
     y, pl = run_gpu(tens, params, route)
     ref, sc = oracle_full(tens, params)
     assert y.shape == ref.shape
-    e = norm_error(y, ref, sc, bias_abs_full(tens, ref.shape))
+    e = norm_error(y, ref, sc, bias_abs_full(tens, ref.shape),
+                   C.ACTIVATIONS[params.get("activation", "none")])
     say(f"[gpu]   -> plan route {pl.route}, max normalised error {e:.3e}")
     assert e <= TOL[tens.dtype], f"{tag}: error {e} above {TOL[tens.dtype]}"
     return y, ref, pl

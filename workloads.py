@@ -39,7 +39,7 @@ class Workload:
     output_padding: Tuple[int, ...]
     groups: int
     has_bias: bool
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     x_dist: str
     w_dist: str
     b_dist: str
@@ -139,9 +139,9 @@ class Tensors:
     """Host buffers of one problem instance.
 
     ``x``, ``w``, ``bias`` are float32 arrays holding the exact values (for
-    bfloat16 problems, exactly representable in bfloat16). ``x_dev`` etc. are
-    the arrays in the device dtype, ready to be copied to the GPU: float32
-    arrays, or uint16 bfloat16 bit patterns.
+    bfloat16 / float16 problems, exactly representable in that type). ``x_dev``
+    etc. are the arrays in the device dtype, ready to be copied to the GPU:
+    float32 arrays, or uint16 bit patterns of bfloat16 or IEEE half.
     """
     dtype: str
     x: np.ndarray
@@ -168,6 +168,14 @@ def make_tensors(x_shape: Sequence[int], w_shape: Sequence[int], c_out: int, has
         return Tensors("bf16", bf16_bits_to_f32(xb).reshape(xs), bf16_bits_to_f32(wb).reshape(ws),
                        bf16_bits_to_f32(bb) if bb is not None else None,
                        xb.reshape(xs), wb.reshape(ws), bb)
+    if dtype == "f16":
+        # IEEE half, round to nearest even (numpy's conversion)
+        xh, wh = x.astype(np.float16), w.astype(np.float16)
+        bh = b.astype(np.float16) if b is not None else None
+        return Tensors("f16", xh.astype(np.float32), wh.astype(np.float32),
+                       bh.astype(np.float32) if bh is not None else None,
+                       xh.view(np.uint16), wh.view(np.uint16),
+                       bh.view(np.uint16) if bh is not None else None)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

@@ -131,22 +131,24 @@ namespace tiles {
 struct GemmTile {
     int bm, bn, wgm, bf16, sc, xb;  // xb: halo ring buffers (3: two groups in flight, 2: one)
     int nw;                         // waves per block (4 or 8)
+    int occ;                        // blocks per CU the LDS budget and registers allow (2 or 4)
 };
-constexpr int kGemmLdsPerWave = 20 * 1024;
+// A CU's 160 KiB of LDS shared by its resident blocks.
+constexpr int kGemmLdsPerCU = 160 * 1024;
 constexpr int kGemmTapGroup = 4;   // taps per pipeline stage, at most (the planner picks 1..4)
 constexpr int kGemmWRing = 3;      // weight-tile buffers: two stages in flight
 constexpr int kGemmWRowBytes = 32; // weight row: one chunk of channels
 constexpr int kGemmCfgCount = 7;
 constexpr GemmTile kGemmCfg[kGemmCfgCount] = {
-    {128, 256, 1, 1, 1, 3, 4},  // 0: bf16, waves 128 x 64
-    {64, 256, 1, 1, 1, 3, 4},   // 1: bf16, waves 64 x 64
-    {128, 128, 1, 1, 1, 3, 4},  // 2: bf16, waves 128 x 32
-    {64, 256, 1, 0, 1, 3, 4},   // 3: f32, waves 64 x 64
-    {64, 128, 1, 0, 2, 3, 4},   // 4: f32, waves 64 x 32, two chunks per stage
-    {128, 128, 1, 0, 1, 3, 4},  // 5: f32, waves 128 x 32
-    {128, 256, 1, 1, 1, 2, 4},  // 6: bf16, waves 128 x 64, larger halos (3-D tiles)
+    {128, 256, 1, 1, 1, 3, 4, 2},  // 0: bf16, waves 128 x 64
+    {64, 256, 1, 1, 1, 3, 4, 2},   // 1: bf16, waves 64 x 64
+    {128, 128, 1, 1, 1, 3, 4, 2},  // 2: bf16, waves 128 x 32
+    {64, 256, 1, 0, 1, 3, 4, 2},   // 3: f32, waves 64 x 64
+    {64, 128, 1, 0, 2, 3, 4, 2},   // 4: f32, waves 64 x 32, two chunks per stage
+    {128, 128, 1, 0, 1, 3, 4, 2},  // 5: f32, waves 128 x 32
+    {128, 256, 1, 1, 1, 2, 4, 2},  // 6: bf16, waves 128 x 64, larger halos (3-D tiles)
 };
-constexpr int gemm_lds_budget(const GemmTile &t) { return kGemmLdsPerWave * t.nw; }
+constexpr int gemm_lds_budget(const GemmTile &t) { return kGemmLdsPerCU / t.occ; }
 constexpr int gemm_chunk_ch(const GemmTile &t) { return t.bf16 ? 16 : 8; }
 // one stage's weight tiles
 constexpr int gemm_wbuf_bytes(const GemmTile &t, int gs) {

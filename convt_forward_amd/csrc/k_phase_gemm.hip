@@ -14,7 +14,8 @@
 // the phase split its stride-phase variants name.
 //
 // Block: 256 threads (4 waves as WGM x 4/WGM, one per SIMD), BM output
-// channels x BN positions of one phase; its LDS stays within 80 KiB, so two
+// channels x BN positions of one phase; its LDS stays within 160 KiB / occ
+// (the configuration's blocks per CU; 80 KiB for two), so two
 // blocks share each CU and one block's barrier and LDS waits overlap the
 // other's MFMAs. The BN positions form a
 // (td, th, tw) box in q space. K runs over chunks of 32 bytes of input
@@ -79,7 +80,8 @@
 namespace convt {
 
 template <typename T, int CFG, int GS, bool BWD, bool ACT>
-__global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
+__global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu_waves_per_eu(
+    tiles::kGemmCfg[CFG].occ * tiles::kGemmCfg[CFG].nw / 4, tiles::kGemmCfg[CFG].occ * tiles::kGemmCfg[CFG].nw / 4))) void phase_gemm_kernel(DevParams p, const T *__restrict__ x,
                                                          const T *__restrict__ wr,
                                                          const int32_t *__restrict__ tab,
                                                          const T *__restrict__ bias,
@@ -550,12 +552,17 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
                     bv = half_to_f32<HT>(__builtin_amdgcn_raw_buffer_load_b16(bs, (co_u + lane_co) * 2, 0, 0));
                 else
                     bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (co_u + lane_co) * 4, 0, 0));
+                // rows past Cog (tile padding) store nothing: their channel
+                // offset could wrap the 32-bit range on large planes and
+                // land inside the slice; for real rows yoff + cbytes stays
+                // below 2^32 (the slice is below 2^31 bytes)
+                const bool row_ok = (int)(co_u + lane_co) < co_left;
                 const uint32_t cbytes = (co_u + lane_co) * ypl_bytes;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     float v = acc[mt][nt][j] + bv;
                     if constexpr (ACT) v = activate(act, v);
-                    const uint32_t off = yoff[nt] + cbytes;
+                    const uint32_t off = row_ok ? yoff[nt] + cbytes : kOutOfRange;
                     if constexpr (ES == 2)
                         __builtin_amdgcn_raw_buffer_store_b16(f32_to_half<HT>(v), ys, off, 0, 0);
                     else

@@ -279,8 +279,9 @@ int pick_gemm_cfg(DevParams *dp, int dtype, int ndim, bool bwd, int gs, double *
         // cycles per byte of operands)
         const double lds_ratio = 0.67 * (mt + nt) / (mt * nt) * (bf16 ? 1.0 : 0.25);
         const double eff = std::max(1.0, lds_ratio) * (1.0 + 0.25 / (mt * nt));
-        const double rounds = std::ceil((double)blocks / (256.0 * 8 / t.nw));
-        const double time = rounds * (double)t.bm * t.bn * eff;
+        const double rounds = std::ceil((double)blocks / (256.0 * t.occ));
+        // a round's blocks share the CU's SIMDs (nw/4 waves per SIMD each)
+        const double time = rounds * t.occ * (t.nw / 4.0) * (double)t.bm * t.bn * eff / 2.0;
         if (best < 0 || time < best_t * 0.999) {
             best = c;
             best_t = time;

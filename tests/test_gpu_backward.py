@@ -194,3 +194,28 @@ def test_backward_data_edge_cases():
     pl = C.get_plan((0, 3, 5), (3, 2, 3), (2,), (1,), (1,), (0,), 1, False, "f32")
     assert pl.route_bwd == "none"
     del prm
+
+
+def test_backward_data_large_plane_sampled():
+    """dy planes of 5792^2 positions (1 GiB channel-chunked copy): sampled
+    dx elements on every backward route."""
+    import torch
+    xs, ws = (1, 8, 2896, 2896), (8, 8, 3, 3)
+    prm = dict(stride=(2, 2), padding=(1, 1), dilation=(1, 1), output_padding=(1, 1), groups=1)
+    t = bwd_tensors(xs, ws, prm, "bf16", "uniform", 78)
+    dy = to_device(t.x_dev, "bf16")
+    w = to_device(t.w_dev, "bf16")
+    rng = np.random.default_rng(104)
+    pts = np.stack([rng.integers(0, v, 20000) for v in xs], axis=1).astype(np.int64)
+    xv, sv = oracle.backward_data_points(t.x, t.w, xs, pts, **prm)
+    for route in ["auto", "phase_gemm", "naive"]:
+        pl = C.get_plan(xs, ws, prm["stride"], prm["padding"], prm["dilation"],
+                        prm["output_padding"], 1, False, "bf16", "auto", route)
+        say(f"[gpu] bwd large plane route={pl.route_bwd}")
+        dx = pl.backward_data(dy, w)
+        torch.cuda.synchronize()
+        got = to_host64(dx[tuple(torch.from_numpy(pts.T).to(dx.device))])
+        e = norm_error(got, xv, sv, np.zeros_like(sv))
+        assert e <= TOL["bf16"], f"{route}: {e}"
+        del dx
+        torch.cuda.empty_cache()

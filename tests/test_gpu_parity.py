@@ -357,3 +357,55 @@ def test_prepared_split_matches_forward():
     y2_ref = pl.forward(x2, w, b)
     torch.cuda.synchronize()
     assert np.array_equal(to_host64(y2), to_host64(y2_ref))
+
+
+# ---------------------------------------------------------------------------
+# Maximum sizes: planes of 2^25 - 2^26 positions, channel slices of 1 GiB
+# (the raw buffer resources' 32-bit byte offsets at half their range), on
+# every route that serves them, checked on sampled outputs.
+# ---------------------------------------------------------------------------
+# (the 2-D cases once wrote zeros over real outputs: tile rows past C_out
+# had their channel offset wrap the 32-bit range)
+LARGE = [
+    ("1d_2^24", (1, 16, 1 << 24), (16, 8, 4), (2,), (1,), (1,), (0,), 1, "bf16"),
+    ("2d_4096^2", (1, 8, 4096, 4096), (8, 8, 3, 3), (2, 2), (1, 1), (1, 1), (1, 1), 1, "bf16"),
+    ("2d_2896^2_f32", (1, 8, 2896, 2896), (8, 8, 3, 3), (2, 2), (1, 1), (1, 1), (1, 1), 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", LARGE, ids=[c[0] for c in LARGE])
+def test_large_planes_sampled(case):
+    import torch
+    name, xs, ws, s, p, d, op, g, dt = case
+    prm = dict(stride=s, padding=p, dilation=d, output_padding=op, groups=g)
+    tens = workloads.make_tensors(xs, ws, ws[1] * g, True, dt, "uniform", "uniform",
+                                  "uniform", 77)
+    x = to_device(tens.x_dev, dt)
+    w = to_device(tens.w_dev, dt)
+    b = to_device(tens.bias_dev, dt)
+    pts = None
+    for route in ["auto", "phase_gemm", "grouped", "direct", "naive"]:
+        try:
+            pl = C.get_plan(xs, ws, s, p, d, op, g, True, dt, route)
+        except C.ConvtError as e:
+            assert e.status == 2
+            continue
+        say(f"[gpu] large {name} route={pl.route}")
+        y = pl.forward(x, w, b)
+        torch.cuda.synchronize()
+        if pts is None:
+            rng = np.random.default_rng(103)
+            pts = np.stack([rng.integers(0, v, 20000) for v in y.shape], axis=1).astype(np.int64)
+            # the last outputs of the plane (the far end of the offsets)
+            last = np.array(np.unravel_index(np.arange(y[0, 0].numel() - 64, y[0, 0].numel()),
+                                             tuple(y.shape[2:]))).T
+            tail = np.concatenate([np.tile([[0, y.shape[1] - 1]], (64, 1)), last], axis=1)
+            pts = np.concatenate([pts, tail.astype(np.int64)])
+            yv, sv = oracle.points(tens.x, tens.w, tens.bias, pts, s, p, d, op, g)
+            babs = np.abs(tens.bias[pts[:, 1]].astype(np.float64))
+        got = to_host64(y[tuple(torch.from_numpy(pts.T).to(y.device))])
+        e = norm_error(got, yv, sv, babs)
+        say(f"[gpu]   -> {len(pts)} points, max normalised error {e:.3e}")
+        assert e <= TOL[dt], f"{route}: {e}"
+        del y
+        torch.cuda.empty_cache()

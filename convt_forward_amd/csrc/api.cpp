@@ -114,6 +114,15 @@ convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, cons
     if (needs_weights_in_workspace(pl.route) &&
         (!workspace || ((uintptr_t)workspace % 16) != 0))
         return CONVT_ERR_INVALID_ARGUMENT;
+    if (pl.route == CONVT_ROUTE_PHASE_GEMM && pl.xp_bytes > 0 && pl.wr_elems > 0) {
+        // two-byte elements: the weight reorder and the channel-chunked copy
+        // of x in one launch, then the GEMM
+        const hipStream_t s = (hipStream_t)stream;
+        void *xp = (char *)workspace + pl.xp_offset;
+        const convt_status st = device_status(convt::launch_prep(pl, w, workspace, x, xp, s));
+        if (st != CONVT_OK) return st;
+        return device_status(convt::launch_phase_gemm(pl, xp, workspace, bias, y, s));
+    }
     convt_status st = convt_prepare_weights(plan, w, workspace, stream);
     if (st != CONVT_OK) return st;
     return convt_forward_prepared(plan, x, w, bias, y, workspace, stream);
@@ -135,17 +144,17 @@ convt_status convt_backward_data(convt_plan_t plan, const void *dy, const void *
             return device_status(convt::launch_naive_bwd(pl, dy, w, dx, s));
         case CONVT_ROUTE_PHASE_GEMM: {
             if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
-            convt_status st = device_status(convt::launch_reorder_bwd(pl, w, workspace, s));
-            if (st != CONVT_OK) return st;
-            const void *yin = dy;
             if (pl.bwd_xp_bytes > 0) {
-                // bfloat16: the channel-chunked copy of dy after the weights
+                // two-byte elements: the weight reorder and the channel-chunked
+                // copy of dy (after the weights) in one launch
                 void *xp = (char *)workspace + pl.bwd_xp_offset;
-                st = device_status(convt::launch_pack_dp(pl.bdp, dy, xp, s));
+                const convt_status st = device_status(convt::launch_prep_bwd(pl, w, workspace, dy, xp, s));
                 if (st != CONVT_OK) return st;
-                yin = xp;
+                return device_status(convt::launch_phase_gemm_bwd(pl, xp, workspace, dx, s));
             }
-            return device_status(convt::launch_phase_gemm_bwd(pl, yin, workspace, dx, s));
+            const convt_status st = device_status(convt::launch_reorder_bwd(pl, w, workspace, s));
+            if (st != CONVT_OK) return st;
+            return device_status(convt::launch_phase_gemm_bwd(pl, dy, workspace, dx, s));
         }
         default:
             return CONVT_ERR_UNSUPPORTED;

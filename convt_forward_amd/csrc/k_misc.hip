@@ -24,7 +24,8 @@ namespace convt {
 // then assembles whole destination vectors (VEC channels of one (tap, co))
 // and writes them with one 16-byte store.
 //
-// Block 0 also writes the grouped kernel's slot table: first one int4
+// Block P (every gridDim-th phase when the grid is smaller) also writes
+// phase P's part of the grouped kernel's slot table: first one int4
 // record per phase P (its q counts per axis, then the index of its first
 // slot | its slot count << 16), then per phase and slot (tap, 8-channel
 // slice), at index tapbase(P) * slices + slot, the byte offset of the tap's
@@ -37,7 +38,7 @@ __device__ void grouped_slot_table(const DevParams &p, int2 *__restrict__ gtab) 
     const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
     const int noct = p.Cig >> 3, HH = p.hh, HWP = p.grp_hwp;
     int2 *tab = gtab + 2 * p.nphase;
-    for (int P = 0; P < p.nphase; ++P) {
+    for (int P = blockIdx.x; P < p.nphase; P += gridDim.x) {
         const PhaseDesc ph = phase_desc(p, P);
         const int nslots = ph.ntaps * noct;
         if (threadIdx.x == 0)
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__re
                                                        T *__restrict__ wr, int ocb,
                                                        int2 *__restrict__ gtab) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    if (blockIdx.x == 0 && gtab != nullptr) grouped_slot_table(p, gtab);
+    if (gtab != nullptr) grouped_slot_table(p, gtab);
     T *brick = (T *)lds_raw;
     constexpr int VEC = 16 / sizeof(T);
     const int ktot = p.ktot;
@@ -144,25 +145,27 @@ static int reorder_ocb(const DevParams &p) {
 // consecutive lanes on consecutive elements into LDS, then each lane
 // assembles 16-byte destination halves (VEC channels of one (tap, co)) and
 // stores them, consecutive lanes on consecutive co. The blocks of the first
-// tap range also zero the padding taps of their (chunk, co) tile, and block 0
-// writes the per-tap halo shift table the GEMM reads: entry tapbase(P) + t
+// tap range also zero the padding taps of their (chunk, co) tile, and block P
+// writes phase P's part of the per-tap halo shift table the GEMM reads (the
+// grid may be smaller than the phase count: blocks then take every gridDim-th
+// phase): entry tapbase(P) + t
 // holds, for tap t of phase P in (j0, j1, j2) order, the shift of its input
 // window within the phase's halo box in box positions,
 // (j0 * ostep0 * E1 + j1 * ostep1) * E2 + j2 * ostep2 (E1, E2: the box
 // extents of that phase), and 0 for the padding taps.
 // ---------------------------------------------------------------------------
+// (block `blk` of `nblk`; lds_raw: 32 * CO * KT + 4 * KT bytes)
 template <typename T>
-__global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const T *__restrict__ w,
-                                                              T *__restrict__ wr,
-                                                              int32_t *__restrict__ tab, int CO,
-                                                              int KT, int vec_runs) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+__device__ __forceinline__ void reorder_chunked_block(const DevParams &p, const T *__restrict__ w,
+                                                      T *__restrict__ wr, int32_t *__restrict__ tab,
+                                                      int CO, int KT, int vec_runs, int blk, int nblk,
+                                                      unsigned char *lds_raw) {
     constexpr int VEC = 16 / sizeof(T), BK = 2 * VEC;
     const int ktot = p.ktot;
     const int nchunks = p.cig_pad / BK;
     const int nco = (p.cog_pad + CO - 1) / CO;
     const int nkt = (ktot + KT - 1) / KT;
-    int bid = blockIdx.x;
+    int bid = blk;
     const int kb = bid % nkt;
     bid /= nkt;
     const int cb = bid % nco;
@@ -174,10 +177,15 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
     T *brick = (T *)lds_raw;                              // [BK][CO][KT]
     int *dst_tap = (int *)(lds_raw + (size_t)BK * CO * KT * sizeof(T));
     const int K1 = p.ax[1].K, K2 = p.ax[2].K;
-    for (int k = threadIdx.x; k < nk; k += 256) {
-        const int kk = kk0 + k;
-        dst_tap[k] = tap_in_table(p, kk / (K1 * K2), (kk / K2) % K1, kk % K2);
-    }
+    // each tap's index in the plan order; computed while a lane's first
+    // loads are in flight (the lookups are chains of dependent parameter
+    // reads)
+    auto tap_lookup = [&]() __attribute__((always_inline)) {
+        for (int k = threadIdx.x; k < nk; k += 256) {
+            const int kk = kk0 + k;
+            dst_tap[k] = tap_in_table(p, kk / (K1 * K2), (kk / K2) % K1, kk % K2);
+        }
+    };
     // 1. load. With vec_runs (KT == ktot, whole 16-byte aligned runs, the
     // block's channels inside or wholly outside Cog), each channel's run
     // [co0, co0 + CO) x [0, ktot) moves as 16-byte vectors, 4 per lane in
@@ -186,8 +194,7 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
     if (vec_runs) {
         const int nvr = CO * ktot * (int)sizeof(T) / 16;  // vectors of one channel's run
         const int nv = BK * nvr;
-        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 4) {
-            u32x4 v[4];
+        auto load = [&](int v0, u32x4 *v) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int vi = v0 + 256 * u;
@@ -197,6 +204,12 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
                 if (vi < nv && ci < p.Cig && co0 < p.Cog)
                     v[u] = ((const u32x4 *)(w + (((int64_t)g * p.Cig + ci) * p.Cog + co0) * ktot))[r];
             }
+        };
+        u32x4 v[4];
+        load(threadIdx.x, v);
+        tap_lookup();
+        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 4) {
+            if (v0 != (int)threadIdx.x) load(v0, v);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int vi = v0 + 256 * u;
@@ -207,8 +220,7 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
             }
         }
     } else {
-        for (int e0 = threadIdx.x; e0 < n_in; e0 += 256 * 8) {
-            T v[8];
+        auto load = [&](int e0, T *v) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int e = e0 + 256 * u;
@@ -219,6 +231,12 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
                 v[u] = w[ok ? w_offset(p, g * p.Cig + ci, co, kk0 + k) : 0];
                 if (!ok) v[u] = from_f32<T>(0.0f);
             }
+        };
+        T v[8];
+        load(threadIdx.x, v);
+        tap_lookup();
+        for (int e0 = threadIdx.x; e0 < n_in; e0 += 256 * 8) {
+            if (e0 != (int)threadIdx.x) load(e0, v);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int e = e0 + 256 * u;
@@ -254,8 +272,9 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
         const int phys = half ^ ((co >> 3) & 1);
         *(u32x4 *)&wg[(int64_t)dst_tap[k] * nchunks * chunk_elems + (int64_t)co * BK + phys * VEC] = out;
     }
-    // 3. padding taps of this (chunk, co) tile
-    if (kb == 0) {
+    // 3. padding taps of this (chunk, co) tile (none when every phase's tap
+    // count is a whole number of groups)
+    if (kb == 0 && p.ktot_pad != p.ktot) {
         const int gs = p.gemm_gs;
         for (int P = 0; P < p.nphase; ++P) {
             const int nt = p.ph[P].ntaps;
@@ -268,10 +287,10 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
             }
         }
     }
-    // 4. the halo shift table
-    if (blockIdx.x == 0) {
+    // 4. the halo shift table: block P writes phase P's entries
+    {
         const int gs = p.gemm_gs;
-        for (int P = 0; P < p.nphase; ++P) {
+        for (int P = blk; P < p.nphase; P += nblk) {
             const PhaseDesc ph = phase_desc(p, P);
             const int padded = (ph.ntaps + gs - 1) / gs * gs;
             const int n1 = ph.n[1], n2 = ph.n[2];
@@ -289,36 +308,63 @@ __global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const
     }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void reorder_chunked_kernel(DevParams p, const T *__restrict__ w,
+                                                              T *__restrict__ wr,
+                                                              int32_t *__restrict__ tab, int CO,
+                                                              int KT, int vec_runs) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    reorder_chunked_block<T>(p, w, wr, tab, CO, KT, vec_runs, blockIdx.x, gridDim.x, lds_raw);
+}
+
+// Launch shape of a chunked weight reorder (forward or backward layout):
+// the per-block extents (CO output channels or OCB channel columns, KT
+// taps), whether whole runs move as 16-byte vectors, the grid and the LDS.
+struct ReorderGrid {
+    int a, KT, vec_runs;
+    int64_t blocks;
+    size_t lds;
+};
+
+static hipError_t reorder_chunked_grid(const Plan &pl, const void *w, ReorderGrid *r) {
+    const DevParams &p = pl.dp;
+    const int bk = 32 / pl.elem_bytes;
+    if (p.cig_pad % bk) return hipErrorInvalidValue;
+    // KT taps x CO output channels per block: at most 1024 (co, tap)
+    // pairs, and CO halved while the grid has fewer than 1024 blocks
+    const int KT = p.ktot < 256 ? p.ktot : 256;
+    const int nkt = (p.ktot + KT - 1) / KT;
+    const int64_t base = (int64_t)p.G * (p.cig_pad / bk) * nkt;
+    int CO = 1024 / KT;
+    if (CO < 1) CO = 1;
+    if (CO > p.cog_pad) CO = p.cog_pad;
+    while (CO > 1 && base * ((p.cog_pad + CO - 1) / CO) < 1024) CO /= 2;
+    const int64_t run_bytes = (int64_t)CO * p.ktot * pl.elem_bytes;
+    r->a = CO;
+    r->KT = KT;
+    r->vec_runs = p.w_layout == CONVT_FILTER_CI_CO_K && !p.w_flip && KT == p.ktot &&
+                  run_bytes % 16 == 0 && ((int64_t)p.Cog * p.ktot * pl.elem_bytes) % 16 == 0 &&
+                  p.Cog % CO == 0 && (uintptr_t)w % 16 == 0;
+    r->blocks = base * ((p.cog_pad + CO - 1) / CO);
+    r->lds = (size_t)32 * CO * KT + (size_t)4 * KT;
+    if (r->blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    return hipSuccess;
+}
+
 hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t stream) {
     const DevParams &p = pl.dp;
     if (p.wr_chunked) {
-        const int bk = 32 / pl.elem_bytes;
-        if (p.cig_pad % bk) return hipErrorInvalidValue;
-        // KT taps x CO output channels per block: at most 1024 (co, tap)
-        // pairs, and CO halved while the grid has fewer than 1024 blocks
-        const int KT = p.ktot < 256 ? p.ktot : 256;
-        const int nkt = (p.ktot + KT - 1) / KT;
-        const int64_t base = (int64_t)p.G * (p.cig_pad / bk) * nkt;
-        int CO = 1024 / KT;
-        if (CO < 1) CO = 1;
-        if (CO > p.cog_pad) CO = p.cog_pad;
-        while (CO > 1 && base * ((p.cog_pad + CO - 1) / CO) < 1024) CO /= 2;
-        const int64_t blocks = base * ((p.cog_pad + CO - 1) / CO);
-        const int64_t run_bytes = (int64_t)CO * p.ktot * pl.elem_bytes;
-        const int vec_runs = p.w_layout == CONVT_FILTER_CI_CO_K && !p.w_flip && KT == p.ktot &&
-                             run_bytes % 16 == 0 &&
-                             ((int64_t)p.Cog * p.ktot * pl.elem_bytes) % 16 == 0 &&
-                             p.Cog % CO == 0 && (uintptr_t)w % 16 == 0;
-        if (blocks <= 0) return hipSuccess;
-        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-        const size_t lds = (size_t)32 * CO * KT + (size_t)4 * KT;
+        ReorderGrid r;
+        const hipError_t e = reorder_chunked_grid(pl, w, &r);
+        if (e != hipSuccess) return e;
+        if (r.blocks <= 0) return hipSuccess;
         int32_t *tab = (int32_t *)((char *)wr + pl.tab_offset);
         if (pl.elem_bytes == 2)
-            hipLaunchKernelGGL(reorder_chunked_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds,
-                               stream, p, (const uint16_t *)w, (uint16_t *)wr, tab, CO, KT, vec_runs);
+            hipLaunchKernelGGL(reorder_chunked_kernel<uint16_t>, dim3((unsigned)r.blocks), dim3(256), r.lds,
+                               stream, p, (const uint16_t *)w, (uint16_t *)wr, tab, r.a, r.KT, r.vec_runs);
         else
-            hipLaunchKernelGGL(reorder_chunked_kernel<float>, dim3((unsigned)blocks), dim3(256), lds,
-                               stream, p, (const float *)w, (float *)wr, tab, CO, KT, vec_runs);
+            hipLaunchKernelGGL(reorder_chunked_kernel<float>, dim3((unsigned)r.blocks), dim3(256), r.lds,
+                               stream, p, (const float *)w, (float *)wr, tab, r.a, r.KT, r.vec_runs);
         return hipGetLastError();
     }
     const int vec = 16 / pl.elem_bytes;
@@ -348,11 +394,11 @@ hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t s
 // (b, g, chunk, position): 16 two-byte loads, coalesced over the positions
 // of a wave, and two 16-byte stores.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void pack_x_kernel(DevParams p, const uint16_t *__restrict__ x,
-                                                      uint16_t *__restrict__ xp, int ptiles) {
+__device__ __forceinline__ void pack_x_block(const DevParams &p, const uint16_t *__restrict__ x,
+                                             uint16_t *__restrict__ xp, int ptiles, int blk) {
     const int nchunks = p.cig_pad / 16;
     const int64_t plane = p.x_plane;
-    int bid = blockIdx.x;
+    int bid = blk;
     const int pt = bid % ptiles;
     bid /= ptiles;
     const int c = bid % nchunks;
@@ -383,13 +429,15 @@ __global__ __launch_bounds__(256) void pack_x_kernel(DevParams p, const uint16_t
 // lanes on consecutive pieces of a row), and writes the 256 x 32-byte
 // destination rows with 16-byte stores, consecutive lanes on consecutive
 // 16 bytes.
-__global__ __launch_bounds__(256) void pack_x8_kernel(DevParams p, const uint16_t *__restrict__ x,
-                                                       uint16_t *__restrict__ xp, int ptiles) {
-    constexpr int RS = 256 + 2;  // LDS row stride (elements): 256 positions + 4 bytes
-    __shared__ uint16_t tile[16 * RS];
+constexpr int kPackRS = 256 + 2;  // LDS row stride (elements): 256 positions + 4 bytes
+constexpr int kPackLdsBytes = 16 * kPackRS * 2;
+__device__ __forceinline__ void pack_x8_block(const DevParams &p, const uint16_t *__restrict__ x,
+                                              uint16_t *__restrict__ xp, int ptiles, int blk,
+                                              uint16_t *tile) {
+    constexpr int RS = kPackRS;
     const int nchunks = p.cig_pad / 16;
     const int64_t plane = p.x_plane;
-    int bid = blockIdx.x;
+    int bid = blk;
     const int pt = bid % ptiles;
     bid /= ptiles;
     const int c = bid % nchunks;
@@ -429,27 +477,50 @@ __global__ __launch_bounds__(256) void pack_x8_kernel(DevParams p, const uint16_
     }
 }
 
+__global__ __launch_bounds__(256) void pack_x_kernel(DevParams p, const uint16_t *__restrict__ x,
+                                                      uint16_t *__restrict__ xp, int ptiles) {
+    pack_x_block(p, x, xp, ptiles, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256) void pack_x8_kernel(DevParams p, const uint16_t *__restrict__ x,
+                                                       uint16_t *__restrict__ xp, int ptiles) {
+    __shared__ uint16_t tile[16 * kPackRS];
+    pack_x8_block(p, x, xp, ptiles, blockIdx.x, tile);
+}
+
+// Launch shape of the channel-chunked copy: 256 positions of one (b, g,
+// chunk) per block; x8: planes of whole 16-byte rows (the LDS variant).
+struct PackGrid {
+    bool x8;
+    int ptiles;
+    int64_t blocks;
+};
+
+static hipError_t pack_grid(const DevParams &p, const void *x, PackGrid *g) {
+    g->x8 = p.x_plane % 8 == 0 && (uintptr_t)x % 16 == 0;
+    const int64_t ptiles = ((int64_t)p.x_plane + 255) / 256;
+    g->blocks = (int64_t)p.B * p.G * (p.cig_pad / 16) * ptiles;
+    if (ptiles > 0x7fffffff || g->blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    g->ptiles = (int)ptiles;
+    return hipSuccess;
+}
+
 hipError_t launch_pack_x(const Plan &pl, const void *x, void *xp, hipStream_t stream) {
     if (pl.xp_bytes == 0) return hipSuccess;
     return launch_pack_dp(pl.dp, x, xp, stream);
 }
 
 hipError_t launch_pack_dp(const DevParams &p, const void *x, void *xp, hipStream_t stream) {
-    if (p.x_plane % 8 == 0 && (uintptr_t)x % 16 == 0) {
-        const int64_t ptiles = ((int64_t)p.x_plane + 255) / 256;
-        const int64_t blocks = (int64_t)p.B * p.G * (p.cig_pad / 16) * ptiles;
-        if (blocks <= 0) return hipSuccess;
-        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(pack_x8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p,
-                           (const uint16_t *)x, (uint16_t *)xp, (int)ptiles);
-        return hipGetLastError();
-    }
-    const int64_t ptiles = ((int64_t)p.x_plane + 255) / 256;
-    const int64_t blocks = (int64_t)p.B * p.G * (p.cig_pad / 16) * ptiles;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p,
-                       (const uint16_t *)x, (uint16_t *)xp, (int)ptiles);
+    PackGrid g;
+    const hipError_t e = pack_grid(p, x, &g);
+    if (e != hipSuccess) return e;
+    if (g.blocks <= 0) return hipSuccess;
+    if (g.x8)
+        hipLaunchKernelGGL(pack_x8_kernel, dim3((unsigned)g.blocks), dim3(256), 0, stream, p,
+                           (const uint16_t *)x, (uint16_t *)xp, g.ptiles);
+    else
+        hipLaunchKernelGGL(pack_x_kernel, dim3((unsigned)g.blocks), dim3(256), 0, stream, p,
+                           (const uint16_t *)x, (uint16_t *)xp, g.ptiles);
     return hipGetLastError();
 }
 
@@ -760,26 +831,27 @@ hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void 
 // reads the runs W[m][oc0 .. oc0 + OCB)[kk0 .. kk0 + KT) into LDS with
 // consecutive lanes on consecutive elements, then writes, per (tap, chunk),
 // the 8 rows' 256 contiguous bytes, consecutive lanes on consecutive 16-byte
-// halves. Block 0 also writes the halo shift table: entry tapbase(P) + t
+// halves. Block P also writes phase P's part of the halo shift table (blocks
+// take every gridDim-th phase when the grid is smaller): entry tapbase(P) + t
 // holds, for tap t = (j0, j1, j2) of phase P with input offsets off_a =
 // off0_a + j_a * ostep_a, the row of its window in the phase's halo box
 // (which starts at the phase's largest offset u_a = off0_a + (n_a - 1) *
 // ostep_a), ((u0 - off0) * E1 + (u1 - off1)) * E2 + (u2 - off2), E1 and E2
 // the box extents (the dx tile plus span_max); padding taps get 0.
 // ---------------------------------------------------------------------------
+// (block `blk` of `nblk`; lds_raw: 8 * OCB * KT elements + 4 * KT bytes)
 template <typename T>
-__global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *__restrict__ w,
-                                                          T *__restrict__ wr,
-                                                          int32_t *__restrict__ tab, int OCB,
-                                                          int KT, int vec_runs) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+__device__ __forceinline__ void reorder_bwd_block(const DevParams &p, const T *__restrict__ w,
+                                                  T *__restrict__ wr, int32_t *__restrict__ tab,
+                                                  int OCB, int KT, int vec_runs, int blk, int nblk,
+                                                  unsigned char *lds_raw) {
     constexpr int VEC = 16 / sizeof(T), BK = 2 * VEC, MB = 8;
     const int Cm = p.Cog, Coc = p.Cig, ktot = p.ktot;
     const int nchunks = p.cig_pad / BK;
     const int nob = (p.cig_pad + OCB - 1) / OCB;
     const int nmb = p.cog_pad / MB;
     const int nkt = (ktot + KT - 1) / KT;
-    int bid = blockIdx.x;
+    int bid = blk;
     const int kb = bid % nkt;
     bid /= nkt;
     const int ob = bid % nob;
@@ -792,19 +864,23 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
     T *brick = (T *)lds_raw;  // [MB][OCB][KT]
     int *dst_tap = (int *)(lds_raw + (size_t)MB * OCB * KT * sizeof(T));
     const int K1 = p.ax[1].K, K2 = p.ax[2].K;
-    for (int k = threadIdx.x; k < nk; k += 256) {
-        const int kk = kk0 + k;
-        dst_tap[k] = tap_in_table(p, kk / (K1 * K2), (kk / K2) % K1, kk % K2);
-    }
+    auto tap_lookup = [&]() __attribute__((always_inline)) {
+        for (int k = threadIdx.x; k < nk; k += 256) {
+            const int kk = kk0 + k;
+            dst_tap[k] = tap_in_table(p, kk / (K1 * K2), (kk / K2) % K1, kk % K2);
+        }
+    };
     // With vec_runs (KT == ktot, every chunk of the block inside or wholly
     // outside Cog, 16-byte aligned runs), each row's run [oc0, oc0 + OCB) x
-    // [0, ktot) moves as 16-byte vectors, 4 per lane in flight.
+    // [0, ktot) moves as 16-byte vectors, 4 per lane in flight; the tap
+    // lookups (chains of dependent parameter reads) run while a lane's first
+    // loads are in flight.
     const int n_in = vec_runs ? 0 : MB * noc * nk;
+    if (!vec_runs) tap_lookup();
     if (vec_runs) {
         const int nvr = noc * ktot * (int)sizeof(T) / 16;  // vectors of one row's run
         const int nv = MB * nvr;
-        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 4) {
-            u32x4 v[4];
+        auto load = [&](int v0, u32x4 *v) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int vi = v0 + 256 * u;
@@ -813,6 +889,12 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
                 if (vi < nv && m0 + i < Cm && oc0 < Coc)
                     v[u] = ((const u32x4 *)(w + (((int64_t)g * Cm + m0 + i) * Coc + oc0) * ktot))[r];
             }
+        };
+        u32x4 v[4];
+        load(threadIdx.x, v);
+        tap_lookup();
+        for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * 4) {
+            if (v0 != (int)threadIdx.x) load(v0, v);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int vi = v0 + 256 * u;
@@ -871,8 +953,9 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
         *(u32x4 *)&wg[((int64_t)dst_tap[k] * nchunks + oc0 / BK + cc) * chunk_elems + (int64_t)m * BK +
                       phys * VEC] = out;
     }
-    // padding taps of this (rows, chunks) tile
-    if (kb == 0) {
+    // padding taps of this (rows, chunks) tile (none when every phase's tap
+    // count is a whole number of groups)
+    if (kb == 0 && p.ktot_pad != p.ktot) {
         const int gs = p.gemm_gs;
         for (int P = 0; P < p.nphase; ++P) {
             const int nt = p.ph[P].ntaps;
@@ -885,11 +968,12 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
             }
         }
     }
-    if (blockIdx.x == 0) {
+    // the halo shift table: block P writes phase P's entries
+    {
         const int gs = p.gemm_gs;
         const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
         const int E1 = p.th + a1.span_max, E2 = p.tw + a2.span_max;
-        for (int P = 0; P < p.nphase; ++P) {
+        for (int P = blk; P < p.nphase; P += nblk) {
             const PhaseDesc ph = phase_desc(p, P);
             const int padded = (ph.ntaps + gs - 1) / gs * gs;
             const int n1 = ph.n[1], n2 = ph.n[2];
@@ -909,7 +993,16 @@ __global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *
     }
 }
 
-hipError_t launch_reorder_bwd(const Plan &pl, const void *w, void *wr, hipStream_t stream) {
+template <typename T>
+__global__ __launch_bounds__(256) void reorder_bwd_kernel(DevParams p, const T *__restrict__ w,
+                                                          T *__restrict__ wr,
+                                                          int32_t *__restrict__ tab, int OCB,
+                                                          int KT, int vec_runs) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    reorder_bwd_block<T>(p, w, wr, tab, OCB, KT, vec_runs, blockIdx.x, gridDim.x, lds_raw);
+}
+
+static hipError_t reorder_bwd_grid(const Plan &pl, const void *w, ReorderGrid *r) {
     const DevParams &p = pl.bdp;
     const int es = pl.elem_bytes, bk = 32 / es;
     if (p.cig_pad % bk || p.cog_pad % 8) return hipErrorInvalidValue;
@@ -922,22 +1015,102 @@ hipError_t launch_reorder_bwd(const Plan &pl, const void *w, void *wr, hipStream
     const int64_t nkt = (p.ktot + KT - 1) / KT;
     const int64_t base = (int64_t)p.G * (p.cog_pad / 8) * nkt;
     while (OCB > bk && base * ((p.cig_pad + OCB - 1) / OCB) < 1024) OCB = (OCB / 2 + bk - 1) / bk * bk;
-    const int64_t blocks = base * ((p.cig_pad + OCB - 1) / OCB);
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const int vec_runs = p.w_layout == CONVT_FILTER_CI_CO_K && !p.w_flip && KT == p.ktot &&
-                         p.Cig % OCB == 0 && p.cig_pad % OCB == 0 &&
-                         ((int64_t)p.Cig * p.ktot * es) % 16 == 0 &&
-                         ((int64_t)OCB * p.ktot * es) % 16 == 0 && (uintptr_t)w % 16 == 0;
-    const size_t lds = (size_t)8 * OCB * KT * es + (size_t)4 * KT;
+    r->a = OCB;
+    r->KT = KT;
+    r->blocks = base * ((p.cig_pad + OCB - 1) / OCB);
+    r->vec_runs = p.w_layout == CONVT_FILTER_CI_CO_K && !p.w_flip && KT == p.ktot &&
+                  p.Cig % OCB == 0 && p.cig_pad % OCB == 0 &&
+                  ((int64_t)p.Cig * p.ktot * es) % 16 == 0 &&
+                  ((int64_t)OCB * p.ktot * es) % 16 == 0 && (uintptr_t)w % 16 == 0;
+    r->lds = (size_t)8 * OCB * KT * es + (size_t)4 * KT;
+    if (r->blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    return hipSuccess;
+}
+
+hipError_t launch_reorder_bwd(const Plan &pl, const void *w, void *wr, hipStream_t stream) {
+    const DevParams &p = pl.bdp;
+    ReorderGrid r;
+    const hipError_t e = reorder_bwd_grid(pl, w, &r);
+    if (e != hipSuccess) return e;
+    if (r.blocks <= 0) return hipSuccess;
     int32_t *tab = (int32_t *)((char *)wr + pl.bwd_tab_offset);
-    if (es == 2)
-        hipLaunchKernelGGL(reorder_bwd_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds,
-                           stream, p, (const uint16_t *)w, (uint16_t *)wr, tab, OCB, KT, vec_runs);
+    if (pl.elem_bytes == 2)
+        hipLaunchKernelGGL(reorder_bwd_kernel<uint16_t>, dim3((unsigned)r.blocks), dim3(256), r.lds,
+                           stream, p, (const uint16_t *)w, (uint16_t *)wr, tab, r.a, r.KT, r.vec_runs);
     else
-        hipLaunchKernelGGL(reorder_bwd_kernel<float>, dim3((unsigned)blocks), dim3(256), lds,
-                           stream, p, (const float *)w, (float *)wr, tab, OCB, KT, vec_runs);
+        hipLaunchKernelGGL(reorder_bwd_kernel<float>, dim3((unsigned)r.blocks), dim3(256), r.lds,
+                           stream, p, (const float *)w, (float *)wr, tab, r.a, r.KT, r.vec_runs);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The two preparations of the two-byte phase GEMM in one launch: the weight
+// reorder (forward or backward layout) and the channel-chunked copy of the
+// input are independent, so blocks [0, nrb) reorder and the rest copy, and
+// the reorder's latency (its blocks move little data) hides behind the
+// copy's traffic instead of adding a launch of its own.
+// ---------------------------------------------------------------------------
+template <bool BWD, bool X8>
+__global__ __launch_bounds__(256) void prep_kernel(DevParams p, const uint16_t *__restrict__ w,
+                                                   uint16_t *__restrict__ wr, int32_t *__restrict__ tab,
+                                                   int a, int KT, int vec_runs, int nrb,
+                                                   const uint16_t *__restrict__ x,
+                                                   uint16_t *__restrict__ xp, int ptiles) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    const int blk = blockIdx.x;
+    if (blk < nrb) {
+        if constexpr (BWD)
+            reorder_bwd_block<uint16_t>(p, w, wr, tab, a, KT, vec_runs, blk, nrb, lds_raw);
+        else
+            reorder_chunked_block<uint16_t>(p, w, wr, tab, a, KT, vec_runs, blk, nrb, lds_raw);
+    } else if constexpr (X8) {
+        pack_x8_block(p, x, xp, ptiles, blk - nrb, (uint16_t *)lds_raw);
+    } else {
+        pack_x_block(p, x, xp, ptiles, blk - nrb);
+    }
+}
+
+template <bool BWD>
+static hipError_t launch_prep_t(const Plan &pl, const DevParams &p, const ReorderGrid &r,
+                                const void *w, void *wr, int32_t *tab, const void *x, void *xp,
+                                hipStream_t stream) {
+    PackGrid g;
+    const hipError_t e = pack_grid(p, x, &g);
+    if (e != hipSuccess) return e;
+    const int64_t rb = r.blocks > 0 ? r.blocks : 0, pb = g.blocks > 0 ? g.blocks : 0;
+    if (rb + pb <= 0) return hipSuccess;
+    if (rb + pb > 0x7fffffff) return hipErrorInvalidConfiguration;
+    size_t lds = rb > 0 ? r.lds : 0;
+    if (pb > 0 && g.x8 && lds < (size_t)kPackLdsBytes) lds = kPackLdsBytes;
+    if (g.x8)
+        hipLaunchKernelGGL((prep_kernel<BWD, true>), dim3((unsigned)(rb + pb)), dim3(256), lds, stream, p,
+                           (const uint16_t *)w, (uint16_t *)wr, tab, r.a, r.KT, r.vec_runs, (int)rb,
+                           (const uint16_t *)x, (uint16_t *)xp, g.ptiles);
+    else
+        hipLaunchKernelGGL((prep_kernel<BWD, false>), dim3((unsigned)(rb + pb)), dim3(256), lds, stream, p,
+                           (const uint16_t *)w, (uint16_t *)wr, tab, r.a, r.KT, r.vec_runs, (int)rb,
+                           (const uint16_t *)x, (uint16_t *)xp, g.ptiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep(const Plan &pl, const void *w, void *wr, const void *x, void *xp,
+                       hipStream_t stream) {
+    if (pl.elem_bytes != 2 || !pl.dp.wr_chunked || pl.xp_bytes == 0) return hipErrorInvalidValue;
+    ReorderGrid r;
+    const hipError_t e = reorder_chunked_grid(pl, w, &r);
+    if (e != hipSuccess) return e;
+    return launch_prep_t<false>(pl, pl.dp, r, w, wr, (int32_t *)((char *)wr + pl.tab_offset), x, xp,
+                                stream);
+}
+
+hipError_t launch_prep_bwd(const Plan &pl, const void *w, void *wr, const void *dy, void *xp,
+                           hipStream_t stream) {
+    if (pl.elem_bytes != 2 || pl.bwd_xp_bytes == 0) return hipErrorInvalidValue;
+    ReorderGrid r;
+    const hipError_t e = reorder_bwd_grid(pl, w, &r);
+    if (e != hipSuccess) return e;
+    return launch_prep_t<true>(pl, pl.bdp, r, w, wr, (int32_t *)((char *)wr + pl.bwd_tab_offset), dy,
+                               xp, stream);
 }
 
 }  // namespace convt

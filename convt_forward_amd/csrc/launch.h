@@ -32,4 +32,12 @@ hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void 
 hipError_t launch_phase_gemm_bwd(const Plan &pl, const void *dy, const void *wr, void *dx,
                                  hipStream_t stream);
 
+// Two-byte phase GEMM: the weight reorder and the channel-chunked input copy
+// of the forward (resp. backward) problem in one launch; xp at the plan's
+// xp_offset (resp. bwd_xp_offset) of the workspace wr.
+hipError_t launch_prep(const Plan &pl, const void *w, void *wr, const void *x, void *xp,
+                       hipStream_t stream);
+hipError_t launch_prep_bwd(const Plan &pl, const void *w, void *wr, const void *dy, void *xp,
+                           hipStream_t stream);
+
 }  // namespace convt

@@ -198,6 +198,7 @@ constexpr int kGrpMaxS2 = 4;           // stride of the last axis (residues kept
 // Direct route
 constexpr int kDirThreads = 256;
 constexpr int kDirSlabBytes = 32768;  // weight slab of one group in LDS (float32)
+constexpr int kDirXStageBytes = 32768; // the group's input planes, staged beside it when they fit
 constexpr int kDirCoChunk = 16;       // output channels accumulated per pass
 }  // namespace tiles
 

@@ -643,11 +643,14 @@ hipError_t launch_naive(const Plan &pl, const void *x, const void *w, const void
 // kCo output channels at a time; every input sample it gathers (through the
 // phase table of its output residue, so only contributing taps are visited)
 // feeds all of them. Lanes own whole outputs, so no cross-lane reduction and
-// no atomics are needed.
+// no atomics are needed. When the group's input planes fit (XS), they are
+// staged in LDS after the slab as well: a lane's gathers are then LDS reads
+// after one block-wide coalesced load, rather than a chain of dependent
+// global loads (the taps' bounds checks keep the compiler from batching them).
 // ---------------------------------------------------------------------------
 constexpr int kDirPos = 256;
 
-template <typename T, bool ACT>
+template <typename T, bool ACT, bool XS>
 __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__restrict__ x,
                                                       const T *__restrict__ w,
                                                       const T *__restrict__ bias,
@@ -671,6 +674,12 @@ __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__res
             slab[e] = to_f32(w[w_offset(p, g * p.Cig + ci, co, kk)]);
         }
     }
+    const T *xb = x + ((int64_t)b * p.Ci + (int64_t)g * p.Cig) * p.x_plane;
+    float *xl = slab + slab_n;  // XS: the group's input planes [Cig][x_plane]
+    if constexpr (XS) {
+        const int xn = p.Cig * p.x_plane;
+        for (int e = threadIdx.x; e < xn; e += 256) xl[e] = to_f32(xb[e]);
+    }
     __syncthreads();
     const int o = tile * kDirPos + threadIdx.x;
     if (o >= p.y_plane) return;
@@ -681,7 +690,6 @@ __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__res
     const int n0 = a0.n[r0], n1 = a1.n[r1], n2 = a2.n[r2];
     const int b0 = q0 + a0.off0[r0], b1 = q1 + a1.off0[r1], b2 = q2 + a2.off0[r2];
     const int kb0 = a0.kk0[r0], kb1 = a1.kk0[r1], kb2 = a2.kk0[r2];
-    const T *xb = x + ((int64_t)b * p.Ci + (int64_t)g * p.Cig) * p.x_plane;
     T *yb = y + ((int64_t)b * p.Co + (int64_t)g * p.Cog) * p.y_plane + o;
     for (int co0 = 0; co0 < p.Cog; co0 += kCo) {
         float acc[kCo];
@@ -689,6 +697,7 @@ __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__res
         for (int c = 0; c < kCo; ++c) acc[c] = 0.0f;
         for (int ci = 0; ci < p.Cig; ++ci) {
             const T *xp = xb + (int64_t)ci * p.x_plane;
+            const float *xlp = xl + ci * p.x_plane;
             const float *wc = slab + (ci * p.Cog + co0) * p.ktot;
             for (int j0 = 0; j0 < n0; ++j0) {
                 const int i0 = b0 + j0 * a0.ostep;
@@ -702,7 +711,11 @@ __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__res
                         const int i2 = b2 + j2 * a2.ostep;
                         if (i2 < 0 || i2 >= a2.I) continue;
                         const int k2 = kb2 - j2 * a2.kstep;
-                        const float xv = to_f32(xp[((int64_t)i0 * a1.I + i1) * a2.I + i2]);
+                        float xv;
+                        if constexpr (XS)
+                            xv = xlp[(i0 * a1.I + i1) * a2.I + i2];
+                        else
+                            xv = to_f32(xp[((int64_t)i0 * a1.I + i1) * a2.I + i2]);
                         const float *wt = wc + (k0 * a1.K + k1) * a2.K + k2;
 #pragma unroll
                         for (int c = 0; c < kCo; ++c)
@@ -725,15 +738,24 @@ __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__res
 }
 
 // instances with an activation are separate (none of its code otherwise)
-template <typename T>
-static void launch_direct_t(const DevParams &p, int64_t blocks, size_t lds, const void *x,
+template <typename T, bool XS>
+static void launch_direct_x(const DevParams &p, int64_t blocks, size_t lds, const void *x,
                             const void *w, const void *bias, void *y, hipStream_t stream) {
     if (p.act != CONVT_ACT_NONE)
-        hipLaunchKernelGGL((direct_kernel<T, true>), dim3((unsigned)blocks), dim3(256), lds, stream,
+        hipLaunchKernelGGL((direct_kernel<T, true, XS>), dim3((unsigned)blocks), dim3(256), lds, stream,
                            p, (const T *)x, (const T *)w, (const T *)bias, (T *)y);
     else
-        hipLaunchKernelGGL((direct_kernel<T, false>), dim3((unsigned)blocks), dim3(256), lds,
+        hipLaunchKernelGGL((direct_kernel<T, false, XS>), dim3((unsigned)blocks), dim3(256), lds,
                            stream, p, (const T *)x, (const T *)w, (const T *)bias, (T *)y);
+}
+
+template <typename T>
+static void launch_direct_t(const DevParams &p, int64_t blocks, size_t lds, bool xs, const void *x,
+                            const void *w, const void *bias, void *y, hipStream_t stream) {
+    if (xs)
+        launch_direct_x<T, true>(p, blocks, lds, x, w, bias, y, stream);
+    else
+        launch_direct_x<T, false>(p, blocks, lds, x, w, bias, y, stream);
 }
 
 hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
@@ -743,13 +765,17 @@ hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const voi
     const int64_t blocks = ntile * p.G * p.B;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)p.Cig * p.Cog * p.ktot * sizeof(float);
+    size_t lds = (size_t)p.Cig * p.Cog * p.ktot * sizeof(float);
+    // the group's input planes in LDS too, when they fit beside the slab
+    const int64_t x_bytes = (int64_t)p.Cig * p.x_plane * (int64_t)sizeof(float);
+    const bool xs = x_bytes <= tiles::kDirXStageBytes;
+    if (xs) lds += (size_t)x_bytes;
     if (pl.elem_bytes == 2 && p.f16)
-        launch_direct_t<_Float16>(p, blocks, lds, x, w, bias, y, stream);
+        launch_direct_t<_Float16>(p, blocks, lds, xs, x, w, bias, y, stream);
     else if (pl.elem_bytes == 2)
-        launch_direct_t<uint16_t>(p, blocks, lds, x, w, bias, y, stream);
+        launch_direct_t<uint16_t>(p, blocks, lds, xs, x, w, bias, y, stream);
     else
-        launch_direct_t<float>(p, blocks, lds, x, w, bias, y, stream);
+        launch_direct_t<float>(p, blocks, lds, xs, x, w, bias, y, stream);
     return hipGetLastError();
 }
 

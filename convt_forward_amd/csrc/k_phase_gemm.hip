@@ -436,22 +436,39 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         };
         int chunk = 0, gi = 0, qc = first;  // of stage s
         int c2n = 0, gi2 = 0, q2 = first;   // of stage s + 2
-        if constexpr (BWD) {
+        // Prologue: what stage 0 reads (the first halo, the first weights)
+        // is requested before what later stages read, so that stage 0 waits
+        // for its own copies only (loads complete in issue order).
+        if constexpr (BWD)
             issue_x(0);
-            if (XB == 3 && cx < nchunks) issue_x(1);
-        } else {
+        else
             load_x(0, 0);
-            if (XB == 3 && nchunks > 1) load_x(1, 1);
-        }
         load_w(0, 0, 0, tapbase_of(q2));
         next_stage(c2n, q2, gi2);
-        if (nstages > 1) load_w(1, gi2, c2n, tapbase_of(q2));
+        bool x1 = false;
+        if constexpr (BWD) {
+            if (XB == 3 && cx < nchunks) {
+                issue_x(1);
+                x1 = true;
+            }
+        } else if (XB == 3 && nchunks > 1) {
+            load_x(1, 1);
+            x1 = true;
+        }
+        const bool w1 = nstages > 1;
+        if (w1) load_w(1, gi2, c2n, tapbase_of(q2));
         next_stage(c2n, q2, gi2);
         // halo shifts of the first stage's taps
         int dl[GS];
 #pragma unroll
         for (int u = 0; u < GS; ++u) dl[u] = ptab[tapbase_of(qc) + u];
-        stage_barrier<0>();
+        {
+            const int fly0 = (x1 ? nx : 0) + (w1 ? ndma : 0);
+            if (fly0 == 0)
+                stage_barrier<0>();
+            else
+                stage_barrier_n<NDMA + SC * XCH * XJ>(fly0);
+        }
         int wb = 0, xb = 0;  // buffers of stage s: s % 3, its unit % XB
         for (int s = 0; s < nstages; ++s) {
             const unsigned char *wsb = ws[wb];

@@ -100,14 +100,13 @@ struct GrpArgs {
     int32_t grp_hwp, grp_hshift, grp_nk, grp_nsc;
     int32_t grp_w_off, grp_tab_off, grp_st_off, grp_st_pitch;
     int32_t ktot, nphase;
-    int32_t act;  // convt_activation of the outputs
 };
 
 // Eight waves per SIMD (8 blocks per CU) where the registers allow it: the
 // scalar registers are capped too, since more of them than the cap admits
 // keep blocks from being resident. Instances with more weight fragments in
 // registers (S2 * KS > 2) trade occupancy for having no spills.
-template <int S2, int KS, typename E, bool ACT>
+template <int S2, int KS, typename E, int ACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 2 ? 8 : 4, 8))) void grouped_kernel(
     GrpArgs p, const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const int2 *__restrict__ gtab, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
@@ -282,11 +281,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     const int nsc = pair_dpp ? 2 : p.grp_nsc, nchunk = (nseg + nsc - 1) / nsc;
     const float bvf = (p.has_bias && l16 < Cog) ? half_to_f32<E>(bias[g * Cog + l16]) : 0.0f;
     // the outputs' activation, then one rounding to E, two per word
-    const int act = p.act;
-    auto pack2 = [act](float a, float b) __attribute__((always_inline)) {
-        if constexpr (ACT) {
-            a = activate(act, a);
-            b = activate(act, b);
+    auto pack2 = [](float a, float b) __attribute__((always_inline)) {
+        if constexpr (ACT != CONVT_ACT_NONE) {
+            a = activate<true>(ACT, a);
+            b = activate<true>(ACT, b);
         }
         return pack_half2<E>(a, b);
     };
@@ -610,12 +608,11 @@ static GrpArgs grp_args(const DevParams &p) {
     a.grp_w_off = p.grp_w_off; a.grp_tab_off = p.grp_tab_off; a.grp_st_off = p.grp_st_off;
     a.grp_st_pitch = p.grp_st_pitch;
     a.ktot = p.ktot; a.nphase = p.nphase;
-    a.act = p.act;
     return a;
 }
 
-template <int S2, int KS>
-static void launch_grouped_t(const DevParams &p, const void *x, const void *wr, const int2 *gtab,
+template <int S2, int KS, typename E>
+static void launch_grouped_e(const DevParams &p, const void *x, const void *wr, const int2 *gtab,
                              const void *bias, void *y, int st_align, int x_vec, hipStream_t stream) {
     const dim3 grid(p.G * p.B, p.nt_h, p.nt_d);
     const size_t lds = (size_t)p.grp_lds_bytes;
@@ -623,20 +620,30 @@ static void launch_grouped_t(const DevParams &p, const void *x, const void *wr, 
     const uint16_t *xs = (const uint16_t *)x, *ws = (const uint16_t *)wr,
                    *bs = (const uint16_t *)bias;
     uint16_t *ys = (uint16_t *)y;
-    // instances with an activation are separate (no activation code otherwise)
-    const bool act = p.act != CONVT_ACT_NONE;
-    if (p.f16 && act)
-        hipLaunchKernelGGL((grouped_kernel<S2, KS, _Float16, true>), grid, dim3(256), lds, stream,
-                           a, xs, ws, gtab, bs, ys, st_align, x_vec);
-    else if (p.f16)
-        hipLaunchKernelGGL((grouped_kernel<S2, KS, _Float16, false>), grid, dim3(256), lds, stream,
-                           a, xs, ws, gtab, bs, ys, st_align, x_vec);
-    else if (act)
-        hipLaunchKernelGGL((grouped_kernel<S2, KS, __bf16, true>), grid, dim3(256), lds, stream,
-                           a, xs, ws, gtab, bs, ys, st_align, x_vec);
+    // one instance per activation: the activation folds into the unrolled
+    // store loop (a run-time switch there splits it into branches the
+    // compiler cannot schedule across, which cost even ReLU 70%)
+#define CONVT_GRP_LAUNCH(A)                                                                      \
+    hipLaunchKernelGGL((grouped_kernel<S2, KS, E, A>), grid, dim3(256), lds, stream, a, xs, ws, \
+                       gtab, bs, ys, st_align, x_vec)
+    switch (p.act) {
+        case CONVT_ACT_RELU: CONVT_GRP_LAUNCH(CONVT_ACT_RELU); break;
+        case CONVT_ACT_SIGMOID: CONVT_GRP_LAUNCH(CONVT_ACT_SIGMOID); break;
+        case CONVT_ACT_TANH: CONVT_GRP_LAUNCH(CONVT_ACT_TANH); break;
+        case CONVT_ACT_SILU: CONVT_GRP_LAUNCH(CONVT_ACT_SILU); break;
+        case CONVT_ACT_GELU: CONVT_GRP_LAUNCH(CONVT_ACT_GELU); break;
+        default: CONVT_GRP_LAUNCH(CONVT_ACT_NONE); break;
+    }
+#undef CONVT_GRP_LAUNCH
+}
+
+template <int S2, int KS>
+static void launch_grouped_t(const DevParams &p, const void *x, const void *wr, const int2 *gtab,
+                             const void *bias, void *y, int st_align, int x_vec, hipStream_t stream) {
+    if (p.f16)
+        launch_grouped_e<S2, KS, _Float16>(p, x, wr, gtab, bias, y, st_align, x_vec, stream);
     else
-        hipLaunchKernelGGL((grouped_kernel<S2, KS, __bf16, false>), grid, dim3(256), lds, stream,
-                           a, xs, ws, gtab, bs, ys, st_align, x_vec);
+        launch_grouped_e<S2, KS, __bf16>(p, x, wr, gtab, bias, y, st_align, x_vec, stream);
 }
 
 template <int S2>

@@ -535,7 +535,7 @@ __global__ __launch_bounds__(256) void fill_kernel(DevParams p, const T *__restr
          i += (int64_t)gridDim.x * 256) {
         const int oc = (int)((i / p.y_plane) % p.Co);
         float v = p.has_bias ? to_f32(bias[oc]) : 0.0f;
-        if (p.act != CONVT_ACT_NONE) v = activate(p.act, v);
+        if (p.act != CONVT_ACT_NONE) v = activate<sizeof(T) == 2>(p.act, v);
         y[i] = from_f32<T>(v);
     }
 }
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(256) void naive_kernel(DevParams p, const T *__rest
             }
         }
         if (p.has_bias) acc += to_f32(bias[oc]);
-        if (p.act != CONVT_ACT_NONE) acc = activate(p.act, acc);
+        if (p.act != CONVT_ACT_NONE) acc = activate<sizeof(T) == 2>(p.act, acc);
         y[idx] = from_f32<T>(acc);
     }
 }
@@ -730,7 +730,7 @@ __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__res
             if (co < p.Cog) {
                 float v = acc[c];
                 if (p.has_bias) v += to_f32(bias[g * p.Cog + co]);
-                if constexpr (ACT) v = activate(p.act, v);
+                if constexpr (ACT) v = activate<sizeof(T) == 2>(p.act, v);
                 yb[(int64_t)co * p.y_plane] = from_f32<T>(v);
             }
         }

@@ -578,7 +578,7 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     float v = acc[mt][nt][j] + bv;
-                    if constexpr (ACT) v = activate(act, v);
+                    if constexpr (ACT) v = activate<ES == 2>(act, v);
                     const uint32_t off = row_ok ? yoff[nt] + cbytes : kOutOfRange;
                     if constexpr (ES == 2)
                         __builtin_amdgcn_raw_buffer_store_b16(f32_to_half<HT>(v), ys, off, 0, 0);

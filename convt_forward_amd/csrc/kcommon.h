@@ -64,15 +64,50 @@ __device__ __forceinline__ float logistic(float v) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
 }
 
+// tanh from e = e^(-2|v|) in (0, 1] (hardware exp2 and reciprocal):
+// tanh|v| = (1 - e) / (1 + e), the sign restored. Nothing overflows; near 0
+// the absolute error is a few units of 2^-24.
+__device__ __forceinline__ float tanh_exp2(float v) {
+    const float e = __builtin_amdgcn_exp2f(fabsf(v) * -2.8853900817779268f);  // -2 log2(e)
+    return copysignf((1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), v);
+}
+
+// erf by the rational approximation of Abramowitz and Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (due to Hastings): for x >= 0,
+// erf x = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^(-x^2) with
+// t = 1 / (1 + p x), absolute error at most 1.5e-7; odd in x.
+__device__ __forceinline__ float erf_as7126(float x) {
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+    const float poly =
+        t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    const float e = __builtin_amdgcn_exp2f(ax * ax * -1.4426950408889634f);  // e^(-x^2)
+    return copysignf(1.0f - poly * e, x);
+}
+
 // The activation applied to an output after its bias (convt_activation),
-// in float32.
+// in float32. LOWP: the output is then rounded to a two-byte type (relative
+// step 2^-8 or 2^-11), so tanh and erf take the short forms above, whose
+// errors (below 1.5e-7 absolute) vanish in that rounding; float32 outputs
+// use the device library's tanhf / erff. The short forms matter where
+// outputs are cheap: an HBM-bound kernel has a few dozen VALU cycles per
+// wave-wide output instruction.
+template <bool LOWP = false>
 __device__ __forceinline__ float activate(int act, float v) {
     switch (act) {
         case CONVT_ACT_RELU: return v > 0.0f ? v : 0.0f;
         case CONVT_ACT_SIGMOID: return logistic(v);
-        case CONVT_ACT_TANH: return tanhf(v);
+        case CONVT_ACT_TANH:
+            if constexpr (LOWP)
+                return tanh_exp2(v);
+            else
+                return tanhf(v);
         case CONVT_ACT_SILU: return v * logistic(v);
-        case CONVT_ACT_GELU: return 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
+        case CONVT_ACT_GELU:
+            if constexpr (LOWP)
+                return 0.5f * v * (1.0f + erf_as7126(v * 0.7071067811865476f));
+            else
+                return 0.5f * v * (1.0f + erff(v * 0.7071067811865476f));
         default: return v;
     }
 }

@@ -142,6 +142,8 @@ convt_status convt_backward_data(convt_plan_t plan, const void *dy, const void *
     switch (pl.route_bwd) {
         case CONVT_ROUTE_NAIVE:
             return device_status(convt::launch_naive_bwd(pl, dy, w, dx, s));
+        case CONVT_ROUTE_DIRECT:
+            return device_status(convt::launch_direct_bwd(pl, dy, w, dx, s));
         case CONVT_ROUTE_PHASE_GEMM: {
             if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
             if (pl.bwd_xp_bytes > 0) {

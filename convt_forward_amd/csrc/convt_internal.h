@@ -199,6 +199,15 @@ constexpr int kGrpMaxS2 = 4;           // stride of the last axis (residues kept
 constexpr int kDirThreads = 256;
 constexpr int kDirSlabBytes = 32768;  // weight slab of one group in LDS (float32)
 constexpr int kDirXStageBytes = 32768; // the group's input planes, staged beside it when they fit
+// Direct backward-data kernel (few channels): input channels per pass, and
+// its LDS (weights [tap][Cog padded to 8][Cig padded to a pass] as float32,
+// then 16 bytes per tap)
+constexpr int dir_bwd_ci(int cig) { return cig <= 4 ? 4 : cig <= 8 ? 8 : 16; }
+constexpr int64_t dir_bwd_lds_bytes(int cig, int cog, int ktot) {
+    return (int64_t)ktot * ((cog + 7) / 8 * 8) * ((cig + dir_bwd_ci(cig) - 1) / dir_bwd_ci(cig) * dir_bwd_ci(cig)) * 4 +
+           (int64_t)ktot * 16;
+}
+constexpr int64_t kDirBwdLdsBytes = 49152;
 constexpr int kDirCoChunk = 16;       // output channels accumulated per pass
 }  // namespace tiles
 

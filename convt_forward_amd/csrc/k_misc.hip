@@ -843,6 +843,141 @@ hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void 
 }
 
 // ---------------------------------------------------------------------------
+// Backward data for few channels (the direct kernel turned around):
+//     dx[b][g*Cig + ci][i] = sum over ocl < Cog and taps kk of
+//                            dy[b][g*Cog + ocl][i*s - p + kk*d] * W[g*Cig + ci][ocl][kk]
+// (p: the forward problem). Where Cig or Cog is small, the backward GEMM's
+// tiles (64 dx channels x 16-channel chunks of dy) are mostly padding. A
+// block owns 256 consecutive dx positions of one (batch, group); the group's
+// weights sit in LDS as float32 [kk][ocl, padded to 8][ci, padded to CI], so
+// that one 16-byte read gives four input channels (the same address for
+// every lane: a broadcast), and a table holds each tap's dy offset and
+// per-axis shifts. Each lane owns one dx position and CI input channels at a
+// time; per tap it checks the window once, then takes the output channels 8
+// at a time with buffer loads whose offsets are out of range (reading 0)
+// where the tap falls outside dy or the channel is padding, so the loads
+// carry no branches and issue together.
+// ---------------------------------------------------------------------------
+template <typename T, int CI>
+__global__ __launch_bounds__(256) void direct_bwd_kernel(DevParams p, const T *__restrict__ dy,
+                                                          const T *__restrict__ w,
+                                                          T *__restrict__ dx) {
+    extern __shared__ __attribute__((aligned(16))) float dslab[];
+    const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
+    const int ntile = (p.x_plane + kDirPos - 1) / kDirPos;
+    int bid = blockIdx.x;
+    const int tile = bid % ntile;
+    bid /= ntile;
+    const int g = bid % p.G;
+    const int b = bid / p.G;
+    const int ktot = p.ktot, Cog = p.Cog, Cig = p.Cig;
+    const int cog8 = (Cog + 7) / 8 * 8, cip = (Cig + CI - 1) / CI * CI;
+    const int slab_n = ktot * cog8 * cip;  // (tiles::dir_bwd_lds_bytes: 4 * slab_n + 16 * ktot)
+    for (int e = threadIdx.x; e < slab_n; e += 256) {
+        const int cil = e % cip, r = e / cip, ocl = r % cog8, kk = r / cog8;
+        dslab[e] = (ocl < Cog && cil < Cig) ? to_f32(w[w_offset(p, g * Cig + cil, ocl, kk)]) : 0.0f;
+    }
+    // per tap: dy offset from the tap-0 position, then the per-axis shifts
+    int4 *tk = (int4 *)(dslab + slab_n);
+    for (int kk = threadIdx.x; kk < ktot; kk += 256) {
+        const int k2 = kk % a2.K, k1 = (kk / a2.K) % a1.K, k0 = kk / (a2.K * a1.K);
+        tk[kk] = make_int4(((k0 * a0.D) * a1.O + k1 * a1.D) * a2.O + k2 * a2.D, k0 * a0.D, k1 * a1.D,
+                           k2 * a2.D);
+    }
+    __syncthreads();
+    const int i = tile * kDirPos + threadIdx.x;
+    if (i >= p.x_plane) return;
+    const int i2 = i % a2.I, i1 = (i / a2.I) % a1.I, i0 = i / (a2.I * a1.I);
+    // dy coordinates reached by tap 0
+    const int e0 = i0 * a0.S - a0.P, e1 = i1 * a1.S - a1.P, e2 = i2 * a2.S - a2.P;
+    const int base = (e0 * a1.O + e1) * a2.O + e2;
+    constexpr uint32_t ES = sizeof(T);
+    const uint32_t ypl_bytes = (uint32_t)p.y_plane * ES;
+    const __amdgpu_buffer_rsrc_t ys =
+        make_rsrc(dy + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane, (uint32_t)Cog * ypl_bytes);
+    T *dxb = dx + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane + i;
+    for (int ci0 = 0; ci0 < Cig; ci0 += CI) {
+        float acc[CI];
+#pragma unroll
+        for (int c = 0; c < CI; ++c) acc[c] = 0.0f;
+        for (int kk = 0; kk < ktot; ++kk) {
+            const int4 t = tk[kk];
+            const int o0 = e0 + t.y, o1 = e1 + t.z, o2 = e2 + t.w;
+            const bool ok = o0 >= 0 && o0 < a0.O && o1 >= 0 && o1 < a1.O && o2 >= 0 && o2 < a2.O;
+            const uint32_t off = (uint32_t)(base + t.x) * ES;
+            const float *wk = dslab + (kk * cog8) * cip + ci0;
+            for (int oc0 = 0; oc0 < Cog; oc0 += 8) {
+                float yv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t o = (ok && oc0 + u < Cog) ? off + (uint32_t)(oc0 + u) * ypl_bytes : kOutOfRange;
+                    if constexpr (ES == 4)
+                        yv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ys, o, 0, 0));
+                    else if constexpr (std::is_same<T, _Float16>::value)
+                        yv[u] = half_to_f32<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0));
+                    else
+                        yv[u] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0));
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float *wr = wk + (oc0 + u) * cip;
+#pragma unroll
+                    for (int c4 = 0; c4 < CI; c4 += 4) {
+                        const float4 wv = *(const float4 *)(wr + c4);
+                        acc[c4] += yv[u] * wv.x;
+                        acc[c4 + 1] += yv[u] * wv.y;
+                        acc[c4 + 2] += yv[u] * wv.z;
+                        acc[c4 + 3] += yv[u] * wv.w;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CI; ++c)
+            if (ci0 + c < Cig) dxb[(int64_t)(ci0 + c) * p.x_plane] = from_f32<T>(acc[c]);
+    }
+}
+
+template <typename T>
+static void launch_direct_bwd_t(const DevParams &p, int64_t blocks, int64_t lds, const void *dy,
+                                const void *w, void *dx, hipStream_t stream) {
+    switch (tiles::dir_bwd_ci(p.Cig)) {
+        case 4:
+            hipLaunchKernelGGL((direct_bwd_kernel<T, 4>), dim3((unsigned)blocks), dim3(256), lds, stream, p,
+                               (const T *)dy, (const T *)w, (T *)dx);
+            break;
+        case 8:
+            hipLaunchKernelGGL((direct_bwd_kernel<T, 8>), dim3((unsigned)blocks), dim3(256), lds, stream, p,
+                               (const T *)dy, (const T *)w, (T *)dx);
+            break;
+        default:
+            hipLaunchKernelGGL((direct_bwd_kernel<T, 16>), dim3((unsigned)blocks), dim3(256), lds, stream,
+                               p, (const T *)dy, (const T *)w, (T *)dx);
+            break;
+    }
+}
+
+hipError_t launch_direct_bwd(const Plan &pl, const void *dy, const void *w, void *dx,
+                             hipStream_t stream) {
+    const DevParams &p = pl.dp;  // the forward problem's axes and channels
+    const int64_t ntile = (p.x_plane + kDirPos - 1) / kDirPos;
+    const int64_t blocks = ntile * p.G * p.B;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t lds = tiles::dir_bwd_lds_bytes(p.Cig, p.Cog, p.ktot);
+    // the group's dy planes must fit one buffer resource
+    if (lds > tiles::kDirBwdLdsBytes || (int64_t)p.Cog * p.y_plane * pl.elem_bytes >= ((int64_t)1 << 31))
+        return hipErrorInvalidConfiguration;
+    if (pl.elem_bytes == 2 && p.f16)
+        launch_direct_bwd_t<_Float16>(p, blocks, lds, dy, w, dx, stream);
+    else if (pl.elem_bytes == 2)
+        launch_direct_bwd_t<uint16_t>(p, blocks, lds, dy, w, dx, stream);
+    else
+        launch_direct_bwd_t<float>(p, blocks, lds, dy, w, dx, stream);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Weight reorder for the backward-data GEMM (p: the backward problem, whose
 // rows m are the Cig input channels of a group and whose K channels are its
 // Cog output channels):

@@ -29,6 +29,8 @@ hipError_t launch_fill_dp(const DevParams &p, int elem_bytes, const void *bias, 
 hipError_t launch_reorder_bwd(const Plan &pl, const void *w, void *wr, hipStream_t stream);
 hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void *dx,
                             hipStream_t stream);
+hipError_t launch_direct_bwd(const Plan &pl, const void *dy, const void *w, void *dx,
+                             hipStream_t stream);
 hipError_t launch_phase_gemm_bwd(const Plan &pl, const void *dy, const void *wr, void *dx,
                                  hipStream_t stream);
 

@@ -415,6 +415,13 @@ bool direct_eligible(const DevParams &dp) {
     return slab <= tiles::kDirSlabBytes;
 }
 
+// The direct backward-data kernel (fp: the forward problem): its LDS holds
+// the group's weights, and one buffer resource the group's dy planes.
+bool direct_bwd_eligible(const DevParams &fp, int elem_bytes) {
+    return tiles::dir_bwd_lds_bytes(fp.Cig, fp.Cog, fp.ktot) <= tiles::kDirBwdLdsBytes &&
+           (int64_t)fp.Cog * fp.y_plane * elem_bytes < ((int64_t)1 << 31) && fp.x_plane > 0;
+}
+
 }  // namespace
 
 // ---- backward data ---------------------------------------------------------
@@ -464,8 +471,14 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
             route = CONVT_ROUTE_NONE;
         else if (no_terms)
             route = CONVT_ROUTE_FILL;
+        else if (direct_bwd_eligible(fp, pl->elem_bytes) && (fp.Cig < 32 || fp.Cog < 16))
+            // few channels: the backward GEMM's tiles (64 dx channels, chunks
+            // of 16 dy channels) would be mostly padding
+            route = CONVT_ROUTE_DIRECT;
         else if (gemm_eligible(b, dt, nd, true))
             route = CONVT_ROUTE_PHASE_GEMM;
+        else if (direct_bwd_eligible(fp, pl->elem_bytes))
+            route = CONVT_ROUTE_DIRECT;
         else
             route = CONVT_ROUTE_NAIVE;
     } else {
@@ -475,6 +488,9 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
             case CONVT_ROUTE_FILL: ok = !empty_out && no_terms; break;
             case CONVT_ROUTE_PHASE_GEMM:
                 ok = !empty_out && !no_terms && gemm_eligible(b, dt, nd, true);
+                break;
+            case CONVT_ROUTE_DIRECT:
+                ok = !empty_out && !no_terms && direct_bwd_eligible(fp, pl->elem_bytes);
                 break;
             case CONVT_ROUTE_NAIVE: ok = !empty_out && !no_terms; break;
             default: ok = false;

@@ -245,7 +245,9 @@ convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void
  * large enough, but not in use by a concurrent call. Asynchronous on stream,
  * errors as for convt_forward. Routes (info.route_bwd): NONE (dx empty),
  * FILL (no output channels: dx = 0), PHASE_GEMM (stride phases summed inside
- * one implicit-gather GEMM on MFMA), NAIVE (one thread per dx element).
+ * one implicit-gather GEMM on MFMA), DIRECT (few channels per group: a thread
+ * per dx position over its group's input channels, weights in LDS), NAIVE
+ * (one thread per dx element).
  */
 convt_status convt_backward_data(convt_plan_t plan, const void *dy, const void *w, void *dx,
                                  void *workspace, void *stream);

@@ -279,7 +279,7 @@ def test_padding_hi_fields_validated():
 def test_backward_data_refuses_bad_arguments_before_launch():
     """Host-side checks of convt_backward_data: nothing reaches the device."""
     L = C.lib()
-    pl = plan(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2)
+    pl = plan(x_shape=(1, 32, 8), w_shape=(32, 16, 4), stride=2)
     assert pl.route_bwd == "phase_gemm" and pl.bwd_workspace_bytes > 0
     h = pl.handle
     fake = 4096  # never dereferenced
@@ -293,10 +293,18 @@ def test_backward_data_refuses_bad_arguments_before_launch():
 
 def test_backward_routes():
     """Routes of the backward pass: forced routes that cannot serve are
-    refused; the naive route serves any problem."""
+    refused; the naive route serves any problem; few channels per group take
+    the direct kernel (any stride), many the GEMM."""
     assert plan(x_shape=(0, 2, 5), w_shape=(2, 3, 3)).route_bwd == "none"
     assert plan(x_shape=(1, 2, 5), w_shape=(2, 0, 3)).route_bwd == "fill"
-    assert plan(x_shape=(1, 2, 5), w_shape=(2, 3, 3), stride=19).route_bwd == "naive"
+    assert plan(x_shape=(1, 2, 5), w_shape=(2, 3, 3)).route_bwd == "direct"
+    assert plan(x_shape=(1, 2, 5), w_shape=(2, 3, 3), stride=19).route_bwd == "direct"
+    assert plan(x_shape=(1, 64, 5), w_shape=(64, 64, 3), stride=19).route_bwd == "naive"
+    assert plan(x_shape=(1, 64, 5), w_shape=(64, 64, 3), stride=2).route_bwd == "phase_gemm"
+    assert plan(x_shape=(1, 64, 5), w_shape=(64, 32, 3), route_bwd="direct").route_bwd == "direct"
+    # the direct kernel's weights (64 x 64 x 3 float32 = 48 KiB, plus the tap
+    # table) exceed its LDS
+    assert status_of(x_shape=(1, 64, 5), w_shape=(64, 64, 3), route_bwd="direct") == 2
     assert plan(x_shape=(1, 2, 5), w_shape=(2, 3, 3), route_bwd="naive").route_bwd == "naive"
     assert status_of(x_shape=(1, 2, 5), w_shape=(2, 3, 3), stride=19, route_bwd="phase_gemm") == 2
     assert status_of(x_shape=(1, 2, 5), w_shape=(2, 3, 3), route_bwd="fill") == 2

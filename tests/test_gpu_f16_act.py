@@ -89,7 +89,7 @@ def test_float16_backward_data(case):
     prm = prm_of(case)
     ys = oracle.out_shape(case[1], case[2], case[3], case[4], case[5], case[6], case[7])
     t = workloads.make_tensors(ys, case[2], 0, False, "f16", "uniform", "uniform", "uniform", 62)
-    for route in ["auto", "naive", "phase_gemm"]:
+    for route in ["auto", "naive", "phase_gemm", "direct"]:
         try:
             pl = C.get_plan(case[1], case[2], case[3], case[4], case[5], case[6], case[7], False,
                             "f16", "auto", route)

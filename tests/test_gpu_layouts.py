@@ -79,7 +79,7 @@ def test_filter_layouts_forward_and_backward(case, layout, flipped):
     dref, _ = oracle.backward_data(dyt.x, tens.w, xs, s, p, d, op, g, with_scale=False)
     dexp = dref if dt == "f32" else rne_bf16(dref)
     dy = to_device(dyt.x_dev, dt)
-    for route in ["auto", "naive", "phase_gemm"]:
+    for route in ["auto", "naive", "phase_gemm", "direct"]:
         try:
             pl = C.get_plan(xs, ws, s, p, d, op, g, False, dt, "auto", route, layout, flipped)
         except C.ConvtError as e:

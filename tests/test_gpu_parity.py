@@ -331,25 +331,31 @@ def test_deterministic_and_stream_independent():
     assert np.array_equal(y1, y2)
 
 
-def test_prepared_split_matches_forward():
+# convt_forward runs the two-byte GEMM's weight reorder and input copy as one
+# launch; the split API runs them as two. Both must give the same bytes, on
+# planes of whole 16-byte rows (the copy through LDS) and others.
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("hw", [(11, 13), (8, 16)])
+def test_prepared_split_matches_forward(dt, hw):
     import torch
-    wl = workloads.get("c4b")
-    tens = workloads.make_tensors((2, 40, 11, 13), (40, 40, 3, 3), 40, True, "bf16", "uniform",
+    xs = (2, 40) + hw
+    tens = workloads.make_tensors(xs, (40, 40, 3, 3), 40, True, dt, "uniform",
                                   "uniform", "uniform", 6)
     prm = dict(stride=(1, 1), padding=(2, 2), dilation=(2, 2), output_padding=(0, 0), groups=1)
-    say("[gpu] prepare_weights + forward_prepared")
+    say(f"[gpu] prepare_weights + forward_prepared {dt} {hw}")
     y_ref, pl = run_gpu(tens, prm)
-    x = to_device(tens.x_dev, "bf16")
-    w = to_device(tens.w_dev, "bf16")
-    b = to_device(tens.bias_dev, "bf16")
+    assert pl.route == "phase_gemm"
+    x = to_device(tens.x_dev, dt)
+    w = to_device(tens.w_dev, dt)
+    b = to_device(tens.bias_dev, dt)
     ws = pl.new_workspace(x.device)
     y = pl.new_output(x.device)
     st = torch.cuda.current_stream().cuda_stream
     pl.prepare_weights_ptr(w.data_ptr(), ws.data_ptr(), st)
     pl.forward_prepared_ptr(x.data_ptr(), w.data_ptr(), b.data_ptr(), y.data_ptr(), ws.data_ptr(), st)
     # the prepared weights serve a second input too
-    x2 = to_device(workloads.make_tensors((2, 40, 11, 13), (40, 40, 3, 3), 40, True, "bf16",
-                                          "uniform", "uniform", "uniform", 7).x_dev, "bf16")
+    x2 = to_device(workloads.make_tensors(xs, (40, 40, 3, 3), 40, True, dt,
+                                          "uniform", "uniform", "uniform", 7).x_dev, dt)
     y2 = pl.new_output(x.device)
     pl.forward_prepared_ptr(x2.data_ptr(), w.data_ptr(), b.data_ptr(), y2.data_ptr(), ws.data_ptr(), st)
     torch.cuda.synchronize()

@@ -858,13 +858,14 @@ hipError_t launch_naive_bwd(const Plan &pl, const void *dy, const void *w, void 
 // where the tap falls outside dy or the channel is padding, so the loads
 // carry no branches and issue together.
 // ---------------------------------------------------------------------------
-template <typename T, int CI>
+template <typename T, int CI, int PX>
 __global__ __launch_bounds__(256) void direct_bwd_kernel(DevParams p, const T *__restrict__ dy,
                                                           const T *__restrict__ w,
                                                           T *__restrict__ dx) {
     extern __shared__ __attribute__((aligned(16))) float dslab[];
     const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
-    const int ntile = (p.x_plane + kDirPos - 1) / kDirPos;
+    constexpr int BP = kDirPos * PX;  // dx positions per block
+    const int ntile = (p.x_plane + BP - 1) / BP;
     int bid = blockIdx.x;
     const int tile = bid % ntile;
     bid /= ntile;
@@ -885,74 +886,109 @@ __global__ __launch_bounds__(256) void direct_bwd_kernel(DevParams p, const T *_
                            k2 * a2.D);
     }
     __syncthreads();
-    const int i = tile * kDirPos + threadIdx.x;
-    if (i >= p.x_plane) return;
-    const int i2 = i % a2.I, i1 = (i / a2.I) % a1.I, i0 = i / (a2.I * a1.I);
-    // dy coordinates reached by tap 0
-    const int e0 = i0 * a0.S - a0.P, e1 = i1 * a1.S - a1.P, e2 = i2 * a2.S - a2.P;
-    const int base = (e0 * a1.O + e1) * a2.O + e2;
+    // this lane's PX dx positions, 256 apart; dy coordinates of tap 0 (a
+    // position past the plane gets coordinates no tap can bring inside)
+    const int i_lane = tile * BP + threadIdx.x;
+    if (i_lane >= p.x_plane) return;
+    int e0[PX], e1[PX], e2[PX], base[PX];
+#pragma unroll
+    for (int q = 0; q < PX; ++q) {
+        const int i = i_lane + q * kDirPos;
+        const int i2 = i % a2.I, i1 = (i / a2.I) % a1.I, i0 = i / (a2.I * a1.I);
+        const bool in = i < p.x_plane;
+        e0[q] = in ? i0 * a0.S - a0.P : -(1 << 29);
+        e1[q] = i1 * a1.S - a1.P;
+        e2[q] = i2 * a2.S - a2.P;
+        base[q] = in ? (e0[q] * a1.O + e1[q]) * a2.O + e2[q] : 0;
+    }
     constexpr uint32_t ES = sizeof(T);
     const uint32_t ypl_bytes = (uint32_t)p.y_plane * ES;
     const __amdgpu_buffer_rsrc_t ys =
         make_rsrc(dy + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane, (uint32_t)Cog * ypl_bytes);
-    T *dxb = dx + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane + i;
+    T *dxb = dx + ((int64_t)b * p.Ci + (int64_t)g * Cig) * p.x_plane + i_lane;
     for (int ci0 = 0; ci0 < Cig; ci0 += CI) {
-        float acc[CI];
+        float acc[PX][CI];
 #pragma unroll
-        for (int c = 0; c < CI; ++c) acc[c] = 0.0f;
+        for (int q = 0; q < PX; ++q)
+#pragma unroll
+            for (int c = 0; c < CI; ++c) acc[q][c] = 0.0f;
         for (int kk = 0; kk < ktot; ++kk) {
             const int4 t = tk[kk];
-            const int o0 = e0 + t.y, o1 = e1 + t.z, o2 = e2 + t.w;
-            const bool ok = o0 >= 0 && o0 < a0.O && o1 >= 0 && o1 < a1.O && o2 >= 0 && o2 < a2.O;
-            const uint32_t off = (uint32_t)(base + t.x) * ES;
+            bool ok[PX];
+            uint32_t off[PX];
+#pragma unroll
+            for (int q = 0; q < PX; ++q) {
+                const int o0 = e0[q] + t.y, o1 = e1[q] + t.z, o2 = e2[q] + t.w;
+                ok[q] = o0 >= 0 && o0 < a0.O && o1 >= 0 && o1 < a1.O && o2 >= 0 && o2 < a2.O;
+                off[q] = (uint32_t)(base[q] + t.x) * ES;
+            }
             const float *wk = dslab + (kk * cog8) * cip + ci0;
             for (int oc0 = 0; oc0 < Cog; oc0 += 8) {
-                float yv[8];
+                float yv[PX][8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t o = (ok && oc0 + u < Cog) ? off + (uint32_t)(oc0 + u) * ypl_bytes : kOutOfRange;
-                    if constexpr (ES == 4)
-                        yv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ys, o, 0, 0));
-                    else if constexpr (std::is_same<T, _Float16>::value)
-                        yv[u] = half_to_f32<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0));
-                    else
-                        yv[u] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0));
-                }
+                for (int q = 0; q < PX; ++q)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t o =
+                            (ok[q] && oc0 + u < Cog) ? off[q] + (uint32_t)(oc0 + u) * ypl_bytes : kOutOfRange;
+                        if constexpr (ES == 4)
+                            yv[q][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ys, o, 0, 0));
+                        else if constexpr (std::is_same<T, _Float16>::value)
+                            yv[q][u] = half_to_f32<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0));
+                        else
+                            yv[q][u] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0));
+                    }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const float *wr = wk + (oc0 + u) * cip;
 #pragma unroll
                     for (int c4 = 0; c4 < CI; c4 += 4) {
                         const float4 wv = *(const float4 *)(wr + c4);
-                        acc[c4] += yv[u] * wv.x;
-                        acc[c4 + 1] += yv[u] * wv.y;
-                        acc[c4 + 2] += yv[u] * wv.z;
-                        acc[c4 + 3] += yv[u] * wv.w;
+#pragma unroll
+                        for (int q = 0; q < PX; ++q) {
+                            acc[q][c4] += yv[q][u] * wv.x;
+                            acc[q][c4 + 1] += yv[q][u] * wv.y;
+                            acc[q][c4 + 2] += yv[q][u] * wv.z;
+                            acc[q][c4 + 3] += yv[q][u] * wv.w;
+                        }
                     }
                 }
             }
         }
 #pragma unroll
-        for (int c = 0; c < CI; ++c)
-            if (ci0 + c < Cig) dxb[(int64_t)(ci0 + c) * p.x_plane] = from_f32<T>(acc[c]);
+        for (int q = 0; q < PX; ++q)
+            if (i_lane + q * kDirPos < p.x_plane)
+#pragma unroll
+                for (int c = 0; c < CI; ++c)
+                    if (ci0 + c < Cig)
+                        dxb[(int64_t)(ci0 + c) * p.x_plane + q * kDirPos] = from_f32<T>(acc[q][c]);
     }
 }
 
+// One dx position per lane: the kernel is bound by the latency of its dy
+// loads, which more lanes cover; two or four positions per lane (each LDS
+// weight read serving all of them) measured slower on the grouped workload
+// (90 against 80 us) and on small planes, where blocks become few.
+constexpr int kDirBwdPx = 1;
 template <typename T>
-static void launch_direct_bwd_t(const DevParams &p, int64_t blocks, int64_t lds, const void *dy,
-                                const void *w, void *dx, hipStream_t stream) {
-    switch (tiles::dir_bwd_ci(p.Cig)) {
+static void launch_direct_bwd_t(const DevParams &p, int64_t lds, const void *dy, const void *w,
+                                void *dx, hipStream_t stream) {
+    const int ci = tiles::dir_bwd_ci(p.Cig);
+    const int px = kDirBwdPx;
+    const int64_t ntile = (p.x_plane + (int64_t)kDirPos * px - 1) / ((int64_t)kDirPos * px);
+    const dim3 grid((unsigned)(ntile * p.G * p.B));
+    switch (ci) {
         case 4:
-            hipLaunchKernelGGL((direct_bwd_kernel<T, 4>), dim3((unsigned)blocks), dim3(256), lds, stream, p,
+            hipLaunchKernelGGL((direct_bwd_kernel<T, 4, kDirBwdPx>), grid, dim3(256), lds, stream, p,
                                (const T *)dy, (const T *)w, (T *)dx);
             break;
         case 8:
-            hipLaunchKernelGGL((direct_bwd_kernel<T, 8>), dim3((unsigned)blocks), dim3(256), lds, stream, p,
+            hipLaunchKernelGGL((direct_bwd_kernel<T, 8, kDirBwdPx>), grid, dim3(256), lds, stream, p,
                                (const T *)dy, (const T *)w, (T *)dx);
             break;
         default:
-            hipLaunchKernelGGL((direct_bwd_kernel<T, 16>), dim3((unsigned)blocks), dim3(256), lds, stream,
-                               p, (const T *)dy, (const T *)w, (T *)dx);
+            hipLaunchKernelGGL((direct_bwd_kernel<T, 16, kDirBwdPx>), grid, dim3(256), lds, stream, p,
+                               (const T *)dy, (const T *)w, (T *)dx);
             break;
     }
 }
@@ -960,7 +996,7 @@ static void launch_direct_bwd_t(const DevParams &p, int64_t blocks, int64_t lds,
 hipError_t launch_direct_bwd(const Plan &pl, const void *dy, const void *w, void *dx,
                              hipStream_t stream) {
     const DevParams &p = pl.dp;  // the forward problem's axes and channels
-    const int64_t ntile = (p.x_plane + kDirPos - 1) / kDirPos;
+    const int64_t ntile = (p.x_plane + kDirPos - 1) / kDirPos;  // (at most; fewer with PX > 1)
     const int64_t blocks = ntile * p.G * p.B;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -969,11 +1005,11 @@ hipError_t launch_direct_bwd(const Plan &pl, const void *dy, const void *w, void
     if (lds > tiles::kDirBwdLdsBytes || (int64_t)p.Cog * p.y_plane * pl.elem_bytes >= ((int64_t)1 << 31))
         return hipErrorInvalidConfiguration;
     if (pl.elem_bytes == 2 && p.f16)
-        launch_direct_bwd_t<_Float16>(p, blocks, lds, dy, w, dx, stream);
+        launch_direct_bwd_t<_Float16>(p, lds, dy, w, dx, stream);
     else if (pl.elem_bytes == 2)
-        launch_direct_bwd_t<uint16_t>(p, blocks, lds, dy, w, dx, stream);
+        launch_direct_bwd_t<uint16_t>(p, lds, dy, w, dx, stream);
     else
-        launch_direct_bwd_t<float>(p, blocks, lds, dy, w, dx, stream);
+        launch_direct_bwd_t<float>(p, lds, dy, w, dx, stream);
     return hipGetLastError();
 }
 

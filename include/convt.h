@@ -201,8 +201,10 @@ convt_status convt_plan(const convt_problem *problem, convt_plan_t *out, convt_p
  * otherwise. workspace: device memory of at least info.workspace_bytes bytes
  * (NULL allowed when that is 0), 16-byte aligned; it must not be used by
  * another call until this call's work on `stream` has finished. y must not
- * overlap x, W, bias or the workspace. Runs convt_prepare_weights and then
- * convt_forward_prepared.
+ * overlap x, W, bias or the workspace. Same result, byte for byte, as
+ * convt_prepare_weights followed by convt_forward_prepared; for two-byte
+ * element types on the PHASE_GEMM route it runs their weight reorder and
+ * input copy as one launch.
  */
 convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, const void *bias,
                            void *y, void *workspace, void *stream);

@@ -93,7 +93,7 @@ def stored_traffic(route: str, wl_name: str):
     return float(m_tr.group(1))
 
 
-def cpu_baseline(wl: workloads.Workload, tens: workloads.Tensors, target_s: float = 15.0):
+def cpu_baseline(wl: workloads.Workload, tens: workloads.Tensors, target_s: float = 20.0):
     """The oracle (untuned) on the host cores, on a batch subset of the
     workload sized to roughly target_s seconds (at least one batch item; the
     whole batch repeated if it is faster than that)."""

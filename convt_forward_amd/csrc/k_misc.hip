@@ -650,6 +650,19 @@ hipError_t launch_naive(const Plan &pl, const void *x, const void *w, const void
 // ---------------------------------------------------------------------------
 constexpr int kDirPos = 256;
 
+// c + a.lo * b.lo + a.hi * b.hi for two 16-bit values per word (bfloat16 or
+// half by T), products and sum in float32 (the two-element dot instructions)
+template <typename T>
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float c) {
+    if constexpr (std::is_same<T, _Float16>::value) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
+    }
+}
+
 template <typename T, bool ACT, bool XS>
 __global__ __launch_bounds__(256) void direct_kernel(DevParams p, const T *__restrict__ x,
                                                       const T *__restrict__ w,
@@ -873,10 +886,29 @@ __global__ __launch_bounds__(256) void direct_bwd_kernel(DevParams p, const T *_
     const int b = bid / p.G;
     const int ktot = p.ktot, Cog = p.Cog, Cig = p.Cig;
     const int cog8 = (Cog + 7) / 8 * 8, cip = (Cig + CI - 1) / CI * CI;
-    const int slab_n = ktot * cog8 * cip;  // (tiles::dir_bwd_lds_bytes: 4 * slab_n + 16 * ktot)
-    for (int e = threadIdx.x; e < slab_n; e += 256) {
-        const int cil = e % cip, r = e / cip, ocl = r % cog8, kk = r / cog8;
-        dslab[e] = (ocl < Cog && cil < Cig) ? to_f32(w[w_offset(p, g * Cig + cil, ocl, kk)]) : 0.0f;
+    // Two-byte types (HP): 32-bit words holding the weights of one input
+    // channel for two neighbouring output channels (raw 16-bit values), so
+    // that a two-element dot instruction takes a pair of dy channels at once:
+    // half the LDS reads and half the VALU work of float32 products.
+    constexpr bool HP = sizeof(T) == 2;
+    const int slab_n = HP ? ktot * (cog8 / 2) * cip : ktot * cog8 * cip;  // 32-bit words
+    if constexpr (HP) {
+        uint32_t *ws32 = (uint32_t *)dslab;
+        for (int e = threadIdx.x; e < slab_n; e += 256) {
+            const int cil = e % cip, r = e / cip, pr = r % (cog8 / 2), kk = r / (cog8 / 2);
+            uint32_t lo = 0, hi = 0;
+            if (cil < Cig) {
+                if (2 * pr < Cog) lo = __builtin_bit_cast(uint16_t, w[w_offset(p, g * Cig + cil, 2 * pr, kk)]);
+                if (2 * pr + 1 < Cog)
+                    hi = __builtin_bit_cast(uint16_t, w[w_offset(p, g * Cig + cil, 2 * pr + 1, kk)]);
+            }
+            ws32[e] = lo | hi << 16;
+        }
+    } else {
+        for (int e = threadIdx.x; e < slab_n; e += 256) {
+            const int cil = e % cip, r = e / cip, ocl = r % cog8, kk = r / cog8;
+            dslab[e] = (ocl < Cog && cil < Cig) ? to_f32(w[w_offset(p, g * Cig + cil, ocl, kk)]) : 0.0f;
+        }
     }
     // per tap: dy offset from the tap-0 position, then the per-axis shifts
     int4 *tk = (int4 *)(dslab + slab_n);
@@ -924,6 +956,39 @@ __global__ __launch_bounds__(256) void direct_bwd_kernel(DevParams p, const T *_
             }
             const float *wk = dslab + (kk * cog8) * cip + ci0;
             for (int oc0 = 0; oc0 < Cog; oc0 += 8) {
+                if constexpr (HP) {
+                    // dy channel pairs (oc0 + 2pp, oc0 + 2pp + 1) as raw 16-bit pairs
+                    uint32_t yp[PX][4];
+#pragma unroll
+                    for (int q = 0; q < PX; ++q)
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp) {
+                            uint32_t h[2];
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) {
+                                const int u = 2 * pp + e;
+                                const uint32_t o = (ok[q] && oc0 + u < Cog)
+                                                       ? off[q] + (uint32_t)(oc0 + u) * ypl_bytes
+                                                       : kOutOfRange;
+                                h[e] = __builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0);
+                            }
+                            yp[q][pp] = h[0] | h[1] << 16;
+                        }
+                    const uint32_t *wp = (const uint32_t *)dslab + (kk * (cog8 / 2) + oc0 / 2) * cip + ci0;
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+                        for (int c4 = 0; c4 < CI; c4 += 4) {
+                            const u32x4 wv = *(const u32x4 *)(wp + pp * cip + c4);
+#pragma unroll
+                            for (int q = 0; q < PX; ++q)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    acc[q][c4 + e] = dot2_acc<T>(yp[q][pp], wv[e], acc[q][c4 + e]);
+                        }
+                    }
+                    continue;
+                }
                 float yv[PX][8];
 #pragma unroll
                 for (int q = 0; q < PX; ++q)
@@ -931,12 +996,7 @@ __global__ __launch_bounds__(256) void direct_bwd_kernel(DevParams p, const T *_
                     for (int u = 0; u < 8; ++u) {
                         const uint32_t o =
                             (ok[q] && oc0 + u < Cog) ? off[q] + (uint32_t)(oc0 + u) * ypl_bytes : kOutOfRange;
-                        if constexpr (ES == 4)
-                            yv[q][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ys, o, 0, 0));
-                        else if constexpr (std::is_same<T, _Float16>::value)
-                            yv[q][u] = half_to_f32<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0));
-                        else
-                            yv[q][u] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ys, o, 0, 0));
+                        yv[q][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ys, o, 0, 0));
                     }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {

@@ -558,34 +558,51 @@ __global__ __launch_bounds__(tiles::kGemmCfg[CFG].nw * 64) __attribute__((amdgpu
         const __amdgpu_buffer_rsrc_t bs =
             make_rsrc(bias + g * p.Cog + co_w, p.has_bias ? (uint32_t)co_left * ES : 0u);
         const uint32_t lane_co = 4 * (lane >> 5);
+        // the stores, instantiated per activation code A (the switch on the
+        // activation runs once, outside the unrolled loops)
+        auto store_all = [&](auto act_tag) __attribute__((always_inline)) {
+            constexpr int A = decltype(act_tag)::value;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                // this lane's channel: mt*32 + 8*(j/4) + 4*(lane/32) + j%4
-                const uint32_t co_u = mt * 32 + 8 * (j >> 2) + (j & 3);
-                float bv;
-                if constexpr (ES == 2)
-                    bv = half_to_f32<HT>(__builtin_amdgcn_raw_buffer_load_b16(bs, (co_u + lane_co) * 2, 0, 0));
-                else
-                    bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (co_u + lane_co) * 4, 0, 0));
-                // rows past Cog (tile padding) store nothing: their channel
-                // offset could wrap the 32-bit range on large planes and
-                // land inside the slice; for real rows yoff + cbytes stays
-                // below 2^32 (the slice is below 2^31 bytes)
-                const bool row_ok = (int)(co_u + lane_co) < co_left;
-                const uint32_t cbytes = (co_u + lane_co) * ypl_bytes;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    float v = acc[mt][nt][j] + bv;
-                    if constexpr (ACT) v = activate<ES == 2>(act, v);
-                    const uint32_t off = row_ok ? yoff[nt] + cbytes : kOutOfRange;
+                for (int j = 0; j < 16; ++j) {
+                    // this lane's channel: mt*32 + 8*(j/4) + 4*(lane/32) + j%4
+                    const uint32_t co_u = mt * 32 + 8 * (j >> 2) + (j & 3);
+                    float bv;
                     if constexpr (ES == 2)
-                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_half<HT>(v), ys, off, 0, 0);
+                        bv = half_to_f32<HT>(__builtin_amdgcn_raw_buffer_load_b16(bs, (co_u + lane_co) * 2, 0, 0));
                     else
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ys, off, 0, 0);
+                        bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bs, (co_u + lane_co) * 4, 0, 0));
+                    // rows past Cog (tile padding) store nothing: their channel
+                    // offset could wrap the 32-bit range on large planes and
+                    // land inside the slice; for real rows yoff + cbytes stays
+                    // below 2^32 (the slice is below 2^31 bytes)
+                    const bool row_ok = (int)(co_u + lane_co) < co_left;
+                    const uint32_t cbytes = (co_u + lane_co) * ypl_bytes;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        float v = acc[mt][nt][j] + bv;
+                        if constexpr (A != CONVT_ACT_NONE) v = activate<ES == 2>(A, v);
+                        const uint32_t off = row_ok ? yoff[nt] + cbytes : kOutOfRange;
+                        if constexpr (ES == 2)
+                            __builtin_amdgcn_raw_buffer_store_b16(f32_to_half<HT>(v), ys, off, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ys, off, 0, 0);
+                    }
                 }
             }
+        };
+        if constexpr (ACT) {
+            switch (act) {
+                case CONVT_ACT_RELU: store_all(std::integral_constant<int, CONVT_ACT_RELU>{}); break;
+                case CONVT_ACT_SIGMOID: store_all(std::integral_constant<int, CONVT_ACT_SIGMOID>{}); break;
+                case CONVT_ACT_TANH: store_all(std::integral_constant<int, CONVT_ACT_TANH>{}); break;
+                case CONVT_ACT_SILU: store_all(std::integral_constant<int, CONVT_ACT_SILU>{}); break;
+                case CONVT_ACT_GELU: store_all(std::integral_constant<int, CONVT_ACT_GELU>{}); break;
+                default: store_all(std::integral_constant<int, CONVT_ACT_NONE>{}); break;
+            }
+        } else {
+            store_all(std::integral_constant<int, CONVT_ACT_NONE>{});
         }
     }
 }

@@ -331,8 +331,10 @@ class Plan:
 
     def forward(self, x, w, bias=None, y=None, workspace=None, stream=None):
         """Enqueue y = convT(x, w) + bias on `stream` (default: torch's current
-        stream of x's device). Allocates y / the workspace with torch when not
-        given. Returns y."""
+        stream of x's device; else a torch stream or a raw hipStream_t).
+        Allocates y / the workspace with torch when not given; those
+        allocations are recorded on `stream`, so the caching allocator does
+        not reuse their memory before the kernels there are done. Returns y."""
         import torch
         p = self.problem
         nd = self.ndim
@@ -344,18 +346,21 @@ class Plan:
             self._check(bias, (self.out_shape[1],), "bias")
         elif bias is not None:
             raise ValueError("the plan has no bias")
+        sh, ext = _launch_stream(stream, x.device)
+        owned = []
         if y is None:
             y = self.new_output(x.device)
+            owned.append(y)
         else:
             self._check(y, self.out_shape, "y")
         if workspace is None:
             workspace = self.new_workspace(x.device)
+            owned.append(workspace)
         elif workspace.numel() * workspace.element_size() < self.workspace_bytes:
             raise ValueError("workspace too small")
-        if stream is None:
-            stream = torch.cuda.current_stream(x.device).cuda_stream
         self.forward_ptr(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else 0,
-                         y.data_ptr(), workspace.data_ptr(), stream)
+                         y.data_ptr(), workspace.data_ptr(), sh)
+        _tie_to_stream(owned, ext)
         return y
 
     def new_input_grad(self, device):
@@ -369,26 +374,57 @@ class Plan:
 
     def backward_data(self, dy, w, dx=None, workspace=None, stream=None):
         """Enqueue dx = the gradient with respect to x for the upstream gradient
-        dy (shape out_shape). Allocates dx / the workspace with torch when not
-        given. Returns dx."""
+        dy (shape out_shape), on `stream` as in forward. Allocates dx / the
+        workspace with torch when not given (recorded on `stream`). Returns
+        dx."""
         import torch
         p = self.problem
         nd = self.ndim
         self._check(dy, self.out_shape, "dy")
         self._check(w, self.w_layout_shape, "w")
+        sh, ext = _launch_stream(stream, dy.device)
+        owned = []
         if dx is None:
             dx = self.new_input_grad(dy.device)
+            owned.append(dx)
         else:
             self._check(dx, tuple(p.x_shape[:2 + nd]), "dx")
         if workspace is None:
             workspace = self.new_bwd_workspace(dy.device)
+            owned.append(workspace)
         elif workspace.numel() * workspace.element_size() < self.bwd_workspace_bytes:
             raise ValueError("workspace too small")
-        if stream is None:
-            stream = torch.cuda.current_stream(dy.device).cuda_stream
         self.backward_data_ptr(dy.data_ptr(), w.data_ptr(), dx.data_ptr(), workspace.data_ptr(),
-                               stream)
+                               sh)
+        _tie_to_stream(owned, ext)
         return dx
+
+
+def _launch_stream(stream, device):
+    """(raw handle, torch stream object or None) of the stream a call launches
+    on: torch's current stream of `device` when `stream` is None (then None
+    is returned as the object: nothing needs tying), else `stream` as given
+    (a torch stream or a raw hipStream_t integer)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream, None
+    if isinstance(stream, torch.cuda.Stream):
+        obj = stream
+    else:
+        obj = torch.cuda.ExternalStream(int(stream), device=device)
+    if obj.cuda_stream == torch.cuda.current_stream(device).cuda_stream:
+        return obj.cuda_stream, None
+    return obj.cuda_stream, obj
+
+
+def _tie_to_stream(tensors, ext) -> None:
+    """Tensors allocated here (on torch's current stream) but used by kernels
+    enqueued on another stream: tell the caching allocator, so that their
+    memory is not handed out again before that stream's work completes."""
+    if ext is None:
+        return
+    for t in tensors:
+        t.record_stream(ext)
 
 
 _plan_cache: Dict[tuple, Plan] = {}

@@ -23,29 +23,16 @@ pytestmark = pytest.mark.gpu
 # The five workloads at their full sizes, in the launch configuration the
 # benchmark times (automatic route).
 # ---------------------------------------------------------------------------
-FULL_ORACLE = ["c1", "c2", "c4a"]
-SAMPLED = ["c3", "c4b", "c5"]
+FULL_ORACLE = ["c1", "c2", "c3", "c4a", "c4b", "c5"]
 
 
+# every output of every workload against the full oracle (the threaded
+# double-precision scatter takes seconds per workload on the host cores)
 @pytest.mark.parametrize("name", FULL_ORACLE)
 def test_workload_full_size_all_outputs(name):
     wl = workloads.get(name)
     tens = workloads.workload_tensors(wl)
     check_full(tens, params_of(wl), tag=wl.name)
-
-
-@pytest.mark.parametrize("name", SAMPLED)
-def test_workload_full_size_sampled(name):
-    wl = workloads.get(name)
-    tens = workloads.workload_tensors(wl)
-    prm = params_of(wl)
-    say(f"[gpu] {wl.name} full size, sampled outputs")
-    y, pl = run_gpu(tens, prm)
-    assert np.all(np.isfinite(y))
-    pts = sample_points(y.shape, np.random.default_rng(100))
-    e, _, _ = check_sampled(y, tens, prm, pts)
-    say(f"[gpu]   -> route {pl.route}, {len(pts)} points, max normalised error {e:.3e}")
-    assert e <= TOL[tens.dtype]
 
 
 # ---------------------------------------------------------------------------
@@ -329,6 +316,43 @@ def test_deterministic_and_stream_independent():
     s = torch.cuda.Stream()
     y2, _ = run_gpu(tens, prm, stream=s.cuda_stream)
     assert np.array_equal(y1, y2)
+
+
+# A call on a side stream that lets the binding allocate y and the workspace:
+# those allocations come from torch's current stream, and are freed (the
+# workspace) when the call returns while the kernels on the side stream may
+# still run. The binding records them on the side stream; without that, the
+# buffer allocated and filled on the current stream right after the call
+# could take the workspace's memory under the running GEMM.
+@pytest.mark.parametrize("as_handle", [False, True])
+def test_side_stream_allocations_not_reused(as_handle):
+    import torch
+    wl = workloads.get("c3")
+    tens = workloads.workload_tensors(wl)
+    prm = params_of(wl)
+    say(f"[gpu] c3 side stream, binding-allocated buffers (handle={as_handle})")
+    y_ref, pl = run_gpu(tens, prm)
+    x = to_device(tens.x_dev, "bf16")
+    w = to_device(tens.w_dev, "bf16")
+    b = to_device(tens.bias_dev, "bf16")
+    side = torch.cuda.Stream()
+    # the side stream starts behind a long busy kernel, so that the
+    # convolution is still queued when the host returns
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        busy = torch.randn(4096, 4096, device="cuda")
+        for _ in range(8):
+            busy = busy @ busy
+            busy /= busy.norm()
+    y = pl.forward(x, w, b, stream=side.cuda_stream if as_handle else side)
+    junk = []
+    for _ in range(4):
+        t = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device="cuda")
+        t.fill_(0x5a)
+        junk.append(t)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host64(y), y_ref)
+    del busy, junk
 
 
 # convt_forward runs the two-byte GEMM's weight reorder and input copy as one

@@ -47,13 +47,15 @@ PEAK_HBM_GBS = 8000.0
 
 # the source files whose change invalidates stored PMC traffic figures
 KERNEL_SOURCES = {
-    "phase_gemm": ["k_phase_gemm.hip", "kcommon.h", "convt_internal.h", "plan.cpp"],
+    "phase_gemm": ["k_gemm_nchw.hip", "k_phase_gemm.hip", "kcommon.h", "convt_internal.h", "plan.cpp"],
+    "phase_gemm_packed": ["k_phase_gemm.hip", "kcommon.h", "convt_internal.h", "plan.cpp"],
     "grouped": ["k_grouped.hip", "kcommon.h", "plan.cpp"],
     "direct": ["k_misc.hip", "kcommon.h", "plan.cpp"],
     "naive": ["k_misc.hip", "kcommon.h", "plan.cpp"],
 }
 KERNEL_SYMBOL = {
     "phase_gemm": "phase_gemm_kernel",
+    "phase_gemm_packed": "phase_gemm_kernel",
     "grouped": "grouped_kernel",
     "direct": "direct_kernel",
     "naive": "naive_kernel",
@@ -195,6 +197,8 @@ def main() -> int:
     ap.add_argument("--activation", default="none",
                     choices=["none", "relu", "sigmoid", "tanh", "silu", "gelu"],
                     help="activation fused after the bias (default none, as the workloads)")
+    ap.add_argument("--route", default="auto",
+                    help="force a forward route (convt_route name, e.g. phase_gemm_packed)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-data (input gradient) measurement")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -219,7 +223,7 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pl = C.get_plan(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.dilation,
-                    wl.output_padding, wl.groups, wl.has_bias, wl.dtype,
+                    wl.output_padding, wl.groups, wl.has_bias, wl.dtype, route=args.route,
                     activation=args.activation)
 
     def to_dev(a):
@@ -306,7 +310,7 @@ def main() -> int:
     flops = useful_flops(wl)
     abytes = algorithmic_bytes(wl, pl.out_shape)
     route = pl.route
-    if route in ("phase_gemm", "direct", "naive") and wl.dtype in PEAK_TFLOPS and \
+    if route in ("phase_gemm", "phase_gemm_packed", "direct", "naive") and wl.dtype in PEAK_TFLOPS and \
             flops / abytes > 50.0:
         bound, unit = "mfma", "TFLOP/s"
         achieved = flops / kern_s / 1e12
@@ -318,9 +322,11 @@ def main() -> int:
     traffic = stored_traffic(route, wl.name)
     kernel = KERNEL_SYMBOL.get(route, route)
     if route == "phase_gemm" and wl.dtype != "f32":
-        # the two-byte GEMM reads a channel-chunked copy of x that a pack
+        kernel = "phase_gemm_nchw_kernel"
+    if route == "phase_gemm_packed":
+        # the packed GEMM reads a channel-chunked copy of x that a pack
         # kernel writes inside the same forward call: kernel_us covers both
-        kernel = "pack_x_kernel+" + kernel
+        kernel = "pack_x_kernel+phase_gemm_kernel"
     roofline = {
         "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
         "frac": achieved / peak, "traffic": traffic,

@@ -24,7 +24,14 @@ int64_t numel(const int64_t *shape, int n) {
 convt_status device_status(hipError_t e) { return e == hipSuccess ? CONVT_OK : CONVT_ERR_DEVICE; }
 
 bool needs_weights_in_workspace(int route) {
-    return route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_GROUPED;
+    return route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_PHASE_GEMM_PACKED ||
+           route == CONVT_ROUTE_GROUPED;
+}
+
+// The two-byte phase GEMM that reads x in place takes neighbouring positions
+// in pairs as 32-bit words.
+bool x_misaligned(const convt::Plan &pl, const void *x) {
+    return pl.route == CONVT_ROUTE_PHASE_GEMM && pl.dp.gemm_nchw && ((uintptr_t)x % 4) != 0;
 }
 
 }  // namespace
@@ -80,8 +87,13 @@ convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void
         case CONVT_ROUTE_DIRECT:
             if (!w) return CONVT_ERR_INVALID_ARGUMENT;
             return device_status(convt::launch_direct(pl, x, w, bias, y, s));
-        case CONVT_ROUTE_PHASE_GEMM: {
+        case CONVT_ROUTE_PHASE_GEMM:
+        case CONVT_ROUTE_PHASE_GEMM_PACKED: {
             if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
+            if (pl.dp.gemm_nchw) {
+                if (x_misaligned(pl, x)) return CONVT_ERR_INVALID_ARGUMENT;
+                return device_status(convt::launch_phase_gemm_nchw(pl, x, workspace, bias, y, s));
+            }
             const void *xin = x;
             if (pl.xp_bytes > 0) {
                 // bfloat16: stage the channel-chunked copy of x after the weights
@@ -114,7 +126,8 @@ convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, cons
     if (needs_weights_in_workspace(pl.route) &&
         (!workspace || ((uintptr_t)workspace % 16) != 0))
         return CONVT_ERR_INVALID_ARGUMENT;
-    if (pl.route == CONVT_ROUTE_PHASE_GEMM && pl.xp_bytes > 0 && pl.wr_elems > 0) {
+    if (x_misaligned(pl, x)) return CONVT_ERR_INVALID_ARGUMENT;
+    if (pl.route == CONVT_ROUTE_PHASE_GEMM_PACKED && pl.xp_bytes > 0 && pl.wr_elems > 0) {
         // two-byte elements: the weight reorder and the channel-chunked copy
         // of x in one launch, then the GEMM
         const hipStream_t s = (hipStream_t)stream;
@@ -179,6 +192,7 @@ const char *convt_route_name(int32_t route) {
         case CONVT_ROUTE_NONE: return "none";
         case CONVT_ROUTE_FILL: return "fill";
         case CONVT_ROUTE_PHASE_GEMM: return "phase_gemm";
+        case CONVT_ROUTE_PHASE_GEMM_PACKED: return "phase_gemm_packed";
         case CONVT_ROUTE_GROUPED: return "grouped";
         case CONVT_ROUTE_DIRECT: return "direct";
         case CONVT_ROUTE_NAIVE: return "naive";
@@ -217,6 +231,6 @@ convt_status convt_plan_axis_phase(convt_plan_t plan, int32_t axis, int64_t resi
     return CONVT_OK;
 }
 
-int32_t convt_version(void) { return 200; }
+int32_t convt_version(void) { return 300; }
 
 }  // extern "C"

@@ -83,6 +83,10 @@ struct DevParams {
     int32_t ktot_pad;          // taps per group in the reordered weights (phase GEMM: each
                                // phase padded with zero taps to a multiple of gemm_gs)
     int32_t ph_tab_ok;         // 1: ph[] holds every phase (nphase <= kMaxPhaseTab)
+    int32_t gemm_nchw;         // phase GEMM: 1 = two-byte kernel reading x in NC[D]HW directly
+    int32_t nchw_cfg;          // ... its configuration (tiles::kNchwCfg)
+    int32_t nchw_wgm;          // ... its waves along the output channels (1: 128 rows, 2: 256)
+    int32_t nchw_xcap;         // ... halo positions one LDS halo buffer holds
     int32_t bwd_nstages;       // backward-data GEMM: pipeline stages of a block (all phases)
     int32_t bwd_nlive;         // backward-data GEMM: phases with taps
     uint8_t bwd_live[kMaxPhaseTab];  // their indices, ascending
@@ -185,6 +189,32 @@ static_assert(gemm_lds_bytes(kGemmCfg[5], 4) <= gemm_lds_budget(kGemmCfg[5]), "L
 
 static_assert(gemm_halo_cap(kGemmCfg[0], 4) >= 256 && gemm_halo_cap(kGemmCfg[5], 4) >= 128,
               "halo buffers hold at least the tile");
+// Two-byte phase GEMM reading x directly (k_gemm_nchw.hip): four waves of
+// 128 x 128 accumulators, WGM of them along the output channels; a stage is
+// one 16-channel chunk with all GS taps of the phase. LDS: two stages of
+// weight tiles [GS][128 * WGM][32 bytes], two halo buffers of xcap rows of
+// 32 bytes, and the block's bias in float32. A thread stages at most
+// kNchwMaxUnits halo units (2 positions x 8 channels) per stage.
+constexpr int kNchwMaxUnits = 4;
+constexpr int kNchwLds = 160 * 1024;
+constexpr int64_t nchw_lds_bytes(int wgm, int gs, int xu) {
+    return 2 * (int64_t)gs * 128 * wgm * 32 + 2 * (int64_t)xu * 256 * 32 + 128 * wgm * 4;
+}
+struct NchwCfg {
+    int wgm;  // waves along the output channels (block rows 128 * wgm)
+    int gs;   // taps per stage (every phase padded to it)
+    int xu;   // halo units per thread (the halo holds at most 256 * xu positions)
+};
+constexpr int kNchwCfgCount = 4;
+constexpr NchwCfg kNchwCfg[kNchwCfgCount] = {
+    {2, 4, 2},  // 0: 2-D kernel 4 stride 2 (2 x 2 taps per phase), C_out/groups > 128
+    {1, 4, 2},  // 1: the same, C_out/groups <= 128
+    {1, 8, 4},  // 2: 3-D kernel 4 stride 2 (2 x 2 x 2 taps per phase)
+    {1, 9, 3},  // 3: 2-D kernel 3 stride 1 (3 x 3 taps)
+};
+static_assert(nchw_lds_bytes(2, 4, 2) <= kNchwLds && nchw_lds_bytes(1, 8, 4) <= kNchwLds &&
+                  nchw_lds_bytes(1, 9, 3) <= kNchwLds,
+              "LDS");
 // Grouped route
 constexpr int kGrpThreads = 256;
 constexpr int kGrpCog = 16;           // MFMA N (output channels of a group, padded)

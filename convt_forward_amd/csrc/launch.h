@@ -18,6 +18,9 @@ hipError_t launch_direct(const Plan &pl, const void *x, const void *w, const voi
 // wr: the workspace (reordered weights at offset 0, tap table at tab_offset)
 hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, const void *bias,
                              void *y, hipStream_t stream);
+// two-byte phase GEMM reading x in NC[D]HW (plans with dp.gemm_nchw)
+hipError_t launch_phase_gemm_nchw(const Plan &pl, const void *x, const void *wr, const void *bias,
+                                  void *y, hipStream_t stream);
 hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const void *bias, void *y,
                           hipStream_t stream);
 

@@ -311,6 +311,101 @@ bool gemm_eligible(const DevParams &dp, int dtype, int ndim, bool bwd = false) {
     return pick_gemm_cfg(&tmp, dtype, ndim, bwd) >= 0;
 }
 
+// ---- two-byte phase GEMM reading x in NC[D]HW ------------------------------
+// Halo extents of phase P for a (T0, T1, T2) box: the box grown by the
+// phase's tap span per axis; on the last axis the halo starts at the
+// phase's first offset rounded down to even and its width is rounded up to
+// even (the kernel reads x in pairs of positions).
+int64_t nchw_halo(const DevParams &dp, int P, int T0, int T1, int T2) {
+    const PhaseRec &pr = dp.ph[P];
+    const int n0 = pr.rn[0] >> 8, n1 = pr.rn[1] >> 8, n2 = pr.rn[2] >> 8;
+    const int off2 = pr.qo[2] >> 16;
+    const int64_t E0 = T0 + (int64_t)(n0 > 0 ? n0 - 1 : 0) * dp.ax[0].ostep;
+    const int64_t E1 = T1 + (int64_t)(n1 > 0 ? n1 - 1 : 0) * dp.ax[1].ostep;
+    int64_t E2 = T2 + (int64_t)(n2 > 0 ? n2 - 1 : 0) * dp.ax[2].ostep + (off2 & 1);
+    E2 = (E2 + 1) & ~(int64_t)1;
+    return E0 * E1 * E2;
+}
+
+// Choose the kernel's configuration (tiles::kNchwCfg: waves along C_out,
+// taps per stage, halo units per thread) and q box for a forward problem
+// with a two-byte element type, or return false if the problem does not
+// suit it: an odd x row length (pairs of positions must lie within one
+// row), phases whose tap counts no configuration takes without padding more
+// than a third, at most 64 output channels per group (half of the 128-row
+// tiles would be padding) or no box whose halo the per-thread staging holds.
+bool choose_nchw(DevParams *dp, int ndim) {
+    if (!strides_fit(*dp) || !slices_fit(*dp, 2)) return false;
+    if (dp->ax[2].I % 2 != 0 || dp->Cog <= 64) return false;
+    // the stores address rows up to 256 past a wave's first channel, and
+    // masked positions sit 2^31 out; every such offset stays below 2^32; the
+    // input channels are padded to whole pairs of 16-channel chunks
+    if (!buffer_fits(((int64_t)dp->Cog + 256) * dp->y_plane * 2)) return false;
+    if (!buffer_fits(((int64_t)dp->Cig + 31) * dp->x_plane * 2)) return false;
+    int maxt = 0;
+    int64_t taps = 0;
+    for (int P = 0; P < dp->nphase; ++P) {
+        maxt = std::max(maxt, (int)dp->ph[P].ntaps);
+        taps += dp->ph[P].ntaps;
+    }
+    double best = 0;
+    int bcfg = -1, bd = 0, bh = 0, bw = 0;
+    int64_t bcap = 0;
+    for (int c = 0; c < tiles::kNchwCfgCount; ++c) {
+        const tiles::NchwCfg &cf = tiles::kNchwCfg[c];
+        if (cf.gs < maxt) continue;
+        // the padding taps run MFMAs on zero weights: at most a third extra
+        if ((int64_t)cf.gs * dp->nphase * 3 > taps * 4) continue;
+        const int BN = 4 / cf.wgm * 128;
+        const int64_t co_tiles = ceil_div(dp->Cog, 128 * cf.wgm);
+        for (int tw = 16; tw <= BN; tw *= 2) {
+            for (int th = 1; th * tw <= BN; th *= 2) {
+                const int td = BN / (th * tw);
+                if (td * th * tw != BN) continue;
+                if (ndim < 3 && td != 1) continue;
+                if (ndim < 2 && th != 1) continue;
+                int64_t cap = 0;
+                for (int P = 0; P < dp->nphase; ++P)
+                    cap = std::max(cap, nchw_halo(*dp, P, td, th, tw));
+                if (cap > (int64_t)256 * cf.xu) continue;
+                const int64_t nt = ceil_div(dp->ax[0].qmax, td) * ceil_div(dp->ax[1].qmax, th) *
+                                   ceil_div(dp->ax[2].qmax, tw);
+                const int64_t blocks = nt * co_tiles * dp->nphase * dp->G * dp->B;
+                // blocks run one per CU; a block's time per chunk: its MFMAs
+                // (512 cycles per tap per wave, scaled by the rows it holds)
+                // plus the halo it stages
+                const double rounds = std::ceil((double)blocks / 256.0);
+                const double t = rounds * (512.0 * cf.gs * cf.wgm + 2.0 * cap + 300.0) / cf.wgm;
+                if (bcfg < 0 || t < best * 0.999) {
+                    best = t;
+                    bcfg = c;
+                    bd = td;
+                    bh = th;
+                    bw = tw;
+                    bcap = cap;
+                }
+            }
+        }
+    }
+    if (bcfg < 0) return false;
+    dp->gemm_nchw = 1;
+    dp->nchw_cfg = bcfg;
+    dp->nchw_wgm = tiles::kNchwCfg[bcfg].wgm;
+    dp->nchw_xcap = (int32_t)bcap;
+    dp->gemm_gs = tiles::kNchwCfg[bcfg].gs;
+    dp->gemm_cfg = 0;
+    dp->td = bd;
+    dp->th = bh;
+    dp->tw = bw;
+    dp->hd = bd + dp->ax[0].span_max;
+    dp->hh = bh + dp->ax[1].span_max;
+    dp->hw = bw + dp->ax[2].span_max;
+    dp->nt_d = (int32_t)ceil_div(dp->ax[0].qmax, bd);
+    dp->nt_h = (int32_t)ceil_div(dp->ax[1].qmax, bh);
+    dp->nt_w = (int32_t)ceil_div(dp->ax[2].qmax, bw);
+    return true;
+}
+
 // ---- grouped route tiling -------------------------------------------------
 // A block computes every phase of a tile of q rows (qh) at one qd, over the
 // full q width, for the Cog channels of one group, and stages the output
@@ -559,7 +654,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     const int nd = p->ndim;
     if (nd < 1 || nd > CONVT_MAX_NDIM) return CONVT_ERR_INVALID_ARGUMENT;
     if (p->has_bias != 0 && p->has_bias != 1) return CONVT_ERR_INVALID_ARGUMENT;
-    if (p->route < CONVT_ROUTE_AUTO || p->route > CONVT_ROUTE_NAIVE)
+    if (p->route < CONVT_ROUTE_AUTO || p->route > CONVT_ROUTE_PHASE_GEMM_PACKED)
         return CONVT_ERR_INVALID_ARGUMENT;
     if (p->has_padding_hi != 0 && p->has_padding_hi != 1) return CONVT_ERR_INVALID_ARGUMENT;
     if (p->filter_layout < CONVT_FILTER_CI_CO_K || p->filter_layout > CONVT_FILTER_K_CO_CI ||
@@ -567,7 +662,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
         return CONVT_ERR_INVALID_ARGUMENT;
     if (p->activation < CONVT_ACT_NONE || p->activation > CONVT_ACT_GELU || p->reserved1 != 0)
         return CONVT_ERR_INVALID_ARGUMENT;
-    if (p->route_bwd < CONVT_ROUTE_AUTO || p->route_bwd > CONVT_ROUTE_NAIVE)
+    if (p->route_bwd < CONVT_ROUTE_AUTO || p->route_bwd > CONVT_ROUTE_PHASE_GEMM_PACKED)
         return CONVT_ERR_INVALID_ARGUMENT;
     const int64_t B = p->x_shape[0], Ci = p->x_shape[1];
     const int64_t G = p->groups;
@@ -686,6 +781,9 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
             case CONVT_ROUTE_NONE: ok = empty_out; break;
             case CONVT_ROUTE_FILL: ok = !empty_out && no_terms; break;
             case CONVT_ROUTE_PHASE_GEMM: ok = !empty_out && !no_terms && gemm_eligible(dp, dt, nd); break;
+            case CONVT_ROUTE_PHASE_GEMM_PACKED:
+                ok = !empty_out && !no_terms && dt != CONVT_DTYPE_F32 && gemm_eligible(dp, dt, nd);
+                break;
             case CONVT_ROUTE_GROUPED: ok = !empty_out && !no_terms && grouped_eligible(dp, dt); break;
             case CONVT_ROUTE_DIRECT: ok = !empty_out && !no_terms && direct_eligible(dp); break;
             case CONVT_ROUTE_NAIVE: ok = !empty_out && !no_terms; break;
@@ -698,7 +796,30 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
 
     // ---- tiles and workspace ------------------------------------------------
     int64_t blocks = 0;
-    if (route == CONVT_ROUTE_PHASE_GEMM) {
+    // the two-byte GEMM reads x in place when the problem suits that kernel
+    if (route == CONVT_ROUTE_PHASE_GEMM && dt != CONVT_DTYPE_F32 && !choose_nchw(&dp, nd))
+        route = CONVT_ROUTE_PHASE_GEMM_PACKED;
+    pl->route = route;
+    info.route = route;
+    if (route == CONVT_ROUTE_PHASE_GEMM && dp.gemm_nchw) {
+        const int bm = 128 * dp.nchw_wgm;
+        dp.cog_pad = (int32_t)(ceil_div(Cog, bm) * bm);
+        // whole pairs of 16-channel chunks (the kernel runs two per loop trip)
+        dp.cig_pad = (int32_t)(ceil_div(Cig, 32) * 32);
+        dp.wr_chunked = 1;
+        {
+            // each phase's taps padded to gemm_gs (one stage per chunk)
+            int64_t base = 0;
+            for (int P = 0; P < dp.nphase; ++P) {
+                dp.ph[P].tapbase = (int32_t)base;
+                base += ceil_div(dp.ph[P].ntaps, dp.gemm_gs) * dp.gemm_gs;
+            }
+            if (base > i31) return CONVT_ERR_UNSUPPORTED;
+            dp.ktot_pad = (int32_t)base;
+        }
+        dp.n_co_tiles = (int32_t)ceil_div(Cog, bm);
+        blocks = (int64_t)dp.nt_d * dp.nt_h * dp.nt_w * dp.n_co_tiles * nph * G * B;
+    } else if (route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_PHASE_GEMM_PACKED) {
         pick_gemm_cfg(&dp, dt, nd, false);
         const tiles::GemmTile &t = tiles::kGemmCfg[dp.gemm_cfg];
         // channels of a stage: SC chunks of 32 bytes
@@ -738,14 +859,15 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     dp.n_blocks = (int32_t)blocks;
     // the grouped kernel runs a 3-D grid in plain order
     dp.xcd_remap = (blocks % 8 == 0 && route != CONVT_ROUTE_GROUPED) ? 1 : 0;
-    if (route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_GROUPED) {
+    const bool gemm = route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_PHASE_GEMM_PACKED;
+    if (gemm || route == CONVT_ROUTE_GROUPED) {
         int64_t wr;
-        const int64_t taps = route == CONVT_ROUTE_PHASE_GEMM ? dp.ktot_pad : ktot;
+        const int64_t taps = gemm ? dp.ktot_pad : ktot;
         if (!mul_ok((int64_t)G * taps, (int64_t)dp.cog_pad * dp.cig_pad, lim, &wr))
             return CONVT_ERR_INVALID_ARGUMENT;
         pl->wr_elems = wr;
         info.workspace_bytes = wr * pl->elem_bytes;
-        if (route == CONVT_ROUTE_PHASE_GEMM) {
+        if (gemm) {
             // the per-tap halo shift table (int32 per padded tap of a group)
             pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
             info.workspace_bytes = pl->tab_offset + (int64_t)dp.ktot_pad * 4;
@@ -755,7 +877,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
             pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
             info.workspace_bytes = pl->tab_offset + 16 * (int64_t)dp.nphase + (int64_t)ktot * (Cig / 8) * 8;
         }
-        if (route == CONVT_ROUTE_PHASE_GEMM && dt != CONVT_DTYPE_F32) {
+        if (route == CONVT_ROUTE_PHASE_GEMM_PACKED) {
             // the channel-chunked copy of x: [B][G][chunk][position][32 bytes]
             int64_t xp;
             if (!mul_ok(B * G, (int64_t)dp.cig_pad / 16, lim, &t) || !mul_ok(t, xpl * 32, lim, &xp))

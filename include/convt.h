@@ -95,7 +95,12 @@ typedef enum convt_route {
     CONVT_ROUTE_PHASE_GEMM = 3, /* stride-phase implicit-gather GEMM on MFMA */
     CONVT_ROUTE_GROUPED = 4,    /* grouped / few-channel stride-phase kernel, MFMA, LDS-staged output */
     CONVT_ROUTE_DIRECT = 5,     /* small-channel direct kernel, weight slab in LDS */
-    CONVT_ROUTE_NAIVE = 6       /* one thread per output, gathers its terms */
+    CONVT_ROUTE_NAIVE = 6,      /* one thread per output, gathers its terms */
+    CONVT_ROUTE_PHASE_GEMM_PACKED = 7 /* two-byte types: the phase GEMM on a channel-chunked copy
+                                         of x that each call writes into the workspace (the
+                                         PHASE_GEMM route reads x in place when the problem
+                                         suits that kernel, and plans this one otherwise);
+                                         forward only */
 } convt_route;
 
 /* How W is laid out in memory (the AWS Neuron conv3d_transpose page's
@@ -202,9 +207,12 @@ convt_status convt_plan(const convt_problem *problem, convt_plan_t *out, convt_p
  * (NULL allowed when that is 0), 16-byte aligned; it must not be used by
  * another call until this call's work on `stream` has finished. y must not
  * overlap x, W, bias or the workspace. Same result, byte for byte, as
- * convt_prepare_weights followed by convt_forward_prepared; for two-byte
- * element types on the PHASE_GEMM route it runs their weight reorder and
- * input copy as one launch.
+ * convt_prepare_weights followed by convt_forward_prepared; on the
+ * PHASE_GEMM_PACKED route it runs the weight reorder and the input copy as
+ * one launch. On the PHASE_GEMM route with a two-byte element type, x must
+ * be 4-byte aligned (that kernel reads neighbouring positions in pairs as
+ * 32-bit words); a misaligned x is refused with CONVT_ERR_INVALID_ARGUMENT
+ * before anything is enqueued.
  */
 convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, const void *bias,
                            void *y, void *workspace, void *stream);
@@ -223,7 +231,7 @@ convt_status convt_prepare_weights(convt_plan_t plan, const void *w, void *works
  * convt_prepare_weights (for the same plan and the same W), W itself (used
  * by the routes that read it directly; may be NULL for the others) and bias.
  * The prepared weights at the start of the workspace are left unchanged; the
- * rest of it is scratch that the call overwrites (the two-byte phase-GEMM
+ * rest of it is scratch that the call overwrites (the PHASE_GEMM_PACKED
  * route stages a channel-chunked copy of x there). Arguments as in
  * convt_forward.
  */
@@ -245,7 +253,8 @@ convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void
  * at least info.bwd_workspace_bytes bytes, 16-byte aligned (may be NULL when
  * that is 0); it is scratch, and may be the forward's workspace buffer if
  * large enough, but not in use by a concurrent call. Asynchronous on stream,
- * errors as for convt_forward. Routes (info.route_bwd): NONE (dx empty),
+ * errors as for convt_forward. route_bwd may not be PHASE_GEMM_PACKED
+ * (CONVT_ERR_UNSUPPORTED at planning). Routes (info.route_bwd): NONE (dx empty),
  * FILL (no output channels: dx = 0), PHASE_GEMM (stride phases summed inside
  * one implicit-gather GEMM on MFMA), DIRECT (few channels per group: a thread
  * per dx position over its group's input channels, weights in LDS), NAIVE

@@ -157,17 +157,35 @@ def test_forced_routes():
     assert plan(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2, route="naive").route == "naive"
     assert status_of(x_shape=(0, 1, 3), route="naive") == 2   # nothing to compute
     assert status_of(x_shape=(1, 64, 4), w_shape=(64, 64, 2), stride=17, route="phase_gemm") == 2
+    # the packed phase GEMM serves two-byte types only, and only forward
+    assert status_of(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2,
+                     route="phase_gemm_packed") == 2
+    assert plan(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2, dtype="bf16",
+                route="phase_gemm_packed").route == "phase_gemm_packed"
+    assert status_of(x_shape=(1, 16, 8), w_shape=(16, 8, 4), stride=2, dtype="bf16",
+                     route_bwd="phase_gemm_packed") == 2
+    # a two-byte problem the in-place kernel does not suit (odd input rows)
+    # is planned on the packed variant when PHASE_GEMM is asked for
+    assert plan(x_shape=(2, 72, 9, 13), w_shape=(72, 136, 4, 4), stride=2, padding=1, dtype="bf16",
+                route="phase_gemm").route == "phase_gemm_packed"
 
 
 def test_workspace_sizes():
     wl = workloads.get("c3")
     pl = plan(x_shape=wl.x_shape, w_shape=wl.w_shape, stride=wl.stride, padding=wl.padding,
               dtype="bf16", has_bias=True)
-    # reordered weights (no padding needed at these sizes), the per-tap
-    # halo shift table (16 taps, its 256-byte aligned slot), then the
-    # channel-chunked copy of x that the bfloat16 GEMM reads
+    # reordered weights (no padding needed at these sizes) and the per-tap
+    # halo shift table (16 taps of 4 bytes); the bfloat16 GEMM reads x in
+    # place
+    assert pl.route == "phase_gemm"
     wr_bytes = 512 * 256 * 16 * 2
-    assert pl.workspace_bytes == wr_bytes + 256 + 64 * 512 * 16 * 16 * 2
+    assert pl.workspace_bytes == wr_bytes + 16 * 4
+    # the packed variant adds the channel-chunked copy of x it reads
+    pk = plan(x_shape=wl.x_shape, w_shape=wl.w_shape, stride=wl.stride, padding=wl.padding,
+              dtype="bf16", has_bias=True, route="phase_gemm_packed")
+    assert pk.route == "phase_gemm_packed"
+    # (after the table's 256-byte aligned slot)
+    assert pk.workspace_bytes == wr_bytes + 256 + 64 * 512 * 16 * 16 * 2
     pl = plan(x_shape=(1, 3, 5), w_shape=(3, 5, 3), stride=2, route="phase_gemm")
     # channels padded to the f32 tile: 16 input (two 8-channel chunks per
     # stage), 64 output, 3 taps (phases of 2 and 1 taps, one tap per stage);

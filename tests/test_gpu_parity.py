@@ -68,7 +68,7 @@ def test_reduced_workloads(case):
 
 
 @pytest.mark.parametrize("case", REDUCED, ids=[c[0] for c in REDUCED])
-@pytest.mark.parametrize("route", ["naive", "direct", "phase_gemm", "grouped"])
+@pytest.mark.parametrize("route", ["naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"])
 def test_reduced_workloads_every_route(case, route):
     tens, prm = reduced_tensors(case, seed=8)
     try:
@@ -92,7 +92,7 @@ def rne_bf16(v: np.ndarray) -> np.ndarray:
 
 
 @pytest.mark.parametrize("case", REDUCED, ids=[c[0] for c in REDUCED])
-@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "grouped"])
+@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"])
 def test_integer_inputs_exact(case, route):
     tens, prm = reduced_tensors(case, seed=9, dist="int(4)")
     try:
@@ -169,7 +169,7 @@ def run_grid_case(prm, tag):
     has_bias = bool(prm["seed"] % 2)
     tens = workloads.make_tensors(xs, ws, prm["Cog"] * prm["groups"], has_bias, prm["dtype"],
                                   "normal(1)", "normal(1)", "normal(1)", prm["seed"])
-    for route in ["auto", "naive", "direct", "phase_gemm", "grouped"]:
+    for route in ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"]:
         try:
             C.get_plan(xs, ws, params["stride"], params["padding"], params["dilation"],
                        params["output_padding"], params["groups"], has_bias, prm["dtype"], route)
@@ -233,7 +233,7 @@ ASYM = [
 
 
 @pytest.mark.parametrize("case", ASYM, ids=[c[0] for c in ASYM])
-@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "grouped"])
+@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"])
 def test_asymmetric_padding_every_route(case, route):
     name, xs, ws, s, p, d, op, g, dt = case
     prm = dict(stride=s, padding=p, dilation=d, output_padding=op, groups=g)
@@ -367,8 +367,8 @@ def test_prepared_split_matches_forward(dt, hw):
                                   "uniform", "uniform", 6)
     prm = dict(stride=(1, 1), padding=(2, 2), dilation=(2, 2), output_padding=(0, 0), groups=1)
     say(f"[gpu] prepare_weights + forward_prepared {dt} {hw}")
-    y_ref, pl = run_gpu(tens, prm)
-    assert pl.route == "phase_gemm"
+    y_ref, pl = run_gpu(tens, prm, route="phase_gemm_packed")
+    assert pl.route == "phase_gemm_packed"
     x = to_device(tens.x_dev, dt)
     w = to_device(tens.w_dev, dt)
     b = to_device(tens.bias_dev, dt)
@@ -387,6 +387,29 @@ def test_prepared_split_matches_forward(dt, hw):
     y2_ref = pl.forward(x2, w, b)
     torch.cuda.synchronize()
     assert np.array_equal(to_host64(y2), to_host64(y2_ref))
+
+
+# The same split on the GEMM that reads x in place (even rows, more than 64
+# output channels): convt_forward is the reorder then that kernel.
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_prepared_split_matches_forward_in_place(dt):
+    import torch
+    xs, ws = (2, 40, 10, 16), (40, 96, 4, 4)
+    tens = workloads.make_tensors(xs, ws, 96, True, dt, "uniform", "uniform", "uniform", 16)
+    prm = dict(stride=(2, 2), padding=(1, 1), dilation=(1, 1), output_padding=(0, 0), groups=1)
+    say(f"[gpu] prepare_weights + forward_prepared in place {dt}")
+    y_ref, pl = run_gpu(tens, prm)
+    assert pl.route == "phase_gemm"
+    x = to_device(tens.x_dev, dt)
+    w = to_device(tens.w_dev, dt)
+    b = to_device(tens.bias_dev, dt)
+    ws_t = pl.new_workspace(x.device)
+    y = pl.new_output(x.device)
+    st = torch.cuda.current_stream().cuda_stream
+    pl.prepare_weights_ptr(w.data_ptr(), ws_t.data_ptr(), st)
+    pl.forward_prepared_ptr(x.data_ptr(), w.data_ptr(), b.data_ptr(), y.data_ptr(), ws_t.data_ptr(), st)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host64(y), y_ref)
 
 
 # ---------------------------------------------------------------------------

@@ -144,6 +144,12 @@ def lib() -> ctypes.CDLL:
         L.convt_plan_axis_phase.restype = ctypes.c_int
         L.convt_version.argtypes = []
         L.convt_version.restype = ctypes.c_int32
+        L.convt_plan_query.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+        L.convt_plan_query.restype = ctypes.c_int
+        L.convt_forward_scratch.argtypes = [vp, vp, vp, vp, vp, vp]
+        L.convt_forward_scratch.restype = ctypes.c_int
+        L.convt_scratch_max_bytes.argtypes = []
+        L.convt_scratch_max_bytes.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -284,6 +290,13 @@ class Plan:
                                  workspace or None, stream or None)
         if st != 0:
             raise ConvtError(st, "convt_forward")
+
+    def forward_scratch_ptr(self, x: int, w: int, bias: int, y: int, stream: int) -> None:
+        """convt_forward with the library's own fixed workspace (no allocation)."""
+        st = lib().convt_forward_scratch(self._h, x or None, w or None, bias or None, y or None,
+                                         stream or None)
+        if st != 0:
+            raise ConvtError(st, "convt_forward_scratch")
 
     def prepare_weights_ptr(self, w: int, workspace: int, stream: int) -> None:
         st = lib().convt_prepare_weights(self._h, w or None, workspace or None, stream or None)

@@ -231,6 +231,12 @@ convt_status convt_plan_axis_phase(convt_plan_t plan, int32_t axis, int64_t resi
     return CONVT_OK;
 }
 
+convt_status convt_plan_query(convt_plan_t plan, convt_plan_info *info) {
+    if (!plan || !info) return CONVT_ERR_INVALID_ARGUMENT;
+    *info = plan->plan.info;
+    return CONVT_OK;
+}
+
 int32_t convt_version(void) { return 300; }
 
 }  // extern "C"

@@ -286,8 +286,36 @@ convt_status convt_plan_axis_phase(convt_plan_t plan, int32_t axis, int64_t resi
                                    int64_t *q_count, int64_t *n_taps, int64_t *taps,
                                    int64_t *offsets, int64_t cap);
 
+/* The plan information of an existing plan (what convt_plan returned in
+ * *info). Host only. CONVT_ERR_INVALID_ARGUMENT if plan or info is NULL. */
+convt_status convt_plan_query(convt_plan_t plan, convt_plan_info *info);
+
 /* Library version, major*10000 + minor*100 + patch. */
 int32_t convt_version(void);
+
+/*
+ * For callers that cannot allocate device memory (code under stream or graph
+ * capture that must not call the allocator, tight serving loops, harnesses
+ * that forbid allocation): convt_forward with the workspace taken from a
+ * fixed array of CONVT_SCRATCH_MAX_BYTES bytes inside this library, one
+ * per GPU, held from the library's first use on that GPU until the process
+ * ends. Arguments and result as for convt_forward, without the workspace.
+ * Makes no allocation call (no hipMalloc, no hipFree). Plans whose
+ * info.workspace_bytes exceed CONVT_SCRATCH_MAX_BYTES are refused with
+ * CONVT_ERR_UNSUPPORTED before anything is enqueued; CONVT_ERR_DEVICE if the
+ * array's address on the current device cannot be obtained. Every call on
+ * one GPU uses the same array: calls whose work overlaps on that GPU (other
+ * streams, or another host thread) race on it and must be serialised by the
+ * caller; calls in one stream are ordered and safe. Nothing needs to start
+ * at zero: each call writes every byte it reads from the array before
+ * reading it.
+ */
+#define CONVT_SCRATCH_MAX_BYTES (32 * 1024 * 1024)
+convt_status convt_forward_scratch(convt_plan_t plan, const void *x, const void *w,
+                                   const void *bias, void *y, void *stream);
+
+/* CONVT_SCRATCH_MAX_BYTES, for bindings. */
+int64_t convt_scratch_max_bytes(void);
 
 #ifdef __cplusplus
 }

@@ -358,3 +358,21 @@ def test_activation_and_reserved_fields_validated():
         assert st == want, (act, res, st)
         if st == 0:
             L.convt_destroy(h)
+
+
+def test_scratch_entry_point_host_checks():
+    """convt_forward_scratch: the limit, and refusals made before any device
+    call (a plan whose workspace exceeds the library's array)."""
+    L = C.lib()
+    assert L.convt_scratch_max_bytes() == 32 * 1024 * 1024
+    fake = 4096  # never dereferenced: every call below fails a host-side check
+    assert L.convt_forward_scratch(None, fake, fake, fake, fake, None) == 1
+    big = plan(x_shape=(1, 2048, 4, 4), w_shape=(2048, 1024, 4, 4), stride=2, padding=1,
+               dtype="bf16", has_bias=True)
+    assert big.workspace_bytes > L.convt_scratch_max_bytes()
+    assert L.convt_forward_scratch(big.handle, fake, fake, fake, fake, None) == 2
+    # convt_plan_query reports what convt_plan did
+    info = C.PlanInfo()
+    assert L.convt_plan_query(big.handle, ctypes.byref(info)) == 0
+    assert info.workspace_bytes == big.workspace_bytes and info.route == big.info.route
+    assert L.convt_plan_query(big.handle, None) == 1

@@ -4,11 +4,12 @@
 // For grouped problems with few channels per group (C_in/groups a multiple
 // of 8 up to 64, C_out/groups up to 16) the phase GEMM's tiles would be
 // mostly empty. Here one block owns one (batch, group) and a tile of q rows
-// at one q-depth, over the full q width, for EVERY stride phase: the
-// huggingface ai.onnx.ConvTranspose page's grouped stride-phase blocked
-// variant (an invocation owns output pixels and a block of its group's output
-// channels; every gathered input sample feeds the whole channel block; the
-// group's weight slab is staged once per workgroup), laid out for gfx950.
+// at one q-depth, over the full q width, for EVERY stride phase. This keeps
+// the idea of the grouped stride-phase blocked variant that the huggingface
+// ai.onnx.ConvTranspose page lists under Implementation variants: the work
+// unit is a set of output pixels times all of its group's output channels,
+// so each input value read serves every one of those channels, and the
+// group's weights are brought on chip once per block.
 //
 // The work per output is tiny (a few K slots) and the output is 4x the
 // input, so the kernel is written for a small instruction count per stored

@@ -699,6 +699,19 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
         O[a] = (I[a] - 1) * S[a] - (P[a] + PH) + D[a] * (K[a] - 1) + OP[a] + 1;
         if (O[a] < 1) return CONVT_ERR_INVALID_ARGUMENT;
     }
+    // The kernels index an axis in 32-bit arithmetic: an output position o
+    // reaches the input through o + p - kk*d (from -d(k-1) up to
+    // (I-1)s + d(k-1) + op), and each residue's first input offset is
+    // (r + p - kk*d)/s. Problems whose terms do not fit are valid but not
+    // served.
+    for (int j = 0; j < nd; ++j) {
+        const int a = lead + j;
+        const int64_t PH = p->has_padding_hi ? p->padding_hi[j] : P[a];
+        const int64_t lim30 = (int64_t)1 << 30;
+        if (P[a] > lim30 || PH > lim30 || D[a] * (K[a] - 1) > lim30 ||
+            (I[a] > 0 ? (I[a] - 1) * S[a] : 0) + D[a] * (K[a] - 1) + std::max(S[a], D[a]) >= ((int64_t)1 << 31))
+            return CONVT_ERR_UNSUPPORTED;
+    }
     if (p->dtype < CONVT_DTYPE_F32 || p->dtype > CONVT_DTYPE_I64)
         return CONVT_ERR_INVALID_ARGUMENT;
     if (p->dtype != CONVT_DTYPE_F32 && p->dtype != CONVT_DTYPE_BF16 && p->dtype != CONVT_DTYPE_F16)

@@ -118,6 +118,23 @@ def test_plan_rejects_invalid(kw):
     assert status_of(**kw) == 1
 
 
+# valid problems whose per-axis index terms exceed 32 bits: refused as
+# unsupported rather than indexed with wrapped arithmetic
+TOO_WIDE = [
+    # output size (1048676-1) - 2*2^39 + 2^20*(2^20-1) + 1 = 100
+    dict(x_shape=(1, 1, 1048676), w_shape=(1, 1, 1048576), padding=2 ** 39, dilation=2 ** 20),
+    # low padding 2^31, high padding 0
+    dict(x_shape=(1, 1, 2 ** 12), w_shape=(1, 1, 2 ** 12), padding=((2 ** 31, 0),), dilation=2 ** 20),
+    # (2^31 - 1) * 2 + 1 output positions
+    dict(x_shape=(1, 1, 2 ** 31), w_shape=(1, 1, 1), stride=2),
+]
+
+
+@pytest.mark.parametrize("kw", TOO_WIDE)
+def test_plan_refuses_int32_overflowing_axes(kw):
+    assert status_of(**kw) == 2
+
+
 @pytest.mark.parametrize("dt", ["i8", "i32", "i64"])
 def test_plan_refuses_other_dtypes_loudly(dt):
     assert status_of(dtype=dt) == 2

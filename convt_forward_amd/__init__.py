@@ -21,7 +21,9 @@ import os
 from typing import Dict, Optional, Sequence, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libconvt.so")
+# CONVT_LIB names another build of the same library (the host-sanitizer build
+# of the planner and C ABI); by default the in-tree libconvt.so is loaded
+LIB_PATH = os.environ.get("CONVT_LIB") or os.path.join(_HERE, "libconvt.so")
 
 MAX_NDIM = 3
 

@@ -253,9 +253,14 @@ def default() -> Oracle:
     """The oracle built from this directory's source (compiled if not yet built)."""
     global _default
     if _default is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        _default = Oracle(_LIB)
+        # CONVT_ORACLE_LIB names another build of the same source (the
+        # host-sanitizer build)
+        path = os.environ.get("CONVT_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(path):
+                build(force=True)
+        _default = Oracle(path)
     return _default
 
 

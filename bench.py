@@ -49,6 +49,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "phase_gemm": ["k_gemm_nchw.hip", "k_phase_gemm.hip", "kcommon.h", "convt_internal.h", "plan.cpp"],
     "phase_gemm_packed": ["k_phase_gemm.hip", "kcommon.h", "convt_internal.h", "plan.cpp"],
+    "phase_gemm_allphase": ["k_gemm_allphase.hip", "kcommon.h", "convt_internal.h", "plan.cpp"],
     "grouped": ["k_grouped.hip", "kcommon.h", "plan.cpp"],
     "direct": ["k_misc.hip", "kcommon.h", "plan.cpp"],
     "naive": ["k_misc.hip", "kcommon.h", "plan.cpp"],
@@ -56,6 +57,7 @@ KERNEL_SOURCES = {
 KERNEL_SYMBOL = {
     "phase_gemm": "phase_gemm_kernel",
     "phase_gemm_packed": "phase_gemm_kernel",
+    "phase_gemm_allphase": "allphase_gemm_kernel",
     "grouped": "grouped_kernel",
     "direct": "direct_kernel",
     "naive": "naive_kernel",
@@ -310,7 +312,8 @@ def main() -> int:
     flops = useful_flops(wl)
     abytes = algorithmic_bytes(wl, pl.out_shape)
     route = pl.route
-    if route in ("phase_gemm", "phase_gemm_packed", "direct", "naive") and wl.dtype in PEAK_TFLOPS and \
+    if route in ("phase_gemm", "phase_gemm_packed", "phase_gemm_allphase", "direct", "naive") and \
+            wl.dtype in PEAK_TFLOPS and \
             flops / abytes > 50.0:
         bound, unit = "mfma", "TFLOP/s"
         achieved = flops / kern_s / 1e12

@@ -30,7 +30,7 @@ MAX_NDIM = 3
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported request", 3: "device error"}
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "i8": 3, "i32": 4, "i64": 5}
 ROUTES = {"auto": 0, "none": 1, "fill": 2, "phase_gemm": 3, "grouped": 4, "direct": 5, "naive": 6,
-          "phase_gemm_packed": 7}
+          "phase_gemm_packed": 7, "phase_gemm_allphase": 8}
 ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
 # filter layouts (element (ci, ocl, kk) of W; see include/convt.h):
 #   ci_co_k [C_in][C_out/groups][k...], k_ci_co [k...][C_in][C_out/groups],

@@ -31,7 +31,13 @@ bool needs_weights_in_workspace(int route) {
 // The two-byte phase GEMM that reads x in place takes neighbouring positions
 // in pairs as 32-bit words.
 bool x_misaligned(const convt::Plan &pl, const void *x) {
-    return pl.route == CONVT_ROUTE_PHASE_GEMM && pl.dp.gemm_nchw && ((uintptr_t)x % 4) != 0;
+    return ((pl.route == CONVT_ROUTE_PHASE_GEMM && pl.dp.gemm_nchw) || pl.route == CONVT_ROUTE_PHASE_GEMM_ALLPHASE) &&
+           ((uintptr_t)x % 4) != 0;
+}
+
+// The all-phase GEMM reads W in 16-byte pieces.
+bool w_misaligned(const convt::Plan &pl, const void *w) {
+    return pl.route == CONVT_ROUTE_PHASE_GEMM_ALLPHASE && ((uintptr_t)w % 16) != 0;
 }
 
 }  // namespace
@@ -87,6 +93,9 @@ convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void
         case CONVT_ROUTE_DIRECT:
             if (!w) return CONVT_ERR_INVALID_ARGUMENT;
             return device_status(convt::launch_direct(pl, x, w, bias, y, s));
+        case CONVT_ROUTE_PHASE_GEMM_ALLPHASE:
+            if (!w || x_misaligned(pl, x) || w_misaligned(pl, w)) return CONVT_ERR_INVALID_ARGUMENT;
+            return device_status(convt::launch_allphase(pl, x, w, bias, y, s));
         case CONVT_ROUTE_PHASE_GEMM:
         case CONVT_ROUTE_PHASE_GEMM_PACKED: {
             if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
@@ -126,7 +135,7 @@ convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, cons
     if (needs_weights_in_workspace(pl.route) &&
         (!workspace || ((uintptr_t)workspace % 16) != 0))
         return CONVT_ERR_INVALID_ARGUMENT;
-    if (x_misaligned(pl, x)) return CONVT_ERR_INVALID_ARGUMENT;
+    if (x_misaligned(pl, x) || w_misaligned(pl, w)) return CONVT_ERR_INVALID_ARGUMENT;
     if (pl.route == CONVT_ROUTE_PHASE_GEMM_PACKED && pl.xp_bytes > 0 && pl.wr_elems > 0) {
         // two-byte elements: the weight reorder and the channel-chunked copy
         // of x in one launch, then the GEMM
@@ -193,6 +202,7 @@ const char *convt_route_name(int32_t route) {
         case CONVT_ROUTE_FILL: return "fill";
         case CONVT_ROUTE_PHASE_GEMM: return "phase_gemm";
         case CONVT_ROUTE_PHASE_GEMM_PACKED: return "phase_gemm_packed";
+        case CONVT_ROUTE_PHASE_GEMM_ALLPHASE: return "phase_gemm_allphase";
         case CONVT_ROUTE_GROUPED: return "grouped";
         case CONVT_ROUTE_DIRECT: return "direct";
         case CONVT_ROUTE_NAIVE: return "naive";
@@ -237,6 +247,6 @@ convt_status convt_plan_query(convt_plan_t plan, convt_plan_info *info) {
     return CONVT_OK;
 }
 
-int32_t convt_version(void) { return 300; }
+int32_t convt_version(void) { return 310; }
 
 }  // extern "C"

@@ -93,6 +93,45 @@ struct DevParams {
     PhaseRec ph[kMaxPhaseTab];
 };
 
+// Division by a run-time constant d >= 1 for every 32-bit dividend n:
+// n / d = (mulhi(n, m) + n) >> s in 33-bit arithmetic, with s = ceil(log2 d)
+// and m = floor(2^32 (2^s - d) / d) + 1 (the round-up multiplier of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).
+struct FastDiv {
+    uint32_t m, s;
+};
+
+// All-phase GEMM (two-byte types; stride 2 and dilation 1 on the height and
+// width axes): a block computes every (height, width) residue of a q box for
+// 128 output channels and one depth residue, reading x in NC[D]HW and W in
+// [C_in][C_out/groups][k...] directly. Axes as in DevParams (0 depth, 1
+// height, 2 width; unit depth for 2-D problems).
+struct AllPhaseArgs {
+    int32_t Ci, Co, Cig, Cog, G;
+    int32_t I[3], O[3], K[3];
+    int32_t ktot;               // K0 * K1 * K2
+    int32_t T[3];               // q box (T0 * T1 * T2 = 128; T1, T2 powers of two, T2 >= 16)
+    int32_t lgT1, lgT2;
+    int32_t n_co_tiles, n_rd;   // 128-channel tiles; depth residues
+    int32_t n_blocks, xcd_remap;
+    FastDiv div_co, div_rd, div_t2, div_t1, div_t0, div_g;  // block-index decode
+    int32_t nt[3];              // q tiles per axis
+    int32_t nstages;            // pipeline stages (chunk groups), even
+    int32_t x_plane, y_plane;
+    int32_t has_bias, act, flip;
+    // height / width: the taps of residue r are k = k0[r] - 2j at input
+    // offset off0[r] + j (j < K/2); the halo starts at offset uh (height)
+    // and uw (width, even) from the q box and spans E1 x E2 positions (E2 even)
+    int32_t kh0[2], offh0[2], kw0[2], offw0[2];
+    int32_t uh, uw, E1, E2;
+    // depth: residue rd's taps are k = kd0[rd] - kstep_d j at input offset
+    // offd[rd] + ostep_d j (j < nd, the same count for every residue); its q
+    // count is qnd[rd]
+    int32_t S0, nd, kstep_d, ostep_d;
+    int32_t kd0[kMaxS], offd[kMaxS], qnd[kMaxS];
+};
+
 struct Plan {
     convt_problem prob;
     convt_plan_info info;
@@ -104,6 +143,8 @@ struct Plan {
     int64_t xp_offset;  // bfloat16 phase GEMM: byte offset of the channel-chunked copy of x
     int64_t xp_bytes;   // its size (0 when not used)
     int32_t elem_bytes; // 4 (float32) or 2 (bfloat16)
+    AllPhaseArgs ap;    // CONVT_ROUTE_PHASE_GEMM_ALLPHASE: the kernel's arguments
+    int32_t ap_tw;      // ... taps per phase and chunk (4 or 8)
     // Backward data. bdp is the problem as the backward kernels see it: the
     // input is dy (ax[a].I = O, channels Co in groups of Cog), the output is
     // dx (ax[a].O = I, channels Ci in groups of Cig); the axes keep the

@@ -55,24 +55,6 @@ namespace {
 
 constexpr int kNThreads = 256;
 
-// 32-bit words of two-byte elements: the low halves of a and b, or their
-// high halves, as one word (a's in the low half).
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
-// a / b for 0 <= a < 2^22 and 0 < b < 2^16 through a float32 reciprocal,
-// corrected to the exact quotient (the estimate is within one of it).
-__device__ __forceinline__ int div_small(int a, int b) {
-    int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
-    if (q * b > a) --q;
-    else if ((q + 1) * b <= a) ++q;
-    return q;
-}
-
 }  // namespace
 
 template <typename T, int WGM, int GS, int XU, bool ACT>

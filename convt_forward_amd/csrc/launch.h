@@ -21,6 +21,10 @@ hipError_t launch_phase_gemm(const Plan &pl, const void *x, const void *wr, cons
 // two-byte phase GEMM reading x in NC[D]HW (plans with dp.gemm_nchw)
 hipError_t launch_phase_gemm_nchw(const Plan &pl, const void *x, const void *wr, const void *bias,
                                   void *y, hipStream_t stream);
+// all-phase two-byte GEMM (CONVT_ROUTE_PHASE_GEMM_ALLPHASE): x and W as the
+// caller stores them, no workspace
+hipError_t launch_allphase(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
+                           hipStream_t stream);
 hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const void *bias, void *y,
                           hipStream_t stream);
 

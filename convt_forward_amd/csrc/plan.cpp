@@ -327,6 +327,129 @@ int64_t nchw_halo(const DevParams &dp, int P, int T0, int T1, int T2) {
     return E0 * E1 * E2;
 }
 
+// ---- all-phase two-byte GEMM -------------------------------------------
+FastDiv fast_div_of(uint32_t d) {
+    uint32_t s = 0;
+    while (((uint64_t)1 << s) < d) ++s;
+    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << s) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, s};
+}
+
+// Plan the all-phase kernel (k_gemm_allphase.hip) for a forward problem with
+// a two-byte element type, or return false if it does not apply: it needs
+// stride 2 and dilation 1 on the height and width axes with even kernel
+// extents there (every residue then has K/2 taps), the same tap count for
+// every depth residue, 4 or 8 taps per phase (a stage is then 8 input
+// channels x all taps of the block's four phases, 64 KiB of weights), whole
+// 8-tap octets per depth plane of W, W in [C_in][C_out/groups][k...], an
+// even x row length (pairs of positions) and an output row length that is
+// a multiple of 8 (16-byte output pieces). min_cog: fewer output channels
+// per group are left to the other kernels.
+bool choose_allphase(Plan *pl, const DevParams &dp, int ndim, int dtype, int64_t min_cog) {
+    if (dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16) return false;
+    if (ndim < 2 || dp.w_layout != CONVT_FILTER_CI_CO_K || dp.Cog < min_cog) return false;
+    const DevAxis &a0 = dp.ax[0], &a1 = dp.ax[1], &a2 = dp.ax[2];
+    if (a1.S != 2 || a2.S != 2 || a1.D != 1 || a2.D != 1 || a1.K % 2 || a2.K % 2) return false;
+    if (a0.S > kMaxS) return false;
+    const int nd = a0.n[0];
+    for (int r = 0; r < a0.S; ++r)
+        if (a0.n[r] != nd) return false;
+    if (nd < 1) return false;
+    const int tw = nd * (a1.K / 2) * (a2.K / 2);
+    if (tw != 4 && tw != 8) return false;
+    if ((a1.K * a2.K) % 8 != 0 || a2.I % 2 != 0 || a2.O % 8 != 0) return false;
+    const int sc = 8 / tw;
+    const int64_t cig_span = dp.Cig + 3 * 8 * sc;  // channels the prefetch may address
+    if (!buffer_fits(cig_span * dp.x_plane * 2) ||
+        !buffer_fits(cig_span * dp.Cog * dp.ktot * 2 + (int64_t)256 * dp.ktot * 2) ||
+        !buffer_fits(((int64_t)dp.Cog + 128) * dp.y_plane * 2))
+        return false;
+    const int uw = a2.umin & ~1;
+    const int64_t rows_cap = 512 / sc;
+    double best = 0;
+    int bt[3] = {0, 0, 0};
+    for (int t2 = 16; t2 <= 128; t2 *= 2) {
+        for (int t1 = 1; t1 * t2 <= 128; t1 *= 2) {
+            const int t0 = 128 / (t1 * t2);
+            if (ndim < 3 && t0 != 1) continue;
+            const int64_t e0 = t0 + (int64_t)(nd - 1) * a0.ostep;
+            const int64_t e1 = t1 + a1.umax - a1.umin;
+            const int64_t e2 = (t2 + a2.umax - uw + 1) & ~(int64_t)1;
+            const int64_t rows = e0 * e1 * e2;
+            if (rows > rows_cap) continue;
+            const int64_t nt = ceil_div(a0.qmax, t0) * ceil_div(a1.qmax, t1) * ceil_div(a2.qmax, t2);
+            const int64_t blocks = nt * ceil_div(dp.Cog, 128) * a0.S * dp.G * dp.B;
+            // one block per CU; a stage: 2048 MFMA cycles per wave plus the
+            // halo the block stages
+            const double t = std::ceil((double)blocks / 256.0) * (2048.0 + 2.0 * (double)rows);
+            if (bt[2] == 0 || t < best * 0.999) {
+                best = t;
+                bt[0] = t0;
+                bt[1] = t1;
+                bt[2] = t2;
+            }
+        }
+    }
+    if (bt[2] == 0) return false;
+    AllPhaseArgs &ap = pl->ap;
+    ap = AllPhaseArgs{};
+    ap.Ci = dp.Ci;
+    ap.Co = dp.Co;
+    ap.Cig = dp.Cig;
+    ap.Cog = dp.Cog;
+    ap.G = dp.G;
+    for (int a = 0; a < 3; ++a) {
+        ap.I[a] = dp.ax[a].I;
+        ap.O[a] = dp.ax[a].O;
+        ap.K[a] = dp.ax[a].K;
+        ap.T[a] = bt[a];
+        ap.nt[a] = (int32_t)ceil_div(dp.ax[a].qmax, bt[a]);
+    }
+    ap.ktot = dp.ktot;
+    ap.lgT1 = __builtin_ctz((unsigned)bt[1]);
+    ap.lgT2 = __builtin_ctz((unsigned)bt[2]);
+    ap.n_co_tiles = (int32_t)ceil_div(dp.Cog, 128);
+    ap.n_rd = a0.S;
+    const int64_t blocks = (int64_t)ap.nt[0] * ap.nt[1] * ap.nt[2] * ap.n_co_tiles * ap.n_rd * dp.G * dp.B;
+    if (blocks > ((int64_t)1 << 31) - 1) return false;
+    ap.n_blocks = (int32_t)blocks;
+    ap.xcd_remap = blocks % 8 == 0 ? 1 : 0;
+    ap.div_co = fast_div_of((uint32_t)ap.n_co_tiles);
+    ap.div_rd = fast_div_of((uint32_t)ap.n_rd);
+    ap.div_t2 = fast_div_of((uint32_t)ap.nt[2]);
+    ap.div_t1 = fast_div_of((uint32_t)ap.nt[1]);
+    ap.div_t0 = fast_div_of((uint32_t)ap.nt[0]);
+    ap.div_g = fast_div_of((uint32_t)dp.G);
+    const int64_t stages = ceil_div(ceil_div(dp.Cig, 8), sc);
+    ap.nstages = (int32_t)((stages + 1) / 2 * 2);
+    ap.x_plane = dp.x_plane;
+    ap.y_plane = dp.y_plane;
+    ap.has_bias = dp.has_bias;
+    ap.act = dp.act;
+    ap.flip = dp.w_flip;
+    for (int r = 0; r < 2; ++r) {
+        ap.kh0[r] = a1.kk0[r];
+        ap.offh0[r] = a1.off0[r];
+        ap.kw0[r] = a2.kk0[r];
+        ap.offw0[r] = a2.off0[r];
+    }
+    ap.uh = a1.umin;
+    ap.uw = uw;
+    ap.E1 = bt[1] + a1.umax - a1.umin;
+    ap.E2 = (bt[2] + a2.umax - uw + 1) & ~1;
+    ap.S0 = a0.S;
+    ap.nd = nd;
+    ap.kstep_d = a0.kstep;
+    ap.ostep_d = a0.ostep;
+    for (int r = 0; r < a0.S; ++r) {
+        ap.kd0[r] = a0.kk0[r];
+        ap.offd[r] = a0.off0[r];
+        ap.qnd[r] = a0.qn[r];
+    }
+    pl->ap_tw = tw;
+    return true;
+}
+
 // Choose the kernel's configuration (tiles::kNchwCfg: waves along C_out,
 // taps per stage, halo units per thread) and q box for a forward problem
 // with a two-byte element type, or return false if the problem does not
@@ -654,7 +777,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     const int nd = p->ndim;
     if (nd < 1 || nd > CONVT_MAX_NDIM) return CONVT_ERR_INVALID_ARGUMENT;
     if (p->has_bias != 0 && p->has_bias != 1) return CONVT_ERR_INVALID_ARGUMENT;
-    if (p->route < CONVT_ROUTE_AUTO || p->route > CONVT_ROUTE_PHASE_GEMM_PACKED)
+    if (p->route < CONVT_ROUTE_AUTO || p->route > CONVT_ROUTE_PHASE_GEMM_ALLPHASE)
         return CONVT_ERR_INVALID_ARGUMENT;
     if (p->has_padding_hi != 0 && p->has_padding_hi != 1) return CONVT_ERR_INVALID_ARGUMENT;
     if (p->filter_layout < CONVT_FILTER_CI_CO_K || p->filter_layout > CONVT_FILTER_K_CO_CI ||
@@ -797,6 +920,9 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
             case CONVT_ROUTE_PHASE_GEMM_PACKED:
                 ok = !empty_out && !no_terms && dt != CONVT_DTYPE_F32 && gemm_eligible(dp, dt, nd);
                 break;
+            case CONVT_ROUTE_PHASE_GEMM_ALLPHASE:
+                ok = !empty_out && !no_terms && choose_allphase(pl, dp, nd, dt, 1);
+                break;
             case CONVT_ROUTE_GROUPED: ok = !empty_out && !no_terms && grouped_eligible(dp, dt); break;
             case CONVT_ROUTE_DIRECT: ok = !empty_out && !no_terms && direct_eligible(dp); break;
             case CONVT_ROUTE_NAIVE: ok = !empty_out && !no_terms; break;
@@ -808,6 +934,16 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
     info.route = route;
 
     // ---- tiles and workspace ------------------------------------------------
+    // two-byte problems that the all-phase kernel serves go to it
+    if (p->route == CONVT_ROUTE_AUTO && route == CONVT_ROUTE_PHASE_GEMM && choose_allphase(pl, dp, nd, dt, 65))
+        route = CONVT_ROUTE_PHASE_GEMM_ALLPHASE;
+    if (route == CONVT_ROUTE_PHASE_GEMM_ALLPHASE) {
+        pl->route = route;
+        info.route = route;
+        pl->wr_elems = 0;
+        info.workspace_bytes = 0;
+        return plan_backward(pl, I, K, S, P, D, O);
+    }
     int64_t blocks = 0;
     // the two-byte GEMM reads x in place when the problem suits that kernel
     if (route == CONVT_ROUTE_PHASE_GEMM && dt != CONVT_DTYPE_F32 && !choose_nchw(&dp, nd))

@@ -96,11 +96,16 @@ typedef enum convt_route {
     CONVT_ROUTE_GROUPED = 4,    /* grouped / few-channel stride-phase kernel, MFMA, LDS-staged output */
     CONVT_ROUTE_DIRECT = 5,     /* small-channel direct kernel, weight slab in LDS */
     CONVT_ROUTE_NAIVE = 6,      /* one thread per output, gathers its terms */
-    CONVT_ROUTE_PHASE_GEMM_PACKED = 7 /* two-byte types: the phase GEMM on a channel-chunked copy
+    CONVT_ROUTE_PHASE_GEMM_PACKED = 7, /* two-byte types: the phase GEMM on a channel-chunked copy
                                          of x that each call writes into the workspace (the
                                          PHASE_GEMM route reads x in place when the problem
                                          suits that kernel, and plans this one otherwise);
                                          forward only */
+    CONVT_ROUTE_PHASE_GEMM_ALLPHASE = 8 /* two-byte types, stride 2 and dilation 1 on the two
+                                           innermost axes: one block computes all four of their
+                                           stride phases of an output tile, reading x and W as
+                                           stored (no workspace, one launch per call); AUTO
+                                           plans it where it applies; forward only */
 } convt_route;
 
 /* How W is laid out in memory (the AWS Neuron conv3d_transpose page's
@@ -212,7 +217,9 @@ convt_status convt_plan(const convt_problem *problem, convt_plan_t *out, convt_p
  * one launch. On the PHASE_GEMM route with a two-byte element type, x must
  * be 4-byte aligned (that kernel reads neighbouring positions in pairs as
  * 32-bit words); a misaligned x is refused with CONVT_ERR_INVALID_ARGUMENT
- * before anything is enqueued.
+ * before anything is enqueued. On the PHASE_GEMM_ALLPHASE route x must be
+ * 4-byte aligned and W 16-byte aligned (W is read in 16-byte pieces of 8
+ * taps), else CONVT_ERR_INVALID_ARGUMENT; that route needs no workspace.
  */
 convt_status convt_forward(convt_plan_t plan, const void *x, const void *w, const void *bias,
                            void *y, void *workspace, void *stream);

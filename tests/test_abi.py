@@ -73,8 +73,8 @@ def test_workload_plans(name):
     assert pl.out_shape == oracle.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding,
                                             wl.dilation, wl.output_padding, wl.groups)
     expect_route = {"c1_2d_f32_small": "direct", "c2_1d_f32_upsampler": "phase_gemm",
-                    "c3_2d_bf16_generator": "phase_gemm", "c4a_2d_bf16_grouped": "grouped",
-                    "c4b_2d_bf16_dilated": "phase_gemm", "c5_3d_bf16_video": "phase_gemm"}[name]
+                    "c3_2d_bf16_generator": "phase_gemm_allphase", "c4a_2d_bf16_grouped": "grouped",
+                    "c4b_2d_bf16_dilated": "phase_gemm", "c5_3d_bf16_video": "phase_gemm_allphase"}[name]
     assert pl.route == expect_route
     b, cin = wl.x_shape[:2]
     assert pl.useful_flops == 2 * b * cin * wl.w_shape[1] * int(np.prod(wl.w_shape[2:])) * int(
@@ -189,8 +189,12 @@ def test_forced_routes():
 
 def test_workspace_sizes():
     wl = workloads.get("c3")
-    pl = plan(x_shape=wl.x_shape, w_shape=wl.w_shape, stride=wl.stride, padding=wl.padding,
+    # the all-phase kernel (the automatic choice here) reads W as stored
+    ap = plan(x_shape=wl.x_shape, w_shape=wl.w_shape, stride=wl.stride, padding=wl.padding,
               dtype="bf16", has_bias=True)
+    assert ap.route == "phase_gemm_allphase" and ap.workspace_bytes == 0
+    pl = plan(x_shape=wl.x_shape, w_shape=wl.w_shape, stride=wl.stride, padding=wl.padding,
+              dtype="bf16", has_bias=True, route="phase_gemm")
     # reordered weights (no padding needed at these sizes) and the per-tap
     # halo shift table (16 taps of 4 bytes); the bfloat16 GEMM reads x in
     # place
@@ -238,6 +242,34 @@ def test_phase_table_properties():
                 seen += taps
             assert sorted(seen) == list(range(k))
             assert qsum == O
+
+
+def test_allphase_route_rules():
+    """The all-phase route takes two-byte problems with stride 2 and
+    dilation 1 on the two innermost axes, 4 or 8 taps per phase, an even x
+    row and an output row length that is a multiple of 8; it is refused
+    otherwise, and never serves the backward pass."""
+    ok = dict(x_shape=(1, 16, 6, 16), w_shape=(16, 96, 4, 4), stride=2, padding=1, dtype="bf16")
+    assert plan(**ok, route="phase_gemm_allphase").route == "phase_gemm_allphase"
+    assert plan(**ok).route == "phase_gemm_allphase"
+    assert plan(**dict(ok, dtype="f16"), route="phase_gemm_allphase").workspace_bytes == 0
+    for bad in [dict(dtype="f32"), dict(stride=(2, 1)), dict(dilation=2), dict(x_shape=(1, 16, 6, 15)),
+                dict(padding=(1, 0)),                                    # output rows of 34
+                dict(w_shape=(16, 96, 3, 3)), dict(w_shape=(16, 96, 2, 2)),
+                dict(x_shape=(1, 16, 16), w_shape=(16, 96, 4), stride=2, padding=1),  # 1-D
+                dict(filter_layout="k_ci_co")]:
+        assert status_of(**dict(ok, **bad), route="phase_gemm_allphase") == 2, bad
+    # 64 or fewer output channels per group: the automatic choice is another kernel
+    assert plan(**dict(ok, w_shape=(16, 64, 4, 4))).route != "phase_gemm_allphase"
+    assert status_of(**ok, route_bwd="phase_gemm_allphase") == 1
+    # host-side refusals: x must be 4-byte and W 16-byte aligned
+    L = C.lib()
+    h = plan(**ok, has_bias=False).handle
+    fake = 4096
+    assert L.convt_forward(h, fake + 2, fake, None, fake, None, None) == 1
+    assert L.convt_forward(h, fake, fake + 8, None, fake, None, None) == 1
+    assert L.convt_forward_prepared(h, fake, fake + 8, None, fake, None, None) == 1
+    assert L.convt_forward_prepared(h, fake, None, None, fake, None, None) == 1
 
 
 def test_forward_refuses_bad_arguments_before_launch():
@@ -385,7 +417,7 @@ def test_scratch_entry_point_host_checks():
     fake = 4096  # never dereferenced: every call below fails a host-side check
     assert L.convt_forward_scratch(None, fake, fake, fake, fake, None) == 1
     big = plan(x_shape=(1, 2048, 4, 4), w_shape=(2048, 1024, 4, 4), stride=2, padding=1,
-               dtype="bf16", has_bias=True)
+               dtype="bf16", has_bias=True, route="phase_gemm")
     assert big.workspace_bytes > L.convt_scratch_max_bytes()
     assert L.convt_forward_scratch(big.handle, fake, fake, fake, fake, None) == 2
     # convt_plan_query reports what convt_plan did

@@ -22,7 +22,7 @@ from tests.gpu_util import TOL, check_full, say, to_device, to_host64, norm_erro
 
 pytestmark = pytest.mark.gpu
 
-ROUTES = ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"]
+ROUTES = ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "phase_gemm_allphase", "grouped"]
 
 CASES = [
     # name, x shape, w shape, stride, pad, dil, op, groups

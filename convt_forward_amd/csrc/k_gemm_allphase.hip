@@ -68,27 +68,31 @@ __device__ __forceinline__ int octet_rot(int q) {
 }
 
 constexpr int kAPThreads = 256;
-constexpr int kAPBM = 128;      // output channels per block
-constexpr int kAPPitch = 1040;  // epilogue staging bytes per channel (1 KiB + 16, spreading LDS banks)
 
 }  // namespace
 
-template <typename T, int TW, bool ACT>
+template <typename T, int TW, int MT, bool ACT>
 __global__ __launch_bounds__(kAPThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__restrict__ w,
                           const T *__restrict__ bias, T *__restrict__ y) {
     constexpr int SC = 8 / TW;         // 8-channel chunks per stage
     constexpr int NPAIR = TW / 2;      // K steps (tap pairs) per chunk
     static_assert(SC * NPAIR == 4, "four K steps per stage");
-    constexpr int BM = kAPBM;
+    static_assert(MT == 4 || MT == 2, "128 x 128 or 64 x 256 wave tiles");
+    constexpr int NT = 16 / MT;        // fragments along the positions
+    constexpr int BM = 32 * MT;        // output channels per block
+    constexpr int BN = 32 * NT;        // q positions per block (each wave holds all of them)
+    constexpr int WU = BM / 64;        // weight units (8 channels x 8 taps) per thread and stage
+    constexpr int XU = MT == 4 ? 1 : 2;  // halo units (2 positions x 8 channels) per thread and stage
     constexpr int NSLOT = 4 * TW;      // weight taps one chunk brings in (the block's four phases)
     constexpr int WSUB = NSLOT * BM * 16;
-    constexpr int WBUF = SC * WSUB;    // 64 KiB
-    constexpr int XROWS = 512 / SC;    // halo rows of one chunk
+    constexpr int WBUF = SC * WSUB;
+    constexpr int XROWS = 512 * XU / SC;  // halo rows of one chunk
     constexpr int XSUB = XROWS * 16;
     constexpr int STAGE = WBUF + SC * XSUB;
     constexpr int MAIN = 2 * STAGE;
-    constexpr int EPI = BM * kAPPitch;
+    constexpr int PITCH = 8 * BN + 16;  // epilogue staging bytes per channel (+16 spreads LDS banks)
+    constexpr int EPI = BM * PITCH;
     constexpr int BIAS_OFF = MAIN > EPI ? MAIN : EPI;
     constexpr int SINK = BIAS_OFF + BM * 4;
     using HT = typename std::conditional<std::is_same<T, _Float16>::value, _Float16, __bf16>::type;
@@ -135,30 +139,37 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     if (tid < BM && a.has_bias && co0 + tid < a.Cog)
         bias_v = half_to_f32<HT>(__builtin_bit_cast(uint16_t, bias[g * a.Cog + co0 + tid]));
 
-    // ---- halo unit of this thread: (chunk sc, position pair) with pairs
-    // fastest; xoff: byte offset of its 8 channels' first pair in the (batch,
-    // group) slice (out of range outside x, or past the halo); xdst: LDS
-    // offset of its first row within a stage, or -1 past the halo
+    // ---- halo units of this thread: u = tid + 256k (k < XU) is (chunk sc,
+    // position pair) with pairs fastest; xoff: byte offset of its 8 channels'
+    // first pair in the (batch, group) slice (out of range outside x, or past
+    // the halo); xdst: LDS offset of its first row within a stage, or -1 past
+    // the halo
     const uint32_t plane2 = (uint32_t)a.x_plane * 2u;
-    uint32_t xoff = kOutOfRange;
-    int xdst = -1;
-    if (tid < SC * npairs) {
-        const int sc = tid >= npairs ? 1 : 0;
-        const int pr = tid - sc * npairs;
-        const int hp = E2 >> 1;
-        const int prh = div_small(pr, hp), cp = pr - prh * hp;
-        const int e0 = div_small(prh, E1), e1 = prh - e0 * E1;
-        const int row = (e0 * E1 + e1) * E2 + 2 * cp;
-        xdst = WBUF + sc * XSUB + row * 16;
-        const int i0 = q00 + offd + e0, i1 = q01 + a.uh + e1, i2 = q02 + a.uw + 2 * cp;
-        if (i0 >= 0 && i0 < a.I[0] && i1 >= 0 && i1 < a.I[1] && i2 >= 0 && i2 < a.I[2])
-            xoff = (uint32_t)((i0 * a.I[1] + i1) * a.I[2] + i2) * 2u + (uint32_t)(sc * 8) * plane2;
+    uint32_t xoff[XU];
+    int xdst[XU];
+#pragma unroll
+    for (int k = 0; k < XU; ++k) {
+        const int u = tid + kAPThreads * k;
+        xoff[k] = kOutOfRange;
+        xdst[k] = -1;
+        if (u < SC * npairs) {
+            const int sc = u >= npairs ? 1 : 0;
+            const int pr = u - sc * npairs;
+            const int hp = E2 >> 1;
+            const int prh = div_small(pr, hp), cp = pr - prh * hp;
+            const int e0 = div_small(prh, E1), e1 = prh - e0 * E1;
+            const int row = (e0 * E1 + e1) * E2 + 2 * cp;
+            xdst[k] = WBUF + sc * XSUB + row * 16;
+            const int i0 = q00 + offd + e0, i1 = q01 + a.uh + e1, i2 = q02 + a.uw + 2 * cp;
+            if (i0 >= 0 && i0 < a.I[0] && i1 >= 0 && i1 < a.I[1] && i2 >= 0 && i2 < a.I[2])
+                xoff[k] = (uint32_t)((i0 * a.I[1] + i1) * a.I[2] + i2) * 2u + (uint32_t)(sc * 8) * plane2;
+        }
     }
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + ((int64_t)b * a.Ci + (int64_t)g * a.Cig) * a.x_plane,
                                                  (uint32_t)a.Cig * plane2);
     const uint32_t xstage = (uint32_t)(8 * SC) * plane2;  // bytes between stages' channels
 
-    // ---- weight units of this thread: u = tid + 256k (k = 0, 1) is octet j
+    // ---- weight units of this thread: u = tid + 256k (k < WU) is octet j
     // (of the NPAIR 8-tap octets of a W row that the block uses: depth tap
     // jd, octet o of its plane) of output channel co0 + co in chunk sc, octets
     // fastest, so that a wave's loads cover runs of whole rows; the 8 loads of
@@ -170,10 +181,10 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     const uint32_t wrow = (uint32_t)a.Cog * (uint32_t)a.ktot * 2u;  // bytes between input channels
     const __amdgpu_buffer_rsrc_t wrs =
         make_rsrc(w + (int64_t)g * a.Cig * a.Cog * a.ktot, (uint32_t)a.Cig * wrow);
-    uint32_t woff[2];
-    int wdst[2];
+    uint32_t woff[WU];
+    int wdst[WU];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < WU; ++k) {
         const int u = tid + kAPThreads * k;
         const int j = u % NPAIR, co = (u / NPAIR) % BM, sc = u / (NPAIR * BM);
         const int jd = j / noct, o = j - jd * noct;
@@ -204,20 +215,25 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
         aslot[p] = slot * (BM * 16) + (((lane & 31) ^ octet_rot<NPAIR>(slot >> 3)) * 16);
         boff[p] = ((jd * a.ostep_d * E1 + a.offh0[rh] + jh - a.uh) * E2 + a.offw0[rw] + jw - a.uw) * 16;
     }
-    int brow[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int n = nt * 32 + (lane & 31);
+    // halo row (bytes) of this lane's position n = nt * 32 + (lane & 31) for
+    // a zero tap shift: the box extents are powers of two with T2 >= 16, so
+    // the lane's 5 bits and nt's bits never carry into each other and the row
+    // splits into a per-lane part and a wave-uniform part per fragment
+    auto halo_row = [&](int n) __attribute__((always_inline)) {
         const int c2 = n & (T2 - 1), c1 = (n >> a.lgT2) & (T1 - 1), c0 = n >> (a.lgT1 + a.lgT2);
-        brow[nt] = ((c0 * E1 + c1) * E2 + c2) * 16;
-    }
+        return ((c0 * E1 + c1) * E2 + c2) * 16;
+    };
+    const int brow = halo_row(lane & 31);
+    int bnt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bnt[nt] = __builtin_amdgcn_readfirstlane(halo_row(nt * 32));
 
     // ---- register stages
     struct WRegs {
-        u32x4 v[2][8];
+        u32x4 v[WU][8];
     };
     struct XRegs {
-        uint32_t v[8];
+        uint32_t v[XU][8];
     };
     WRegs WR;
     XRegs X0, X1;
@@ -228,11 +244,11 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
             WR.v[k][e] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, woff[k], cs + (uint32_t)e * wrow, 0));
     };
-    auto load_x = [&](XRegs &xr, int c) __attribute__((always_inline)) {
+    auto load_x = [&](XRegs &xr, int k, int c) __attribute__((always_inline)) {
         const uint32_t cs = (uint32_t)c * xstage;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            xr.v[e] = __builtin_amdgcn_raw_buffer_load_b32(xrs, xoff, cs + (uint32_t)e * plane2, 0);
+            xr.v[k][e] = __builtin_amdgcn_raw_buffer_load_b32(xrs, xoff[k], cs + (uint32_t)e * plane2, 0);
     };
     // unit k's 8 x 8 block (input channel e holds taps 2j, 2j + 1 in word j)
     // as 8 slot rows (tap t holds channels 2j, 2j + 1 in word j)
@@ -254,32 +270,32 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     // the pair's two position rows (8 channels each); units past the halo
     // write the sink (a select, not a branch, keeps the K step in one
     // scheduling region)
-    auto store_x = [&](const XRegs &xr, unsigned char *stage) __attribute__((always_inline)) {
-        const uint32_t *d = xr.v;
+    auto store_x = [&](const XRegs &xr, int k, unsigned char *stage) __attribute__((always_inline)) {
+        const uint32_t *d = xr.v[k];
         const u32x4 r0 = {lo_pair(d[0], d[1]), lo_pair(d[2], d[3]), lo_pair(d[4], d[5]), lo_pair(d[6], d[7])};
         const u32x4 r1 = {hi_pair(d[0], d[1]), hi_pair(d[2], d[3]), hi_pair(d[4], d[5]), hi_pair(d[6], d[7])};
-        unsigned char *p0 = xdst >= 0 ? stage + xdst : lds + SINK;
+        unsigned char *p0 = xdst[k] >= 0 ? stage + xdst[k] : lds + SINK;
         *(u32x4 *)p0 = r0;
         *(u32x4 *)(p0 + 16) = r1;
     };
 
-    f32x16 acc[4][4];
-    Frag fa[2][4], fb[2][4];
-    auto read_frags = [&](Frag (&A)[4], Frag (&B)[4], const unsigned char *stage, int i)
+    f32x16 acc[MT][NT];
+    Frag fa[2][MT], fb[2][NT];
+    auto read_frags = [&](Frag (&A)[MT], Frag (&B)[NT], const unsigned char *stage, int i)
         __attribute__((always_inline)) {
         const int sc = i / NPAIR, p = i % NPAIR;
         const unsigned char *wt = stage + sc * WSUB + aslot[p];
-        const unsigned char *xt = stage + WBUF + sc * XSUB + boff[p];
+        const unsigned char *xt = stage + WBUF + sc * XSUB + boff[p];  // + brow + bnt[nt]
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) A[mt] = __builtin_bit_cast(Frag, *(const u32x4 *)(wt + mt * 512));
+        for (int mt = 0; mt < MT; ++mt) A[mt] = __builtin_bit_cast(Frag, *(const u32x4 *)(wt + mt * 512));
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) B[nt] = __builtin_bit_cast(Frag, *(const u32x4 *)(xt + brow[nt]));
+        for (int nt = 0; nt < NT; ++nt) B[nt] = __builtin_bit_cast(Frag, *(const u32x4 *)(xt + brow + bnt[nt]));
     };
-    auto mfma = [&](const Frag (&A)[4], const Frag (&B)[4]) __attribute__((always_inline)) {
+    auto mfma = [&](const Frag (&A)[MT], const Frag (&B)[NT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
                 if constexpr (std::is_same<T, _Float16>::value)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[mt], B[nt], acc[mt][nt], 0, 0, 0);
                 else
@@ -309,8 +325,8 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
         __builtin_amdgcn_sched_barrier(0);
         read_frags(fa[1], fb[1], cur, 1);
         mfma(fa[0], fb[0]);
-        store_x(xs, nxt);
-        load_x(xl, cl);
+        store_x(xs, 0, nxt);
+        load_x(xl, 0, cl);
         interleave(std::integral_constant<int, 2>{});
         __builtin_amdgcn_sched_barrier(0);
         read_frags(fa[0], fb[0], cur, 2);
@@ -321,8 +337,13 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
         __builtin_amdgcn_sched_barrier(0);
         read_frags(fa[1], fb[1], cur, 3);
         mfma(fa[0], fb[0]);
-        store_w(1, nxt);
-        load_w(1, cl);
+        if constexpr (WU == 2) {
+            store_w(1, nxt);
+            load_w(1, cl);
+        } else {
+            store_x(xs, 1, nxt);
+            load_x(xl, 1, cl);
+        }
         interleave(std::integral_constant<int, 2>{});
         __builtin_amdgcn_sched_barrier(0);
         barrier();
@@ -337,26 +358,29 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     };
 
     unsigned char *buf0 = lds, *buf1 = lds + STAGE;
-    load_w(0, 0);
-    load_w(1, 0);
-    load_x(X0, 0);
-    load_x(X1, 1);
-    store_w(0, buf0);
-    store_w(1, buf0);
-    store_x(X0, buf0);
+#pragma unroll
+    for (int k = 0; k < WU; ++k) load_w(k, 0);
+#pragma unroll
+    for (int k = 0; k < XU; ++k) load_x(X0, k, 0);
+#pragma unroll
+    for (int k = 0; k < XU; ++k) load_x(X1, k, 1);
+#pragma unroll
+    for (int k = 0; k < WU; ++k) store_w(k, buf0);
+#pragma unroll
+    for (int k = 0; k < XU; ++k) store_x(X0, k, buf0);
     if (tid < BM) bias_s[tid] = bias_v;
-    load_w(0, 1);
-    load_w(1, 1);
+#pragma unroll
+    for (int k = 0; k < WU; ++k) load_w(k, 1);
     barrier();
     // the accumulators start at the bias of their output channel (lane l of
     // fragment (mt, nt) holds rows mt*32 + 8*(j/4) + 4*(l/32) + j%4)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const float bv = bias_s[mt * 32 + 8 * (j >> 2) + 4 * kv + (j & 3)];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) acc[mt][nt][j] = bv;
+            for (int nt = 0; nt < NT; ++nt) acc[mt][nt][j] = bv;
         }
     read_frags(fa[0], fb[0], buf0, 0);
     for (int s = 0; s < a.nstages; s += 2) {
@@ -371,12 +395,12 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     auto stage_out = [&](auto act_tag) __attribute__((always_inline)) {
         constexpr int A = decltype(act_tag)::value;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             const int n = nt * 32 + (lane & 31);
             const int c2 = n & (T2 - 1), c1 = (n >> a.lgT2) & (T1 - 1), c0 = n >> (a.lgT1 + a.lgT2);
             const int pos = ((c0 * 2 * T1 + 2 * c1 + rh) * 2 * T2 + 2 * c2 + rw) * 2;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int j = 0; j < 16; j += 2) {
                     const int co = mt * 32 + 8 * (j >> 2) + 4 * kv + (j & 3);
@@ -386,8 +410,8 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
                         v1 = activate<true>(A, v1);
                     }
                     const uint32_t pk = pack_half2<HT>(v0, v1);
-                    *(uint16_t *)(lds + co * kAPPitch + pos) = (uint16_t)pk;
-                    *(uint16_t *)(lds + (co + 1) * kAPPitch + pos) = (uint16_t)(pk >> 16);
+                    *(uint16_t *)(lds + co * PITCH + pos) = (uint16_t)pk;
+                    *(uint16_t *)(lds + (co + 1) * PITCH + pos) = (uint16_t)(pk >> 16);
                 }
         }
     };
@@ -406,8 +430,8 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     barrier();
 
     // ---- stores: per channel the block's outputs are T0 * 2T1 rows of 2T2
-    // (a multiple of 32) outputs, 1 KiB in staging order; piece pc (16 bytes)
-    // of channel co = pc / 64. Channels past Cog fall outside the store
+    // (a multiple of 32) outputs, 8 * BN bytes in staging order; piece pc (16
+    // bytes) of channel co = pc / (BN / 2). Channels past Cog fall outside the store
     // resource (which ends at Cog); rows past the output (or q past the depth
     // residue's count) take the out-of-range offset.
     const uint32_t ypl2 = (uint32_t)a.y_plane * 2u;
@@ -418,11 +442,12 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
 #pragma unroll 4
     for (int i = 0; i < 32; ++i) {
         const int pc = tid + kAPThreads * i;
-        const int co = pc >> 6, rem = pc & 63;
+        constexpr int LGPC = MT == 4 ? 6 : 7;  // log2 of the pieces per channel, BN / 2
+        const int co = pc >> LGPC, rem = pc & ((1 << LGPC) - 1);
         const int row = rem >> lgp, cp = rem & ((1 << lgp) - 1);
         const int c0 = row >> (a.lgT1 + 1), r1 = row & (2 * T1 - 1);
         const int od = a.S0 * (q00 + c0) + rd, oh = 2 * q01 + r1, ow = 2 * q02 + 8 * cp;
-        const u32x4 v = *(const u32x4 *)(lds + co * kAPPitch + rem * 16);
+        const u32x4 v = *(const u32x4 *)(lds + co * PITCH + rem * 16);
         uint32_t off = kOutOfRange;
         if (q00 + c0 < qnd && oh < a.O[1] && ow < a.O[2])
             off = (uint32_t)(co0 + co) * ypl2 + (uint32_t)((od * a.O[1] + oh) * a.O[2] + ow) * 2u;
@@ -430,31 +455,37 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     }
 }
 
-template <typename T, int TW>
+template <typename T, int TW, int MT>
 static hipError_t launch_allphase_t(const Plan &pl, const void *x, const void *w, const void *bias,
                                     void *y, hipStream_t stream) {
     const AllPhaseArgs &a = pl.ap;
     const dim3 grid(a.n_blocks), block(kAPThreads);
     if (a.act != CONVT_ACT_NONE)
-        hipLaunchKernelGGL((allphase_gemm_kernel<T, TW, true>), grid, block, 0, stream, a, (const T *)x,
+        hipLaunchKernelGGL((allphase_gemm_kernel<T, TW, MT, true>), grid, block, 0, stream, a, (const T *)x,
                            (const T *)w, (const T *)bias, (T *)y);
     else
-        hipLaunchKernelGGL((allphase_gemm_kernel<T, TW, false>), grid, block, 0, stream, a, (const T *)x,
+        hipLaunchKernelGGL((allphase_gemm_kernel<T, TW, MT, false>), grid, block, 0, stream, a, (const T *)x,
                            (const T *)w, (const T *)bias, (T *)y);
     return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_allphase_cfg(const Plan &pl, const void *x, const void *w, const void *bias,
+                                      void *y, hipStream_t stream) {
+    const int tw = pl.ap_tw, mt = pl.ap_mt;
+    if (tw == 4 && mt == 4) return launch_allphase_t<T, 4, 4>(pl, x, w, bias, y, stream);
+    if (tw == 4 && mt == 2) return launch_allphase_t<T, 4, 2>(pl, x, w, bias, y, stream);
+    if (tw == 8 && mt == 4) return launch_allphase_t<T, 8, 4>(pl, x, w, bias, y, stream);
+    if (tw == 8 && mt == 2) return launch_allphase_t<T, 8, 2>(pl, x, w, bias, y, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_allphase(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
                            hipStream_t stream) {
     if (pl.ap.n_blocks <= 0) return hipSuccess;
     if (pl.route != CONVT_ROUTE_PHASE_GEMM_ALLPHASE || pl.elem_bytes != 2) return hipErrorInvalidValue;
-    if (pl.ap_tw == 4)
-        return pl.dp.f16 ? launch_allphase_t<_Float16, 4>(pl, x, w, bias, y, stream)
-                         : launch_allphase_t<uint16_t, 4>(pl, x, w, bias, y, stream);
-    if (pl.ap_tw == 8)
-        return pl.dp.f16 ? launch_allphase_t<_Float16, 8>(pl, x, w, bias, y, stream)
-                         : launch_allphase_t<uint16_t, 8>(pl, x, w, bias, y, stream);
-    return hipErrorInvalidValue;
+    return pl.dp.f16 ? launch_allphase_cfg<_Float16>(pl, x, w, bias, y, stream)
+                     : launch_allphase_cfg<uint16_t>(pl, x, w, bias, y, stream);
 }
 
 }  // namespace convt

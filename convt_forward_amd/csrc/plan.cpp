@@ -362,31 +362,40 @@ bool choose_allphase(Plan *pl, const DevParams &dp, int ndim, int dtype, int64_t
     const int64_t cig_span = dp.Cig + 3 * 8 * sc;  // channels the prefetch may address
     if (!buffer_fits(cig_span * dp.x_plane * 2) ||
         !buffer_fits(cig_span * dp.Cog * dp.ktot * 2 + (int64_t)256 * dp.ktot * 2) ||
-        !buffer_fits(((int64_t)dp.Cog + 128) * dp.y_plane * 2))
+        !buffer_fits(((int64_t)dp.Cog + 128) * dp.y_plane * 2))  // rows up to a tile past Cog
         return false;
     const int uw = a2.umin & ~1;
-    const int64_t rows_cap = 512 / sc;
     double best = 0;
-    int bt[3] = {0, 0, 0};
-    for (int t2 = 16; t2 <= 128; t2 *= 2) {
-        for (int t1 = 1; t1 * t2 <= 128; t1 *= 2) {
-            const int t0 = 128 / (t1 * t2);
-            if (ndim < 3 && t0 != 1) continue;
-            const int64_t e0 = t0 + (int64_t)(nd - 1) * a0.ostep;
-            const int64_t e1 = t1 + a1.umax - a1.umin;
-            const int64_t e2 = (t2 + a2.umax - uw + 1) & ~(int64_t)1;
-            const int64_t rows = e0 * e1 * e2;
-            if (rows > rows_cap) continue;
-            const int64_t nt = ceil_div(a0.qmax, t0) * ceil_div(a1.qmax, t1) * ceil_div(a2.qmax, t2);
-            const int64_t blocks = nt * ceil_div(dp.Cog, 128) * a0.S * dp.G * dp.B;
-            // one block per CU; a stage: 2048 MFMA cycles per wave plus the
-            // halo the block stages
-            const double t = std::ceil((double)blocks / 256.0) * (2048.0 + 2.0 * (double)rows);
-            if (bt[2] == 0 || t < best * 0.999) {
-                best = t;
-                bt[0] = t0;
-                bt[1] = t1;
-                bt[2] = t2;
+    int bt[3] = {0, 0, 0}, bmt = 0;
+    // wave tiles of 64 channels x 256 positions (mt 2) or 128 x 128 (mt 4);
+    // a block holds 32 * mt channels and a q box of 512 / mt positions, and
+    // stages up to 512 * (halo units per thread: 2 or 1) / sc halo rows
+    for (int mt = 2; mt <= 4; mt += 2) {
+        const int bn = 512 / mt, bm = 32 * mt;
+        const int64_t rows_cap = 512 * (mt == 4 ? 1 : 2) / sc;
+        for (int t2 = 16; t2 <= bn; t2 *= 2) {
+            for (int t1 = 1; t1 * t2 <= bn; t1 *= 2) {
+                const int t0 = bn / (t1 * t2);
+                if (ndim < 3 && t0 != 1) continue;
+                const int64_t e0 = t0 + (int64_t)(nd - 1) * a0.ostep;
+                const int64_t e1 = t1 + a1.umax - a1.umin;
+                const int64_t e2 = (t2 + a2.umax - uw + 1) & ~(int64_t)1;
+                const int64_t rows = e0 * e1 * e2;
+                if (rows > rows_cap) continue;
+                const int64_t nt = ceil_div(a0.qmax, t0) * ceil_div(a1.qmax, t1) * ceil_div(a2.qmax, t2);
+                const int64_t blocks = nt * ceil_div(dp.Cog, bm) * a0.S * dp.G * dp.B;
+                // one block per CU; a stage: 2048 MFMA cycles per wave, plus
+                // the staging of its weights (64 KiB for 128 channels) and
+                // halo, which the MFMAs hide only in part
+                const double stage = 2048.0 + 8.0 * bm + 2.0 * (double)rows;
+                const double t = std::ceil((double)blocks / 256.0) * stage;
+                if (bt[2] == 0 || t < best * 0.999) {
+                    best = t;
+                    bt[0] = t0;
+                    bt[1] = t1;
+                    bt[2] = t2;
+                    bmt = mt;
+                }
             }
         }
     }
@@ -408,7 +417,7 @@ bool choose_allphase(Plan *pl, const DevParams &dp, int ndim, int dtype, int64_t
     ap.ktot = dp.ktot;
     ap.lgT1 = __builtin_ctz((unsigned)bt[1]);
     ap.lgT2 = __builtin_ctz((unsigned)bt[2]);
-    ap.n_co_tiles = (int32_t)ceil_div(dp.Cog, 128);
+    ap.n_co_tiles = (int32_t)ceil_div(dp.Cog, 32 * bmt);
     ap.n_rd = a0.S;
     const int64_t blocks = (int64_t)ap.nt[0] * ap.nt[1] * ap.nt[2] * ap.n_co_tiles * ap.n_rd * dp.G * dp.B;
     if (blocks > ((int64_t)1 << 31) - 1) return false;
@@ -447,6 +456,7 @@ bool choose_allphase(Plan *pl, const DevParams &dp, int ndim, int dtype, int64_t
         ap.qnd[r] = a0.qn[r];
     }
     pl->ap_tw = tw;
+    pl->ap_mt = bmt;
     return true;
 }
 

@@ -135,9 +135,6 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     const int E0 = T0 + (a.nd - 1) * a.ostep_d, E1 = a.E1, E2 = a.E2;
     const int npairs = E0 * E1 * (E2 >> 1);  // position pairs of one chunk's halo
 
-    float bias_v = 0.0f;
-    if (tid < BM && a.has_bias && co0 + tid < a.Cog)
-        bias_v = half_to_f32<HT>(__builtin_bit_cast(uint16_t, bias[g * a.Cog + co0 + tid]));
 
     // ---- halo units of this thread: u = tid + 256k (k < XU) is (chunk sc,
     // position pair) with pairs fastest; xoff: byte offset of its 8 channels'
@@ -364,11 +361,19 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     for (int k = 0; k < XU; ++k) load_x(X0, k, 0);
 #pragma unroll
     for (int k = 0; k < XU; ++k) load_x(X1, k, 1);
+    // the bias of the block's channels, requested behind the first stages'
+    // loads through a range-checked load (zero past Cog or without a bias),
+    // not a branch, so that nothing waits on it before they are issued
+    const __amdgpu_buffer_rsrc_t brs =
+        make_rsrc(a.has_bias ? (const void *)(bias + g * a.Cog) : (const void *)bias,
+                  a.has_bias ? (uint32_t)a.Cog * 2u : 0u);
+    const uint16_t bias_raw = __builtin_amdgcn_raw_buffer_load_b16(
+        brs, tid < BM ? (uint32_t)(co0 + tid) * 2u : kOutOfRange, 0, 0);
 #pragma unroll
     for (int k = 0; k < WU; ++k) store_w(k, buf0);
 #pragma unroll
     for (int k = 0; k < XU; ++k) store_x(X0, k, buf0);
-    if (tid < BM) bias_s[tid] = bias_v;
+    if (tid < BM) bias_s[tid] = half_to_f32<HT>(bias_raw);
 #pragma unroll
     for (int k = 0; k < WU; ++k) load_w(k, 1);
     barrier();

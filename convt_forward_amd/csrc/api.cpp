@@ -24,8 +24,7 @@ int64_t numel(const int64_t *shape, int n) {
 convt_status device_status(hipError_t e) { return e == hipSuccess ? CONVT_OK : CONVT_ERR_DEVICE; }
 
 bool needs_weights_in_workspace(int route) {
-    return route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_PHASE_GEMM_PACKED ||
-           route == CONVT_ROUTE_GROUPED;
+    return route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_PHASE_GEMM_PACKED;
 }
 
 // The two-byte phase GEMM that reads x in place takes neighbouring positions
@@ -114,8 +113,8 @@ convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void
             return device_status(convt::launch_phase_gemm(pl, xin, workspace, bias, y, s));
         }
         case CONVT_ROUTE_GROUPED:
-            if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
-            return device_status(convt::launch_grouped(pl, x, workspace, bias, y, s));
+            if (!w) return CONVT_ERR_INVALID_ARGUMENT;
+            return device_status(convt::launch_grouped(pl, x, w, bias, y, s));
         default:
             return CONVT_ERR_UNSUPPORTED;
     }

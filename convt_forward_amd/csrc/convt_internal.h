@@ -132,6 +132,21 @@ struct AllPhaseArgs {
     int32_t kd0[kMaxS], offd[kMaxS], qnd[kMaxS];
 };
 
+// Grouped route: the kernel's slot table and tap map, built by the planner
+// and passed with the kernel's arguments (the kernel copies the table to LDS
+// and gathers its group's weights from W as stored).
+constexpr int kGrpTabMax = 2 * kMaxPhaseTab + 64;  // int2 entries: 2 per phase, then the slots
+constexpr int kGrpMaxTaps = 64;                    // taps of the grouped route (its weight slab bound)
+static_assert(kGrpTabMax <= 256, "the grouped kernel copies one table entry per thread");
+struct GrpTables {
+    int32_t tab_n;                    // int2 entries used
+    int32_t tab[2 * kGrpTabMax];      // per phase an int4 record (q counts; first slot | slot
+                                      // count << 16), then per (tap, 8-channel slice) slot the
+                                      // halo byte offset of the tap's window and the element
+                                      // offset of its weights in the LDS slab [tap][16][Cig]
+    uint8_t tg_of[kGrpMaxTaps];       // tap in plan order of each stored tap (W's own tap index)
+};
+
 struct Plan {
     convt_problem prob;
     convt_plan_info info;
@@ -143,6 +158,7 @@ struct Plan {
     int64_t xp_offset;  // bfloat16 phase GEMM: byte offset of the channel-chunked copy of x
     int64_t xp_bytes;   // its size (0 when not used)
     int32_t elem_bytes; // 4 (float32) or 2 (bfloat16)
+    GrpTables gt;       // CONVT_ROUTE_GROUPED: the kernel's tables
     AllPhaseArgs ap;    // CONVT_ROUTE_PHASE_GEMM_ALLPHASE: the kernel's arguments
     int32_t ap_tw;      // ... taps per phase and chunk (4 or 8)
     int32_t ap_mt;      // ... 32-channel fragments per wave (4: 128 x 128 wave tiles, 2: 64 x 256)

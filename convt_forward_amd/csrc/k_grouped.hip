@@ -37,6 +37,9 @@
 //     moves into the padding lanes (DPP) and a lane permutation orders the
 //     row pieces; otherwise chunks go through a per-wave LDS staging area.
 //     Edge segments are stored straight from registers.
+#include <cstddef>
+#include <cstring>
+
 #include "kcommon.h"
 #include "launch.h"
 
@@ -101,6 +104,10 @@ struct GrpArgs {
     int32_t grp_hwp, grp_hshift, grp_nk, grp_nsc;
     int32_t grp_w_off, grp_tab_off, grp_st_off, grp_st_pitch;
     int32_t ktot, nphase;
+    int32_t w_layout;                   // convt_filter_layout of W
+    int32_t tab_n;                      // int2 entries of tab
+    uint32_t tg_of[kGrpMaxTaps / 4];    // plan-order tap of each stored tap, 4 bytes per word
+    int32_t tab[2 * kGrpTabMax];        // the slot table (GrpTables)
 };
 
 // Eight waves per SIMD (8 blocks per CU) where the registers allow it: the
@@ -109,9 +116,8 @@ struct GrpArgs {
 // registers (S2 * KS > 2) trade occupancy for having no spills.
 template <int S2, int KS, typename E, int ACT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 2 ? 8 : 4, 8))) void grouped_kernel(
-    GrpArgs p, const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-    const int2 *__restrict__ gtab, const uint16_t *__restrict__ bias, uint16_t *__restrict__ y,
-    int st_align, int x_vec) {
+    GrpArgs p, const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ y, int st_align, int x_vec) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const uint16_t *wsl = (const uint16_t *)(lds + p.grp_w_off);
 
@@ -130,24 +136,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     const int h0 = qd + a0.umin, h1 = q0h + a1.umin, h2 = a2.umin;
     const int nrow = p.hd * HH;
 
-    // 1a. the group's weights [tap][16][Cig] and the slot table (written
-    // with the reordered weights: a record per phase, then per (tap, slice)
+    // 1a. the group's weights, gathered from W as stored into the LDS slab
+    // [tap][16 channels][Cig], taps in the plan's order (tg_of maps each
+    // stored tap to its place, so the tap flip and the phase grouping happen
+    // here), and the slot table (a record per phase, then per (tap, slice)
     // slot the LDS byte offset of the tap's window origin in the halo and the
-    // weight offset) -> LDS by DMA, in 1 KiB and 256-byte pieces dealt to the
-    // waves (their areas are whole pieces); the halo follows.
-    const int nvec = p.ktot * tiles::kGrpCog * noct, nslot = 2 * p.nphase + p.ktot * noct;
-    {
-        const u32x4 wrw = rsrc_words(wr + (int64_t)g * p.ktot * tiles::kGrpCog * Cig, (uint32_t)nvec * 16);
-        const uint32_t w_lds =
-            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(lds + p.grp_w_off);
-        for (int j = wave; j * 64 < nvec; j += 4)  // uniform
-            copy_to_lds<16>(w_lds + (uint32_t)j * 1024, (uint32_t)(j * 64 + lane) * 16, wrw);
-        const u32x4 trw = rsrc_words(gtab, (uint32_t)nslot * 8);
-        const uint32_t t_lds =
-            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)(lds + p.grp_tab_off);
-        for (int j = wave; j * 64 < 2 * nslot; j += 4)  // uniform
-            copy_to_lds<4>(t_lds + (uint32_t)j * 256, (uint32_t)(j * 64 + lane) * 4, trw);
+    // weight offset), both from the kernel arguments. Every read is issued
+    // here at once, none depending on another (W in its own memory order,
+    // coalesced; the map entry of each element's stored tap and the table
+    // entry per lane): no read of the argument segment (a slow path) sits in
+    // a dependent chain. They are written before the halo is staged (the
+    // halo's registers leave no room to hold them across it).
+    const unsigned char *kseg = (const unsigned char *)__builtin_amdgcn_kernarg_segment_ptr();
+    const uint8_t *tgp = kseg + offsetof(GrpArgs, tg_of);
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(w, (uint32_t)p.Ci * (uint32_t)p.Cog * (uint32_t)p.ktot * 2u);
+    const int nraw = Cig * p.Cog * p.ktot;  // the group's elements of W
+    // element e of the group's W in memory order: the element (zero past the
+    // group), its stored tap and its offset co * Cig + cil within a tap
+    auto raw_elem = [&](int e, int &st, int &cc) __attribute__((always_inline)) {
+        int cil, co;
+        uint32_t o;
+        if (p.w_layout == CONVT_FILTER_K_CI_CO) {  // [k][C_in][Cog]
+            const int r = div_small(e, p.Cog);
+            co = e - r * p.Cog;
+            st = div_small(r, Cig);
+            cil = r - st * Cig;
+            o = ((uint32_t)st * p.Ci + g * Cig + cil) * p.Cog + co;
+        } else if (p.w_layout == CONVT_FILTER_K_CO_CI) {  // [k][C_out][Cig]
+            const int r = div_small(e, Cig);
+            cil = e - r * Cig;
+            st = div_small(r, p.Cog);
+            co = r - st * p.Cog;
+            o = ((uint32_t)st * p.Co + g * p.Cog + co) * Cig + cil;
+        } else {  // [C_in][Cog][k]
+            const int r = div_small(e, p.ktot);
+            st = e - r * p.ktot;
+            cil = div_small(r, p.Cog);
+            co = r - cil * p.Cog;
+            o = (uint32_t)(g * Cig) * p.Cog * p.ktot + (uint32_t)e;
+        }
+        cc = co * Cig + cil;
+        st = e < nraw ? st : 0;
+        return __builtin_amdgcn_raw_buffer_load_b16(wrs, e < nraw ? o * 2u : kOutOfRange, 0, 0);
+    };
+    // the first 4 elements of each thread: value | (co * Cig + cil) << 16
+    // (< 2^10), and the plan-order tap of its stored tap
+    uint32_t wfirst[4];
+    uint32_t wtg[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        int st, cc;
+        wfirst[u] = (uint32_t)raw_elem(tid + 256 * u, st, cc) | (uint32_t)cc << 16;
+        wtg[u] = tgp[st];
     }
+    // the table has at most kGrpTabMax <= 256 entries: one per thread
+    const int2 tab0 = ((const int2 *)(kseg + offsetof(GrpArgs, tab)))[min(tid, kGrpTabMax - 1)];
+    // the slot table, then the weight slab: the first batch, W's remaining
+    // elements (past 1024), and zero rows for the channels past Cog
+    auto write_tables = [&]() __attribute__((always_inline)) {
+        if (tid < p.tab_n) ((int2 *)(lds + p.grp_tab_off))[tid] = tab0;
+        uint16_t *slab = (uint16_t *)(lds + p.grp_w_off);
+        const int tap_el = tiles::kGrpCog * Cig;  // slab elements per tap
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (tid + 256 * u < nraw) slab[(int)wtg[u] * tap_el + (int)(wfirst[u] >> 16)] = (uint16_t)wfirst[u];
+        for (int e0 = 1024; e0 < nraw; e0 += 1024) {  // uniform
+            uint16_t v[4];
+            int cc[4], tg[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                int st;
+                v[u] = raw_elem(e0 + tid + 256 * u, st, cc[u]);
+                tg[u] = tgp[st];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (e0 + tid + 256 * u < nraw) slab[tg[u] * tap_el + cc[u]] = v[u];
+        }
+        const int zc = tiles::kGrpCog - p.Cog;  // padding channels per tap
+        for (int e = tid; e < p.ktot * zc * Cig; e += 256) {
+            const int r = div_small(e, Cig), cil = e - r * Cig;
+            const int tg = div_small(r, zc), c = r - tg * zc;
+            slab[(tg * tiles::kGrpCog + p.Cog + c) * Cig + cil] = 0;
+        }
+    };
+    write_tables();
     // 1b. input halo -> LDS cells; positions outside the input read an
     // out-of-range offset (zero).
     const uint32_t xpl_bytes = (uint32_t)p.x_plane * 2;
@@ -171,20 +245,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
         // input read zero. Neighbouring lanes take neighbouring rows, whose
         // cells the odd row pitch spreads over the LDS banks.
         const int units = nrow * noct * nk;
-        for (int u = tid; u < units; u += 256) {
+        // unit u's source offset (out of range for rows outside the input
+        // and past the last unit) and its first cell
+        auto unit_at = [&](int u, unsigned char *&dst) __attribute__((always_inline)) {
             const int row = u % nrow, t = u / nrow;
             const int oct = t % noct, k = t / noct;
             const int d = row / HH, h = row - d * HH;
             const int i0 = h0 + d, i1 = h1 + h;
-            const bool ok = i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I;
-            const uint32_t off =
-                ok ? (uint32_t)(oct * 8) * xpl_bytes + (uint32_t)((i0 * a1.I + i1) * a2.I + 8 * k) * 2
-                   : kGrpOutOfRange;
-            u32x4 v[8];  // v[c]: positions 8k .. 8k+7 of channel 8*oct + c
+            const bool ok = u < units && i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I;
+            dst = lds + ((row * noct + oct) * HWP + col0 + 8 * k) * 16;
+            return ok ? (uint32_t)(oct * 8) * xpl_bytes + (uint32_t)((i0 * a1.I + i1) * a2.I + 8 * k) * 2
+                      : kGrpOutOfRange;
+        };
+        // v[c]: positions 8k .. 8k+7 of channel 8*oct + c
+        auto unit_load = [&](uint32_t off, u32x4 (&v)[8]) __attribute__((always_inline)) {
 #pragma unroll
             for (int c = 0; c < 8; ++c)
                 v[c] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off + c * xpl_bytes, 0, 0);
-            unsigned char *dst = lds + ((row * noct + oct) * HWP + col0 + 8 * k) * 16;
+        };
+        auto unit_store = [&](const u32x4 (&v)[8], unsigned char *dst) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 u32x4 cell;  // position 8k + e, channels 2i, 2i+1 in word i
@@ -194,6 +273,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
                                                     (e & 1) ? kPermHi : kPermLo);
                 *(u32x4 *)(dst + e * 16) = cell;
             }
+        };
+        for (int u = tid; u < units; u += 256) {
+            unsigned char *dst;
+            u32x4 v[8];
+            unit_load(unit_at(u, dst), v);
+            unit_store(v, dst);
         }
     } else {
         // Element loads: a wave takes whole halo rows (one slice each) and its
@@ -599,7 +684,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     compute_rows(0, R);
 }
 
-static GrpArgs grp_args(const DevParams &p) {
+static GrpArgs grp_args(const Plan &pl) {
+    const DevParams &p = pl.dp;
     GrpArgs a;
     for (int i = 0; i < 3; ++i) a.ax[i] = GrpAxis{p.ax[i].I, p.ax[i].O, p.ax[i].S, p.ax[i].umin};
     a.G = p.G; a.Ci = p.Ci; a.Co = p.Co; a.Cig = p.Cig; a.Cog = p.Cog; a.has_bias = p.has_bias;
@@ -609,24 +695,29 @@ static GrpArgs grp_args(const DevParams &p) {
     a.grp_w_off = p.grp_w_off; a.grp_tab_off = p.grp_tab_off; a.grp_st_off = p.grp_st_off;
     a.grp_st_pitch = p.grp_st_pitch;
     a.ktot = p.ktot; a.nphase = p.nphase;
+    a.w_layout = p.w_layout;
+    a.tab_n = pl.gt.tab_n;
+    memcpy(a.tg_of, pl.gt.tg_of, sizeof(a.tg_of));
+    memcpy(a.tab, pl.gt.tab, sizeof(a.tab));
     return a;
 }
 
 template <int S2, int KS, typename E>
-static void launch_grouped_e(const DevParams &p, const void *x, const void *wr, const int2 *gtab,
-                             const void *bias, void *y, int st_align, int x_vec, hipStream_t stream) {
+static void launch_grouped_e(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
+                             int st_align, int x_vec, hipStream_t stream) {
+    const DevParams &p = pl.dp;
     const dim3 grid(p.G * p.B, p.nt_h, p.nt_d);
     const size_t lds = (size_t)p.grp_lds_bytes;
-    const GrpArgs a = grp_args(p);
-    const uint16_t *xs = (const uint16_t *)x, *ws = (const uint16_t *)wr,
+    const GrpArgs a = grp_args(pl);
+    const uint16_t *xs = (const uint16_t *)x, *ws = (const uint16_t *)w,
                    *bs = (const uint16_t *)bias;
     uint16_t *ys = (uint16_t *)y;
     // one instance per activation: the activation folds into the unrolled
     // store loop (a run-time switch there splits it into branches the
     // compiler cannot schedule across, which cost even ReLU 70%)
 #define CONVT_GRP_LAUNCH(A)                                                                      \
-    hipLaunchKernelGGL((grouped_kernel<S2, KS, E, A>), grid, dim3(256), lds, stream, a, xs, ws, \
-                       gtab, bs, ys, st_align, x_vec)
+    hipLaunchKernelGGL((grouped_kernel<S2, KS, E, A>), grid, dim3(256), lds, stream, a, xs, ws, bs, \
+                       ys, st_align, x_vec)
     switch (p.act) {
         case CONVT_ACT_RELU: CONVT_GRP_LAUNCH(CONVT_ACT_RELU); break;
         case CONVT_ACT_SIGMOID: CONVT_GRP_LAUNCH(CONVT_ACT_SIGMOID); break;
@@ -639,28 +730,27 @@ static void launch_grouped_e(const DevParams &p, const void *x, const void *wr, 
 }
 
 template <int S2, int KS>
-static void launch_grouped_t(const DevParams &p, const void *x, const void *wr, const int2 *gtab,
-                             const void *bias, void *y, int st_align, int x_vec, hipStream_t stream) {
-    if (p.f16)
-        launch_grouped_e<S2, KS, _Float16>(p, x, wr, gtab, bias, y, st_align, x_vec, stream);
+static void launch_grouped_t(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
+                             int st_align, int x_vec, hipStream_t stream) {
+    if (pl.dp.f16)
+        launch_grouped_e<S2, KS, _Float16>(pl, x, w, bias, y, st_align, x_vec, stream);
     else
-        launch_grouped_e<S2, KS, __bf16>(p, x, wr, gtab, bias, y, st_align, x_vec, stream);
+        launch_grouped_e<S2, KS, __bf16>(pl, x, w, bias, y, st_align, x_vec, stream);
 }
 
 template <int S2>
-static hipError_t launch_grouped_s(const DevParams &p, const void *x, const void *wr,
-                                   const int2 *gtab, const void *bias, void *y, int st_align,
-                                   int x_vec, hipStream_t stream) {
-    switch (p.grp_ksteps) {
-        case 1: launch_grouped_t<S2, 1>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
-        case 2: launch_grouped_t<S2, 2>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
-        case 4: launch_grouped_t<S2, 4>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
+static hipError_t launch_grouped_s(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
+                                   int st_align, int x_vec, hipStream_t stream) {
+    switch (pl.dp.grp_ksteps) {
+        case 1: launch_grouped_t<S2, 1>(pl, x, w, bias, y, st_align, x_vec, stream); break;
+        case 2: launch_grouped_t<S2, 2>(pl, x, w, bias, y, st_align, x_vec, stream); break;
+        case 4: launch_grouped_t<S2, 4>(pl, x, w, bias, y, st_align, x_vec, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipSuccess;
 }
 
-hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const void *bias, void *y,
+hipError_t launch_grouped(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
                           hipStream_t stream) {
     const DevParams &p = pl.dp;
     if (p.n_blocks <= 0) return hipSuccess;
@@ -680,15 +770,14 @@ hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const v
     // chunked halo gather: x rows are whole 16-byte chunks (the plan then
     // gives the halo rows whole chunks of columns)
     const int x_vec = (uintptr_t)x % 16 == 0 && p.grp_nk > 0;
-    const int2 *gtab = (const int2 *)((const char *)wr + pl.tab_offset);
     if ((int64_t)p.G * p.B > 0x7fffffff || p.nt_h > 65535 || p.nt_d > 65535)
         return hipErrorInvalidConfiguration;
     hipError_t e;
     switch (S2) {
-        case 1: e = launch_grouped_s<1>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
-        case 2: e = launch_grouped_s<2>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
-        case 3: e = launch_grouped_s<3>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
-        case 4: e = launch_grouped_s<4>(p, x, wr, gtab, bias, y, st_align, x_vec, stream); break;
+        case 1: e = launch_grouped_s<1>(pl, x, w, bias, y, st_align, x_vec, stream); break;
+        case 2: e = launch_grouped_s<2>(pl, x, w, bias, y, st_align, x_vec, stream); break;
+        case 3: e = launch_grouped_s<3>(pl, x, w, bias, y, st_align, x_vec, stream); break;
+        case 4: e = launch_grouped_s<4>(pl, x, w, bias, y, st_align, x_vec, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -25,7 +25,8 @@ hipError_t launch_phase_gemm_nchw(const Plan &pl, const void *x, const void *wr,
 // caller stores them, no workspace
 hipError_t launch_allphase(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
                            hipStream_t stream);
-hipError_t launch_grouped(const Plan &pl, const void *x, const void *wr, const void *bias, void *y,
+// grouped kernel: W as stored (it gathers its group's slab itself), no workspace
+hipError_t launch_grouped(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
                           hipStream_t stream);
 
 // Backward data (dx from dy). The channel-chunked copy and the fill use the

@@ -623,6 +623,53 @@ bool choose_grouped_tile(DevParams *dp) {
     return true;
 }
 
+// The grouped kernel's tables (GrpTables): a record per phase, the (tap,
+// slice) slots of each phase in its taps' order, and the plan-order tap of
+// every stored tap of W (flipped where W's taps are stored reversed).
+bool grouped_tables(Plan *pl) {
+    const DevParams &p = pl->dp;
+    GrpTables &gt = pl->gt;
+    const int noct = p.Cig >> 3;
+    if (p.nphase > kMaxPhaseTab || p.ktot > kGrpMaxTaps || 2 * p.nphase + p.ktot * noct > kGrpTabMax)
+        return false;
+    const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
+    gt.tab_n = 2 * p.nphase + p.ktot * noct;
+    int32_t *slots = gt.tab + 4 * p.nphase;
+    for (int P = 0; P < p.nphase; ++P) {
+        const PhaseRec &rec = p.ph[P];
+        int r[3], n[3], qn[3], off0[3];
+        for (int a = 0; a < 3; ++a) {
+            r[a] = rec.rn[a] & 0xff;
+            n[a] = rec.rn[a] >> 8;
+            qn[a] = rec.qo[a] & 0xffff;
+            off0[a] = rec.qo[a] >> 16;
+        }
+        const int nslots = rec.ntaps * noct;
+        gt.tab[4 * P + 0] = qn[0];
+        gt.tab[4 * P + 1] = qn[1];
+        gt.tab[4 * P + 2] = qn[2];
+        gt.tab[4 * P + 3] = rec.tapbase * noct | nslots << 16;
+        for (int sl = 0; sl < nslots; ++sl) {
+            const int tap = sl / noct, oct = sl % noct;
+            const int j2 = tap % n[2], j1 = (tap / n[2]) % n[1], j0 = tap / (n[2] * n[1]);
+            const int hrow = (off0[0] - a0.umin + j0 * a0.ostep) * p.hh + (off0[1] - a1.umin + j1 * a1.ostep);
+            const int col = off0[2] - a2.umin + j2 * a2.ostep + p.grp_hshift;
+            int32_t *e = slots + 2 * (rec.tapbase * noct + sl);
+            e[0] = ((hrow * noct + oct) * p.grp_hwp + col) * 16;
+            e[1] = (rec.tapbase + tap) * tiles::kGrpCog * p.Cig + oct * 8;
+        }
+        for (int t = 0; t < rec.ntaps; ++t) {
+            const int j2 = t % n[2], j1 = (t / n[2]) % n[1], j0 = t / (n[2] * n[1]);
+            const int k0 = a0.kk0[r[0]] - j0 * a0.kstep, k1 = a1.kk0[r[1]] - j1 * a1.kstep,
+                      k2 = a2.kk0[r[2]] - j2 * a2.kstep;
+            const int st = p.w_flip ? ((a0.K - 1 - k0) * a1.K + (a1.K - 1 - k1)) * a2.K + (a2.K - 1 - k2)
+                                    : (k0 * a1.K + k1) * a2.K + k2;
+            gt.tg_of[st] = (uint8_t)(rec.tapbase + t);
+        }
+    }
+    return true;
+}
+
 bool grouped_eligible(const DevParams &dp, int dtype) {
     if ((dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16) || dp.ktot > 4096) return false;
     if (!slices_fit(dp, 2)) return false;
@@ -638,6 +685,10 @@ bool grouped_eligible(const DevParams &dp, int dtype) {
     }
     if (max_taps * (dp.Cig / 8) > 4 * tiles::kGrpMaxKSteps) return false;
     if ((int64_t)dp.ktot * tiles::kGrpCog * dp.Cig * 2 > tiles::kGrpWBytes) return false;
+    if (dp.ktot > kGrpMaxTaps || 2 * dp.nphase + dp.ktot * (dp.Cig / 8) > kGrpTabMax) return false;
+    // the kernel gathers its group's weights from all of W through one
+    // range-checked resource (masked elements take an offset past its end)
+    if (!buffer_fits((int64_t)dp.Ci * dp.Cog * dp.ktot * 2)) return false;
     DevParams tmp = dp;
     return choose_grouped_tile(&tmp);
 }
@@ -1013,29 +1064,25 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
         dp.cig_pad = (int32_t)Cig;
         dp.n_co_tiles = 1;
         blocks = (int64_t)dp.nt_d * dp.nt_h * G * B;
+        if (!grouped_tables(pl)) return CONVT_ERR_UNSUPPORTED;
     }
     if (blocks > i31) return CONVT_ERR_UNSUPPORTED;
     dp.n_blocks = (int32_t)blocks;
     // the grouped kernel runs a 3-D grid in plain order
     dp.xcd_remap = (blocks % 8 == 0 && route != CONVT_ROUTE_GROUPED) ? 1 : 0;
     const bool gemm = route == CONVT_ROUTE_PHASE_GEMM || route == CONVT_ROUTE_PHASE_GEMM_PACKED;
-    if (gemm || route == CONVT_ROUTE_GROUPED) {
+    // (the grouped kernel reads W as stored and takes its tables with its
+    // arguments: no workspace)
+    if (gemm) {
         int64_t wr;
-        const int64_t taps = gemm ? dp.ktot_pad : ktot;
+        const int64_t taps = dp.ktot_pad;
         if (!mul_ok((int64_t)G * taps, (int64_t)dp.cog_pad * dp.cig_pad, lim, &wr))
             return CONVT_ERR_INVALID_ARGUMENT;
         pl->wr_elems = wr;
         info.workspace_bytes = wr * pl->elem_bytes;
-        if (gemm) {
-            // the per-tap halo shift table (int32 per padded tap of a group)
-            pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
-            info.workspace_bytes = pl->tab_offset + (int64_t)dp.ktot_pad * 4;
-        } else {
-            // the grouped kernel's slot table: a 16-byte record per phase,
-            // then (halo byte offset, weight offset) per (tap, 8-channel slice)
-            pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
-            info.workspace_bytes = pl->tab_offset + 16 * (int64_t)dp.nphase + (int64_t)ktot * (Cig / 8) * 8;
-        }
+        // the per-tap halo shift table (int32 per padded tap of a group)
+        pl->tab_offset = (info.workspace_bytes + 255) / 256 * 256;
+        info.workspace_bytes = pl->tab_offset + (int64_t)dp.ktot_pad * 4;
         if (route == CONVT_ROUTE_PHASE_GEMM_PACKED) {
             // the channel-chunked copy of x: [B][G][chunk][position][32 bytes]
             int64_t xp;

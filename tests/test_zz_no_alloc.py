@@ -2,8 +2,8 @@
 workspace (its scratch is a fixed device array of the library): through the
 C ABI it must give, byte for byte, what convt_forward gives with a caller's
 workspace, on two calls in a row whose second problem is smaller, on the
-routes that use a workspace (the in-place phase GEMM, its packed variant,
-the grouped kernel)."""
+routes that use a workspace (the in-place phase GEMM, its packed variant)
+and on the grouped kernel, which needs none."""
 import numpy as np
 import pytest
 
@@ -30,7 +30,10 @@ def setup(case, seed):
                                   seed)
     pl = C.get_plan(xs, ws, s, p, d, op, g, True, "bf16", route)
     assert pl.route == route, (name, pl.route)
-    assert 0 < pl.workspace_bytes <= C.lib().convt_scratch_max_bytes()
+    # (the grouped route reads W as stored: no workspace, the scratch entry
+    # point then passes none)
+    assert 0 <= pl.workspace_bytes <= C.lib().convt_scratch_max_bytes()
+    assert (pl.workspace_bytes == 0) == (route == "grouped")
     x, w, b = (to_device(a, "bf16") for a in (tens.x_dev, tens.w_dev, tens.bias_dev))
     return pl, x, w, b
 

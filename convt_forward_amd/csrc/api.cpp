@@ -165,6 +165,11 @@ convt_status convt_backward_data(convt_plan_t plan, const void *dy, const void *
             return device_status(convt::launch_naive_bwd(pl, dy, w, dx, s));
         case CONVT_ROUTE_DIRECT:
             return device_status(convt::launch_direct_bwd(pl, dy, w, dx, s));
+        case CONVT_ROUTE_PHASE_GEMM_ALLPHASE:
+            // dy read in 4-byte pairs, W in 16-byte pieces, dx stored in 16-byte pieces
+            if ((uintptr_t)dy % 4 != 0 || (uintptr_t)w % 16 != 0 || (uintptr_t)dx % 16 != 0)
+                return CONVT_ERR_INVALID_ARGUMENT;
+            return device_status(convt::launch_allphase_bwd(pl, dy, w, dx, s));
         case CONVT_ROUTE_PHASE_GEMM: {
             if (!workspace || ((uintptr_t)workspace % 16) != 0) return CONVT_ERR_INVALID_ARGUMENT;
             if (pl.bwd_xp_bytes > 0) {
@@ -246,6 +251,6 @@ convt_status convt_plan_query(convt_plan_t plan, convt_plan_info *info) {
     return CONVT_OK;
 }
 
-int32_t convt_version(void) { return 310; }
+int32_t convt_version(void) { return 320; }
 
 }  // extern "C"

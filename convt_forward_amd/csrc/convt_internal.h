@@ -132,6 +132,34 @@ struct AllPhaseArgs {
     int32_t kd0[kMaxS], offd[kMaxS], qnd[kMaxS];
 };
 
+// Backward data on the all-phase kernel (two-byte types; stride 2, dilation
+// 1 and an even tap count on the height and width axes, 16 taps over the
+// two): a block computes 128 dx channels x a box of one depth position and
+// T1 x T2 = 256 positions, its K loop running over (8-channel chunk of dy,
+// depth tap) stages of all 16 height x width taps.
+constexpr int kBwdPlaneRows = 383;  // halo rows per phase plane, at most (one more row absorbs idle units)
+struct BwdAPArgs {
+    int32_t Ci, Co, Cig, Cog, G;  // the forward problem's channels: dx has Ci (groups of Cig), dy Co
+    int32_t I[3], O[3], K[3];     // dx extents, dy extents, taps
+    int32_t ktot;
+    int32_t T1, T2, lgT2;         // the box (powers of two, T1 * T2 = 256)
+    int32_t E1, E2;               // halo rows of one phase plane: E1 x E2 <= kBwdPlaneRows
+    int32_t n_ci_tiles;           // 128-channel tiles of Cig
+    int32_t nt[3];                // boxes per axis (nt[0] = I[0]: one depth position per box)
+    int32_t n_blocks, xcd_remap;
+    FastDiv div_ci, div_t2, div_t1, div_t0, div_g;  // block-index decode
+    int32_t nstages;              // ceil(Cog / 8) * K[0], rounded up to even
+    FastDiv div_k0;               // stage -> (chunk, depth tap)
+    int32_t x_plane, y_plane;     // dx plane (I0 I1 I2), dy plane (O0 O1 O2)
+    int32_t flip;
+    int32_t S0, P0, D0;           // depth: dx position i reads dy depth S0*i - P0 + kd*D0
+    // height / width: tap k = 2m + c reads the dy phase plane of residue
+    // r[c] (positions 2j + r[c]) at j = i + tmin + m + u[c]; the halo of a
+    // box starting at i0 covers j in [i0 + tmin, i0 + tmin + E)
+    int32_t tmin1, tmin2;
+    int32_t r1[2], u1[2], r2[2], u2[2];
+};
+
 // Grouped route: the kernel's slot table and tap map, built by the planner
 // and passed with the kernel's arguments (the kernel copies the table to LDS
 // and gathers its group's weights from W as stored).
@@ -172,6 +200,7 @@ struct Plan {
     int64_t bwd_tab_offset;  // byte offset of the per-tap halo shift table
     int64_t bwd_xp_offset;   // bfloat16: byte offset of the channel-chunked copy of dy
     int64_t bwd_xp_bytes;    // its size (0 when not used)
+    BwdAPArgs bap;           // route_bwd PHASE_GEMM_ALLPHASE: the kernel's arguments
 };
 
 // Tile constants of the kernels, shared with the planner so that it sizes

@@ -41,6 +41,10 @@ hipError_t launch_direct_bwd(const Plan &pl, const void *dy, const void *w, void
                              hipStream_t stream);
 hipError_t launch_phase_gemm_bwd(const Plan &pl, const void *dy, const void *wr, void *dx,
                                  hipStream_t stream);
+// backward all-phase GEMM (route_bwd PHASE_GEMM_ALLPHASE): dy and W as the
+// caller stores them, no workspace
+hipError_t launch_allphase_bwd(const Plan &pl, const void *dy, const void *w, void *dx,
+                               hipStream_t stream);
 
 // Two-byte phase GEMM: the weight reorder and the channel-chunked input copy
 // of the forward (resp. backward) problem in one launch; xp at the plan's

@@ -706,6 +706,110 @@ bool direct_bwd_eligible(const DevParams &fp, int elem_bytes) {
            (int64_t)fp.Cog * fp.y_plane * elem_bytes < ((int64_t)1 << 31) && fp.x_plane > 0;
 }
 
+// Plan the backward all-phase kernel (k_bwd_allphase.hip) for the input
+// gradient of a two-byte problem (fp: the forward problem), or return false
+// if it does not apply: W in the C_in x C_out x taps layout; stride 2 and
+// dilation 1 on the height and width axes with even tap counts there and 16
+// taps over the two; an even dy row length (a 4-byte pair of dy positions
+// lies in one row), dx rows of whole 16-byte pieces; 32-bit buffer offsets
+// (dy up to 32 channels past the group, for the stages the pipeline loads
+// ahead); at least min_cig dx channels per group. The box is one depth
+// position x T1 x T2 = 256 positions whose four phase-plane halos fit the
+// kernel's planes.
+bool choose_bwd_allphase(Plan *pl, int ndim, int dtype, int64_t min_cig) {
+    const DevParams &fp = pl->dp;
+    if (dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16) return false;
+    if (ndim < 2 || fp.w_layout != CONVT_FILTER_CI_CO_K || fp.Cig < min_cig || fp.Cig < 1 || fp.Cog < 1)
+        return false;
+    const DevAxis &a0 = fp.ax[0], &a1 = fp.ax[1], &a2 = fp.ax[2];
+    if (a1.S != 2 || a2.S != 2 || a1.D != 1 || a2.D != 1 || a1.K % 2 || a2.K % 2 || a1.K * a2.K != 16)
+        return false;
+    if (a2.O % 2 != 0 || a2.I % 8 != 0 || a1.I < 1 || a0.I < 1) return false;
+    if (!buffer_fits(((int64_t)fp.Cog + 32) * fp.y_plane * 2) ||
+        !buffer_fits((int64_t)fp.Cig * fp.Cog * fp.ktot * 2) || !buffer_fits((int64_t)fp.Cig * fp.x_plane * 2))
+        return false;
+    // per axis: tap k = 2m + c reads plane residue (c - p) mod 2 at index
+    // i + m + floor((c - p) / 2); tmin = floor(-p / 2) (the c = 0 value)
+    auto floor_half = [](int64_t v) { return v >= 0 ? v / 2 : -((1 - v) / 2); };
+    BwdAPArgs &ba = pl->bap;
+    ba = BwdAPArgs{};
+    const DevAxis *hw[2] = {&a1, &a2};
+    int32_t tmin[2], r[2][2], u[2][2];
+    for (int x = 0; x < 2; ++x) {
+        const int64_t p = hw[x]->P;
+        tmin[x] = (int32_t)floor_half(-p);
+        for (int c = 0; c < 2; ++c) {
+            r[x][c] = (int32_t)pmod(c - p, 2);
+            u[x][c] = (int32_t)(floor_half(c - p) - tmin[x]);
+        }
+    }
+    // the box: the fewest boxes per plane, then the smallest halo
+    int T1 = 0, T2 = 0;
+    int64_t E1 = 0, E2 = 0, best_boxes = 0;
+    for (int t2 = 16; t2 <= 64; t2 *= 2) {
+        const int t1 = 256 / t2;
+        const int64_t e1 = t1 + a1.K / 2 - 1 + u[0][1], e2 = t2 + a2.K / 2 - 1 + u[1][1];
+        if (e1 * e2 > kBwdPlaneRows) continue;
+        const int64_t boxes = ceil_div(a1.I, t1) * ceil_div(a2.I, t2);
+        if (T2 == 0 || boxes < best_boxes || (boxes == best_boxes && e1 * e2 < E1 * E2)) {
+            T1 = t1;
+            T2 = t2;
+            E1 = e1;
+            E2 = e2;
+            best_boxes = boxes;
+        }
+    }
+    if (T2 == 0) return false;
+    ba.Ci = fp.Ci;
+    ba.Co = fp.Co;
+    ba.Cig = fp.Cig;
+    ba.Cog = fp.Cog;
+    ba.G = fp.G;
+    for (int a = 0; a < 3; ++a) {
+        ba.I[a] = fp.ax[a].I;
+        ba.O[a] = fp.ax[a].O;
+        ba.K[a] = fp.ax[a].K;
+    }
+    ba.ktot = fp.ktot;
+    ba.T1 = T1;
+    ba.T2 = T2;
+    ba.lgT2 = __builtin_ctz((unsigned)T2);
+    ba.E1 = (int32_t)E1;
+    ba.E2 = (int32_t)E2;
+    ba.n_ci_tiles = (int32_t)ceil_div(fp.Cig, 128);
+    ba.nt[0] = a0.I;
+    ba.nt[1] = (int32_t)ceil_div(a1.I, T1);
+    ba.nt[2] = (int32_t)ceil_div(a2.I, T2);
+    const int64_t blocks = (int64_t)ba.nt[0] * ba.nt[1] * ba.nt[2] * ba.n_ci_tiles * fp.G * fp.B;
+    if (blocks < 1 || blocks > ((int64_t)1 << 31) - 1) return false;
+    ba.n_blocks = (int32_t)blocks;
+    ba.xcd_remap = blocks % 8 == 0 ? 1 : 0;
+    ba.div_ci = fast_div_of((uint32_t)ba.n_ci_tiles);
+    ba.div_t2 = fast_div_of((uint32_t)ba.nt[2]);
+    ba.div_t1 = fast_div_of((uint32_t)ba.nt[1]);
+    ba.div_t0 = fast_div_of((uint32_t)ba.nt[0]);
+    ba.div_g = fast_div_of((uint32_t)fp.G);
+    const int64_t stages = ceil_div(fp.Cog, 8) * a0.K;
+    if (stages > ((int64_t)1 << 30)) return false;
+    ba.nstages = (int32_t)((stages + 1) / 2 * 2);
+    ba.div_k0 = fast_div_of((uint32_t)a0.K);
+    ba.x_plane = fp.x_plane;
+    ba.y_plane = fp.y_plane;
+    ba.flip = fp.w_flip;
+    ba.S0 = a0.S;
+    ba.P0 = a0.P;
+    ba.D0 = a0.D;
+    ba.tmin1 = tmin[0];
+    ba.tmin2 = tmin[1];
+    for (int c = 0; c < 2; ++c) {
+        ba.r1[c] = r[0][c];
+        ba.u1[c] = u[0][c];
+        ba.r2[c] = r[1][c];
+        ba.u2[c] = u[1][c];
+    }
+    return true;
+}
+
 }  // namespace
 
 // ---- backward data ---------------------------------------------------------
@@ -759,6 +863,8 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
             // few channels: the backward GEMM's tiles (64 dx channels, chunks
             // of 16 dy channels) would be mostly padding
             route = CONVT_ROUTE_DIRECT;
+        else if (choose_bwd_allphase(pl, nd, dt, 65))
+            route = CONVT_ROUTE_PHASE_GEMM_ALLPHASE;
         else if (gemm_eligible(b, dt, nd, true))
             route = CONVT_ROUTE_PHASE_GEMM;
         else if (direct_bwd_eligible(fp, pl->elem_bytes))
@@ -773,6 +879,9 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
             case CONVT_ROUTE_PHASE_GEMM:
                 ok = !empty_out && !no_terms && gemm_eligible(b, dt, nd, true);
                 break;
+            case CONVT_ROUTE_PHASE_GEMM_ALLPHASE:
+                ok = !empty_out && !no_terms && choose_bwd_allphase(pl, nd, dt, 1);
+                break;
             case CONVT_ROUTE_DIRECT:
                 ok = !empty_out && !no_terms && direct_bwd_eligible(fp, pl->elem_bytes);
                 break;
@@ -784,7 +893,7 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
     pl->route_bwd = route;
     pl->info.route_bwd = route;
     pl->info.bwd_workspace_bytes = 0;
-    if (route != CONVT_ROUTE_PHASE_GEMM) return CONVT_OK;
+    if (route != CONVT_ROUTE_PHASE_GEMM) return CONVT_OK;  // the all-phase kernel needs no workspace
 
     const int64_t i31 = ((int64_t)1 << 31) - 1, lim = (int64_t)1 << 62;
     pick_gemm_cfg(&b, dt, nd, true);
@@ -846,7 +955,7 @@ convt_status make_plan(const convt_problem *p, Plan *pl) {
         return CONVT_ERR_INVALID_ARGUMENT;
     if (p->activation < CONVT_ACT_NONE || p->activation > CONVT_ACT_GELU || p->reserved1 != 0)
         return CONVT_ERR_INVALID_ARGUMENT;
-    if (p->route_bwd < CONVT_ROUTE_AUTO || p->route_bwd > CONVT_ROUTE_PHASE_GEMM_PACKED)
+    if (p->route_bwd < CONVT_ROUTE_AUTO || p->route_bwd > CONVT_ROUTE_PHASE_GEMM_ALLPHASE)
         return CONVT_ERR_INVALID_ARGUMENT;
     const int64_t B = p->x_shape[0], Ci = p->x_shape[1];
     const int64_t G = p->groups;

@@ -248,7 +248,7 @@ def test_allphase_route_rules():
     """The all-phase route takes two-byte problems with stride 2 and
     dilation 1 on the two innermost axes, 4 or 8 taps per phase, an even x
     row and an output row length that is a multiple of 8; it is refused
-    otherwise, and never serves the backward pass."""
+    otherwise."""
     ok = dict(x_shape=(1, 16, 6, 16), w_shape=(16, 96, 4, 4), stride=2, padding=1, dtype="bf16")
     assert plan(**ok, route="phase_gemm_allphase").route == "phase_gemm_allphase"
     assert plan(**ok).route == "phase_gemm_allphase"
@@ -261,7 +261,6 @@ def test_allphase_route_rules():
         assert status_of(**dict(ok, **bad), route="phase_gemm_allphase") == 2, bad
     # 64 or fewer output channels per group: the automatic choice is another kernel
     assert plan(**dict(ok, w_shape=(16, 64, 4, 4))).route != "phase_gemm_allphase"
-    assert status_of(**ok, route_bwd="phase_gemm_allphase") == 1
     # host-side refusals: x must be 4-byte and W 16-byte aligned
     L = C.lib()
     h = plan(**ok, has_bias=False).handle
@@ -356,6 +355,39 @@ def test_backward_data_refuses_bad_arguments_before_launch():
     assert L.convt_backward_data(h, fake, None, fake, fake, None) == 1        # w required
     assert L.convt_backward_data(h, fake, fake, fake, None, None) == 1        # workspace required
     assert L.convt_backward_data(h, fake, fake, fake, fake + 8, None) == 1    # misaligned
+
+
+def test_allphase_backward_route_rules():
+    """The backward all-phase kernel takes two-byte problems with stride 2
+    and dilation 1 on the two innermost axes, 16 taps over them (4x4, 2x8,
+    8x2), an even dy row and a dx row length that is a multiple of 8, W in
+    the C_in x C_out x taps layout; no workspace. The automatic choice takes
+    it for more than 64 dx channels per group."""
+    ok = dict(x_shape=(1, 96, 6, 16), w_shape=(96, 24, 4, 4), stride=2, padding=1, dtype="bf16")
+    pl = plan(**ok)
+    assert pl.route_bwd == "phase_gemm_allphase" and pl.bwd_workspace_bytes == 0
+    for good in [dict(), dict(dtype="f16"), dict(w_shape=(96, 24, 2, 8)), dict(w_shape=(96, 24, 8, 2)),
+                 dict(padding=(0, 2)), dict(padding=((1, 3), (0, 2))), dict(groups=2, w_shape=(96, 8, 4, 4)),
+                 dict(x_shape=(1, 96, 3, 6, 16), w_shape=(96, 24, 3, 4, 4), stride=(1, 2, 2), padding=1),
+                 dict(x_shape=(1, 96, 3, 6, 16), w_shape=(96, 24, 4, 4, 4), stride=2, padding=1)]:
+        assert plan(**dict(ok, **good), route_bwd="phase_gemm_allphase").route_bwd == "phase_gemm_allphase"
+    for bad in [dict(dtype="f32"), dict(stride=(2, 1)), dict(dilation=2), dict(x_shape=(1, 96, 6, 12)),
+                dict(output_padding=(0, 1)),                              # dy rows of 33
+                dict(w_shape=(96, 24, 3, 3)), dict(w_shape=(96, 24, 4, 8)), dict(w_shape=(96, 24, 2, 2)),
+                dict(x_shape=(1, 96, 16), w_shape=(96, 24, 4), stride=2, padding=1),  # 1-D
+                dict(filter_layout="k_ci_co")]:
+        assert status_of(**dict(ok, **bad), route_bwd="phase_gemm_allphase") == 2, bad
+    # 64 or fewer dx channels per group: the automatic choice is another kernel
+    assert plan(**dict(ok, x_shape=(1, 64, 6, 16), w_shape=(64, 24, 4, 4))).route_bwd == "phase_gemm"
+    # the forward's packed route has no backward counterpart
+    assert status_of(**ok, route_bwd="phase_gemm_packed") == 2
+    # host-side refusals: dy must be 4-byte, W and dx 16-byte aligned
+    L = C.lib()
+    h = pl.handle
+    fake = 4096  # never dereferenced
+    assert L.convt_backward_data(h, fake + 2, fake, fake, None, None) == 1
+    assert L.convt_backward_data(h, fake, fake + 8, fake, None, None) == 1
+    assert L.convt_backward_data(h, fake, fake, fake + 8, None, None) == 1
 
 
 def test_backward_routes():

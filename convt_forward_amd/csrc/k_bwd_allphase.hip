@@ -198,18 +198,35 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
     struct XRegs {
         uint32_t v[XU][8];
     };
+    // a stage's wave-uniform load offsets, computed once ahead of its K steps
+    // and held in scalar registers (the empty asm keeps the selects from
+    // being turned into branches inside the K steps, which would split their
+    // scheduling regions)
+    struct StageOffs {
+        uint32_t x, w[8];
+    };
+    auto stage_offs = [&](int cl) __attribute__((always_inline)) {
+        StageOffs o;
+        o.x = __builtin_amdgcn_readfirstlane(x_stage(cl));
+        asm volatile("" : "+s"(o.x));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o.w[e] = __builtin_amdgcn_readfirstlane(w_stage(cl, e));
+            asm volatile("" : "+s"(o.w[e]));
+        }
+        return o;
+    };
     u32x4 WR[8];
     XRegs X0, X1;
-    auto load_w = [&](int cl) __attribute__((always_inline)) {
+    auto load_w = [&](const StageOffs &so) __attribute__((always_inline)) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            WR[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, woff, w_stage(cl, e), 0));
+            WR[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, woff, so.w[e], 0));
     };
-    auto load_x = [&](XRegs &xr, int k, int cl) __attribute__((always_inline)) {
-        const uint32_t cs = x_stage(cl);
+    auto load_x = [&](XRegs &xr, int k, const StageOffs &so) __attribute__((always_inline)) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            xr.v[k][e] = __builtin_amdgcn_raw_buffer_load_b32(xrs, xoff[k], cs + (uint32_t)e * ypl2, 0);
+            xr.v[k][e] = __builtin_amdgcn_raw_buffer_load_b32(xrs, xoff[k], so.x + (uint32_t)e * ypl2, 0);
     };
     // rows 4h .. 4h+3 of the unit's 8 x 8 block (dy channel e holds taps
     // 2j, 2j + 1 in word j) as slot rows (tap t holds channels 2j, 2j + 1 in
@@ -287,23 +304,24 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
     // buffer nxt and loads stage cl = s+2 (halo into xl, weights into WR)
     auto stage_body = [&](unsigned char *cur, unsigned char *nxt, const XRegs &xs, XRegs &xl, int cl)
         __attribute__((always_inline)) {
+        const StageOffs so = stage_offs(cl);
         __builtin_amdgcn_sched_barrier(0);
         read_frags(fa[1], fb[1], cur, 1);
         mfma(fa[0], fb[0]);
         store_x(xs, 0, nxt);
-        load_x(xl, 0, cl);
+        load_x(xl, 0, so);
         interleave(V1{});
         __builtin_amdgcn_sched_barrier(0);
         read_frags(fa[0], fb[0], cur, 2);
         mfma(fa[1], fb[1]);
         store_x(xs, 1, nxt);
-        load_x(xl, 1, cl);
+        load_x(xl, 1, so);
         interleave(V1{});
         __builtin_amdgcn_sched_barrier(0);
         read_frags(fa[1], fb[1], cur, 3);
         mfma(fa[0], fb[0]);
         store_x(xs, 2, nxt);
-        load_x(xl, 2, cl);
+        load_x(xl, 2, so);
         interleave(V1{});
         __builtin_amdgcn_sched_barrier(0);
         read_frags(fa[0], fb[0], cur, 4);
@@ -314,7 +332,7 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
         read_frags(fa[1], fb[1], cur, 5);
         mfma(fa[0], fb[0]);
         store_w(nxt, 1);
-        load_w(cl);
+        load_w(so);
         interleave(V2{});
         __builtin_amdgcn_sched_barrier(0);
         read_frags(fa[0], fb[0], cur, 6);
@@ -337,16 +355,17 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
     };
 
     unsigned char *buf0 = lds, *buf1 = lds + STAGE;
-    load_w(0);
+    const StageOffs so0 = stage_offs(0), so1 = stage_offs(1);
+    load_w(so0);
 #pragma unroll
-    for (int k = 0; k < XU; ++k) load_x(X0, k, 0);
+    for (int k = 0; k < XU; ++k) load_x(X0, k, so0);
 #pragma unroll
-    for (int k = 0; k < XU; ++k) load_x(X1, k, 1);
+    for (int k = 0; k < XU; ++k) load_x(X1, k, so1);
     store_w(buf0, 0);
     store_w(buf0, 1);
 #pragma unroll
     for (int k = 0; k < XU; ++k) store_x(X0, k, buf0);
-    load_w(1);
+    load_w(so1);
     barrier();
     read_frags(fa[0], fb[0], buf0, 0);
     for (int s = 0; s < a.nstages; s += 2) {

@@ -79,7 +79,7 @@ struct DevParams {
     int32_t grp_ksteps;        // grouped route: MFMA K steps per phase (1, 2 or 4)
     int32_t gemm_cfg;          // phase GEMM: index into tiles::kGemmCfg
     int32_t gemm_gs;           // phase GEMM: taps per pipeline stage (1..kGemmTapGroup)
-    int32_t wr_chunked;        // reordered weights: 1 = [g][tap][chunk][co][32 B], 0 = [g][tap][co][ci]
+    int32_t wr_chunked;        // 1: the route reorders W into [g][tap][chunk][co][32 B] (0: W read as stored)
     int32_t ktot_pad;          // taps per group in the reordered weights (phase GEMM: each
                                // phase padded with zero taps to a multiple of gemm_gs)
     int32_t ph_tab_ok;         // 1: ph[] holds every phase (nphase <= kMaxPhaseTab)

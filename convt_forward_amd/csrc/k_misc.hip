@@ -1,135 +1,10 @@
-// Weight reorder, bias fill, the one-thread-per-output gather kernel and the
-// small-channel direct kernel.
+// Weight reorder (phase GEMM layouts), the channel-chunked input copy, bias
+// fill, the one-thread-per-output gather kernels and the small-channel direct
+// kernels.
 #include "kcommon.h"
 #include "launch.h"
 
 namespace convt {
-
-// ---------------------------------------------------------------------------
-// Weight reorder + tap flip.
-//
-// W[g*Cig + ci][co][k0][k1][k2] (forward orientation, the layout the SKaiNET
-// convTranspose2d page states) -> Wr[g][tap][co][ci] (the grouped route's
-// layout; the phase GEMM's follows below), where `tap` enumerates
-// the taps phase by phase (phases in lexicographic residue order) and, within
-// a phase, in ascending input offset (descending kk per axis: the
-// tap-reversed order). ci is contiguous so that MFMA operands are 16-byte
-// reads; co and ci are zero-padded to cog_pad and cig_pad so that the GEMM
-// loads need no masks.
-//
-// A block owns one 16-byte vector of input channels (VEC = 8 bfloat16 or 4
-// float32 channels) and a block of `ocb` output channels, over all taps. For
-// each of its channels the [ocb][ktot] slab is contiguous in W, so the block
-// reads it with consecutive lanes on consecutive elements into LDS; each lane
-// then assembles whole destination vectors (VEC channels of one (tap, co))
-// and writes them with one 16-byte store.
-//
-// Block P (every gridDim-th phase when the grid is smaller) also writes
-// phase P's part of the grouped kernel's slot table: first one int4
-// record per phase P (its q counts per axis, then the index of its first
-// slot | its slot count << 16), then per phase and slot (tap, 8-channel
-// slice), at index tapbase(P) * slices + slot, the byte offset of the tap's
-// window origin in that kernel's LDS halo, [halo row][slice][column] of
-// 16-byte cells with hh rows per depth plane, grp_hwp cells per row and halo
-// position 0 at column grp_hshift, and the element offset of (tap, co 0,
-// slice) in the group's Wr slab.
-// ---------------------------------------------------------------------------
-__device__ void grouped_slot_table(const DevParams &p, int2 *__restrict__ gtab) {
-    const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
-    const int noct = p.Cig >> 3, HH = p.hh, HWP = p.grp_hwp;
-    int2 *tab = gtab + 2 * p.nphase;
-    for (int P = blockIdx.x; P < p.nphase; P += gridDim.x) {
-        const PhaseDesc ph = phase_desc(p, P);
-        const int nslots = ph.ntaps * noct;
-        if (threadIdx.x == 0)
-            ((int4 *)gtab)[P] = make_int4(ph.qn[0], ph.qn[1], ph.qn[2], ph.tapbase * noct | nslots << 16);
-        const int n1 = ph.n[1], n2 = ph.n[2];
-        for (int sl = threadIdx.x; sl < nslots; sl += blockDim.x) {
-            const int tap = sl / noct, oct = sl - tap * noct;
-            const int j2 = tap % n2, j1 = (tap / n2) % n1, j0 = tap / (n2 * n1);
-            const int hrow = (ph.off0[0] - a0.umin + j0 * a0.ostep) * HH +
-                             (ph.off0[1] - a1.umin + j1 * a1.ostep);
-            const int col = ph.off0[2] - a2.umin + j2 * a2.ostep + p.grp_hshift;
-            tab[ph.tapbase * noct + sl] = make_int2(((hrow * noct + oct) * HWP + col) * 16,
-                                                    (ph.tapbase + tap) * tiles::kGrpCog * p.Cig + oct * 8);
-        }
-    }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void reorder_kernel(DevParams p, const T *__restrict__ w,
-                                                       T *__restrict__ wr, int ocb,
-                                                       int2 *__restrict__ gtab) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    if (gtab != nullptr) grouped_slot_table(p, gtab);
-    T *brick = (T *)lds_raw;
-    constexpr int VEC = 16 / sizeof(T);
-    const int ktot = p.ktot;
-    const int nci = p.cig_pad / VEC;
-    const int nco = (p.cog_pad + ocb - 1) / ocb;
-    int bid = blockIdx.x;
-    const int co_b = bid % nco;
-    bid /= nco;
-    const int ci_b = bid % nci;
-    const int g = bid / nci;
-    const int n = ocb * ktot;
-    const int co0 = co_b * ocb;
-    // loads are unconditional (a masked element reads the slab's first
-    // element and is then zeroed) and issued in batches of 8 before their
-    // LDS stores, so that a batch is in flight together
-    const T *wg = w + (int64_t)g * p.Cig * p.Cog * ktot;
-    const int lim = (p.Cog - co0) * ktot;  // elements of a channel row inside W
-    const int total = VEC * n;
-    const bool plain = w_plain(p);
-    for (int e0 = threadIdx.x; e0 < total; e0 += 256 * 8) {
-        T v[8];
-        bool ok[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = e0 + 256 * u;
-            const int cil = e / n, r = e - cil * n;
-            const int ci = ci_b * VEC + cil;
-            ok[u] = e < total && ci < p.Cig && r < lim;
-            if (plain)
-                v[u] = wg[ok[u] ? ((int64_t)ci * p.Cog + co0) * ktot + r : 0];
-            else
-                v[u] = w[ok[u] ? w_offset(p, g * p.Cig + ci, co0 + r / ktot, r % ktot) : 0];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = e0 + 256 * u;
-            if (e < total) brick[e] = ok[u] ? v[u] : from_f32<T>(0.0f);
-        }
-    }
-    __syncthreads();
-    const int K1 = p.ax[1].K, K2 = p.ax[2].K;
-    for (int v = threadIdx.x; v < n; v += 256) {
-        const int col = v / ktot, kk = v - col * ktot;
-        const int co = co0 + col;
-        if (co >= p.cog_pad) continue;
-        const int k2 = kk % K2, k1 = (kk / K2) % K1, k0 = kk / (K1 * K2);
-        const int tg = tap_global(p, k0, k1, k2);
-        u32x4 out;
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                out[e] = (uint32_t)brick[(2 * e) * n + v] | ((uint32_t)brick[(2 * e + 1) * n + v] << 16);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = __float_as_uint((float)brick[e * n + v]);
-        }
-        *(u32x4 *)&wr[(((int64_t)g * ktot + tg) * p.cog_pad + co) * p.cig_pad + ci_b * VEC] = out;
-    }
-}
-
-// Output channels per reorder block: the LDS brick (16 bytes per output
-// channel and tap) stays within 32 KiB.
-static int reorder_ocb(const DevParams &p) {
-    int ocb = 32768 / (16 * p.ktot);
-    if (ocb < 1) ocb = 1;
-    if (ocb > p.cog_pad) ocb = p.cog_pad;
-    return ocb;
-}
 
 // ---------------------------------------------------------------------------
 // Weight reorder for the phase GEMM:
@@ -367,23 +242,8 @@ hipError_t launch_reorder(const Plan &pl, const void *w, void *wr, hipStream_t s
                                stream, p, (const float *)w, (float *)wr, tab, r.a, r.KT, r.vec_runs);
         return hipGetLastError();
     }
-    const int vec = 16 / pl.elem_bytes;
-    if (p.cig_pad % vec) return hipErrorInvalidValue;
-    const int ocb = reorder_ocb(p);
-    const int64_t nco = (p.cog_pad + ocb - 1) / ocb;
-    const int64_t blocks = (int64_t)p.G * (p.cig_pad / vec) * nco;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)16 * ocb * p.ktot;
-    if (lds > 65536) return hipErrorInvalidConfiguration;
-    int2 *gtab = pl.route == CONVT_ROUTE_GROUPED ? (int2 *)((char *)wr + pl.tab_offset) : nullptr;
-    if (pl.elem_bytes == 2)
-        hipLaunchKernelGGL(reorder_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), lds, stream,
-                           p, (const uint16_t *)w, (uint16_t *)wr, ocb, gtab);
-    else
-        hipLaunchKernelGGL(reorder_kernel<float>, dim3((unsigned)blocks), dim3(256), lds, stream, p,
-                           (const float *)w, (float *)wr, ocb, gtab);
-    return hipGetLastError();
+    // every route that reorders W into the workspace uses the chunked layout
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

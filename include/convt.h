@@ -105,7 +105,8 @@ typedef enum convt_route {
                                            innermost axes: one block computes all four of their
                                            stride phases of an output tile, reading x and W as
                                            stored (no workspace, one launch per call); AUTO
-                                           plans it where it applies; forward only */
+                                           plans it where it applies; as route_bwd, the input
+                                           gradient's counterpart (16 taps over those axes) */
 } convt_route;
 
 /* How W is laid out in memory (the AWS Neuron conv3d_transpose page's
@@ -263,9 +264,13 @@ convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void
  * errors as for convt_forward. route_bwd may not be PHASE_GEMM_PACKED
  * (CONVT_ERR_UNSUPPORTED at planning). Routes (info.route_bwd): NONE (dx empty),
  * FILL (no output channels: dx = 0), PHASE_GEMM (stride phases summed inside
- * one implicit-gather GEMM on MFMA), DIRECT (few channels per group: a thread
- * per dx position over its group's input channels, weights in LDS), NAIVE
- * (one thread per dx element).
+ * one implicit-gather GEMM on MFMA), PHASE_GEMM_ALLPHASE (two-byte types,
+ * stride 2 and dilation 1 on the two innermost axes with 16 taps over them,
+ * W in the CI_CO_K layout: one MFMA GEMM reads dy and W as stored and sums
+ * the four stride phases of each dx box from one halo; no workspace; dy must
+ * be 4-byte and W and dx 16-byte aligned, else CONVT_ERR_INVALID_ARGUMENT),
+ * DIRECT (few channels per group: a thread per dx position over its group's
+ * input channels, weights in LDS), NAIVE (one thread per dx element).
  */
 convt_status convt_backward_data(convt_plan_t plan, const void *dy, const void *w, void *dx,
                                  void *workspace, void *stream);

@@ -135,15 +135,18 @@ struct AllPhaseArgs {
 // Backward data on the all-phase kernel (two-byte types; stride 2, dilation
 // 1 and an even tap count on the height and width axes, 16 taps over the
 // two): a block computes 128 dx channels x a box of one depth position and
-// T1 x T2 = 256 positions, its K loop running over (8-channel chunk of dy,
-// depth tap) stages of all 16 height x width taps.
-constexpr int kBwdPlaneRows = 383;  // halo rows per phase plane, at most (one more row absorbs idle units)
+// T1 x T2 = 256 positions (128 with the K split: the waves then share each
+// stage's K steps in two pairs), its K loop running over (8-channel chunk of
+// dy, depth tap) stages of all 16 height x width taps.
+constexpr int kBwdPlaneRows = 383;    // halo rows per phase plane, at most (one more row absorbs idle units)
+constexpr int kBwdPlaneRowsKS = 255;  // ... with the K split (a 128-position box)
 struct BwdAPArgs {
     int32_t Ci, Co, Cig, Cog, G;  // the forward problem's channels: dx has Ci (groups of Cig), dy Co
     int32_t I[3], O[3], K[3];     // dx extents, dy extents, taps
     int32_t ktot;
-    int32_t T1, T2, lgT2;         // the box (powers of two, T1 * T2 = 256)
-    int32_t E1, E2;               // halo rows of one phase plane: E1 x E2 <= kBwdPlaneRows
+    int32_t T1, T2, lgT2;         // the box (powers of two, T1 * T2 = 256, or 128 with ksplit)
+    int32_t E1, E2;               // halo rows of one phase plane: E1 x E2 <= kBwdPlaneRows(KS)
+    int32_t ksplit;               // 1: 128-position box, the K steps split between wave pairs
     int32_t n_ci_tiles;           // 128-channel tiles of Cig
     int32_t nt[3];                // boxes per axis (nt[0] = I[0]: one depth position per box)
     int32_t n_blocks, xcd_remap;

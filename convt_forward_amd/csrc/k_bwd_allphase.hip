@@ -53,23 +53,30 @@ namespace {
 constexpr int kBwdThreads = 256;
 }  // namespace
 
-template <typename T>
+template <typename T, bool KS>
 __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restrict__ w,
                          T *__restrict__ dx) {
+    // KS (the K split): a 128-position box, waves (w & 1, w >> 1) = (channel
+    // half, K half), each holding all 128 positions and taking four of a
+    // stage's eight K steps; the two K halves' sums meet in LDS at the end
     constexpr int BM = 128;                    // dx channels per block
-    constexpr int BN = 256;                    // dx positions per block (the box)
+    constexpr int BN = KS ? 128 : 256;         // dx positions per block (the box)
     constexpr int MT = 2, NT = 4;              // fragments per wave: channels, positions
+    constexpr int NK = KS ? 4 : 8;             // K steps per wave and stage
     constexpr int NSLOT = 16;                  // height x width taps
     constexpr int WSUB = NSLOT * BM * 16;      // a stage's weight rows
-    constexpr int PLANE = (kBwdPlaneRows + 1) * 16;
+    constexpr int PROWS = KS ? kBwdPlaneRowsKS : kBwdPlaneRows;
+    constexpr int PLANE = (PROWS + 1) * 16;
     constexpr int STAGE = WSUB + 4 * PLANE;
     constexpr int MAIN = 2 * STAGE;
     constexpr int PITCH = 2 * BN + 16;         // epilogue staging bytes per channel
     constexpr int EPI = BM * PITCH;
-    constexpr int LDS_BYTES = MAIN > EPI ? MAIN : EPI;
-    constexpr int XU = 3;                      // halo units per thread and stage
-    static_assert(XU * kBwdThreads >= 2 * kBwdPlaneRows, "halo units cover two planes' rows");
+    constexpr int RED = KS ? 2 * 64 * MT * NT * 64 : 0;  // the K-split sums of two waves, float32
+    constexpr int LDS_A = MAIN > EPI ? MAIN : EPI;
+    constexpr int LDS_BYTES = LDS_A > RED ? LDS_A : RED;
+    constexpr int XU = KS ? 2 : 3;             // halo units per thread and stage
+    static_assert(XU * kBwdThreads >= 2 * PROWS, "halo units cover two planes' rows");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     using HT = typename std::conditional<std::is_same<T, _Float16>::value, _Float16, __bf16>::type;
     using Frag = typename std::conditional<std::is_same<T, _Float16>::value, f16x8, bf16x8>::type;
@@ -78,7 +85,9 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;  // channel half, position half
+    const int wm = KS ? wave & 1 : wave >> 1;  // channel half
+    const int wn = KS ? 0 : wave & 1;          // position half
+    const int kh = KS ? wave >> 1 : 0;         // K half
     const int kv = lane >> 5;                 // lane half: first or second tap of a K step
 
     // ---- block coordinates: channel tile fastest, then the box (width,
@@ -119,7 +128,7 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
     for (int k = 0; k < XU; ++k) {
         const int u = tid + kBwdThreads * k;
         xoff[k] = kOutOfRange;
-        xdst[k] = WSUB + kBwdPlaneRows * 16;
+        xdst[k] = WSUB + PROWS * 16;
         if (u < 2 * npl) {
             const int rh = u >= npl ? 1 : 0;
             const int rem = u - rh * npl;
@@ -167,14 +176,14 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
         return co < a.Cog ? ((uint32_t)co * (uint32_t)ktot + (uint32_t)kds * NSLOT) * 2u : wbytes;
     };
 
-    // ---- MFMA operands. K step i of a stage: taps 2i (lanes 0-31) and
-    // 2i + 1 (lanes 32-63) in (height, width) order. Per lane: the tap's
-    // weight slot row (this lane's channel row of the wave's half) and its
-    // halo plane and shift.
-    int aslot[8], boff[8];
+    // ---- MFMA operands. K step i of a stage (i + 4 kh with the K split):
+    // taps 2i (lanes 0-31) and 2i + 1 (lanes 32-63) in (height, width)
+    // order. Per lane: the tap's weight slot row (this lane's channel row of
+    // the wave's half) and its halo plane and shift.
+    int aslot[NK], boff[NK];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = 2 * i + kv;
+    for (int i = 0; i < NK; ++i) {
+        const int t = 2 * (i + kh * NK) + kv;
         const int kh = t / K2, kw = t - (t / K2) * K2;
         const int sh = a.flip ? a.K[1] - 1 - kh : kh, sw = a.flip ? K2 - 1 - kw : kw;
         const int sl = sh * K2 + sw;
@@ -300,48 +309,71 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
     };
     using V1 = std::integral_constant<int, 1>;
     using V2 = std::integral_constant<int, 2>;
+    using V3 = std::integral_constant<int, 3>;
     // stage s from buffer cur: writes stage s+1 (halo xs, weights in WR) to
     // buffer nxt and loads stage cl = s+2 (halo into xl, weights into WR)
     auto stage_body = [&](unsigned char *cur, unsigned char *nxt, const XRegs &xs, XRegs &xl, int cl)
         __attribute__((always_inline)) {
         const StageOffs so = stage_offs(cl);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(fa[1], fb[1], cur, 1);
-        mfma(fa[0], fb[0]);
-        store_x(xs, 0, nxt);
-        load_x(xl, 0, so);
-        interleave(V1{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(fa[0], fb[0], cur, 2);
-        mfma(fa[1], fb[1]);
-        store_x(xs, 1, nxt);
-        load_x(xl, 1, so);
-        interleave(V1{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(fa[1], fb[1], cur, 3);
-        mfma(fa[0], fb[0]);
-        store_x(xs, 2, nxt);
-        load_x(xl, 2, so);
-        interleave(V1{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(fa[0], fb[0], cur, 4);
-        mfma(fa[1], fb[1]);
-        store_w(nxt, 0);
-        interleave(V2{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(fa[1], fb[1], cur, 5);
-        mfma(fa[0], fb[0]);
-        store_w(nxt, 1);
-        load_w(so);
-        interleave(V2{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(fa[0], fb[0], cur, 6);
-        mfma(fa[1], fb[1]);
-        interleave(V1{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(fa[1], fb[1], cur, 7);
-        mfma(fa[0], fb[0]);
-        interleave(V1{});
+        if constexpr (KS) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[1], fb[1], cur, 1);
+            mfma(fa[0], fb[0]);
+            store_x(xs, 0, nxt);
+            load_x(xl, 0, so);
+            interleave(V1{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[0], fb[0], cur, 2);
+            mfma(fa[1], fb[1]);
+            store_x(xs, 1, nxt);
+            load_x(xl, 1, so);
+            store_w(nxt, 0);
+            interleave(V3{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[1], fb[1], cur, 3);
+            mfma(fa[0], fb[0]);
+            store_w(nxt, 1);
+            load_w(so);
+            interleave(V2{});
+        } else {
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[1], fb[1], cur, 1);
+            mfma(fa[0], fb[0]);
+            store_x(xs, 0, nxt);
+            load_x(xl, 0, so);
+            interleave(V1{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[0], fb[0], cur, 2);
+            mfma(fa[1], fb[1]);
+            store_x(xs, 1, nxt);
+            load_x(xl, 1, so);
+            interleave(V1{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[1], fb[1], cur, 3);
+            mfma(fa[0], fb[0]);
+            store_x(xs, 2, nxt);
+            load_x(xl, 2, so);
+            interleave(V1{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[0], fb[0], cur, 4);
+            mfma(fa[1], fb[1]);
+            store_w(nxt, 0);
+            interleave(V2{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[1], fb[1], cur, 5);
+            mfma(fa[0], fb[0]);
+            store_w(nxt, 1);
+            load_w(so);
+            interleave(V2{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[0], fb[0], cur, 6);
+            mfma(fa[1], fb[1]);
+            interleave(V1{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(fa[1], fb[1], cur, 7);
+            mfma(fa[0], fb[0]);
+            interleave(V1{});
+        }
         __builtin_amdgcn_sched_barrier(0);
         barrier();
         read_frags(fa[0], fb[0], nxt, 0);
@@ -378,6 +410,36 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
     // (mt, nt) holds channel wm*64 + mt*32 + (l & 31) at positions
     // wn*128 + nt*32 + 8q + 4(l / 32) + (0..3) in elements 4q .. 4q+3
     barrier();
+    if constexpr (KS) {
+        // the second K half's sums go through LDS to the first's waves, 16
+        // bytes per lane and instruction, lanes contiguous
+        float4 *red = (float4 *)lds + wm * (MT * NT * 4 * 64) + lane;
+        if (kh == 1) {
+#pragma unroll
+            for (int f = 0; f < MT * NT; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16 &v = acc[f / NT][f % NT];
+                    red[(f * 4 + q) * 64] = float4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+                }
+        }
+        barrier();
+        if (kh == 0) {
+#pragma unroll
+            for (int f = 0; f < MT * NT; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 o = red[(f * 4 + q) * 64];
+                    f32x16 &v = acc[f / NT][f % NT];
+                    v[4 * q] += o.x;
+                    v[4 * q + 1] += o.y;
+                    v[4 * q + 2] += o.z;
+                    v[4 * q + 3] += o.w;
+                }
+        }
+        barrier();
+    }
+    if (kh == 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int ci = wm * 64 + mt * 32 + (lane & 31);
@@ -391,10 +453,11 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
                 *(u32x2 *)(lds + ci * PITCH + pos * 2) = v;
             }
     }
+    }
     barrier();
 
-    // ---- stores: piece pc (16 bytes, 8 positions) is channel pc / 32, box
-    // positions 8 (pc % 32) ..; the box's rows are T1 rows of T2 positions,
+    // ---- stores: piece pc (16 bytes, 8 positions) is channel pc / (BN / 8),
+    // box positions 8 (pc % (BN / 8)) ..; the box's rows are T1 rows of T2 positions,
     // whole pieces since T2 and the dx row length are multiples of 8.
     // Channels past Cig and positions past dx take the out-of-range offset.
     const uint32_t xpl2 = (uint32_t)a.x_plane * 2u;
@@ -404,7 +467,7 @@ void allphase_bwd_kernel(BwdAPArgs a, const T *__restrict__ dy, const T *__restr
 #pragma unroll 4
     for (int i = 0; i < BM * BN / 8 / kBwdThreads; ++i) {
         const int pc = tid + kBwdThreads * i;
-        const int ci = pc >> 5, rem = pc & 31;
+        const int ci = pc / (BN / 8), rem = pc % (BN / 8);
         const int pos = rem * 8;
         const int row = pos >> a.lgT2, col = pos & (T2 - 1);
         const u32x4 v = *(const u32x4 *)(lds + ci * PITCH + rem * 16);
@@ -419,8 +482,12 @@ template <typename T>
 static hipError_t launch_bwd_allphase_t(const Plan &pl, const void *dy, const void *w, void *dx,
                                         hipStream_t stream) {
     const BwdAPArgs &a = pl.bap;
-    hipLaunchKernelGGL((allphase_bwd_kernel<T>), dim3(a.n_blocks), dim3(kBwdThreads), 0, stream, a,
-                       (const T *)dy, (const T *)w, (T *)dx);
+    if (a.ksplit)
+        hipLaunchKernelGGL((allphase_bwd_kernel<T, true>), dim3(a.n_blocks), dim3(kBwdThreads), 0, stream, a,
+                           (const T *)dy, (const T *)w, (T *)dx);
+    else
+        hipLaunchKernelGGL((allphase_bwd_kernel<T, false>), dim3(a.n_blocks), dim3(kBwdThreads), 0, stream, a,
+                           (const T *)dy, (const T *)w, (T *)dx);
     return hipGetLastError();
 }
 

@@ -714,8 +714,8 @@ bool direct_bwd_eligible(const DevParams &fp, int elem_bytes) {
 // lies in one row), dx rows of whole 16-byte pieces; 32-bit buffer offsets
 // (dy up to 32 channels past the group, for the stages the pipeline loads
 // ahead); at least min_cig dx channels per group. The box is one depth
-// position x T1 x T2 = 256 positions whose four phase-plane halos fit the
-// kernel's planes.
+// position x T1 x T2 = 256 positions (128 with the K split) whose four
+// phase-plane halos fit the kernel's planes.
 bool choose_bwd_allphase(Plan *pl, int ndim, int dtype, int64_t min_cig) {
     const DevParams &fp = pl->dp;
     if (dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16) return false;
@@ -743,20 +743,30 @@ bool choose_bwd_allphase(Plan *pl, int ndim, int dtype, int64_t min_cig) {
             u[x][c] = (int32_t)(floor_half(c - p) - tmin[x]);
         }
     }
-    // the box: the fewest boxes per plane, then the smallest halo
-    int T1 = 0, T2 = 0;
-    int64_t E1 = 0, E2 = 0, best_boxes = 0;
-    for (int t2 = 16; t2 <= 64; t2 *= 2) {
-        const int t1 = 256 / t2;
-        const int64_t e1 = t1 + a1.K / 2 - 1 + u[0][1], e2 = t2 + a2.K / 2 - 1 + u[1][1];
-        if (e1 * e2 > kBwdPlaneRows) continue;
-        const int64_t boxes = ceil_div(a1.I, t1) * ceil_div(a2.I, t2);
-        if (T2 == 0 || boxes < best_boxes || (boxes == best_boxes && e1 * e2 < E1 * E2)) {
-            T1 = t1;
-            T2 = t2;
-            E1 = e1;
-            E2 = e2;
-            best_boxes = boxes;
+    // the box and the K split: a block per CU (256 CUs) and per stage about
+    // 2048 MFMA cycles per wave plus ~1000 of staging, or with the K split
+    // (128-position boxes, two wave pairs sharing a stage's K steps) 1024 +
+    // ~730; among equal times the smaller halo
+    const int64_t n_ci = ceil_div(fp.Cig, 128), per_img = (int64_t)a0.I * n_ci * fp.G * fp.B;
+    int T1 = 0, T2 = 0, KS = 0;
+    int64_t E1 = 0, E2 = 0;
+    double best = 0;
+    for (int ks = 0; ks <= 1; ++ks) {
+        const int bn = ks ? 128 : 256;
+        for (int t2 = 16; t2 <= 64; t2 *= 2) {
+            const int t1 = bn / t2;
+            const int64_t e1 = t1 + a1.K / 2 - 1 + u[0][1], e2 = t2 + a2.K / 2 - 1 + u[1][1];
+            if (e1 * e2 > (ks ? kBwdPlaneRowsKS : kBwdPlaneRows)) continue;
+            const int64_t blocks = ceil_div(a1.I, t1) * ceil_div(a2.I, t2) * per_img;
+            const double t = std::ceil((double)blocks / 256.0) * (ks ? 1760.0 : 3050.0);
+            if (T2 == 0 || t < best * 0.999 || (t <= best * 1.001 && e1 * e2 < E1 * E2)) {
+                T1 = t1;
+                T2 = t2;
+                E1 = e1;
+                E2 = e2;
+                KS = ks;
+                best = t;
+            }
         }
     }
     if (T2 == 0) return false;
@@ -776,6 +786,7 @@ bool choose_bwd_allphase(Plan *pl, int ndim, int dtype, int64_t min_cig) {
     ba.lgT2 = __builtin_ctz((unsigned)T2);
     ba.E1 = (int32_t)E1;
     ba.E2 = (int32_t)E2;
+    ba.ksplit = KS;
     ba.n_ci_tiles = (int32_t)ceil_div(fp.Cig, 128);
     ba.nt[0] = a0.I;
     ba.nt[1] = (int32_t)ceil_div(a1.I, T1);

@@ -122,9 +122,10 @@ struct AllPhaseArgs {
     int32_t has_bias, act, flip;
     // height / width: the taps of residue r are k = k0[r] - 2j at input
     // offset off0[r] + j (j < K/2); the halo starts at offset uh (height)
-    // and uw (width, even) from the q box and spans E1 x E2 positions (E2 even)
+    // and uw (width, even) from the q box and spans E1 x E2 positions (E2
+    // even), its rows E2p apart in LDS (24 for 16-wide boxes, else E2)
     int32_t kh0[2], offh0[2], kw0[2], offw0[2];
-    int32_t uh, uw, E1, E2;
+    int32_t uh, uw, E1, E2, E2p;
     // depth: residue rd's taps are k = kd0[rd] - kstep_d j at input offset
     // offd[rd] + ostep_d j (j < nd, the same count for every residue); its q
     // count is qnd[rd]

@@ -132,7 +132,7 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
     const int q00 = t0 * T0, q01 = t1 * T1, q02 = t2 * T2;
     const int co0 = co_t * BM;
     const int offd = a.offd[rd];
-    const int E0 = T0 + (a.nd - 1) * a.ostep_d, E1 = a.E1, E2 = a.E2;
+    const int E0 = T0 + (a.nd - 1) * a.ostep_d, E1 = a.E1, E2 = a.E2, E2p = a.E2p;
     const int npairs = E0 * E1 * (E2 >> 1);  // position pairs of one chunk's halo
 
 
@@ -155,7 +155,7 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
             const int hp = E2 >> 1;
             const int prh = div_small(pr, hp), cp = pr - prh * hp;
             const int e0 = div_small(prh, E1), e1 = prh - e0 * E1;
-            const int row = (e0 * E1 + e1) * E2 + 2 * cp;
+            const int row = (e0 * E1 + e1) * E2p + 2 * cp;
             xdst[k] = WBUF + sc * XSUB + row * 16;
             const int i0 = q00 + offd + e0, i1 = q01 + a.uh + e1, i2 = q02 + a.uw + 2 * cp;
             if (i0 >= 0 && i0 < a.I[0] && i1 >= 0 && i1 < a.I[1] && i2 >= 0 && i2 < a.I[2])
@@ -210,17 +210,20 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
         // the slot's rows are swizzled by its octet (slot / 8), within 32-row groups
         const int slot = jd * K12 + kh * a.K[2] + kw;
         aslot[p] = slot * (BM * 16) + (((lane & 31) ^ octet_rot<NPAIR>(slot >> 3)) * 16);
-        boff[p] = ((jd * a.ostep_d * E1 + a.offh0[rh] + jh - a.uh) * E2 + a.offw0[rw] + jw - a.uw) * 16;
+        boff[p] = ((jd * a.ostep_d * E1 + a.offh0[rh] + jh - a.uh) * E2p + a.offw0[rw] + jw - a.uw) * 16;
     }
-    // halo row (bytes) of this lane's position n = nt * 32 + (lane & 31) for
-    // a zero tap shift: the box extents are powers of two with T2 >= 16, so
-    // the lane's 5 bits and nt's bits never carry into each other and the row
-    // splits into a per-lane part and a wave-uniform part per fragment
+    // halo row (bytes) of this lane's position n = nt * 32 + fpos for a zero
+    // tap shift (fpos: the lane's place in the fragment, frag16_pos for
+    // 16-wide boxes, whose halo rows are E2p = 24 apart): the box extents are
+    // powers of two with T2 >= 16, so the lane's 5 bits and nt's bits never
+    // carry into each other and the row splits into a per-lane part and a
+    // wave-uniform part per fragment
     auto halo_row = [&](int n) __attribute__((always_inline)) {
         const int c2 = n & (T2 - 1), c1 = (n >> a.lgT2) & (T1 - 1), c0 = n >> (a.lgT1 + a.lgT2);
-        return ((c0 * E1 + c1) * E2 + c2) * 16;
+        return ((c0 * E1 + c1) * E2p + c2) * 16;
     };
-    const int brow = halo_row(lane & 31);
+    const int fpos = T2 == 16 ? frag16_pos(lane & 31) : (lane & 31);
+    const int brow = halo_row(fpos);
     int bnt[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) bnt[nt] = __builtin_amdgcn_readfirstlane(halo_row(nt * 32));
@@ -401,7 +404,7 @@ void allphase_gemm_kernel(AllPhaseArgs a, const T *__restrict__ x, const T *__re
         constexpr int A = decltype(act_tag)::value;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int n = nt * 32 + (lane & 31);
+            const int n = nt * 32 + fpos;
             const int c2 = n & (T2 - 1), c1 = (n >> a.lgT2) & (T1 - 1), c0 = n >> (a.lgT1 + a.lgT2);
             const int pos = ((c0 * 2 * T1 + 2 * c1 + rh) * 2 * T2 + 2 * c2 + rw) * 2;
 #pragma unroll

@@ -293,6 +293,18 @@ __device__ __forceinline__ int div_small(int a, int b) {
     return q;
 }
 
+// The box position (within a 32-position operand fragment) that lane i
+// (0..31) reads when the box rows are 16 positions long, so that a fragment
+// covers two box rows: lanes 0-7 and 24-31 the first (columns 0-7, 8-15),
+// lanes 8-23 the second. With the rows 24 x 16 bytes apart in LDS, a wave's
+// 16-byte reads of such a fragment then meet no bank conflict (measured on
+// gfx950 with an LDS probe under rocprofv3: lanes 0-15 on the first row
+// conflict two-way at every row pitch that is not a multiple of 16 rows).
+__device__ __forceinline__ int frag16_pos(int i) {
+    const int q = i >> 3;
+    return ((q == 1 || q == 2) ? 16 : 0) + (i & 7) + ((q >> 1) << 3);
+}
+
 // n / d for any 32-bit n through the multiplier the planner derives for d
 // (FastDiv): q = (mulhi(n, m) + n) >> s in 33-bit arithmetic.
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {

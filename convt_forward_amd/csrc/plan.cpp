@@ -380,7 +380,9 @@ bool choose_allphase(Plan *pl, const DevParams &dp, int ndim, int dtype, int64_t
                 const int64_t e0 = t0 + (int64_t)(nd - 1) * a0.ostep;
                 const int64_t e1 = t1 + a1.umax - a1.umin;
                 const int64_t e2 = (t2 + a2.umax - uw + 1) & ~(int64_t)1;
-                const int64_t rows = e0 * e1 * e2;
+                // 16-wide boxes: halo rows 24 apart (allphase_halo_pitch)
+                if (t2 == 16 && e2 > 24) continue;
+                const int64_t rows = e0 * e1 * (t2 == 16 ? 24 : e2);
                 if (rows > rows_cap) continue;
                 const int64_t nt = ceil_div(a0.qmax, t0) * ceil_div(a1.qmax, t1) * ceil_div(a2.qmax, t2);
                 const int64_t blocks = nt * ceil_div(dp.Cog, bm) * a0.S * dp.G * dp.B;
@@ -446,6 +448,7 @@ bool choose_allphase(Plan *pl, const DevParams &dp, int ndim, int dtype, int64_t
     ap.uw = uw;
     ap.E1 = bt[1] + a1.umax - a1.umin;
     ap.E2 = (bt[2] + a2.umax - uw + 1) & ~1;
+    ap.E2p = bt[2] == 16 ? 24 : ap.E2;
     ap.S0 = a0.S;
     ap.nd = nd;
     ap.kstep_d = a0.kstep;

@@ -57,7 +57,7 @@ constexpr int kNThreads = 256;
 
 }  // namespace
 
-template <typename T, int WGM, int GS, int XU, bool ACT>
+template <typename T, int WGM, int GS, int XU, bool ACT, bool Y16>
 __global__ __launch_bounds__(kNThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__restrict__ wr,
                             const T *__restrict__ bias, T *__restrict__ y) {
@@ -403,22 +403,72 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
                 }
             }
     };
+    // Y16 (width stride 1, output rows of whole 16-byte pieces, y 16-byte
+    // aligned; a compile-time choice, so that each instance holds one store
+    // path): a wave stages 32 channels x its 128 positions at a time in
+    // LDS (the stage buffers are free past the loop's last barrier) and
+    // stores 16-byte row pieces, 8 positions each, instead of 2-byte stores
+    auto store_staged = [&](auto act_tag) __attribute__((always_inline)) {
+        constexpr int A = decltype(act_tag)::value;
+        constexpr int SP = 2 * NT * 32 + 16;  // staging bytes per channel
+        unsigned char *stg = lds + wave * (32 * SP);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int j = 0; j < 16; j += 2) {
+                const int r = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);  // fragment rows r, r + 1
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    float v0 = acc[mt][nt][j], v1 = acc[mt][nt][j + 1];
+                    if constexpr (A != CONVT_ACT_NONE) {
+                        v0 = activate<true>(A, v0);
+                        v1 = activate<true>(A, v1);
+                    }
+                    const uint32_t pk = pack_half2<HT>(v0, v1);
+                    const int pos = nt * 32 + (lane & 31);
+                    *(uint16_t *)(stg + r * SP + pos * 2) = (uint16_t)pk;
+                    *(uint16_t *)(stg + (r + 1) * SP + pos * 2) = (uint16_t)(pk >> 16);
+                }
+            }
+            // piece k = lane + 64 i: channel row k / 16, positions 8 (k % 16) ..
+#pragma unroll
+            for (int i = 0; i < NT * 32 * 32 / 8 / 64; ++i) {
+                const int k = lane + 64 * i, r = k >> 4, pp = k & 15;
+                const u32x4 v = *(const u32x4 *)(stg + r * SP + pp * 16);
+                const int n = wn * NT * 32 + pp * 8;
+                const int c2 = n & (T2 - 1), c1 = (n >> lg2) & (T1 - 1), c0 = n >> (lg2 + lg1);
+                const int qd = q00 + c0, qh = q01 + c1, qw = q02 + c2;
+                uint32_t off = kOutOfRange;
+                if (qd < ph.qn[0] && qh < ph.qn[1] && qw < ph.qn[2]) {
+                    const int o0 = a0.S * qd + ph.r[0], o1 = a1.S * qh + ph.r[1];
+                    off = (uint32_t)((o0 * a1.O + o1) * a2.O + qw) * 2u;
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(v, ys, off, (uint32_t)(mt * 32 + r) * ypl_bytes, 0);
+            }
+        }
+    };
+    auto store = [&](auto act_tag) __attribute__((always_inline)) {
+        if constexpr (Y16)
+            store_staged(act_tag);
+        else
+            store_all(act_tag);
+    };
     if constexpr (ACT) {
         switch (p.act) {
-            case CONVT_ACT_RELU: store_all(std::integral_constant<int, CONVT_ACT_RELU>{}); break;
-            case CONVT_ACT_SIGMOID: store_all(std::integral_constant<int, CONVT_ACT_SIGMOID>{}); break;
-            case CONVT_ACT_TANH: store_all(std::integral_constant<int, CONVT_ACT_TANH>{}); break;
-            case CONVT_ACT_SILU: store_all(std::integral_constant<int, CONVT_ACT_SILU>{}); break;
-            case CONVT_ACT_GELU: store_all(std::integral_constant<int, CONVT_ACT_GELU>{}); break;
-            default: store_all(std::integral_constant<int, CONVT_ACT_NONE>{}); break;
+            case CONVT_ACT_RELU: store(std::integral_constant<int, CONVT_ACT_RELU>{}); break;
+            case CONVT_ACT_SIGMOID: store(std::integral_constant<int, CONVT_ACT_SIGMOID>{}); break;
+            case CONVT_ACT_TANH: store(std::integral_constant<int, CONVT_ACT_TANH>{}); break;
+            case CONVT_ACT_SILU: store(std::integral_constant<int, CONVT_ACT_SILU>{}); break;
+            case CONVT_ACT_GELU: store(std::integral_constant<int, CONVT_ACT_GELU>{}); break;
+            default: store(std::integral_constant<int, CONVT_ACT_NONE>{}); break;
         }
     } else {
-        store_all(std::integral_constant<int, CONVT_ACT_NONE>{});
+        store(std::integral_constant<int, CONVT_ACT_NONE>{});
     }
 }
 
-template <typename T, int CFG>
-static hipError_t launch_nchw_t(const Plan &pl, const void *x, const void *wr, const void *bias,
+template <typename T, int CFG, bool Y16>
+static hipError_t launch_nchw_y(const Plan &pl, const void *x, const void *wr, const void *bias,
                                 void *y, hipStream_t stream) {
     constexpr tiles::NchwCfg C = tiles::kNchwCfg[CFG];
     const DevParams &p = pl.dp;
@@ -426,13 +476,24 @@ static hipError_t launch_nchw_t(const Plan &pl, const void *x, const void *wr, c
     const size_t lds = 0;  // static
 #ifndef NCHW_TUNE
     if (p.act != CONVT_ACT_NONE)
-        hipLaunchKernelGGL((phase_gemm_nchw_kernel<T, C.wgm, C.gs, C.xu, true>), grid, block, lds, stream,
+        hipLaunchKernelGGL((phase_gemm_nchw_kernel<T, C.wgm, C.gs, C.xu, true, Y16>), grid, block, lds, stream,
                            p, (const T *)x, (const T *)wr, (const T *)bias, (T *)y);
     else
 #endif
-        hipLaunchKernelGGL((phase_gemm_nchw_kernel<T, C.wgm, C.gs, C.xu, false>), grid, block, lds, stream,
+        hipLaunchKernelGGL((phase_gemm_nchw_kernel<T, C.wgm, C.gs, C.xu, false, Y16>), grid, block, lds, stream,
                            p, (const T *)x, (const T *)wr, (const T *)bias, (T *)y);
     return hipGetLastError();
+}
+
+template <typename T, int CFG>
+static hipError_t launch_nchw_t(const Plan &pl, const void *x, const void *wr, const void *bias,
+                                void *y, hipStream_t stream) {
+    const DevParams &p = pl.dp;
+    // 16-byte output pieces: width stride 1 (a phase's outputs contiguous
+    // along the row), rows and the box's width whole 8-position pieces
+    const bool y16 = p.ax[2].S == 1 && p.ax[2].O % 8 == 0 && p.tw % 8 == 0 && (uintptr_t)y % 16 == 0;
+    return y16 ? launch_nchw_y<T, CFG, true>(pl, x, wr, bias, y, stream)
+               : launch_nchw_y<T, CFG, false>(pl, x, wr, bias, y, stream);
 }
 
 template <typename T>

@@ -31,6 +31,11 @@ CASES = [
     ("k4s2_asym", (1, 32, 12, 16), (32, 160, 4, 4), (2, 2), ((0, 2), (2, 1)), (1, 1), (1, 0), 1),
     ("k4s2_3d_asym", (1, 24, 4, 5, 10), (24, 80, 4, 4, 4), (2, 2, 2), ((1, 0), (0, 2), (2, 1)),
      (1, 1, 1), (0, 1, 1), 1),
+    # width stride 1 with output rows of whole 16-byte pieces: the outputs
+    # leave through LDS staging as 16-byte row pieces
+    ("k3s1_dil2_rows24", (2, 40, 22, 24), (40, 130, 3, 3), (1, 1), (2, 2), (2, 2), (0, 0), 1),
+    ("k3s1_rows16_groups", (2, 48, 13, 16), (48, 72, 3, 3), (1, 1), (1, 1), (1, 1), (0, 0), 2),
+    ("k3s1_rows40_op", (1, 32, 9, 40), (32, 200, 3, 3), (1, 1), (1, 1), (1, 1), (0, 0), 1),
 ]
 
 

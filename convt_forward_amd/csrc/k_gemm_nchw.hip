@@ -160,9 +160,9 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
     const int nchunks = p.cig_pad / 16;
     const uint32_t tile_stride = (uint32_t)nchunks * (uint32_t)p.cog_pad * WROW;  // between taps
     const uint32_t chunk_stride = (uint32_t)p.cog_pad * WROW;
-    const __amdgpu_buffer_rsrc_t wrs =
-        make_rsrc(wr + (int64_t)(g * p.ktot_pad + ph.tapbase) * nchunks * p.cog_pad * 16,
-                  (uint32_t)GS * tile_stride);
+    const u32x4 wrs = rsrc_words(wr + (int64_t)(g * p.ktot_pad + ph.tapbase) * nchunks * p.cog_pad * 16,
+                                 (uint32_t)GS * tile_stride);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)&lds[0];
     uint32_t woff[WV];
 #pragma unroll
     for (int j = 0; j < WV; ++j) {
@@ -171,22 +171,27 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
         woff[j] = (uint32_t)t * tile_stride + (uint32_t)co0 * WROW + (uint32_t)within * 16u;
     }
 
-    // ---- register stages ----
-    struct Stage {
-        u32x4 w[WV];
-        uint32_t xv[XU][8];
-    };
-    // part t (of GS) of loading chunk c into a stage's registers: the weight
-    // vectors j and halo units k with j, k = t (mod GS)
-    // (offsets common to the wave go in the scalar offset, which the range
-    // check includes like the vector one)
-    auto load_part = [&](Stage &st, int c, int t) __attribute__((always_inline)) {
+    // ---- weights go global -> LDS directly (16-byte LDS-destination
+    // loads, one stage ahead: lane l of vector v = tid + 256 j lands at
+    // wsb + v * 16, the tiles' linear layout); part t (of GS) copies the
+    // vectors j with j = t (mod GS) of chunk c into buffer wsb
+    auto copy_w_part = [&](unsigned char *wsb, int c, int t) __attribute__((always_inline)) {
         const uint32_t cw = (uint32_t)c * chunk_stride;
+        const uint32_t base = lds_base + (uint32_t)(wsb - lds) + (uint32_t)wave * 1024u;
 #pragma unroll
         for (int j = 0; j < WV; ++j) {
             if (j % GS != t) continue;
-            st.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, woff[j], cw, 0));
+            copy_to_lds<16>(base + (uint32_t)(j * kNThreads * 16), woff[j] + cw, wrs);
         }
+    };
+    // ---- register stages (the input halo) ----
+    struct Stage {
+        uint32_t xv[XU][8];
+    };
+    // part t (of GS) of loading chunk c into a stage's registers: the halo
+    // units k with k = t (mod GS) (offsets common to the wave go in the
+    // scalar offset, which the range check includes like the vector one)
+    auto load_part = [&](Stage &st, int c, int t) __attribute__((always_inline)) {
         const uint32_t cx = (uint32_t)(c * 16) * plane2;
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
@@ -200,17 +205,9 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
 #pragma unroll
         for (int t = 0; t < GS; ++t) load_part(st, c, t);
     };
-    // part t (of GS) of writing a stage's registers to LDS: the weight
-    // vectors j and halo units k with j, k = t (mod GS); units past the halo
-    // write nothing
-    auto store_part = [&](const Stage &st, unsigned char *wsb, unsigned char *xsb, int t)
-        __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < WV; ++j) {
-            if (j % GS != t) continue;
-            const int v = tid + kNThreads * j;
-            *(u32x4 *)(wsb + v * 16) = st.w[j];
-        }
+    // part t (of GS) of writing a stage's registers to LDS: the halo units k
+    // with k = t (mod GS); units past the halo write the sink
+    auto store_part = [&](const Stage &st, unsigned char *xsb, int t) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
             if (k % GS != t) continue;
@@ -224,9 +221,9 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
             *(u32x4 *)(xsb + (used ? xdst[k] + WROW : sink + 16)) = r1;
         }
     };
-    auto store_stage = [&](const Stage &st, unsigned char *wsb, unsigned char *xsb) __attribute__((always_inline)) {
+    auto store_stage = [&](const Stage &st, unsigned char *xsb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < GS; ++t) store_part(st, wsb, xsb, t);
+        for (int t = 0; t < GS; ++t) store_part(st, xsb, t);
     };
 
     // ---- MFMA operands ----
@@ -289,12 +286,13 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
     };
     // the MFMAs of one stage from LDS buffers (wsb, xsb). Between the taps'
     // MFMA groups (issued as a whole, so the matrix pipe stays fed) the wave
-    // writes part of the next stage's registers (nst) to its LDS buffers
-    // (nwsb, nxsb), which no wave reads during this stage, and issues part of
-    // the global loads of chunk lc into the registers lst: spread this way,
+    // copies part of chunk wc's weights into the next stage's buffer nwsb,
+    // writes part of the next stage's halo registers (nst) to its buffer
+    // nxsb (no wave reads those buffers during this stage), and issues part
+    // of the halo loads of chunk lc into the registers lst: spread this way,
     // neither the loads nor the stores hold up the MFMA issue in one burst.
     auto compute = [&](const unsigned char *wsb, const unsigned char *xsb, const Stage &nst,
-                       unsigned char *nwsb, unsigned char *nxsb, Stage &lst, int lc)
+                       unsigned char *nwsb, unsigned char *nxsb, Stage &lst, int lc, int wc)
         __attribute__((always_inline)) {
         Frag fa[2][MT], fb[2][NT];
         read_frags(fa[0], fb[0], wsb, xsb, 0);
@@ -303,7 +301,8 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
             __builtin_amdgcn_sched_barrier(0);
             if (t + 1 < GS) read_frags(fa[(t + 1) & 1], fb[(t + 1) & 1], wsb, xsb, t + 1);
             mfma(fa[t & 1], fb[t & 1]);
-            store_part(nst, nwsb, nxsb, t);
+            copy_w_part(nwsb, wc, t);
+            store_part(nst, nxsb, t);
             load_part(lst, lc, t);
             // issue order within the tap: each MFMA followed by at most one
             // LDS read, one global load, one LDS write and a few VALU ops
@@ -318,18 +317,20 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto barrier = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    };
+    // the weight copies of the next stage (and every other load) landed,
+    // this wave's LDS writes done, then the block's barrier
+    auto barrier = [&]() __attribute__((always_inline)) { stage_barrier<0>(); };
 
     // ---- pipeline over the chunks (an even count: the planner pads the
     // channels to whole pairs of chunks with zero weights) ----
     const int last = nchunks - 1;
     Stage R0, R1;
+#pragma unroll
+    for (int t = 0; t < GS; ++t) copy_w_part(ws0, 0, t);
     load_stage(R0, 0);
     load_stage(R1, 1);
     if (tid < BM) bias_s[tid] = bias_v;
-    store_stage(R0, ws0, xs0);
+    store_stage(R0, xs0);
     barrier();
     // the accumulators start at the bias of their output channel (lane l of
     // fragment (mt, nt) holds rows mt*32 + 8*(j/4) + 4*(l/32) + j%4)
@@ -345,10 +346,10 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
         // stage c from buffers 0, writing stage c + 1 (R1) to buffers 1 and
         // loading chunk c + 2 into R0; the loads past the last chunk repeat
         // it and are never used
-        compute(ws0, xs0, R1, ws1, xs1, R0, min(c + 2, last));
+        compute(ws0, xs0, R1, ws1, xs1, R0, min(c + 2, last), c + 1);
         barrier();
         // stage c + 1 from buffers 1, writing stage c + 2 (R0) to buffers 0
-        compute(ws1, xs1, R0, ws0, xs0, R1, min(c + 3, last));
+        compute(ws1, xs1, R0, ws0, xs0, R1, min(c + 3, last), min(c + 2, last));
         barrier();
     }
 

@@ -164,19 +164,23 @@ struct BwdAPArgs {
     int32_t r1[2], u1[2], r2[2], u2[2];
 };
 
-// Grouped route: the kernel's slot table and tap map, built by the planner
-// and passed with the kernel's arguments (the kernel copies the table to LDS
-// and gathers its group's weights from W as stored).
+// Grouped route: the kernel's slot table, built by the planner and passed
+// with the kernel's arguments (the kernel copies it to LDS together with its
+// group's weights as W stores them, and reads its weight fragments there).
 constexpr int kGrpTabMax = 2 * kMaxPhaseTab + 64;  // int2 entries: 2 per phase, then the slots
 constexpr int kGrpMaxTaps = 64;                    // taps of the grouped route (its weight slab bound)
-static_assert(kGrpTabMax <= 256, "the grouped kernel copies one table entry per thread");
+static_assert(kGrpTabMax <= 256, "the grouped kernel's table fits one 4-byte copy per lane of 8 waves");
 struct GrpTables {
     int32_t tab_n;                    // int2 entries used
     int32_t tab[2 * kGrpTabMax];      // per phase an int4 record (q counts; first slot | slot
                                       // count << 16), then per (tap, 8-channel slice) slot the
-                                      // halo byte offset of the tap's window and the element
-                                      // offset of its weights in the LDS slab [tap][16][Cig]
-    uint8_t tg_of[kGrpMaxTaps];       // tap in plan order of each stored tap (W's own tap index)
+                                      // halo byte offset of the tap's window and the byte offset
+                                      // in the group's weights (as stored) of the tap's first
+                                      // channel of the slice, output channel 0
+    int32_t w_sc, w_so;               // bytes between consecutive input / output channels of
+                                      // the group's weights as stored
+    int32_t w_tap_pieces;             // 16-byte pieces per tap when W stores the group's
+                                      // weights tap by tap (taps outermost), else 0 (one run)
 };
 
 struct Plan {

@@ -104,9 +104,8 @@ struct GrpArgs {
     int32_t grp_hwp, grp_hshift, grp_nk, grp_nsc;
     int32_t grp_w_off, grp_tab_off, grp_st_off, grp_st_pitch;
     int32_t ktot, nphase;
-    int32_t w_layout;                   // convt_filter_layout of W
     int32_t tab_n;                      // int2 entries of tab
-    uint32_t tg_of[kGrpMaxTaps / 4];    // plan-order tap of each stored tap, 4 bytes per word
+    int32_t w_sc, w_so, w_tap_pieces;   // the group's weights as stored (GrpTables)
     int32_t tab[2 * kGrpTabMax];        // the slot table (GrpTables)
 };
 
@@ -114,12 +113,17 @@ struct GrpArgs {
 // scalar registers are capped too, since more of them than the cap admits
 // keep blocks from being resident. Instances with more weight fragments in
 // registers (S2 * KS > 2) trade occupancy for having no spills.
-template <int S2, int KS, typename E, int ACT>
+//
+// PD: the host has checked that every item takes the segment-pair path
+// (width stride 2, at most 8 channels, whole segments, every phase's slots
+// filling its K steps, y aligned for 16-byte row pieces); the instance holds
+// only that path, none of the other paths' set-up.
+template <int S2, int KS, typename E, int ACT, bool PD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 2 ? 8 : 4, 8))) void grouped_kernel(
     GrpArgs p, const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ y, int st_align, int x_vec) {
+    static_assert(!PD || S2 == 2, "the segment-pair path needs width stride 2");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    const uint16_t *wsl = (const uint16_t *)(lds + p.grp_w_off);
 
     const int tid = threadIdx.x, lane = tid & 63;
     // uniform per wave: lets the plan tables be read with scalar loads
@@ -136,92 +140,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     const int h0 = qd + a0.umin, h1 = q0h + a1.umin, h2 = a2.umin;
     const int nrow = p.hd * HH;
 
-    // 1a. the group's weights, gathered from W as stored into the LDS slab
-    // [tap][16 channels][Cig], taps in the plan's order (tg_of maps each
-    // stored tap to its place, so the tap flip and the phase grouping happen
-    // here), and the slot table (a record per phase, then per (tap, slice)
-    // slot the LDS byte offset of the tap's window origin in the halo and the
-    // weight offset), both from the kernel arguments. Every read is issued
-    // here at once, none depending on another (W in its own memory order,
-    // coalesced; the map entry of each element's stored tap and the table
-    // entry per lane): no read of the argument segment (a slow path) sits in
-    // a dependent chain. They are written before the halo is staged (the
-    // halo's registers leave no room to hold them across it).
-    const unsigned char *kseg = (const unsigned char *)__builtin_amdgcn_kernarg_segment_ptr();
-    const uint8_t *tgp = kseg + offsetof(GrpArgs, tg_of);
-    const __amdgpu_buffer_rsrc_t wrs =
-        make_rsrc(w, (uint32_t)p.Ci * (uint32_t)p.Cog * (uint32_t)p.ktot * 2u);
-    const int nraw = Cig * p.Cog * p.ktot;  // the group's elements of W
-    // element e of the group's W in memory order: the element (zero past the
-    // group), its stored tap and its offset co * Cig + cil within a tap
-    auto raw_elem = [&](int e, int &st, int &cc) __attribute__((always_inline)) {
-        int cil, co;
-        uint32_t o;
-        if (p.w_layout == CONVT_FILTER_K_CI_CO) {  // [k][C_in][Cog]
-            const int r = div_small(e, p.Cog);
-            co = e - r * p.Cog;
-            st = div_small(r, Cig);
-            cil = r - st * Cig;
-            o = ((uint32_t)st * p.Ci + g * Cig + cil) * p.Cog + co;
-        } else if (p.w_layout == CONVT_FILTER_K_CO_CI) {  // [k][C_out][Cig]
-            const int r = div_small(e, Cig);
-            cil = e - r * Cig;
-            st = div_small(r, p.Cog);
-            co = r - st * p.Cog;
-            o = ((uint32_t)st * p.Co + g * p.Cog + co) * Cig + cil;
-        } else {  // [C_in][Cog][k]
-            const int r = div_small(e, p.ktot);
-            st = e - r * p.ktot;
-            cil = div_small(r, p.Cog);
-            co = r - cil * p.Cog;
-            o = (uint32_t)(g * Cig) * p.Cog * p.ktot + (uint32_t)e;
-        }
-        cc = co * Cig + cil;
-        st = e < nraw ? st : 0;
-        return __builtin_amdgcn_raw_buffer_load_b16(wrs, e < nraw ? o * 2u : kOutOfRange, 0, 0);
-    };
-    // the first 4 elements of each thread: value | (co * Cig + cil) << 16
-    // (< 2^10), and the plan-order tap of its stored tap
-    uint32_t wfirst[4];
-    uint32_t wtg[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        int st, cc;
-        wfirst[u] = (uint32_t)raw_elem(tid + 256 * u, st, cc) | (uint32_t)cc << 16;
-        wtg[u] = tgp[st];
-    }
-    // the table has at most kGrpTabMax <= 256 entries: one per thread
-    const int2 tab0 = ((const int2 *)(kseg + offsetof(GrpArgs, tab)))[min(tid, kGrpTabMax - 1)];
-    // the slot table, then the weight slab: the first batch, W's remaining
-    // elements (past 1024), and zero rows for the channels past Cog
-    auto write_tables = [&]() __attribute__((always_inline)) {
-        if (tid < p.tab_n) ((int2 *)(lds + p.grp_tab_off))[tid] = tab0;
-        uint16_t *slab = (uint16_t *)(lds + p.grp_w_off);
-        const int tap_el = tiles::kGrpCog * Cig;  // slab elements per tap
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (tid + 256 * u < nraw) slab[(int)wtg[u] * tap_el + (int)(wfirst[u] >> 16)] = (uint16_t)wfirst[u];
-        for (int e0 = 1024; e0 < nraw; e0 += 1024) {  // uniform
-            uint16_t v[4];
-            int cc[4], tg[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                int st;
-                v[u] = raw_elem(e0 + tid + 256 * u, st, cc[u]);
-                tg[u] = tgp[st];
+    // 1a. the group's part of W, as stored, and the slot table (a record per
+    // phase, then per (tap, slice) slot the LDS byte offset of the tap's
+    // window origin in the halo and the byte offset of its weights in the
+    // group's part of W) -> LDS by DMA, in 1 KiB and 256-byte pieces dealt
+    // to the waves (their areas are whole pieces). The weights need no
+    // reordering: the MFMA fragments are read from them as stored (per lane
+    // eight input channels of one output channel, w_sc bytes apart). The
+    // copies take no registers and land while the halo is staged.
+    {
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)&lds[0];
+        const int npc = (Cig * p.Cog) >> 3;       // 16-byte pieces per tap
+        const int nw = npc * p.ktot;              // ... of the group's weights
+        const int tpc = p.w_tap_pieces;           // 0: one run, else tap by tap
+        const u32x4 wrw = rsrc_words(w, (uint32_t)p.Ci * (uint32_t)p.Cog * (uint32_t)p.ktot * 2u);
+        const uint32_t w_lds = lds_base + (uint32_t)p.grp_w_off;
+        for (int j = wave; j * 64 < nw; j += 4) {  // uniform
+            const int pc = j * 64 + lane;
+            uint32_t off;
+            if (tpc == 0) {  // uniform
+                off = (uint32_t)(g * nw + pc) * 16u;
+            } else {
+                const int st = div_small(pc, tpc);
+                off = ((uint32_t)(st * p.G + g) * (uint32_t)tpc + (uint32_t)(pc - st * tpc)) * 16u;
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (e0 + tid + 256 * u < nraw) slab[tg[u] * tap_el + cc[u]] = v[u];
+            copy_to_lds<16>(w_lds + (uint32_t)j * 1024, pc < nw ? off : kOutOfRange, wrw);
         }
-        const int zc = tiles::kGrpCog - p.Cog;  // padding channels per tap
-        for (int e = tid; e < p.ktot * zc * Cig; e += 256) {
-            const int r = div_small(e, Cig), cil = e - r * Cig;
-            const int tg = div_small(r, zc), c = r - tg * zc;
-            slab[(tg * tiles::kGrpCog + p.Cog + c) * Cig + cil] = 0;
-        }
-    };
-    write_tables();
+        const unsigned char *kseg = (const unsigned char *)__builtin_amdgcn_kernarg_segment_ptr();
+        const u32x4 trw = rsrc_words(kseg + offsetof(GrpArgs, tab), (uint32_t)p.tab_n * 8u);
+        const uint32_t t_lds = lds_base + (uint32_t)p.grp_tab_off;
+        for (int j = wave; j * 64 < 2 * p.tab_n; j += 4)  // uniform
+            copy_to_lds<4>(t_lds + (uint32_t)j * 256, (uint32_t)(j * 64 + lane) * 4, trw);
+    }
     // 1b. input halo -> LDS cells; positions outside the input read an
     // out-of-range offset (zero).
     const uint32_t xpl_bytes = (uint32_t)p.x_plane * 2;
@@ -234,7 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
         const int zl = col0, zn = HWP - a2.I;
         const int zunits = nrow * noct * zn;
         for (int u = tid; u < zunits; u += 256) {
-            const int ro = u / zn, z = u - ro * zn;
+            const int ro = div_small(u, zn), z = u - ro * zn;
             const int col = z < zl ? z : z + a2.I;
             *(u32x4 *)(lds + (ro * HWP + col) * 16) = u32x4{0u, 0u, 0u, 0u};
         }
@@ -248,9 +198,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
         // unit u's source offset (out of range for rows outside the input
         // and past the last unit) and its first cell
         auto unit_at = [&](int u, unsigned char *&dst) __attribute__((always_inline)) {
-            const int row = u % nrow, t = u / nrow;
-            const int oct = t % noct, k = t / noct;
-            const int d = row / HH, h = row - d * HH;
+            const int t = div_small(u, nrow), row = u - t * nrow;
+            const int k = div_small(t, noct), oct = t - k * noct;
+            const int d = div_small(row, HH), h = row - d * HH;
             const int i0 = h0 + d, i1 = h1 + h;
             const bool ok = u < units && i0 >= 0 && i0 < a0.I && i1 >= 0 && i1 < a1.I;
             dst = lds + ((row * noct + oct) * HWP + col0 + 8 * k) * 16;
@@ -360,6 +310,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     const int l16 = lane & 15, kg4 = lane >> 4;
     const int Cog = p.Cog;
     const int O2 = a2.O;
+    // this lane's output channel in the group's weights as stored (the
+    // padding channels take the last one: their columns are never stored)
+    const unsigned char *wraw = lds + p.grp_w_off + min(l16, Cog - 1) * p.w_so;
+    const int wsc = p.w_sc;
     const int nseg = (Qw + 15) >> 4;
     // nsc == 0: width stride 2, at most 8 channels, an even segment count:
     // chunks are segment pairs that leave through DPP (no staging)
@@ -378,9 +332,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     // output planes of the group; a lane's channel plane, or out of range
     // (dropped) for the padding channels
     const uint32_t ypl_bytes = (uint32_t)p.y_plane * 2;
+    // (its address words read from lane 0: the compiler then holds the
+    // resource in scalar registers, with no per-store loop over distinct
+    // resources; each word is taken as unsigned, so the low one is not
+    // sign-extended into the high one)
+    const uint64_t ya = (uint64_t)(y + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane);
+    const uint32_t ya_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ya);
+    const uint32_t ya_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ya >> 32));
     const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(y + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane), (short)0,
-        (int)((uint32_t)Cog * ypl_bytes), kGrpRsrcWord3);
+        (void *)(((uint64_t)ya_hi << 32) | (uint64_t)ya_lo), (short)0,
+        (int)__builtin_amdgcn_readfirstlane(Cog * ypl_bytes), kGrpRsrcWord3);
     const uint32_t lane_st =
         (l16 < Cog ? (uint32_t)l16 * ypl_bytes : kGrpOutOfRange) + (uint32_t)(S2 * 4 * kg4) * 2;
     // staging: this lane's run in segment s of a chunk at st_w + s * 32 * S2
@@ -448,12 +409,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
 #pragma unroll
                 for (int kb = 0; kb < KS; ++kb) {
                     const int slot = kb * 4 + kg4;
-                    sl_ok[r2][kb] = slot < nslots;
+                    sl_ok[r2][kb] = PD || slot < nslots;
                     int2 e = make_int2(0, 0);
                     u32x4 wv = {0u, 0u, 0u, 0u};
                     if (sl_ok[r2][kb]) {
                         e = tab[sbase + slot];
-                        wv = *(const u32x4 *)&wsl[e.y + l16 * Cig];
+                        const unsigned char *wp = wraw + e.y;
+                        if (wsc == 2) {  // uniform: the eight channels are adjacent
+                            wv = *(const u32x4 *)wp;
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                wv[i] = (uint32_t)*(const uint16_t *)(wp + 2 * i * wsc) |
+                                        (uint32_t)*(const uint16_t *)(wp + (2 * i + 1) * wsc) << 16;
+                        }
                     }
                     rd[r2][kb] = (uint32_t)e.x + (uint32_t)l16 * 16;
                     bw[r2][kb] = __builtin_bit_cast(typename GrpElem<E>::v8, wv);
@@ -617,54 +586,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
                     }
                 }
             };
+            // segment pairs through DPP (width stride 2, at most 8 channels;
+            // generic, so that only the instances that call it compile it)
+            auto run_dpp = [&](auto) __attribute__((always_inline)) {
+                // segment pairs: the second segment's runs move into lanes
+                // 8..15 of each 16-lane row (the padding channels), then the
+                // lanes are permuted so that one 16-byte store writes 8
+                // channels x one whole 128-byte row, 8 lanes per row
+                int it = wave, ch = ch0;
+                uint32_t ub = (uint32_t)qb0 * row_lds + (uint32_t)(ch0 * 2) * seg_lds;
+                uint32_t so = so0 + (uint32_t)qb0 * yrow_bytes + (uint32_t)(ch0 * 2) * seg_y;
+                while (it < nitems) {  // uniform
+                    u32x4 pr[2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        f32x4 acc[MS];
+#pragma unroll
+                        for (int r2 = 0; r2 < MS; ++r2) {
+                            acc[r2] = binit;
+#pragma unroll
+                            for (int kb = 0; kb < KS; ++kb) {
+                                const u32x4 av = *(const u32x4 *)(lds + rd[r2][kb] + ub + s * 256);
+                                acc[r2] = GrpElem<E>::mfma(av, bw[r2][kb], acc[r2]);
+                            }
+                        }
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2)
+                            pr[s][e2] = pack2(acc[(2 * e2) % 2][(2 * e2) / 2],
+                                                    acc[(2 * e2 + 1) % 2][(2 * e2 + 1) / 2]);
+                    }
+                    // row_ror:8 (lane i of a row takes lane i - 8), written
+                    // to lanes 8..15 of each row only (bank mask 0b1100)
+                    u32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = __builtin_amdgcn_update_dpp((int)pr[0][e], (int)pr[1][e], 0x128, 0xf,
+                                                                  0xc, false);
+                        v[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(bp_src, m);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ys, dpp_st, so, 0);
+                    it += 4;
+                    ch += dc;
+                    ub += ub_step;
+                    so += so_step;
+                    if (ch >= nchunk) {
+                        ch -= nchunk;
+                        ub += ub_wrap;
+                        so += so_wrap;
+                    }
+                }
+            };
+            if constexpr (PD) {
+                run_dpp(0);
+                continue;
+            } else {
             if constexpr (MS == 2 && KS >= 1) {
                 if (pair_dpp && regular && (st_align & kStageOk) && nfull == nseg) {  // uniform
-                    // segment pairs: the second segment's runs move into lanes
-                    // 8..15 of each 16-lane row (the padding channels), then the
-                    // lanes are permuted so that one 16-byte store writes 8
-                    // channels x one whole 128-byte row, 8 lanes per row
-                    int it = wave, ch = ch0;
-                    uint32_t ub = (uint32_t)qb0 * row_lds + (uint32_t)(ch0 * 2) * seg_lds;
-                    uint32_t so = so0 + (uint32_t)qb0 * yrow_bytes + (uint32_t)(ch0 * 2) * seg_y;
-                    while (it < nitems) {  // uniform
-                        u32x4 pr[2];
-#pragma unroll
-                        for (int s = 0; s < 2; ++s) {
-                            f32x4 acc[MS];
-#pragma unroll
-                            for (int r2 = 0; r2 < MS; ++r2) {
-                                acc[r2] = binit;
-#pragma unroll
-                                for (int kb = 0; kb < KS; ++kb) {
-                                    const u32x4 av = *(const u32x4 *)(lds + rd[r2][kb] + ub + s * 256);
-                                    acc[r2] = GrpElem<E>::mfma(av, bw[r2][kb], acc[r2]);
-                                }
-                            }
-#pragma unroll
-                            for (int e2 = 0; e2 < 4; ++e2)
-                                pr[s][e2] = pack2(acc[(2 * e2) % 2][(2 * e2) / 2],
-                                                        acc[(2 * e2 + 1) % 2][(2 * e2 + 1) / 2]);
-                        }
-                        // row_ror:8 (lane i of a row takes lane i - 8), written
-                        // to lanes 8..15 of each row only (bank mask 0b1100)
-                        u32x4 v;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int m = __builtin_amdgcn_update_dpp((int)pr[0][e], (int)pr[1][e], 0x128, 0xf,
-                                                                      0xc, false);
-                            v[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(bp_src, m);
-                        }
-                        __builtin_amdgcn_raw_buffer_store_b128(v, ys, dpp_st, so, 0);
-                        it += 4;
-                        ch += dc;
-                        ub += ub_step;
-                        so += so_step;
-                        if (ch >= nchunk) {
-                            ch -= nchunk;
-                            ub += ub_wrap;
-                            so += so_wrap;
-                        }
-                    }
+                    run_dpp(0);
                     continue;
                 }
             }
@@ -678,6 +656,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
                 run_items(BoolTag<false>{});
             else
                 run_items(BoolTag<true>{});
+            }
         }
     }
     };
@@ -695,16 +674,17 @@ static GrpArgs grp_args(const Plan &pl) {
     a.grp_w_off = p.grp_w_off; a.grp_tab_off = p.grp_tab_off; a.grp_st_off = p.grp_st_off;
     a.grp_st_pitch = p.grp_st_pitch;
     a.ktot = p.ktot; a.nphase = p.nphase;
-    a.w_layout = p.w_layout;
     a.tab_n = pl.gt.tab_n;
-    memcpy(a.tg_of, pl.gt.tg_of, sizeof(a.tg_of));
+    a.w_sc = pl.gt.w_sc;
+    a.w_so = pl.gt.w_so;
+    a.w_tap_pieces = pl.gt.w_tap_pieces;
     memcpy(a.tab, pl.gt.tab, sizeof(a.tab));
     return a;
 }
 
 template <int S2, int KS, typename E>
 static void launch_grouped_e(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
-                             int st_align, int x_vec, hipStream_t stream) {
+                             int st_align, int x_vec, bool pd, hipStream_t stream) {
     const DevParams &p = pl.dp;
     const dim3 grid(p.G * p.B, p.nt_h, p.nt_d);
     const size_t lds = (size_t)p.grp_lds_bytes;
@@ -715,9 +695,18 @@ static void launch_grouped_e(const Plan &pl, const void *x, const void *w, const
     // one instance per activation: the activation folds into the unrolled
     // store loop (a run-time switch there splits it into branches the
     // compiler cannot schedule across, which cost even ReLU 70%)
-#define CONVT_GRP_LAUNCH(A)                                                                      \
-    hipLaunchKernelGGL((grouped_kernel<S2, KS, E, A>), grid, dim3(256), lds, stream, a, xs, ws, bs, \
-                       ys, st_align, x_vec)
+#define CONVT_GRP_LAUNCH(A)                                                                           \
+    do {                                                                                              \
+        if constexpr (S2 == 2) {                                                                      \
+            if (pd) {                                                                                 \
+                hipLaunchKernelGGL((grouped_kernel<S2, KS, E, A, true>), grid, dim3(256), lds, stream, a, \
+                                   xs, ws, bs, ys, st_align, x_vec);                                  \
+                break;                                                                                \
+            }                                                                                         \
+        }                                                                                             \
+        hipLaunchKernelGGL((grouped_kernel<S2, KS, E, A, false>), grid, dim3(256), lds, stream, a, xs, \
+                           ws, bs, ys, st_align, x_vec);                                              \
+    } while (0)
     switch (p.act) {
         case CONVT_ACT_RELU: CONVT_GRP_LAUNCH(CONVT_ACT_RELU); break;
         case CONVT_ACT_SIGMOID: CONVT_GRP_LAUNCH(CONVT_ACT_SIGMOID); break;
@@ -731,20 +720,20 @@ static void launch_grouped_e(const Plan &pl, const void *x, const void *w, const
 
 template <int S2, int KS>
 static void launch_grouped_t(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
-                             int st_align, int x_vec, hipStream_t stream) {
+                             int st_align, int x_vec, bool pd, hipStream_t stream) {
     if (pl.dp.f16)
-        launch_grouped_e<S2, KS, _Float16>(pl, x, w, bias, y, st_align, x_vec, stream);
+        launch_grouped_e<S2, KS, _Float16>(pl, x, w, bias, y, st_align, x_vec, pd, stream);
     else
-        launch_grouped_e<S2, KS, __bf16>(pl, x, w, bias, y, st_align, x_vec, stream);
+        launch_grouped_e<S2, KS, __bf16>(pl, x, w, bias, y, st_align, x_vec, pd, stream);
 }
 
 template <int S2>
 static hipError_t launch_grouped_s(const Plan &pl, const void *x, const void *w, const void *bias, void *y,
-                                   int st_align, int x_vec, hipStream_t stream) {
+                                   int st_align, int x_vec, bool pd, hipStream_t stream) {
     switch (pl.dp.grp_ksteps) {
-        case 1: launch_grouped_t<S2, 1>(pl, x, w, bias, y, st_align, x_vec, stream); break;
-        case 2: launch_grouped_t<S2, 2>(pl, x, w, bias, y, st_align, x_vec, stream); break;
-        case 4: launch_grouped_t<S2, 4>(pl, x, w, bias, y, st_align, x_vec, stream); break;
+        case 1: launch_grouped_t<S2, 1>(pl, x, w, bias, y, st_align, x_vec, pd, stream); break;
+        case 2: launch_grouped_t<S2, 2>(pl, x, w, bias, y, st_align, x_vec, pd, stream); break;
+        case 4: launch_grouped_t<S2, 4>(pl, x, w, bias, y, st_align, x_vec, pd, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipSuccess;
@@ -772,12 +761,19 @@ hipError_t launch_grouped(const Plan &pl, const void *x, const void *w, const vo
     const int x_vec = (uintptr_t)x % 16 == 0 && p.grp_nk > 0;
     if ((int64_t)p.G * p.B > 0x7fffffff || p.nt_h > 65535 || p.nt_d > 65535)
         return hipErrorInvalidConfiguration;
+    // every item takes the segment-pair path (each phase's slots fill its K
+    // steps and its q width covers every segment): the instance without the
+    // other paths
+    bool pd = S2 == 2 && p.grp_nsc == 0 && (st_align & kStageOk);
+    const int nseg = (p.tw + 15) >> 4;
+    for (int P = 0; pd && P < p.nphase; ++P)
+        pd = (pl.gt.tab[4 * P + 3] >> 16) == 4 * p.grp_ksteps && (pl.gt.tab[4 * P + 2] >> 4) >= nseg;
     hipError_t e;
     switch (S2) {
-        case 1: e = launch_grouped_s<1>(pl, x, w, bias, y, st_align, x_vec, stream); break;
-        case 2: e = launch_grouped_s<2>(pl, x, w, bias, y, st_align, x_vec, stream); break;
-        case 3: e = launch_grouped_s<3>(pl, x, w, bias, y, st_align, x_vec, stream); break;
-        case 4: e = launch_grouped_s<4>(pl, x, w, bias, y, st_align, x_vec, stream); break;
+        case 1: e = launch_grouped_s<1>(pl, x, w, bias, y, st_align, x_vec, pd, stream); break;
+        case 2: e = launch_grouped_s<2>(pl, x, w, bias, y, st_align, x_vec, pd, stream); break;
+        case 3: e = launch_grouped_s<3>(pl, x, w, bias, y, st_align, x_vec, pd, stream); break;
+        case 4: e = launch_grouped_s<4>(pl, x, w, bias, y, st_align, x_vec, pd, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -581,9 +581,9 @@ bool choose_grouped_tile(DevParams *dp) {
     const int64_t st_bytes =
         pair_dpp ? 0 : (int64_t)tiles::kGrpThreads / 64 * (dp->Cog + 1) * st_pitch;
     auto al = [](int64_t v) { return (v + 15) / 16 * 16; };
-    // the weights and the slot table reach LDS by DMA in 1 KiB and 256-byte
-    // pieces: their areas are whole pieces
-    const int64_t w_bytes = ((int64_t)dp->ktot * tiles::kGrpCog * dp->Cig * 2 + 1023) / 1024 * 1024;
+    // the group's weights (as W stores them) and the slot table reach LDS by
+    // DMA in 1 KiB and 256-byte pieces: their areas are whole pieces
+    const int64_t w_bytes = ((int64_t)dp->ktot * dp->Cog * dp->Cig * 2 + 1023) / 1024 * 1024;
     // slot table: a 16-byte record per phase, then (halo offset, weight
     // offset) per (tap, 8-channel slice)
     const int64_t tab_bytes =
@@ -626,15 +626,29 @@ bool choose_grouped_tile(DevParams *dp) {
     return true;
 }
 
-// The grouped kernel's tables (GrpTables): a record per phase, the (tap,
-// slice) slots of each phase in its taps' order, and the plan-order tap of
-// every stored tap of W (flipped where W's taps are stored reversed).
+// The grouped kernel's tables (GrpTables): a record per phase and the (tap,
+// slice) slots of each phase in its taps' order, each naming the tap's halo
+// window and its weights in the group's part of W as stored (the stored tap
+// is the spatially reversed one where W's taps are stored flipped).
 bool grouped_tables(Plan *pl) {
     const DevParams &p = pl->dp;
     GrpTables &gt = pl->gt;
     const int noct = p.Cig >> 3;
     if (p.nphase > kMaxPhaseTab || p.ktot > kGrpMaxTaps || 2 * p.nphase + p.ktot * noct > kGrpTabMax)
         return false;
+    // element strides of the group's weights: stored tap, input channel,
+    // output channel
+    int64_t ss, sc, so;
+    if (p.w_layout == CONVT_FILTER_K_CI_CO) {  // [k][C_in][Cog]: per tap a [Cig][Cog] run
+        ss = (int64_t)p.Cig * p.Cog, sc = p.Cog, so = 1;
+    } else if (p.w_layout == CONVT_FILTER_K_CO_CI) {  // [k][C_out][Cig]: per tap a [Cog][Cig] run
+        ss = (int64_t)p.Cig * p.Cog, sc = 1, so = p.Cig;
+    } else {  // [C_in][Cog][k]: one [Cig][Cog][k] run
+        ss = 1, sc = (int64_t)p.Cog * p.ktot, so = p.ktot;
+    }
+    gt.w_sc = (int32_t)(2 * sc);
+    gt.w_so = (int32_t)(2 * so);
+    gt.w_tap_pieces = p.w_layout == CONVT_FILTER_CI_CO_K ? 0 : p.Cig * p.Cog / 8;
     const DevAxis &a0 = p.ax[0], &a1 = p.ax[1], &a2 = p.ax[2];
     gt.tab_n = 2 * p.nphase + p.ktot * noct;
     int32_t *slots = gt.tab + 4 * p.nphase;
@@ -657,17 +671,14 @@ bool grouped_tables(Plan *pl) {
             const int j2 = tap % n[2], j1 = (tap / n[2]) % n[1], j0 = tap / (n[2] * n[1]);
             const int hrow = (off0[0] - a0.umin + j0 * a0.ostep) * p.hh + (off0[1] - a1.umin + j1 * a1.ostep);
             const int col = off0[2] - a2.umin + j2 * a2.ostep + p.grp_hshift;
-            int32_t *e = slots + 2 * (rec.tapbase * noct + sl);
-            e[0] = ((hrow * noct + oct) * p.grp_hwp + col) * 16;
-            e[1] = (rec.tapbase + tap) * tiles::kGrpCog * p.Cig + oct * 8;
-        }
-        for (int t = 0; t < rec.ntaps; ++t) {
-            const int j2 = t % n[2], j1 = (t / n[2]) % n[1], j0 = t / (n[2] * n[1]);
+            // the tap's kernel indices, then its index as W stores it
             const int k0 = a0.kk0[r[0]] - j0 * a0.kstep, k1 = a1.kk0[r[1]] - j1 * a1.kstep,
                       k2 = a2.kk0[r[2]] - j2 * a2.kstep;
             const int st = p.w_flip ? ((a0.K - 1 - k0) * a1.K + (a1.K - 1 - k1)) * a2.K + (a2.K - 1 - k2)
                                     : (k0 * a1.K + k1) * a2.K + k2;
-            gt.tg_of[st] = (uint8_t)(rec.tapbase + t);
+            int32_t *e = slots + 2 * (rec.tapbase * noct + sl);
+            e[0] = ((hrow * noct + oct) * p.grp_hwp + col) * 16;
+            e[1] = (int32_t)(2 * (st * ss + 8 * oct * sc));
         }
     }
     return true;

@@ -151,8 +151,8 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
         }
     }
     // the (batch, group) slice of x: channels past Cig read zero
-    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x + ((int64_t)b * p.Ci + (int64_t)g * p.Cig) * p.x_plane,
-                                                 (uint32_t)p.Cig * plane2);
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc_uniform(
+        x + ((int64_t)b * p.Ci + (int64_t)g * p.Cig) * p.x_plane, (uint32_t)p.Cig * plane2);
 
     // ---- weight tiles: stage c (chunk c) holds, for the phase's taps
     // t < GS, the tile Wr[g][tapbase + t][c][co0 .. co0 + BM)[32 bytes];
@@ -371,8 +371,8 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
     const int co_left = p.Cog - co_w;
     if (co_left <= 0) return;
     const uint32_t ypl_bytes = (uint32_t)p.y_plane * 2u;
-    const __amdgpu_buffer_rsrc_t ys =
-        make_rsrc(y + ((int64_t)b * p.Co + (int64_t)g * p.Cog + co_w) * p.y_plane, (uint32_t)co_left * ypl_bytes);
+    const __amdgpu_buffer_rsrc_t ys = make_rsrc_uniform(
+        y + ((int64_t)b * p.Co + (int64_t)g * p.Cog + co_w) * p.y_plane, (uint32_t)co_left * ypl_bytes);
     const uint32_t lane_co = 4u * (uint32_t)(lane >> 5);
     // The lane's position (and its half's 4-row channel step) in the vector
     // offset, the fragment row in the scalar one: the range check covers

@@ -332,16 +332,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     // output planes of the group; a lane's channel plane, or out of range
     // (dropped) for the padding channels
     const uint32_t ypl_bytes = (uint32_t)p.y_plane * 2;
-    // (its address words read from lane 0: the compiler then holds the
-    // resource in scalar registers, with no per-store loop over distinct
-    // resources; each word is taken as unsigned, so the low one is not
-    // sign-extended into the high one)
-    const uint64_t ya = (uint64_t)(y + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane);
-    const uint32_t ya_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ya);
-    const uint32_t ya_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ya >> 32));
-    const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(((uint64_t)ya_hi << 32) | (uint64_t)ya_lo), (short)0,
-        (int)__builtin_amdgcn_readfirstlane(Cog * ypl_bytes), kGrpRsrcWord3);
+    // (built from lane 0's words: kept in scalar registers, no per-store
+    // loop over the lanes' resources)
+    const __amdgpu_buffer_rsrc_t ys = make_rsrc_uniform(
+        y + ((int64_t)b * p.Co + (int64_t)g * Cog) * p.y_plane, Cog * ypl_bytes, kGrpRsrcWord3);
     const uint32_t lane_st =
         (l16 < Cog ? (uint32_t)l16 * ypl_bytes : kGrpOutOfRange) + (uint32_t)(S2 * 4 * kg4) * 2;
     // staging: this lane's run in segment s of a chunk at st_w + s * 32 * S2

@@ -222,6 +222,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              (int)kRsrcWord3);
 }
 
+// A resource whose base and size are the same in every lane, built from
+// lane 0's words so that the compiler holds it in scalar registers (else a
+// resource it cannot prove uniform is kept in vector registers and each
+// access loops over the lanes' resources). The words are taken unsigned: a
+// signed low word would be sign-extended into the high one.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void *base, uint32_t bytes,
+                                                                    int word3 = (int)kRsrcWord3) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | (uint64_t)lo), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), word3);
+}
+
 // The same resource as four scalar words, for the copy instructions below.
 __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
     const uint64_t a = (uint64_t)base;

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libconvt.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["plan.cpp", "api.cpp", "k_misc.hip", "k_phase_gemm.hip", "k_gemm_nchw.hip", "k_gemm_allphase.hip",
-           "k_bwd_allphase.hip", "k_grouped.hip", "noalloc.hip"]
+           "k_bwd_allphase.hip", "k_bwd_grouped.hip", "k_grouped.hip", "noalloc.hip"]
 
 # Packed-FP32 instructions are kept out of every kernel (the target feature is
 # switched off for the device pass; the host pass ignores it with a warning).

@@ -165,6 +165,12 @@ convt_status convt_backward_data(convt_plan_t plan, const void *dy, const void *
             return device_status(convt::launch_naive_bwd(pl, dy, w, dx, s));
         case CONVT_ROUTE_DIRECT:
             return device_status(convt::launch_direct_bwd(pl, dy, w, dx, s));
+        case CONVT_ROUTE_GROUPED:
+            // dy read in 16-byte pieces, W copied in 16-byte pieces; otherwise
+            // the direct kernel (eligible for every plan of this route)
+            if ((uintptr_t)dy % 16 != 0 || (uintptr_t)w % 16 != 0)
+                return device_status(convt::launch_direct_bwd(pl, dy, w, dx, s));
+            return device_status(convt::launch_grouped_bwd(pl, dy, w, dx, s));
         case CONVT_ROUTE_PHASE_GEMM_ALLPHASE:
             // dy read in 4-byte pairs, W in 16-byte pieces, dx stored in 16-byte pieces
             if ((uintptr_t)dy % 4 != 0 || (uintptr_t)w % 16 != 0 || (uintptr_t)dx % 16 != 0)

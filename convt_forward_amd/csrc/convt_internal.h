@@ -141,6 +141,31 @@ struct AllPhaseArgs {
 // dy, depth tap) stages of all 16 height x width taps.
 constexpr int kBwdPlaneRows = 383;    // halo rows per phase plane, at most (one more row absorbs idle units)
 constexpr int kBwdPlaneRowsKS = 255;  // ... with the K split (a 128-position box)
+// route_bwd GROUPED (k_bwd_grouped.hip): the input gradient of a 2-D grouped
+// problem with few channels, as a strided correlation of dy on MFMA. A block
+// owns one (batch, group) and R dx rows over the full dx width; dy's halo for
+// those rows goes to LDS as 16-byte cells of 8 dy channels
+// [halo row][slice][column].
+constexpr int kGbMaxSlots = 16;     // (tap, 8-channel dy slice) slots: four MFMA K steps
+constexpr int kGbLdsBudget = 24576;  // LDS per block (halo + weights)
+struct GrpBwdArgs {
+    int32_t G, Ci, Co, Cig, Cog, noct;  // the forward problem's channels; noct = Cog / 8
+    int32_t I1, I2, O1, O2;             // dx and dy extents (height, width)
+    int32_t S1, S2, P1, P2, D1, D2;     // stride, low padding, dilation
+    int32_t K1, K2, ktot, nslots, ks;   // taps; slots = ktot * noct; K steps
+    int32_t R, nt_h;                    // dx rows per block, row tiles
+    int32_t hr, hwp;                    // halo rows, halo row pitch (cells, odd)
+    int32_t x_plane, y_plane;           // dx and dy plane elements
+    int32_t w_off, lds_bytes;           // LDS: halo from 0, W from w_off
+    int32_t w_sci, w_sco, w_tap_pieces; // W as stored: bytes between input / output
+                                        // channels of a group; 16-byte pieces per tap
+                                        // when taps are outermost, else 0
+    int32_t slot_w[kGbMaxSlots];        // per slot: byte offset of its stored tap and
+                                        // slice's first output channel in the group's W
+    int32_t slot_h[kGbMaxSlots];        // per slot: halo byte offset of the tap for dx
+                                        // row 0, position 0
+};
+
 struct BwdAPArgs {
     int32_t Ci, Co, Cig, Cog, G;  // the forward problem's channels: dx has Ci (groups of Cig), dy Co
     int32_t I[3], O[3], K[3];     // dx extents, dy extents, taps
@@ -209,6 +234,7 @@ struct Plan {
     int64_t bwd_xp_offset;   // bfloat16: byte offset of the channel-chunked copy of dy
     int64_t bwd_xp_bytes;    // its size (0 when not used)
     BwdAPArgs bap;           // route_bwd PHASE_GEMM_ALLPHASE: the kernel's arguments
+    GrpBwdArgs gb;           // route_bwd GROUPED: the kernel's arguments
 };
 
 // Tile constants of the kernels, shared with the planner so that it sizes

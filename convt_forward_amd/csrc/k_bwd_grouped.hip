@@ -1,0 +1,247 @@
+// Input gradient of a 2-D grouped transposed convolution with few channels
+// per group (bfloat16 or half, MFMA 16x16x32).
+//
+// The adjoint of the forward scatter-add gathers, per input position i and
+// input channel ci of group g,
+//   dx[ci][i] = sum over (co < C_out/g, tap k) of W[ci][co][k] * dy[co][s*i - p + d*k]
+// (the input adjoint that the SKaiNET convTranspose2d pull request's Summary
+// lists beside the forward; its index map is the forward's scatter index read
+// backwards). That is a strided correlation of dy,
+// a dense contraction over K = (tap, output channel) for each dx position,
+// so it runs on MFMA: rows = 16 dx positions along the width, columns = the
+// group's input channels (at most 16), K = (tap, 8-channel slice of dy)
+// slots, four per MFMA step, up to four steps.
+//
+// A block owns one (batch, group) and R dx rows over the full dx width:
+//  1. the group's part of W, as W stores it, goes to LDS by LDS-destination
+//     buffer loads (no registers, no arithmetic per element); the MFMA weight
+//     fragments are read from that layout with its channel strides, once per
+//     wave;
+//  2. dy's halo for the R rows (every tap's rows, the full dy width) goes to
+//     LDS as 16-byte cells of 8 dy channels, [halo row][slice][column]: a
+//     lane loads 8 positions of each of 8 channels (eight 16-byte loads) and
+//     transposes the 8 x 8 block in registers; columns outside dy hold zeros;
+//  3. each wave takes items (dx row, 16-position segment): one A fragment
+//     read per K step (lane = dx position, its cell s positions apart from
+//     the next lane's), the MFMAs, one rounding, and 8-byte stores of 4
+//     consecutive dx values per lane (2-byte stores at ragged or unaligned
+//     rows).
+#include <cstddef>
+#include <cstring>
+
+#include "kcommon.h"
+#include "launch.h"
+
+namespace convt {
+
+constexpr uint32_t kGbPermLo = 0x05040100u;  // {second.lo, first.lo}
+constexpr uint32_t kGbPermHi = 0x07060302u;  // {second.hi, first.hi}
+
+template <typename E> struct GbElem;
+template <> struct GbElem<__bf16> {
+    static __device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+};
+template <> struct GbElem<_Float16> {
+    static __device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                      c, 0, 0, 0);
+    }
+};
+
+// KS: MFMA K steps (slots / 4, rounded up); ST8: dx rows are whole 8-byte
+// pieces from an 8-byte aligned dx (4 values per lane in one store).
+template <typename E, int KS, bool ST8>
+__global__ __launch_bounds__(256) void grouped_bwd_kernel(GrpBwdArgs a, const uint16_t *__restrict__ dy,
+                                                          const uint16_t *__restrict__ w,
+                                                          uint16_t *__restrict__ dx) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = blockIdx.x / a.G, g = blockIdx.x - b * a.G;
+    const int i1_0 = blockIdx.y * a.R;  // the block's first dx row
+    const int Cig = a.Cig, Cog = a.Cog, noct = a.noct, HWP = a.hwp;
+    const unsigned char *kseg = (const unsigned char *)__builtin_amdgcn_kernarg_segment_ptr();
+
+    // 1. the group's W, as stored, -> LDS at w_off (1 KiB pieces per wave
+    // instruction; the area is whole pieces)
+    {
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)&lds[0];
+        const int nw = (Cig * Cog * a.ktot) >> 3;  // 16-byte pieces
+        const int tpc = a.w_tap_pieces;
+        const u32x4 wrw = rsrc_words(w, (uint32_t)a.Ci * (uint32_t)Cog * (uint32_t)a.ktot * 2u);
+        for (int j = wave; j * 64 < nw; j += 4) {  // uniform
+            const int pc = j * 64 + lane;
+            uint32_t off;
+            if (tpc == 0) {  // uniform: one run of the group's elements
+                off = (uint32_t)(g * nw + pc) * 16u;
+            } else {  // tap by tap: each tap's run of the group
+                const int st = div_small(pc, tpc);
+                off = ((uint32_t)(st * a.G + g) * (uint32_t)tpc + (uint32_t)(pc - st * tpc)) * 16u;
+            }
+            copy_to_lds<16>(lds_base + (uint32_t)a.w_off + (uint32_t)j * 1024, pc < nw ? off : kOutOfRange, wrw);
+        }
+    }
+
+    // 2. dy's halo: halo row hr is dy row S1 * i1_0 - P1 + hr, cell column hc
+    // is dy column hc - P2
+    const uint32_t ypl_bytes = (uint32_t)a.y_plane * 2u;
+    const __amdgpu_buffer_rsrc_t ys =
+        make_rsrc_uniform(dy + ((int64_t)b * a.Co + (int64_t)g * Cog) * a.y_plane, (uint32_t)Cog * ypl_bytes);
+    const int oh0 = a.S1 * i1_0 - a.P1;
+    const int nrs = a.hr * noct;  // (halo row, slice) pairs
+    {
+        // zero cells: columns left of dy (P2 of them) and right of it
+        const int zn = HWP - a.O2, zunits = nrs * zn;
+        for (int u = tid; u < zunits; u += 256) {
+            const int rs = div_small(u, zn), z = u - rs * zn;
+            const int col = z < a.P2 ? z : z + a.O2;
+            *(u32x4 *)(lds + (rs * HWP + col) * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    {
+        // unit = (halo row, slice, chunk k of 8 dy positions 8k .. 8k+7):
+        // cells P2 + 8k .. +7 of the row; rows outside dy read zero. Chunks
+        // are fastest, so 8 neighbouring lanes read a row's 128 contiguous
+        // bytes of one channel per load.
+        const int nk = a.O2 >> 3, units = nrs * nk;
+        for (int u = tid; u < units; u += 256) {
+            const int rs = div_small(u, nk), k = u - rs * nk;
+            const int hr = div_small(rs, noct), oct = rs - hr * noct;
+            const int oh = oh0 + hr;
+            const uint32_t off = (oh >= 0 && oh < a.O1)
+                                     ? (uint32_t)(oct * 8) * ypl_bytes + (uint32_t)(oh * a.O2 + 8 * k) * 2u
+                                     : kOutOfRange;
+            u32x4 v[8];  // v[c]: positions 8k .. 8k+7 of channel 8 oct + c
+#pragma unroll
+            for (int c = 0; c < 8; ++c) v[c] = __builtin_amdgcn_raw_buffer_load_b128(ys, off + c * ypl_bytes, 0, 0);
+            unsigned char *dst = lds + (rs * HWP + a.P2 + 8 * k) * 16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                u32x4 cell;  // position 8k + e, channels 2i, 2i+1 in word i
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    cell[i] = __builtin_amdgcn_perm(v[2 * i + 1][e >> 1], v[2 * i][e >> 1],
+                                                    (e & 1) ? kGbPermHi : kGbPermLo);
+                *(u32x4 *)(dst + e * 16) = cell;
+            }
+        }
+    }
+    // every copy (weights, halo) has landed and the cells are written
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // 3. this lane's K slots: slot = 4 kb + kg4; its weight fragment (8 dy
+    // channels of input channel l16; channels past Cig take the last one,
+    // their columns are never stored; slots past nslots are zero) and the
+    // halo byte offset of its tap for dx row 0, position 0
+    const int l16 = lane & 15, kg4 = lane >> 4;
+    const int32_t *slot_w = (const int32_t *)(kseg + offsetof(GrpBwdArgs, slot_w));
+    const int32_t *slot_h = (const int32_t *)(kseg + offsetof(GrpBwdArgs, slot_h));
+    const unsigned char *wl = lds + a.w_off + min(l16, Cig - 1) * a.w_sci;
+    const int wsco = a.w_sco;
+    u32x4 bw[KS];
+    uint32_t aoff[KS];
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) {
+        const int slot = 4 * kb + kg4;
+        const bool ok = slot < a.nslots;
+        u32x4 wv = {0u, 0u, 0u, 0u};
+        if (ok) {
+            const unsigned char *wp = wl + slot_w[slot];
+            if (wsco == 2) {  // uniform: the 8 dy channels are adjacent
+                wv = *(const u32x4 *)wp;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    wv[i] = (uint32_t)*(const uint16_t *)(wp + 2 * i * wsco) |
+                            (uint32_t)*(const uint16_t *)(wp + (2 * i + 1) * wsco) << 16;
+            }
+        }
+        bw[kb] = wv;
+        aoff[kb] = (uint32_t)slot_h[ok ? slot : 0];
+    }
+
+    // items (dx row r, segment sg) dealt to the waves in turn
+    const int rows = min(a.R, a.I1 - i1_0), nseg = (a.I2 + 15) >> 4;
+    const uint32_t xpl_bytes = (uint32_t)a.x_plane * 2u;
+    const __amdgpu_buffer_rsrc_t xs =
+        make_rsrc_uniform(dx + ((int64_t)b * a.Ci + (int64_t)g * Cig) * a.x_plane, (uint32_t)Cig * xpl_bytes);
+    const uint32_t lane_x = l16 < Cig ? (uint32_t)l16 * xpl_bytes : kOutOfRange;
+    const uint32_t row_lds = (uint32_t)(a.S1 * noct * HWP * 16);  // halo bytes per dx row
+    int r = 0, sg = wave;
+    while (sg >= nseg) {  // uniform
+        sg -= nseg;
+        ++r;
+    }
+    for (; r < rows;) {  // uniform
+        // this lane's dx position (clamped into the row for the read)
+        const int i2 = sg * 16 + l16;
+        const uint32_t abase = (uint32_t)r * row_lds + (uint32_t)(a.S2 * min(i2, a.I2 - 1) * 16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KS; ++kb) {
+            const u32x4 av = *(const u32x4 *)(lds + abase + aoff[kb]);
+            acc = GbElem<E>::mfma(av, bw[kb], acc);
+        }
+        // lane: input channel l16, dx positions sg*16 + 4 kg4 + j
+        const int p0 = sg * 16 + 4 * kg4;
+        const uint32_t rowoff = (uint32_t)((i1_0 + r) * a.I2 + p0) * 2u;
+        const uint32_t w0 = pack_half2<E>(acc[0], acc[1]), w1 = pack_half2<E>(acc[2], acc[3]);
+        if (ST8 && p0 < a.I2) {
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, xs, lane_x + rowoff, 0, 0);
+        } else if (!ST8) {
+            const uint32_t wv[2] = {w0, w1};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (p0 + j < a.I2)
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(wv[j >> 1] >> (16 * (j & 1))), xs,
+                                                          lane_x + rowoff + 2u * j, 0, 0);
+        }
+        sg += 4;
+        while (sg >= nseg) {  // uniform
+            sg -= nseg;
+            ++r;
+        }
+    }
+}
+
+template <typename E, int KS>
+static void launch_gb_e(const Plan &pl, const void *dy, const void *w, void *dx, bool st8, hipStream_t stream) {
+    const GrpBwdArgs &a = pl.gb;
+    const dim3 grid(a.G * pl.bdp.B, a.nt_h);
+    const uint16_t *d = (const uint16_t *)dy, *ww = (const uint16_t *)w;
+    uint16_t *o = (uint16_t *)dx;
+    if (st8)
+        hipLaunchKernelGGL((grouped_bwd_kernel<E, KS, true>), grid, dim3(256), (size_t)a.lds_bytes, stream, a, d, ww, o);
+    else
+        hipLaunchKernelGGL((grouped_bwd_kernel<E, KS, false>), grid, dim3(256), (size_t)a.lds_bytes, stream, a, d, ww,
+                           o);
+}
+
+template <typename E>
+static hipError_t launch_gb_t(const Plan &pl, const void *dy, const void *w, void *dx, bool st8, hipStream_t stream) {
+    switch (pl.gb.ks) {
+        case 1: launch_gb_e<E, 1>(pl, dy, w, dx, st8, stream); break;
+        case 2: launch_gb_e<E, 2>(pl, dy, w, dx, st8, stream); break;
+        case 3: launch_gb_e<E, 3>(pl, dy, w, dx, st8, stream); break;
+        case 4: launch_gb_e<E, 4>(pl, dy, w, dx, st8, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_grouped_bwd(const Plan &pl, const void *dy, const void *w, void *dx, hipStream_t stream) {
+    const GrpBwdArgs &a = pl.gb;
+    if (pl.bdp.B == 0 || a.nt_h == 0) return hipSuccess;
+    if ((int64_t)a.G * pl.bdp.B > 0x7fffffff || a.nt_h > 65535) return hipErrorInvalidConfiguration;
+    // 8-byte stores: dx rows of whole 8-byte pieces from an 8-byte aligned dx
+    const bool st8 = a.I2 % 4 == 0 && (uintptr_t)dx % 8 == 0;
+    const hipError_t e = pl.dp.f16 ? launch_gb_t<_Float16>(pl, dy, w, dx, st8, stream)
+                                   : launch_gb_t<__bf16>(pl, dy, w, dx, st8, stream);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+}  // namespace convt

@@ -43,6 +43,7 @@ hipError_t launch_phase_gemm_bwd(const Plan &pl, const void *dy, const void *wr,
                                  hipStream_t stream);
 // backward all-phase GEMM (route_bwd PHASE_GEMM_ALLPHASE): dy and W as the
 // caller stores them, no workspace
+hipError_t launch_grouped_bwd(const Plan &pl, const void *dy, const void *w, void *dx, hipStream_t stream);
 hipError_t launch_allphase_bwd(const Plan &pl, const void *dy, const void *w, void *dx,
                                hipStream_t stream);
 

@@ -720,6 +720,76 @@ bool direct_bwd_eligible(const DevParams &fp, int elem_bytes) {
            (int64_t)fp.Cog * fp.y_plane * elem_bytes < ((int64_t)1 << 31) && fp.x_plane > 0;
 }
 
+// Plan the grouped backward kernel (k_bwd_grouped.hip) for the input
+// gradient of a two-byte 2-D problem (fp: the forward problem), or return
+// false if it does not apply: output channels per group a multiple of 8 with
+// at most 16 (tap, 8-channel slice) slots, at most 16 input channels per
+// group, dy rows of whole 16-byte chunks, 32-bit buffer offsets, and the
+// direct backward kernel eligible too (it serves calls whose dy or dx is not
+// aligned for this one). A block takes R dx rows (a power of two up to 16,
+// about 256 dx positions) whose dy halo and weights fit the LDS budget.
+bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
+    const DevParams &fp = pl->dp;
+    if (dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16) return false;
+    if (ndim != 2) return false;
+    const DevAxis &a1 = fp.ax[1], &a2 = fp.ax[2];
+    if (fp.Cog < 8 || fp.Cog % 8 != 0 || fp.Cig < 1 || fp.Cig > 16) return false;
+    const int64_t noct = fp.Cog / 8, ktot = (int64_t)a1.K * a2.K;
+    if (ktot != fp.ktot || ktot * noct > kGbMaxSlots) return false;
+    if (a2.O % 8 != 0 || a1.O < 1 || a1.I < 1 || a2.I < 1) return false;
+    if (!direct_bwd_eligible(fp, 2)) return false;
+    if (!buffer_fits((int64_t)fp.Cog * fp.y_plane * 2) || !buffer_fits((int64_t)fp.Cig * fp.x_plane * 2) ||
+        !buffer_fits((int64_t)fp.Ci * fp.Cog * fp.ktot * 2))
+        return false;
+    // halo row pitch (cells, odd): every column a dx row's taps read and all
+    // of dy's row (staged as whole chunks) after the P2 zero columns
+    const int64_t hwp =
+        std::max<int64_t>((int64_t)a2.S * (a2.I - 1) + (int64_t)a2.D * (a2.K - 1) + 1, (int64_t)a2.P + a2.O) | 1;
+    const int64_t w_bytes = ((int64_t)fp.Cig * fp.Cog * ktot * 2 + 1023) / 1024 * 1024;
+    auto halo_rows = [&](int64_t r) { return (int64_t)a1.S * (r - 1) + (int64_t)a1.D * (a1.K - 1) + 1; };
+    auto halo_bytes = [&](int64_t r) { return halo_rows(r) * noct * hwp * 16; };
+    int64_t R = 1;
+    while (R < 16 && 2 * R * a2.I <= 256 && 2 * R <= a1.I) R *= 2;
+    while (R > 1 && halo_bytes(R) + w_bytes > kGbLdsBudget) R /= 2;
+    if (halo_bytes(R) + w_bytes > kGbLdsBudget) return false;
+    const int64_t nt_h = ceil_div(a1.I, R);
+    if (nt_h > 65535 || (int64_t)fp.G * fp.B > 0x7fffffff) return false;
+    GrpBwdArgs &g = pl->gb;
+    memset(&g, 0, sizeof(g));
+    g.G = fp.G; g.Ci = fp.Ci; g.Co = fp.Co; g.Cig = fp.Cig; g.Cog = fp.Cog; g.noct = (int32_t)noct;
+    g.I1 = a1.I; g.I2 = a2.I; g.O1 = a1.O; g.O2 = a2.O;
+    g.S1 = a1.S; g.S2 = a2.S; g.P1 = a1.P; g.P2 = a2.P; g.D1 = a1.D; g.D2 = a2.D;
+    g.K1 = a1.K; g.K2 = a2.K; g.ktot = (int32_t)ktot;
+    g.nslots = (int32_t)(ktot * noct);
+    g.ks = (g.nslots + 3) / 4;
+    g.R = (int32_t)R; g.nt_h = (int32_t)nt_h;
+    g.hr = (int32_t)halo_rows(R); g.hwp = (int32_t)hwp;
+    g.x_plane = fp.x_plane; g.y_plane = fp.y_plane;
+    g.w_off = (int32_t)halo_bytes(R);
+    g.lds_bytes = (int32_t)(halo_bytes(R) + w_bytes);
+    // element strides of the group's weights: stored tap, input channel,
+    // output channel
+    int64_t ss, sci, sco;
+    if (fp.w_layout == CONVT_FILTER_K_CI_CO) {  // [k][C_in][Cog]: per tap a [Cig][Cog] run
+        ss = (int64_t)fp.Cig * fp.Cog, sci = fp.Cog, sco = 1;
+    } else if (fp.w_layout == CONVT_FILTER_K_CO_CI) {  // [k][C_out][Cig]: per tap a [Cog][Cig] run
+        ss = (int64_t)fp.Cig * fp.Cog, sci = 1, sco = fp.Cig;
+    } else {  // [C_in][Cog][k]: one [Cig][Cog][k] run
+        ss = 1, sci = (int64_t)fp.Cog * ktot, sco = ktot;
+    }
+    g.w_sci = (int32_t)(2 * sci);
+    g.w_sco = (int32_t)(2 * sco);
+    g.w_tap_pieces = fp.w_layout == CONVT_FILTER_CI_CO_K ? 0 : fp.Cig * fp.Cog / 8;
+    for (int slot = 0; slot < g.nslots; ++slot) {
+        const int t = slot / (int)noct, oct = slot % (int)noct;
+        const int kh = t / a2.K, kw = t % a2.K;
+        const int st = fp.w_flip ? (a1.K - 1 - kh) * a2.K + (a2.K - 1 - kw) : kh * a2.K + kw;
+        g.slot_w[slot] = (int32_t)(2 * (st * ss + 8 * oct * sco));
+        g.slot_h[slot] = (int32_t)(((a1.D * kh * noct + oct) * hwp + a2.D * kw) * 16);
+    }
+    return true;
+}
+
 // Plan the backward all-phase kernel (k_bwd_allphase.hip) for the input
 // gradient of a two-byte problem (fp: the forward problem), or return false
 // if it does not apply: W in the C_in x C_out x taps layout; stride 2 and
@@ -884,6 +954,8 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
             route = CONVT_ROUTE_NONE;
         else if (no_terms)
             route = CONVT_ROUTE_FILL;
+        else if (choose_grouped_bwd(pl, nd, dt))
+            route = CONVT_ROUTE_GROUPED;
         else if (direct_bwd_eligible(fp, pl->elem_bytes) && (fp.Cig < 32 || fp.Cog < 16))
             // few channels: the backward GEMM's tiles (64 dx channels, chunks
             // of 16 dy channels) would be mostly padding
@@ -910,6 +982,7 @@ convt_status plan_backward(Plan *pl, const int64_t I[3], const int64_t K[3], con
             case CONVT_ROUTE_DIRECT:
                 ok = !empty_out && !no_terms && direct_bwd_eligible(fp, pl->elem_bytes);
                 break;
+            case CONVT_ROUTE_GROUPED: ok = !empty_out && !no_terms && choose_grouped_bwd(pl, nd, dt); break;
             case CONVT_ROUTE_NAIVE: ok = !empty_out && !no_terms; break;
             default: ok = false;
         }

@@ -93,7 +93,9 @@ typedef enum convt_route {
     CONVT_ROUTE_NONE = 1,       /* the output is empty: nothing to launch */
     CONVT_ROUTE_FILL = 2,       /* no input channels: y = bias (or 0) */
     CONVT_ROUTE_PHASE_GEMM = 3, /* stride-phase implicit-gather GEMM on MFMA */
-    CONVT_ROUTE_GROUPED = 4,    /* grouped / few-channel stride-phase kernel, MFMA, LDS-staged output */
+    CONVT_ROUTE_GROUPED = 4,    /* grouped / few-channel stride-phase kernel, MFMA, LDS-staged output;
+                                   as route_bwd, its input gradient on MFMA (see
+                                   convt_backward_data) */
     CONVT_ROUTE_DIRECT = 5,     /* small-channel direct kernel, weight slab in LDS */
     CONVT_ROUTE_NAIVE = 6,      /* one thread per output, gathers its terms */
     CONVT_ROUTE_PHASE_GEMM_PACKED = 7, /* two-byte types: the phase GEMM on a channel-chunked copy
@@ -269,6 +271,12 @@ convt_status convt_forward_prepared(convt_plan_t plan, const void *x, const void
  * W in the CI_CO_K layout: one MFMA GEMM reads dy and W as stored and sums
  * the four stride phases of each dx box from one halo; no workspace; dy must
  * be 4-byte and W and dx 16-byte aligned, else CONVT_ERR_INVALID_ARGUMENT),
+ * GROUPED (two-byte 2-D problems whose output channels per group are a
+ * multiple of 8 with at most 16 (tap, 8-channel slice) slots, at most 16
+ * input channels per group and dy rows of whole 16-byte chunks: a strided
+ * correlation of dy on MFMA, a block per (batch, group, dx row tile) with
+ * dy's halo and the group's W in LDS; no workspace; when dy or W is not
+ * 16-byte aligned the call runs the DIRECT kernel instead, same result),
  * DIRECT (few channels per group: a thread per dx position over its group's
  * input channels, weights in LDS), NAIVE (one thread per dx element).
  */

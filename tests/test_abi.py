@@ -390,6 +390,28 @@ def test_allphase_backward_route_rules():
     assert L.convt_backward_data(h, fake, fake, fake + 8, None, None) == 1
 
 
+def test_grouped_backward_route_rules():
+    """route_bwd GROUPED: two-byte 2-D problems with output channels per group
+    a multiple of 8 (at most 16 (tap, 8-channel slice) slots), at most 16
+    input channels per group and dy rows of whole 16-byte chunks; AUTO takes
+    it there (the grouped workload), forced elsewhere it is refused."""
+    wl = workloads.get("c4a")
+    assert plan(x_shape=wl.x_shape, w_shape=wl.w_shape, stride=wl.stride, padding=wl.padding,
+                groups=wl.groups, dtype="bf16").route_bwd == "grouped"
+    ok = dict(x_shape=(1, 16, 9, 16), w_shape=(16, 8, 4, 4), stride=2, padding=1, groups=2, dtype="bf16")
+    assert plan(**ok).route_bwd == "grouped"
+    assert plan(**dict(ok, dtype="f16")).route_bwd == "grouped"
+    for bad in (dict(dtype="f32"),                                        # element type
+                dict(w_shape=(16, 4, 4, 4)),                              # Cog not a multiple of 8
+                dict(x_shape=(1, 34, 9, 16), w_shape=(34, 8, 4, 4)),      # 17 input channels per group
+                dict(w_shape=(16, 24, 4, 4)),                             # 3 slices x 16 taps > 16 slots
+                dict(x_shape=(1, 16, 9, 15)),                             # dy rows of 30 values
+                dict(x_shape=(1, 16, 3, 9, 16), w_shape=(16, 8, 2, 4, 4), stride=(1, 2, 2),
+                     padding=(0, 1, 1))):                                 # 3-D
+        assert status_of(**dict(ok, **bad), route_bwd="grouped") == 2, bad
+        assert plan(**dict(ok, **bad)).route_bwd != "grouped", bad
+
+
 def test_backward_routes():
     """Routes of the backward pass: forced routes that cannot serve are
     refused; the naive route serves any problem; few channels per group take

@@ -19,7 +19,7 @@ from tests.gpu_util import TOL, norm_error, say, to_device, to_host64
 
 pytestmark = pytest.mark.gpu
 
-ROUTES = ["auto", "naive", "phase_gemm", "direct", "phase_gemm_allphase"]
+ROUTES = ["auto", "naive", "phase_gemm", "direct", "phase_gemm_allphase", "grouped"]
 
 
 def bwd_tensors(xs, ws, prm, dtype, dist, seed):

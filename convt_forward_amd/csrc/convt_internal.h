@@ -147,7 +147,8 @@ constexpr int kBwdPlaneRowsKS = 255;  // ... with the K split (a 128-position bo
 // those rows goes to LDS as 16-byte cells of 8 dy channels
 // [halo row][slice][column].
 constexpr int kGbMaxSlots = 16;     // (tap, 8-channel dy slice) slots: four MFMA K steps
-constexpr int kGbLdsBudget = 24576;  // LDS per block (halo + weights)
+constexpr int kGbLdsBudget = 24576;  // LDS per block (halo + weights + fragment slab)
+constexpr int kGbSlabPitch = 17 * 16; // bytes per input channel in the fragment slab
 struct GrpBwdArgs {
     int32_t G, Ci, Co, Cig, Cog, noct;  // the forward problem's channels; noct = Cog / 8
     int32_t I1, I2, O1, O2;             // dx and dy extents (height, width)
@@ -156,7 +157,8 @@ struct GrpBwdArgs {
     int32_t R, nt_h;                    // dx rows per block, row tiles
     int32_t hr, hwp;                    // halo rows, halo row pitch (cells, odd)
     int32_t x_plane, y_plane;           // dx and dy plane elements
-    int32_t w_off, lds_bytes;           // LDS: halo from 0, W from w_off
+    int32_t w_off, slab_off, lds_bytes; // LDS: halo from 0, W from w_off, the fragment
+                                        // slab [input channel][17 slots][16 B] from slab_off
     int32_t w_sci, w_sco, w_tap_pieces; // W as stored: bytes between input / output
                                         // channels of a group; 16-byte pieces per tap
                                         // when taps are outermost, else 0

@@ -14,9 +14,12 @@
 //
 // A block owns one (batch, group) and R dx rows over the full dx width:
 //  1. the group's part of W, as W stores it, goes to LDS by LDS-destination
-//     buffer loads (no registers, no arithmetic per element); the MFMA weight
-//     fragments are read from that layout with its channel strides, once per
-//     wave;
+//     buffer loads (no registers, no arithmetic per element); after the first
+//     barrier the block gathers the MFMA weight fragments from that layout
+//     (its channel strides) into a slab whose rows the 16 lanes of a fragment
+//     read without bank conflicts (gathered per wave straight from the stored
+//     layout, 16 input channels whose rows lie 2 * C_out/g * taps bytes
+//     apart conflicted up to 16-way);
 //  2. dy's halo for the R rows (every tap's rows, the full dy width) goes to
 //     LDS as 16-byte cells of 8 dy channels, [halo row][slice][column]: a
 //     lane loads 8 positions of each of 8 channels (eight 16-byte loads) and
@@ -132,35 +135,46 @@ __global__ __launch_bounds__(256) void grouped_bwd_kernel(GrpBwdArgs a, const ui
     // every copy (weights, halo) has landed and the cells are written
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // 3. this lane's K slots: slot = 4 kb + kg4; its weight fragment (8 dy
-    // channels of input channel l16; channels past Cig take the last one,
-    // their columns are never stored; slots past nslots are zero) and the
-    // halo byte offset of its tap for dx row 0, position 0
-    const int l16 = lane & 15, kg4 = lane >> 4;
+    // 3. the fragment slab: thread t builds (input channel t / 16, slot
+    // t % 16), the slot's 8 dy channels of that input channel read from W as
+    // stored (channel strides w_sci, w_sco), written as one 16-byte row at
+    // [channel][slot] (pitch 17 slots: the 16 lanes of a fragment read fall
+    // on distinct banks). Slots past nslots are zero.
     const int32_t *slot_w = (const int32_t *)(kseg + offsetof(GrpBwdArgs, slot_w));
     const int32_t *slot_h = (const int32_t *)(kseg + offsetof(GrpBwdArgs, slot_h));
-    const unsigned char *wl = lds + a.w_off + min(l16, Cig - 1) * a.w_sci;
-    const int wsco = a.w_sco;
+    {
+        const int ci = tid >> 4, slot = tid & 15;
+        if (ci < Cig) {
+            u32x4 wv = {0u, 0u, 0u, 0u};
+            if (slot < a.nslots) {
+                const unsigned char *wp = lds + a.w_off + ci * a.w_sci + slot_w[slot];
+                const int wsco = a.w_sco;
+                if (wsco == 2) {  // uniform: the 8 dy channels are adjacent
+                    wv = *(const u32x4 *)wp;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        wv[i] = (uint32_t)*(const uint16_t *)(wp + 2 * i * wsco) |
+                                (uint32_t)*(const uint16_t *)(wp + (2 * i + 1) * wsco) << 16;
+                }
+            }
+            *(u32x4 *)(lds + a.slab_off + ci * kGbSlabPitch + slot * 16) = wv;
+        }
+    }
+    __syncthreads();
+    // this lane's K slots: slot = 4 kb + kg4, its weight fragment (input
+    // channel l16; channels past Cig take the last one, their columns are
+    // never stored) and the halo byte offset of its tap for dx row 0,
+    // position 0
+    const int l16 = lane & 15, kg4 = lane >> 4;
+    const unsigned char *slab = lds + a.slab_off + min(l16, Cig - 1) * kGbSlabPitch;
     u32x4 bw[KS];
     uint32_t aoff[KS];
 #pragma unroll
     for (int kb = 0; kb < KS; ++kb) {
         const int slot = 4 * kb + kg4;
-        const bool ok = slot < a.nslots;
-        u32x4 wv = {0u, 0u, 0u, 0u};
-        if (ok) {
-            const unsigned char *wp = wl + slot_w[slot];
-            if (wsco == 2) {  // uniform: the 8 dy channels are adjacent
-                wv = *(const u32x4 *)wp;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    wv[i] = (uint32_t)*(const uint16_t *)(wp + 2 * i * wsco) |
-                            (uint32_t)*(const uint16_t *)(wp + (2 * i + 1) * wsco) << 16;
-            }
-        }
-        bw[kb] = wv;
-        aoff[kb] = (uint32_t)slot_h[ok ? slot : 0];
+        bw[kb] = *(const u32x4 *)(slab + slot * 16);
+        aoff[kb] = (uint32_t)slot_h[slot < a.nslots ? slot : 0];
     }
 
     // items (dx row r, segment sg) dealt to the waves in turn

@@ -745,7 +745,8 @@ bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
     // of dy's row (staged as whole chunks) after the P2 zero columns
     const int64_t hwp =
         std::max<int64_t>((int64_t)a2.S * (a2.I - 1) + (int64_t)a2.D * (a2.K - 1) + 1, (int64_t)a2.P + a2.O) | 1;
-    const int64_t w_bytes = ((int64_t)fp.Cig * fp.Cog * ktot * 2 + 1023) / 1024 * 1024;
+    // the group's W as stored (whole 1 KiB pieces), then the fragment slab
+    const int64_t w_bytes = ((int64_t)fp.Cig * fp.Cog * ktot * 2 + 1023) / 1024 * 1024 + 16 * kGbSlabPitch;
     auto halo_rows = [&](int64_t r) { return (int64_t)a1.S * (r - 1) + (int64_t)a1.D * (a1.K - 1) + 1; };
     auto halo_bytes = [&](int64_t r) { return halo_rows(r) * noct * hwp * 16; };
     int64_t R = 1;
@@ -766,6 +767,7 @@ bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
     g.hr = (int32_t)halo_rows(R); g.hwp = (int32_t)hwp;
     g.x_plane = fp.x_plane; g.y_plane = fp.y_plane;
     g.w_off = (int32_t)halo_bytes(R);
+    g.slab_off = (int32_t)(halo_bytes(R) + w_bytes - 16 * kGbSlabPitch);
     g.lds_bytes = (int32_t)(halo_bytes(R) + w_bytes);
     // element strides of the group's weights: stored tap, input channel,
     // output channel

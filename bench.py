@@ -351,6 +351,9 @@ def main() -> int:
         "ms_per_step": sec_per_step * 1e3,
         "ms_per_step_median": float(np.median(step_us)) / 1e3,
         "ms_per_step_min": float(np.min(step_us)) / 1e3,
+        "timing": ("ms_per_step (and value): K steps back to back on the host clock, synchronized "
+                   "before and after; ms_per_step_median / _min: single steps between event pairs "
+                   "in a separate pass, each without the overlap of its neighbours' launches"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -147,7 +147,7 @@ constexpr int kBwdPlaneRowsKS = 255;  // ... with the K split (a 128-position bo
 // those rows goes to LDS as 16-byte cells of 8 dy channels
 // [halo row][slice][column].
 constexpr int kGbMaxSlots = 16;     // (tap, 8-channel dy slice) slots: four MFMA K steps
-constexpr int kGbLdsBudget = 24576;  // LDS per block (halo + weights + fragment slab)
+constexpr int kGbLdsBudget = 28672;  // LDS per block (halo + weights + fragment slab)
 constexpr int kGbSlabPitch = 17 * 16; // bytes per input channel in the fragment slab
 struct GrpBwdArgs {
     int32_t G, Ci, Co, Cig, Cog, noct;  // the forward problem's channels; noct = Cog / 8

@@ -727,7 +727,8 @@ bool direct_bwd_eligible(const DevParams &fp, int elem_bytes) {
 // group, dy rows of whole 16-byte chunks, 32-bit buffer offsets, and the
 // direct backward kernel eligible too (it serves calls whose dy or dx is not
 // aligned for this one). A block takes R dx rows (a power of two up to 16,
-// about 256 dx positions) whose dy halo and weights fit the LDS budget.
+// about 256 dx positions) whose dy halo, weights and fragment slab fit the
+// LDS budget.
 bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
     const DevParams &fp = pl->dp;
     if (dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16) return false;

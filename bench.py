@@ -285,20 +285,24 @@ def main() -> int:
     # The dominant kernel alone: back-to-back launches over the same rotating
     # buffer sets (weights prepared once per set), bracketed by one event
     # pair on the launch stream, so that dispatch gaps after the reorder
-    # kernel are not charged to it.
+    # kernel are not charged to it. At least 100 launches: under sustained
+    # MFMA load the part's clock moves over the first milliseconds (a short
+    # fast stretch, a slower one, then steady), so a few tens of launches
+    # would measure whichever stretch they fall in.
     for s in sets:
         pl.prepare_weights_ptr(s["w"].data_ptr(), s["ws"].data_ptr(), sh)
     torch.cuda.synchronize()
+    KK = max(K, 100)
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
-    for i in range(K):
+    for i in range(KK):
         s = sets[i % nsets]
         pl.forward_prepared_ptr(s["x"].data_ptr(), s["w"].data_ptr(),
                                 s["b"].data_ptr() if s["b"] is not None else 0, s["y"].data_ptr(),
                                 s["ws"].data_ptr(), sh)
     k1.record(stream)
     torch.cuda.synchronize()
-    kern_s = k0.elapsed_time(k1) / 1e3 / K
+    kern_s = k0.elapsed_time(k1) / 1e3 / KK
 
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -333,7 +337,7 @@ def main() -> int:
     roofline = {
         "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
         "frac": achieved / peak, "traffic": traffic,
-        "kernel": kernel, "kernel_us": kern_s * 1e6,
+        "kernel": kernel, "kernel_us": kern_s * 1e6, "kernel_launches": KK,
         "step_us_events": step_gpu_s * 1e6,
         "step_us_events_median": float(np.median(step_us)),
         "step_us_events_min": float(np.min(step_us)),

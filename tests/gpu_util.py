@@ -22,6 +22,12 @@ import workloads
 # float16: one rounding of the output (2^-11 of its magnitude, which the
 # denominator bounds) plus float32 accumulation: 1e-3
 TOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 1e-3}
+# A rounding into the subnormal range errs by up to half the subnormal
+# spacing, an absolute amount that the relative bounds above do not cover
+# (a float16 output of 2.1e-5 = one product x*w, rounded once, is off by
+# 1.06e-3 of itself): the error measure subtracts this floor first. float16
+# 2^-25, bfloat16 2^-134, float32 2^-150.
+SUBNORMAL_FLOOR = {"f32": 2.0 ** -150, "bf16": 2.0 ** -134, "f16": 2.0 ** -25}
 # Lipschitz constant of each activation (convt_activation code): with an
 # activation f the denominator becomes L_f * (scale + |bias|) + |f(y_ref)|,
 # the bound on the pre-activation error carried through f plus the rounding
@@ -75,9 +81,11 @@ def oracle_full(tens: workloads.Tensors, params: dict):
 
 
 def norm_error(y_gpu: np.ndarray, y_ref: np.ndarray, scale: np.ndarray, bias_abs: np.ndarray,
-               act: int = 0):
+               act: int = 0, dtype: str | None = None):
     """max normalised error; outputs with zero denominator must match exactly.
-    With an activation, the denominator is L_f * (scale + |bias|) + |y_ref|."""
+    With an activation, the denominator is L_f * (scale + |bias|) + |y_ref|.
+    With the element type given, the error first loses the type's subnormal
+    rounding floor (SUBNORMAL_FLOOR)."""
     den = scale + bias_abs
     if act:
         den = ACT_LIPSCHITZ[act] * den + np.abs(y_ref)
@@ -87,6 +95,8 @@ def norm_error(y_gpu: np.ndarray, y_ref: np.ndarray, scale: np.ndarray, bias_abs
         return float("inf")
     if np.all(zero):
         return 0.0
+    if dtype is not None:
+        diff = np.maximum(diff - SUBNORMAL_FLOOR[dtype], 0.0)
     return float(np.max(diff[~zero] / den[~zero]))
 
 
@@ -103,7 +113,7 @@ def check_full(tens, params, route="auto", tag=""):
     ref, sc = oracle_full(tens, params)
     assert y.shape == ref.shape
     e = norm_error(y, ref, sc, bias_abs_full(tens, ref.shape),
-                   C.ACTIVATIONS[params.get("activation", "none")])
+                   C.ACTIVATIONS[params.get("activation", "none")], tens.dtype)
     say(f"[gpu]   -> plan route {pl.route}, max normalised error {e:.3e}")
     assert e <= TOL[tens.dtype], f"{tag}: error {e} above {TOL[tens.dtype]}"
     return y, ref, pl
@@ -133,4 +143,4 @@ def check_sampled(y: np.ndarray, tens, params, pts):
                            params["dilation"], params["output_padding"], params["groups"])
     got = y[tuple(pts.T)]
     babs = np.abs(tens.bias[pts[:, 1]].astype(np.float64)) if tens.bias is not None else 0.0 * yv
-    return norm_error(got, yv, sv, babs), got, yv
+    return norm_error(got, yv, sv, babs, dtype=tens.dtype), got, yv

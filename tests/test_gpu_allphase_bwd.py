@@ -85,7 +85,7 @@ def test_uniform(case, dtype):
     say(f"[gpu] bwd allphase {case[0]} {dtype}")
     dx, ref, sc = run(case, dtype, "uniform", 81)
     assert dx.shape == ref.shape
-    e = norm_error(dx, ref, sc, np.zeros_like(sc))
+    e = norm_error(dx, ref, sc, np.zeros_like(sc), dtype=dtype)
     say(f"[gpu]   -> max normalised error {e:.3e}")
     assert e <= TOL[dtype]
 
@@ -127,7 +127,7 @@ def test_matches_the_phase_gemm_route():
         say(f"[gpu] bwd {route} {case[0]} normal(1)")
         dx = pl.backward_data(dy, w)
         torch.cuda.synchronize()
-        e = norm_error(to_host64(dx), ref, sc, np.zeros_like(sc))
+        e = norm_error(to_host64(dx), ref, sc, np.zeros_like(sc), dtype="bf16")
         assert e <= TOL["bf16"], f"{route}: {e}"
 
 

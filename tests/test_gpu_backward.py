@@ -58,7 +58,7 @@ def check_bwd_full(xs, ws, prm, dtype, route, seed, tag):
     ref, sc = oracle.backward_data(tens.x, tens.w, xs, prm["stride"], prm["padding"],
                                    prm["dilation"], prm["output_padding"], prm["groups"])
     assert dx.shape == ref.shape
-    e = norm_error(dx, ref, sc, np.zeros_like(sc))
+    e = norm_error(dx, ref, sc, np.zeros_like(sc), dtype=dtype)
     say(f"[gpu]   -> plan route {pl.route_bwd}, max normalised error {e:.3e}")
     assert e <= TOL[dtype], f"{tag}: error {e}"
 
@@ -162,7 +162,7 @@ def test_backward_data_workloads_all_outputs(name):
     ref, sc = oracle.backward_data(tens.x, tens.w, wl.x_shape, prm["stride"], prm["padding"],
                                    prm["dilation"], prm["output_padding"], prm["groups"])
     assert dx.shape == ref.shape
-    e = norm_error(dx, ref, sc, np.zeros_like(sc))
+    e = norm_error(dx, ref, sc, np.zeros_like(sc), dtype=wl.dtype)
     say(f"[gpu]   -> route {pl.route_bwd}, max normalised error {e:.3e}")
     assert e <= TOL[wl.dtype]
 
@@ -206,7 +206,7 @@ def test_backward_data_large_plane_sampled():
         dx = pl.backward_data(dy, w)
         torch.cuda.synchronize()
         got = to_host64(dx[tuple(torch.from_numpy(pts.T).to(dx.device))])
-        e = norm_error(got, xv, sv, np.zeros_like(sv))
+        e = norm_error(got, xv, sv, np.zeros_like(sv), dtype="bf16")
         assert e <= TOL["bf16"], f"{route}: {e}"
         del dx
         torch.cuda.empty_cache()

@@ -101,7 +101,7 @@ def test_float16_backward_data(case):
         torch.cuda.synchronize()
         ref, sc = oracle.backward_data(t.x, t.w, case[1], case[3], case[4], case[5], case[6],
                                        case[7])
-        e = norm_error(to_host64(dx), ref, sc, np.zeros_like(sc))
+        e = norm_error(to_host64(dx), ref, sc, np.zeros_like(sc), dtype="f16")
         assert e <= TOL["f16"], f"backward {route}: {e}"
 
 

@@ -58,6 +58,6 @@ def test_output_address_with_bit31(case, dtype):
     pl.forward(x, w, b, y=y)
     torch.cuda.synchronize()
     ref, sc = oracle_full(tens, dict(stride=s, padding=p, dilation=d, output_padding=op, groups=g))
-    e = norm_error(to_host64(y), ref, sc, bias_abs_full(tens, ref.shape))
+    e = norm_error(to_host64(y), ref, sc, bias_abs_full(tens, ref.shape), dtype=dtype)
     del base
     assert e <= TOL[dtype], f"{name} {dtype}: error {e}"

@@ -71,7 +71,7 @@ def test_grouped_backward_uniform(case, dtype):
     dx = pl.backward_data(to_device(t.x_dev, dtype), to_device(t.w_dev, dtype))
     torch.cuda.synchronize()
     ref, sc = oracle.backward_data(t.x, t.w, xs, s, p, d, op, g)
-    e = norm_error(to_host64(dx), ref, sc, np.zeros(ref.shape))
+    e = norm_error(to_host64(dx), ref, sc, np.zeros(ref.shape), dtype=dtype)
     assert e <= TOL[dtype], f"{name} {dtype}: error {e}"
 
 

@@ -31,7 +31,9 @@ def rearrange(w: np.ndarray, groups: int, layout: str, flipped: bool) -> np.ndar
         wg = w.reshape((groups, ci // groups, cog) + w.shape[2:])
         out = np.moveaxis(wg, (0, 1, 2), (nd, nd + 2, nd + 1)).reshape(
             w.shape[2:] + (groups * cog, ci // groups))
-    return np.ascontiguousarray(out)
+    # a copy: a flipped size-1 axis keeps a negative stride that numpy still
+    # calls contiguous (and torch.from_numpy refuses)
+    return np.array(out, order="C", copy=True)
 
 
 def rne_bf16(v):

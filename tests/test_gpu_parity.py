@@ -457,7 +457,7 @@ def test_large_planes_sampled(case):
             yv, sv = oracle.points(tens.x, tens.w, tens.bias, pts, s, p, d, op, g)
             babs = np.abs(tens.bias[pts[:, 1]].astype(np.float64))
         got = to_host64(y[tuple(torch.from_numpy(pts.T).to(y.device))])
-        e = norm_error(got, yv, sv, babs)
+        e = norm_error(got, yv, sv, babs, dtype=dt)
         say(f"[gpu]   -> {len(pts)} points, max normalised error {e:.3e}")
         assert e <= TOL[dt], f"{route}: {e}"
         del y

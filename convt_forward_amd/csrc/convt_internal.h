@@ -154,7 +154,8 @@ struct GrpBwdArgs {
     int32_t I1, I2, O1, O2;             // dx and dy extents (height, width)
     int32_t S1, S2, P1, P2, D1, D2;     // stride, low padding, dilation
     int32_t K1, K2, ktot, nslots, ks;   // taps; slots = ktot * noct; K steps
-    int32_t R, nt_h;                    // dx rows per block, row tiles
+    int32_t R, nt_h, B;                 // dx rows per tile, row tiles, batch; tiles =
+                                        // G * B * nt_h, row tiles fastest, groups slowest
     int32_t hr, hwp;                    // halo rows, halo row pitch (cells, odd)
     int32_t x_plane, y_plane;           // dx and dy plane elements
     int32_t w_off, slab_off, lds_bytes; // LDS: halo from 0, W from w_off, the fragment

@@ -726,9 +726,9 @@ bool direct_bwd_eligible(const DevParams &fp, int elem_bytes) {
 // at most 16 (tap, 8-channel slice) slots, at most 16 input channels per
 // group, dy rows of whole 16-byte chunks, 32-bit buffer offsets, and the
 // direct backward kernel eligible too (it serves calls whose dy or dx is not
-// aligned for this one). A block takes R dx rows (a power of two up to 16,
-// about 256 dx positions) whose dy halo, weights and fragment slab fit the
-// LDS budget.
+// aligned for this one). A tile is R dx rows (a power of two up to 16, about
+// 256 dx positions) whose dy halo, weights and fragment slab fit the LDS
+// budget and whose halo is at most 256 load units (one per thread).
 bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
     const DevParams &fp = pl->dp;
     if (dtype != CONVT_DTYPE_BF16 && dtype != CONVT_DTYPE_F16) return false;
@@ -750,10 +750,12 @@ bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
     const int64_t w_bytes = ((int64_t)fp.Cig * fp.Cog * ktot * 2 + 1023) / 1024 * 1024 + 16 * kGbSlabPitch;
     auto halo_rows = [&](int64_t r) { return (int64_t)a1.S * (r - 1) + (int64_t)a1.D * (a1.K - 1) + 1; };
     auto halo_bytes = [&](int64_t r) { return halo_rows(r) * noct * hwp * 16; };
+    // halo load units (row, slice, 8-position chunk): one per thread
+    auto units = [&](int64_t r) { return halo_rows(r) * noct * (a2.O / 8); };
     int64_t R = 1;
     while (R < 16 && 2 * R * a2.I <= 256 && 2 * R <= a1.I) R *= 2;
-    while (R > 1 && halo_bytes(R) + w_bytes > kGbLdsBudget) R /= 2;
-    if (halo_bytes(R) + w_bytes > kGbLdsBudget) return false;
+    while (R > 1 && (halo_bytes(R) + w_bytes > kGbLdsBudget || units(R) > 256)) R /= 2;
+    if (halo_bytes(R) + w_bytes > kGbLdsBudget || units(R) > 256) return false;
     const int64_t nt_h = ceil_div(a1.I, R);
     if (nt_h > 65535 || (int64_t)fp.G * fp.B > 0x7fffffff) return false;
     GrpBwdArgs &g = pl->gb;
@@ -764,7 +766,8 @@ bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
     g.K1 = a1.K; g.K2 = a2.K; g.ktot = (int32_t)ktot;
     g.nslots = (int32_t)(ktot * noct);
     g.ks = (g.nslots + 3) / 4;
-    g.R = (int32_t)R; g.nt_h = (int32_t)nt_h;
+    g.R = (int32_t)R; g.nt_h = (int32_t)nt_h; g.B = fp.B;
+    if ((int64_t)fp.G * fp.B * nt_h > 0x7fffffff) return false;
     g.hr = (int32_t)halo_rows(R); g.hwp = (int32_t)hwp;
     g.x_plane = fp.x_plane; g.y_plane = fp.y_plane;
     g.w_off = (int32_t)halo_bytes(R);

@@ -74,6 +74,9 @@ struct DevParams {
                                // not whole chunks); chunk k sits at column 8k + hshift - umin
     int32_t grp_nsc;           // grouped route: q segments (16 positions) per staged chunk
                                // (0: segment pairs leave through DPP, no staging)
+    int32_t grp_slab_off;      // grouped route: LDS offset (bytes) of the weight-fragment slab
+                               // [Cog][slot (pitch grp_ns | 1)][8 input channels]
+    int32_t grp_ns;            // grouped route: (tap, 8-channel slice) slots of all phases
     int32_t grp_st_off;        // grouped route: LDS offset (bytes) of the per-wave output staging
     int32_t grp_st_pitch;      // grouped route: staging bytes per channel (chunk bytes + 16)
     int32_t grp_ksteps;        // grouped route: MFMA K steps per phase (1, 2 or 4)

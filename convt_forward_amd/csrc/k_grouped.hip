@@ -102,7 +102,7 @@ struct GrpArgs {
     int32_t x_plane, y_plane;
     int32_t th, tw, hd, hh, hw;
     int32_t grp_hwp, grp_hshift, grp_nk, grp_nsc;
-    int32_t grp_w_off, grp_tab_off, grp_st_off, grp_st_pitch;
+    int32_t grp_w_off, grp_tab_off, grp_st_off, grp_st_pitch, grp_slab_off, grp_ns;
     int32_t ktot, nphase;
     int32_t tab_n;                      // int2 entries of tab
     int32_t w_sc, w_so, w_tap_pieces;   // the group's weights as stored (GrpTables)
@@ -296,6 +296,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     // every wave's copies (weights, table; halo without DMA) have landed and
     // the cells are written
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the weight-fragment slab, built in place of the weights: entry (output
+    // channel co, slot s) holds the slot's 8 input channels of channel co,
+    // gathered from W as stored (the slot's weight offset from the table,
+    // channel strides w_so, w_sc); rows of ns | 1 slots, so the 16 lanes of
+    // a fragment read fall on distinct banks (read per pair straight from the
+    // stored layout, they conflicted). Each thread gathers its entries (at
+    // most 4: the group's weights are at most 16 KiB) into registers before
+    // any is written.
+    const int ns = p.grp_ns, slab_pitch = (ns | 1) * 16;
+    {
+        const int wsc = p.w_sc, nent = p.Cog * ns;
+        u32x4 ent[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i;
+            if (e < nent) {
+                const int co = div_small(e, ns), sl = e - co * ns;
+                const unsigned char *wp = lds + p.grp_w_off + co * p.w_so + tab[sl].y;
+                if (wsc == 2) {  // uniform: the eight channels are adjacent
+                    ent[i] = *(const u32x4 *)wp;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        ent[i][k] = (uint32_t)*(const uint16_t *)(wp + 2 * k * wsc) |
+                                    (uint32_t)*(const uint16_t *)(wp + (2 * k + 1) * wsc) << 16;
+                }
+            }
+        }
+        __syncthreads();  // every gather has read the weights
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i;
+            if (e < nent) {
+                const int co = div_small(e, ns), sl = e - co * ns;
+                *(u32x4 *)(lds + p.grp_slab_off + co * slab_pitch + sl * 16) = ent[i];
+            }
+        }
+    }
+    __syncthreads();
 
     // 2. Per (depth residue, height residue) pair, each wave takes chunks of
     // nsc 16-position segments of the block's q rows in turn. For a segment
@@ -310,10 +349,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     const int l16 = lane & 15, kg4 = lane >> 4;
     const int Cog = p.Cog;
     const int O2 = a2.O;
-    // this lane's output channel in the group's weights as stored (the
-    // padding channels take the last one: their columns are never stored)
-    const unsigned char *wraw = lds + p.grp_w_off + min(l16, Cog - 1) * p.w_so;
-    const int wsc = p.w_sc;
+    // this lane's row of the fragment slab (the padding channels take the
+    // last one: their columns are never stored)
+    const unsigned char *slab_lane = lds + p.grp_slab_off + min(l16, Cog - 1) * slab_pitch;
     const int nseg = (Qw + 15) >> 4;
     // nsc == 0: width stride 2, at most 8 channels, an even segment count:
     // chunks are segment pairs that leave through DPP (no staging)
@@ -408,15 +446,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
                     u32x4 wv = {0u, 0u, 0u, 0u};
                     if (sl_ok[r2][kb]) {
                         e = tab[sbase + slot];
-                        const unsigned char *wp = wraw + e.y;
-                        if (wsc == 2) {  // uniform: the eight channels are adjacent
-                            wv = *(const u32x4 *)wp;
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                wv[i] = (uint32_t)*(const uint16_t *)(wp + 2 * i * wsc) |
-                                        (uint32_t)*(const uint16_t *)(wp + (2 * i + 1) * wsc) << 16;
-                        }
+                        wv = *(const u32x4 *)(slab_lane + (sbase + slot) * 16);
                     }
                     rd[r2][kb] = (uint32_t)e.x + (uint32_t)l16 * 16;
                     bw[r2][kb] = __builtin_bit_cast(typename GrpElem<E>::v8, wv);
@@ -667,6 +697,8 @@ static GrpArgs grp_args(const Plan &pl) {
     a.grp_hwp = p.grp_hwp; a.grp_hshift = p.grp_hshift; a.grp_nk = p.grp_nk; a.grp_nsc = p.grp_nsc;
     a.grp_w_off = p.grp_w_off; a.grp_tab_off = p.grp_tab_off; a.grp_st_off = p.grp_st_off;
     a.grp_st_pitch = p.grp_st_pitch;
+    a.grp_slab_off = p.grp_slab_off;
+    a.grp_ns = p.grp_ns;
     a.ktot = p.ktot; a.nphase = p.nphase;
     a.tab_n = pl.gt.tab_n;
     a.w_sc = pl.gt.w_sc;

@@ -582,12 +582,19 @@ bool choose_grouped_tile(DevParams *dp) {
         pair_dpp ? 0 : (int64_t)tiles::kGrpThreads / 64 * (dp->Cog + 1) * st_pitch;
     auto al = [](int64_t v) { return (v + 15) / 16 * 16; };
     // the group's weights (as W stores them) and the slot table reach LDS by
-    // DMA in 1 KiB and 256-byte pieces: their areas are whole pieces
-    const int64_t w_bytes = ((int64_t)dp->ktot * dp->Cog * dp->Cig * 2 + 1023) / 1024 * 1024;
+    // DMA in 1 KiB and 256-byte pieces: their areas are whole pieces. The
+    // weight-fragment slab replaces the weights in place: per output channel
+    // a row of 16 bytes per slot, an odd number of slots per row (the 16
+    // lanes of a fragment read, one channel each, fall on distinct banks)
+    const int64_t ns = (int64_t)dp->ktot * (dp->Cig / 8);
+    const int64_t slab_bytes = (int64_t)dp->Cog * (ns | 1) * 16;
+    const int64_t w_bytes =
+        std::max<int64_t>(((int64_t)dp->ktot * dp->Cog * dp->Cig * 2 + 1023) / 1024 * 1024, slab_bytes);
     // slot table: a 16-byte record per phase, then (halo offset, weight
     // offset) per (tap, 8-channel slice)
     const int64_t tab_bytes =
         (16 * (int64_t)dp->nphase + (int64_t)dp->ktot * (dp->Cig / 8) * 8 + 255) / 256 * 256;
+
     int best = 0;
     int64_t best_halo = 0;
     for (int rows = 1; rows <= 64; rows *= 2) {
@@ -621,6 +628,8 @@ bool choose_grouped_tile(DevParams *dp) {
     dp->nt_w = 1;
     dp->grp_w_off = (int32_t)al(best_halo);
     dp->grp_tab_off = (int32_t)(al(best_halo) + al(w_bytes));
+    dp->grp_slab_off = dp->grp_w_off;
+    dp->grp_ns = (int32_t)ns;
     dp->grp_st_off = (int32_t)(al(best_halo) + al(w_bytes) + al(tab_bytes));
     dp->grp_lds_bytes = (int32_t)(dp->grp_st_off + st_bytes);
     return true;

@@ -8,8 +8,8 @@ meets those conditions (q width 32, output rows of 64 two-byte values, 16-byte
 aligned torch allocations), so the instance runs; they vary what it must get
 right: fewer than 8 channels per group (padding columns), two slices per tap
 (two K steps), a 3-D problem, each activation in both two-byte types, and the
-three filter layouts with and without flipped taps (the kernel reads its MFMA
-weight fragments from W as stored). Small-integer data must equal the oracle
+three filter layouts with and without flipped taps (the kernel gathers its
+MFMA weight fragments from W as stored). Small-integer data must equal the oracle
 rounded once; uniform data must meet the normalised-error bound.
 """
 import numpy as np

@@ -57,7 +57,7 @@ constexpr int kNThreads = 256;
 
 }  // namespace
 
-template <typename T, int WGM, int GS, int XU, bool ACT, bool Y16>
+template <typename T, int WGM, int GS, int XU, int ACT, bool Y16>
 __global__ __launch_bounds__(kNThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__restrict__ wr,
                             const T *__restrict__ bias, T *__restrict__ y) {
@@ -384,8 +384,7 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
     for (int nt = 0; nt < NT; ++nt) vo[nt] = yoff[nt] + lane_co * ypl_bytes;
     // channel j pairs (j, j + 1), j even, are rows 1 apart: one conversion
     // gives both, stored from the low and the high half
-    auto store_all = [&](auto act_tag) __attribute__((always_inline)) {
-        constexpr int A = decltype(act_tag)::value;
+    auto store_all = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -394,9 +393,9 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     float v0 = acc[mt][nt][j], v1 = acc[mt][nt][j + 1];
-                    if constexpr (A != CONVT_ACT_NONE) {
-                        v0 = activate<true>(A, v0);
-                        v1 = activate<true>(A, v1);
+                    if constexpr (ACT != CONVT_ACT_NONE) {
+                        v0 = activate<true>(ACT, v0);
+                        v1 = activate<true>(ACT, v1);
                     }
                     const uint32_t pk = pack_half2<HT>(v0, v1);
                     __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, ys, vo[nt], so, 0);
@@ -409,8 +408,7 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
     // path): a wave stages 32 channels x its 128 positions at a time in
     // LDS (the stage buffers are free past the loop's last barrier) and
     // stores 16-byte row pieces, 8 positions each, instead of 2-byte stores
-    auto store_staged = [&](auto act_tag) __attribute__((always_inline)) {
-        constexpr int A = decltype(act_tag)::value;
+    auto store_staged = [&]() __attribute__((always_inline)) {
         constexpr int SP = 2 * NT * 32 + 16;  // staging bytes per channel
         unsigned char *stg = lds + wave * (32 * SP);
 #pragma unroll
@@ -421,9 +419,9 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     float v0 = acc[mt][nt][j], v1 = acc[mt][nt][j + 1];
-                    if constexpr (A != CONVT_ACT_NONE) {
-                        v0 = activate<true>(A, v0);
-                        v1 = activate<true>(A, v1);
+                    if constexpr (ACT != CONVT_ACT_NONE) {
+                        v0 = activate<true>(ACT, v0);
+                        v1 = activate<true>(ACT, v1);
                     }
                     const uint32_t pk = pack_half2<HT>(v0, v1);
                     const int pos = nt * 32 + (lane & 31);
@@ -448,24 +446,14 @@ void phase_gemm_nchw_kernel(DevParams p, const T *__restrict__ x, const T *__res
             }
         }
     };
-    auto store = [&](auto act_tag) __attribute__((always_inline)) {
-        if constexpr (Y16)
-            store_staged(act_tag);
-        else
-            store_all(act_tag);
-    };
-    if constexpr (ACT) {
-        switch (p.act) {
-            case CONVT_ACT_RELU: store(std::integral_constant<int, CONVT_ACT_RELU>{}); break;
-            case CONVT_ACT_SIGMOID: store(std::integral_constant<int, CONVT_ACT_SIGMOID>{}); break;
-            case CONVT_ACT_TANH: store(std::integral_constant<int, CONVT_ACT_TANH>{}); break;
-            case CONVT_ACT_SILU: store(std::integral_constant<int, CONVT_ACT_SILU>{}); break;
-            case CONVT_ACT_GELU: store(std::integral_constant<int, CONVT_ACT_GELU>{}); break;
-            default: store(std::integral_constant<int, CONVT_ACT_NONE>{}); break;
-        }
-    } else {
-        store(std::integral_constant<int, CONVT_ACT_NONE>{});
-    }
+    // The activation kind is a template parameter (the launcher picks the
+    // instance), so each instance holds one store path: an inlined copy per
+    // kind behind a run-time switch left the staged instances with
+    // kilobytes of scratch per lane in the epilogue.
+    if constexpr (Y16)
+        store_staged();
+    else
+        store_all();
 }
 
 template <typename T, int CFG, bool Y16>
@@ -475,14 +463,22 @@ static hipError_t launch_nchw_y(const Plan &pl, const void *x, const void *wr, c
     const DevParams &p = pl.dp;
     const dim3 grid(p.n_blocks), block(kNThreads);
     const size_t lds = 0;  // static
+    auto go = [&](auto act_tag) {
+        hipLaunchKernelGGL((phase_gemm_nchw_kernel<T, C.wgm, C.gs, C.xu, decltype(act_tag)::value, Y16>), grid,
+                           block, lds, stream, p, (const T *)x, (const T *)wr, (const T *)bias, (T *)y);
+    };
 #ifndef NCHW_TUNE
-    if (p.act != CONVT_ACT_NONE)
-        hipLaunchKernelGGL((phase_gemm_nchw_kernel<T, C.wgm, C.gs, C.xu, true, Y16>), grid, block, lds, stream,
-                           p, (const T *)x, (const T *)wr, (const T *)bias, (T *)y);
-    else
+    switch (p.act) {
+        case CONVT_ACT_RELU: go(std::integral_constant<int, CONVT_ACT_RELU>{}); break;
+        case CONVT_ACT_SIGMOID: go(std::integral_constant<int, CONVT_ACT_SIGMOID>{}); break;
+        case CONVT_ACT_TANH: go(std::integral_constant<int, CONVT_ACT_TANH>{}); break;
+        case CONVT_ACT_SILU: go(std::integral_constant<int, CONVT_ACT_SILU>{}); break;
+        case CONVT_ACT_GELU: go(std::integral_constant<int, CONVT_ACT_GELU>{}); break;
+        default: go(std::integral_constant<int, CONVT_ACT_NONE>{}); break;
+    }
+#else
+    go(std::integral_constant<int, CONVT_ACT_NONE>{});
 #endif
-        hipLaunchKernelGGL((phase_gemm_nchw_kernel<T, C.wgm, C.gs, C.xu, false, Y16>), grid, block, lds, stream,
-                           p, (const T *)x, (const T *)wr, (const T *)bias, (T *)y);
     return hipGetLastError();
 }
 

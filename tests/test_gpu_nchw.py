@@ -93,8 +93,11 @@ def test_no_bias_and_packed_route_agree_with_oracle(case):
 
 
 @pytest.mark.parametrize("act", ["relu", "sigmoid", "tanh", "silu", "gelu"])
-@pytest.mark.parametrize("case", [CASES[0], CASES[4], CASES[5]], ids=["k4s2", "k4s2_3d", "k3s1"])
+@pytest.mark.parametrize("case", [CASES[0], CASES[4], CASES[5], CASES[9], CASES[10]],
+                         ids=["k4s2", "k4s2_3d", "k3s1", "k3s1_rows24", "k3s1_rows16_groups"])
 def test_activations(case, act):
+    # the last two store 16-byte row pieces through LDS staging: an instance
+    # per activation kind on each store path
     tens, prm = tensors(case, "bf16", "uniform", 14)
     prm = dict(prm, activation=act)
     check_full(tens, prm, route="phase_gemm", tag=f"nchw {case[0]} {act}")

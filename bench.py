@@ -285,14 +285,17 @@ def main() -> int:
     # The dominant kernel alone: back-to-back launches over the same rotating
     # buffer sets (weights prepared once per set), bracketed by one event
     # pair on the launch stream, so that dispatch gaps after the reorder
-    # kernel are not charged to it. At least 100 launches: under sustained
+    # kernel are not charged to it. At least 400 launches: under sustained
     # MFMA load the part's clock moves over the first milliseconds (a short
-    # fast stretch, a slower one, then steady), so a few tens of launches
-    # would measure whichever stretch they fall in.
+    # fast stretch of about 20 launches of the generator workload's kernel,
+    # a slower one of several tens, then steady), so a pass of 100 launches
+    # measured whichever stretch it fell in (about 69 us per launch when it
+    # started after 105 launches, 75 us after 45); 400 launches span the
+    # slow stretch and the steady state that sustained use runs in.
     for s in sets:
         pl.prepare_weights_ptr(s["w"].data_ptr(), s["ws"].data_ptr(), sh)
     torch.cuda.synchronize()
-    KK = max(K, 100)
+    KK = max(K, 400)
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record(stream)
     for i in range(KK):

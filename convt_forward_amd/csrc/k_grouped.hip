@@ -14,17 +14,21 @@
 // The work per output is tiny (a few K slots) and the output is 4x the
 // input, so the kernel is written for a small instruction count per stored
 // byte and for stores that write whole 128-byte rows:
-//  1. the group's reordered weights [tap][16 co][Cig] and a slot table (a
-//     record per phase; per (tap, 8-channel slice) slot the LDS offset of the
-//     tap's window and of its weights), both prepared with the weights, are
-//     copied to LDS; the input halo (the q tile grown by the union of all
+//  1. the group's part of W, as stored, and a slot table (a record per
+//     phase; per (tap, 8-channel slice) slot the LDS offset of the tap's
+//     window and the byte offset of the tap's weights in that part of W),
+//     built by the planner and passed with the kernel's arguments, are
+//     copied to LDS; the block then gathers each MFMA weight fragment (8
+//     input channels of one output channel for one slot) once into a slab
+//     [output channel][slot] of 16-byte entries written over the stored
+//     copy; the input halo (the q tile grown by the union of all
 //     phases' input windows) goes to LDS as 16-byte cells of 8 channels,
 //     [halo row][slice][column]. When x rows are whole 16-byte chunks, a lane
 //     loads 8 positions of each of 8 channels (eight 16-byte loads),
 //     transposes the 8 x 8 block in registers (v_perm) and writes 8 cells;
 //     otherwise it falls back to 2-byte loads;
-//  2. per (depth, height) residue pair, a wave keeps the weight fragments of
-//     every width residue in registers and takes chunks of 16-position
+//  2. per (depth, height) residue pair, a wave reads the weight fragments of
+//     every width residue from the slab into registers and takes chunks of 16-position
 //     segments of the block's q rows in turn: per segment and width residue
 //     up to four 16x16x32 MFMAs (rows = 16 positions, columns =
 //     the group's output channels padded to 16, K = (tap, slice) slots, four
@@ -145,9 +149,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(S2 * KS <= 
     // window origin in the halo and the byte offset of its weights in the
     // group's part of W) -> LDS by DMA, in 1 KiB and 256-byte pieces dealt
     // to the waves (their areas are whole pieces). The weights need no
-    // reordering: the MFMA fragments are read from them as stored (per lane
-    // eight input channels of one output channel, w_sc bytes apart). The
-    // copies take no registers and land while the halo is staged.
+    // reordering: the MFMA fragments are gathered from them as stored (per
+    // fragment eight input channels of one output channel, w_sc bytes apart)
+    // into the slab below. The copies take no registers and land while the
+    // halo is staged.
     {
         const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)&lds[0];
         const int npc = (Cig * p.Cog) >> 3;       // 16-byte pieces per tap

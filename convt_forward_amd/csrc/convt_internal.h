@@ -159,7 +159,10 @@ struct GrpBwdArgs {
     int32_t K1, K2, ktot, nslots, ks;   // taps; slots = ktot * noct; K steps
     int32_t R, nt_h, B;                 // dx rows per tile, row tiles, batch; tiles =
                                         // G * B * nt_h, row tiles fastest, groups slowest
-    int32_t hr, hwp;                    // halo rows, halo row pitch (cells, odd)
+    int32_t hr, hwp;                    // halo rows, pitch of a (halo row, slice) in cells (odd)
+    int32_t hwr, hp, sp;                // halo columns; with width stride 2 (sp = 2) the even
+                                        // columns take cells 0 .. hp-1 and the odd ones hp ..,
+                                        // column c at cell (c % sp) * hp + c / sp; else sp = 1
     int32_t x_plane, y_plane;           // dx and dy plane elements
     int32_t w_off, slab_off, lds_bytes; // LDS: halo from 0, W from w_off, the fragment
                                         // slab [input channel][17 slots][16 B] from slab_off

@@ -25,10 +25,14 @@
 //  2. dy's halo for the R rows (every tap's rows, the full dy width) goes to
 //     LDS as 16-byte cells of 8 dy channels, [halo row][slice][column]: a
 //     lane loads 8 positions of each of 8 channels (eight 16-byte loads) and
-//     transposes the 8 x 8 block in registers; columns outside dy hold zeros;
+//     transposes the 8 x 8 block in registers; columns outside dy hold
+//     zeros. With width stride 2 a (halo row, slice) holds its even columns
+//     first, then its odd ones, so that neighbouring dx positions read
+//     neighbouring cells (in column order they lie 2 cells apart, and the
+//     lanes of a read shared banks);
 //  3. each wave takes items (dx row, 16-position segment): one A fragment
-//     read per K step (lane = dx position, its cell s positions apart from
-//     the next lane's), the MFMAs, one rounding, and 8-byte stores of 4
+//     read per K step (lane = dx position), the MFMAs, one rounding, and
+//     8-byte stores of 4
 //     consecutive dx values per lane (2-byte stores at ragged or unaligned
 //     rows).
 #include <cstddef>
@@ -67,6 +71,10 @@ __global__ __launch_bounds__(256) void grouped_bwd_kernel(GrpBwdArgs a, const ui
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int Cig = a.Cig, Cog = a.Cog, noct = a.noct, HWP = a.hwp;
+    // halo column c -> its cell within a (halo row, slice): with width stride
+    // 2 the even columns come first, then the odd ones (sp = 2), else in order
+    const int sp1 = a.sp - 1, hp = a.hp;
+    auto cell = [&](int c) __attribute__((always_inline)) { return (c & sp1) * hp + (c >> sp1); };
     const unsigned char *kseg = (const unsigned char *)__builtin_amdgcn_kernarg_segment_ptr();
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)&lds[0];
     const int ntiles = a.G * a.B * a.nt_h;
@@ -109,7 +117,8 @@ __global__ __launch_bounds__(256) void grouped_bwd_kernel(GrpBwdArgs a, const ui
     const bool has_unit = tid < nrs * nk;
     const int u_rs = div_small(tid, nk), u_k = tid - u_rs * nk;
     const int u_hr = div_small(u_rs, noct), u_oct = u_rs - u_hr * noct;
-    unsigned char *u_dst = lds + (u_rs * HWP + a.P2 + 8 * u_k) * 16;
+    unsigned char *u_dst = lds + u_rs * HWP * 16;
+    const int u_c0 = a.P2 + 8 * u_k;  // halo column of the unit's first position
     auto halo_load = [&](int b, int g, int i1_0, u32x4 (&v)[8]) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t ys = make_rsrc_uniform(
             dy + ((int64_t)b * a.Co + (int64_t)g * Cog) * a.y_plane, (uint32_t)Cog * ypl_bytes);
@@ -125,22 +134,22 @@ __global__ __launch_bounds__(256) void grouped_bwd_kernel(GrpBwdArgs a, const ui
     auto halo_store = [&](const u32x4 (&v)[8]) __attribute__((always_inline)) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            u32x4 cell;
+            u32x4 cv;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                cell[i] = __builtin_amdgcn_perm(v[2 * i + 1][e >> 1], v[2 * i][e >> 1], (e & 1) ? kGbPermHi : kGbPermLo);
-            *(u32x4 *)(u_dst + e * 16) = cell;
+                cv[i] = __builtin_amdgcn_perm(v[2 * i + 1][e >> 1], v[2 * i][e >> 1], (e & 1) ? kGbPermHi : kGbPermLo);
+            *(u32x4 *)(u_dst + cell(u_c0 + e) * 16) = cv;
         }
     };
 
     // zero cells (columns left of dy, P2 of them, and right of it): the same
     // for every tile, written once
     {
-        const int zn = HWP - a.O2, zunits = nrs * zn;
+        const int zn = a.hwr - a.O2, zunits = nrs * zn;
         for (int u = tid; u < zunits; u += 256) {
             const int rs = div_small(u, zn), z = u - rs * zn;
             const int col = z < a.P2 ? z : z + a.O2;
-            *(u32x4 *)(lds + (rs * HWP + col) * 16) = u32x4{0u, 0u, 0u, 0u};
+            *(u32x4 *)(lds + (rs * HWP + cell(col)) * 16) = u32x4{0u, 0u, 0u, 0u};
         }
     }
 
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(256) void grouped_bwd_kernel(GrpBwdArgs a, const ui
         for (; r < rows;) {  // uniform
             // this lane's dx position (clamped into the row for the read)
             const int i2 = sg * 16 + l16;
-            const uint32_t abase = (uint32_t)r * row_lds + (uint32_t)(a.S2 * min(i2, a.I2 - 1) * 16);
+            const uint32_t abase = (uint32_t)r * row_lds + (uint32_t)((a.S2 >> sp1) * min(i2, a.I2 - 1) * 16);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KS; ++kb) {

@@ -751,10 +751,17 @@ bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
     if (!buffer_fits((int64_t)fp.Cog * fp.y_plane * 2) || !buffer_fits((int64_t)fp.Cig * fp.x_plane * 2) ||
         !buffer_fits((int64_t)fp.Ci * fp.Cog * fp.ktot * 2))
         return false;
-    // halo row pitch (cells, odd): every column a dx row's taps read and all
-    // of dy's row (staged as whole chunks) after the P2 zero columns
-    const int64_t hwp =
-        std::max<int64_t>((int64_t)a2.S * (a2.I - 1) + (int64_t)a2.D * (a2.K - 1) + 1, (int64_t)a2.P + a2.O) | 1;
+    // halo columns: every column a dx row's taps read and all of dy's row
+    // (staged as whole chunks) after the P2 zero columns. With width stride
+    // 2 the even and odd columns go to separate halves, so that the 16
+    // lanes of an A fragment (dx positions 2 columns apart) read consecutive
+    // cells; the pitch of a (halo row, slice) stays odd.
+    const int64_t hwr =
+        std::max<int64_t>((int64_t)a2.S * (a2.I - 1) + (int64_t)a2.D * (a2.K - 1) + 1, (int64_t)a2.P + a2.O);
+    const int64_t sp = a2.S == 2 ? 2 : 1;
+    const int64_t hp = sp == 1 ? (hwr | 1) : (hwr + 1) / 2;
+    const int64_t hwp = sp == 1 ? hp : 2 * hp + 1;
+    auto cell = [&](int64_t c) { return (c & (sp - 1)) * hp + (c >> (sp - 1)); };
     // the group's W as stored (whole 1 KiB pieces), then the fragment slab
     const int64_t w_bytes = ((int64_t)fp.Cig * fp.Cog * ktot * 2 + 1023) / 1024 * 1024 + 16 * kGbSlabPitch;
     auto halo_rows = [&](int64_t r) { return (int64_t)a1.S * (r - 1) + (int64_t)a1.D * (a1.K - 1) + 1; };
@@ -778,6 +785,7 @@ bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
     g.R = (int32_t)R; g.nt_h = (int32_t)nt_h; g.B = fp.B;
     if ((int64_t)fp.G * fp.B * nt_h > 0x7fffffff) return false;
     g.hr = (int32_t)halo_rows(R); g.hwp = (int32_t)hwp;
+    g.hwr = (int32_t)hwr; g.hp = (int32_t)hp; g.sp = (int32_t)sp;
     g.x_plane = fp.x_plane; g.y_plane = fp.y_plane;
     g.w_off = (int32_t)halo_bytes(R);
     g.slab_off = (int32_t)(halo_bytes(R) + w_bytes - 16 * kGbSlabPitch);
@@ -800,7 +808,7 @@ bool choose_grouped_bwd(Plan *pl, int ndim, int dtype) {
         const int kh = t / a2.K, kw = t % a2.K;
         const int st = fp.w_flip ? (a1.K - 1 - kh) * a2.K + (a2.K - 1 - kw) : kh * a2.K + kw;
         g.slot_w[slot] = (int32_t)(2 * (st * ss + 8 * oct * sco));
-        g.slot_h[slot] = (int32_t)(((a1.D * kh * noct + oct) * hwp + a2.D * kw) * 16);
+        g.slot_h[slot] = (int32_t)(((a1.D * kh * noct + oct) * hwp + cell((int64_t)a2.D * kw)) * 16);
     }
     return true;
 }
